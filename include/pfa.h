@@ -1,0 +1,148 @@
+/*
+ * pfa.h -- C ABI of libpfa, the MI355X (gfx950) prefill attention core:
+ * per-(token, head) RMSNorm of Q and K, NeoX rotary embedding, and causal
+ * grouped-query softmax attention over token-major f32 activations.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout.  Token-major and contiguous: element (token t, head h, dim c) of a
+ *    tensor with `heads` heads sits at (t * heads + h) * head_dim + c.  Q and the
+ *    attention output are [T, n_head * head_dim]; K and V are
+ *    [T, n_head_kv * head_dim].  This is the layout the dense Qwen3 prefill of
+ *    memra-engine 0.130.0 (src/forward.rs, `Model::forward`, activation-layout
+ *    note and SDPA block) keeps between its projections and its attention.
+ *  Pointers.  Tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *    aligned.  The library allocates no device memory and keeps no state beyond
+ *    its loaded code objects.
+ *  Sequences.  `seq_offsets` is a HOST array of n_seqs + 1 int32 values
+ *    (cumulative lengths: seq_offsets[0] = 0, non-decreasing, seq_offsets[n_seqs]
+ *    = T).  NULL means one sequence [0, T) (n_seqs is then ignored).  Token t of
+ *    sequence s has rotary position t - seq_offsets[s]; attention never crosses
+ *    a sequence boundary.  At most PFA_MAX_SEQS sequences; empty sequences are
+ *    allowed and skipped.
+ *  Streams.  `stream` is a hipStream_t (NULL: the null stream).  Every call only
+ *    enqueues kernels on it and returns; nothing synchronises.  A device fault
+ *    therefore surfaces at the caller's next synchronisation.
+ *  Errors.  Each call returns a pfa_status and never aborts or throws.  All
+ *    arguments are checked on the host before anything is enqueued, so a
+ *    non-OK return means no kernel ran; pfa_last_error() then describes the
+ *    problem (thread-local, valid until the next call on the same thread).
+ *    T == 0 is a successful no-op.
+ *  Limits.  head_dim in {64, 128}; n_head a multiple of n_head_kv; rope_dim even,
+ *    2 <= rope_dim <= head_dim; T * max(n_head, n_head_kv) * head_dim < 2^31.
+ */
+#ifndef PFA_H
+#define PFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PFA_MAX_SEQS 128
+
+typedef enum {
+    PFA_OK = 0,
+    PFA_ERR_INVALID_ARG = -1, /* a pointer, size or flag is invalid */
+    PFA_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
+    PFA_ERR_HIP = -3          /* the HIP runtime refused a launch */
+} pfa_status;
+
+/* Input type of the two matrix products inside attention.  Accumulation,
+ * softmax and the output are f32 in both cases; PFA_PREC_BF16 rounds the
+ * normalised Q, K, V and the softmax weights to bf16 (round to nearest even)
+ * before each product. */
+typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1 } pfa_precision;
+
+/*
+ * qknorm_rope -- QK-norm followed by NeoX rotary embedding, for Q and K at once.
+ *
+ * Passages: memra-engine 0.130.0 src/forward.rs, `Model::forward`, QK-norm block
+ * (RMSNorm over head_dim rows, one row per (token, head), each row multiplied by
+ * the learned q_norm / k_norm vector of length head_dim) and RoPE block (NeoX
+ * rotation of Q and K given head_dim, the rotated-dimension count and the
+ * frequency base); needle-core v3/model.rs, `rope_at` / `rope` (frequency of
+ * pair i = base^(-2i / dims), angle = position x frequency).
+ *
+ * For every row x of length head_dim (T * n_head rows of Q, T * n_head_kv of K):
+ *   y_c = x_c * w_c / sqrt(mean_c(x_c^2) + rms_eps)        (w = q_norm_w or k_norm_w)
+ * then, for j < rope_dim / 2, with p the token's position and
+ * theta = p * rope_freq_base^(-2j / rope_dim):
+ *   (y_j, y_{j+rope_dim/2}) <- (y_j cos theta - y_{j+rope_dim/2} sin theta,
+ *                               y_j sin theta + y_{j+rope_dim/2} cos theta)
+ * and dimensions rope_dim..head_dim-1 are left as normalised.  The angle is
+ * reduced in f64 before its cosine and sine are taken, so long positions keep
+ * f32 accuracy.
+ *
+ *  q_in  [T, n_head*head_dim]     f32, device, read
+ *  k_in  [T, n_head_kv*head_dim]  f32, device, read
+ *  q_out, k_out  same shapes, f32, device, written; q_out may equal q_in and
+ *        k_out may equal k_in (in place); any other overlap is an error.
+ *  q_norm_w, k_norm_w  [head_dim] f32, device, read
+ *  rms_eps >= 0, rope_freq_base > 0.
+ */
+int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
+                const float* q_norm_w, const float* k_norm_w,
+                const int32_t* seq_offsets, int n_seqs,
+                int T, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                float rope_freq_base, float rms_eps, void* stream);
+
+/*
+ * gqa_prefill_attn -- causal grouped-query scaled-dot-product attention.
+ *
+ * Passages: memra-engine 0.130.0 src/forward.rs, `Model::forward`, SDPA block
+ * (query heads n_head over n_head_kv K/V heads, T_q = T_kv = T, causal, scale
+ * 1/sqrt(head_dim) from the start of the function); memra-engine 0.101.0
+ * src/spec.rs, `full_attn_verify` per-row fallback (row r attends its own key
+ * and every earlier one).
+ *
+ * With g = n_head / n_head_kv, query head h reads K/V head kv = h / g.  For a
+ * query token i of sequence s = [a, b), the visible keys are a <= j <= i when
+ * `causal` is non-zero, else a <= j < b, and
+ *   out[i, h, :] = sum_j softmax_j(scale * q[i,h,:] . k[j,kv,:]) v[j,kv,:].
+ *
+ *  q    [T, n_head*head_dim]     f32, device, read (already normalised/rotated)
+ *  k, v [T, n_head_kv*head_dim]  f32, device, read
+ *  out  [T, n_head*head_dim]     f32, device, written; must not overlap q, k, v.
+ *  scale  finite; precision  a pfa_precision value.
+ */
+int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
+                     const int32_t* seq_offsets, int n_seqs,
+                     int T, int n_head, int n_head_kv, int head_dim,
+                     float scale, int causal, int precision, void* stream);
+
+/*
+ * qk_prep_attn -- the whole attention core in one call: qknorm_rope applied to
+ * the raw Q and K, then gqa_prefill_attn, with the normalised and rotated Q and
+ * K kept on chip (they are built inside the attention kernel as its Q and K
+ * tiles are loaded).
+ *
+ * Passages: as for qknorm_rope and gqa_prefill_attn; needle-core v3/model.rs,
+ * cache fill after the prefill (the keys a cache keeps are the normalised,
+ * rotated ones) for the optional k_rot_out.
+ *
+ *  q [T, n_head*head_dim], k, v [T, n_head_kv*head_dim]  raw f32, device, read
+ *  out  [T, n_head*head_dim] f32, device, written; must not overlap the inputs.
+ *  k_rot_out  NULL, or [T, n_head_kv*head_dim] f32, device: also receives the
+ *        normalised, rotated K (what a KV cache would store); must not overlap
+ *        the inputs or out.
+ */
+int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
+                 const float* q_norm_w, const float* k_norm_w,
+                 const int32_t* seq_offsets, int n_seqs,
+                 int T, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                 float rope_freq_base, float rms_eps, float scale, int causal, int precision,
+                 float* k_rot_out, void* stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* pfa_last_error(void);
+
+/* Library version string. */
+const char* pfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PFA_H */

@@ -1,0 +1,147 @@
+"""CPU oracle for the prefill attention core -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never calls it and
+shares no code with it.
+
+``oracle.c`` holds the arithmetic (plain f64 loops, threaded over independent
+rows); this module builds it with the host C compiler and wraps it for numpy.
+
+* :func:`qknorm_rope` -- per-(token, head) RMSNorm with a learned scale, then
+  NeoX rotary embedding (memra-engine 0.130.0 ``src/forward.rs``,
+  ``Model::forward``, QK-norm and RoPE blocks; needle-core ``v3/model.rs``,
+  ``rope_at`` / ``rope``).
+* :func:`gqa_attn` -- causal grouped-query softmax attention
+  (``Model::forward``, SDPA block; memra-engine 0.101.0 ``src/spec.rs``,
+  ``full_attn_verify`` per-row fallback for the causal rule).
+* :func:`qk_prep_attn` -- the two composed in f64 with no rounding between.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (always recompiles)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-fno-fast-math", "-o", _LIB + ".tmp", _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.POINTER(ctypes.c_double)
+    fp = ctypes.POINTER(ctypes.c_float)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lp = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_qknorm_rope.argtypes = [fp, fp, fp, fp, ip, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_double, ctypes.c_double, dp, dp, ctypes.c_int]
+    lib.oracle_qknorm_rope.restype = ctypes.c_int
+    lib.oracle_gqa_attn.argtypes = [dp, dp, dp, ip, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                    lp, ctypes.c_int64, dp, ctypes.c_int]
+    lib.oracle_gqa_attn.restype = ctypes.c_int
+    lib.oracle_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _offsets(seq_offsets, T):
+    if seq_offsets is None:
+        return np.array([0, T], dtype=np.int32)
+    return np.ascontiguousarray(seq_offsets, dtype=np.int32)
+
+
+def qknorm_rope(q, k, wq, wk, *, n_head, n_head_kv, head_dim, rope_dim, rope_freq_base,
+                rms_eps, seq_offsets=None, n_threads=0):
+    """O1 + O2 on f32 inputs ``q [T, n_head*head_dim]``, ``k [T, n_head_kv*head_dim]``.
+
+    Returns ``(q', k')`` as float64 arrays of the same shapes."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    wq = np.ascontiguousarray(wq, dtype=np.float32)
+    wk = np.ascontiguousarray(wk, dtype=np.float32)
+    T = q.shape[0]
+    if q.size != T * n_head * head_dim or k.size != T * n_head_kv * head_dim:
+        raise ValueError("q/k shapes do not match the head geometry")
+    if wq.size != head_dim or wk.size != head_dim:
+        raise ValueError("norm weights must have head_dim entries")
+    offs = _offsets(seq_offsets, T)
+    qo = np.empty((T, n_head * head_dim), dtype=np.float64)
+    ko = np.empty((T, n_head_kv * head_dim), dtype=np.float64)
+    rc = _load().oracle_qknorm_rope(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                    _ptr(wq, ctypes.c_float), _ptr(wk, ctypes.c_float),
+                                    _ptr(offs, ctypes.c_int32), len(offs) - 1, T, n_head,
+                                    n_head_kv, head_dim, rope_dim, float(rope_freq_base),
+                                    float(rms_eps), _ptr(qo, ctypes.c_double),
+                                    _ptr(ko, ctypes.c_double), n_threads)
+    if rc != 0:
+        raise ValueError(f"oracle_qknorm_rope failed ({rc})")
+    return qo, ko
+
+
+def gqa_attn(q, k, v, *, n_head, n_head_kv, head_dim, scale, causal=True, seq_offsets=None,
+             rows=None, n_threads=0):
+    """O3 on ``q [T, n_head*head_dim]``, ``k``/``v [T, n_head_kv*head_dim]`` (any float
+    dtype; converted to f64 exactly).  With ``rows`` only those query rows are computed and
+    the result is ``[len(rows), n_head*head_dim]``; otherwise ``[T, n_head*head_dim]``."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    T = q.shape[0]
+    if q.size != T * n_head * head_dim or k.size != T * n_head_kv * head_dim or v.size != k.size:
+        raise ValueError("q/k/v shapes do not match the head geometry")
+    offs = _offsets(seq_offsets, T)
+    if rows is None:
+        rows_arr, n_rows, rp = None, T, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows_arr.size
+        rp = _ptr(rows_arr, ctypes.c_int64)
+    out = np.empty((n_rows, n_head * head_dim), dtype=np.float64)
+    rc = _load().oracle_gqa_attn(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                 _ptr(v, ctypes.c_double), _ptr(offs, ctypes.c_int32),
+                                 len(offs) - 1, T, n_head, n_head_kv, head_dim, float(scale),
+                                 1 if causal else 0, rp, n_rows, _ptr(out, ctypes.c_double),
+                                 n_threads)
+    if rc != 0:
+        raise ValueError(f"oracle_gqa_attn failed ({rc})")
+    return out
+
+
+def qk_prep_attn(q, k, v, wq, wk, *, n_head, n_head_kv, head_dim, rope_dim, rope_freq_base,
+                 rms_eps, scale, causal=True, seq_offsets=None, rows=None, n_threads=0,
+                 return_k_rot=False):
+    """O3 applied to O1+O2 of the raw f32 Q and K, all in f64 with no rounding between."""
+    qn, kn = qknorm_rope(q, k, wq, wk, n_head=n_head, n_head_kv=n_head_kv, head_dim=head_dim,
+                         rope_dim=rope_dim, rope_freq_base=rope_freq_base, rms_eps=rms_eps,
+                         seq_offsets=seq_offsets, n_threads=n_threads)
+    out = gqa_attn(qn, kn, v, n_head=n_head, n_head_kv=n_head_kv, head_dim=head_dim,
+                   scale=scale, causal=causal, seq_offsets=seq_offsets, rows=rows,
+                   n_threads=n_threads)
+    return (out, kn) if return_k_rot else out
+
+
+def version() -> str:
+    return _load().oracle_version().decode()

@@ -1,0 +1,469 @@
+"""Pins for the CPU oracle (no GPU).  Each test ties the oracle to something other
+than itself: a closed form, an invariant the mathematics fixes, a special case
+that reduces to a library routine (torch's f64 CPU RMSNorm and SDPA, the Qwen3
+rotate-half routine in ``transformers``), or brute force on tiny inputs.
+
+Passages pinned (paraphrased):
+* memra-engine 0.130.0 ``src/forward.rs``, ``Model::forward``, QK-norm block --
+  per-(token, head) RMSNorm over head_dim rows, times the learned scale vector.
+* same page, RoPE block, and needle-core ``v3/model.rs`` ``rope_at`` / ``rope`` --
+  NeoX rotation, frequency base^(-2i/dims), angle = position x frequency.
+* same page, SDPA block -- causal GQA with scale 1/sqrt(head_dim).
+* memra-engine 0.101.0 ``src/spec.rs``, ``full_attn_verify`` per-row fallback --
+  row r sees keys 0..r inclusive.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from transformer_prefill_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _qkn(q, k, wq, wk, H, Hkv, d, n, base=1e6, eps=1e-6, offs=None):
+    return oracle.qknorm_rope(q, k, wq, wk, n_head=H, n_head_kv=Hkv, head_dim=d, rope_dim=n,
+                              rope_freq_base=base, rms_eps=eps, seq_offsets=offs)
+
+
+def _attn(q, k, v, H, Hkv, d, scale, causal=True, offs=None, rows=None):
+    return oracle.gqa_attn(q, k, v, n_head=H, n_head_kv=Hkv, head_dim=d, scale=scale,
+                           causal=causal, seq_offsets=offs, rows=rows)
+
+
+# --------------------------------------------------------------------------- O1 QK-norm
+
+def test_rmsnorm_unit_rms_without_eps():
+    """w = 1, eps = 0: every normalised row has mean square exactly 1 (rope off)."""
+    r = _rng(1)
+    T, H, Hkv, d = 5, 3, 1, 64
+    q = r.standard_normal((T, H * d)).astype(np.float32) * 3
+    k = r.standard_normal((T, Hkv * d)).astype(np.float32)
+    one = np.ones(d, np.float32)
+    qn, kn = _qkn(q, k, one, one, H, Hkv, d, 0, eps=0.0)
+    ms = (qn.reshape(T * H, d) ** 2).mean(axis=1)
+    np.testing.assert_allclose(ms, 1.0, rtol=0, atol=1e-13)
+    ms = (kn.reshape(T * Hkv, d) ** 2).mean(axis=1)
+    np.testing.assert_allclose(ms, 1.0, rtol=0, atol=1e-13)
+
+
+def test_rmsnorm_eps_inside_root_closed_form():
+    """w = 1: mean(y^2) = ms / (ms + eps) -- eps is added to the mean square, under the root."""
+    r = _rng(2)
+    T, H, d = 4, 2, 128
+    q = r.standard_normal((T, H * d)).astype(np.float32) * 0.5
+    k = q[:, :d].copy()
+    one = np.ones(d, np.float32)
+    eps = 0.25
+    qn, _ = _qkn(q, k, one, one, H, 1, d, 0, eps=eps)
+    x = q.astype(np.float64).reshape(T * H, d)
+    ms = (x ** 2).mean(axis=1)
+    got = (qn.reshape(T * H, d) ** 2).mean(axis=1)
+    np.testing.assert_allclose(got, ms / (ms + eps), rtol=1e-13)
+
+
+def test_rmsnorm_scale_is_per_channel_multiplier():
+    """y(w) = y(1) * w channel by channel (the learned vector multiplies, it is not 1 + w)."""
+    r = _rng(3)
+    T, H, d = 3, 2, 64
+    q = r.standard_normal((T, H * d)).astype(np.float32)
+    w = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    one = np.ones(d, np.float32)
+    y1, _ = _qkn(q, q[:, :d], one, one, H, 1, d, 0)
+    yw, _ = _qkn(q, q[:, :d], w, w, H, 1, d, 0)
+    np.testing.assert_allclose(yw.reshape(T, H, d), y1.reshape(T, H, d) * w.astype(np.float64),
+                               rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_matches_torch_f64():
+    """Library routine: torch.nn.functional.rms_norm in f64 on every (token, head) row."""
+    r = _rng(4)
+    T, H, Hkv, d = 7, 4, 2, 128
+    q = r.standard_normal((T, H * d)).astype(np.float32)
+    k = r.standard_normal((T, Hkv * d)).astype(np.float32)
+    wq = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    wk = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    qn, kn = _qkn(q, k, wq, wk, H, Hkv, d, 0, eps=1e-6)
+    ref_q = F.rms_norm(torch.from_numpy(q.astype(np.float64)).view(T, H, d), [d],
+                       weight=torch.from_numpy(wq.astype(np.float64)), eps=1e-6)
+    ref_k = F.rms_norm(torch.from_numpy(k.astype(np.float64)).view(T, Hkv, d), [d],
+                       weight=torch.from_numpy(wk.astype(np.float64)), eps=1e-6)
+    np.testing.assert_allclose(qn, ref_q.reshape(T, H * d).numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(kn, ref_k.reshape(T, Hkv * d).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_rmsnorm_scale_invariance_erases_outlier_factor():
+    """norm(8x) = norm(x) up to O(eps/ms): the x8 outlier keys vanish after QK-norm."""
+    r = _rng(5)
+    T, d = 6, 128
+    k = r.standard_normal((T, d)).astype(np.float32)
+    w = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    _, a = _qkn(k, k, w, w, 1, 1, d, d)
+    _, b = _qkn(k, (k * 8).astype(np.float32), w, w, 1, 1, d, d)
+    np.testing.assert_allclose(a, b, rtol=0, atol=5e-6)
+
+
+# --------------------------------------------------------------------------- O2 RoPE
+
+def test_rope_identity_at_position_zero_bit_exact():
+    """Position 0 (the first token of every sequence) is not rotated at all."""
+    r = _rng(6)
+    d = 128
+    offs = np.array([0, 3, 8, 9], np.int32)
+    T = 9
+    q = r.standard_normal((T, 2 * d)).astype(np.float32)
+    w = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    with_rope, _ = _qkn(q, q[:, :d], w, w, 2, 1, d, d, offs=offs)
+    no_rope, _ = _qkn(q, q[:, :d], w, w, 2, 1, d, 0, offs=offs)
+    for s in offs[:-1]:
+        assert np.array_equal(with_rope[s], no_rope[s])
+    assert not np.allclose(with_rope[1], no_rope[1])
+
+
+def test_rope_one_radian_closed_form():
+    """base 1e4, rope_dim 4: pair j=1 has frequency 1e4^(-1/2) = 0.01, so at position 100 it
+    turns by exactly 1 rad; pair j=0 (frequency 1) turns by 100 rad.  Pairs are (j, j+2);
+    dims 4..7 of an 8-wide head pass through untouched."""
+    d, n, T = 8, 4, 101
+    x = np.zeros((T, d), np.float32)
+    r = _rng(7)
+    x[100] = r.standard_normal(d).astype(np.float32)
+    one = np.ones(d, np.float32)
+    eps = 0.0
+    y, _ = _qkn(x, x, one, one, 1, 1, d, n, base=1e4, eps=eps)
+    base_norm, _ = _qkn(x, x, one, one, 1, 1, d, 0, base=1e4, eps=eps)
+    a = base_norm[100]
+    got = y[100]
+    for j, th in ((0, 100.0), (1, 1.0)):
+        c, s = math.cos(th), math.sin(th)
+        assert got[j] == pytest.approx(a[j] * c - a[j + 2] * s, abs=1e-13)
+        assert got[j + 2] == pytest.approx(a[j] * s + a[j + 2] * c, abs=1e-13)
+    assert np.array_equal(got[4:], a[4:])
+
+
+def test_rope_pairs_are_rotate_half_not_interleaved():
+    """A unit vector on dim 0 only ever moves into dim n/2, never into dim 1."""
+    d = n = 64
+    T = 40
+    x = np.zeros((T, d), np.float32)
+    x[:, 0] = 1.0
+    one = np.ones(d, np.float32)
+    y, _ = _qkn(x, x, one, one, 1, 1, d, n, eps=0.0)
+    y = y / math.sqrt(d)  # undo the norm of a unit vector (rms = 1/sqrt(d))
+    mask = np.ones(d, bool)
+    mask[[0, n // 2]] = False
+    assert np.all(y[:, mask] == 0.0)
+    np.testing.assert_allclose(y[:, 0] ** 2 + y[:, n // 2] ** 2, 1.0, atol=1e-14)
+    # the turn is counter-clockwise: dim n/2 gets +sin(theta), theta = p for pair 0
+    p = np.arange(T)
+    np.testing.assert_allclose(y[:, n // 2], np.sin(p), atol=1e-14)
+
+
+def test_rope_matches_transformers_rotate_half():
+    """Library routine: the Qwen3 ``apply_rotary_pos_emb`` in ``transformers`` (rotate-half),
+    fed f64 cos/sin of position x base^(-2i/d), on the f64 RMSNorm output."""
+    from transformers.models.qwen3.modeling_qwen3 import apply_rotary_pos_emb
+    r = _rng(8)
+    T, H, Hkv, d = 33, 4, 2, 128
+    base = 1e6
+    q = r.standard_normal((T, H * d)).astype(np.float32)
+    k = r.standard_normal((T, Hkv * d)).astype(np.float32)
+    wq = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    wk = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    qn, kn = _qkn(q, k, wq, wk, H, Hkv, d, d, base=base)
+    q0, k0 = _qkn(q, k, wq, wk, H, Hkv, d, 0, base=base)
+    inv = base ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+    ang = np.arange(T, dtype=np.float64)[:, None] * inv[None, :]
+    emb = np.concatenate([ang, ang], axis=1)
+    cos = torch.from_numpy(np.cos(emb))[None]
+    sin = torch.from_numpy(np.sin(emb))[None]
+    tq = torch.from_numpy(q0).view(1, T, H, d).transpose(1, 2)
+    tk = torch.from_numpy(k0).view(1, T, Hkv, d).transpose(1, 2)
+    rq, rk = apply_rotary_pos_emb(tq, tk, cos, sin)
+    np.testing.assert_allclose(qn, rq.transpose(1, 2).reshape(T, H * d).numpy(), atol=1e-12)
+    np.testing.assert_allclose(kn, rk.transpose(1, 2).reshape(T, Hkv * d).numpy(), atol=1e-12)
+
+
+def test_rope_relative_position_property():
+    """<R_m q, R_n k> depends only on m - n: the same raw q/k rows placed at positions
+    (9, 4) and (20, 15) give the same dot product; at (20, 4) they do not."""
+    r = _rng(9)
+    d = 128
+    T = 21
+    x = r.standard_normal((T, d)).astype(np.float32)
+    qv = r.standard_normal(d).astype(np.float32)
+    kv = r.standard_normal(d).astype(np.float32)
+    for t in (9, 20):
+        x[t] = qv
+    for t in (4, 15):
+        x[t] = kv
+    one = np.ones(d, np.float32)
+    y, _ = _qkn(x, x, one, one, 1, 1, d, d, base=1e4)
+    a = y[9] @ y[4]
+    b = y[20] @ y[15]
+    c = y[20] @ y[4]
+    assert a == pytest.approx(b, rel=1e-12, abs=1e-10)
+    assert abs(a - c) > 1e-3
+
+
+def test_rope_partial_rotary_uses_rope_dim_in_exponent():
+    """rope_dim 64 of head_dim 128 (the mixed workload): pair j turns by p * base^(-2j/64)
+    (not /128), and dims 64..127 are untouched."""
+    d, n, base = 128, 64, 1e4
+    T = 6
+    x = np.zeros((T, d), np.float32)
+    x[:, 1] = 1.0                      # pair j = 1 -> dims (1, 33)
+    x[:, 100] = 2.0                    # pass-through dim
+    one = np.ones(d, np.float32)
+    y, _ = _qkn(x, x, one, one, 1, 1, d, n, base=base, eps=0.0)
+    rms = math.sqrt(5.0 / d)
+    th = np.arange(T) * base ** (-2.0 / n)
+    np.testing.assert_allclose(y[:, 1] * rms, np.cos(th), atol=1e-14)
+    np.testing.assert_allclose(y[:, 33] * rms, np.sin(th), atol=1e-14)
+    np.testing.assert_allclose(y[:, 100] * rms, 2.0, atol=1e-14)
+
+
+def test_positions_restart_per_sequence():
+    """Packed sequences: token offs[s] + p has position p, whatever came before it."""
+    r = _rng(10)
+    d = 64
+    lens = [5, 1, 7]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = offs[-1]
+    x = r.standard_normal((T, d)).astype(np.float32)
+    one = np.ones(d, np.float32)
+    packed, _ = _qkn(x, x, one, one, 1, 1, d, d, offs=offs)
+    for s in range(len(lens)):
+        a, b = offs[s], offs[s + 1]
+        alone, _ = _qkn(x[a:b], x[a:b], one, one, 1, 1, d, d)
+        assert np.array_equal(packed[a:b], alone)
+
+
+# --------------------------------------------------------------------------- O3 attention
+
+def _torch_sdpa(q, k, v, H, Hkv, d, scale, causal, offs):
+    T = q.shape[0]
+    out = np.empty((T, H * d))
+    for s in range(len(offs) - 1):
+        a, b = int(offs[s]), int(offs[s + 1])
+        if b == a:
+            continue
+        tq = torch.from_numpy(np.asarray(q[a:b], np.float64)).view(b - a, H, d).transpose(0, 1)[None]
+        tk = torch.from_numpy(np.asarray(k[a:b], np.float64)).view(b - a, Hkv, d).transpose(0, 1)[None]
+        tv = torch.from_numpy(np.asarray(v[a:b], np.float64)).view(b - a, Hkv, d).transpose(0, 1)[None]
+        o = F.scaled_dot_product_attention(tq.contiguous(), tk.contiguous(), tv.contiguous(),
+                                           is_causal=causal, scale=scale, enable_gqa=True)
+        out[a:b] = o[0].transpose(0, 1).reshape(b - a, H * d).numpy()
+    return out
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("H,Hkv,d", [(4, 2, 64), (8, 8, 32), (6, 2, 16), (4, 1, 128)])
+def test_attention_matches_torch_sdpa_f64(H, Hkv, d, causal):
+    """Library routine: torch's f64 CPU scaled_dot_product_attention with GQA head
+    repetition (query head h reads K/V head h // (H/Hkv)), per packed sequence."""
+    r = _rng(11 + H + d)
+    lens = [1, 9, 23, 2]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(offs[-1])
+    q = r.standard_normal((T, H * d)).astype(np.float32)
+    k = r.standard_normal((T, Hkv * d)).astype(np.float32)
+    v = r.standard_normal((T, Hkv * d)).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    got = _attn(q, k, v, H, Hkv, d, scale, causal=causal, offs=offs)
+    ref = _torch_sdpa(q, k, v, H, Hkv, d, scale, causal, offs)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_attention_first_row_is_v_exactly():
+    """A sequence's first causal row sees one key, with weight exactly 1: it equals V."""
+    w = wl.CONFIGS["mixed"].with_(seq_lens=(3, 1, 17, 40), n_head=8, n_head_kv=2)
+    x = wl.make_inputs(w)
+    offs = w.seq_offsets
+    out = _attn(x.q, x.k, x.v, 8, 2, 128, w.softmax_scale, offs=offs)
+    for s in offs[:-1]:
+        for h in range(8):
+            kv = h // 4
+            assert np.array_equal(out[s, h * 128:(h + 1) * 128],
+                                  x.v[s, kv * 128:(kv + 1) * 128].astype(np.float64))
+
+
+def test_attention_constant_values():
+    """Softmax weights sum to one: V = c everywhere gives c everywhere."""
+    r = _rng(12)
+    T, H, Hkv, d = 37, 4, 2, 64
+    q = r.standard_normal((T, H * d)) * 4
+    k = r.standard_normal((T, Hkv * d)) * 4
+    v = np.full((T, Hkv * d), -1.75)
+    out = _attn(q, k, v, H, Hkv, d, 0.125, causal=True)
+    np.testing.assert_allclose(out, -1.75, rtol=1e-14)
+
+
+def test_attention_gqa_head_map_probe():
+    """V[:, kv, :] = kv: query head h must output kv = h // (H / Hkv) (consecutive query
+    heads share a K/V head)."""
+    r = _rng(13)
+    T, H, Hkv, d = 11, 8, 2, 16
+    q = r.standard_normal((T, H * d))
+    k = r.standard_normal((T, Hkv * d))
+    v = np.repeat(np.arange(Hkv, dtype=np.float64), d)[None, :].repeat(T, 0)
+    out = _attn(q, k, v, H, Hkv, d, 0.25)
+    for h in range(H):
+        np.testing.assert_allclose(out[:, h * d:(h + 1) * d], h // (H // Hkv), rtol=1e-14)
+
+
+def test_attention_mha_special_case():
+    """H = Hkv is plain multi-head attention: each head equals a one-head run on its own
+    slices."""
+    r = _rng(14)
+    T, H, d = 19, 3, 32
+    q = r.standard_normal((T, H * d))
+    k = r.standard_normal((T, H * d))
+    v = r.standard_normal((T, H * d))
+    out = _attn(q, k, v, H, H, d, 0.2)
+    for h in range(H):
+        sl = slice(h * d, (h + 1) * d)
+        one = _attn(q[:, sl], k[:, sl], v[:, sl], 1, 1, d, 0.2)
+        assert np.array_equal(out[:, sl], one)
+
+
+def test_attention_future_perturbation_leaves_past_rows_bit_exact():
+    r = _rng(15)
+    T, H, Hkv, d = 30, 4, 2, 32
+    q = r.standard_normal((T, H * d))
+    k = r.standard_normal((T, Hkv * d))
+    v = r.standard_normal((T, Hkv * d))
+    a = _attn(q, k, v, H, Hkv, d, 0.3)
+    j = 17
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[j:] += 5
+    k2[j:] *= -3
+    v2[j:] = 100
+    b = _attn(q2, k2, v2, H, Hkv, d, 0.3)
+    assert np.array_equal(a[:j], b[:j])
+    assert not np.allclose(a[j:], b[j:])
+
+
+def test_attention_packed_equals_separate():
+    r = _rng(16)
+    H, Hkv, d = 4, 2, 32
+    lens = [6, 1, 13, 4]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(offs[-1])
+    q = r.standard_normal((T, H * d))
+    k = r.standard_normal((T, Hkv * d))
+    v = r.standard_normal((T, Hkv * d))
+    for causal in (True, False):
+        packed = _attn(q, k, v, H, Hkv, d, 0.25, causal=causal, offs=offs)
+        for s in range(len(lens)):
+            a, b = offs[s], offs[s + 1]
+            alone = _attn(q[a:b], k[a:b], v[a:b], H, Hkv, d, 0.25, causal=causal)
+            assert np.array_equal(packed[a:b], alone)
+
+
+def test_attention_two_token_closed_form():
+    """T = 2, one head, d = 2, scale 1: row 1 weighs key 0 (score 0) and key 1 (score 1)
+    as 1 : e."""
+    q = np.array([[0.0, 3.0], [1.0, 0.0]])
+    k = np.array([[0.0, 5.0], [1.0, 0.0]])
+    v = np.array([[2.0, -1.0], [4.0, 1.0]])
+    out = _attn(q, k, v, 1, 1, 2, 1.0)
+    e = math.e
+    np.testing.assert_allclose(out[0], v[0], rtol=0)
+    np.testing.assert_allclose(out[1], (v[0] + e * v[1]) / (1 + e), rtol=1e-15)
+
+
+def test_attention_large_scores_are_stable():
+    """Scores of +-1000 must not overflow: the softmax is max-subtracted.
+    Row 2 sees scores (1000, -1000, 999) -> weights (1, 0, e^-1) / (1 + e^-1)."""
+    q = np.array([[1.0], [1.0], [1.0]])
+    k = np.array([[1000.0], [-1000.0], [999.0]])
+    v = np.array([[1.0], [7.0], [3.0]])
+    out = _attn(q, k, v, 1, 1, 1, 1.0)
+    w = math.exp(-1.0)
+    assert out[2, 0] == pytest.approx((1.0 + 3.0 * w) / (1.0 + w), rel=1e-14)
+    assert np.all(np.isfinite(out))
+
+
+def test_attention_row_sampling_matches_full():
+    r = _rng(17)
+    H, Hkv, d = 4, 2, 64
+    offs = np.array([0, 10, 31], np.int32)
+    q = r.standard_normal((31, H * d))
+    k = r.standard_normal((31, Hkv * d))
+    v = r.standard_normal((31, Hkv * d))
+    full = _attn(q, k, v, H, Hkv, d, 0.125, offs=offs)
+    rows = np.array([30, 0, 10, 9, 11])
+    part = _attn(q, k, v, H, Hkv, d, 0.125, offs=offs, rows=rows)
+    assert np.array_equal(part, full[rows])
+
+
+def test_oracle_thread_count_does_not_change_results():
+    r = _rng(18)
+    T, H, Hkv, d = 50, 4, 2, 64
+    q = r.standard_normal((T, H * d))
+    k = r.standard_normal((T, Hkv * d))
+    v = r.standard_normal((T, Hkv * d))
+    a = oracle.gqa_attn(q, k, v, n_head=H, n_head_kv=Hkv, head_dim=d, scale=0.1, n_threads=1)
+    b = oracle.gqa_attn(q, k, v, n_head=H, n_head_kv=Hkv, head_dim=d, scale=0.1, n_threads=7)
+    assert np.array_equal(a, b)
+
+
+def test_oracle_rejects_bad_arguments():
+    q = np.zeros((4, 24))
+    k = np.zeros((4, 16))
+    with pytest.raises(ValueError):  # n_head not a multiple of n_head_kv
+        oracle.gqa_attn(q, k, k, n_head=3, n_head_kv=2, head_dim=8, scale=1.0)
+    q = np.zeros((4, 8))
+    with pytest.raises(ValueError):
+        oracle.gqa_attn(q, q, q, n_head=1, n_head_kv=1, head_dim=8, scale=1.0,
+                        seq_offsets=np.array([0, 5], np.int32))
+
+
+# --------------------------------------------------------------------------- whole chain
+
+def test_tiny_config_chain_against_library_routines():
+    """The tiny workload end to end: torch RMSNorm -> transformers rotate-half RoPE ->
+    torch SDPA (all f64) equals the oracle's qk_prep_attn."""
+    from transformers.models.qwen3.modeling_qwen3 import apply_rotary_pos_emb
+    w = wl.CONFIGS["tiny"]
+    x = wl.make_inputs(w)
+    T, H, Hkv, d = w.T, w.n_head, w.n_head_kv, w.head_dim
+    got = oracle.qk_prep_attn(x.q, x.k, x.v, x.wq, x.wk, n_head=H, n_head_kv=Hkv, head_dim=d,
+                              rope_dim=w.rope_dim, rope_freq_base=w.rope_freq_base,
+                              rms_eps=w.rms_eps, scale=w.softmax_scale)
+    eps = float(np.float32(w.rms_eps))
+    tq = F.rms_norm(torch.from_numpy(x.q.astype(np.float64)).view(T, H, d), [d],
+                    weight=torch.from_numpy(x.wq.astype(np.float64)), eps=eps)
+    tk = F.rms_norm(torch.from_numpy(x.k.astype(np.float64)).view(T, Hkv, d), [d],
+                    weight=torch.from_numpy(x.wk.astype(np.float64)), eps=eps)
+    inv = w.rope_freq_base ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+    ang = np.arange(T, dtype=np.float64)[:, None] * inv[None, :]
+    emb = np.concatenate([ang, ang], axis=1)
+    cos, sin = torch.from_numpy(np.cos(emb))[None], torch.from_numpy(np.sin(emb))[None]
+    rq, rk = apply_rotary_pos_emb(tq.transpose(0, 1)[None], tk.transpose(0, 1)[None], cos, sin)
+    tv = torch.from_numpy(x.v.astype(np.float64)).view(T, Hkv, d).transpose(0, 1)[None]
+    o = F.scaled_dot_product_attention(rq.contiguous(), rk.contiguous(), tv.contiguous(),
+                                       is_causal=True, scale=w.softmax_scale, enable_gqa=True)
+    ref = o[0].transpose(0, 1).reshape(T, H * d).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_workload_generator_is_seeded_and_shaped():
+    w = wl.CONFIGS["long"].with_(seq_lens=(1000,))
+    a, b = wl.make_inputs(w), wl.make_inputs(w)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.outliers, b.outliers)
+    assert a.q.dtype == np.float32 and a.q.shape == (1000, 32 * 128)
+    assert a.k.shape == (1000, 8 * 128) and a.wq.shape == (128,)
+    assert a.outliers.size == 10 and len(set(a.outliers.tolist())) == 10
+    assert wl.CONFIGS["mixed"].seq_offsets.tolist() == [0, 128, 384, 896, 1920, 3968, 6968,
+                                                        11064, 16064]
+    assert wl.CONFIGS["prefill_8192"].attn_flops() == 4 * 128 * 32 * (8192 * 8193 // 2)

@@ -1,0 +1,205 @@
+"""Python binding of ``libpfa.so`` (declared in ``include/pfa.h``).
+
+Argument marshalling only: shapes, dtypes and devices are checked, output
+tensors are allocated with torch when the caller passes none, and the C entry
+point of the same name is called with raw device pointers and the current torch
+stream.  Every step of the computation runs in the library's HIP kernels; there
+is no fallback of any kind -- if the library is missing, every op raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpfa.so")
+
+PRECISION_F32 = 0
+PRECISION_BF16 = 1
+_PRECISIONS = {"f32": PRECISION_F32, "fp32": PRECISION_F32, "float32": PRECISION_F32,
+               "bf16": PRECISION_BF16, "bfloat16": PRECISION_BF16,
+               PRECISION_F32: PRECISION_F32, PRECISION_BF16: PRECISION_BF16}
+
+# Every symbol include/pfa.h declares.
+EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_last_error", "pfa_version")
+
+
+class PfaError(RuntimeError):
+    """A libpfa entry point returned a non-OK status (or the library is missing)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[pfa status {status}] {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libpfa.so``, with argument types declared.  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise PfaError(-100, f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; "
+                             "g.build()'` first (there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, fp_ = ctypes.c_void_p, ctypes.c_void_p
+    i32, f32 = ctypes.c_int, ctypes.c_float
+    L.qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+    L.qknorm_rope.restype = i32
+    L.gqa_prefill_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    L.gqa_prefill_attn.restype = i32
+    L.qk_prep_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
+                               f32, i32, i32, fp_, vp]
+    L.qk_prep_attn.restype = i32
+    L.pfa_last_error.restype = ctypes.c_char_p
+    L.pfa_last_error.argtypes = []
+    L.pfa_version.restype = ctypes.c_char_p
+    L.pfa_version.argtypes = []
+    _lib = L
+    return L
+
+
+def version() -> str:
+    return lib().pfa_version().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise PfaError(status, lib().pfa_last_error().decode())
+
+
+def _offsets(seq_offsets, T):
+    """Host int32 array for the C call (kept alive by the caller), or None."""
+    if seq_offsets is None:
+        return None, 0, None
+    try:
+        import torch
+        if isinstance(seq_offsets, torch.Tensor):
+            seq_offsets = seq_offsets.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    arr = np.ascontiguousarray(np.asarray(seq_offsets), dtype=np.int32)
+    return arr, arr.size - 1, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev_f32(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _heads(t, head_dim, name):
+    """(T, heads) of a [T, heads*head_dim] or [T, heads, head_dim] tensor."""
+    if t.dim() == 3:
+        if t.shape[2] != head_dim:
+            raise ValueError(f"{name}: last dim {t.shape[2]} != head_dim {head_dim}")
+        return t.shape[0], t.shape[1]
+    if t.dim() != 2 or t.shape[1] % head_dim:
+        raise ValueError(f"{name} must be [T, heads*head_dim] or [T, heads, head_dim]")
+    return t.shape[0], t.shape[1] // head_dim
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _prec(precision):
+    try:
+        return _PRECISIONS[precision]
+    except KeyError:
+        raise ValueError(f"precision must be 'f32' or 'bf16', got {precision!r}") from None
+
+
+def qknorm_rope(q, k, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
+                rope_freq_base: float, rms_eps: float,
+                seq_offsets: Optional[Sequence[int]] = None, q_out=None, k_out=None):
+    """QK RMSNorm + NeoX RoPE (``qknorm_rope`` in ``include/pfa.h``).
+
+    Returns ``(q_out, k_out)``; pass ``q_out=q, k_out=k`` to work in place."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        _dev_f32(t, n)
+    T, H = _heads(q, head_dim, "q")
+    Tk, Hkv = _heads(k, head_dim, "k")
+    if Tk != T:
+        raise ValueError(f"q has {T} tokens but k has {Tk}")
+    q_out = torch.empty_like(q) if q_out is None else _dev_f32(q_out, "q_out")
+    k_out = torch.empty_like(k) if k_out is None else _dev_f32(k_out, "k_out")
+    if q_out.numel() != q.numel() or k_out.numel() != k.numel():
+        raise ValueError("output shapes must match the inputs")
+    offs, n_seqs, op = _offsets(seq_offsets, T)
+    _check(lib().qknorm_rope(_ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out), _ptr(q_norm_w),
+                             _ptr(k_norm_w), op, n_seqs, T, H, Hkv, head_dim, rope_dim,
+                             float(rope_freq_base), float(rms_eps), _stream(q)))
+    return q_out, k_out
+
+
+def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
+                     causal: bool = True, precision="f32",
+                     seq_offsets: Optional[Sequence[int]] = None, out=None):
+    """Causal GQA attention (``gqa_prefill_attn`` in ``include/pfa.h``); returns ``out``."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_f32(t, n)
+    T, H = _heads(q, head_dim, "q")
+    Tk, Hkv = _heads(k, head_dim, "k")
+    if Tk != T or v.shape != k.shape:
+        raise ValueError("q, k, v must have the same token count and k, v the same shape")
+    out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = head_dim ** -0.5
+    offs, n_seqs, op = _offsets(seq_offsets, T)
+    _check(lib().gqa_prefill_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), op, n_seqs, T, H, Hkv,
+                                  head_dim, float(scale), 1 if causal else 0, _prec(precision),
+                                  _stream(q)))
+    return out
+
+
+def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
+                 rope_freq_base: float, rms_eps: float, scale: Optional[float] = None,
+                 causal: bool = True, precision="f32",
+                 seq_offsets: Optional[Sequence[int]] = None, out=None, k_rot_out=None):
+    """Fused QK-norm + RoPE + causal GQA attention (``qk_prep_attn`` in ``include/pfa.h``).
+
+    Returns ``out`` (and also writes ``k_rot_out`` when one is given)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        _dev_f32(t, n)
+    T, H = _heads(q, head_dim, "q")
+    Tk, Hkv = _heads(k, head_dim, "k")
+    if Tk != T or v.shape != k.shape:
+        raise ValueError("q, k, v must have the same token count and k, v the same shape")
+    out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    if k_rot_out is not None:
+        _dev_f32(k_rot_out, "k_rot_out")
+        if k_rot_out.numel() != k.numel():
+            raise ValueError("k_rot_out must have k's shape")
+    if scale is None:
+        scale = head_dim ** -0.5
+    offs, n_seqs, op = _offsets(seq_offsets, T)
+    _check(lib().qk_prep_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(q_norm_w),
+                              _ptr(k_norm_w), op, n_seqs, T, H, Hkv, head_dim, rope_dim,
+                              float(rope_freq_base), float(rms_eps), float(scale),
+                              1 if causal else 0, _prec(precision), _ptr(k_rot_out), _stream(q)))
+    return out
