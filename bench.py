@@ -1,0 +1,196 @@
+"""Benchmark of the prefill attention core on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+raw Q, K, V (token-major f32, already resident in HBM) -> per-head QK RMSNorm ->
+NeoX RoPE -> causal GQA attention -> O.  ``--path fused`` runs it as the single
+``qk_prep_attn`` call; ``--path unfused`` as ``qknorm_rope`` followed by
+``gqa_prefill_attn``.  The throughput is causal attention TFLOP/s: 4 * head_dim *
+n_head FLOPs per visible (query, key) pair, masked work not counted.
+
+Prints one JSON line.  ``roofline`` describes the attention kernel (HIP events
+around each of its launches on the stream it runs on, inside the timed region);
+``cpu_baseline`` is the f64 CPU oracle timed on a bounded sample of query rows
+of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal GQA prefill attention TFLOP/s (and % of MFMA peak) at T=512..16384"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "transformer_prefill_attention_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str, precision: str, path: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; otherwise None."""
+    f = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(f):
+        return None
+    try:
+        rec = json.load(open(f))
+    except Exception:
+        return None
+    key = f"{workload}/{kernel}/{precision}/{path}"
+    e = rec.get(key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, target_s: float):
+    """The oracle (as it stands) on evenly spaced query rows of the workload, all heads."""
+    import numpy as np
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    kw = dict(n_head=w.n_head, n_head_kv=w.n_head_kv, head_dim=w.head_dim, rope_dim=w.rope_dim,
+              rope_freq_base=float(np.float32(w.rope_freq_base)),
+              rms_eps=float(np.float32(w.rms_eps)), scale=w.softmax_scale,
+              seq_offsets=w.seq_offsets, n_threads=threads)
+    offs = w.seq_offsets
+
+    def flops_of(rows):
+        tot = 0
+        for r in rows:
+            s = int(np.searchsorted(offs, r, side="right") - 1)
+            tot += 4 * w.head_dim * w.n_head * (int(r) - int(offs[s]) + 1)
+        return tot
+
+    def run(n):
+        rows = np.unique(np.linspace(0, w.T - 1, n).round().astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.qk_prep_attn(x.q, x.k, x.v, x.wq, x.wk, rows=rows, **kw)
+        return rows, time.perf_counter() - t0
+
+    rows, dt = run(32)  # calibration
+    rate = flops_of(rows) / dt
+    per_row = flops_of(rows) / len(rows)
+    n = int(max(32, min(w.T, target_s * rate / per_row)))
+    rows, dt = run(n)
+    fl = flops_of(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} query rows evenly spaced over T={w.T}, all {w.n_head} heads "
+                      f"(QK-norm + RoPE of the whole sequence included); {fl:.3e} causal FLOPs "
+                      f"in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_8192")
+    ap.add_argument("--seq-len", type=int, default=0, help="override: one sequence of this length "
+                                                           "with the 8B-like heads")
+    ap.add_argument("--precision", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--path", default="fused", choices=["fused", "unfused"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the path "
+              "shards by K/V head with no exchange, so N GPUs would each run the one-GPU kernel "
+              "on n_head_kv/N heads.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import transformer_prefill_attention_amd as pfa
+    from transformer_prefill_attention_amd import workloads as wl
+
+    w = wl.sweep_workload(args.seq_len) if args.seq_len else wl.CONFIGS[args.workload]
+    x = wl.make_inputs(w)
+    k_in = wl.with_outlier_keys(x.k, x.outliers)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(x.q).to(dev)
+    k = torch.from_numpy(k_in).to(dev)
+    v = torch.from_numpy(x.v).to(dev)
+    wq = torch.from_numpy(x.wq).to(dev)
+    wk = torch.from_numpy(x.wk).to(dev)
+    out = torch.empty_like(q)
+    qn = torch.empty_like(q)
+    kn = torch.empty_like(k)
+    offs = w.seq_offsets if w.n_seqs > 1 else None
+    kw_rope = dict(head_dim=w.head_dim, rope_dim=w.rope_dim, rope_freq_base=w.rope_freq_base,
+                   rms_eps=w.rms_eps, seq_offsets=offs)
+    stream = torch.cuda.current_stream(dev)
+    ev = []
+
+    def step(record):
+        if args.path == "fused":
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            pfa.qk_prep_attn(q, k, v, wq, wk, scale=w.softmax_scale, precision=args.precision,
+                             out=out, **kw_rope)
+            if record:
+                b.record(stream)
+                ev.append((a, b))
+        else:
+            pfa.qknorm_rope(q, k, wq, wk, q_out=qn, k_out=kn, **kw_rope)
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            pfa.gqa_prefill_attn(qn, kn, v, head_dim=w.head_dim, scale=w.softmax_scale,
+                                 precision=args.precision, seq_offsets=offs, out=out)
+            if record:
+                b.record(stream)
+                ev.append((a, b))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    flops = w.attn_flops()
+    value = flops / (elapsed / args.steps) / 1e12
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[args.precision]
+    kernel = "attn_f32_kernel<128,true>" if args.path == "fused" else "attn_f32_kernel<128,false>"
+    traffic = load_traffic(w.name, kernel, args.precision, args.path)
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.precision, "data": "synthetic (seeded N(0,1) Q/K/V, norm weights 1+N(0,0.1))",
+        "config": {"workload": f"{w.name}: causal GQA prefill, T={w.T}, n_head={w.n_head}, "
+                               f"n_head_kv={w.n_head_kv}, head_dim={w.head_dim}, "
+                               f"rope_dim={w.rope_dim}, seqs={w.n_seqs}",
+                   "T": w.T, "n_head": w.n_head, "n_head_kv": w.n_head_kv,
+                   "head_dim": w.head_dim, "path": args.path, "causal_flops": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": kernel, "kernel_ms": round(kern_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, wl.Inputs(x.q, k_in, x.v, x.wq, x.wk, x.outliers),
+                                           args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+"""The C ABI boundary, without a GPU: the library loads, exports every function
+``include/pfa.h`` declares, and rejects bad arguments with a status code and a
+message before anything is enqueued (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_prefill_attention_amd as pfa
+from transformer_prefill_attention_amd import ops
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "pfa.h")
+
+OK, INVALID, UNSUPPORTED = 0, -1, -2
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.fail("libpfa.so is not built (run __graft_entry__.build())")
+    return pfa.lib()
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared()
+    for n in ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_last_error", "pfa_version"):
+        assert n in names
+    assert set(names) == set(ops.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared():
+        assert hasattr(L, n), f"libpfa.so does not export {n}"
+    assert "gfx950" in pfa.version()
+
+
+def _attn(L, T=16, H=4, Hkv=2, D=64, scale=0.125, causal=1, prec=0, offs=None, n_seqs=0,
+          ptrs=(8, 8, 8, 8 << 20)):
+    q, k, v, o = (ctypes.c_void_p(p) for p in ptrs)
+    return L.gqa_prefill_attn(q, k, v, o, offs, n_seqs, T, H, Hkv, D, scale, causal, prec, None)
+
+
+def _msg(L):
+    return L.pfa_last_error().decode()
+
+
+def test_zero_tokens_is_ok_without_pointers(L):
+    assert _attn(L, T=0, ptrs=(0, 0, 0, 0)) == OK
+    n = ctypes.c_void_p(0)
+    assert L.qknorm_rope(n, n, n, n, n, n, None, 0, 0, 4, 2, 64, 64, 1e6, 1e-6, None) == OK
+    assert L.qk_prep_attn(n, n, n, n, n, n, None, 0, 0, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0, n,
+                          None) == OK
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(H=3, Hkv=2), INVALID, "multiple"),
+    (dict(H=0), INVALID, "positive"),
+    (dict(T=-1), INVALID, ">= 0"),
+    (dict(D=96), UNSUPPORTED, "head_dim"),
+    (dict(D=256), UNSUPPORTED, "head_dim"),
+    (dict(prec=7), INVALID, "precision"),
+    (dict(scale=float("inf")), INVALID, "scale"),
+    (dict(ptrs=(0, 8, 8, 8 << 20)), INVALID, "null"),
+    (dict(ptrs=(8, 8, 8, 16)), INVALID, "overlap"),
+    (dict(T=1 << 20, H=64, Hkv=8, D=128), UNSUPPORTED, "2^31"),
+])
+def test_attention_rejects(L, kw, status, needle):
+    assert _attn(L, **kw) == status
+    assert needle in _msg(L)
+
+
+def test_bad_seq_offsets(L):
+    for offs, n, needle in (([0, 5, 3, 16], 3, "non-decreasing"), ([1, 16], 1, "[0]"),
+                            ([0, 8, 15], 2, "T ="), ([0, 16], 0, "n_seqs")):
+        arr = (ctypes.c_int32 * len(offs))(*offs)
+        assert _attn(L, offs=ctypes.cast(arr, ctypes.c_void_p), n_seqs=n) == INVALID
+        assert needle in _msg(L)
+    arr = (ctypes.c_int32 * 130)(*([0] * 129 + [16]))
+    assert _attn(L, offs=ctypes.cast(arr, ctypes.c_void_p), n_seqs=129) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("rope_dim,base,eps,needle", [
+    (63, 1e6, 1e-6, "rope_dim"), (0, 1e6, 1e-6, "rope_dim"), (130, 1e6, 1e-6, "rope_dim"),
+    (64, 0.0, 1e-6, "rope_freq_base"), (64, float("nan"), 1e-6, "rope_freq_base"),
+    (64, 1e6, -1.0, "rms_eps"),
+])
+def test_rope_argument_checks(L, rope_dim, base, eps, needle):
+    p = ctypes.c_void_p
+    ptrs = [p(8), p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p(5 << 20)]
+    assert L.qknorm_rope(*ptrs, None, 0, 16, 4, 2, 64, rope_dim, base, eps, None) == INVALID
+    assert needle in _msg(L)
+    assert L.qk_prep_attn(p(8), p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p(5 << 20), None,
+                          0, 16, 4, 2, 64, rope_dim, base, eps, 0.125, 1, 0, p(0),
+                          None) == INVALID
+
+
+def test_qknorm_rope_aliasing_rules(L):
+    p = ctypes.c_void_p
+    q, k = 1 << 20, 2 << 20  # 16 tokens x 4 heads x 64 dims x 4 B = 16 KiB
+    w = 3 << 20
+    # partial overlap of q_out with q_in is an error; exact in-place is accepted by the
+    # checks (not launched here: only the error path runs on the CPU)
+    assert L.qknorm_rope(p(q), p(k), p(q + 64), p(k), p(w), p(w), None, 0, 16, 4, 2, 64, 64,
+                         1e6, 1e-6, None) == INVALID
+    assert "overlap" in _msg(L)
+    assert L.qknorm_rope(p(q), p(k), p(k), p(q), p(w), p(w), None, 0, 16, 4, 2, 64, 64,
+                         1e6, 1e-6, None) == INVALID
+
+
+def test_k_rot_out_must_not_alias(L):
+    p = ctypes.c_void_p
+    assert L.qk_prep_attn(p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p(5 << 20),
+                          p(5 << 20), None, 0, 16, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0,
+                          p(2 << 20), None) == INVALID
+    assert "k_rot_out" in _msg(L)
+
+
+def test_python_binding_raises_without_gpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        pfa.gqa_prefill_attn(torch.zeros(4, 128), torch.zeros(4, 64), torch.zeros(4, 64),
+                             head_dim=64)
+    with pytest.raises(TypeError):
+        pfa.gqa_prefill_attn(torch.zeros(4, 128, dtype=torch.float64), torch.zeros(4, 64),
+                             torch.zeros(4, 64), head_dim=64)

@@ -1,0 +1,461 @@
+// attn_f32.hip -- flash-style causal grouped-query attention on f32 MFMA.
+//
+// Passages: memra-engine 0.130.0 src/forward.rs, `Model::forward`, SDPA block
+// (causal GQA, T_q = T_kv = T, scale 1/sqrt(head_dim)); memra-engine 0.101.0
+// src/spec.rs, `full_attn_verify` per-row fallback (row r attends keys up to
+// and including itself).  The reference prefill calls an untiled ("naive")
+// kernel; this one is tiled for gfx950:
+//
+//  * A workgroup is four wavefronts sharing one K/V head: `hpw` query heads of
+//    the group times `rb` blocks of 32 query rows (hpw * rb = 4).  Every K/V
+//    tile is read from HBM/L2 once per workgroup and reused from LDS by all of
+//    its wavefronts -- the GQA reuse.
+//  * Each wavefront computes S^T = K Q^T for 32 keys x its 32 queries with
+//    v_mfma_f32_32x32x2f32 (64 steps over head_dim 128).  Computing the
+//    transpose leaves every lane holding 16 scores of ONE query, which is exactly
+//    the B-operand layout the second product O^T += V^T P^T needs, so the
+//    probabilities never leave registers; the contraction index of each step is
+//    free to permute, and the V reads follow the score registers' key order.
+//  * Online softmax in base 2: Q is pre-multiplied by scale * log2(e); the row
+//    max is a 16-register max plus one cross-half exchange; the row sum stays a
+//    per-lane partial until the end.
+//  * Causal tile skipping: a workgroup visits only key tiles up to its last
+//    query row; a wavefront skips the tiles past its own diagonal, and only the
+//    diagonal/last tile is masked.
+//  * K/V tiles are double-buffered in LDS (global loads for tile t+1 are in
+//    flight while tile t is multiplied); the output is transposed through LDS
+//    so the stores are coalesced rows.
+//  * Work items are scheduled longest first across all packed sequences, and
+//    the K/V head is the fastest-varying block index, so consecutive
+//    workgroups (which the dispatcher spreads over the 8 XCDs) walk the same
+//    key tiles of one head together while each XCD's L2 keeps them.
+//
+// PREP = true is the fused entry: raw Q rows are RMS-normalised and rotated as
+// the Q tile is staged, and every K tile is normalised and rotated in LDS right
+// after it lands (optionally copied out as the cache-ready K).
+#include "pfa_device.h"
+#include "pfa_internal.h"
+
+namespace pfa {
+
+namespace {
+
+constexpr int kBN = 32;       // keys per tile
+constexpr int kWaves = 4;     // wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
+
+__device__ __forceinline__ floatx16 mfma32x32x2(float a, float b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Normalise (and rotate) one head row of length D held in LDS, in place, by one
+// wavefront: lane L owns dims L and L + 64 (one dim when D == 64).  `pos` is the
+// rotary position; `turns` the lane's per-position angle in turns for each of
+// its dims (0 for dims that are not rotated); `partner` the LDS index offset of
+// the other half of the pair (0 if none).
+template <int D>
+__device__ __forceinline__ void prep_row_lds(float* row, const float* w, int pos, int n,
+                                             const double* turns, float eps, int lane) {
+    constexpr int E = D / 64;
+    const int half = n >> 1;
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = row[lane + 64 * e];
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss += x[e] * x[e];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = x[e] * r * w[e];
+    // Every lane has finished reading the raw row (the reduction above depends on
+    // all of it), so the normalised values can be published in place and the
+    // partners read back from LDS.
+#pragma unroll
+    for (int e = 0; e < E; ++e) row[lane + 64 * e] = y[e];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): our writes are visible
+    __builtin_amdgcn_wave_barrier();
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int c = lane + 64 * e;
+        if (c < n) {
+            const bool first = c < half;
+            const float pv = row[first ? c + half : c - half];
+            float cs, sn;
+            rope_cos_sin(pos, turns[e], cs, sn);
+            o[e] = first ? y[e] * cs - pv * sn : y[e] * cs + pv * sn;
+        } else {
+            o[e] = y[e];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int e = 0; e < E; ++e) row[lane + 64 * e] = o[e];
+}
+
+template <int D, bool PREP>
+__global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ out, AttnSched sched, AttnGeom geom, PrepParams prep) {
+    constexpr int KS = D + 4;          // K tile row stride in LDS (floats): b128 reads conflict-free
+    constexpr int VS = D + 8;          // V tile row stride
+    constexpr int NQ = D / 2;          // Q operand registers per lane = MFMA steps of K Q^T
+    constexpr int NCB = D / 32;        // 32-wide column blocks of O^T
+    constexpr int BUF = kBN * KS + kBN * VS;
+    constexpr int F4_PER_ROW = D / 4;
+    constexpr int LD_PER_THREAD = kBN * F4_PER_ROW / kThreads;  // float4 of K (and of V) per thread
+    constexpr int QS = D + 4;          // staging stride of Q / O rows
+    static_assert(kWaves * 32 * QS <= 2 * BUF, "Q/O staging must fit in the K/V buffers");
+    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, hl = lane >> 5, ln = lane & 31;
+
+    // ---- work item (uniform across the workgroup)
+    int bid = blockIdx.x;
+    const int kv = bid % geom.Hkv;
+    bid /= geom.Hkv;
+    const int chunk = bid % geom.chunks;
+    const int item = bid / geom.chunks;
+    int seg = 0;
+    while (item >= sched.seg_start[seg + 1]) ++seg;
+    const int local = item - sched.seg_start[seg];
+    const int per = seg + 1;
+    const int sid = sched.order[local % per];
+    const int sb = sched.seg_top[seg] - 1 - local / per;
+    const int s0 = sched.off[sid], s1 = sched.off[sid + 1];
+    const int q0 = s0 + sb * sched.rows_per_item;
+    const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
+    const int n_tiles =
+        geom.causal ? (min(q0 + sched.rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
+
+    // ---- wavefront role
+    const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;
+    const int h = kv * geom.g + chunk * geom.hpw + hloc;
+    const int wq0 = q0 + rblk * 32;
+    const bool active = wq0 < s1;
+    const int diag_tile = (wq0 - s0) / kBN;
+    const int wave_tiles = geom.causal ? min(diag_tile + 1, nt_seq) : nt_seq;
+    const int qi = wq0 + ln;
+
+    // Rotary frequencies (turns per position) of this lane's dims, for PREP.
+    double turns[D / 64];
+    float wqv[D / 64], wkv[D / 64];
+    if constexpr (PREP) {
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) {
+            const int c = lane + 64 * e;
+            const int half = prep.rope_dim >> 1;
+            turns[e] = c < prep.rope_dim ? rope_turns_per_pos(c < half ? c : c - half,
+                                                              prep.rope_dim, prep.base)
+                                         : 0.0;
+            wqv[e] = prep.wq[c];
+            wkv[e] = prep.wk[c];
+        }
+    }
+
+    // ---- Q tile -> MFMA B operand: lane (hl, ln) holds Q[qi][hl*NQ .. hl*NQ+NQ),
+    // pre-multiplied by scale * log2(e).
+    float qr[NQ];
+    if constexpr (!PREP) {
+        const bool ok = active && qi < s1;
+        const float* src = q + ((int64_t)(ok ? qi : s0) * geom.H + h) * D + hl * NQ;
+#pragma unroll
+        for (int c4 = 0; c4 < NQ / 4; ++c4) {
+            const floatx4 x = ok ? *reinterpret_cast<const floatx4*>(src + 4 * c4)
+                                 : floatx4{0.f, 0.f, 0.f, 0.f};
+            qr[4 * c4 + 0] = x[0] * geom.qscale;
+            qr[4 * c4 + 1] = x[1] * geom.qscale;
+            qr[4 * c4 + 2] = x[2] * geom.qscale;
+            qr[4 * c4 + 3] = x[3] * geom.qscale;
+        }
+    } else {
+        // Fused entry: stage the raw rows in LDS (coalesced), normalise and rotate
+        // them there one row per wavefront step, then pick up the operand layout.
+        float* qs = smem + wave * 32 * QS;
+        if (active) {
+#pragma unroll 8
+            for (int r = 0; r < 32; ++r) {
+                const int row = wq0 + r;
+                float* dst = qs + r * QS;
+                const float* src = q + ((int64_t)(row < s1 ? row : s0) * geom.H + h) * D;
+#pragma unroll
+                for (int e = 0; e < D / 64; ++e)
+                    dst[lane + 64 * e] = row < s1 ? src[lane + 64 * e] : 0.0f;
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            for (int r = 0; r < 32 && wq0 + r < s1; ++r)
+                prep_row_lds<D>(qs + r * QS, wqv, wq0 + r - s0, prep.rope_dim, turns, prep.eps,
+                                lane);
+        }
+        __syncthreads();
+        const float* src = qs + ln * QS + hl * NQ;
+#pragma unroll
+        for (int c4 = 0; c4 < NQ / 4; ++c4) {
+            const floatx4 x = *reinterpret_cast<const floatx4*>(src + 4 * c4);
+            qr[4 * c4 + 0] = x[0] * geom.qscale;
+            qr[4 * c4 + 1] = x[1] * geom.qscale;
+            qr[4 * c4 + 2] = x[2] * geom.qscale;
+            qr[4 * c4 + 3] = x[3] * geom.qscale;
+        }
+        __syncthreads();
+    }
+
+    // ---- K/V tile staging: global -> registers -> LDS, K and V separately so
+    // that only one of them is held in registers at a time.
+    floatx4 kvreg[LD_PER_THREAD];
+    // Thread tid moves float4 number tid + 256 i of the 32 x D tile: row f / (D/4),
+    // column 4 (f % (D/4)).  Its offset inside a tile never changes, so only the
+    // (wavefront-uniform) tile base pointer moves from tile to tile.
+    unsigned kv_off[LD_PER_THREAD];
+    int kv_row[LD_PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < LD_PER_THREAD; ++i) {
+        const int f = tid + kThreads * i;
+        kv_row[i] = f / F4_PER_ROW;
+        kv_off[i] = (unsigned)(kv_row[i] * geom.Hkv * D + 4 * (f % F4_PER_ROW));
+    }
+    auto load_rows = [&](const float* base, int t) {
+        const int k0 = s0 + t * kBN;
+        const float* tile = base + ((int64_t)k0 * geom.Hkv + kv) * D;
+        const int rows_left = s1 - k0;
+#pragma unroll
+        for (int i = 0; i < LD_PER_THREAD; ++i)
+            kvreg[i] = kv_row[i] < rows_left
+                           ? *reinterpret_cast<const floatx4*>(tile + kv_off[i])
+                           : floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto store_rows = [&](float* dst, int stride) {
+#pragma unroll
+        for (int i = 0; i < LD_PER_THREAD; ++i) {
+            const int f = tid + kThreads * i;
+            const int row = f / F4_PER_ROW, c4 = f % F4_PER_ROW;
+            *reinterpret_cast<floatx4*>(dst + row * stride + 4 * c4) = kvreg[i];
+        }
+    };
+    // Fused entry: normalise + rotate the K rows of a freshly stored tile (wave w
+    // takes rows w, w+4, ...), and copy them out once if asked.
+    auto prep_tile = [&](int buf, int t) {
+        if constexpr (PREP) {
+            float* ks = smem + buf * BUF;
+            const int k0 = s0 + t * kBN;
+            // exactly one workgroup writes each key row: the one whose query
+            // super-block covers the same rows (first head chunk)
+            const bool writer = prep.k_rot_out && chunk == 0 &&
+                                (t * kBN) / sched.rows_per_item == sb;
+            for (int r = wave; r < kBN; r += kWaves) {
+                const int key = k0 + r;
+                if (key >= s1) continue;
+                float* row = ks + r * KS;
+                prep_row_lds<D>(row, wkv, key - s0, prep.rope_dim, turns, prep.eps, lane);
+                if (writer) {
+                    __builtin_amdgcn_s_waitcnt(0xc07f);
+                    __builtin_amdgcn_wave_barrier();
+                    float* dst = prep.k_rot_out + ((int64_t)key * geom.Hkv + kv) * D;
+#pragma unroll
+                    for (int e = 0; e < D / 64; ++e) dst[lane + 64 * e] = row[lane + 64 * e];
+                }
+            }
+        }
+    };
+
+    // ---- accumulators
+    floatx16 oacc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.0f;
+    // The softmax denominator is carried in f64: in a row dominated by one key
+    // each lane's per-tile sum of the other weights can fall below half an f32
+    // ulp of the running sum and would be dropped every time, a systematic
+    // underestimate (~1e-5 relative at T = 16k with x8 outlier keys).
+    float m_run = -INFINITY;
+    double l_run = 0.0;
+
+    load_rows(k, 0);
+    store_rows(smem, KS);
+    load_rows(v, 0);
+    store_rows(smem + kBN * KS, VS);
+    __syncthreads();
+    if constexpr (PREP) {
+        prep_tile(0, 0);
+        __syncthreads();
+    }
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const int cur = t & 1;
+        const bool more = t + 1 < n_tiles;
+        float* kn = smem + (cur ^ 1) * BUF;
+        if (more) load_rows(k, t + 1);
+        if (active && t < wave_tiles) {
+            const float* ks = smem + cur * BUF;
+            const float* vs = ks + kBN * KS;
+            // S^T[key][query] = sum_d K[key][d] Q[query][d]; step s contracts
+            // d = hl * NQ + s (lanes 0-31 and 32-63 supply the two k-slices).
+            // Two partial sums (even / odd 4-step chunks): the MFMA rounds after
+            // every product, so halving each chain's length and magnitude halves
+            // the rounding error of the scores.
+            floatx16 sacc, sacc1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] = 0.0f;
+                sacc1[r] = 0.0f;
+            }
+            const float* kp = ks + ln * KS + hl * NQ;
+            // Operands are read one 8-step chunk ahead of the MFMAs that use them;
+            // the scheduling fence stops the compiler from hoisting every read to
+            // the top (which would hold 64 extra registers).
+            floatx4 ka = *reinterpret_cast<const floatx4*>(kp);
+            floatx4 kb = *reinterpret_cast<const floatx4*>(kp + 4);
+#pragma unroll
+            for (int c4 = 0; c4 < NQ / 4; c4 += 2) {
+                floatx4 na = ka, nb = kb;
+                if (c4 + 2 < NQ / 4) {
+                    na = *reinterpret_cast<const floatx4*>(kp + 4 * c4 + 8);
+                    nb = *reinterpret_cast<const floatx4*>(kp + 4 * c4 + 12);
+                }
+                sacc = mfma32x32x2(ka[0], qr[4 * c4 + 0], sacc);
+                sacc1 = mfma32x32x2(kb[0], qr[4 * c4 + 4], sacc1);
+                sacc = mfma32x32x2(ka[1], qr[4 * c4 + 1], sacc);
+                sacc1 = mfma32x32x2(kb[1], qr[4 * c4 + 5], sacc1);
+                sacc = mfma32x32x2(ka[2], qr[4 * c4 + 2], sacc);
+                sacc1 = mfma32x32x2(kb[2], qr[4 * c4 + 6], sacc1);
+                sacc = mfma32x32x2(ka[3], qr[4 * c4 + 3], sacc);
+                sacc1 = mfma32x32x2(kb[3], qr[4 * c4 + 7], sacc1);
+                ka = na;
+                kb = nb;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] += sacc1[r];
+            // Register r of lane (hl, ln) holds key k0 + 8(r/4) + 4hl + r%4 for query qi.
+            const int k0 = s0 + t * kBN;
+            if (t == diag_tile || t == nt_seq - 1) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if ((geom.causal && key > qi) || key >= s1) sacc[r] = -INFINITY;
+                }
+            }
+            float mt = sacc[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            float psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - m_new);
+                psum += sacc[r];
+            }
+            l_run = l_run * (double)alpha + (double)psum;
+            if (more) {
+                store_rows(kn, KS);
+                load_rows(v, t + 1);
+            }
+            // O^T[d][query] = alpha * O^T + sum_key V[key][d] P[query][key].  Each
+            // tile's products go into a fresh accumulator that is folded into O
+            // with one FMA per element: O is rounded once per tile instead of once
+            // per key, which keeps long rows dominated by one key accurate.  Step s
+            // contracts key 8(s/4) + 4hl + s%4, i.e. score register s of the lane.
+            float vop[16], vnext[16];
+            auto read_v = [&](int cb, float* dst) {
+#pragma unroll
+                for (int s = 0; s < 16; ++s)
+                    dst[s] = vs[(8 * (s >> 2) + 4 * hl + (s & 3)) * VS + ln + 32 * cb];
+            };
+            read_v(0, vop);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                if (cb + 1 < NCB) read_v(cb + 1, vnext);
+                floatx16 pv;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pv[r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < 16; ++s) pv = mfma32x32x2(vop[s], sacc[s], pv);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[cb][r] = fmaf(oacc[cb][r], alpha, pv[r]);
+#pragma unroll
+                for (int s = 0; s < 16; ++s) vop[s] = vnext[s];
+                // keep the column-block chains apart (bounded live registers)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if (more) {
+            // this wavefront has no work on tile t but still stages tile t+1
+            store_rows(kn, KS);
+            load_rows(v, t + 1);
+        }
+        if (more) store_rows(kn + kBN * KS, VS);
+        __syncthreads();
+        if constexpr (PREP) {
+            if (t + 1 < n_tiles) {
+                prep_tile(cur ^ 1, t + 1);
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- epilogue: 1/l, transpose through LDS, coalesced row stores
+    const double l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = (float)(1.0 / l_tot);
+    float* os = smem + wave * 32 * QS;
+    if (active) {
+        // lane (hl, ln), register r of block cb holds O[qi][cb*32 + 8(r/4) + 4hl + r%4]
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                floatx4 x;
+                x[0] = oacc[cb][4 * r4 + 0] * inv;
+                x[1] = oacc[cb][4 * r4 + 1] * inv;
+                x[2] = oacc[cb][4 * r4 + 2] * inv;
+                x[3] = oacc[cb][4 * r4 + 3] * inv;
+                *reinterpret_cast<floatx4*>(os + ln * QS + cb * 32 + 8 * r4 + 4 * hl) = x;
+            }
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < 32 * F4_PER_ROW / 64; ++i) {
+            const int f = lane + 64 * i;
+            const int r = f / F4_PER_ROW, c4 = f % F4_PER_ROW;
+            const int row = wq0 + r;
+            if (row < s1)
+                *reinterpret_cast<floatx4*>(out + ((int64_t)row * geom.H + h) * D + 4 * c4) =
+                    *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out,
+                           const AttnSched& sched, const AttnGeom& geom, int D,
+                           const PrepParams* prep, int n_items, hipStream_t stream) {
+    const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(kThreads);
+    const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
+    if (D == 128) {
+        if (prep)
+            hipLaunchKernelGGL((attn_f32_kernel<128, true>), grid, block, 0, stream, q, k, v, out,
+                               sched, geom, p);
+        else
+            hipLaunchKernelGGL((attn_f32_kernel<128, false>), grid, block, 0, stream, q, k, v,
+                               out, sched, geom, p);
+    } else {
+        if (prep)
+            hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, block, 0, stream, q, k, v, out,
+                               sched, geom, p);
+        else
+            hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, block, 0, stream, q, k, v, out,
+                               sched, geom, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pfa

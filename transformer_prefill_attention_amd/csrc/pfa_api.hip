@@ -1,0 +1,237 @@
+// pfa_api.hip -- the extern "C" entry points of libpfa (declared in
+// include/pfa.h): argument validation, the packed-sequence tables and the
+// attention work schedule are built on the host, then kernels are enqueued on
+// the caller's stream.  Nothing here allocates device memory or synchronises.
+//
+// Error convention (needle-core v3/model.rs keeps failures recoverable for its
+// binding callers: an empty prompt is an empty result and bad shapes come back
+// as errors rather than aborts): every problem is reported as a status code
+// with a thread-local message, and T == 0 succeeds without a launch.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "pfa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+// Shared shape checks.  Returns PFA_OK or a failure (message set).
+int check_geometry(int T, int n_head, int n_head_kv, int head_dim) {
+    if (T < 0) return fail(PFA_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+    if (n_head <= 0 || n_head_kv <= 0)
+        return fail(PFA_ERR_INVALID_ARG, "n_head (%d) and n_head_kv (%d) must be positive", n_head,
+                    n_head_kv);
+    if (n_head % n_head_kv)
+        return fail(PFA_ERR_INVALID_ARG, "n_head (%d) must be a multiple of n_head_kv (%d)",
+                    n_head, n_head_kv);
+    if (head_dim <= 0) return fail(PFA_ERR_INVALID_ARG, "head_dim must be positive");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PFA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+    const long long elems = (long long)T * std::max(n_head, n_head_kv) * head_dim;
+    if (elems >= (1LL << 31))
+        return fail(PFA_ERR_UNSUPPORTED, "T * heads * head_dim = %lld exceeds 2^31 - 1", elems);
+    return PFA_OK;
+}
+
+int check_rope(int head_dim, int rope_dim, float base, float eps) {
+    if (rope_dim < 2 || rope_dim > head_dim || (rope_dim & 1))
+        return fail(PFA_ERR_INVALID_ARG, "rope_dim must be even with 2 <= rope_dim <= head_dim "
+                                         "(got %d, head_dim %d)", rope_dim, head_dim);
+    if (!(base > 0.0f) || !std::isfinite(base))
+        return fail(PFA_ERR_INVALID_ARG, "rope_freq_base must be finite and > 0");
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(PFA_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+    return PFA_OK;
+}
+
+// Copies seq_offsets (host) into a kernel-argument table.
+int build_seqs(const int32_t* seq_offsets, int n_seqs, int T, pfa::SeqTable& st) {
+    if (!seq_offsets) {
+        st.n_seqs = 1;
+        st.off[0] = 0;
+        st.off[1] = T;
+        return PFA_OK;
+    }
+    if (n_seqs < 1) return fail(PFA_ERR_INVALID_ARG, "n_seqs must be >= 1 (got %d)", n_seqs);
+    if (n_seqs > PFA_MAX_SEQS)
+        return fail(PFA_ERR_UNSUPPORTED, "at most %d packed sequences (got %d)", PFA_MAX_SEQS,
+                    n_seqs);
+    if (seq_offsets[0] != 0) return fail(PFA_ERR_INVALID_ARG, "seq_offsets[0] must be 0");
+    for (int s = 0; s < n_seqs; ++s)
+        if (seq_offsets[s + 1] < seq_offsets[s])
+            return fail(PFA_ERR_INVALID_ARG, "seq_offsets must be non-decreasing (index %d)", s);
+    if (seq_offsets[n_seqs] != T)
+        return fail(PFA_ERR_INVALID_ARG, "seq_offsets[n_seqs] = %d but T = %d",
+                    seq_offsets[n_seqs], T);
+    st.n_seqs = n_seqs;
+    for (int s = 0; s <= n_seqs; ++s) st.off[s] = seq_offsets[s];
+    return PFA_OK;
+}
+
+// Work split of a workgroup (four wavefronts) for group size g: as many heads of
+// the group as divide both g and 4, the rest of the four wavefronts take more
+// 32-row query blocks.
+void choose_geometry(int H, int Hkv, float scale, int causal, pfa::AttnGeom& geom) {
+    const int g = H / Hkv;
+    int hpw = 1;
+    while (hpw < 4 && g % (hpw * 2) == 0) hpw *= 2;
+    geom.H = H;
+    geom.Hkv = Hkv;
+    geom.g = g;
+    geom.hpw = hpw;
+    geom.rb = 4 / hpw;
+    geom.chunks = g / hpw;
+    geom.qscale = scale * 1.4426950408889634f;
+    geom.causal = causal ? 1 : 0;
+}
+
+// Longest-first schedule of (sequence, super-block) items.
+int build_sched(const pfa::SeqTable& st, int rows_per_item, pfa::AttnSched& sc) {
+    sc.n_seqs = st.n_seqs;
+    sc.rows_per_item = rows_per_item;
+    for (int s = 0; s <= st.n_seqs; ++s) sc.off[s] = st.off[s];
+    int nsb[PFA_MAX_SEQS];
+    int idx[PFA_MAX_SEQS];
+    for (int s = 0; s < st.n_seqs; ++s) {
+        nsb[s] = (st.off[s + 1] - st.off[s] + rows_per_item - 1) / rows_per_item;
+        idx[s] = s;
+    }
+    std::stable_sort(idx, idx + st.n_seqs, [&](int a, int b) { return nsb[a] > nsb[b]; });
+    int n_nonempty = 0;
+    for (int s = 0; s < st.n_seqs; ++s) {
+        sc.order[s] = (int16_t)idx[s];
+        if (nsb[idx[s]] > 0) ++n_nonempty;
+    }
+    int items = 0;
+    sc.n_segs = n_nonempty;
+    for (int kk = 0; kk < n_nonempty; ++kk) {
+        const int top = nsb[idx[kk]];
+        const int next = kk + 1 < n_nonempty ? nsb[idx[kk + 1]] : 0;
+        sc.seg_start[kk] = items;
+        sc.seg_top[kk] = top;
+        items += (kk + 1) * (top - next);
+    }
+    sc.seg_start[n_nonempty] = items;
+    return items;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(PFA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+    return PFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pfa_last_error(void) { return g_err; }
+
+const char* pfa_version(void) { return "pfa 0.1 (gfx950; f32 MFMA attention)"; }
+
+int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
+                const float* q_norm_w, const float* k_norm_w, const int32_t* seq_offsets,
+                int n_seqs, int T, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                float rope_freq_base, float rms_eps, void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T, n_head, n_head_kv, head_dim);
+    if (rc) return rc;
+    if ((rc = check_rope(head_dim, rope_dim, rope_freq_base, rms_eps))) return rc;
+    if (T == 0) return PFA_OK;
+    if (!q_in || !k_in || !q_out || !k_out || !q_norm_w || !k_norm_w)
+        return fail(PFA_ERR_INVALID_ARG, "null tensor pointer");
+    const size_t qb = (size_t)T * n_head * head_dim * 4, kb = (size_t)T * n_head_kv * head_dim * 4;
+    if (q_out != q_in && overlaps(q_out, qb, q_in, qb))
+        return fail(PFA_ERR_INVALID_ARG, "q_out partially overlaps q_in");
+    if (k_out != k_in && overlaps(k_out, kb, k_in, kb))
+        return fail(PFA_ERR_INVALID_ARG, "k_out partially overlaps k_in");
+    if (overlaps(q_out, qb, k_in, kb) || overlaps(q_out, qb, k_out, kb) ||
+        overlaps(k_out, kb, q_in, qb))
+        return fail(PFA_ERR_INVALID_ARG, "Q and K buffers overlap");
+    pfa::SeqTable st;
+    if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
+    return hip_status(pfa::launch_qknorm_rope(q_in, k_in, q_out, k_out, q_norm_w, k_norm_w, st, T,
+                                              n_head, n_head_kv, head_dim, rope_dim,
+                                              rope_freq_base, rms_eps, (hipStream_t)stream),
+                      "qknorm_rope launch");
+}
+
+static int attn_common(const float* q, const float* k, const float* v, float* out,
+                       const int32_t* seq_offsets, int n_seqs, int T, int n_head, int n_head_kv,
+                       int head_dim, float scale, int causal, int precision,
+                       const pfa::PrepParams* prep, void* stream) {
+    if (!std::isfinite(scale)) return fail(PFA_ERR_INVALID_ARG, "scale must be finite");
+    if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16)
+        return fail(PFA_ERR_INVALID_ARG, "precision must be PFA_PREC_F32 or PFA_PREC_BF16 (got %d)",
+                    precision);
+    if (T == 0) return PFA_OK;
+    if (!q || !k || !v || !out) return fail(PFA_ERR_INVALID_ARG, "null tensor pointer");
+    const size_t qb = (size_t)T * n_head * head_dim * 4, kb = (size_t)T * n_head_kv * head_dim * 4;
+    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kb) || overlaps(out, qb, v, kb))
+        return fail(PFA_ERR_INVALID_ARG, "out must not overlap q, k or v");
+    if (prep && prep->k_rot_out &&
+        (overlaps(prep->k_rot_out, kb, q, qb) || overlaps(prep->k_rot_out, kb, k, kb) ||
+         overlaps(prep->k_rot_out, kb, v, kb) || overlaps(prep->k_rot_out, kb, out, qb)))
+        return fail(PFA_ERR_INVALID_ARG, "k_rot_out must not overlap the inputs or out");
+    pfa::SeqTable st;
+    int rc = build_seqs(seq_offsets, n_seqs, T, st);
+    if (rc) return rc;
+    pfa::AttnGeom geom;
+    choose_geometry(n_head, n_head_kv, scale, causal, geom);
+    pfa::AttnSched sched;
+    const int items = build_sched(st, 32 * geom.rb, sched);
+    if (items == 0) return PFA_OK;
+    if ((long long)items * geom.chunks * geom.Hkv >= (1LL << 31))
+        return fail(PFA_ERR_UNSUPPORTED, "grid too large");
+    if (precision == PFA_PREC_BF16)
+        return fail(PFA_ERR_UNSUPPORTED, "bf16 attention is not built into this library yet");
+    return hip_status(pfa::launch_attn_f32(q, k, v, out, sched, geom, head_dim, prep, items,
+                                           (hipStream_t)stream),
+                      prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
+}
+
+int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
+                     const int32_t* seq_offsets, int n_seqs, int T, int n_head, int n_head_kv,
+                     int head_dim, float scale, int causal, int precision, void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T, n_head, n_head_kv, head_dim);
+    if (rc) return rc;
+    return attn_common(q, k, v, out, seq_offsets, n_seqs, T, n_head, n_head_kv, head_dim, scale,
+                       causal, precision, nullptr, stream);
+}
+
+int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
+                 const float* q_norm_w, const float* k_norm_w, const int32_t* seq_offsets,
+                 int n_seqs, int T, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                 float rope_freq_base, float rms_eps, float scale, int causal, int precision,
+                 float* k_rot_out, void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T, n_head, n_head_kv, head_dim);
+    if (rc) return rc;
+    if ((rc = check_rope(head_dim, rope_dim, rope_freq_base, rms_eps))) return rc;
+    if (T > 0 && (!q_norm_w || !k_norm_w)) return fail(PFA_ERR_INVALID_ARG, "null norm weights");
+    pfa::PrepParams prep{q_norm_w, k_norm_w, k_rot_out, rope_dim, rms_eps,
+                         (double)rope_freq_base};
+    return attn_common(q, k, v, out, seq_offsets, n_seqs, T, n_head, n_head_kv, head_dim, scale,
+                       causal, precision, &prep, stream);
+}
+
+}  // extern "C"

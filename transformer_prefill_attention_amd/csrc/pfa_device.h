@@ -1,0 +1,56 @@
+// pfa_device.h -- small device helpers shared by the libpfa kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pfa {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kInvTwoPi = 0.15915494309189533577;  // 1 / (2 pi)
+
+// Sum over the 64 lanes of a wavefront (every lane receives the total).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Turns per position of rotary pair j: base^(-2j/n) / (2 pi), in f64.
+__device__ __forceinline__ double rope_turns_per_pos(int j, int n, double base) {
+    return pow(base, -2.0 * (double)j / (double)n) * kInvTwoPi;
+}
+
+// cos and sin of the rotary angle pos * base^(-2j/n).  The angle is formed in
+// f64 as a number of turns and reduced to [-1/2, 1/2] turn there, so only the
+// final sincos runs in f32 on an argument of at most pi: the result keeps f32
+// accuracy at any position (an f32 angle would lose ~1e-3 rad near 16k).
+__device__ __forceinline__ void rope_cos_sin(int pos, double turns_per_pos, float& c, float& s) {
+    double r = (double)pos * turns_per_pos;
+    r -= rint(r);
+    sincospif((float)(2.0 * r), &s, &c);
+}
+
+// Index of the packed sequence holding token t: the largest s < n_seqs with
+// off[s] <= t (empty sequences resolve to the next non-empty one).
+__device__ __forceinline__ int find_seq(const int* off, int n_seqs, int t) {
+    int lo = 0, hi = n_seqs;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (off[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace pfa

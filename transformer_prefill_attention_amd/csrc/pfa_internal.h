@@ -1,0 +1,71 @@
+// pfa_internal.h -- types shared by the host entry points and the kernels of
+// libpfa.  Not part of the public ABI (that is include/pfa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pfa.h"
+
+namespace pfa {
+
+// Packed-sequence boundaries, passed to kernels by value (kernel arguments),
+// so no device buffer and no host-to-device copy is needed.
+struct SeqTable {
+    int n_seqs;
+    int off[PFA_MAX_SEQS + 1];  // cumulative token offsets, off[n_seqs] = T
+};
+
+// Work schedule of the attention kernels, also passed by value.
+//
+// A work item is one (sequence, query super-block) pair; a super-block is
+// rows_per_item consecutive query rows of one sequence.  Items are ordered
+// longest first: the causal cost of super-block b is about b + 1 key tiles, so
+// listing super-blocks from the top index down, across all sequences at once,
+// is longest-processing-time-first order.  With the sequences sorted by their
+// super-block count (order[]), the k+1 longest sequences are exactly the ones
+// that have a super-block at levels seg_top[k+1] < level <= seg_top[k]; segment
+// k holds those levels, k+1 items per level.
+struct AttnSched {
+    int n_seqs;
+    int n_segs;                      // segments in use
+    int rows_per_item;               // query rows per super-block (32 * row blocks)
+    int off[PFA_MAX_SEQS + 1];       // as SeqTable::off
+    int seg_start[PFA_MAX_SEQS + 1]; // first item of each segment; [n_segs] = item count
+    int seg_top[PFA_MAX_SEQS];       // super-block count of the (k+1)-th longest sequence
+    int16_t order[PFA_MAX_SEQS];     // sequence ids, most super-blocks first
+};
+
+// Geometry common to the attention launches.
+struct AttnGeom {
+    int H, Hkv, g;          // query heads, K/V heads, group size
+    int hpw;                // query heads per workgroup (one wave each per row block)
+    int rb;                 // 32-row blocks per workgroup
+    int chunks;             // workgroups per K/V head per item (g / hpw)
+    float qscale;           // softmax scale * log2(e), folded into Q
+    int causal;
+};
+
+// Rotary + norm parameters for the fused entry.
+struct PrepParams {
+    const float* wq;
+    const float* wk;
+    float* k_rot_out;       // may be null
+    int rope_dim;
+    float eps;
+    double base;            // rotary frequency base
+};
+
+// Launchers (defined next to their kernels).  They only enqueue.
+hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
+                              const float* wq, const float* wk, const SeqTable& seqs, int T,
+                              int H, int Hkv, int D, int rope_dim, float base, float eps,
+                              hipStream_t stream);
+
+// prep == nullptr: plain attention on already-normalised Q/K; otherwise the
+// fused entry (Q and K normalised and rotated inside the kernel).
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out,
+                           const AttnSched& sched, const AttnGeom& geom, int D,
+                           const PrepParams* prep, int n_items, hipStream_t stream);
+
+}  // namespace pfa

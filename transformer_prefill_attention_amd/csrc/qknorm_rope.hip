@@ -1,0 +1,168 @@
+// qknorm_rope.hip -- per-(token, head) RMSNorm of Q and K with learned scales,
+// followed by NeoX (rotate-half) rotary embedding, in one HBM pass.
+//
+// Passages: memra-engine 0.130.0 src/forward.rs, `Model::forward`, QK-norm and
+// RoPE blocks (the reference runs them as four launches with two extra HBM
+// round trips; here one wavefront reads each row once and writes it once);
+// needle-core v3/model.rs, `rope_at` / `rope` (frequency and angle).
+//
+// Layout of the work: one wavefront owns one token and walks all of its
+// n_head + n_head_kv head rows.  Lane L holds dims L and L + 64 of a row (one
+// dim for head_dim 64), so every load and store is a 256-byte coalesced
+// segment, the sum of squares is a wavefront reduction, and the rotary cos/sin
+// of the token are computed once per lane and reused by every head.
+//
+// Rotary pair (j, j + n/2): with n == head_dim == 128 both dims of a pair sit
+// in the same lane (no data movement); with n == 64 the partner is lane L ^ 32
+// (one cross-half shuffle); any other even n uses a general two-shuffle path.
+#include "pfa_device.h"
+#include "pfa_internal.h"
+
+namespace pfa {
+
+namespace {
+
+enum PairMode { kPairInLane = 0, kPairXor32 = 1, kPairGeneral = 2 };
+
+constexpr int kRowsInFlight = 4;  // head rows loaded before the first is reduced
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(
+    const float* q_in, const float* k_in, float* q_out, float* k_out,
+    const float* __restrict__ wq, const float* __restrict__ wk, SeqTable seqs, int T, int H,
+    int Hkv, int n, double base, float eps) {
+    constexpr int E = D / 64;  // dims per lane
+    const int lane = threadIdx.x & 63;
+    const int half = n >> 1;
+
+    // Per-lane constants: which rotary pair each of this lane's dims belongs to.
+    double turns[E];
+    float sgn[E], wqv[E], wkv[E];
+    int src[E], slot[E];
+    bool rot[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int c = lane + 64 * e;
+        rot[e] = c < n;
+        const bool first = c < half;
+        const int j = first ? c : c - half;
+        const int p = first ? c + half : c - half;
+        sgn[e] = first ? -1.0f : 1.0f;
+        src[e] = p & 63;
+        slot[e] = p >> 6;
+        turns[e] = rot[e] ? rope_turns_per_pos(j, n, base) : 0.0;
+        wqv[e] = wq[c];
+        wkv[e] = wk[c];
+    }
+
+    const int waves = gridDim.x * (blockDim.x >> 6);
+    for (int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < T; t += waves) {
+        const int s = find_seq(seqs.off, seqs.n_seqs, t);
+        const int pos = t - seqs.off[s];
+        float cs[E], sn[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (rot[e]) {
+                rope_cos_sin(pos, turns[e], cs[e], sn[e]);
+            } else {
+                cs[e] = 1.0f;
+                sn[e] = 0.0f;
+            }
+        }
+
+        auto do_rows = [&](const float* in, float* out, int nrows, const float* wv) {
+            for (int h0 = 0; h0 < nrows; h0 += kRowsInFlight) {
+                float x[kRowsInFlight][E];
+#pragma unroll
+                for (int u = 0; u < kRowsInFlight; ++u) {
+                    if (h0 + u < nrows) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) x[u][e] = in[(h0 + u) * D + lane + 64 * e];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kRowsInFlight; ++u) {
+                    if (h0 + u >= nrows) break;
+                    float ss = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) ss += x[u][e] * x[u][e];
+                    ss = wave_sum(ss);
+                    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+                    float y[E], o[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) y[e] = x[u][e] * r * wv[e];
+                    if (MODE == kPairInLane) {
+                        // n == D == 128: dims L and L + 64 are the two halves of pair L.
+                        o[0] = y[0] * cs[0] - y[E - 1] * sn[0];
+                        o[E - 1] = y[E - 1] * cs[0] + y[0] * sn[0];
+                    } else if (MODE == kPairXor32) {
+                        // n == 64: the partner of dim L (< 64) is dim L ^ 32, in lane L ^ 32.
+                        const float pv = __shfl_xor(y[0], 32, 64);
+                        o[0] = y[0] * cs[0] + sgn[0] * pv * sn[0];
+#pragma unroll
+                        for (int e = 1; e < E; ++e) o[e] = y[e];
+                    } else {
+                        float pv[E];
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            float best = 0.0f;
+#pragma unroll
+                            for (int sl = 0; sl < E; ++sl) {
+                                const float cand = __shfl(y[sl], src[e], 64);
+                                if (slot[e] == sl) best = cand;
+                            }
+                            pv[e] = best;
+                        }
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            o[e] = rot[e] ? y[e] * cs[e] + sgn[e] * pv[e] * sn[e] : y[e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < E; ++e) out[(h0 + u) * D + lane + 64 * e] = o[e];
+                }
+            }
+        };
+        do_rows(q_in + (int64_t)t * H * D, q_out + (int64_t)t * H * D, H, wqv);
+        do_rows(k_in + (int64_t)t * Hkv * D, k_out + (int64_t)t * Hkv * D, Hkv, wkv);
+    }
+}
+
+template <int D, int MODE>
+hipError_t launch_mode(const float* q_in, const float* k_in, float* q_out, float* k_out,
+                       const float* wq, const float* wk, const SeqTable& seqs, int T, int H,
+                       int Hkv, int n, float base, float eps, hipStream_t stream) {
+    // Up to 4 tokens per wavefront so the per-lane rotary frequencies (f64 pow)
+    // are amortised; at least enough workgroups to cover every CU several times.
+    int blocks = (T + 3) / 4;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL((qknorm_rope_kernel<D, MODE>), dim3(blocks), dim3(256), 0, stream, q_in,
+                       k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv, n, (double)base, eps);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
+                              const float* wq, const float* wk, const SeqTable& seqs, int T,
+                              int H, int Hkv, int D, int rope_dim, float base, float eps,
+                              hipStream_t stream) {
+    if (D == 128) {
+        if (rope_dim == 128)
+            return launch_mode<128, kPairInLane>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H,
+                                                 Hkv, rope_dim, base, eps, stream);
+        if (rope_dim == 64)
+            return launch_mode<128, kPairXor32>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H,
+                                                Hkv, rope_dim, base, eps, stream);
+        return launch_mode<128, kPairGeneral>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv,
+                                              rope_dim, base, eps, stream);
+    }
+    // D == 64: one dim per lane.
+    if (rope_dim == 64)
+        return launch_mode<64, kPairXor32>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv,
+                                           rope_dim, base, eps, stream);
+    return launch_mode<64, kPairGeneral>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv,
+                                         rope_dim, base, eps, stream);
+}
+
+}  // namespace pfa
