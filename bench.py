@@ -100,10 +100,26 @@ def main():
     ap.add_argument("--seq-len", type=int, default=0, help="override: one sequence of this length "
                                                            "with the 8B-like heads")
     ap.add_argument("--precision", default="f32", choices=["f32", "bf16"])
-    ap.add_argument("--path", default="fused", choices=["fused", "unfused"])
+    ap.add_argument("--path", default="unfused", choices=["fused", "unfused"],
+                    help="unfused (default, currently the faster): qknorm_rope then "
+                         "gqa_prefill_attn; fused: the single qk_prep_attn call")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run torch copies of a MIB-sized f32 buffer (reference kernel of "
+                         "known traffic for the rocprofv3 FETCH_SIZE / WRITE_SIZE scale factor)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 4 * n, "dispatches": 3}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the path "
