@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "causal GQA prefill attention TFLOP/s (and % of MFMA peak) at T=512..16384"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "bf16x3": 2500.0}   # MI355X dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 
 
@@ -99,7 +99,7 @@ def main():
     ap.add_argument("--workload", default="prefill_8192")
     ap.add_argument("--seq-len", type=int, default=0, help="override: one sequence of this length "
                                                            "with the 8B-like heads")
-    ap.add_argument("--precision", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--precision", default="f32", choices=["f32", "bf16", "bf16x3"])
     ap.add_argument("--path", default="unfused", choices=["fused", "unfused"],
                     help="unfused (default, currently the faster): qknorm_rope then "
                          "gqa_prefill_attn; fused: the single qk_prep_attn call")
@@ -186,7 +186,10 @@ def main():
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.precision]
-    kernel = "attn_f32_kernel<128,true>" if args.path == "fused" else "attn_f32_kernel<128,false>"
+    if args.precision != "f32":
+        kernel = f"attn_bf16_kernel<{w.head_dim},{'true' if args.precision == 'bf16x3' else 'false'}>"
+    else:
+        kernel = f"attn_f32_kernel<{w.head_dim},{'true' if args.path == 'fused' else 'false'}>"
     traffic = load_traffic(w.name, kernel, args.precision, args.path)
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,

@@ -50,10 +50,16 @@ typedef enum {
 } pfa_status;
 
 /* Input type of the two matrix products inside attention.  Accumulation,
- * softmax and the output are f32 in both cases; PFA_PREC_BF16 rounds the
- * normalised Q, K, V and the softmax weights to bf16 (round to nearest even)
- * before each product. */
-typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1 } pfa_precision;
+ * softmax and the output are f32 in every case.
+ *  PFA_PREC_F32    f32 products.
+ *  PFA_PREC_BF16   the (scaled) Q, K, V and the softmax weights are rounded to
+ *                  bf16 (round to nearest even) before each product.
+ *  PFA_PREC_BF16X3 as PFA_PREC_BF16 for P.V; the scores use Q and K each split
+ *                  into a bf16 high part plus a bf16 low part (three products),
+ *                  which keeps the score error from growing with large key norms.
+ * The bf16 modes are available in gqa_prefill_attn; qk_prep_attn takes
+ * PFA_PREC_F32 only (PFA_ERR_UNSUPPORTED otherwise). */
+typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_precision;
 
 /*
  * qknorm_rope -- QK-norm followed by NeoX rotary embedding, for Q and K at once.

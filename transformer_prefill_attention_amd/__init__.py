@@ -5,8 +5,8 @@ C ABI, declared in ``include/pfa.h``).  :mod:`.ops` is the thin Python binding:
 argument marshalling for torch tensors, nothing else.  The library is loaded on
 first use; if it has not been built every op raises.
 """
-from .ops import (PRECISION_BF16, PRECISION_F32, PfaError, gqa_prefill_attn, lib, qk_prep_attn,
-                  qknorm_rope, version)
+from .ops import (PRECISION_BF16, PRECISION_BF16X3, PRECISION_F32, PfaError, gqa_prefill_attn,
+                  lib, qk_prep_attn, qknorm_rope, version)
 
 __all__ = ["qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "lib", "version", "PfaError",
-           "PRECISION_F32", "PRECISION_BF16"]
+           "PRECISION_F32", "PRECISION_BF16", "PRECISION_BF16X3"]

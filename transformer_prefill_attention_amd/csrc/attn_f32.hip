@@ -115,19 +115,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const int lane = tid & 63, wave = tid >> 6, hl = lane >> 5, ln = lane & 31;
 
     // ---- work item (uniform across the workgroup)
-    int bid = blockIdx.x;
-    const int kv = bid % geom.Hkv;
-    bid /= geom.Hkv;
-    const int chunk = bid % geom.chunks;
-    const int item = bid / geom.chunks;
-    int seg = 0;
-    while (item >= sched.seg_start[seg + 1]) ++seg;
-    const int local = item - sched.seg_start[seg];
-    const int per = seg + 1;
-    const int sid = sched.order[local % per];
-    const int sb = sched.seg_top[seg] - 1 - local / per;
-    const int s0 = sched.off[sid], s1 = sched.off[sid + 1];
-    const int q0 = s0 + sb * sched.rows_per_item;
+    const WorkItem wi = decode_item(sched, geom, blockIdx.x);
+    const int kv = wi.kv, chunk = wi.chunk, sb = wi.sb, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
     const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
     const int n_tiles =
         geom.causal ? (min(q0 + sched.rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;

@@ -145,7 +145,7 @@ extern "C" {
 
 const char* pfa_last_error(void) { return g_err; }
 
-const char* pfa_version(void) { return "pfa 0.1 (gfx950; f32 MFMA attention)"; }
+const char* pfa_version(void) { return "pfa 0.2 (gfx950; f32 and bf16 MFMA attention)"; }
 
 int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
                 const float* q_norm_w, const float* k_norm_w, const int32_t* seq_offsets,
@@ -179,8 +179,9 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
                        int head_dim, float scale, int causal, int precision,
                        const pfa::PrepParams* prep, void* stream) {
     if (!std::isfinite(scale)) return fail(PFA_ERR_INVALID_ARG, "scale must be finite");
-    if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16)
-        return fail(PFA_ERR_INVALID_ARG, "precision must be PFA_PREC_F32 or PFA_PREC_BF16 (got %d)",
+    if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3)
+        return fail(PFA_ERR_INVALID_ARG,
+                    "precision must be PFA_PREC_F32, PFA_PREC_BF16 or PFA_PREC_BF16X3 (got %d)",
                     precision);
     if (T == 0) return PFA_OK;
     if (!q || !k || !v || !out) return fail(PFA_ERR_INVALID_ARG, "null tensor pointer");
@@ -201,8 +202,16 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
     if (items == 0) return PFA_OK;
     if ((long long)items * geom.chunks * geom.Hkv >= (1LL << 31))
         return fail(PFA_ERR_UNSUPPORTED, "grid too large");
-    if (precision == PFA_PREC_BF16)
-        return fail(PFA_ERR_UNSUPPORTED, "bf16 attention is not built into this library yet");
+    if (precision != PFA_PREC_F32) {
+        if (prep)
+            return fail(PFA_ERR_UNSUPPORTED,
+                        "qk_prep_attn with PFA_PREC_BF16/BF16X3 is not implemented; call "
+                        "qknorm_rope then gqa_prefill_attn with that precision");
+        return hip_status(pfa::launch_attn_bf16(q, k, v, out, sched, geom, head_dim,
+                                                precision == PFA_PREC_BF16X3, items,
+                                                (hipStream_t)stream),
+                          "gqa_prefill_attn launch");
+    }
     return hip_status(pfa::launch_attn_f32(q, k, v, out, sched, geom, head_dim, prep, items,
                                            (hipStream_t)stream),
                       prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");

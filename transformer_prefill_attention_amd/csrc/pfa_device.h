@@ -53,4 +53,34 @@ __device__ __forceinline__ int find_seq(const int* off, int n_seqs, int t) {
     return lo;
 }
 
+// One workgroup's share of the attention work (see AttnSched): K/V head, head
+// chunk of the group, and the sequence and query super-block it covers.
+struct WorkItem {
+    int kv, chunk, sb;   // K/V head, head chunk, super-block index in the sequence
+    int s0, s1;          // sequence token range [s0, s1)
+    int q0;              // first query row of the super-block
+};
+
+// blockIdx.x -> work item.  The K/V head is the fastest-varying index (so the
+// workgroups that the dispatcher deals to the 8 XCDs in turn share heads), the
+// head chunk next, and the longest-first item order slowest.
+template <class Sched, class Geom>
+__device__ __forceinline__ WorkItem decode_item(const Sched& sched, const Geom& geom, int bid) {
+    WorkItem w;
+    w.kv = bid % geom.Hkv;
+    bid /= geom.Hkv;
+    w.chunk = bid % geom.chunks;
+    const int item = bid / geom.chunks;
+    int seg = 0;
+    while (item >= sched.seg_start[seg + 1]) ++seg;
+    const int local = item - sched.seg_start[seg];
+    const int per = seg + 1;
+    const int sid = sched.order[local % per];
+    w.sb = sched.seg_top[seg] - 1 - local / per;
+    w.s0 = sched.off[sid];
+    w.s1 = sched.off[sid + 1];
+    w.q0 = w.s0 + w.sb * sched.rows_per_item;
+    return w;
+}
+
 }  // namespace pfa

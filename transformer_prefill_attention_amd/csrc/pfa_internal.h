@@ -68,4 +68,9 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
                            const AttnSched& sched, const AttnGeom& geom, int D,
                            const PrepParams* prep, int n_items, hipStream_t stream);
 
+// bf16-input / f32-accumulate attention on already-normalised Q/K.
+// split_qk: scores from bf16 high + low parts of Q and K (PFA_PREC_BF16X3).
+hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out,
+                            const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
+                            int n_items, hipStream_t stream);
 }  // namespace pfa

@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(_HERE, "libpfa.so")
 
 PRECISION_F32 = 0
 PRECISION_BF16 = 1
+PRECISION_BF16X3 = 2
 _PRECISIONS = {"f32": PRECISION_F32, "fp32": PRECISION_F32, "float32": PRECISION_F32,
-               "bf16": PRECISION_BF16, "bfloat16": PRECISION_BF16,
-               PRECISION_F32: PRECISION_F32, PRECISION_BF16: PRECISION_BF16}
+               "bf16": PRECISION_BF16, "bfloat16": PRECISION_BF16, "bf16x3": PRECISION_BF16X3,
+               PRECISION_F32: PRECISION_F32, PRECISION_BF16: PRECISION_BF16,
+               PRECISION_BF16X3: PRECISION_BF16X3}
 
 # Every symbol include/pfa.h declares.
 EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_last_error", "pfa_version")
@@ -124,7 +126,7 @@ def _prec(precision):
     try:
         return _PRECISIONS[precision]
     except KeyError:
-        raise ValueError(f"precision must be 'f32' or 'bf16', got {precision!r}") from None
+        raise ValueError(f"precision must be 'f32', 'bf16' or 'bf16x3', got {precision!r}") from None
 
 
 def qknorm_rope(q, k, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
