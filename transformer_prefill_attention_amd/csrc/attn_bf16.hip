@@ -13,10 +13,10 @@
 //  * 64-key tiles: a bf16 MFMA step is 16x cheaper than the f32 one, so the
 //    per-tile fixed costs (barrier, row max) are spread over twice the keys.
 //  * K is staged row-major as bf16 (row stride d+8: ds_read_b128 conflict-free);
-//    V is staged transposed, V^T[d][key] (stride 64+4 keys), because each lane's
-//    A operand of P.V is 8 consecutive keys of one column; global V loads are
-//    4-byte and coalesced along d, and each thread packs 4 keys into one
-//    ds_write_b64.
+//    V is staged transposed, V^T[d][key] (stride 64+4 keys, 4-key chunks
+//    XOR-swizzled), because each lane's A operand of P.V is 8 consecutive keys
+//    of one column; each thread loads 4x4 blocks as float4 rows and writes them
+//    back as one bf16x4 of 4 keys per column.
 //  * O is accumulated by the MFMA directly and rescaled only when the running
 //    max of some query of the wavefront moves.
 //
@@ -59,11 +59,20 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
     constexpr int NCB = D / 32;           // 32-wide column blocks of O^T
     constexpr int QS = D + 4;             // f32 staging stride of O rows (epilogue)
     static_assert(kWaves * 32 * QS * 4 <= 2 * BUF, "O staging must fit in the K/V buffers");
-    // K staging: thread tid moves float4 (row tid/32 + 8i, column 4 (tid%32)) [D=128]
+    // K staging: thread tid moves float4 number tid + 256 i of the tile (row f/(D/4),
+    // columns 4 (f % (D/4)) ..+3), converted to bf16.
     constexpr int KF4_ROW = D / 4;
     constexpr int K_PER_THREAD = kBN * KF4_ROW / kThreads;
-    // V staging: thread owns column c = tid % D and KPT consecutive keys from vk0
-    constexpr int V_KEYS = kBN * D / kThreads;  // keys per thread (32 for D=128)
+    // V staging: thread tid owns columns 4 cg..4 cg+3 (cg = tid % (D/4)) and V_BLK
+    // blocks of 4 consecutive keys (key 4 kg + KG_STRIDE i, kg = tid / (D/4)); it
+    // loads them as 4 float4 rows per block and writes them transposed, one bf16x4
+    // of 4 keys per column.  The 4-key chunk index inside a V^T row is XOR-swizzled
+    // with ((column >> 4) & 3), which makes both these writes and the operand reads
+    // below free of LDS bank conflicts.
+    constexpr int V_CG = D / 4;                       // column groups
+    constexpr int V_KG = kThreads / V_CG;             // key groups (8 for D=128)
+    constexpr int V_BLK = kBN / (4 * V_KG);           // 4-key blocks per thread
+    constexpr int KG_STRIDE = 4 * V_KG;               // keys between a thread's blocks
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
 
     const int tid = threadIdx.x;
@@ -103,22 +112,34 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
         }
     }
 
-    // ---- staging helpers
+    // ---- staging helpers.  Each tile is read through a buffer resource that starts
+    // at the tile's first row of this K/V head and ends after the sequence's last
+    // row of it: rows past the end of the sequence read as zeros, with no branches.
+    // Per-thread byte offsets inside a tile are fixed.
     floatx4 kreg[K_PER_THREAD];
-    float vreg[V_KEYS];
-    const int v_col = tid % D, v_key0 = (tid / D) * V_KEYS;
-    auto load_k = [&](int t) {
-        const int k0 = s0 + t * kBN;
-        const float* tile = k + ((int64_t)k0 * geom.Hkv + kv) * D;
-        const int rows_left = s1 - k0;
+    floatx4 vreg[4 * V_BLK];
+    const int v_cg = tid % V_CG, v_kg = tid / V_CG;
+    const uint32_t row_bytes = (uint32_t)geom.Hkv * D * 4;  // bytes between tokens
+    uint32_t koff[K_PER_THREAD], voff[4 * V_BLK];
 #pragma unroll
-        for (int i = 0; i < K_PER_THREAD; ++i) {
-            const int f = tid + kThreads * i;
-            const int row = f / KF4_ROW, c4 = f % KF4_ROW;
-            kreg[i] = row < rows_left
-                          ? *reinterpret_cast<const floatx4*>(tile + (unsigned)(row * geom.Hkv * D + 4 * c4))
-                          : floatx4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int i = 0; i < K_PER_THREAD; ++i) {
+        const int f = tid + kThreads * i;
+        koff[i] = (f / KF4_ROW) * row_bytes + 16 * (f % KF4_ROW);
+    }
+#pragma unroll
+    for (int b = 0; b < V_BLK; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            voff[4 * b + e] = (4 * v_kg + KG_STRIDE * b + e) * row_bytes + 16 * v_cg;
+    auto tile_rsrc = [&](const float* base, int t) {
+        const int k0 = s0 + t * kBN;
+        const uint32_t bytes = (uint32_t)(s1 - k0 - 1) * row_bytes + D * 4;
+        return buffer_rsrc(base + ((int64_t)k0 * geom.Hkv + kv) * D, bytes);
+    };
+    auto load_k = [&](int t) {
+        const auto r = tile_rsrc(k, t);
+#pragma unroll
+        for (int i = 0; i < K_PER_THREAD; ++i) kreg[i] = buffer_load_f4(r, koff[i]);
     };
     auto store_k = [&](int buf) {
         __bf16* ks = reinterpret_cast<__bf16*>(smem + buf * BUF);
@@ -138,26 +159,24 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
             }
         }
     };
-    // the key base is the same for the whole wavefront: keep the row pointers in
-    // scalar registers, so each of the V_KEYS loads only carries the column offset
-    const int v_key0_u = __builtin_amdgcn_readfirstlane(v_key0);
     auto load_v = [&](int t) {
-        const int k0 = s0 + t * kBN;
-        const float* tile = v + ((int64_t)(k0 + v_key0_u) * geom.Hkv + kv) * D;
-        const int rows_left = s1 - k0 - v_key0_u;
-        const int64_t stride = (int64_t)geom.Hkv * D;
+        const auto r = tile_rsrc(v, t);
 #pragma unroll
-        for (int j = 0; j < V_KEYS; ++j)
-            vreg[j] = j < rows_left ? tile[j * stride + v_col] : 0.0f;
+        for (int i = 0; i < 4 * V_BLK; ++i) vreg[i] = buffer_load_f4(r, voff[i]);
     };
     auto store_v = [&](int buf) {
         __bf16* vt = reinterpret_cast<__bf16*>(smem + buf * BUF + KBYTES);
 #pragma unroll
-        for (int j = 0; j < V_KEYS; j += 4) {
-            bf16x4 x;
+        for (int b = 0; b < V_BLK; ++b) {
+            const int chunk = v_kg + V_KG * b;  // 4-key chunk index of this block
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (__bf16)vreg[j + e];
-            *reinterpret_cast<bf16x4*>(vt + v_col * VTS + v_key0 + j) = x;
+            for (int c = 0; c < 4; ++c) {
+                const int col = 4 * v_cg + c;
+                bf16x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (__bf16)vreg[4 * b + e][c];
+                *reinterpret_cast<bf16x4*>(vt + col * VTS + 4 * (chunk ^ ((col >> 4) & 3))) = x;
+            }
         }
     };
 
@@ -205,15 +224,15 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
         }
         if (work) {
             const int k0 = s0 + t * kBN;
-            // register r of block kb: key k0 + 32kb + 8(r/4) + 4hl + r%4
+            // register r of block kb: key k0 + 32kb + 8(r/4) + 4hl + r%4.  A key is
+            // hidden when it lies past min(qi, s1-1) (causal) or past s1-1.
             if ((geom.causal && k0 + kBN - 1 > wq0) || k0 + kBN > s1) {
+                const int lim = (geom.causal ? min(qi, s1 - 1) : s1 - 1) - (k0 + 4 * hl);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                        if ((geom.causal && key > qi) || key >= s1) sacc[kb][r] = -INFINITY;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
             }
             float mt = sacc[0][0];
 #pragma unroll
@@ -248,15 +267,19 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
             }
             // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]; step s contracts
             // keys 16s + 8(e/4) + 4hl + e%4 (e = 0..7), i.e. P registers 8(s%2)+e of
-            // score block s/2.  The A operand is two 4-key runs of V^T row d.
+            // score block s/2.  The A operand is two 4-key runs of V^T row d (the
+            // 4-key chunks of a row are XOR-swizzled with (d >> 4) & 3).
             const __bf16* vt = reinterpret_cast<const __bf16*>(smem + cur * BUF + KBYTES);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                const __bf16* vrow = vt + (cb * 32 + ln) * VTS + 4 * hl;
+                const int col = cb * 32 + ln;
+                const int sw = (col >> 4) & 3;  // the chunk swizzle of this V^T row
+                const __bf16* vrow = vt + col * VTS;
+                const int c_lo = hl ^ sw, c_hi = (2 + hl) ^ sw;  // chunks 4s+hl, 4s+2+hl
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 16 * s);
-                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16 * s + 8);
+                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 16 * s + 4 * c_lo);
+                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16 * s + 4 * c_hi);
                     const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     oacc[cb] = mfma_bf16(va, pop[s], oacc[cb]);
                 }

@@ -12,6 +12,19 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kInvTwoPi = 0.15915494309189533577;  // 1 / (2 pi)
 
+// A raw buffer resource over `bytes` bytes from `base` (wavefront-uniform).
+// Buffer loads whose per-lane byte offset (the VGPR offset) falls outside
+// [0, bytes) return zeros, so tiles that run past the end of a sequence need no
+// branches.  0x00020000 is the gfx9 data-format word of an untyped buffer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ floatx4 buffer_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // Sum over the 64 lanes of a wavefront (every lane receives the total).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
