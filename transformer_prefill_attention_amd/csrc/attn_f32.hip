@@ -30,9 +30,11 @@
 //    workgroups (which the dispatcher spreads over the 8 XCDs) walk the same
 //    key tiles of one head together while each XCD's L2 keeps them.
 //
-// PREP = true is the fused entry: raw Q rows are RMS-normalised and rotated as
-// the Q tile is staged, and every K tile is normalised and rotated in LDS right
-// after it lands (optionally copied out as the cache-ready K).
+// PREP = true is the fused entry: raw Q rows are RMS-normalised and rotated once
+// as the Q tile is staged, and every K tile is normalised and rotated in
+// registers on its way into LDS -- between the score and context products of
+// the previous tile, so the matrix cores stay busy -- and optionally copied out
+// as the cache-ready K.
 #include "pfa_device.h"
 #include "pfa_internal.h"
 
@@ -48,52 +50,47 @@ __device__ __forceinline__ floatx16 mfma32x32x2(float a, float b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Normalise (and rotate) one head row of length D held in LDS, in place, by one
-// wavefront: lane L owns dims L and L + 64 (one dim when D == 64).  `pos` is the
-// rotary position; `turns` the lane's per-position angle in turns for each of
-// its dims (0 for dims that are not rotated); `partner` the LDS index offset of
-// the other half of the pair (0 if none).
+// Fused entry: RMS-normalise and rotate one head row held in registers by one
+// wavefront.  Lane L holds dims L + 64e (e < D/64) of the row (x[e], in place).
+// w: the lane's norm weights; cs/sn: cos/sin of the row's rotary angle for each of
+// the lane's dims (ignored for dims >= n); n: rotated dims.  With n == D == 128
+// both halves of a pair sit in one lane; with n == 64 the partner of dim L < 64
+// is lane L ^ 32; any other n exchanges through two shuffles.
 template <int D>
-__device__ __forceinline__ void prep_row_lds(float* row, const float* w, int pos, int n,
-                                             const double* turns, float eps, int lane) {
+__device__ __forceinline__ void prep_row(float (&x)[D / 64], const float* w, const float* cs,
+                                         const float* sn, int n, float eps, int lane) {
     constexpr int E = D / 64;
     const int half = n >> 1;
-    float x[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = row[lane + 64 * e];
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) ss += x[e] * x[e];
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+    ss = wave_sum_dpp(ss);
+    const float rs = 1.0f / sqrtf(ss * (1.0f / D) + eps);
     float y[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = x[e] * r * w[e];
-    // Every lane has finished reading the raw row (the reduction above depends on
-    // all of it), so the normalised values can be published in place and the
-    // partners read back from LDS.
+    for (int e = 0; e < E; ++e) y[e] = x[e] * rs * w[e];
+    if (E == 2 && n == 128) {
+        x[0] = y[0] * cs[0] - y[E - 1] * sn[0];
+        x[E - 1] = y[E - 1] * cs[0] + y[0] * sn[0];
+    } else if (n == 64) {
+        const float pv = __shfl_xor(y[0], 32, 64);
+        x[0] = lane < 32 ? y[0] * cs[0] - pv * sn[0] : y[0] * cs[0] + pv * sn[0];
 #pragma unroll
-    for (int e = 0; e < E; ++e) row[lane + 64 * e] = y[e];
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): our writes are visible
-    __builtin_amdgcn_wave_barrier();
-    float o[E];
+        for (int e = 1; e < E; ++e) x[e] = y[e];
+    } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int c = lane + 64 * e;
-        if (c < n) {
-            const bool first = c < half;
-            const float pv = row[first ? c + half : c - half];
-            float cs, sn;
-            rope_cos_sin(pos, turns[e], cs, sn);
-            o[e] = first ? y[e] * cs - pv * sn : y[e] * cs + pv * sn;
-        } else {
-            o[e] = y[e];
+        for (int e = 0; e < E; ++e) {
+            const int c = lane + 64 * e;
+            const int p = c < half ? c + half : c - half;
+            float pv = 0.0f;
+#pragma unroll
+            for (int sl = 0; sl < E; ++sl) {
+                const float cand = __shfl(y[sl], p & 63, 64);
+                if ((p >> 6) == sl) pv = cand;
+            }
+            x[e] = c >= n ? y[e] : (c < half ? y[e] * cs[e] - pv * sn[e] : y[e] * cs[e] + pv * sn[e]);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int e = 0; e < E; ++e) row[lane + 64 * e] = o[e];
 }
 
 template <int D, bool PREP>
@@ -117,9 +114,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     // ---- work item (uniform across the workgroup)
     const WorkItem wi = decode_item(sched, geom, blockIdx.x);
     const int kv = wi.kv, chunk = wi.chunk, sb = wi.sb, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
+    // (the lambdas below must not capture the kernel-argument structs: taking their
+    // address copies them into scratch memory and makes every value read from them
+    // look divergent; they use these locals instead)
+    const int rows_per_item = sched.rows_per_item;
+    const int n_kv = geom.Hkv, n_q = geom.H;
+    float* const k_rot_out = prep.k_rot_out;
+    const float* const k_in = k;
+    const int rope_dim = prep.rope_dim;
+    const float rms_eps = prep.eps;
     const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
     const int n_tiles =
-        geom.causal ? (min(q0 + sched.rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
+        geom.causal ? (min(q0 + rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
 
     // ---- wavefront role
     const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;
@@ -130,19 +136,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const int wave_tiles = geom.causal ? min(diag_tile + 1, nt_seq) : nt_seq;
     const int qi = wq0 + ln;
 
-    // Rotary frequencies (turns per position) of this lane's dims, for PREP.
-    double turns[D / 64];
-    float wqv[D / 64], wkv[D / 64];
+    // Fused entry, per lane: norm weights and rotary frequency (turns per position)
+    // of its dims L + 64e, and the cos/sin of a 4-position step (K rows of one
+    // wavefront are 4 positions apart inside a tile).
+    constexpr int E = D / 64;
+    double turns[E];
+    float wqv[E], wkv[E], c4s[E], s4s[E];
     if constexpr (PREP) {
+        const int half = prep.rope_dim >> 1;
 #pragma unroll
-        for (int e = 0; e < D / 64; ++e) {
+        for (int e = 0; e < E; ++e) {
             const int c = lane + 64 * e;
-            const int half = prep.rope_dim >> 1;
-            turns[e] = c < prep.rope_dim ? rope_turns_per_pos(c < half ? c : c - half,
-                                                              prep.rope_dim, prep.base)
-                                         : 0.0;
+            turns[e] = c < prep.rope_dim
+                           ? rope_turns_per_pos(c < half ? c : c - half, prep.rope_dim, prep.base)
+                           : 0.0;
             wqv[e] = prep.wq[c];
             wkv[e] = prep.wk[c];
+            rope_cos_sin(kWaves, turns[e], c4s[e], s4s[e]);
         }
     }
 
@@ -162,24 +172,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             qr[4 * c4 + 3] = x[3] * geom.qscale;
         }
     } else {
-        // Fused entry: stage the raw rows in LDS (coalesced), normalise and rotate
-        // them there one row per wavefront step, then pick up the operand layout.
+        // Fused entry: each wavefront normalises and rotates its 32 raw Q rows in
+        // registers (8 at a time, lane L holding dims L + 64e), parks them in LDS
+        // and picks up the operand layout from there.
         float* qs = smem + wave * 32 * QS;
         if (active) {
-#pragma unroll 8
-            for (int r = 0; r < 32; ++r) {
-                const int row = wq0 + r;
-                float* dst = qs + r * QS;
-                const float* src = q + ((int64_t)(row < s1 ? row : s0) * geom.H + h) * D;
+#pragma unroll 1
+            for (int r0 = 0; r0 < 32; r0 += 8) {
+                float x[8][E];
 #pragma unroll
-                for (int e = 0; e < D / 64; ++e)
-                    dst[lane + 64 * e] = row < s1 ? src[lane + 64 * e] : 0.0f;
+                for (int r = 0; r < 8; ++r) {
+                    const int row = wq0 + r0 + r;
+                    const float* src = q + ((int64_t)(row < s1 ? row : s0) * geom.H + h) * D;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) x[r][e] = row < s1 ? src[lane + 64 * e] : 0.0f;
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    float cs[E], sn[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) rope_cos_sin(wq0 + r0 + r - s0, turns[e], cs[e], sn[e]);
+                    prep_row<D>(x[r], wqv, cs, sn, prep.rope_dim, prep.eps, lane);
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        qs[(r0 + r) * QS + lane + 64 * e] = wq0 + r0 + r < s1 ? x[r][e] : 0.0f;
             }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
-            for (int r = 0; r < 32 && wq0 + r < s1; ++r)
-                prep_row_lds<D>(qs + r * QS, wqv, wq0 + r - s0, prep.rope_dim, turns, prep.eps,
-                                lane);
         }
         __syncthreads();
         const float* src = qs + ln * QS + hl * NQ;
@@ -194,29 +214,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
         __syncthreads();
     }
 
-    // ---- K/V tile staging: global -> registers -> LDS, K and V separately so
-    // that only one of them is held in registers at a time.
-    floatx4 kvreg[LD_PER_THREAD];
+    // ---- K/V tile staging: global -> registers -> LDS, K and V separately so that
+    // only one of them is held in registers at a time.  Each tile is read through a
+    // buffer resource that ends after the sequence's last row of this K/V head, so
+    // rows past the end of the sequence read as zeros without any branch.
     // Thread tid moves float4 number tid + 256 i of the 32 x D tile: row f / (D/4),
-    // column 4 (f % (D/4)).  Its offset inside a tile never changes, so only the
-    // (wavefront-uniform) tile base pointer moves from tile to tile.
-    unsigned kv_off[LD_PER_THREAD];
-    int kv_row[LD_PER_THREAD];
+    // column 4 (f % (D/4)); its byte offset inside a tile is fixed.
+    const uint32_t row_bytes = (uint32_t)n_kv * D * 4;
+    floatx4 kvreg[LD_PER_THREAD];
+    uint32_t kv_off[LD_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < LD_PER_THREAD; ++i) {
         const int f = tid + kThreads * i;
-        kv_row[i] = f / F4_PER_ROW;
-        kv_off[i] = (unsigned)(kv_row[i] * geom.Hkv * D + 4 * (f % F4_PER_ROW));
+        kv_off[i] = (f / F4_PER_ROW) * row_bytes + 16 * (f % F4_PER_ROW);
     }
-    auto load_rows = [&](const float* base, int t) {
+    auto tile_rsrc = [&](const float* base, int t) {
         const int k0 = s0 + t * kBN;
-        const float* tile = base + ((int64_t)k0 * geom.Hkv + kv) * D;
-        const int rows_left = s1 - k0;
+        const uint32_t bytes = (uint32_t)(s1 - k0 - 1) * row_bytes + D * 4;
+        return buffer_rsrc(base + ((int64_t)k0 * n_kv + kv) * D, bytes);
+    };
+    auto load_rows = [&](const float* base, int t) {
+        const auto r = tile_rsrc(base, t);
 #pragma unroll
-        for (int i = 0; i < LD_PER_THREAD; ++i)
-            kvreg[i] = kv_row[i] < rows_left
-                           ? *reinterpret_cast<const floatx4*>(tile + kv_off[i])
-                           : floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < LD_PER_THREAD; ++i) kvreg[i] = buffer_load_f4(r, kv_off[i]);
     };
     auto store_rows = [&](float* dst, int stride) {
 #pragma unroll
@@ -226,30 +246,58 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             *reinterpret_cast<floatx4*>(dst + row * stride + 4 * c4) = kvreg[i];
         }
     };
-    // Fused entry: normalise + rotate the K rows of a freshly stored tile (wave w
-    // takes rows w, w+4, ...), and copy them out once if asked.
-    auto prep_tile = [&](int buf, int t) {
-        if constexpr (PREP) {
-            float* ks = smem + buf * BUF;
-            const int k0 = s0 + t * kBN;
-            // exactly one workgroup writes each key row: the one whose query
-            // super-block covers the same rows (first head chunk)
-            const bool writer = prep.k_rot_out && chunk == 0 &&
-                                (t * kBN) / sched.rows_per_item == sb;
-            for (int r = wave; r < kBN; r += kWaves) {
-                const int key = k0 + r;
-                if (key >= s1) continue;
-                float* row = ks + r * KS;
-                prep_row_lds<D>(row, wkv, key - s0, prep.rope_dim, turns, prep.eps, lane);
-                if (writer) {
-                    __builtin_amdgcn_s_waitcnt(0xc07f);
-                    __builtin_amdgcn_wave_barrier();
-                    float* dst = prep.k_rot_out + ((int64_t)key * geom.Hkv + kv) * D;
+    // Fused entry: the raw K rows of a tile in the wave-per-row layout (wavefront w
+    // owns rows w, w+4, ..., lane L dims L + 64e), normalised and rotated in
+    // registers and then written to the LDS tile (and, by exactly one workgroup --
+    // the first head chunk of the super-block covering those rows -- to k_rot_out).
+    constexpr int KR = kBN / kWaves;  // rows per wavefront
+    float kraw[KR][E];
+    auto load_k_prep = [&](int t) {
+        const auto r = tile_rsrc(k_in, t);
 #pragma unroll
-                    for (int e = 0; e < D / 64; ++e) dst[lane + 64 * e] = row[lane + 64 * e];
+        for (int i = 0; i < KR; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                kraw[i][e] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(
+                               r, (wave + kWaves * i) * row_bytes + 4 * (lane + 64 * e), 0, 0));
+    };
+    auto prep_store_k = [&](float* ks, int t, bool real) {
+        if constexpr (PREP) {
+            const int k0 = s0 + t * kBN;
+            // angle of row `wave`, then one 4-position turn per further row
+            float cs[E], sn[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) rope_cos_sin(k0 + wave - s0, turns[e], cs[e], sn[e]);
+            const bool writer = real && k_rot_out && chunk == 0 && (t * kBN) / rows_per_item == sb;
+#pragma unroll
+            for (int i = 0; i < KR; ++i) {
+                prep_row<D>(kraw[i], wkv, cs, sn, rope_dim, rms_eps, lane);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float c = cs[e] * c4s[e] - sn[e] * s4s[e];
+                    sn[e] = sn[e] * c4s[e] + cs[e] * s4s[e];
+                    cs[e] = c;
+                }
+                const int row = wave + kWaves * i;
+                const bool ok = k0 + row < s1;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float y = ok ? kraw[i][e] : 0.0f;
+                    ks[row * KS + lane + 64 * e] = y;
+                    if (writer && ok)
+                        k_rot_out[((int64_t)(k0 + row) * n_kv + kv) * D + lane + 64 * e] = y;
                 }
             }
         }
+    };
+    auto load_k_tile = [&](int t) {
+        if constexpr (PREP) load_k_prep(t);
+        else load_rows(k_in, t);
+    };
+    auto store_k_tile = [&](float* ks, int t) {
+        if constexpr (PREP) prep_store_k(ks, t, true);
+        else store_rows(ks, KS);
     };
 
     // ---- accumulators
@@ -265,21 +313,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     float m_run = -INFINITY;
     double l_run = 0.0;
 
-    load_rows(k, 0);
-    store_rows(smem, KS);
+    load_k_tile(0);
+    store_k_tile(smem, 0);
     load_rows(v, 0);
     store_rows(smem + kBN * KS, VS);
     __syncthreads();
-    if constexpr (PREP) {
-        prep_tile(0, 0);
-        __syncthreads();
-    }
 
     for (int t = 0; t < n_tiles; ++t) {
         const int cur = t & 1;
         const bool more = t + 1 < n_tiles;
         float* kn = smem + (cur ^ 1) * BUF;
-        if (more) load_rows(k, t + 1);
+        if (more) load_k_tile(t + 1);
         if (active && t < wave_tiles) {
             const float* ks = smem + cur * BUF;
             const float* vs = ks + kBN * KS;
@@ -345,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             }
             l_run = l_run * (double)alpha + (double)psum;
             if (more) {
-                store_rows(kn, KS);
+                if constexpr (!PREP) store_rows(kn, KS);
                 load_rows(v, t + 1);
             }
             // O^T[d][query] = alpha * O^T + sum_key V[key][d] P[query][key].  Each
@@ -377,17 +421,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             }
         } else if (more) {
             // this wavefront has no work on tile t but still stages tile t+1
-            store_rows(kn, KS);
+            if constexpr (!PREP) store_rows(kn, KS);
             load_rows(v, t + 1);
         }
-        if (more) store_rows(kn + kBN * KS, VS);
-        __syncthreads();
-        if constexpr (PREP) {
-            if (t + 1 < n_tiles) {
-                prep_tile(cur ^ 1, t + 1);
-                __syncthreads();
-            }
+        if (more) {
+            // fused entry: the raw K rows of tile t+1 (loaded at the top of this
+            // tile) are normalised and rotated here, where the score registers are
+            // free, while the context MFMAs are still draining
+            if constexpr (PREP) prep_store_k(kn, t + 1, true);
+            store_rows(kn + kBN * KS, VS);
         }
+        __syncthreads();
     }
 
     // ---- epilogue: 1/l, transpose through LDS, coalesced row stores
@@ -416,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             const int r = f / F4_PER_ROW, c4 = f % F4_PER_ROW;
             const int row = wq0 + r;
             if (row < s1)
-                *reinterpret_cast<floatx4*>(out + ((int64_t)row * geom.H + h) * D + 4 * c4) =
+                *reinterpret_cast<floatx4*>(out + ((int64_t)row * n_q + h) * D + 4 * c4) =
                     *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
         }
     }

@@ -117,7 +117,7 @@ int build_sched(const pfa::SeqTable& st, int rows_per_item, pfa::AttnSched& sc) 
     std::stable_sort(idx, idx + st.n_seqs, [&](int a, int b) { return nsb[a] > nsb[b]; });
     int n_nonempty = 0;
     for (int s = 0; s < st.n_seqs; ++s) {
-        sc.order[s] = (int16_t)idx[s];
+        sc.order[s] = idx[s];
         if (nsb[idx[s]] > 0) ++n_nonempty;
     }
     int items = 0;

@@ -32,6 +32,24 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Sum over the 64 lanes of a wavefront: DPP rotations and quad permutations
+// inside each 16-lane row (plain VALU operand modifiers), then two cross-row
+// exchanges.  Every lane receives the total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                  CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x += dpp_f32<0x128>(x);  // row_ror:8
+    x += dpp_f32<0x124>(x);  // row_ror:4
+    x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {

@@ -33,7 +33,7 @@ struct AttnSched {
     int off[PFA_MAX_SEQS + 1];       // as SeqTable::off
     int seg_start[PFA_MAX_SEQS + 1]; // first item of each segment; [n_segs] = item count
     int seg_top[PFA_MAX_SEQS];       // super-block count of the (k+1)-th longest sequence
-    int16_t order[PFA_MAX_SEQS];     // sequence ids, most super-blocks first
+    int32_t order[PFA_MAX_SEQS];     // sequence ids, most super-blocks first (32-bit: scalar loads)
 };
 
 // Geometry common to the attention launches.
