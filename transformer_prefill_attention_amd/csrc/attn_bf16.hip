@@ -37,17 +37,22 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = 64;       // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Wavefronts per workgroup: 8 for head_dim 128 (two per SIMD, all sharing each
+// K/V tile, which halves every wavefront's share of the staging and conversion
+// work), 4 for head_dim 64.
+template <int D>
+constexpr int waves_for() { return D == 128 ? 8 : 4; }
 
 __device__ __forceinline__ floatx16 mfma_bf16(bf16x8 a, bf16x8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
+__global__ __launch_bounds__(64 * waves_for<D>(), (SPLIT || D == 128) ? 1 : 2) void attn_bf16_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, AttnSched sched, AttnGeom geom) {
+    constexpr int kWaves = waves_for<D>();
+    constexpr int kThreads = 64 * kWaves;
     // K row in LDS: [high parts | low parts (SPLIT only)], padded so that
     // ds_read_b128 of 32 different rows is conflict-free
     constexpr int KS = (SPLIT ? 2 * D : D) + 8;  // K row stride in LDS (bf16 elements)
@@ -58,7 +63,9 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
     constexpr int NQS = D / 16;           // MFMA steps of K Q^T (16 dims each)
     constexpr int NCB = D / 32;           // 32-wide column blocks of O^T
     constexpr int QS = D + 4;             // f32 staging stride of O rows (epilogue)
-    static_assert(kWaves * 32 * QS * 4 <= 2 * BUF, "O staging must fit in the K/V buffers");
+    // the epilogue stages O through LDS four wavefronts at a time
+    static_assert(4 * 32 * QS * 4 <= 2 * BUF, "O staging must fit in the K/V buffers");
+    static_assert(kBN * D % (16 * kThreads) == 0, "V staging moves whole 4x4 blocks");
     // K staging: thread tid moves float4 number tid + 256 i of the tile (row f/(D/4),
     // columns 4 (f % (D/4)) ..+3), converted to bf16.
     constexpr int KF4_ROW = D / 4;
@@ -293,33 +300,38 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
         __syncthreads();
     }
 
-    // ---- epilogue
+    // ---- epilogue: 1/l, transpose through LDS (four wavefronts at a time), coalesced rows
     const double l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = (float)(1.0 / l_tot);
-    float* os = reinterpret_cast<float*>(smem) + wave * 32 * QS;
-    if (active) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
+    for (int round = 0; round < kWaves / 4; ++round) {
+        const bool mine = (wave >> 2) == round;
+        float* os = reinterpret_cast<float*>(smem) + (wave & 3) * 32 * QS;
+        if (mine && active) {
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                floatx4 x;
+            for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = oacc[cb][4 * r4 + e] * inv;
-                *reinterpret_cast<floatx4*>(os + ln * QS + cb * 32 + 8 * r4 + 4 * hl) = x;
-            }
-    }
-    __syncthreads();
-    if (active) {
-        constexpr int F4 = D / 4;
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    floatx4 x;
 #pragma unroll
-        for (int i = 0; i < 32 * F4 / 64; ++i) {
-            const int f = lane + 64 * i;
-            const int r = f / F4, c4 = f % F4;
-            const int row = wq0 + r;
-            if (row < s1)
-                *reinterpret_cast<floatx4*>(out + ((int64_t)row * geom.H + h) * D + 4 * c4) =
-                    *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
+                    for (int e = 0; e < 4; ++e) x[e] = oacc[cb][4 * r4 + e] * inv;
+                    *reinterpret_cast<floatx4*>(os + ln * QS + cb * 32 + 8 * r4 + 4 * hl) = x;
+                }
         }
+        __syncthreads();
+        if (mine && active) {
+            constexpr int F4 = D / 4;
+#pragma unroll
+            for (int i = 0; i < 32 * F4 / 64; ++i) {
+                const int f = lane + 64 * i;
+                const int r = f / F4, c4 = f % F4;
+                const int row = wq0 + r;
+                if (row < s1)
+                    *reinterpret_cast<floatx4*>(out + ((int64_t)row * geom.H + h) * D + 4 * c4) =
+                        *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
+            }
+        }
+        if (round + 1 < kWaves / 4) __syncthreads();
     }
 }
 
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(kThreads, SPLIT ? 1 : 2) void attn_bf16_kernel(
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
                             int n_items, hipStream_t stream) {
-    const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(kThreads);
+    const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(64 * (D == 128 ? 8 : 4));
 #define PFA_LAUNCH_BF16(DD, SS)                                                                  \
     hipLaunchKernelGGL((attn_bf16_kernel<DD, SS>), grid, block, 0, stream, q, k, v, out, sched, \
                        geom)

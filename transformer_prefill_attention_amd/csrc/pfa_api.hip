@@ -86,10 +86,10 @@ int build_seqs(const int32_t* seq_offsets, int n_seqs, int T, pfa::SeqTable& st)
     return PFA_OK;
 }
 
-// Work split of a workgroup (four wavefronts) for group size g: as many heads of
-// the group as divide both g and 4, the rest of the four wavefronts take more
-// 32-row query blocks.
-void choose_geometry(int H, int Hkv, float scale, int causal, pfa::AttnGeom& geom) {
+// Work split of a workgroup of `waves` wavefronts for group size g: as many heads
+// of the group as divide both g and 4, the other wavefronts take more 32-row
+// query blocks.
+void choose_geometry(int H, int Hkv, float scale, int causal, int waves, pfa::AttnGeom& geom) {
     const int g = H / Hkv;
     int hpw = 1;
     while (hpw < 4 && g % (hpw * 2) == 0) hpw *= 2;
@@ -97,7 +97,7 @@ void choose_geometry(int H, int Hkv, float scale, int causal, pfa::AttnGeom& geo
     geom.Hkv = Hkv;
     geom.g = g;
     geom.hpw = hpw;
-    geom.rb = 4 / hpw;
+    geom.rb = waves / hpw;
     geom.chunks = g / hpw;
     geom.qscale = scale * 1.4426950408889634f;
     geom.causal = causal ? 1 : 0;
@@ -196,7 +196,9 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
     int rc = build_seqs(seq_offsets, n_seqs, T, st);
     if (rc) return rc;
     pfa::AttnGeom geom;
-    choose_geometry(n_head, n_head_kv, scale, causal, geom);
+    // the bf16 kernel runs 8 wavefronts per workgroup at head_dim 128, else 4
+    const int waves = (precision != PFA_PREC_F32 && head_dim == 128) ? 8 : 4;
+    choose_geometry(n_head, n_head_kv, scale, causal, waves, geom);
     pfa::AttnSched sched;
     const int items = build_sched(st, 32 * geom.rb, sched);
     if (items == 0) return PFA_OK;
