@@ -13,7 +13,8 @@
  *    note and SDPA block) keeps between its projections and its attention.
  *  Pointers.  Tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *    aligned.  The library allocates no device memory and keeps no state beyond
- *    its loaded code objects.
+ *    its loaded code objects; the bf16 attention modes take a caller-owned
+ *    device workspace (see pfa_workspace_bytes).
  *  Sequences.  `seq_offsets` is a HOST array of n_seqs + 1 int32 values
  *    (cumulative lengths: seq_offsets[0] = 0, non-decreasing, seq_offsets[n_seqs]
  *    = T).  NULL means one sequence [0, T) (n_seqs is then ignored).  Token t of
@@ -34,6 +35,7 @@
 #ifndef PFA_H
 #define PFA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -50,7 +52,8 @@ typedef enum {
 } pfa_status;
 
 /* Input type of the two matrix products inside attention.  Accumulation,
- * softmax and the output are f32 in every case.
+ * softmax and the output are f32 in every case (the inputs and output stay f32
+ * tensors; the bf16 modes convert K and V once into the workspace).
  *  PFA_PREC_F32    f32 products.
  *  PFA_PREC_BF16   the (scaled) Q, K, V and the softmax weights are rounded to
  *                  bf16 (round to nearest even) before each product.
@@ -60,6 +63,15 @@ typedef enum {
  * The bf16 modes are available in gqa_prefill_attn; qk_prep_attn takes
  * PFA_PREC_F32 only (PFA_ERR_UNSUPPORTED otherwise). */
 typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_precision;
+
+/* Device workspace in bytes that gqa_prefill_attn / qk_prep_attn need at this
+ * size and precision: 0 for PFA_PREC_F32; for the bf16 modes, K and V converted
+ * once to bf16 in 64-key tiles per sequence (K twice, high and low parts, for
+ * PFA_PREC_BF16X3):
+ *   n_head_kv * (ceil(T / 64) + max(n_seqs, 1)) * 64 * head_dim * 2 * (2 or 3)
+ * bytes.  n_seqs is the count passed with seq_offsets (1 when that is NULL).
+ * Returns 0 for arguments the attention calls would reject. */
+size_t pfa_workspace_bytes(int T, int n_seqs, int n_head_kv, int head_dim, int precision);
 
 /*
  * qknorm_rope -- QK-norm followed by NeoX rotary embedding, for Q and K at once.
@@ -112,11 +124,17 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
  *  k, v [T, n_head_kv*head_dim]  f32, device, read
  *  out  [T, n_head*head_dim]     f32, device, written; must not overlap q, k, v.
  *  scale  finite; precision  a pfa_precision value.
+ *  workspace, workspace_bytes  device memory owned by the caller, 256-byte
+ *        aligned, at least pfa_workspace_bytes(T, n_seqs, n_head_kv, head_dim,
+ *        precision) bytes, not overlapping the tensors; its contents are
+ *        overwritten (calls in flight at the same time need separate
+ *        workspaces).  Ignored, and may be NULL, for PFA_PREC_F32.
  */
 int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
                      const int32_t* seq_offsets, int n_seqs,
                      int T, int n_head, int n_head_kv, int head_dim,
-                     float scale, int causal, int precision, void* stream);
+                     float scale, int causal, int precision,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * qk_prep_attn -- the whole attention core in one call: qknorm_rope applied to
@@ -133,13 +151,14 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
  *  k_rot_out  NULL, or [T, n_head_kv*head_dim] f32, device: also receives the
  *        normalised, rotated K (what a KV cache would store); must not overlap
  *        the inputs or out.
+ *  workspace, workspace_bytes  as for gqa_prefill_attn.
  */
 int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
                  const float* q_norm_w, const float* k_norm_w,
                  const int32_t* seq_offsets, int n_seqs,
                  int T, int n_head, int n_head_kv, int head_dim, int rope_dim,
                  float rope_freq_base, float rms_eps, float scale, int causal, int precision,
-                 float* k_rot_out, void* stream);
+                 float* k_rot_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pfa_last_error(void);

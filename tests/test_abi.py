@@ -31,7 +31,8 @@ def L():
 
 def test_header_declares_the_three_entry_points():
     names = _declared()
-    for n in ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_last_error", "pfa_version"):
+    for n in ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_workspace_bytes",
+              "pfa_last_error", "pfa_version"):
         assert n in names
     assert set(names) == set(ops.EXPORTS)
 
@@ -43,9 +44,10 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def _attn(L, T=16, H=4, Hkv=2, D=64, scale=0.125, causal=1, prec=0, offs=None, n_seqs=0,
-          ptrs=(8, 8, 8, 8 << 20)):
+          ptrs=(8, 8, 8, 8 << 20), ws=0, ws_bytes=0):
     q, k, v, o = (ctypes.c_void_p(p) for p in ptrs)
-    return L.gqa_prefill_attn(q, k, v, o, offs, n_seqs, T, H, Hkv, D, scale, causal, prec, None)
+    return L.gqa_prefill_attn(q, k, v, o, offs, n_seqs, T, H, Hkv, D, scale, causal, prec,
+                              ctypes.c_void_p(ws), ws_bytes, None)
 
 
 def _msg(L):
@@ -57,7 +59,7 @@ def test_zero_tokens_is_ok_without_pointers(L):
     n = ctypes.c_void_p(0)
     assert L.qknorm_rope(n, n, n, n, n, n, None, 0, 0, 4, 2, 64, 64, 1e6, 1e-6, None) == OK
     assert L.qk_prep_attn(n, n, n, n, n, n, None, 0, 0, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0, n,
-                          None) == OK
+                          n, 0, None) == OK
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -99,7 +101,7 @@ def test_rope_argument_checks(L, rope_dim, base, eps, needle):
     assert needle in _msg(L)
     assert L.qk_prep_attn(p(8), p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p(5 << 20), None,
                           0, 16, 4, 2, 64, rope_dim, base, eps, 0.125, 1, 0, p(0),
-                          None) == INVALID
+                          p(0), 0, None) == INVALID
 
 
 def test_qknorm_rope_aliasing_rules(L):
@@ -119,7 +121,7 @@ def test_k_rot_out_must_not_alias(L):
     p = ctypes.c_void_p
     assert L.qk_prep_attn(p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p(5 << 20),
                           p(5 << 20), None, 0, 16, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0,
-                          p(2 << 20), None) == INVALID
+                          p(2 << 20), p(0), 0, None) == INVALID
     assert "k_rot_out" in _msg(L)
 
 
@@ -131,3 +133,42 @@ def test_python_binding_raises_without_gpu_tensors():
     with pytest.raises(TypeError):
         pfa.gqa_prefill_attn(torch.zeros(4, 128, dtype=torch.float64), torch.zeros(4, 64),
                              torch.zeros(4, 64), head_dim=64)
+
+
+def _tiles(T, n_seqs):
+    return -(-T // 64) + max(n_seqs, 1)
+
+
+@pytest.mark.parametrize("T,n_seqs,Hkv,D", [(16, 0, 2, 64), (8192, 1, 8, 128), (16064, 8, 4, 64),
+                                           (1, 128, 1, 128)])
+def test_workspace_bytes_formula(L, T, n_seqs, Hkv, D):
+    # the documented bound: K and V as bf16 in 64-key tiles (K twice for bf16x3)
+    per_part = Hkv * _tiles(T, n_seqs) * 64 * D * 2
+    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 0) == 0
+    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 1) == 2 * per_part
+    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 2) == 3 * per_part
+    assert pfa.workspace_bytes(T, n_seqs, Hkv, D, "bf16x3") == 3 * per_part
+
+
+def test_workspace_bytes_rejects_what_attention_rejects(L):
+    assert L.pfa_workspace_bytes(16, 1, 2, 96, 1) == 0
+    assert L.pfa_workspace_bytes(16, 1, 2, 64, 7) == 0
+    assert L.pfa_workspace_bytes(16, 129, 2, 64, 1) == 0
+    assert L.pfa_workspace_bytes(-1, 1, 2, 64, 1) == 0
+
+
+@pytest.mark.parametrize("prec", [1, 2])
+def test_bf16_modes_check_the_workspace(L, prec):
+    # every call below must fail its checks before any launch (the pointers are not real)
+    ptrs = (1 << 20, 2 << 20, 3 << 20, 4 << 20)   # q 16x4x64 f32 = 16 KiB, k/v 8 KiB each
+    need = L.pfa_workspace_bytes(16, 1, 2, 64, prec)
+    exact = (2 if prec == 1 else 3) * 2 * 1 * 64 * 64 * 2   # one 64-key tile per K/V head
+    assert exact <= need
+    assert _attn(L, prec=prec, ptrs=ptrs) == INVALID
+    assert "workspace" in _msg(L)
+    assert _attn(L, prec=prec, ptrs=ptrs, ws=8 << 20, ws_bytes=exact - 1) == INVALID
+    assert "needed" in _msg(L)
+    assert _attn(L, prec=prec, ptrs=ptrs, ws=(8 << 20) + 16, ws_bytes=need) == INVALID
+    assert "aligned" in _msg(L)
+    assert _attn(L, prec=prec, ptrs=ptrs, ws=(3 << 20) + 4096, ws_bytes=need) == INVALID
+    assert "overlap" in _msg(L)

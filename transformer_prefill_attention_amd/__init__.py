@@ -6,7 +6,8 @@ argument marshalling for torch tensors, nothing else.  The library is loaded on
 first use; if it has not been built every op raises.
 """
 from .ops import (PRECISION_BF16, PRECISION_BF16X3, PRECISION_F32, PfaError, gqa_prefill_attn,
-                  lib, qk_prep_attn, qknorm_rope, version)
+                  lib, qk_prep_attn, qknorm_rope, version, workspace_bytes)
 
-__all__ = ["qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "lib", "version", "PfaError",
+__all__ = ["qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "workspace_bytes", "lib", "version",
+           "PfaError",
            "PRECISION_F32", "PRECISION_BF16", "PRECISION_BF16X3"]

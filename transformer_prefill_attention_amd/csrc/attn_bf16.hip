@@ -7,24 +7,40 @@
 // K, V and the softmax weights P, each just before its product; the scores, the
 // softmax, the accumulation and the output stay f32 (the denominator f64).
 //
-// Same work split as the f32 kernel (four wavefronts on one K/V head, LDS tiles
-// shared by the query heads of a group, longest-first items, S^T = K Q^T so
-// that P lands in the B-operand layout).  Differences:
-//  * 64-key tiles: a bf16 MFMA step is 16x cheaper than the f32 one, so the
-//    per-tile fixed costs (barrier, row max) are spread over twice the keys.
-//  * K is staged row-major as bf16 (row stride d+8: ds_read_b128 conflict-free);
-//    V is staged transposed, V^T[d][key] (stride 64+4 keys, 4-key chunks
-//    XOR-swizzled), because each lane's A operand of P.V is 8 consecutive keys
-//    of one column; each thread loads 4x4 blocks as float4 rows and writes them
-//    back as one bf16x4 of 4 keys per column.
-//  * O is accumulated by the MFMA directly and rescaled only when the running
-//    max of some query of the wavefront moves.
+// Two kernels:
+//  * stage_kv_bf16_kernel converts K and V once into a workspace of 64-key
+//    tiles per (K/V head, sequence), each tile laid out byte for byte as the
+//    attention kernel keeps it in LDS: K row-major with the 16-byte chunks of a
+//    row XOR-swizzled by the row index, V transposed (V^T[d][key]) with the keys
+//    of each row in MFMA operand order and the same kind of swizzle.  Rows past
+//    the end of a sequence are zeros.  Without this step every workgroup would
+//    convert every tile it visits again (about T/64 times per tile).
+//  * attn_bf16_kernel: one workgroup of eight wavefronts per (K/V head, query
+//    super-block), S^T = K Q^T so that P lands in the B-operand layout of
+//    O^T += V^T P^T, online softmax in base 2 as in the f32 kernel.  Tiles move
+//    HBM/L2 -> LDS with direct-to-LDS loads (no registers, no conversion).
+//
+// Ping-pong schedule.  Wavefronts 0-3 (group A) and 4-7 (group B) sit on the
+// four SIMDs in pairs (one of each group per SIMD).  Each wavefront runs the
+// same sequence of phases, matrix phase M(t) = [P(t-1) V(t-1), S(t) = K(t) Q^T]
+// then softmax phase X(t) = [scores -> P(t)], with a workgroup barrier after
+// every phase; group B starts one phase late.  So in every barrier interval one
+// wavefront of each SIMD issues MFMAs while the other does the exponentials,
+// and the softmax work hides behind the matrix cores instead of adding to them.
+// The loads of K(t+1) and V(t) are issued in global phase 2t and waited for at
+// the end of phase 2t+1; LDS holds two K and two V tiles.
+//
+// O is rescaled lazily: the running max used for the exponentials only moves
+// when a new score exceeds it by more than 8 (log2 units), so P stays <= 256
+// and, on typical data, O is rescaled only in the first tiles.  The softmax
+// denominator adds up the bf16-rounded weights (v_dot2 against ones), the same
+// numbers the P.V product uses.
 //
 // SPLIT = true is the PFA_PREC_BF16X3 mode: Q and K are each split into a bf16
 // high part and a bf16 low part (x = hi + lo to ~2^-17) and the scores take the
 // three products hi.hi + hi.lo + lo.hi, so score rounding no longer grows with
 // |score| the way plain bf16 inputs do (keys with large norms); P and V stay
-// plain bf16.  K's low parts double its LDS tile, so one workgroup per CU.
+// plain bf16.  The K tiles carry both parts.
 #include "pfa_device.h"
 #include "pfa_internal.h"
 
@@ -33,77 +49,154 @@ namespace pfa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBN = 64;       // keys per tile
-// Wavefronts per workgroup: 8 for head_dim 128 (two per SIMD, all sharing each
-// K/V tile, which halves every wavefront's share of the staging and conversion
-// work), 4 for head_dim 64.
-template <int D>
-constexpr int waves_for() { return D == 128 ? 8 : 4; }
+constexpr int kBN = kBf16TileKeys;  // keys per tile (64)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+// the running max moves only when exceeded by more than this (log2 units)
+constexpr float kLazyMax = 8.0f;
 
 __device__ __forceinline__ floatx16 mfma_bf16(bf16x8 a, bf16x8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Position of 16-byte chunk `c` in row `row` of an LDS tile with `nch` chunks per
+// row.  Any 16 consecutive rows of a 32-row block map one logical chunk to 16
+// different positions (and rows of equal parity to 8 different ones), so the
+// ds_read_b128 of one chunk from 32 rows spreads over all banks.
+__device__ __forceinline__ int swz(int row, int c, int nch) {
+    return c ^ ((row % nch) ^ ((row / nch) & 1));
+}
+
+// v_max3_f32 without the NaN-quieting operand canonicalisation fmaxf gets (the
+// scores are MFMA results or -inf, never signalling NaNs)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max of the 16 registers of a score block
+__device__ __forceinline__ float max16(const floatx16& x) {
+    float m = max3(x[0], x[1], x[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) m = max3(m, x[r], x[r + 1]);
+    return max3(m, x[15], x[15]);
+}
+
+__device__ __forceinline__ float max_halves(float x) {
+    // v_permlane32_swap: lanes 0-31 and 32-63 exchange, so max(r[0], r[1]) is the
+    // max over the two lanes of one query
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+// ---------------------------------------------------------------------------
+// K/V -> bf16 tiles.  Block = (K/V head, tile over all sequences).
+//  K tile: KP parts (high, low) x 64 rows x D; element (r, c) at r*D + 8*swz(r, c/8, D/8) + c%8.
+//  V tile: D rows x 64 keys; row d holds 8 groups of 8 keys, group p = 2s + h being
+//  keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3} (the keys lane half h feeds
+//  at P.V step s), group p stored at position swz(d, p, 8).
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(64 * waves_for<D>(), (SPLIT || D == 128) ? 1 : 2) void attn_bf16_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ out, AttnSched sched, AttnGeom geom) {
-    constexpr int kWaves = waves_for<D>();
-    constexpr int kThreads = 64 * kWaves;
-    // K row in LDS: [high parts | low parts (SPLIT only)], padded so that
-    // ds_read_b128 of 32 different rows is conflict-free
-    constexpr int KS = (SPLIT ? 2 * D : D) + 8;  // K row stride in LDS (bf16 elements)
-    constexpr int VTS = kBN + 4;          // V^T row stride (bf16 elements)
-    constexpr int KBYTES = kBN * KS * 2;
-    constexpr int VBYTES = D * VTS * 2;
-    constexpr int BUF = KBYTES + VBYTES;  // bytes per stage
-    constexpr int NQS = D / 16;           // MFMA steps of K Q^T (16 dims each)
-    constexpr int NCB = D / 32;           // 32-wide column blocks of O^T
-    constexpr int QS = D + 4;             // f32 staging stride of O rows (epilogue)
-    // the epilogue stages O through LDS four wavefronts at a time
-    static_assert(4 * 32 * QS * 4 <= 2 * BUF, "O staging must fit in the K/V buffers");
-    static_assert(kBN * D % (16 * kThreads) == 0, "V staging moves whole 4x4 blocks");
-    // K staging: thread tid moves float4 number tid + 256 i of the tile (row f/(D/4),
-    // columns 4 (f % (D/4)) ..+3), converted to bf16.
-    constexpr int KF4_ROW = D / 4;
-    constexpr int K_PER_THREAD = kBN * KF4_ROW / kThreads;
-    // V staging: thread tid owns columns 4 cg..4 cg+3 (cg = tid % (D/4)) and V_BLK
-    // blocks of 4 consecutive keys (key 4 kg + KG_STRIDE i, kg = tid / (D/4)); it
-    // loads them as 4 float4 rows per block and writes them transposed, one bf16x4
-    // of 4 keys per column.  The 4-key chunk index inside a V^T row is XOR-swizzled
-    // with ((column >> 4) & 3), which makes both these writes and the operand reads
-    // below free of LDS bank conflicts.
-    constexpr int V_CG = D / 4;                       // column groups
-    constexpr int V_KG = kThreads / V_CG;             // key groups (8 for D=128)
-    constexpr int V_BLK = kBN / (4 * V_KG);           // 4-key blocks per thread
-    constexpr int KG_STRIDE = 4 * V_KG;               // keys between a thread's blocks
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+__global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restrict__ k,
+                                                            const float* __restrict__ v,
+                                                            __bf16* __restrict__ ws,
+                                                            AttnSched sched, int Hkv) {
+    constexpr int KP = SPLIT ? 2 : 1;
+    constexpr int NCH = D / 8;
+    const int kv = blockIdx.x % Hkv;
+    const int gt = blockIdx.x / Hkv;
+    const int n_tiles = sched.n_tiles;
+    const int s = find_seq(sched.tile_off, sched.n_seqs, gt);
+    const int k0 = sched.off[s] + (gt - sched.tile_off[s]) * kBN;
+    const int nval = min(kBN, sched.off[s + 1] - k0);
+    const int64_t row_stride = (int64_t)Hkv * D;
+    __bf16* kt = ws + ((int64_t)kv * n_tiles + gt) * (KP * kBN * D);
+    __bf16* vt = ws + (int64_t)Hkv * n_tiles * (KP * kBN * D) +
+                 ((int64_t)kv * n_tiles + gt) * (kBN * D);
+    for (int f = threadIdx.x; f < kBN * NCH; f += 256) {
+        const int r = f / NCH, c = f % NCH;
+        floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+        if (r < nval) {
+            const float* src = k + (k0 + r) * row_stride + kv * D + 8 * c;
+            a = *reinterpret_cast<const floatx4*>(src);
+            b = *reinterpret_cast<const floatx4*>(src + 4);
+        }
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = e < 4 ? a[e] : b[e - 4];
+            hi[e] = (__bf16)x;
+            if constexpr (SPLIT) lo[e] = (__bf16)(x - (float)hi[e]);
+        }
+        const int pos = swz(r, c, NCH);
+        *reinterpret_cast<bf16x8*>(kt + r * D + 8 * pos) = hi;
+        if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(kt + kBN * D + r * D + 8 * pos) = lo;
+    }
+    for (int f = threadIdx.x; f < 8 * D; f += 256) {
+        const int d = f % D, p = f / D;
+        const int s4 = p >> 1, h = p & 1;
+        const float* src = v + (int64_t)k0 * row_stride + kv * D + d;
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int key = 16 * s4 + 8 * (e >> 2) + 4 * h + (e & 3);
+            x[e] = key < nval ? (__bf16)src[key * row_stride] : (__bf16)0.0f;
+        }
+        *reinterpret_cast<bf16x8*>(vt + d * kBN + 8 * swz(d, p, 8)) = x;
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __restrict__ q,
+                                                                const __bf16* __restrict__ ws,
+                                                                float* __restrict__ out,
+                                                                AttnSched sched, AttnGeom geom) {
+    constexpr int KP = SPLIT ? 2 : 1;
+    constexpr int NCH = D / 8;            // 16-byte chunks per K row
+    constexpr int KT = KP * kBN * D * 2;  // K tile bytes
+    constexpr int VT = kBN * D * 2;       // V tile bytes
+    constexpr int NQS = D / 16;           // MFMA steps of K Q^T
+    constexpr int NCB = D / 32;           // 32-row blocks of O^T
+    constexpr int QS = D + 4;             // f32 row stride of the epilogue staging
+    constexpr int K_LOADS = KT / (kThreads * 16);  // 16-byte direct loads per thread
+    constexpr int V_LOADS = VT / (kThreads * 16);
+    static_assert(K_LOADS >= 1 && V_LOADS >= 1 && KT % (kThreads * 16) == 0 &&
+                  VT % (kThreads * 16) == 0, "tiles are whole 8 KB workgroup loads");
+    constexpr int SMEM_TILES = 2 * KT + 2 * VT;
+    constexpr int SMEM_OUT = 4 * 32 * QS * 4;
+    __shared__ __attribute__((aligned(16)))
+    unsigned char smem[SMEM_TILES > SMEM_OUT ? SMEM_TILES : SMEM_OUT];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, hl = lane >> 5, ln = lane & 31;
+    const int lane = tid & 63, hl = lane >> 5, ln = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool grp_b = wave >= 4;
 
     const WorkItem wi = decode_item(sched, geom, blockIdx.x);
-    const int kv = wi.kv, chunk = wi.chunk, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
+    const int kv = wi.kv, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
+    const int causal = geom.causal, H = geom.H, Hkv = geom.Hkv;
+    const float qscale = geom.qscale;
+    const int n_all = sched.n_tiles, tile0 = sched.tile_off[wi.sid];
     const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
-    const int n_tiles =
-        geom.causal ? (min(q0 + sched.rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
+    const int n_tiles = causal ? (min(q0 + sched.rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
 
     const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;
-    const int h = kv * geom.g + chunk * geom.hpw + hloc;
+    const int h = kv * geom.g + wi.chunk * geom.hpw + hloc;
     const int wq0 = q0 + rblk * 32;
     const bool active = wq0 < s1;
-    const int wave_last = geom.causal ? min((wq0 + 31 - s0) / kBN, nt_seq - 1) : nt_seq - 1;
+    const int wave_last = causal ? min((wq0 + 31 - s0) / kBN, nt_seq - 1) : nt_seq - 1;
     const int qi = wq0 + ln;
 
-    // ---- Q operand (B of K Q^T): for step s (16 dims), lane (hl, ln) supplies
+    // ---- Q operand (B of K Q^T): for step s, lane (hl, ln) supplies
     // Q[qi][hl*D/2 + 8s + e], e = 0..7 -- the contraction order is free to permute.
     bf16x8 qop[NQS], qlo[SPLIT ? NQS : 1];
     {
         const bool ok = active && qi < s1;
-        const float* src = q + ((int64_t)(ok ? qi : s0) * geom.H + h) * D + hl * (D / 2);
+        const float* src = q + ((int64_t)(ok ? qi : s0) * H + h) * D + hl * (D / 2);
 #pragma unroll
         for (int s = 0; s < NQS; ++s) {
             floatx4 a = ok ? *reinterpret_cast<const floatx4*>(src + 8 * s) : floatx4{0, 0, 0, 0};
@@ -111,200 +204,216 @@ __global__ __launch_bounds__(64 * waves_for<D>(), (SPLIT || D == 128) ? 1 : 2) v
                            : floatx4{0, 0, 0, 0};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = (e < 4 ? a[e] : b[e - 4]) * geom.qscale;
+                const float x = (e < 4 ? a[e] : b[e - 4]) * qscale;
                 qop[s][e] = (__bf16)x;
-                // high part + low part = x to ~2^-17 relative
                 if constexpr (SPLIT) qlo[s][e] = (__bf16)(x - (float)qop[s][e]);
             }
         }
     }
 
-    // ---- staging helpers.  Each tile is read through a buffer resource that starts
-    // at the tile's first row of this K/V head and ends after the sequence's last
-    // row of it: rows past the end of the sequence read as zeros, with no branches.
-    // Per-thread byte offsets inside a tile are fixed.
-    floatx4 kreg[K_PER_THREAD];
-    floatx4 vreg[4 * V_BLK];
-    const int v_cg = tid % V_CG, v_kg = tid / V_CG;
-    const uint32_t row_bytes = (uint32_t)geom.Hkv * D * 4;  // bytes between tokens
-    uint32_t koff[K_PER_THREAD], voff[4 * V_BLK];
+    // ---- tile sources in the workspace and per-lane LDS read addresses
+    const unsigned char* kt_src =
+        reinterpret_cast<const unsigned char*>(ws) + ((int64_t)kv * n_all + tile0) * KT;
+    const unsigned char* vt_src = reinterpret_cast<const unsigned char*>(ws) +
+                                  (int64_t)Hkv * n_all * KT + ((int64_t)kv * n_all + tile0) * VT;
+    // K operand of step s, key block 0: row ln, chunk hl*NCH/2 + s (block 1: +32 rows)
+    uint32_t kaddr[NQS];
 #pragma unroll
-    for (int i = 0; i < K_PER_THREAD; ++i) {
-        const int f = tid + kThreads * i;
-        koff[i] = (f / KF4_ROW) * row_bytes + 16 * (f % KF4_ROW);
-    }
+    for (int s = 0; s < NQS; ++s) kaddr[s] = ln * (D * 2) + 16 * swz(ln, hl * (NCH / 2) + s, NCH);
+    // V^T operand of step s, row block 0: row ln, key group 2s + hl (block cb: +32cb rows)
+    uint32_t vaddr[4];
 #pragma unroll
-    for (int b = 0; b < V_BLK; ++b)
+    for (int s = 0; s < 4; ++s) vaddr[s] = 2 * KT + ln * (kBN * 2) + 16 * swz(ln, 2 * s + hl, 8);
+
+    // Direct-to-LDS copies: lane l of wavefront w moves bytes 16 (64 w + l) + 8192 i.
+    auto load_tiles = [&](int t) {
+        if (t + 1 < n_tiles) {
+            const unsigned char* src = kt_src + (int64_t)(t + 1) * KT + 16 * tid;
+            unsigned char* dst = smem + ((t + 1) & 1) * KT + 1024 * wave;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            voff[4 * b + e] = (4 * v_kg + KG_STRIDE * b + e) * row_bytes + 16 * v_cg;
-    auto tile_rsrc = [&](const float* base, int t) {
-        const int k0 = s0 + t * kBN;
-        const uint32_t bytes = (uint32_t)(s1 - k0 - 1) * row_bytes + D * 4;
-        return buffer_rsrc(base + ((int64_t)k0 * geom.Hkv + kv) * D, bytes);
-    };
-    auto load_k = [&](int t) {
-        const auto r = tile_rsrc(k, t);
+            for (int i = 0; i < K_LOADS; ++i)
+                __builtin_amdgcn_global_load_lds(src + 8192 * i, dst + 8192 * i, 16, 0, 0);
+        }
+        if (t < n_tiles) {
+            const unsigned char* src = vt_src + (int64_t)t * VT + 16 * tid;
+            unsigned char* dst = smem + 2 * KT + (t & 1) * VT + 1024 * wave;
 #pragma unroll
-        for (int i = 0; i < K_PER_THREAD; ++i) kreg[i] = buffer_load_f4(r, koff[i]);
-    };
-    auto store_k = [&](int buf) {
-        __bf16* ks = reinterpret_cast<__bf16*>(smem + buf * BUF);
-#pragma unroll
-        for (int i = 0; i < K_PER_THREAD; ++i) {
-            const int f = tid + kThreads * i;
-            const int row = f / KF4_ROW, c4 = f % KF4_ROW;
-            bf16x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (__bf16)kreg[i][e];
-            *reinterpret_cast<bf16x4*>(ks + row * KS + 4 * c4) = x;
-            if constexpr (SPLIT) {
-                bf16x4 y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = (__bf16)(kreg[i][e] - (float)x[e]);
-                *reinterpret_cast<bf16x4*>(ks + row * KS + D + 4 * c4) = y;
-            }
+            for (int i = 0; i < V_LOADS; ++i)
+                __builtin_amdgcn_global_load_lds(src + 8192 * i, dst + 8192 * i, 16, 0, 0);
         }
     };
-    auto load_v = [&](int t) {
-        const auto r = tile_rsrc(v, t);
-#pragma unroll
-        for (int i = 0; i < 4 * V_BLK; ++i) vreg[i] = buffer_load_f4(r, voff[i]);
-    };
-    auto store_v = [&](int buf) {
-        __bf16* vt = reinterpret_cast<__bf16*>(smem + buf * BUF + KBYTES);
-#pragma unroll
-        for (int b = 0; b < V_BLK; ++b) {
-            const int chunk = v_kg + V_KG * b;  // 4-key chunk index of this block
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int col = 4 * v_cg + c;
-                bf16x4 x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (__bf16)vreg[4 * b + e][c];
-                *reinterpret_cast<bf16x4*>(vt + col * VTS + 4 * (chunk ^ ((col >> 4) & 3))) = x;
-            }
-        }
-    };
+    auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    // Phase barrier: LDS reads done, then s_barrier.  Unlike __syncthreads() it
+    // does not wait for the direct-to-LDS loads in flight (vmcnt); those are
+    // waited for explicitly, one phase later.
+    auto phase_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
     floatx16 oacc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.0f;
+    floatx16 sacc[2];
+    bf16x8 pop[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pop[i][e] = (__bf16)0.0f;
     float m_run = -INFINITY;
     double l_run = 0.0;
 
-    load_k(0);
-    store_k(0);
-    load_v(0);
-    store_v(0);
-    __syncthreads();
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int cur = t & 1;
-        const bool more = t + 1 < n_tiles;
-        if (more) load_k(t + 1);
-        const bool work = active && t <= wave_last;
-        floatx16 sacc[2];
-        if (work) {
-            const __bf16* ks = reinterpret_cast<const __bf16*>(smem + cur * BUF);
-            // S^T for keys kb*32 + (0..31): A = K rows, B = Q^T; step s contracts
-            // dims hl*D/2 + 8s + (0..7) for lane half hl.
+    // M(t): P(t-1) V(t-1) into O, then S(t) = K(t) Q^T, as one stream of MFMAs
+    // whose LDS operands are read kAhead reads ahead.  It always runs whole: P is
+    // zero when there is nothing to add (before the first tile and past the
+    // wavefront's last one, whose stale K reads are discarded), and the V buffer
+    // read before the first tile is zeroed in the prologue.  PAR = t & 1.
+    auto m_phase = [&](auto par_) {
+        constexpr int PAR = decltype(par_)::value;
+        constexpr int NPV = 4 * NCB;        // P.V: step s = i / NCB, block cb = i % NCB
+        constexpr int NQK = 2 * NQS * KP;   // K.Q^T: step s, key block kb, part
+        constexpr int N = NPV + NQK;
+        constexpr int kAhead = 4;
+        const unsigned char* vb = smem + (PAR ^ 1) * VT;  // vaddr holds the V region offset
+        const unsigned char* kb_ = smem + PAR * KT;
+        auto rd = [&](int i) -> bf16x8 {
+            if (i < NPV)
+                return *reinterpret_cast<const bf16x8*>(vb + vaddr[i / NCB] +
+                                                        (i % NCB) * 32 * kBN * 2);
+            const int j = i - NPV;
+            const int part = j % KP, kb = (j / KP) % 2, s = j / (2 * KP);
+            return *reinterpret_cast<const bf16x8*>(kb_ + kaddr[s] + kb * 32 * D * 2 +
+                                                    part * kBN * D * 2);
+        };
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-                const __bf16* kp = ks + (kb * 32 + ln) * KS + hl * (D / 2);
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+        bf16x8 opnd[N];
 #pragma unroll
-                for (int s = 0; s < NQS; ++s) {
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + 8 * s);
-                    if constexpr (SPLIT) {
-                        // small cross terms first, then the high product
-                        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(kp + D + 8 * s);
-                        sacc[kb] = mfma_bf16(kl, qop[s], sacc[kb]);
-                        sacc[kb] = mfma_bf16(ka, qlo[s], sacc[kb]);
+        for (int i = 0; i < kAhead; ++i) opnd[i] = rd(i);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if (i + kAhead < N) opnd[i + kAhead] = rd(i + kAhead);
+            if (i < NPV) {
+                // step s contracts keys 16s + 8(e/4) + 4hl + e%4: P registers 8(s%2)+e
+                // of score block s/2, V^T key group 2s + hl
+                oacc[i % NCB] = mfma_bf16(opnd[i], pop[i / NCB], oacc[i % NCB]);
+            } else {
+                const int j = i - NPV;
+                const int part = j % KP, kb = (j / KP) % 2, s = j / (2 * KP);
+                if constexpr (SPLIT) {
+                    // per key block: the two small cross terms first, then the high product
+                    if (part == 1) {
+                        sacc[kb] = mfma_bf16(opnd[i], qop[s], sacc[kb]);
+                        sacc[kb] = mfma_bf16(opnd[i - 1], qlo[s], sacc[kb]);
+                        sacc[kb] = mfma_bf16(opnd[i - 1], qop[s], sacc[kb]);
                     }
-                    sacc[kb] = mfma_bf16(ka, qop[s], sacc[kb]);
+                } else {
+                    sacc[kb] = mfma_bf16(opnd[i], qop[s], sacc[kb]);
                 }
             }
         }
-        if (work) {
-            const int k0 = s0 + t * kBN;
-            // register r of block kb: key k0 + 32kb + 8(r/4) + 4hl + r%4.  A key is
-            // hidden when it lies past min(qi, s1-1) (causal) or past s1-1.
-            if ((geom.causal && k0 + kBN - 1 > wq0) || k0 + kBN > s1) {
-                const int lim = (geom.causal ? min(qi, s1 - 1) : s1 - 1) - (k0 + 4 * hl);
+        // issue order: kAhead reads, then each MFMA followed by the next read
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < N; ++i) {
+            const int nm = (i < NPV || !SPLIT) ? 1 : ((i - NPV) % KP == 1 ? 3 : 0);
+            if (nm == 1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (nm == 3) __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+            if (i + kAhead < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // X(t): scores of tile t -> P(t) (bf16, B-operand layout), running max and sum.
+    auto x_phase = [&](int t) {
+        if (t < 0 || t > wave_last) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
-            }
-            float mt = sacc[0][0];
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[1][r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            float psum = 0.0f;
-            bf16x8 pop[4];
+                for (int e = 0; e < 8; ++e) pop[i][e] = (__bf16)0.0f;
+            return;
+        }
+        const int k0 = s0 + t * kBN;
+        // register r of block kb: key k0 + 32kb + 8(r/4) + 4hl + r%4.  A key is
+        // hidden when it lies past min(qi, s1-1) (causal) or past s1-1.
+        if ((causal && k0 + kBN - 1 > wq0) || k0 + kBN > s1) {
+            const int lim = (causal ? min(qi, s1 - 1) : s1 - 1) - (k0 + 4 * hl);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
-                    psum += p;
-                    pop[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
-                }
-            l_run = l_run * (double)alpha + (double)psum;
-            // rescale O only if the max moved for some query of this wavefront
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-            }
-            if (more) {
-                store_k(cur ^ 1);
-                load_v(t + 1);
-            }
-            // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]; step s contracts
-            // keys 16s + 8(e/4) + 4hl + e%4 (e = 0..7), i.e. P registers 8(s%2)+e of
-            // score block s/2.  The A operand is two 4-key runs of V^T row d (the
-            // 4-key chunks of a row are XOR-swizzled with (d >> 4) & 3).
-            const __bf16* vt = reinterpret_cast<const __bf16*>(smem + cur * BUF + KBYTES);
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const int col = cb * 32 + ln;
-                const int sw = (col >> 4) & 3;  // the chunk swizzle of this V^T row
-                const __bf16* vrow = vt + col * VTS;
-                const int c_lo = hl ^ sw, c_hi = (2 + hl) ^ sw;  // chunks 4s+hl, 4s+2+hl
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + 16 * s + 4 * c_lo);
-                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + 16 * s + 4 * c_hi);
-                    const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    oacc[cb] = mfma_bf16(va, pop[s], oacc[cb]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else if (more) {
-            store_k(cur ^ 1);
-            load_v(t + 1);
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
         }
-        if (more) store_v(cur ^ 1);
-        __syncthreads();
+        float mt = max_halves(fmaxf(max16(sacc[0]), max16(sacc[1])));
+        // every processed tile shows each query at least one key, so mt is finite
+        const bool bump = mt > m_run + kLazyMax;
+        const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+        if (bump) m_run = mt;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                pop[2 * kb + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_run);
+        // the denominator sums the weights as rounded for the P.V product, so the
+        // output is a weighted mean of V with exactly the weights that were applied
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float ps[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2 pr = {pop[i][2 * e], pop[i][2 * e + 1]};
+                ps[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[e & 1], false);
+            }
+        l_run = l_run * (double)alpha + (double)(ps[0] + ps[1]);
+        if (__any(bump)) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+        }
+    };
+
+    // ---- prologue: K(0) in LDS, V buffer 1 (read by M(0) with P = 0) zeroed;
+    // group B runs one phase behind group A
+    for (int i = tid; i < VT / 16; i += kThreads)
+        *reinterpret_cast<floatx4*>(smem + 2 * KT + VT + 16 * i) = floatx4{0.f, 0.f, 0.f, 0.f};
+    load_tiles(-1);
+    wait_loads();
+    phase_barrier();
+    if (grp_b) {
+        load_tiles(0);
+        phase_barrier();
     }
+    // ---- main loop: per tile two phases, a barrier after each.  Loads of K(t+1)
+    // and V(t) are issued in global phase 2t (A: before M(t); B: before X(t-1),
+    // i.e. B issues tile t+1's loads before its X(t)) and waited for at the end of
+    // global phase 2t+1.
+    for (int t0 = 0; t0 <= n_tiles; t0 += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = t0 + u;
+            if (t > n_tiles) break;
+            if (!grp_b) load_tiles(t);
+            if (u == 0) m_phase(std::integral_constant<int, 0>{});
+            else m_phase(std::integral_constant<int, 1>{});
+            if (grp_b) wait_loads();
+            phase_barrier();
+            if (grp_b) load_tiles(t + 1);
+            x_phase(t);
+            if (!grp_b) wait_loads();
+            phase_barrier();
+        }
+    }
+    if (!grp_b) phase_barrier();
 
     // ---- epilogue: 1/l, transpose through LDS (four wavefronts at a time), coalesced rows
     const double l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = (float)(1.0 / l_tot);
 #pragma unroll
-    for (int round = 0; round < kWaves / 4; ++round) {
+    for (int round = 0; round < 2; ++round) {
         const bool mine = (wave >> 2) == round;
         float* os = reinterpret_cast<float*>(smem) + (wave & 3) * 32 * QS;
         if (mine && active) {
@@ -327,23 +436,29 @@ __global__ __launch_bounds__(64 * waves_for<D>(), (SPLIT || D == 128) ? 1 : 2) v
                 const int r = f / F4, c4 = f % F4;
                 const int row = wq0 + r;
                 if (row < s1)
-                    *reinterpret_cast<floatx4*>(out + ((int64_t)row * geom.H + h) * D + 4 * c4) =
+                    *reinterpret_cast<floatx4*>(out + ((int64_t)row * H + h) * D + 4 * c4) =
                         *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
             }
         }
-        if (round + 1 < kWaves / 4) __syncthreads();
+        if (round == 0) __syncthreads();
     }
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out,
+hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
                             int n_items, hipStream_t stream) {
-    const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(64 * (D == 128 ? 8 : 4));
-#define PFA_LAUNCH_BF16(DD, SS)                                                                  \
-    hipLaunchKernelGGL((attn_bf16_kernel<DD, SS>), grid, block, 0, stream, q, k, v, out, sched, \
-                       geom)
+    __bf16* w = static_cast<__bf16*>(ws);
+    const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
+    const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(kThreads);
+#define PFA_LAUNCH_BF16(DD, SS)                                                                 \
+    do {                                                                                        \
+        hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS>), sgrid, sblock, 0, stream, k, v, w,  \
+                           sched, geom.Hkv);                                                    \
+        hipLaunchKernelGGL((attn_bf16_kernel<DD, SS>), grid, block, 0, stream, q, w, out,      \
+                           sched, geom);                                                        \
+    } while (0)
     if (D == 128) {
         if (split_qk) PFA_LAUNCH_BF16(128, true);
         else PFA_LAUNCH_BF16(128, false);

@@ -130,7 +130,19 @@ int build_sched(const pfa::SeqTable& st, int rows_per_item, pfa::AttnSched& sc) 
         items += (kk + 1) * (top - next);
     }
     sc.seg_start[n_nonempty] = items;
+    // 64-key tiles of each sequence in the bf16 workspace
+    sc.tile_off[0] = 0;
+    for (int s = 0; s < st.n_seqs; ++s)
+        sc.tile_off[s + 1] =
+            sc.tile_off[s] + (st.off[s + 1] - st.off[s] + pfa::kBf16TileKeys - 1) /
+                                 pfa::kBf16TileKeys;
+    sc.n_tiles = sc.tile_off[st.n_seqs];
     return items;
+}
+
+// Upper bound of the bf16 tile count: sum over sequences of ceil(len / 64).
+long long tile_bound(int T, int n_seqs) {
+    return (long long)(T + pfa::kBf16TileKeys - 1) / pfa::kBf16TileKeys + std::max(n_seqs, 1);
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -145,7 +157,16 @@ extern "C" {
 
 const char* pfa_last_error(void) { return g_err; }
 
-const char* pfa_version(void) { return "pfa 0.2 (gfx950; f32 and bf16 MFMA attention)"; }
+const char* pfa_version(void) { return "pfa 0.3 (gfx950; f32 and bf16 MFMA attention)"; }
+
+size_t pfa_workspace_bytes(int T, int n_seqs, int n_head_kv, int head_dim, int precision) {
+    if (precision == PFA_PREC_F32) return 0;
+    if ((precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) || T < 0 ||
+        n_head_kv <= 0 || (head_dim != 64 && head_dim != 128) || n_seqs > PFA_MAX_SEQS)
+        return 0;
+    return pfa::bf16_workspace_bytes((int)tile_bound(T, n_seqs), n_head_kv, head_dim,
+                                     precision == PFA_PREC_BF16X3);
+}
 
 int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
                 const float* q_norm_w, const float* k_norm_w, const int32_t* seq_offsets,
@@ -177,7 +198,8 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
 static int attn_common(const float* q, const float* k, const float* v, float* out,
                        const int32_t* seq_offsets, int n_seqs, int T, int n_head, int n_head_kv,
                        int head_dim, float scale, int causal, int precision,
-                       const pfa::PrepParams* prep, void* stream) {
+                       const pfa::PrepParams* prep, void* workspace, size_t workspace_bytes,
+                       void* stream) {
     if (!std::isfinite(scale)) return fail(PFA_ERR_INVALID_ARG, "scale must be finite");
     if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3)
         return fail(PFA_ERR_INVALID_ARG,
@@ -196,8 +218,8 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
     int rc = build_seqs(seq_offsets, n_seqs, T, st);
     if (rc) return rc;
     pfa::AttnGeom geom;
-    // the bf16 kernel runs 8 wavefronts per workgroup at head_dim 128, else 4
-    const int waves = (precision != PFA_PREC_F32 && head_dim == 128) ? 8 : 4;
+    // the bf16 kernel runs 8 wavefronts per workgroup, the f32 one 4
+    const int waves = precision != PFA_PREC_F32 ? 8 : 4;
     choose_geometry(n_head, n_head_kv, scale, causal, waves, geom);
     pfa::AttnSched sched;
     const int items = build_sched(st, 32 * geom.rb, sched);
@@ -209,9 +231,21 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
             return fail(PFA_ERR_UNSUPPORTED,
                         "qk_prep_attn with PFA_PREC_BF16/BF16X3 is not implemented; call "
                         "qknorm_rope then gqa_prefill_attn with that precision");
-        return hip_status(pfa::launch_attn_bf16(q, k, v, out, sched, geom, head_dim,
-                                                precision == PFA_PREC_BF16X3, items,
-                                                (hipStream_t)stream),
+        const bool split = precision == PFA_PREC_BF16X3;
+        const size_t need = pfa::bf16_workspace_bytes(sched.n_tiles, n_head_kv, head_dim, split);
+        if (!workspace)
+            return fail(PFA_ERR_INVALID_ARG, "precision %d needs a workspace (%zu bytes)",
+                        precision, need);
+        if (workspace_bytes < need)
+            return fail(PFA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed",
+                        workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % 256)
+            return fail(PFA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+        if (overlaps(workspace, need, q, qb) || overlaps(workspace, need, k, kb) ||
+            overlaps(workspace, need, v, kb) || overlaps(workspace, need, out, qb))
+            return fail(PFA_ERR_INVALID_ARG, "workspace must not overlap the tensors");
+        return hip_status(pfa::launch_attn_bf16(q, k, v, out, workspace, sched, geom, head_dim,
+                                                split, items, (hipStream_t)stream),
                           "gqa_prefill_attn launch");
     }
     return hip_status(pfa::launch_attn_f32(q, k, v, out, sched, geom, head_dim, prep, items,
@@ -221,19 +255,20 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
 
 int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
                      const int32_t* seq_offsets, int n_seqs, int T, int n_head, int n_head_kv,
-                     int head_dim, float scale, int causal, int precision, void* stream) {
+                     int head_dim, float scale, int causal, int precision, void* workspace,
+                     size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     int rc = check_geometry(T, n_head, n_head_kv, head_dim);
     if (rc) return rc;
     return attn_common(q, k, v, out, seq_offsets, n_seqs, T, n_head, n_head_kv, head_dim, scale,
-                       causal, precision, nullptr, stream);
+                       causal, precision, nullptr, workspace, workspace_bytes, stream);
 }
 
 int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
                  const float* q_norm_w, const float* k_norm_w, const int32_t* seq_offsets,
                  int n_seqs, int T, int n_head, int n_head_kv, int head_dim, int rope_dim,
                  float rope_freq_base, float rms_eps, float scale, int causal, int precision,
-                 float* k_rot_out, void* stream) {
+                 float* k_rot_out, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     int rc = check_geometry(T, n_head, n_head_kv, head_dim);
     if (rc) return rc;
@@ -242,7 +277,7 @@ int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
     pfa::PrepParams prep{q_norm_w, k_norm_w, k_rot_out, rope_dim, rms_eps,
                          (double)rope_freq_base};
     return attn_common(q, k, v, out, seq_offsets, n_seqs, T, n_head, n_head_kv, head_dim, scale,
-                       causal, precision, &prep, stream);
+                       causal, precision, &prep, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -88,6 +88,7 @@ __device__ __forceinline__ int find_seq(const int* off, int n_seqs, int t) {
 // chunk of the group, and the sequence and query super-block it covers.
 struct WorkItem {
     int kv, chunk, sb;   // K/V head, head chunk, super-block index in the sequence
+    int sid;             // sequence index
     int s0, s1;          // sequence token range [s0, s1)
     int q0;              // first query row of the super-block
 };
@@ -108,6 +109,7 @@ __device__ __forceinline__ WorkItem decode_item(const Sched& sched, const Geom& 
     const int per = seg + 1;
     const int sid = sched.order[local % per];
     w.sb = sched.seg_top[seg] - 1 - local / per;
+    w.sid = sid;
     w.s0 = sched.off[sid];
     w.s1 = sched.off[sid + 1];
     w.q0 = w.s0 + w.sb * sched.rows_per_item;

@@ -34,6 +34,10 @@ struct AttnSched {
     int seg_start[PFA_MAX_SEQS + 1]; // first item of each segment; [n_segs] = item count
     int seg_top[PFA_MAX_SEQS];       // super-block count of the (k+1)-th longest sequence
     int32_t order[PFA_MAX_SEQS];     // sequence ids, most super-blocks first (32-bit: scalar loads)
+    // 64-key tiles of the bf16 workspace (see launch_attn_bf16): sequence s owns
+    // tiles tile_off[s] .. tile_off[s+1]-1 of each K/V head; n_tiles in all.
+    int n_tiles;
+    int tile_off[PFA_MAX_SEQS + 1];
 };
 
 // Geometry common to the attention launches.
@@ -70,7 +74,14 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
 
 // bf16-input / f32-accumulate attention on already-normalised Q/K.
 // split_qk: scores from bf16 high + low parts of Q and K (PFA_PREC_BF16X3).
-hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out,
+// Two kernels: K and V are first converted once into `ws` (bf16 tiles in the byte
+// image the attention kernel keeps in LDS), then the attention kernel copies those
+// tiles straight into LDS.  ws must hold bf16_workspace_bytes(...) bytes.
+constexpr int kBf16TileKeys = 64;
+inline size_t bf16_workspace_bytes(int n_tiles, int Hkv, int D, bool split_qk) {
+    return (size_t)n_tiles * Hkv * (split_qk ? 3 : 2) * kBf16TileKeys * D * 2;
+}
+hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
                             int n_items, hipStream_t stream);
 }  // namespace pfa

@@ -26,7 +26,8 @@ _PRECISIONS = {"f32": PRECISION_F32, "fp32": PRECISION_F32, "float32": PRECISION
                PRECISION_BF16X3: PRECISION_BF16X3}
 
 # Every symbol include/pfa.h declares.
-EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_last_error", "pfa_version")
+EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_workspace_bytes",
+           "pfa_last_error", "pfa_version")
 
 
 class PfaError(RuntimeError):
@@ -50,14 +51,17 @@ def lib() -> ctypes.CDLL:
                              "g.build()'` first (there is no fallback path)")
     L = ctypes.CDLL(LIB_PATH)
     vp, fp_ = ctypes.c_void_p, ctypes.c_void_p
-    i32, f32 = ctypes.c_int, ctypes.c_float
+    i32, f32, sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     L.qknorm_rope.restype = i32
-    L.gqa_prefill_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    L.gqa_prefill_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
+                                   vp, sz, vp]
     L.gqa_prefill_attn.restype = i32
     L.qk_prep_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
-                               f32, i32, i32, fp_, vp]
+                               f32, i32, i32, fp_, vp, sz, vp]
     L.qk_prep_attn.restype = i32
+    L.pfa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.pfa_workspace_bytes.restype = sz
     L.pfa_last_error.restype = ctypes.c_char_p
     L.pfa_last_error.argtypes = []
     L.pfa_version.restype = ctypes.c_char_p
@@ -129,6 +133,25 @@ def _prec(precision):
         raise ValueError(f"precision must be 'f32', 'bf16' or 'bf16x3', got {precision!r}") from None
 
 
+def workspace_bytes(T: int, n_seqs: int, n_head_kv: int, head_dim: int, precision="f32") -> int:
+    """Device workspace the attention calls need (``pfa_workspace_bytes``); 0 for f32."""
+    return int(lib().pfa_workspace_bytes(T, n_seqs, n_head_kv, head_dim, _prec(precision)))
+
+
+def _workspace(workspace, T, n_seqs, Hkv, head_dim, prec, device):
+    """(pointer, size) of the caller's workspace, or of a new one from torch's allocator."""
+    import torch
+    need = int(lib().pfa_workspace_bytes(T, max(n_seqs, 1), Hkv, head_dim, prec))
+    if need == 0:
+        return None, ctypes.c_void_p(0), 0
+    if workspace is None:
+        # torch's caching allocator hands out 512-byte aligned blocks
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    elif not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a GPU torch.Tensor")
+    return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
 def qknorm_rope(q, k, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
                 rope_freq_base: float, rms_eps: float,
                 seq_offsets: Optional[Sequence[int]] = None, q_out=None, k_out=None):
@@ -155,8 +178,11 @@ def qknorm_rope(q, k, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
 
 def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
                      causal: bool = True, precision="f32",
-                     seq_offsets: Optional[Sequence[int]] = None, out=None):
-    """Causal GQA attention (``gqa_prefill_attn`` in ``include/pfa.h``); returns ``out``."""
+                     seq_offsets: Optional[Sequence[int]] = None, out=None, workspace=None):
+    """Causal GQA attention (``gqa_prefill_attn`` in ``include/pfa.h``); returns ``out``.
+
+    The bf16 precisions use a device workspace: ``workspace`` (a GPU tensor of at
+    least :func:`workspace_bytes` bytes), else one taken from torch's allocator."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev_f32(t, n)
@@ -170,8 +196,10 @@ def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
     if scale is None:
         scale = head_dim ** -0.5
     offs, n_seqs, op = _offsets(seq_offsets, T)
+    prec = _prec(precision)
+    ws, wp, wn = _workspace(workspace, T, n_seqs, Hkv, head_dim, prec, q.device)
     _check(lib().gqa_prefill_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), op, n_seqs, T, H, Hkv,
-                                  head_dim, float(scale), 1 if causal else 0, _prec(precision),
+                                  head_dim, float(scale), 1 if causal else 0, prec, wp, wn,
                                   _stream(q)))
     return out
 
@@ -179,7 +207,8 @@ def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
 def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
                  rope_freq_base: float, rms_eps: float, scale: Optional[float] = None,
                  causal: bool = True, precision="f32",
-                 seq_offsets: Optional[Sequence[int]] = None, out=None, k_rot_out=None):
+                 seq_offsets: Optional[Sequence[int]] = None, out=None, k_rot_out=None,
+                 workspace=None):
     """Fused QK-norm + RoPE + causal GQA attention (``qk_prep_attn`` in ``include/pfa.h``).
 
     Returns ``out`` (and also writes ``k_rot_out`` when one is given)."""
@@ -200,8 +229,10 @@ def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
     if scale is None:
         scale = head_dim ** -0.5
     offs, n_seqs, op = _offsets(seq_offsets, T)
+    prec = _prec(precision)
+    ws, wp, wn = _workspace(workspace, T, n_seqs, Hkv, head_dim, prec, q.device)
     _check(lib().qk_prep_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(q_norm_w),
                               _ptr(k_norm_w), op, n_seqs, T, H, Hkv, head_dim, rope_dim,
                               float(rope_freq_base), float(rms_eps), float(scale),
-                              1 if causal else 0, _prec(precision), _ptr(k_rot_out), _stream(q)))
+                              1 if causal else 0, prec, _ptr(k_rot_out), wp, wn, _stream(q)))
     return out
