@@ -7,8 +7,10 @@ NeoX RoPE -> causal GQA attention -> O.  ``--path fused`` runs it as the single
 ``gqa_prefill_attn``.  The throughput is causal attention TFLOP/s: 4 * head_dim *
 n_head FLOPs per visible (query, key) pair, masked work not counted.
 
-Prints one JSON line.  ``roofline`` describes the attention kernel (HIP events
-around each of its launches on the stream it runs on, inside the timed region);
+Prints one JSON line.  ``roofline`` describes the attention call (HIP events
+around each gqa_prefill_attn / qk_prep_attn launch on the stream it runs on,
+inside the timed region; in the bf16 modes that call is the K/V staging kernel
+followed by the attention kernel, and the events bracket both);
 ``cpu_baseline`` is the f64 CPU oracle timed on a bounded sample of query rows
 of the same workload on this host.
 """
@@ -94,8 +96,12 @@ def cpu_baseline(w, x, target_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--spinup-ms", type=float, default=300.0,
+                    help="before the warmup steps, run untimed steps for this long so the GPU "
+                         "leaves its idle clock (it needs ~30 ms of load to reach its steady "
+                         "shader clock); the timed region is still exactly --steps steps")
     ap.add_argument("--workload", default="prefill_8192")
     ap.add_argument("--seq-len", type=int, default=0, help="override: one sequence of this length "
                                                            "with the 8B-like heads")
@@ -172,6 +178,10 @@ def main():
                 b.record(stream)
                 ev.append((a, b))
 
+    t_spin = time.perf_counter()
+    while (time.perf_counter() - t_spin) * 1e3 < args.spinup_ms:
+        step(False)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -187,13 +197,17 @@ def main():
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.precision]
     if args.precision != "f32":
-        kernel = f"attn_bf16_kernel<{w.head_dim},{'true' if args.precision == 'bf16x3' else 'false'}>"
+        # gqa_prefill_attn in the bf16 modes is two launches (the events bracket both):
+        # the K/V staging kernel, then the attention kernel
+        split = "true" if args.precision == "bf16x3" else "false"
+        kernel = f"stage_kv_bf16_kernel<{w.head_dim},{split}> + attn_bf16_kernel<{w.head_dim},{split}>"
     else:
         kernel = f"attn_f32_kernel<{w.head_dim},{'true' if args.path == 'fused' else 'false'}>"
     traffic = load_traffic(w.name, kernel, args.precision, args.path)
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "spinup_ms": args.spinup_ms,
+        "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": args.precision, "data": "synthetic (seeded N(0,1) Q/K/V, norm weights 1+N(0,0.1))",
         "config": {"workload": f"{w.name}: causal GQA prefill, T={w.T}, n_head={w.n_head}, "

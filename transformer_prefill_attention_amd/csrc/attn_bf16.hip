@@ -49,6 +49,7 @@ namespace pfa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBN = kBf16TileKeys;  // keys per tile (64)
@@ -106,6 +107,9 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
                                                             AttnSched sched, int Hkv) {
     constexpr int KP = SPLIT ? 2 : 1;
     constexpr int NCH = D / 8;
+    constexpr int VTS = kBN + 8;  // V^T row stride in LDS (bf16): 4-key runs stay 8-byte aligned
+    __shared__ __attribute__((aligned(16))) __bf16 vts[D * VTS];
+    const int tid = threadIdx.x;
     const int kv = blockIdx.x % Hkv;
     const int gt = blockIdx.x / Hkv;
     const int n_tiles = sched.n_tiles;
@@ -116,11 +120,36 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
     __bf16* kt = ws + ((int64_t)kv * n_tiles + gt) * (KP * kBN * D);
     __bf16* vt = ws + (int64_t)Hkv * n_tiles * (KP * kBN * D) +
                  ((int64_t)kv * n_tiles + gt) * (kBN * D);
-    for (int f = threadIdx.x; f < kBN * NCH; f += 256) {
+    const float* kin = k + (int64_t)k0 * row_stride + kv * D;
+    const float* vin = v + (int64_t)k0 * row_stride + kv * D;
+    // V: 4 keys x 4 dims per block, loaded as 4 float4 rows, written to LDS as four
+    // 4-key runs of V^T.  Block b: dims 4 (b % (D/4)) .., keys 4 (b / (D/4)) ..
+    constexpr int VB = kBN * D / 16;
+#pragma unroll
+    for (int i = 0; i < VB / 256; ++i) {
+        const int b = tid + 256 * i;
+        const int d0 = 4 * (b % (D / 4)), key0 = 4 * (b / (D / 4));
+        floatx4 r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r[e] = key0 + e < nval ? *reinterpret_cast<const floatx4*>(vin + (key0 + e) * row_stride + d0)
+                                   : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bf16x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (__bf16)r[e][c];
+            *reinterpret_cast<bf16x4*>(vts + (d0 + c) * VTS + key0) = x;
+        }
+    }
+    // K: 16-byte chunks (8 dims) of each row, converted and written to their swizzled place
+#pragma unroll
+    for (int i = 0; i < kBN * NCH / 256; ++i) {
+        const int f = tid + 256 * i;
         const int r = f / NCH, c = f % NCH;
         floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
         if (r < nval) {
-            const float* src = k + (k0 + r) * row_stride + kv * D + 8 * c;
+            const float* src = kin + r * row_stride + 8 * c;
             a = *reinterpret_cast<const floatx4*>(src);
             b = *reinterpret_cast<const floatx4*>(src + 4);
         }
@@ -135,16 +164,16 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
         *reinterpret_cast<bf16x8*>(kt + r * D + 8 * pos) = hi;
         if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(kt + kBN * D + r * D + 8 * pos) = lo;
     }
-    for (int f = threadIdx.x; f < 8 * D; f += 256) {
-        const int d = f % D, p = f / D;
-        const int s4 = p >> 1, h = p & 1;
-        const float* src = v + (int64_t)k0 * row_stride + kv * D + d;
-        bf16x8 x;
+    __syncthreads();
+    // V^T rows out: group p = 2s + h of row d is keys 16s + 4h + {0..3} then 16s + 8 + 4h + {0..3}
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int key = 16 * s4 + 8 * (e >> 2) + 4 * h + (e & 3);
-            x[e] = key < nval ? (__bf16)src[key * row_stride] : (__bf16)0.0f;
-        }
+    for (int i = 0; i < 8 * D / 256; ++i) {
+        const int f = tid + 256 * i;
+        const int d = f / 8, p = f % 8;
+        const int s4 = p >> 1, h = p & 1;
+        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(vts + d * VTS + 16 * s4 + 4 * h);
+        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vts + d * VTS + 16 * s4 + 8 + 4 * h);
+        const bf16x8 x = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         *reinterpret_cast<bf16x8*>(vt + d * kBN + 8 * swz(d, p, 8)) = x;
     }
 }
