@@ -36,6 +36,11 @@
 // denominator adds up the bf16-rounded weights (v_dot2 against ones), the same
 // numbers the P.V product uses.
 //
+// PREP = true is the fused entry (qk_prep_attn): the staging kernel RMS-normalises
+// and rotates each K row before converting it (and can copy the rotated rows out
+// for a cache), and the attention kernel does the same to its Q rows once, in its
+// prologue.  The normalised Q and K never go to HBM except for that optional copy.
+//
 // SPLIT = true is the PFA_PREC_BF16X3 mode: Q and K are each split into a bf16
 // high part and a bf16 low part (x = hi + lo to ~2^-17) and the scores take the
 // three products hi.hi + hi.lo + lo.hi, so score rounding no longer grows with
@@ -86,13 +91,20 @@ __device__ __forceinline__ float max16(const floatx16& x) {
     return max3(m, x[15], x[15]);
 }
 
-__device__ __forceinline__ float max_halves(float x) {
-    // v_permlane32_swap: lanes 0-31 and 32-63 exchange, so max(r[0], r[1]) is the
-    // max over the two lanes of one query
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                    __builtin_bit_cast(unsigned, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+// The value lane l ^ 32 holds.  v_permlane32_swap(a, b) leaves lanes 0-31 of a in
+// both halves of its first result and lanes 32-63 of b in both halves of its
+// second.  The second operand goes through an empty asm so that the compiler
+// cannot treat the two operands, and hence the two results, as one value (it
+// folds the second result into the first when both operands are the same value).
+__device__ __forceinline__ float other_half(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
+
+// max over the two lanes of one query (lanes l and l ^ 32)
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, other_half(x)); }
 
 // ---------------------------------------------------------------------------
 // K/V -> bf16 tiles.  Block = (K/V head, tile over all sequences).
@@ -100,15 +112,19 @@ __device__ __forceinline__ float max_halves(float x) {
 //  V tile: D rows x 64 keys; row d holds 8 groups of 8 keys, group p = 2s + h being
 //  keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3} (the keys lane half h feeds
 //  at P.V step s), group p stored at position swz(d, p, 8).
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool PREP>
 __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restrict__ k,
                                                             const float* __restrict__ v,
                                                             __bf16* __restrict__ ws,
-                                                            AttnSched sched, int Hkv) {
+                                                            AttnSched sched, int Hkv,
+                                                            PrepParams prep) {
     constexpr int KP = SPLIT ? 2 : 1;
     constexpr int NCH = D / 8;
     constexpr int VTS = kBN + 8;  // V^T row stride in LDS (bf16): 4-key runs stay 8-byte aligned
+    constexpr int KRS = D + 4;    // raw K row stride in LDS (f32), fused entry only
     __shared__ __attribute__((aligned(16))) __bf16 vts[D * VTS];
+    __shared__ __attribute__((aligned(16))) float kraw[PREP ? kBN * KRS : 4];
+    __shared__ double tpp[PREP ? D / 2 : 1];
     const int tid = threadIdx.x;
     const int kv = blockIdx.x % Hkv;
     const int gt = blockIdx.x / Hkv;
@@ -122,6 +138,18 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
                  ((int64_t)kv * n_tiles + gt) * (kBN * D);
     const float* kin = k + (int64_t)k0 * row_stride + kv * D;
     const float* vin = v + (int64_t)k0 * row_stride + kv * D;
+    // 8 dims (logical chunk c of row r) -> bf16 high (and low) parts at the swizzled place
+    auto store_k_chunk = [](__bf16* tile, int r, int c, const float* x) {
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hi[e] = (__bf16)x[e];
+            if constexpr (SPLIT) lo[e] = (__bf16)(x[e] - (float)hi[e]);
+        }
+        const int pos = swz(r, c, NCH);
+        *reinterpret_cast<bf16x8*>(tile + r * D + 8 * pos) = hi;
+        if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(tile + kBN * D + r * D + 8 * pos) = lo;
+    };
     // V: 4 keys x 4 dims per block, loaded as 4 float4 rows, written to LDS as four
     // 4-key runs of V^T.  Block b: dims 4 (b % (D/4)) .., keys 4 (b / (D/4)) ..
     constexpr int VB = kBN * D / 16;
@@ -142,27 +170,70 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
             *reinterpret_cast<bf16x4*>(vts + (d0 + c) * VTS + key0) = x;
         }
     }
-    // K: 16-byte chunks (8 dims) of each row, converted and written to their swizzled place
+    if constexpr (!PREP) {
+        // K: 16-byte chunks (8 dims) of each row, converted and written to their swizzled place
 #pragma unroll
-    for (int i = 0; i < kBN * NCH / 256; ++i) {
-        const int f = tid + 256 * i;
-        const int r = f / NCH, c = f % NCH;
-        floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-        if (r < nval) {
-            const float* src = kin + r * row_stride + 8 * c;
-            a = *reinterpret_cast<const floatx4*>(src);
-            b = *reinterpret_cast<const floatx4*>(src + 4);
-        }
-        bf16x8 hi, lo;
+        for (int i = 0; i < kBN * NCH / 256; ++i) {
+            const int f = tid + 256 * i;
+            const int r = f / NCH, c = f % NCH;
+            floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+            if (r < nval) {
+                const float* src = kin + r * row_stride + 8 * c;
+                a = *reinterpret_cast<const floatx4*>(src);
+                b = *reinterpret_cast<const floatx4*>(src + 4);
+            }
+            float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = e < 4 ? a[e] : b[e - 4];
-            hi[e] = (__bf16)x;
-            if constexpr (SPLIT) lo[e] = (__bf16)(x - (float)hi[e]);
+            for (int e = 0; e < 8; ++e) x[e] = e < 4 ? a[e] : b[e - 4];
+            store_k_chunk(kt, r, c, x);
         }
-        const int pos = swz(r, c, NCH);
-        *reinterpret_cast<bf16x8*>(kt + r * D + 8 * pos) = hi;
-        if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(kt + kBN * D + r * D + 8 * pos) = lo;
+    } else {
+        // Fused entry: RMS-normalise and rotate each K row on its way in.  Raw rows go to
+        // LDS; four threads per row then take D/4 dims each (rotation partners are read
+        // back from LDS, so any rope_dim works).  Rows past the sequence end are zeros.
+        const int n = prep.rope_dim, half = n >> 1;
+#pragma unroll
+        for (int i = 0; i < kBN * D / 4 / 256; ++i) {
+            const int f = tid + 256 * i;
+            const int r = f / (D / 4), c4 = f % (D / 4);
+            const floatx4 x = r < nval ? *reinterpret_cast<const floatx4*>(kin + r * row_stride + 4 * c4)
+                                       : floatx4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<floatx4*>(kraw + r * KRS + 4 * c4) = x;
+        }
+        if (tid < half) tpp[tid] = rope_turns_per_pos(tid, n, prep.base);
+        __syncthreads();
+        constexpr int DQ = D / 4;  // dims per thread
+        const int r = tid >> 2, c0 = (tid & 3) * DQ;
+        const float* xr = kraw + r * KRS;
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < DQ; ++i) ss += xr[c0 + i] * xr[c0 + i];
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        const float rs = 1.0f / sqrtf(ss * (1.0f / D) + prep.eps);
+        const int pos = k0 + r - sched.off[s];
+        float y[DQ];
+#pragma unroll
+        for (int i = 0; i < DQ; ++i) {
+            const int c = c0 + i;
+            float yc = xr[c] * rs * prep.wk[c];
+            if (c < n) {
+                const int j = c < half ? c : c - half, pc = c < half ? c + half : c - half;
+                const float yp = xr[pc] * rs * prep.wk[pc];
+                float cs, sn;
+                rope_cos_sin(pos, tpp[j], cs, sn);
+                yc = c < half ? yc * cs - yp * sn : yc * cs + yp * sn;
+            }
+            y[i] = r < nval ? yc : 0.0f;
+        }
+        if (prep.k_rot_out && r < nval) {
+            float* dst = prep.k_rot_out + (int64_t)(k0 + r) * row_stride + kv * D + c0;
+#pragma unroll
+            for (int i = 0; i < DQ; i += 4)
+                *reinterpret_cast<floatx4*>(dst + i) = floatx4{y[i], y[i + 1], y[i + 2], y[i + 3]};
+        }
+#pragma unroll
+        for (int cc = 0; cc < DQ / 8; ++cc) store_k_chunk(kt, r, c0 / 8 + cc, y + 8 * cc);
     }
     __syncthreads();
     // V^T rows out: group p = 2s + h of row d is keys 16s + 4h + {0..3} then 16s + 8 + 4h + {0..3}
@@ -179,11 +250,12 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool PREP>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __restrict__ q,
                                                                 const __bf16* __restrict__ ws,
                                                                 float* __restrict__ out,
-                                                                AttnSched sched, AttnGeom geom) {
+                                                                AttnSched sched, AttnGeom geom,
+                                                                PrepParams prep) {
     constexpr int KP = SPLIT ? 2 : 1;
     constexpr int NCH = D / 8;            // 16-byte chunks per K row
     constexpr int KT = KP * kBN * D * 2;  // K tile bytes
@@ -226,18 +298,75 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     {
         const bool ok = active && qi < s1;
         const float* src = q + ((int64_t)(ok ? qi : s0) * H + h) * D + hl * (D / 2);
+        float xq[NQS][8];
 #pragma unroll
         for (int s = 0; s < NQS; ++s) {
             floatx4 a = ok ? *reinterpret_cast<const floatx4*>(src + 8 * s) : floatx4{0, 0, 0, 0};
             floatx4 b = ok ? *reinterpret_cast<const floatx4*>(src + 8 * s + 4)
                            : floatx4{0, 0, 0, 0};
 #pragma unroll
+            for (int e = 0; e < 8; ++e) xq[s][e] = e < 4 ? a[e] : b[e - 4];
+        }
+        if constexpr (PREP) {
+            // Fused entry: RMS-normalise and rotate the wavefront's 32 Q rows once.  The
+            // two lanes of a row hold half of it each; the rotation partners come back
+            // through LDS (four wavefronts at a time), so any rope_dim works.
+            __shared__ double qtpp[D / 2];
+            const int n = prep.rope_dim, half = n >> 1;
+            if (tid < half) qtpp[tid] = rope_turns_per_pos(tid, n, prep.base);
+            float ss = 0.0f;
+#pragma unroll
+            for (int s = 0; s < NQS; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += xq[s][e] * xq[s][e];
+            ss += other_half(ss);
+            const float rs = 1.0f / sqrtf(ss * (1.0f / D) + prep.eps);
+#pragma unroll
+            for (int s = 0; s < NQS; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    xq[s][e] = ok ? xq[s][e] * rs * prep.wq[hl * (D / 2) + 8 * s + e] : 0.0f;
+            const int pos = qi - s0;
+            float* qs = reinterpret_cast<float*>(smem) + (wave & 3) * 32 * QS + ln * QS;
+#pragma unroll
+            for (int round = 0; round < 2; ++round) {
+                const bool mine = (wave >> 2) == round;
+                if (mine) {
+#pragma unroll
+                    for (int s = 0; s < NQS; ++s) {
+                        *reinterpret_cast<floatx4*>(qs + hl * (D / 2) + 8 * s) =
+                            floatx4{xq[s][0], xq[s][1], xq[s][2], xq[s][3]};
+                        *reinterpret_cast<floatx4*>(qs + hl * (D / 2) + 8 * s + 4) =
+                            floatx4{xq[s][4], xq[s][5], xq[s][6], xq[s][7]};
+                    }
+                }
+                __syncthreads();
+                if (mine) {
+#pragma unroll
+                    for (int s = 0; s < NQS; ++s)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int c = hl * (D / 2) + 8 * s + e;
+                            if (c < n) {
+                                const int j = c < half ? c : c - half;
+                                const float yp = qs[c < half ? c + half : c - half];
+                                float cs, sn;
+                                rope_cos_sin(pos, qtpp[j], cs, sn);
+                                xq[s][e] = c < half ? xq[s][e] * cs - yp * sn : xq[s][e] * cs + yp * sn;
+                            }
+                        }
+                }
+                __syncthreads();
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < NQS; ++s)
+#pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = (e < 4 ? a[e] : b[e - 4]) * qscale;
+                const float x = xq[s][e] * qscale;
                 qop[s][e] = (__bf16)x;
                 if constexpr (SPLIT) qlo[s][e] = (__bf16)(x - (float)qop[s][e]);
             }
-        }
     }
 
     // ---- tile sources in the workspace and per-lane LDS read addresses
@@ -477,24 +606,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
-                            int n_items, hipStream_t stream) {
+                            const PrepParams* prep, int n_items, hipStream_t stream) {
     __bf16* w = static_cast<__bf16*>(ws);
+    const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
     const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
     const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(kThreads);
-#define PFA_LAUNCH_BF16(DD, SS)                                                                 \
+#define PFA_LAUNCH_BF16(DD, SS, PP)                                                             \
     do {                                                                                        \
-        hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS>), sgrid, sblock, 0, stream, k, v, w,  \
-                           sched, geom.Hkv);                                                    \
-        hipLaunchKernelGGL((attn_bf16_kernel<DD, SS>), grid, block, 0, stream, q, w, out,      \
-                           sched, geom);                                                        \
+        hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, PP>), sgrid, sblock, 0, stream, k, v, \
+                           w, sched, geom.Hkv, p);                                              \
+        hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP>), grid, block, 0, stream, q, w, out,  \
+                           sched, geom, p);                                                     \
+    } while (0)
+#define PFA_LAUNCH_BF16_P(DD, SS)                   \
+    do {                                            \
+        if (prep) PFA_LAUNCH_BF16(DD, SS, true);    \
+        else PFA_LAUNCH_BF16(DD, SS, false);        \
     } while (0)
     if (D == 128) {
-        if (split_qk) PFA_LAUNCH_BF16(128, true);
-        else PFA_LAUNCH_BF16(128, false);
+        if (split_qk) PFA_LAUNCH_BF16_P(128, true);
+        else PFA_LAUNCH_BF16_P(128, false);
     } else {
-        if (split_qk) PFA_LAUNCH_BF16(64, true);
-        else PFA_LAUNCH_BF16(64, false);
+        if (split_qk) PFA_LAUNCH_BF16_P(64, true);
+        else PFA_LAUNCH_BF16_P(64, false);
     }
+#undef PFA_LAUNCH_BF16_P
 #undef PFA_LAUNCH_BF16
     return hipGetLastError();
 }

@@ -227,10 +227,6 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
     if ((long long)items * geom.chunks * geom.Hkv >= (1LL << 31))
         return fail(PFA_ERR_UNSUPPORTED, "grid too large");
     if (precision != PFA_PREC_F32) {
-        if (prep)
-            return fail(PFA_ERR_UNSUPPORTED,
-                        "qk_prep_attn with PFA_PREC_BF16/BF16X3 is not implemented; call "
-                        "qknorm_rope then gqa_prefill_attn with that precision");
         const bool split = precision == PFA_PREC_BF16X3;
         const size_t need = pfa::bf16_workspace_bytes(sched.n_tiles, n_head_kv, head_dim, split);
         if (!workspace)
@@ -242,11 +238,12 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
         if (reinterpret_cast<uintptr_t>(workspace) % 256)
             return fail(PFA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
         if (overlaps(workspace, need, q, qb) || overlaps(workspace, need, k, kb) ||
-            overlaps(workspace, need, v, kb) || overlaps(workspace, need, out, qb))
+            overlaps(workspace, need, v, kb) || overlaps(workspace, need, out, qb) ||
+            (prep && prep->k_rot_out && overlaps(workspace, need, prep->k_rot_out, kb)))
             return fail(PFA_ERR_INVALID_ARG, "workspace must not overlap the tensors");
         return hip_status(pfa::launch_attn_bf16(q, k, v, out, workspace, sched, geom, head_dim,
-                                                split, items, (hipStream_t)stream),
-                          "gqa_prefill_attn launch");
+                                                split, prep, items, (hipStream_t)stream),
+                          prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
     }
     return hip_status(pfa::launch_attn_f32(q, k, v, out, sched, geom, head_dim, prep, items,
                                            (hipStream_t)stream),

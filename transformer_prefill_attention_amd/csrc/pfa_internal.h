@@ -72,7 +72,7 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
                            const AttnSched& sched, const AttnGeom& geom, int D,
                            const PrepParams* prep, int n_items, hipStream_t stream);
 
-// bf16-input / f32-accumulate attention on already-normalised Q/K.
+// bf16-input / f32-accumulate attention.
 // split_qk: scores from bf16 high + low parts of Q and K (PFA_PREC_BF16X3).
 // Two kernels: K and V are first converted once into `ws` (bf16 tiles in the byte
 // image the attention kernel keeps in LDS), then the attention kernel copies those
@@ -81,7 +81,8 @@ constexpr int kBf16TileKeys = 64;
 inline size_t bf16_workspace_bytes(int n_tiles, int Hkv, int D, bool split_qk) {
     return (size_t)n_tiles * Hkv * (split_qk ? 3 : 2) * kBf16TileKeys * D * 2;
 }
+// prep != nullptr: the fused entry (K and Q normalised and rotated on the way in).
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
-                            int n_items, hipStream_t stream);
+                            const PrepParams* prep, int n_items, hipStream_t stream);
 }  // namespace pfa
