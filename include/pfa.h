@@ -67,10 +67,13 @@ typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_pr
 /* Device workspace in bytes that gqa_prefill_attn / qk_prep_attn need at this
  * size and precision: 0 for PFA_PREC_F32; for the bf16 modes, K and V converted
  * once to bf16 in 64-key tiles per sequence (K twice, high and low parts, for
- * PFA_PREC_BF16X3):
+ * PFA_PREC_BF16X3), plus qk_prep_attn's rotary table ((cos, sin) f32 pairs per
+ * position and pair):
  *   n_head_kv * (ceil(T / 64) + max(n_seqs, 1)) * 64 * head_dim * 2 * (2 or 3)
- * bytes.  n_seqs is the count passed with seq_offsets (1 when that is NULL).
- * Returns 0 for arguments the attention calls would reject. */
+ *   + T * (head_dim / 2) * 8
+ * bytes, enough for either entry point.  n_seqs is the count passed with
+ * seq_offsets (1 when that is NULL).  Returns 0 for arguments the attention
+ * calls would reject. */
 size_t pfa_workspace_bytes(int T, int n_seqs, int n_head_kv, int head_dim, int precision);
 
 /*

@@ -142,12 +142,14 @@ def _tiles(T, n_seqs):
 @pytest.mark.parametrize("T,n_seqs,Hkv,D", [(16, 0, 2, 64), (8192, 1, 8, 128), (16064, 8, 4, 64),
                                            (1, 128, 1, 128)])
 def test_workspace_bytes_formula(L, T, n_seqs, Hkv, D):
-    # the documented bound: K and V as bf16 in 64-key tiles (K twice for bf16x3)
+    # the documented bound: K and V as bf16 in 64-key tiles (K twice for bf16x3), plus
+    # the fused entry's rotary table of T x head_dim/2 (cos, sin) f32 pairs
     per_part = Hkv * _tiles(T, n_seqs) * 64 * D * 2
+    table = T * (D // 2) * 8
     assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 0) == 0
-    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 1) == 2 * per_part
-    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 2) == 3 * per_part
-    assert pfa.workspace_bytes(T, n_seqs, Hkv, D, "bf16x3") == 3 * per_part
+    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 1) == 2 * per_part + table
+    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 2) == 3 * per_part + table
+    assert pfa.workspace_bytes(T, n_seqs, Hkv, D, "bf16x3") == 3 * per_part + table
 
 
 def test_workspace_bytes_rejects_what_attention_rejects(L):

@@ -64,6 +64,9 @@ SMALL = [
     wl.Workload("g8", (70, 41), 16, 2, 128, 64, 1e4, 1e-6, seed=14),
     wl.Workload("g3", (90,), 6, 2, 64, 64, 1e6, 1e-6, seed=15),
     wl.Workload("d64_g4", (31, 257), 8, 2, 64, 32, 1e6, 1e-6, seed=16, scale=0.125),
+    # a rope_dim that is neither head_dim nor head_dim/2 (the kernels' general pairing)
+    wl.Workload("rope96", (150, 70), 8, 2, 128, 96, 1e4, 1e-6, seed=17),
+    wl.Workload("d64_rope48", (99,), 4, 2, 64, 48, 1e6, 1e-6, seed=18),
 ]
 
 
@@ -353,10 +356,10 @@ def test_row_max_covers_both_lane_halves(gpu_device, precision):
     ref = _attn_ref(w, x)
     if precision == "f32":
         # scores ~100x those of the workloads: f32 score rounding grows with them, so this
-        # stress case gets 1e-4 rather than the workloads' 2e-5
+        # stress case gets 1e-4 (max abs and relative L2) rather than the workloads. gates
         max_abs, rel = errors(got, ref)
         print(f"row max over both halves f32: max|err| {max_abs:.3e} rel L2 {rel:.3e}", flush=True)
-        assert max_abs <= 1e-4 and rel <= 1e-5
+        assert max_abs <= 1e-4 and rel <= 1e-4
     else:
         # the scores are ~200 (natural units): bf16 inputs move them by ~1, so compare
         # against the oracle on the rounded inputs (what the bf16 modes promise)

@@ -106,6 +106,33 @@ __device__ __forceinline__ float other_half(float x) {
 // max over the two lanes of one query (lanes l and l ^ 32)
 __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, other_half(x)); }
 
+// Rotary table of the fused entry, after the K and V tiles in the workspace:
+// (cos, sin) of position p and pair j at p * D/2 + j (pairs j >= rope_dim/2 unused).
+template <int D, bool SPLIT>
+__device__ __forceinline__ const float2* rope_table(const __bf16* ws, int Hkv, int n_tiles) {
+    constexpr int KP = SPLIT ? 2 : 1;
+    return reinterpret_cast<const float2*>(ws + (int64_t)Hkv * n_tiles * (KP + 1) * kBN * D);
+}
+
+// One entry per (position < rows, pair j < D/2), angle reduced in f64 (rope_cos_sin).
+// A block covers kTabRows positions; thread t owns pair t % (D/2) (one pow each).
+constexpr int kTabRows = 64;
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(256) void rope_table_kernel(__bf16* ws, int Hkv, int n_tiles,
+                                                         int rows, int n, double base) {
+    float2* tab = const_cast<float2*>(rope_table<D, SPLIT>(ws, Hkv, n_tiles));
+    constexpr int RPP = 256 / (D / 2);  // positions per pass
+    const int j = threadIdx.x % (D / 2);
+    const bool rot = 2 * j < n;
+    const double turns = rot ? rope_turns_per_pos(j, n, base) : 0.0;
+    const int p_end = min(rows, (int)(blockIdx.x + 1) * kTabRows);
+    for (int pos = blockIdx.x * kTabRows + threadIdx.x / (D / 2); pos < p_end; pos += RPP) {
+        float c = 1.0f, sn = 0.0f;
+        if (rot) rope_cos_sin(pos, turns, c, sn);
+        tab[(int64_t)pos * (D / 2) + j] = float2{c, sn};
+    }
+}
+
 // ---------------------------------------------------------------------------
 // K/V -> bf16 tiles.  Block = (K/V head, tile over all sequences).
 //  K tile: KP parts (high, low) x 64 rows x D; element (r, c) at r*D + 8*swz(r, c/8, D/8) + c%8.
@@ -124,7 +151,6 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
     constexpr int KRS = D + 4;    // raw K row stride in LDS (f32), fused entry only
     __shared__ __attribute__((aligned(16))) __bf16 vts[D * VTS];
     __shared__ __attribute__((aligned(16))) float kraw[PREP ? kBN * KRS : 4];
-    __shared__ double tpp[PREP ? D / 2 : 1];
     const int tid = threadIdx.x;
     const int kv = blockIdx.x % Hkv;
     const int gt = blockIdx.x / Hkv;
@@ -188,45 +214,72 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
             store_k_chunk(kt, r, c, x);
         }
     } else {
-        // Fused entry: RMS-normalise and rotate each K row on its way in.  Raw rows go to
-        // LDS; four threads per row then take D/4 dims each (rotation partners are read
-        // back from LDS, so any rope_dim works).  Rows past the sequence end are zeros.
+        // Fused entry: RMS-normalise and rotate each K row on its way in.  Four threads
+        // per row take D/4 consecutive dims each.  A rotation partner (dim c +- n/2) sits
+        // in the quarter two apart when n = D and one apart when n = D/2 (DPP quad
+        // permutations); any other rope_dim goes through LDS.  Rows past the sequence
+        // end are zeros.
         const int n = prep.rope_dim, half = n >> 1;
-#pragma unroll
-        for (int i = 0; i < kBN * D / 4 / 256; ++i) {
-            const int f = tid + 256 * i;
-            const int r = f / (D / 4), c4 = f % (D / 4);
-            const floatx4 x = r < nval ? *reinterpret_cast<const floatx4*>(kin + r * row_stride + 4 * c4)
-                                       : floatx4{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<floatx4*>(kraw + r * KRS + 4 * c4) = x;
-        }
-        if (tid < half) tpp[tid] = rope_turns_per_pos(tid, n, prep.base);
-        __syncthreads();
+        const float2* tab = rope_table<D, SPLIT>(ws, Hkv, n_tiles);
         constexpr int DQ = D / 4;  // dims per thread
-        const int r = tid >> 2, c0 = (tid & 3) * DQ;
-        const float* xr = kraw + r * KRS;
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < DQ; ++i) ss += xr[c0 + i] * xr[c0 + i];
-        ss += __shfl_xor(ss, 1, 64);
-        ss += __shfl_xor(ss, 2, 64);
-        const float rs = 1.0f / sqrtf(ss * (1.0f / D) + prep.eps);
-        const int pos = k0 + r - sched.off[s];
+        const int r = tid >> 2, qd = tid & 3, c0 = qd * DQ;
+        const bool valid = r < nval;
+        const int pos = valid ? k0 + r - sched.off[s] : 0;  // rows past the end: any valid entry
         float y[DQ];
 #pragma unroll
-        for (int i = 0; i < DQ; ++i) {
-            const int c = c0 + i;
-            float yc = xr[c] * rs * prep.wk[c];
-            if (c < n) {
-                const int j = c < half ? c : c - half, pc = c < half ? c + half : c - half;
-                const float yp = xr[pc] * rs * prep.wk[pc];
-                float cs, sn;
-                rope_cos_sin(pos, tpp[j], cs, sn);
-                yc = c < half ? yc * cs - yp * sn : yc * cs + yp * sn;
-            }
-            y[i] = r < nval ? yc : 0.0f;
+        for (int i = 0; i < DQ; i += 4) {
+            const floatx4 x = valid ? *reinterpret_cast<const floatx4*>(kin + r * row_stride + c0 + i)
+                                    : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[i + e] = x[e];
         }
-        if (prep.k_rot_out && r < nval) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < DQ; ++i) ss += y[i] * y[i];
+        ss += dpp_f32<0xB1>(ss);  // quad_perm [1,0,3,2]
+        ss += dpp_f32<0x4E>(ss);  // quad_perm [2,3,0,1]
+        const float rs = 1.0f / sqrtf(ss * (1.0f / D) + prep.eps);
+#pragma unroll
+        for (int i = 0; i < DQ; i += 4) {
+            const floatx4 w = *reinterpret_cast<const floatx4*>(prep.wk + c0 + i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[i + e] *= rs * w[e];
+        }
+        const float2* trow = tab + pos * (D / 2);
+        if (n == D || n == D / 2) {
+            // partner quarter: qd ^ 2 (n = D) or qd ^ 1 (n = D/2, quarters 0 and 1 only)
+            const bool full = n == D;
+            const bool first = full ? qd < 2 : qd == 0;  // holds the pair's first dims
+            const bool rot = full || qd < 2;
+            const float2* tj = trow + (full ? (qd & 1) * DQ : 0);
+#pragma unroll
+            for (int i = 0; i < DQ; ++i) {
+                const float yp = full ? dpp_f32<0x4E>(y[i]) : dpp_f32<0xB1>(y[i]);
+                const float2 t = tj[i];
+                const float yr = first ? y[i] * t.x - yp * t.y : y[i] * t.x + yp * t.y;
+                y[i] = rot ? yr : y[i];
+            }
+        } else {
+            __syncthreads();  // (uniform: n is a kernel argument)
+            float* xr = kraw + r * KRS;
+#pragma unroll
+            for (int i = 0; i < DQ; i += 4)
+                *reinterpret_cast<floatx4*>(xr + c0 + i) = floatx4{y[i], y[i + 1], y[i + 2], y[i + 3]};
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < DQ; ++i) {
+                const int c = c0 + i;
+                if (c < n) {
+                    const int j = c < half ? c : c - half;
+                    const float yp = xr[c < half ? c + half : c - half];
+                    const float2 t = trow[j];
+                    y[i] = c < half ? y[i] * t.x - yp * t.y : y[i] * t.x + yp * t.y;
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < DQ; ++i) y[i] = valid ? y[i] : 0.0f;
+        if (prep.k_rot_out && valid) {
             float* dst = prep.k_rot_out + (int64_t)(k0 + r) * row_stride + kv * D + c0;
 #pragma unroll
             for (int i = 0; i < DQ; i += 4)
@@ -309,11 +362,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
         }
         if constexpr (PREP) {
             // Fused entry: RMS-normalise and rotate the wavefront's 32 Q rows once.  The
-            // two lanes of a row hold half of it each; the rotation partners come back
-            // through LDS (four wavefronts at a time), so any rope_dim works.
-            __shared__ double qtpp[D / 2];
+            // two lanes of a row hold half of it each.
             const int n = prep.rope_dim, half = n >> 1;
-            if (tid < half) qtpp[tid] = rope_turns_per_pos(tid, n, prep.base);
+            const float2* tab = rope_table<D, SPLIT>(ws, Hkv, n_all);
             float ss = 0.0f;
 #pragma unroll
             for (int s = 0; s < NQS; ++s)
@@ -326,37 +377,74 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     xq[s][e] = ok ? xq[s][e] * rs * prep.wq[hl * (D / 2) + 8 * s + e] : 0.0f;
-            const int pos = qi - s0;
-            float* qs = reinterpret_cast<float*>(smem) + (wave & 3) * 32 * QS + ln * QS;
+            const int pos = ok ? qi - s0 : 0;  // rows past the end: any valid table entry
+            const float2* trow = tab + pos * (D / 2);
+            if (n == D) {
+                // dim c pairs with c +- D/2: the same register of the other lane half.
+                // Registers are exchanged two at a time: swap(a, b) hands lanes 0-31
+                // the upper half of a and lanes 32-63 the lower half of b, swap(b, a)
+                // the other two, so each lane receives its partner of both.
 #pragma unroll
-            for (int round = 0; round < 2; ++round) {
-                const bool mine = (wave >> 2) == round;
-                if (mine) {
+                for (int s = 0; s < NQS; ++s)
 #pragma unroll
-                    for (int s = 0; s < NQS; ++s) {
-                        *reinterpret_cast<floatx4*>(qs + hl * (D / 2) + 8 * s) =
-                            floatx4{xq[s][0], xq[s][1], xq[s][2], xq[s][3]};
-                        *reinterpret_cast<floatx4*>(qs + hl * (D / 2) + 8 * s + 4) =
-                            floatx4{xq[s][4], xq[s][5], xq[s][6], xq[s][7]};
+                    for (int e = 0; e < 8; e += 2) {
+                        const unsigned a = __builtin_bit_cast(unsigned, xq[s][e]);
+                        const unsigned b = __builtin_bit_cast(unsigned, xq[s][e + 1]);
+                        const auto ab = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+                        const auto ba = __builtin_amdgcn_permlane32_swap(b, a, false, false);
+                        const float pa = __builtin_bit_cast(float, hl ? ba[0] : ab[1]);
+                        const float pb = __builtin_bit_cast(float, hl ? ab[0] : ba[1]);
+                        const float sg = hl ? 1.0f : -1.0f;
+                        const float2 ta = trow[8 * s + e], tb = trow[8 * s + e + 1];
+                        xq[s][e] = xq[s][e] * ta.x + sg * pa * ta.y;
+                        xq[s][e + 1] = xq[s][e + 1] * tb.x + sg * pb * tb.y;
                     }
-                }
-                __syncthreads();
-                if (mine) {
+            } else if (n == D / 2) {
+                // dims c < D/2 (lane half 0) pair with c + D/4: register step s + NQS/2
+                if (hl == 0) {
 #pragma unroll
-                    for (int s = 0; s < NQS; ++s)
+                    for (int s = 0; s < NQS / 2; ++s)
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const int c = hl * (D / 2) + 8 * s + e;
-                            if (c < n) {
-                                const int j = c < half ? c : c - half;
-                                const float yp = qs[c < half ? c + half : c - half];
-                                float cs, sn;
-                                rope_cos_sin(pos, qtpp[j], cs, sn);
-                                xq[s][e] = c < half ? xq[s][e] * cs - yp * sn : xq[s][e] * cs + yp * sn;
-                            }
+                            const float a = xq[s][e], b = xq[s + NQS / 2][e];
+                            const float2 t = trow[8 * s + e];
+                            xq[s][e] = a * t.x - b * t.y;
+                            xq[s + NQS / 2][e] = a * t.y + b * t.x;
                         }
                 }
-                __syncthreads();
+            } else {
+                // any other rope_dim: partners through LDS, four wavefronts at a time
+                float* qs = reinterpret_cast<float*>(smem) + (wave & 3) * 32 * QS + ln * QS;
+#pragma unroll
+                for (int round = 0; round < 2; ++round) {
+                    const bool mine = (wave >> 2) == round;
+                    if (mine) {
+#pragma unroll
+                        for (int s = 0; s < NQS; ++s) {
+                            *reinterpret_cast<floatx4*>(qs + hl * (D / 2) + 8 * s) =
+                                floatx4{xq[s][0], xq[s][1], xq[s][2], xq[s][3]};
+                            *reinterpret_cast<floatx4*>(qs + hl * (D / 2) + 8 * s + 4) =
+                                floatx4{xq[s][4], xq[s][5], xq[s][6], xq[s][7]};
+                        }
+                    }
+                    __syncthreads();
+                    if (mine) {
+#pragma unroll
+                        for (int s = 0; s < NQS; ++s)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const int c = hl * (D / 2) + 8 * s + e;
+                                if (c < n) {
+                                    const int j = c < half ? c : c - half;
+                                    const float yp = qs[c < half ? c + half : c - half];
+                                    const float2 t = trow[j];
+                                    xq[s][e] = c < half ? xq[s][e] * t.x - yp * t.y
+                                                        : xq[s][e] * t.x + yp * t.y;
+                                }
+                            }
+                    }
+                    __syncthreads();
+                }
             }
         }
 #pragma unroll
@@ -611,8 +699,12 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
     const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
     const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(kThreads);
+    const dim3 tgrid((unsigned)((sched.max_len + kTabRows - 1) / kTabRows)), tblock(256);
 #define PFA_LAUNCH_BF16(DD, SS, PP)                                                             \
     do {                                                                                        \
+        if (PP)                                                                                 \
+            hipLaunchKernelGGL((rope_table_kernel<DD, SS>), tgrid, tblock, 0, stream, w,      \
+                               geom.Hkv, sched.n_tiles, sched.max_len, p.rope_dim, p.base);    \
         hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, PP>), sgrid, sblock, 0, stream, k, v, \
                            w, sched, geom.Hkv, p);                                              \
         hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP>), grid, block, 0, stream, q, w, out,  \

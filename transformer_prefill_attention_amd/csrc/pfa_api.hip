@@ -137,6 +137,8 @@ int build_sched(const pfa::SeqTable& st, int rows_per_item, pfa::AttnSched& sc) 
             sc.tile_off[s] + (st.off[s + 1] - st.off[s] + pfa::kBf16TileKeys - 1) /
                                  pfa::kBf16TileKeys;
     sc.n_tiles = sc.tile_off[st.n_seqs];
+    sc.max_len = 0;
+    for (int s = 0; s < st.n_seqs; ++s) sc.max_len = std::max(sc.max_len, st.off[s + 1] - st.off[s]);
     return items;
 }
 
@@ -165,7 +167,7 @@ size_t pfa_workspace_bytes(int T, int n_seqs, int n_head_kv, int head_dim, int p
         n_head_kv <= 0 || (head_dim != 64 && head_dim != 128) || n_seqs > PFA_MAX_SEQS)
         return 0;
     return pfa::bf16_workspace_bytes((int)tile_bound(T, n_seqs), n_head_kv, head_dim,
-                                     precision == PFA_PREC_BF16X3);
+                                     precision == PFA_PREC_BF16X3, T);
 }
 
 int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
@@ -228,7 +230,8 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
         return fail(PFA_ERR_UNSUPPORTED, "grid too large");
     if (precision != PFA_PREC_F32) {
         const bool split = precision == PFA_PREC_BF16X3;
-        const size_t need = pfa::bf16_workspace_bytes(sched.n_tiles, n_head_kv, head_dim, split);
+        const size_t need = pfa::bf16_workspace_bytes(sched.n_tiles, n_head_kv, head_dim, split,
+                                                      prep ? sched.max_len : 0);
         if (!workspace)
             return fail(PFA_ERR_INVALID_ARG, "precision %d needs a workspace (%zu bytes)",
                         precision, need);

@@ -38,6 +38,7 @@ struct AttnSched {
     // tiles tile_off[s] .. tile_off[s+1]-1 of each K/V head; n_tiles in all.
     int n_tiles;
     int tile_off[PFA_MAX_SEQS + 1];
+    int max_len;                     // longest sequence (rows of the fused entry's rotary table)
 };
 
 // Geometry common to the attention launches.
@@ -77,9 +78,11 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
 // Two kernels: K and V are first converted once into `ws` (bf16 tiles in the byte
 // image the attention kernel keeps in LDS), then the attention kernel copies those
 // tiles straight into LDS.  ws must hold bf16_workspace_bytes(...) bytes.
+// The fused entry adds a rotary table of rope_rows x D/2 (cos, sin) f32 pairs.
 constexpr int kBf16TileKeys = 64;
-inline size_t bf16_workspace_bytes(int n_tiles, int Hkv, int D, bool split_qk) {
-    return (size_t)n_tiles * Hkv * (split_qk ? 3 : 2) * kBf16TileKeys * D * 2;
+inline size_t bf16_workspace_bytes(int n_tiles, int Hkv, int D, bool split_qk, int rope_rows) {
+    return (size_t)n_tiles * Hkv * (split_qk ? 3 : 2) * kBf16TileKeys * D * 2 +
+           (size_t)rope_rows * (D / 2) * 8;
 }
 // prep != nullptr: the fused entry (K and Q normalised and rotated on the way in).
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
