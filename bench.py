@@ -197,10 +197,14 @@ def main():
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.precision]
     if args.precision != "f32":
-        # gqa_prefill_attn in the bf16 modes is two launches (the events bracket both):
-        # the K/V staging kernel, then the attention kernel
+        # the bf16 modes are several launches per call (the events bracket all of them):
+        # [rotary table (fused entry)], the K/V staging kernel, the attention kernel
         split = "true" if args.precision == "bf16x3" else "false"
-        kernel = f"stage_kv_bf16_kernel<{w.head_dim},{split}> + attn_bf16_kernel<{w.head_dim},{split}>"
+        fused = "true" if args.path == "fused" else "false"
+        kernel = (f"stage_kv_bf16_kernel<{w.head_dim},{split},{fused}> + "
+                  f"attn_bf16_kernel<{w.head_dim},{split},{fused}>")
+        if args.path == "fused":
+            kernel = f"rope_table_kernel<{w.head_dim},{split}> + " + kernel
     else:
         kernel = f"attn_f32_kernel<{w.head_dim},{'true' if args.path == 'fused' else 'false'}>"
     traffic = load_traffic(w.name, kernel, args.precision, args.path)
