@@ -13,8 +13,8 @@
  *    note and SDPA block) keeps between its projections and its attention.
  *  Pointers.  Tensor pointers are DEVICE pointers owned by the caller, 16-byte
  *    aligned.  The library allocates no device memory and keeps no state beyond
- *    its loaded code objects; the bf16 attention modes take a caller-owned
- *    device workspace (see pfa_workspace_bytes).
+ *    its loaded code objects; the attention calls take a caller-owned device
+ *    workspace (see pfa_workspace_bytes).
  *  Sequences.  `seq_offsets` is a HOST array of n_seqs + 1 int32 values
  *    (cumulative lengths: seq_offsets[0] = 0, non-decreasing, seq_offsets[n_seqs]
  *    = T).  NULL means one sequence [0, T) (n_seqs is then ignored).  Token t of
@@ -64,17 +64,23 @@ typedef enum {
  * PFA_PREC_F32 only (PFA_ERR_UNSUPPORTED otherwise). */
 typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_precision;
 
-/* Device workspace in bytes that gqa_prefill_attn / qk_prep_attn need at this
- * size and precision: 0 for PFA_PREC_F32; for the bf16 modes, K and V converted
- * once to bf16 in 64-key tiles per sequence (K twice, high and low parts, for
- * PFA_PREC_BF16X3), plus qk_prep_attn's rotary table ((cos, sin) f32 pairs per
- * position and pair):
- *   n_head_kv * (ceil(T / 64) + max(n_seqs, 1)) * 64 * head_dim * 2 * (2 or 3)
- *   + T * (head_dim / 2) * 8
- * bytes, enough for either entry point.  n_seqs is the count passed with
- * seq_offsets (1 when that is NULL).  Returns 0 for arguments the attention
- * calls would reject. */
-size_t pfa_workspace_bytes(int T, int n_seqs, int n_head_kv, int head_dim, int precision);
+/* Device workspace in bytes that gqa_prefill_attn / qk_prep_attn use for these
+ * arguments (the same seq_offsets, n_seqs, T, heads, head_dim and precision as
+ * the call; enough for either entry point).  It holds, in this order:
+ *  - bf16 modes: K and V converted once to bf16 in 64-key tiles per sequence (K
+ *    twice, high and low parts, for PFA_PREC_BF16X3),
+ *      n_head_kv * sum_s ceil(len_s / 64) * 64 * head_dim * 2 * (2 or 3) bytes,
+ *    then qk_prep_attn's rotary table, max_s(len_s) * (head_dim / 2) * 8 bytes;
+ *  - any precision, short inputs only: when the (query block, head) work items
+ *    cannot fill the GPU, each item's key range is split over several workgroups
+ *    whose partial results (32 x head_dim f32 plus two f32 per row, per
+ *    wavefront) are merged by one more kernel; 0 bytes otherwise.
+ * For PFA_PREC_F32 the workspace is optional: without it (or with less than this)
+ * the call runs without the key split.  Returns 0 when nothing is needed or the
+ * arguments are ones the attention calls would reject (pfa_last_error() then
+ * says why). */
+size_t pfa_workspace_bytes(const int32_t* seq_offsets, int n_seqs, int T, int n_head,
+                           int n_head_kv, int head_dim, int precision);
 
 /*
  * qknorm_rope -- QK-norm followed by NeoX rotary embedding, for Q and K at once.
@@ -128,10 +134,11 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
  *  out  [T, n_head*head_dim]     f32, device, written; must not overlap q, k, v.
  *  scale  finite; precision  a pfa_precision value.
  *  workspace, workspace_bytes  device memory owned by the caller, 256-byte
- *        aligned, at least pfa_workspace_bytes(T, n_seqs, n_head_kv, head_dim,
- *        precision) bytes, not overlapping the tensors; its contents are
- *        overwritten (calls in flight at the same time need separate
- *        workspaces).  Ignored, and may be NULL, for PFA_PREC_F32.
+ *        aligned, at least pfa_workspace_bytes(seq_offsets, n_seqs, T, n_head,
+ *        n_head_kv, head_dim, precision) bytes, not overlapping the tensors; its
+ *        contents are overwritten (calls in flight at the same time need separate
+ *        workspaces).  Required for the bf16 modes; optional for PFA_PREC_F32
+ *        (may be NULL: short inputs then run without the key split).
  */
 int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
                      const int32_t* seq_offsets, int n_seqs,

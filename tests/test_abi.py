@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import transformer_prefill_attention_amd as pfa
@@ -135,35 +136,81 @@ def test_python_binding_raises_without_gpu_tensors():
                              torch.zeros(4, 64), head_dim=64)
 
 
-def _tiles(T, n_seqs):
-    return -(-T // 64) + max(n_seqs, 1)
+def _ceil(a, b):
+    return -(-a // b)
 
 
-@pytest.mark.parametrize("T,n_seqs,Hkv,D", [(16, 0, 2, 64), (8192, 1, 8, 128), (16064, 8, 4, 64),
-                                           (1, 128, 1, 128)])
-def test_workspace_bytes_formula(L, T, n_seqs, Hkv, D):
-    # the documented bound: K and V as bf16 in 64-key tiles (K twice for bf16x3), plus
-    # the fused entry's rotary table of T x head_dim/2 (cos, sin) f32 pairs
-    per_part = Hkv * _tiles(T, n_seqs) * 64 * D * 2
-    table = T * (D // 2) * 8
-    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 0) == 0
-    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 1) == 2 * per_part + table
-    assert L.pfa_workspace_bytes(T, n_seqs, Hkv, D, 2) == 3 * per_part + table
-    assert pfa.workspace_bytes(T, n_seqs, Hkv, D, "bf16x3") == 3 * per_part + table
+def _expected_workspace(lens, H, Hkv, D, prec):
+    """The workspace rule pfa_workspace_bytes documents, restated: bf16 tiles and rotary
+    table, plus partial results when the (query block, head) items cannot fill the GPU's
+    256 CUs once (2 f32 workgroups or 1 bf16 workgroup per CU) and are split by key."""
+    bf16 = prec != 0
+    waves, tile = (8, 64) if bf16 else (4, 32)
+    g = H // Hkv
+    hpw = 1
+    while hpw < 4 and g % (hpw * 2) == 0:
+        hpw *= 2
+    chunks, rows = g // hpw, 32 * (waves // hpw)
+    items = sum(_ceil(n, rows) for n in lens)
+    n_max = _ceil(max(lens), tile)
+    wgs, target = items * chunks * Hkv, (1 if bf16 else 2) * 256
+    kchunk = 0
+    if wgs < target and n_max > 1:
+        kchunk = max(1, _ceil(wgs * n_max, target))
+        if kchunk >= n_max:
+            kchunk = 0
+    parts = 0
+    if kchunk:
+        units = items * _ceil(n_max, kchunk) * chunks * Hkv
+        parts = units * waves * 32 * (D * 4 + 8)
+    base = 0
+    if bf16:
+        base = Hkv * sum(_ceil(n, 64) for n in lens) * 64 * D * 2 * (3 if prec == 2 else 2)
+        base += max(lens) * (D // 2) * 8
+    return (_ceil(base, 256) * 256 + parts) if parts else base
+
+
+def _ws(L, lens, H, Hkv, D, prec, pass_offsets=True):
+    offs = np.cumsum([0] + list(lens)).astype(np.int32)
+    arr = (ctypes.c_int32 * len(offs))(*offs.tolist())
+    ptr = ctypes.cast(arr, ctypes.c_void_p) if pass_offsets else None
+    return L.pfa_workspace_bytes(ptr, len(lens), int(offs[-1]), H, Hkv, D, prec)
+
+
+@pytest.mark.parametrize("lens,H,Hkv,D", [
+    ((8192,), 32, 8, 128), ((512,), 16, 8, 128), ((512,), 32, 8, 128), ((1024,), 32, 8, 128),
+    ((128, 256, 512, 1024, 2048, 3000, 4096, 5000), 16, 4, 128), ((16,), 4, 2, 64),
+    ((300,), 8, 2, 128), ((1, 33, 0, 64, 65, 97), 4, 2, 128), ((90,), 6, 2, 64)])
+@pytest.mark.parametrize("prec", [0, 1, 2])
+def test_workspace_bytes_rule(L, lens, H, Hkv, D, prec):
+    assert _ws(L, lens, H, Hkv, D, prec) == _expected_workspace(lens, H, Hkv, D, prec)
+
+
+def test_workspace_bytes_cases():
+    # long inputs in f32 need nothing; the T = 512 shapes split their keys
+    L = pfa.lib()
+    assert _ws(L, (8192,), 32, 8, 128, 0) == 0
+    assert _ws(L, (512,), 16, 8, 128, 0) > 0
+    assert _ws(L, (8192,), 32, 8, 128, 1, pass_offsets=False) == \
+        8 * 128 * 64 * 128 * 2 * 2 + 8192 * 64 * 8
+    assert pfa.workspace_bytes(8192, 32, 8, 128, "bf16x3") == \
+        8 * 128 * 64 * 128 * 2 * 3 + 8192 * 64 * 8
 
 
 def test_workspace_bytes_rejects_what_attention_rejects(L):
-    assert L.pfa_workspace_bytes(16, 1, 2, 96, 1) == 0
-    assert L.pfa_workspace_bytes(16, 1, 2, 64, 7) == 0
-    assert L.pfa_workspace_bytes(16, 129, 2, 64, 1) == 0
-    assert L.pfa_workspace_bytes(-1, 1, 2, 64, 1) == 0
+    assert _ws(L, (16,), 4, 2, 96, 1) == 0
+    assert "head_dim" in L.pfa_last_error().decode()
+    assert _ws(L, (16,), 4, 2, 64, 7) == 0
+    assert "precision" in L.pfa_last_error().decode()
+    assert _ws(L, (16,) * 129, 4, 2, 64, 1) == 0
+    assert _ws(L, (16,), 3, 2, 64, 1) == 0
 
 
 @pytest.mark.parametrize("prec", [1, 2])
 def test_bf16_modes_check_the_workspace(L, prec):
     # every call below must fail its checks before any launch (the pointers are not real)
     ptrs = (1 << 20, 2 << 20, 3 << 20, 4 << 20)   # q 16x4x64 f32 = 16 KiB, k/v 8 KiB each
-    need = L.pfa_workspace_bytes(16, 1, 2, 64, prec)
+    need = _ws(L, (16,), 4, 2, 64, prec)
     exact = (2 if prec == 1 else 3) * 2 * 1 * 64 * 64 * 2   # one 64-key tile per K/V head
     assert exact <= need
     assert _attn(L, prec=prec, ptrs=ptrs) == INVALID

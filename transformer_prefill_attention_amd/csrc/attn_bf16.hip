@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                                                                 const __bf16* __restrict__ ws,
                                                                 float* __restrict__ out,
                                                                 AttnSched sched, AttnGeom geom,
-                                                                PrepParams prep) {
+                                                                PrepParams prep, Partials part) {
     constexpr int KP = SPLIT ? 2 : 1;
     constexpr int NCH = D / 8;            // 16-byte chunks per K row
     constexpr int KT = KP * kBN * D * 2;  // K tile bytes
@@ -337,6 +337,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     const int n_all = sched.n_tiles, tile0 = sched.tile_off[wi.sid];
     const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
     const int n_tiles = causal ? (min(q0 + sched.rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
+    // key split: this workgroup takes tiles [t_begin, t_begin + n_local) of the item
+    const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles;
+    const int n_chunks = (n_tiles + kchunk - 1) / kchunk;
+    if (wi.kc >= n_chunks) return;  // (uniform: the whole workgroup leaves)
+    const int t_begin = wi.kc * kchunk, n_local = min(kchunk, n_tiles - t_begin);
+    const bool split = n_chunks > 1;
 
     const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;
     const int h = kv * geom.g + wi.chunk * geom.hpw + hloc;
@@ -458,10 +464,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     }
 
     // ---- tile sources in the workspace and per-lane LDS read addresses
-    const unsigned char* kt_src =
-        reinterpret_cast<const unsigned char*>(ws) + ((int64_t)kv * n_all + tile0) * KT;
+    // (tile sources start at this workgroup's first tile; tiles are indexed locally)
+    const unsigned char* kt_src = reinterpret_cast<const unsigned char*>(ws) +
+                                  ((int64_t)kv * n_all + tile0 + t_begin) * KT;
     const unsigned char* vt_src = reinterpret_cast<const unsigned char*>(ws) +
-                                  (int64_t)Hkv * n_all * KT + ((int64_t)kv * n_all + tile0) * VT;
+                                  (int64_t)Hkv * n_all * KT +
+                                  ((int64_t)kv * n_all + tile0 + t_begin) * VT;
     // K operand of step s, key block 0: row ln, chunk hl*NCH/2 + s (block 1: +32 rows)
     uint32_t kaddr[NQS];
 #pragma unroll
@@ -472,15 +480,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     for (int s = 0; s < 4; ++s) vaddr[s] = 2 * KT + ln * (kBN * 2) + 16 * swz(ln, 2 * s + hl, 8);
 
     // Direct-to-LDS copies: lane l of wavefront w moves bytes 16 (64 w + l) + 8192 i.
+    // load_tiles(t): K of local tile t+1 and V of local tile t (those that exist).
     auto load_tiles = [&](int t) {
-        if (t + 1 < n_tiles) {
+        if (t + 1 < n_local) {
             const unsigned char* src = kt_src + (int64_t)(t + 1) * KT + 16 * tid;
             unsigned char* dst = smem + ((t + 1) & 1) * KT + 1024 * wave;
 #pragma unroll
             for (int i = 0; i < K_LOADS; ++i)
                 __builtin_amdgcn_global_load_lds(src + 8192 * i, dst + 8192 * i, 16, 0, 0);
         }
-        if (t < n_tiles) {
+        if (t >= 0 && t < n_local) {
             const unsigned char* src = vt_src + (int64_t)t * VT + 16 * tid;
             unsigned char* dst = smem + 2 * KT + (t & 1) * VT + 1024 * wave;
 #pragma unroll
@@ -572,9 +581,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // X(t): scores of tile t -> P(t) (bf16, B-operand layout), running max and sum.
-    auto x_phase = [&](int t) {
-        if (t < 0 || t > wave_last) {
+    // X(lt): scores of local tile lt -> P (bf16, B-operand layout), running max and sum.
+    auto x_phase = [&](int lt) {
+        const int t = t_begin + lt;
+        if (lt < 0 || lt >= n_local || t > wave_last) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -637,11 +647,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     // and V(t) are issued in global phase 2t (A: before M(t); B: before X(t-1),
     // i.e. B issues tile t+1's loads before its X(t)) and waited for at the end of
     // global phase 2t+1.
-    for (int t0 = 0; t0 <= n_tiles; t0 += 2) {
+    for (int t0 = 0; t0 <= n_local; t0 += 2) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int t = t0 + u;
-            if (t > n_tiles) break;
+            const int t = t0 + u;  // local tile index
+            if (t > n_local) break;
             if (!grp_b) load_tiles(t);
             if (u == 0) m_phase(std::integral_constant<int, 0>{});
             else m_phase(std::integral_constant<int, 1>{});
@@ -656,8 +666,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     if (!grp_b) phase_barrier();
 
     // ---- epilogue: 1/l, transpose through LDS (four wavefronts at a time), coalesced rows
+    // to the output, or for a split item to this unit's partial-result slot
     const double l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = (float)(1.0 / l_tot);
+    const float inv = l_tot > 0.0 ? (float)(1.0 / l_tot) : 0.0f;
+    const size_t slot = (size_t)blockIdx.x * kWaves + wave;
+    if (split && hl == 0) part.ml[slot * 32 + ln] = float2{m_run, (float)l_tot};
 #pragma unroll
     for (int round = 0; round < 2; ++round) {
         const bool mine = (wave >> 2) == round;
@@ -681,9 +694,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 const int f = lane + 64 * i;
                 const int r = f / F4, c4 = f % F4;
                 const int row = wq0 + r;
-                if (row < s1)
-                    *reinterpret_cast<floatx4*>(out + ((int64_t)row * H + h) * D + 4 * c4) =
-                        *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
+                const floatx4 x = *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
+                if (split)
+                    *reinterpret_cast<floatx4*>(part.o + (slot * 32 + r) * D + 4 * c4) = x;
+                else if (row < s1)
+                    *reinterpret_cast<floatx4*>(out + ((int64_t)row * H + h) * D + 4 * c4) = x;
             }
         }
         if (round == 0) __syncthreads();
@@ -694,11 +709,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
-                            const PrepParams* prep, int n_items, hipStream_t stream) {
+                            const PrepParams* prep, const Partials& part, int n_items,
+                            hipStream_t stream) {
     __bf16* w = static_cast<__bf16*>(ws);
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
     const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
-    const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(kThreads);
+    const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv),
+        block(kThreads);
     const dim3 tgrid((unsigned)((sched.max_len + kTabRows - 1) / kTabRows)), tblock(256);
 #define PFA_LAUNCH_BF16(DD, SS, PP)                                                             \
     do {                                                                                        \
@@ -708,7 +725,7 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
         hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, PP>), sgrid, sblock, 0, stream, k, v, \
                            w, sched, geom.Hkv, p);                                              \
         hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP>), grid, block, 0, stream, q, w, out,  \
-                           sched, geom, p);                                                     \
+                           sched, geom, p, part);                                               \
     } while (0)
 #define PFA_LAUNCH_BF16_P(DD, SS)                   \
     do {                                            \
@@ -724,7 +741,10 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
     }
 #undef PFA_LAUNCH_BF16_P
 #undef PFA_LAUNCH_BF16
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && sched.max_chunks > 1)
+        e = launch_attn_combine(part, out, sched, geom, D, kWaves, kBN, n_items, stream);
+    return e;
 }
 
 }  // namespace pfa

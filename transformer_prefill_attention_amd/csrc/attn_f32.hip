@@ -96,7 +96,7 @@ __device__ __forceinline__ void prep_row(float (&x)[D / 64], const float* w, con
 template <int D, bool PREP>
 __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ out, AttnSched sched, AttnGeom geom, PrepParams prep) {
+    float* __restrict__ out, AttnSched sched, AttnGeom geom, PrepParams prep, Partials part) {
     constexpr int KS = D + 4;          // K tile row stride in LDS (floats): b128 reads conflict-free
     constexpr int VS = D + 8;          // V tile row stride
     constexpr int NQ = D / 2;          // Q operand registers per lane = MFMA steps of K Q^T
@@ -126,6 +126,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
     const int n_tiles =
         geom.causal ? (min(q0 + rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
+    // key split: this workgroup takes tiles [t_begin, t_end) of the item
+    const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles;
+    const int n_chunks = (n_tiles + kchunk - 1) / kchunk;
+    if (wi.kc >= n_chunks) return;  // (uniform: the whole workgroup leaves)
+    const int t_begin = wi.kc * kchunk, t_end = min(t_begin + kchunk, n_tiles);
+    const bool split = n_chunks > 1;
 
     // ---- wavefront role
     const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;
@@ -313,15 +319,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     float m_run = -INFINITY;
     double l_run = 0.0;
 
-    load_k_tile(0);
-    store_k_tile(smem, 0);
-    load_rows(v, 0);
+    load_k_tile(t_begin);
+    store_k_tile(smem, t_begin);
+    load_rows(v, t_begin);
     store_rows(smem + kBN * KS, VS);
     __syncthreads();
 
-    for (int t = 0; t < n_tiles; ++t) {
-        const int cur = t & 1;
-        const bool more = t + 1 < n_tiles;
+    for (int t = t_begin; t < t_end; ++t) {
+        const int cur = (t - t_begin) & 1;
+        const bool more = t + 1 < t_end;
         float* kn = smem + (cur ^ 1) * BUF;
         if (more) load_k_tile(t + 1);
         if (active && t < wave_tiles) {
@@ -434,9 +440,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
         __syncthreads();
     }
 
-    // ---- epilogue: 1/l, transpose through LDS, coalesced row stores
+    // ---- epilogue: 1/l, transpose through LDS, coalesced row stores (to the output,
+    // or for a split item to this unit's partial-result slot)
     const double l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = (float)(1.0 / l_tot);
+    const float inv = l_tot > 0.0 ? (float)(1.0 / l_tot) : 0.0f;
+    const size_t slot = (size_t)blockIdx.x * kWaves + wave;
+    if (split && hl == 0) part.ml[slot * 32 + ln] = float2{m_run, (float)l_tot};
     float* os = smem + wave * 32 * QS;
     if (active) {
         // lane (hl, ln), register r of block cb holds O[qi][cb*32 + 8(r/4) + 4hl + r%4]
@@ -459,9 +468,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             const int f = lane + 64 * i;
             const int r = f / F4_PER_ROW, c4 = f % F4_PER_ROW;
             const int row = wq0 + r;
-            if (row < s1)
-                *reinterpret_cast<floatx4*>(out + ((int64_t)row * n_q + h) * D + 4 * c4) =
-                    *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
+            const floatx4 x = *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
+            if (split)
+                *reinterpret_cast<floatx4*>(part.o + (slot * 32 + r) * D + 4 * c4) = x;
+            else if (row < s1)
+                *reinterpret_cast<floatx4*>(out + ((int64_t)row * n_q + h) * D + 4 * c4) = x;
         }
     }
 }
@@ -470,25 +481,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
 
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out,
                            const AttnSched& sched, const AttnGeom& geom, int D,
-                           const PrepParams* prep, int n_items, hipStream_t stream) {
-    const dim3 grid((unsigned)n_items * geom.chunks * geom.Hkv), block(kThreads);
+                           const PrepParams* prep, const Partials& part, int n_items,
+                           hipStream_t stream) {
+    const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv), block(kThreads);
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
+#define PFA_LAUNCH_F32(DD, PP)                                                                    \
+    hipLaunchKernelGGL((attn_f32_kernel<DD, PP>), grid, block, 0, stream, q, k, v, out, sched,  \
+                       geom, p, part)
     if (D == 128) {
-        if (prep)
-            hipLaunchKernelGGL((attn_f32_kernel<128, true>), grid, block, 0, stream, q, k, v, out,
-                               sched, geom, p);
-        else
-            hipLaunchKernelGGL((attn_f32_kernel<128, false>), grid, block, 0, stream, q, k, v,
-                               out, sched, geom, p);
+        if (prep) PFA_LAUNCH_F32(128, true);
+        else PFA_LAUNCH_F32(128, false);
     } else {
-        if (prep)
-            hipLaunchKernelGGL((attn_f32_kernel<64, true>), grid, block, 0, stream, q, k, v, out,
-                               sched, geom, p);
-        else
-            hipLaunchKernelGGL((attn_f32_kernel<64, false>), grid, block, 0, stream, q, k, v, out,
-                               sched, geom, p);
+        if (prep) PFA_LAUNCH_F32(64, true);
+        else PFA_LAUNCH_F32(64, false);
     }
-    return hipGetLastError();
+#undef PFA_LAUNCH_F32
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && sched.max_chunks > 1)
+        e = launch_attn_combine(part, out, sched, geom, D, kWaves, kBN, n_items, stream);
+    return e;
 }
 
 }  // namespace pfa

@@ -142,9 +142,65 @@ int build_sched(const pfa::SeqTable& st, int rows_per_item, pfa::AttnSched& sc) 
     return items;
 }
 
-// Upper bound of the bf16 tile count: sum over sequences of ceil(len / 64).
-long long tile_bound(int T, int n_seqs) {
-    return (long long)(T + pfa::kBf16TileKeys - 1) / pfa::kBf16TileKeys + std::max(n_seqs, 1);
+// Everything an attention call launches, decided on the host from its arguments
+// (the same for pfa_workspace_bytes and the call itself).
+struct Plan {
+    pfa::AttnGeom geom;
+    pfa::AttnSched sched;
+    int items = 0;
+    int waves = 0, tile_keys = 0;
+    size_t tile_bytes = 0;   // bf16: K/V tiles
+    size_t table_bytes = 0;  // bf16 fused entry: rotary table (max_len x d/2 pairs)
+    size_t part_bytes = 0;   // key split: partial results
+};
+
+constexpr int kF32TileKeys = 32;
+// Workgroups that fill the GPU once: 256 CUs x (2 f32 or 1 bf16 workgroups per CU).
+constexpr int kCUs = 256;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Key split: when items x head chunks x K/V heads workgroups cannot fill the GPU
+// once, cut every item's key tiles into chunks of kchunk so that all units still
+// run at once.  With the longest item at n_max tiles, a causal item of n tiles
+// becomes ceil(n / kchunk) units; kchunk = wgs n_max / target keeps a causal
+// single sequence near target / 2 + wgs / 2 units (each unit re-reads its Q rows
+// and writes a partial result, so fewer, longer chunks beat one chunk per tile).
+void choose_split(Plan& p, int head_dim) {
+    const long long wgs = (long long)p.items * p.geom.chunks * p.geom.Hkv;
+    const int target = (p.waves == 8 ? 1 : 2) * kCUs;
+    const int n_max = (p.sched.max_len + p.tile_keys - 1) / p.tile_keys;
+    int kchunk = 0;
+    if (wgs < target && n_max > 1) {
+        const long long k = (wgs * n_max + target - 1) / target;
+        kchunk = (int)std::max(1LL, k);
+        if (kchunk >= n_max) kchunk = 0;
+    }
+    p.sched.kchunk = kchunk;
+    p.sched.max_chunks = kchunk ? (n_max + kchunk - 1) / kchunk : 1;
+    const long long units =
+        (long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv;
+    p.part_bytes = kchunk ? pfa::partials_bytes((int)units, p.waves, head_dim) : 0;
+}
+
+// Geometry, schedule, key split and workspace parts of one attention call.
+int make_plan(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim, float scale,
+              int causal, int precision, Plan& p) {
+    const bool bf16 = precision != PFA_PREC_F32;
+    // the bf16 kernel runs 8 wavefronts per workgroup, the f32 one 4
+    p.waves = bf16 ? 8 : 4;
+    p.tile_keys = bf16 ? pfa::kBf16TileKeys : kF32TileKeys;
+    choose_geometry(n_head, n_head_kv, scale, causal, p.waves, p.geom);
+    p.items = build_sched(st, 32 * p.geom.rb, p.sched);
+    choose_split(p, head_dim);
+    if ((long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv >= (1LL << 31))
+        return fail(PFA_ERR_UNSUPPORTED, "grid too large");
+    if (bf16) {
+        p.tile_bytes = pfa::bf16_workspace_bytes(p.sched.n_tiles, n_head_kv, head_dim,
+                                                 precision == PFA_PREC_BF16X3, 0);
+        p.table_bytes = pfa::bf16_workspace_bytes(0, n_head_kv, head_dim, false, p.sched.max_len);
+    }
+    return PFA_OK;
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -161,13 +217,24 @@ const char* pfa_last_error(void) { return g_err; }
 
 const char* pfa_version(void) { return "pfa 0.3 (gfx950; f32 and bf16 MFMA attention)"; }
 
-size_t pfa_workspace_bytes(int T, int n_seqs, int n_head_kv, int head_dim, int precision) {
-    if (precision == PFA_PREC_F32) return 0;
-    if ((precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) || T < 0 ||
-        n_head_kv <= 0 || (head_dim != 64 && head_dim != 128) || n_seqs > PFA_MAX_SEQS)
+size_t pfa_workspace_bytes(const int32_t* seq_offsets, int n_seqs, int T, int n_head,
+                           int n_head_kv, int head_dim, int precision) {
+    g_err[0] = 0;
+    if (check_geometry(T, n_head, n_head_kv, head_dim)) return 0;
+    if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) {
+        fail(PFA_ERR_INVALID_ARG, "precision must be PFA_PREC_F32, PFA_PREC_BF16 or "
+                                  "PFA_PREC_BF16X3 (got %d)", precision);
         return 0;
-    return pfa::bf16_workspace_bytes((int)tile_bound(T, n_seqs), n_head_kv, head_dim,
-                                     precision == PFA_PREC_BF16X3, T);
+    }
+    if (T == 0) return 0;
+    pfa::SeqTable st;
+    if (build_seqs(seq_offsets, n_seqs, T, st)) return 0;
+    Plan p;
+    if (make_plan(st, n_head, n_head_kv, head_dim, 1.0f, 1, precision, p)) return 0;
+    if (p.items == 0) return 0;
+    // room for both entry points: the rotary table is reserved even if only the fused one uses it
+    return p.part_bytes ? align256(p.tile_bytes + p.table_bytes) + p.part_bytes
+                        : p.tile_bytes + p.table_bytes;
 }
 
 int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
@@ -219,19 +286,22 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
     pfa::SeqTable st;
     int rc = build_seqs(seq_offsets, n_seqs, T, st);
     if (rc) return rc;
-    pfa::AttnGeom geom;
-    // the bf16 kernel runs 8 wavefronts per workgroup, the f32 one 4
-    const int waves = precision != PFA_PREC_F32 ? 8 : 4;
-    choose_geometry(n_head, n_head_kv, scale, causal, waves, geom);
-    pfa::AttnSched sched;
-    const int items = build_sched(st, 32 * geom.rb, sched);
-    if (items == 0) return PFA_OK;
-    if ((long long)items * geom.chunks * geom.Hkv >= (1LL << 31))
-        return fail(PFA_ERR_UNSUPPORTED, "grid too large");
-    if (precision != PFA_PREC_F32) {
-        const bool split = precision == PFA_PREC_BF16X3;
-        const size_t need = pfa::bf16_workspace_bytes(sched.n_tiles, n_head_kv, head_dim, split,
-                                                      prep ? sched.max_len : 0);
+    Plan p;
+    if ((rc = make_plan(st, n_head, n_head_kv, head_dim, scale, causal, precision, p))) return rc;
+    if (p.items == 0) return PFA_OK;
+    const bool bf16 = precision != PFA_PREC_F32;
+    // workspace parts: [bf16 K/V tiles][rotary table, fused entry][partials, key split]
+    const size_t base = p.tile_bytes + (prep ? p.table_bytes : 0);
+    const size_t part_off = p.part_bytes ? align256(base) : base;
+    if (!bf16 && p.part_bytes &&
+        (!workspace || workspace_bytes < part_off + p.part_bytes)) {
+        // f32 runs without the key split when the caller gives no (or too small a) workspace
+        p.sched.kchunk = 0;
+        p.sched.max_chunks = 1;
+        p.part_bytes = 0;
+    }
+    const size_t need = p.part_bytes ? part_off + p.part_bytes : base;
+    if (need > 0) {
         if (!workspace)
             return fail(PFA_ERR_INVALID_ARG, "precision %d needs a workspace (%zu bytes)",
                         precision, need);
@@ -244,12 +314,22 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
             overlaps(workspace, need, v, kb) || overlaps(workspace, need, out, qb) ||
             (prep && prep->k_rot_out && overlaps(workspace, need, prep->k_rot_out, kb)))
             return fail(PFA_ERR_INVALID_ARG, "workspace must not overlap the tensors");
-        return hip_status(pfa::launch_attn_bf16(q, k, v, out, workspace, sched, geom, head_dim,
-                                                split, prep, items, (hipStream_t)stream),
-                          prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
     }
-    return hip_status(pfa::launch_attn_f32(q, k, v, out, sched, geom, head_dim, prep, items,
-                                           (hipStream_t)stream),
+    pfa::Partials part{nullptr, nullptr};
+    if (p.part_bytes) {
+        const long long units =
+            (long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv;
+        char* w = static_cast<char*>(workspace) + part_off;
+        part.o = reinterpret_cast<float*>(w);
+        part.ml = reinterpret_cast<float2*>(w + (size_t)units * p.waves * 32 * head_dim * 4);
+    }
+    if (bf16)
+        return hip_status(pfa::launch_attn_bf16(q, k, v, out, workspace, p.sched, p.geom, head_dim,
+                                                precision == PFA_PREC_BF16X3, prep, part, p.items,
+                                                (hipStream_t)stream),
+                          prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
+    return hip_status(pfa::launch_attn_f32(q, k, v, out, p.sched, p.geom, head_dim, prep, part,
+                                           p.items, (hipStream_t)stream),
                       prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
 }
 

@@ -85,27 +85,23 @@ __device__ __forceinline__ int find_seq(const int* off, int n_seqs, int t) {
 }
 
 // One workgroup's share of the attention work (see AttnSched): K/V head, head
-// chunk of the group, and the sequence and query super-block it covers.
+// chunk of the group, the sequence and query super-block it covers, and which
+// chunk of that super-block's key tiles.
 struct WorkItem {
     int kv, chunk, sb;   // K/V head, head chunk, super-block index in the sequence
+    int kc;              // key chunk (0 when the key range is not split)
+    int item;            // index in the longest-first item order
     int sid;             // sequence index
     int s0, s1;          // sequence token range [s0, s1)
     int q0;              // first query row of the super-block
 };
 
-// blockIdx.x -> work item.  The K/V head is the fastest-varying index (so the
-// workgroups that the dispatcher deals to the 8 XCDs in turn share heads), the
-// head chunk next, and the longest-first item order slowest.
-template <class Sched, class Geom>
-__device__ __forceinline__ WorkItem decode_item(const Sched& sched, const Geom& geom, int bid) {
-    WorkItem w;
-    w.kv = bid % geom.Hkv;
-    bid /= geom.Hkv;
-    w.chunk = bid % geom.chunks;
-    const int item = bid / geom.chunks;
+// item -> sequence and super-block (segment decode of the longest-first order).
+template <class Sched>
+__device__ __forceinline__ void decode_seq(const Sched& sched, WorkItem& w) {
     int seg = 0;
-    while (item >= sched.seg_start[seg + 1]) ++seg;
-    const int local = item - sched.seg_start[seg];
+    while (w.item >= sched.seg_start[seg + 1]) ++seg;
+    const int local = w.item - sched.seg_start[seg];
     const int per = seg + 1;
     const int sid = sched.order[local % per];
     w.sb = sched.seg_top[seg] - 1 - local / per;
@@ -113,6 +109,21 @@ __device__ __forceinline__ WorkItem decode_item(const Sched& sched, const Geom& 
     w.s0 = sched.off[sid];
     w.s1 = sched.off[sid + 1];
     w.q0 = w.s0 + w.sb * sched.rows_per_item;
+}
+
+// blockIdx.x -> work unit.  The K/V head is the fastest-varying index (so the
+// workgroups that the dispatcher deals to the 8 XCDs in turn share heads), then
+// the head chunk, then the key chunk, and the longest-first item order slowest.
+template <class Sched, class Geom>
+__device__ __forceinline__ WorkItem decode_item(const Sched& sched, const Geom& geom, int bid) {
+    WorkItem w;
+    w.kv = bid % geom.Hkv;
+    bid /= geom.Hkv;
+    w.chunk = bid % geom.chunks;
+    bid /= geom.chunks;
+    w.kc = bid % sched.max_chunks;
+    w.item = bid / sched.max_chunks;
+    decode_seq(sched, w);
     return w;
 }
 

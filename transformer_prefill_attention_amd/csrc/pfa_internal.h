@@ -39,7 +39,25 @@ struct AttnSched {
     int n_tiles;
     int tile_off[PFA_MAX_SEQS + 1];
     int max_len;                     // longest sequence (rows of the fused entry's rotary table)
+    // Key split for short inputs: when the items alone cannot fill the GPU, each
+    // item's key tiles are cut into chunks of kchunk tiles, one workgroup each
+    // (grid = items x max_chunks x head chunks x K/V heads; chunk slots past an
+    // item's count exit at once).  Items with more than one chunk write partial
+    // results that attn_combine_kernel merges.  kchunk = 0: no split (max_chunks 1).
+    int kchunk;
+    int max_chunks;
 };
+
+// Partial results of a split item, per work unit (blockIdx) and wavefront:
+// 32 rows x D of O / l (f32), and per row (m, l): running max (log2 units) and
+// softmax denominator.  An empty wavefront writes m = -inf, l = 0.
+struct Partials {
+    float* o;       // [units][waves][32][D]
+    float2* ml;     // [units][waves][32]
+};
+inline size_t partials_bytes(int units, int waves, int D) {
+    return (size_t)units * waves * 32 * (D * 4 + 8);
+}
 
 // Geometry common to the attention launches.
 struct AttnGeom {
@@ -71,7 +89,14 @@ hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out
 // fused entry (Q and K normalised and rotated inside the kernel).
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out,
                            const AttnSched& sched, const AttnGeom& geom, int D,
-                           const PrepParams* prep, int n_items, hipStream_t stream);
+                           const PrepParams* prep, const Partials& part, int n_items,
+                           hipStream_t stream);
+
+// Merges the partial results of split items into out (no-op for unsplit ones).
+// tile_keys: the key-tile size of the attention kernel that wrote the partials.
+hipError_t launch_attn_combine(const Partials& part, float* out, const AttnSched& sched,
+                               const AttnGeom& geom, int D, int waves, int tile_keys, int n_items,
+                               hipStream_t stream);
 
 // bf16-input / f32-accumulate attention.
 // split_qk: scores from bf16 high + low parts of Q and K (PFA_PREC_BF16X3).
@@ -87,5 +112,6 @@ inline size_t bf16_workspace_bytes(int n_tiles, int Hkv, int D, bool split_qk, i
 // prep != nullptr: the fused entry (K and Q normalised and rotated on the way in).
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
-                            const PrepParams* prep, int n_items, hipStream_t stream);
+                            const PrepParams* prep, const Partials& part, int n_items,
+                            hipStream_t stream);
 }  // namespace pfa

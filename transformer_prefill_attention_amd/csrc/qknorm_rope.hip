@@ -6,15 +6,19 @@
 // round trips; here one wavefront reads each row once and writes it once);
 // needle-core v3/model.rs, `rope_at` / `rope` (frequency and angle).
 //
-// Layout of the work: one wavefront owns one token and walks all of its
-// n_head + n_head_kv head rows.  Lane L holds dims L and L + 64 of a row (one
-// dim for head_dim 64), so every load and store is a 256-byte coalesced
-// segment, the sum of squares is a wavefront reduction, and the rotary cos/sin
-// of the token are computed once per lane and reused by every head.
+// Layout of the work: one wavefront owns one token, or for short inputs one of
+// `groups` consecutive runs of its n_head + n_head_kv head rows (Q heads first,
+// then K heads), so that short inputs still have enough wavefronts in flight.
+// Lane L holds dims L and L + 64 of a row (one dim for head_dim 64), so every
+// load and store is a 256-byte coalesced segment, the sum of squares is a
+// wavefront reduction, and the rotary cos/sin of the token are computed once per
+// lane and reused by every head of the run.
 //
 // Rotary pair (j, j + n/2): with n == head_dim == 128 both dims of a pair sit
 // in the same lane (no data movement); with n == 64 the partner is lane L ^ 32
 // (one cross-half shuffle); any other even n uses a general two-shuffle path.
+#include <algorithm>
+
 #include "pfa_device.h"
 #include "pfa_internal.h"
 
@@ -30,7 +34,7 @@ template <int D, int MODE>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const float* q_in, const float* k_in, float* q_out, float* k_out,
     const float* __restrict__ wq, const float* __restrict__ wk, SeqTable seqs, int T, int H,
-    int Hkv, int n, double base, float eps) {
+    int Hkv, int n, double base, float eps, int groups) {
     constexpr int E = D / 64;  // dims per lane
     const int lane = threadIdx.x & 63;
     const int half = n >> 1;
@@ -56,7 +60,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     }
 
     const int waves = gridDim.x * (blockDim.x >> 6);
-    for (int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < T; t += waves) {
+    const int rows = H + Hkv, per = (rows + groups - 1) / groups;  // head rows per unit
+    for (int u = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); u < T * groups; u += waves) {
+        const int t = u / groups, r0 = (u % groups) * per, r1 = min(r0 + per, rows);
         const int s = find_seq(seqs.off, seqs.n_seqs, t);
         const int pos = t - seqs.off[s];
         float cs[E], sn[E];
@@ -122,8 +128,15 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
                 }
             }
         };
-        do_rows(q_in + (int64_t)t * H * D, q_out + (int64_t)t * H * D, H, wqv);
-        do_rows(k_in + (int64_t)t * Hkv * D, k_out + (int64_t)t * Hkv * D, Hkv, wkv);
+        // rows [r0, r1) of (Q heads, then K heads)
+        if (r0 < H)
+            do_rows(q_in + ((int64_t)t * H + r0) * D, q_out + ((int64_t)t * H + r0) * D,
+                    min(r1, H) - r0, wqv);
+        if (r1 > H) {
+            const int k0 = max(r0, H) - H;
+            do_rows(k_in + ((int64_t)t * Hkv + k0) * D, k_out + ((int64_t)t * Hkv + k0) * D,
+                    r1 - H - k0, wkv);
+        }
     }
 }
 
@@ -131,13 +144,18 @@ template <int D, int MODE>
 hipError_t launch_mode(const float* q_in, const float* k_in, float* q_out, float* k_out,
                        const float* wq, const float* wk, const SeqTable& seqs, int T, int H,
                        int Hkv, int n, float base, float eps, hipStream_t stream) {
-    // Up to 4 tokens per wavefront so the per-lane rotary frequencies (f64 pow)
-    // are amortised; at least enough workgroups to cover every CU several times.
-    int blocks = (T + 3) / 4;
-    if (blocks > 2048) blocks = 2048;
+    // Work units: tokens, or for short inputs runs of at least 4 head rows of a
+    // token, so that ~8192 wavefronts (2048 workgroups of 4) have work.  Up to 4
+    // units per wavefront so the per-lane rotary frequencies (f64 pow) are
+    // amortised.
+    const int rows = H + Hkv;
+    int groups = (8192 + T - 1) / T;
+    groups = std::max(1, std::min(groups, (rows + 3) / 4));
+    const long long units = (long long)T * groups;
+    int blocks = (int)std::min<long long>((units + 3) / 4, 2048);
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL((qknorm_rope_kernel<D, MODE>), dim3(blocks), dim3(256), 0, stream, q_in,
-                       k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv, n, (double)base, eps);
+                       k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv, n, (double)base, eps, groups);
     return hipGetLastError();
 }
 

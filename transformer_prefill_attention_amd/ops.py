@@ -60,7 +60,7 @@ def lib() -> ctypes.CDLL:
     L.qk_prep_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
                                f32, i32, i32, fp_, vp, sz, vp]
     L.qk_prep_attn.restype = i32
-    L.pfa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.pfa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32]
     L.pfa_workspace_bytes.restype = sz
     L.pfa_last_error.restype = ctypes.c_char_p
     L.pfa_last_error.argtypes = []
@@ -133,15 +133,18 @@ def _prec(precision):
         raise ValueError(f"precision must be 'f32', 'bf16' or 'bf16x3', got {precision!r}") from None
 
 
-def workspace_bytes(T: int, n_seqs: int, n_head_kv: int, head_dim: int, precision="f32") -> int:
-    """Device workspace the attention calls need (``pfa_workspace_bytes``); 0 for f32."""
-    return int(lib().pfa_workspace_bytes(T, n_seqs, n_head_kv, head_dim, _prec(precision)))
+def workspace_bytes(T: int, n_head: int, n_head_kv: int, head_dim: int, precision="f32",
+                    seq_offsets: Optional[Sequence[int]] = None) -> int:
+    """Device workspace the attention calls use for these arguments (``pfa_workspace_bytes``)."""
+    offs, n_seqs, op = _offsets(seq_offsets, T)
+    return int(lib().pfa_workspace_bytes(op, n_seqs, T, n_head, n_head_kv, head_dim,
+                                         _prec(precision)))
 
 
-def _workspace(workspace, T, n_seqs, Hkv, head_dim, prec, device):
-    """(pointer, size) of the caller's workspace, or of a new one from torch's allocator."""
+def _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, device):
+    """(tensor, pointer, size) of the caller's workspace, or of a new one from torch's allocator."""
     import torch
-    need = int(lib().pfa_workspace_bytes(T, max(n_seqs, 1), Hkv, head_dim, prec))
+    need = int(lib().pfa_workspace_bytes(op, n_seqs, T, H, Hkv, head_dim, prec))
     if need == 0:
         return None, ctypes.c_void_p(0), 0
     if workspace is None:
@@ -197,7 +200,7 @@ def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
         scale = head_dim ** -0.5
     offs, n_seqs, op = _offsets(seq_offsets, T)
     prec = _prec(precision)
-    ws, wp, wn = _workspace(workspace, T, n_seqs, Hkv, head_dim, prec, q.device)
+    ws, wp, wn = _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, q.device)
     _check(lib().gqa_prefill_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), op, n_seqs, T, H, Hkv,
                                   head_dim, float(scale), 1 if causal else 0, prec, wp, wn,
                                   _stream(q)))
@@ -230,7 +233,7 @@ def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
         scale = head_dim ** -0.5
     offs, n_seqs, op = _offsets(seq_offsets, T)
     prec = _prec(precision)
-    ws, wp, wn = _workspace(workspace, T, n_seqs, Hkv, head_dim, prec, q.device)
+    ws, wp, wn = _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, q.device)
     _check(lib().qk_prep_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(q_norm_w),
                               _ptr(k_norm_w), op, n_seqs, T, H, Hkv, head_dim, rope_dim,
                               float(rope_freq_base), float(rms_eps), float(scale),
