@@ -602,16 +602,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 for (int r = 0; r < 16; ++r)
                     if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
         }
-        float mt = max_halves(fmaxf(max16(sacc[0]), max16(sacc[1])));
-        // every processed tile shows each query at least one key, so mt is finite
-        const bool bump = mt > m_run + kLazyMax;
-        const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-        if (bump) m_run = mt;
+        // Weights against the running max straight away; the lane's score max is
+        // checked beside them.  Only when some score lies more than kLazyMax above
+        // the running max (the first tile, or a real jump) is the row max taken and
+        // the weights recomputed, so the result is that of taking the row max
+        // first: m moves to it when it passes m + kLazyMax.
+        const float lmax = fmaxf(max16(sacc[0]), max16(sacc[1]));
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 pop[2 * kb + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_run);
+        // (issued ahead of the check, not sunk below it onto the max's critical path)
+        asm volatile("" : "+v"(pop[0]), "+v"(pop[1]), "+v"(pop[2]), "+v"(pop[3]));
+        if (__any(lmax > m_run + kLazyMax)) {
+            // every processed tile shows each query at least one key, so mt is finite
+            const float mt = max_halves(lmax);
+            const bool bump = mt > m_run + kLazyMax;
+            float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+            if (bump) m_run = mt;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    pop[2 * kb + (r >> 3)][r & 7] =
+                        (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_run);
+            l_run *= (double)alpha;
+            // alpha is 1 in rows without a bump; hidden from the optimiser, which
+            // would otherwise make the multiplication unconditional
+            asm volatile("" : "+v"(alpha));
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+        }
         // the denominator sums the weights as rounded for the P.V product, so the
         // output is a weighted mean of V with exactly the weights that were applied
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -623,13 +647,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 const bf16x2 pr = {pop[i][2 * e], pop[i][2 * e + 1]};
                 ps[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[e & 1], false);
             }
-        l_run = l_run * (double)alpha + (double)(ps[0] + ps[1]);
-        if (__any(bump)) {
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-        }
+        l_run += (double)(ps[0] + ps[1]);
     };
 
     // ---- prologue: K(0) in LDS, V buffer 1 (read by M(0) with P = 0) zeroed;
