@@ -60,27 +60,30 @@ typedef enum {
  *  PFA_PREC_BF16X3 as PFA_PREC_BF16 for P.V; the scores use Q and K each split
  *                  into a bf16 high part plus a bf16 low part (three products),
  *                  which keeps the score error from growing with large key norms.
- * The bf16 modes are available in gqa_prefill_attn; qk_prep_attn takes
- * PFA_PREC_F32 only (PFA_ERR_UNSUPPORTED otherwise). */
+ * Both attention entry points take every mode. */
 typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_precision;
 
-/* Device workspace in bytes that gqa_prefill_attn / qk_prep_attn use for these
- * arguments (the same seq_offsets, n_seqs, T, heads, head_dim and precision as
- * the call; enough for either entry point).  It holds, in this order:
+/* Device workspace in bytes that gqa_prefill_attn (fused = 0) or qk_prep_attn
+ * (fused = 1) uses for these arguments (the same seq_offsets, n_seqs, T, heads,
+ * head_dim and precision as the call).  It holds, in this order:
  *  - bf16 modes: K and V converted once to bf16 in 64-key tiles per sequence (K
  *    twice, high and low parts, for PFA_PREC_BF16X3),
  *      n_head_kv * sum_s ceil(len_s / 64) * 64 * head_dim * 2 * (2 or 3) bytes,
- *    then qk_prep_attn's rotary table, max_s(len_s) * (head_dim / 2) * 8 bytes;
- *  - any precision, short inputs only: when the (query block, head) work items
- *    cannot fill the GPU, each item's key range is split over several workgroups
- *    whose partial results (32 x head_dim f32 plus two f32 per row, per
- *    wavefront) are merged by one more kernel; 0 bytes otherwise.
- * For PFA_PREC_F32 the workspace is optional: without it (or with less than this)
- * the call runs without the key split.  Returns 0 when nothing is needed or the
+ *    then, for qk_prep_attn, a rotary table of max_s(len_s) * (head_dim / 2) * 8
+ *    bytes;
+ *  - PFA_PREC_F32, qk_prep_attn: the normalised, rotated K, T * n_head_kv *
+ *    head_dim * 4 bytes (not used when the call is given k_rot_out);
+ *  - any precision, short inputs only, at the next multiple of 256 bytes: when
+ *    the (query block, head) work items cannot fill the GPU, each item's key
+ *    range is split over several workgroups whose partial results (32 x head_dim
+ *    f32 plus two f32 per row, per wavefront) are merged by one more kernel;
+ *    0 bytes otherwise.
+ * For PFA_PREC_F32 the partial results are optional: without room for them the
+ * call runs without the key split.  Returns 0 when nothing is needed or the
  * arguments are ones the attention calls would reject (pfa_last_error() then
  * says why). */
 size_t pfa_workspace_bytes(const int32_t* seq_offsets, int n_seqs, int T, int n_head,
-                           int n_head_kv, int head_dim, int precision);
+                           int n_head_kv, int head_dim, int precision, int fused);
 
 /*
  * qknorm_rope -- QK-norm followed by NeoX rotary embedding, for Q and K at once.
@@ -135,7 +138,7 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
  *  scale  finite; precision  a pfa_precision value.
  *  workspace, workspace_bytes  device memory owned by the caller, 256-byte
  *        aligned, at least pfa_workspace_bytes(seq_offsets, n_seqs, T, n_head,
- *        n_head_kv, head_dim, precision) bytes, not overlapping the tensors; its
+ *        n_head_kv, head_dim, precision, 0) bytes, not overlapping the tensors; its
  *        contents are overwritten (calls in flight at the same time need separate
  *        workspaces).  Required for the bf16 modes; optional for PFA_PREC_F32
  *        (may be NULL: short inputs then run without the key split).
@@ -148,9 +151,10 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
 
 /*
  * qk_prep_attn -- the whole attention core in one call: qknorm_rope applied to
- * the raw Q and K, then gqa_prefill_attn, with the normalised and rotated Q and
- * K kept on chip (they are built inside the attention kernel as its Q and K
- * tiles are loaded).
+ * the raw Q and K, then gqa_prefill_attn.  The normalised, rotated Q never goes
+ * to memory (each attention workgroup builds its Q rows on chip); K is prepared
+ * once per call, into the workspace (bf16: straight into the bf16 tiles; f32:
+ * into k_rot_out when given, else the workspace).
  *
  * Passages: as for qknorm_rope and gqa_prefill_attn; needle-core v3/model.rs,
  * cache fill after the prefill (the keys a cache keeps are the normalised,
@@ -161,7 +165,10 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
  *  k_rot_out  NULL, or [T, n_head_kv*head_dim] f32, device: also receives the
  *        normalised, rotated K (what a KV cache would store); must not overlap
  *        the inputs or out.
- *  workspace, workspace_bytes  as for gqa_prefill_attn.
+ *  workspace, workspace_bytes  as for gqa_prefill_attn, at least
+ *        pfa_workspace_bytes(..., precision, 1) bytes; for PFA_PREC_F32 it may be
+ *        NULL only when k_rot_out is given (short inputs then run without the key
+ *        split).
  */
 int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
                  const float* q_norm_w, const float* k_norm_w,

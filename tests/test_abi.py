@@ -140,10 +140,11 @@ def _ceil(a, b):
     return -(-a // b)
 
 
-def _expected_workspace(lens, H, Hkv, D, prec):
-    """The workspace rule pfa_workspace_bytes documents, restated: bf16 tiles and rotary
-    table, plus partial results when the (query block, head) items cannot fill the GPU's
-    256 CUs once (2 f32 workgroups or 1 bf16 workgroup per CU) and are split by key."""
+def _expected_workspace(lens, H, Hkv, D, prec, fused):
+    """The workspace rule pfa_workspace_bytes documents, restated: bf16 tiles (plus the
+    rotary table for the fused entry) or the f32 fused entry's rotated K, then partial
+    results when the (query block, head) items cannot fill the GPU's 256 CUs once (2 f32
+    workgroups or 1 bf16 workgroup per CU) and are split by key."""
     bf16 = prec != 0
     waves, tile = (8, 64) if bf16 else (4, 32)
     g = H // Hkv
@@ -166,15 +167,18 @@ def _expected_workspace(lens, H, Hkv, D, prec):
     base = 0
     if bf16:
         base = Hkv * sum(_ceil(n, 64) for n in lens) * 64 * D * 2 * (3 if prec == 2 else 2)
-        base += max(lens) * (D // 2) * 8
+        if fused:
+            base += max(lens) * (D // 2) * 8
+    elif fused:
+        base = sum(lens) * Hkv * D * 4
     return (_ceil(base, 256) * 256 + parts) if parts else base
 
 
-def _ws(L, lens, H, Hkv, D, prec, pass_offsets=True):
+def _ws(L, lens, H, Hkv, D, prec, pass_offsets=True, fused=0):
     offs = np.cumsum([0] + list(lens)).astype(np.int32)
     arr = (ctypes.c_int32 * len(offs))(*offs.tolist())
     ptr = ctypes.cast(arr, ctypes.c_void_p) if pass_offsets else None
-    return L.pfa_workspace_bytes(ptr, len(lens), int(offs[-1]), H, Hkv, D, prec)
+    return L.pfa_workspace_bytes(ptr, len(lens), int(offs[-1]), H, Hkv, D, prec, fused)
 
 
 @pytest.mark.parametrize("lens,H,Hkv,D", [
@@ -182,18 +186,22 @@ def _ws(L, lens, H, Hkv, D, prec, pass_offsets=True):
     ((128, 256, 512, 1024, 2048, 3000, 4096, 5000), 16, 4, 128), ((16,), 4, 2, 64),
     ((300,), 8, 2, 128), ((1, 33, 0, 64, 65, 97), 4, 2, 128), ((90,), 6, 2, 64)])
 @pytest.mark.parametrize("prec", [0, 1, 2])
-def test_workspace_bytes_rule(L, lens, H, Hkv, D, prec):
-    assert _ws(L, lens, H, Hkv, D, prec) == _expected_workspace(lens, H, Hkv, D, prec)
+@pytest.mark.parametrize("fused", [0, 1])
+def test_workspace_bytes_rule(L, lens, H, Hkv, D, prec, fused):
+    assert _ws(L, lens, H, Hkv, D, prec, fused=fused) == \
+        _expected_workspace(lens, H, Hkv, D, prec, fused)
 
 
 def test_workspace_bytes_cases():
     # long inputs in f32 need nothing; the T = 512 shapes split their keys
     L = pfa.lib()
     assert _ws(L, (8192,), 32, 8, 128, 0) == 0
+    assert _ws(L, (8192,), 32, 8, 128, 0, fused=1) == 8192 * 8 * 128 * 4  # rotated K
     assert _ws(L, (512,), 16, 8, 128, 0) > 0
-    assert _ws(L, (8192,), 32, 8, 128, 1, pass_offsets=False) == \
+    assert _ws(L, (8192,), 32, 8, 128, 1, pass_offsets=False) == 8 * 128 * 64 * 128 * 2 * 2
+    assert _ws(L, (8192,), 32, 8, 128, 1, pass_offsets=False, fused=1) == \
         8 * 128 * 64 * 128 * 2 * 2 + 8192 * 64 * 8
-    assert pfa.workspace_bytes(8192, 32, 8, 128, "bf16x3") == \
+    assert pfa.workspace_bytes(8192, 32, 8, 128, "bf16x3", fused=True) == \
         8 * 128 * 64 * 128 * 2 * 3 + 8192 * 64 * 8
 
 
@@ -221,3 +229,19 @@ def test_bf16_modes_check_the_workspace(L, prec):
     assert "aligned" in _msg(L)
     assert _attn(L, prec=prec, ptrs=ptrs, ws=(3 << 20) + 4096, ws_bytes=need) == INVALID
     assert "overlap" in _msg(L)
+
+
+def test_f32_fused_needs_a_workspace_or_k_rot_out(L):
+    # the rotated K goes to k_rot_out or the workspace; with neither the call is refused
+    # before any launch (the pointers are not real)
+    p = ctypes.c_void_p
+    assert L.qk_prep_attn(p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p(5 << 20),
+                          p(5 << 20), None, 0, 16, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0,
+                          p(0), p(0), 0, None) == INVALID
+    assert "workspace" in _msg(L)
+    need = _ws(L, (16,), 4, 2, 64, 0, fused=1)
+    assert need == 16 * 2 * 64 * 4
+    assert L.qk_prep_attn(p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p(5 << 20),
+                          p(5 << 20), None, 0, 16, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0,
+                          p(0), p(8 << 20), need - 1, None) == INVALID
+    assert "needed" in _msg(L)

@@ -31,10 +31,10 @@
 //    key tiles of one head together while each XCD's L2 keeps them.
 //
 // PREP = true is the fused entry: raw Q rows are RMS-normalised and rotated once
-// as the Q tile is staged, and every K tile is normalised and rotated in
-// registers on its way into LDS -- between the score and context products of
-// the previous tile, so the matrix cores stay busy -- and optionally copied out
-// as the cache-ready K.
+// as the Q tile is staged.  K arrives already normalised and rotated (the entry
+// point prepares it once, into the caller's k_rot_out or the workspace, before
+// this kernel runs): preparing it per tile here would repeat the work in every
+// workgroup that visits the tile.
 #include "pfa_device.h"
 #include "pfa_internal.h"
 
@@ -113,16 +113,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
 
     // ---- work item (uniform across the workgroup)
     const WorkItem wi = decode_item(sched, geom, blockIdx.x);
-    const int kv = wi.kv, chunk = wi.chunk, sb = wi.sb, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
+    const int kv = wi.kv, chunk = wi.chunk, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
     // (the lambdas below must not capture the kernel-argument structs: taking their
     // address copies them into scratch memory and makes every value read from them
     // look divergent; they use these locals instead)
     const int rows_per_item = sched.rows_per_item;
     const int n_kv = geom.Hkv, n_q = geom.H;
-    float* const k_rot_out = prep.k_rot_out;
     const float* const k_in = k;
-    const int rope_dim = prep.rope_dim;
-    const float rms_eps = prep.eps;
     const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
     const int n_tiles =
         geom.causal ? (min(q0 + rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
@@ -142,12 +139,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const int wave_tiles = geom.causal ? min(diag_tile + 1, nt_seq) : nt_seq;
     const int qi = wq0 + ln;
 
-    // Fused entry, per lane: norm weights and rotary frequency (turns per position)
-    // of its dims L + 64e, and the cos/sin of a 4-position step (K rows of one
-    // wavefront are 4 positions apart inside a tile).
+    // Fused entry, per lane: Q norm weights and rotary frequency (turns per position)
+    // of its dims L + 64e.
     constexpr int E = D / 64;
     double turns[E];
-    float wqv[E], wkv[E], c4s[E], s4s[E];
+    float wqv[E];
     if constexpr (PREP) {
         const int half = prep.rope_dim >> 1;
 #pragma unroll
@@ -157,8 +153,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
                            ? rope_turns_per_pos(c < half ? c : c - half, prep.rope_dim, prep.base)
                            : 0.0;
             wqv[e] = prep.wq[c];
-            wkv[e] = prep.wk[c];
-            rope_cos_sin(kWaves, turns[e], c4s[e], s4s[e]);
         }
     }
 
@@ -252,60 +246,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             *reinterpret_cast<floatx4*>(dst + row * stride + 4 * c4) = kvreg[i];
         }
     };
-    // Fused entry: the raw K rows of a tile in the wave-per-row layout (wavefront w
-    // owns rows w, w+4, ..., lane L dims L + 64e), normalised and rotated in
-    // registers and then written to the LDS tile (and, by exactly one workgroup --
-    // the first head chunk of the super-block covering those rows -- to k_rot_out).
-    constexpr int KR = kBN / kWaves;  // rows per wavefront
-    float kraw[KR][E];
-    auto load_k_prep = [&](int t) {
-        const auto r = tile_rsrc(k_in, t);
-#pragma unroll
-        for (int i = 0; i < KR; ++i)
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                kraw[i][e] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(
-                               r, (wave + kWaves * i) * row_bytes + 4 * (lane + 64 * e), 0, 0));
-    };
-    auto prep_store_k = [&](float* ks, int t, bool real) {
-        if constexpr (PREP) {
-            const int k0 = s0 + t * kBN;
-            // angle of row `wave`, then one 4-position turn per further row
-            float cs[E], sn[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) rope_cos_sin(k0 + wave - s0, turns[e], cs[e], sn[e]);
-            const bool writer = real && k_rot_out && chunk == 0 && (t * kBN) / rows_per_item == sb;
-#pragma unroll
-            for (int i = 0; i < KR; ++i) {
-                prep_row<D>(kraw[i], wkv, cs, sn, rope_dim, rms_eps, lane);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float c = cs[e] * c4s[e] - sn[e] * s4s[e];
-                    sn[e] = sn[e] * c4s[e] + cs[e] * s4s[e];
-                    cs[e] = c;
-                }
-                const int row = wave + kWaves * i;
-                const bool ok = k0 + row < s1;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float y = ok ? kraw[i][e] : 0.0f;
-                    ks[row * KS + lane + 64 * e] = y;
-                    if (writer && ok)
-                        k_rot_out[((int64_t)(k0 + row) * n_kv + kv) * D + lane + 64 * e] = y;
-                }
-            }
-        }
-    };
-    auto load_k_tile = [&](int t) {
-        if constexpr (PREP) load_k_prep(t);
-        else load_rows(k_in, t);
-    };
-    auto store_k_tile = [&](float* ks, int t) {
-        if constexpr (PREP) prep_store_k(ks, t, true);
-        else store_rows(ks, KS);
-    };
-
     // ---- accumulators
     floatx16 oacc[NCB];
 #pragma unroll
@@ -319,8 +259,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     float m_run = -INFINITY;
     double l_run = 0.0;
 
-    load_k_tile(t_begin);
-    store_k_tile(smem, t_begin);
+    load_rows(k_in, t_begin);
+    store_rows(smem, KS);
     load_rows(v, t_begin);
     store_rows(smem + kBN * KS, VS);
     __syncthreads();
@@ -329,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
         const int cur = (t - t_begin) & 1;
         const bool more = t + 1 < t_end;
         float* kn = smem + (cur ^ 1) * BUF;
-        if (more) load_k_tile(t + 1);
+        if (more) load_rows(k_in, t + 1);
         if (active && t < wave_tiles) {
             const float* ks = smem + cur * BUF;
             const float* vs = ks + kBN * KS;
@@ -395,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             }
             l_run = l_run * (double)alpha + (double)psum;
             if (more) {
-                if constexpr (!PREP) store_rows(kn, KS);
+                store_rows(kn, KS);
                 load_rows(v, t + 1);
             }
             // O^T[d][query] = alpha * O^T + sum_key V[key][d] P[query][key].  Each
@@ -427,16 +367,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             }
         } else if (more) {
             // this wavefront has no work on tile t but still stages tile t+1
-            if constexpr (!PREP) store_rows(kn, KS);
+            store_rows(kn, KS);
             load_rows(v, t + 1);
         }
-        if (more) {
-            // fused entry: the raw K rows of tile t+1 (loaded at the top of this
-            // tile) are normalised and rotated here, where the score registers are
-            // free, while the context MFMAs are still draining
-            if constexpr (PREP) prep_store_k(kn, t + 1, true);
-            store_rows(kn + kBN * KS, VS);
-        }
+        if (more) store_rows(kn + kBN * KS, VS);
         __syncthreads();
     }
 

@@ -151,6 +151,7 @@ struct Plan {
     int waves = 0, tile_keys = 0;
     size_t tile_bytes = 0;   // bf16: K/V tiles
     size_t table_bytes = 0;  // bf16 fused entry: rotary table (max_len x d/2 pairs)
+    size_t krot_bytes = 0;   // f32 fused entry: the normalised, rotated K (T x Hkv x d)
     size_t part_bytes = 0;   // key split: partial results
 };
 
@@ -199,8 +200,18 @@ int make_plan(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim, 
         p.tile_bytes = pfa::bf16_workspace_bytes(p.sched.n_tiles, n_head_kv, head_dim,
                                                  precision == PFA_PREC_BF16X3, 0);
         p.table_bytes = pfa::bf16_workspace_bytes(0, n_head_kv, head_dim, false, p.sched.max_len);
+    } else {
+        p.krot_bytes = (size_t)st.off[st.n_seqs] * n_head_kv * head_dim * 4;
     }
     return PFA_OK;
+}
+
+// Workspace bytes ahead of the partial results: the bf16 K/V tiles (+ the rotary
+// table for the fused entry), or for the f32 fused entry the rotated K unless it
+// goes to the caller's k_rot_out.
+size_t prep_part_bytes(const Plan& p, bool bf16, bool fused, bool k_rot_given) {
+    if (bf16) return p.tile_bytes + (fused ? p.table_bytes : 0);
+    return fused && !k_rot_given ? p.krot_bytes : 0;
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -218,7 +229,7 @@ const char* pfa_last_error(void) { return g_err; }
 const char* pfa_version(void) { return "pfa 0.3 (gfx950; f32 and bf16 MFMA attention)"; }
 
 size_t pfa_workspace_bytes(const int32_t* seq_offsets, int n_seqs, int T, int n_head,
-                           int n_head_kv, int head_dim, int precision) {
+                           int n_head_kv, int head_dim, int precision, int fused) {
     g_err[0] = 0;
     if (check_geometry(T, n_head, n_head_kv, head_dim)) return 0;
     if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) {
@@ -232,9 +243,8 @@ size_t pfa_workspace_bytes(const int32_t* seq_offsets, int n_seqs, int T, int n_
     Plan p;
     if (make_plan(st, n_head, n_head_kv, head_dim, 1.0f, 1, precision, p)) return 0;
     if (p.items == 0) return 0;
-    // room for both entry points: the rotary table is reserved even if only the fused one uses it
-    return p.part_bytes ? align256(p.tile_bytes + p.table_bytes) + p.part_bytes
-                        : p.tile_bytes + p.table_bytes;
+    const size_t base = prep_part_bytes(p, precision != PFA_PREC_F32, fused != 0, false);
+    return p.part_bytes ? align256(base) + p.part_bytes : base;
 }
 
 int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
@@ -290,8 +300,9 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
     if ((rc = make_plan(st, n_head, n_head_kv, head_dim, scale, causal, precision, p))) return rc;
     if (p.items == 0) return PFA_OK;
     const bool bf16 = precision != PFA_PREC_F32;
-    // workspace parts: [bf16 K/V tiles][rotary table, fused entry][partials, key split]
-    const size_t base = p.tile_bytes + (prep ? p.table_bytes : 0);
+    // workspace parts: [bf16 K/V tiles + rotary table (fused), or f32 rotated K (fused,
+    // no k_rot_out)][partials, key split]
+    const size_t base = prep_part_bytes(p, bf16, prep != nullptr, prep && prep->k_rot_out);
     const size_t part_off = p.part_bytes ? align256(base) : base;
     if (!bf16 && p.part_bytes &&
         (!workspace || workspace_bytes < part_off + p.part_bytes)) {
@@ -328,8 +339,22 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
                                                 precision == PFA_PREC_BF16X3, prep, part, p.items,
                                                 (hipStream_t)stream),
                           prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
-    return hip_status(pfa::launch_attn_f32(q, k, v, out, p.sched, p.geom, head_dim, prep, part,
-                                           p.items, (hipStream_t)stream),
+    const float* k_attn = k;
+    if (prep) {
+        // f32 fused entry: K is normalised and rotated once, by the QK-norm + RoPE
+        // kernel over the K rows alone, into k_rot_out or the workspace; the
+        // attention kernel then prepares only its own Q rows
+        float* krot = prep->k_rot_out ? prep->k_rot_out : static_cast<float*>(workspace);
+        if ((rc = hip_status(pfa::launch_qknorm_rope(nullptr, k, nullptr, krot, prep->wq, prep->wk,
+                                                     st, T, 0, n_head_kv, head_dim, prep->rope_dim,
+                                                     (float)prep->base, prep->eps,
+                                                     (hipStream_t)stream),
+                             "qk_prep_attn launch")))
+            return rc;
+        k_attn = krot;
+    }
+    return hip_status(pfa::launch_attn_f32(q, k_attn, v, out, p.sched, p.geom, head_dim, prep,
+                                           part, p.items, (hipStream_t)stream),
                       prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
 }
 

@@ -60,7 +60,7 @@ def lib() -> ctypes.CDLL:
     L.qk_prep_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
                                f32, i32, i32, fp_, vp, sz, vp]
     L.qk_prep_attn.restype = i32
-    L.pfa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32]
+    L.pfa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_workspace_bytes.restype = sz
     L.pfa_last_error.restype = ctypes.c_char_p
     L.pfa_last_error.argtypes = []
@@ -134,17 +134,18 @@ def _prec(precision):
 
 
 def workspace_bytes(T: int, n_head: int, n_head_kv: int, head_dim: int, precision="f32",
-                    seq_offsets: Optional[Sequence[int]] = None) -> int:
-    """Device workspace the attention calls use for these arguments (``pfa_workspace_bytes``)."""
+                    seq_offsets: Optional[Sequence[int]] = None, fused: bool = False) -> int:
+    """Device workspace ``gqa_prefill_attn`` (``fused=False``) or ``qk_prep_attn``
+    (``fused=True``) uses for these arguments (``pfa_workspace_bytes``)."""
     offs, n_seqs, op = _offsets(seq_offsets, T)
     return int(lib().pfa_workspace_bytes(op, n_seqs, T, n_head, n_head_kv, head_dim,
-                                         _prec(precision)))
+                                         _prec(precision), 1 if fused else 0))
 
 
-def _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, device):
+def _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, fused, device):
     """(tensor, pointer, size) of the caller's workspace, or of a new one from torch's allocator."""
     import torch
-    need = int(lib().pfa_workspace_bytes(op, n_seqs, T, H, Hkv, head_dim, prec))
+    need = int(lib().pfa_workspace_bytes(op, n_seqs, T, H, Hkv, head_dim, prec, 1 if fused else 0))
     if need == 0:
         return None, ctypes.c_void_p(0), 0
     if workspace is None:
@@ -200,7 +201,7 @@ def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
         scale = head_dim ** -0.5
     offs, n_seqs, op = _offsets(seq_offsets, T)
     prec = _prec(precision)
-    ws, wp, wn = _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, q.device)
+    ws, wp, wn = _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, False, q.device)
     _check(lib().gqa_prefill_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), op, n_seqs, T, H, Hkv,
                                   head_dim, float(scale), 1 if causal else 0, prec, wp, wn,
                                   _stream(q)))
@@ -214,7 +215,9 @@ def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
                  workspace=None):
     """Fused QK-norm + RoPE + causal GQA attention (``qk_prep_attn`` in ``include/pfa.h``).
 
-    Returns ``out`` (and also writes ``k_rot_out`` when one is given)."""
+    Returns ``out`` (and also writes ``k_rot_out`` when one is given).  The device
+    workspace (``workspace_bytes(..., fused=True)`` bytes) is ``workspace`` or one
+    taken from torch's allocator."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
         _dev_f32(t, n)
@@ -233,7 +236,7 @@ def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
         scale = head_dim ** -0.5
     offs, n_seqs, op = _offsets(seq_offsets, T)
     prec = _prec(precision)
-    ws, wp, wn = _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, q.device)
+    ws, wp, wn = _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, True, q.device)
     _check(lib().qk_prep_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(q_norm_w),
                               _ptr(k_norm_w), op, n_seqs, T, H, Hkv, head_dim, rope_dim,
                               float(rope_freq_base), float(rms_eps), float(scale),
