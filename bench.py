@@ -205,8 +205,13 @@ def main():
                   f"attn_bf16_kernel<{w.head_dim},{split},{fused}>")
         if args.path == "fused":
             kernel = f"rope_table_kernel<{w.head_dim},{split}> + " + kernel
+    elif args.path == "fused":
+        # the f32 fused entry: K prepared once (QK-norm + RoPE over the K rows), then
+        # the attention kernel preparing its own Q rows
+        mode = 0 if w.rope_dim == w.head_dim == 128 else (1 if w.rope_dim == 64 else 2)
+        kernel = f"qknorm_rope_kernel<{w.head_dim},{mode}> + attn_f32_kernel<{w.head_dim},true>"
     else:
-        kernel = f"attn_f32_kernel<{w.head_dim},{'true' if args.path == 'fused' else 'false'}>"
+        kernel = f"attn_f32_kernel<{w.head_dim},false>"
     traffic = load_traffic(w.name, kernel, args.precision, args.path)
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
