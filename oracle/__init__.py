@@ -58,6 +58,16 @@ def _load():
                                     ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                     lp, ctypes.c_int64, dp, ctypes.c_int]
     lib.oracle_gqa_attn.restype = ctypes.c_int
+    lib.oracle_qknorm_rope_from.argtypes = [fp, fp, fp, fp, ip, ctypes.c_int, lp, ctypes.c_int64,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_double, ctypes.c_double, dp,
+                                            dp, ctypes.c_int]
+    lib.oracle_qknorm_rope_from.restype = ctypes.c_int
+    lib.oracle_chunk_attn.argtypes = [dp, dp, dp, ip, ip, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_double, ctypes.c_int, lp, ctypes.c_int64, dp,
+                                      ctypes.c_int]
+    lib.oracle_chunk_attn.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -74,8 +84,9 @@ def _offsets(seq_offsets, T):
 
 
 def qknorm_rope(q, k, wq, wk, *, n_head, n_head_kv, head_dim, rope_dim, rope_freq_base,
-                rms_eps, seq_offsets=None, n_threads=0):
+                rms_eps, seq_offsets=None, pos0=None, n_threads=0):
     """O1 + O2 on f32 inputs ``q [T, n_head*head_dim]``, ``k [T, n_head_kv*head_dim]``.
+    Row r of sequence s sits at position ``pos0[s] + r`` (``pos0`` None: r).
 
     Returns ``(q', k')`` as float64 arrays of the same shapes."""
     q = np.ascontiguousarray(q, dtype=np.float32)
@@ -90,12 +101,20 @@ def qknorm_rope(q, k, wq, wk, *, n_head, n_head_kv, head_dim, rope_dim, rope_fre
     offs = _offsets(seq_offsets, T)
     qo = np.empty((T, n_head * head_dim), dtype=np.float64)
     ko = np.empty((T, n_head_kv * head_dim), dtype=np.float64)
-    rc = _load().oracle_qknorm_rope(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
-                                    _ptr(wq, ctypes.c_float), _ptr(wk, ctypes.c_float),
-                                    _ptr(offs, ctypes.c_int32), len(offs) - 1, T, n_head,
-                                    n_head_kv, head_dim, rope_dim, float(rope_freq_base),
-                                    float(rms_eps), _ptr(qo, ctypes.c_double),
-                                    _ptr(ko, ctypes.c_double), n_threads)
+    if pos0 is None:
+        p0 = None
+    else:
+        p0 = np.ascontiguousarray(pos0, dtype=np.int64)
+        if p0.size != len(offs) - 1:
+            raise ValueError("pos0 needs one entry per sequence")
+    rc = _load().oracle_qknorm_rope_from(_ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                         _ptr(wq, ctypes.c_float), _ptr(wk, ctypes.c_float),
+                                         _ptr(offs, ctypes.c_int32), len(offs) - 1,
+                                         None if p0 is None else _ptr(p0, ctypes.c_int64), T,
+                                         n_head, n_head_kv, head_dim, rope_dim,
+                                         float(rope_freq_base), float(rms_eps),
+                                         _ptr(qo, ctypes.c_double), _ptr(ko, ctypes.c_double),
+                                         n_threads)
     if rc != 0:
         raise ValueError(f"oracle_qknorm_rope failed ({rc})")
     return qo, ko
@@ -141,6 +160,75 @@ def qk_prep_attn(q, k, v, wq, wk, *, n_head, n_head_kv, head_dim, rope_dim, rope
                    scale=scale, causal=causal, seq_offsets=seq_offsets, rows=rows,
                    n_threads=n_threads)
     return (out, kn) if return_k_rot else out
+
+
+def chunk_attn(q, k_cache, v_cache, *, n_head, n_head_kv, head_dim, scale, causal=True,
+               q_offsets=None, kv_offsets=None, rows=None, n_threads=0):
+    """Attention of the query rows ``q [T_q, n_head*head_dim]`` over a K/V cache
+    ``k_cache``/``v_cache [T_kv, n_head_kv*head_dim]``: sequence s owns query rows
+    ``q_offsets[s]..q_offsets[s+1]`` and cache rows ``kv_offsets[s]..kv_offsets[s+1]``
+    (at least as many); its queries are the last rows of its cache, so query row r sits
+    at position ``base_s + r`` with ``base_s`` the rows cached before.  Causal: row r
+    sees cache rows 0 .. base_s + r of its sequence.  Offsets: both or neither."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k_cache, dtype=np.float64)
+    v = np.ascontiguousarray(v_cache, dtype=np.float64)
+    T_q, T_kv = q.shape[0], k.shape[0]
+    if q.size != T_q * n_head * head_dim or k.size != T_kv * n_head_kv * head_dim or \
+            v.size != k.size:
+        raise ValueError("q/k/v shapes do not match the head geometry")
+    if (q_offsets is None) != (kv_offsets is None):
+        raise ValueError("give both offset arrays or neither")
+    qo = _offsets(q_offsets, T_q)
+    ko = _offsets(kv_offsets, T_kv)
+    if rows is None:
+        n_rows, rp = T_q, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows, rp = rows_arr.size, _ptr(rows_arr, ctypes.c_int64)
+    out = np.empty((n_rows, n_head * head_dim), dtype=np.float64)
+    rc = _load().oracle_chunk_attn(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                   _ptr(v, ctypes.c_double), _ptr(qo, ctypes.c_int32),
+                                   _ptr(ko, ctypes.c_int32), len(qo) - 1, T_q, T_kv, n_head,
+                                   n_head_kv, head_dim, float(scale), 1 if causal else 0, rp,
+                                   n_rows, _ptr(out, ctypes.c_double), n_threads)
+    if rc != 0:
+        raise ValueError(f"oracle_chunk_attn failed ({rc})")
+    return out
+
+
+def qk_prep_chunk_attn(q, k, v, wq, wk, k_cache, v_cache, *, n_head, n_head_kv, head_dim,
+                       rope_dim, rope_freq_base, rms_eps, scale, causal=True, q_offsets=None,
+                       kv_offsets=None, rows=None, n_threads=0):
+    """A block of new rows over a cache: the raw f32 ``q``, ``k``, ``v [T_q, ...]`` are
+    normalised and rotated (Q and K) at the positions of the new rows, K and V are
+    written into the last rows of each sequence's cache range, and the queries attend
+    the cache (:func:`chunk_attn`).  ``k_cache``/``v_cache [T_kv, ...]`` supply the rows
+    cached before (their other rows are ignored).  Returns ``(out, k_cache', v_cache')``
+    in f64, the caches with the new rows in place."""
+    T_q = np.asarray(q).shape[0]
+    T_kv = np.asarray(k_cache).shape[0]
+    if (q_offsets is None) != (kv_offsets is None):
+        raise ValueError("give both offset arrays or neither")
+    qo = _offsets(q_offsets, T_q)
+    ko = _offsets(kv_offsets, T_kv)
+    base = (ko[1:] - ko[:-1]) - (qo[1:] - qo[:-1])
+    if np.any(base < 0):
+        raise ValueError("a sequence has fewer cache rows than new rows")
+    qn, kn = qknorm_rope(q, k, wq, wk, n_head=n_head, n_head_kv=n_head_kv, head_dim=head_dim,
+                         rope_dim=rope_dim, rope_freq_base=rope_freq_base, rms_eps=rms_eps,
+                         seq_offsets=qo, pos0=base, n_threads=n_threads)
+    kc = np.array(k_cache, dtype=np.float64, copy=True).reshape(T_kv, n_head_kv * head_dim)
+    vc = np.array(v_cache, dtype=np.float64, copy=True).reshape(T_kv, n_head_kv * head_dim)
+    v = np.asarray(v, dtype=np.float64).reshape(T_q, n_head_kv * head_dim)
+    for s in range(len(qo) - 1):
+        dst = slice(int(ko[s] + base[s]), int(ko[s + 1]))
+        kc[dst] = kn[qo[s]:qo[s + 1]]
+        vc[dst] = v[qo[s]:qo[s + 1]]
+    out = chunk_attn(qn, kc, vc, n_head=n_head, n_head_kv=n_head_kv, head_dim=head_dim,
+                     scale=scale, causal=causal, q_offsets=qo, kv_offsets=ko, rows=rows,
+                     n_threads=n_threads)
+    return out, kc, vc
 
 
 def version() -> str:

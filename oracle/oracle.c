@@ -28,6 +28,13 @@
  *  - memra-engine 0.101.0 src/spec.rs, `full_attn_verify`, per-row fallback:
  *    row r of a block attends base_len + r + 1 keys, i.e. itself and every
  *    earlier key (the diagonal is visible).
+ *  - same function: a block of t new rows over a cache that already holds
+ *    base_len rows is normalised and rotated at the positions of the new rows,
+ *    its K and V are appended to the cache, and row r then attends cache rows
+ *    0 .. base_len + r (the chunk entry points below; base_len = 0 is plain
+ *    prefill).
+ *  - needle-core v3/model.rs, cache fill after the prefill: what a cache keeps
+ *    are the normalised, rotated keys and the values.
  *
  * Readings taken where the pages are silent (each one is listed with its
  * reason in the design notes of the repository):
@@ -167,6 +174,7 @@ typedef struct {
     const float* w;     /* [d] */
     double* out;        /* [T, heads*d] */
     const int32_t* offsets;
+    const int64_t* pos0; /* position of each sequence's first row; NULL: all 0 */
     int n_seqs, heads, d, n;
     double base, eps;
 } qknorm_ctx;
@@ -177,6 +185,7 @@ static void qknorm_unit(void* vctx, int64_t unit, double* scratch) {
     int h = (int)(unit % c->heads);
     int s = seq_of_token(c->offsets, c->n_seqs, t);
     int64_t pos = t - c->offsets[s];
+    if (c->pos0) pos += c->pos0[s];
     double* x = scratch;         /* d */
     double* w = scratch + c->d;  /* d */
     const float* src = c->x + (t * c->heads + h) * (int64_t)c->d;
@@ -191,11 +200,13 @@ static void qknorm_unit(void* vctx, int64_t unit, double* scratch) {
 
 /* O1 then O2 on every head row of Q (n_head heads, scale wq) and K (n_head_kv
  * heads, scale wk).  Inputs are f32 as the GPU receives them; outputs are f64.
- * seq_offsets may be NULL (one sequence [0, T)). */
-int oracle_qknorm_rope(const float* q, const float* k, const float* wq, const float* wk,
-                       const int32_t* seq_offsets, int n_seqs, int64_t T, int n_head,
-                       int n_head_kv, int head_dim, int rope_dim, double base, double eps,
-                       double* q_out, double* k_out, int n_threads) {
+ * seq_offsets may be NULL (one sequence [0, T)).  Row r of sequence s sits at
+ * position pos0[s] + r (pos0 NULL: r). */
+int oracle_qknorm_rope_from(const float* q, const float* k, const float* wq, const float* wk,
+                            const int32_t* seq_offsets, int n_seqs, const int64_t* pos0,
+                            int64_t T, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                            double base, double eps, double* q_out, double* k_out,
+                            int n_threads) {
     int32_t one[2];
     if (T < 0 || n_head <= 0 || n_head_kv <= 0 || head_dim <= 0 || rope_dim < 0 ||
         rope_dim > head_dim || (rope_dim & 1) || !(base > 0.0) || eps < 0.0)
@@ -208,21 +219,36 @@ int oracle_qknorm_rope(const float* q, const float* k, const float* wq, const fl
         n_seqs = 1;
     }
     if (!check_offsets(seq_offsets, n_seqs, T)) return ORACLE_BAD_ARG;
-    qknorm_ctx c = {q, wq, q_out, seq_offsets, n_seqs, n_head, head_dim, rope_dim, base, eps};
+    for (int s = 0; pos0 && s < n_seqs; ++s)
+        if (pos0[s] < 0) return ORACLE_BAD_ARG;
+    qknorm_ctx c = {q, wq, q_out, seq_offsets, pos0, n_seqs, n_head, head_dim, rope_dim, base,
+                    eps};
     int rc = run_pool(qknorm_unit, &c, T * n_head, 2 * (size_t)head_dim, n_threads);
     if (rc) return rc;
-    qknorm_ctx ck = {k, wk, k_out, seq_offsets, n_seqs, n_head_kv, head_dim, rope_dim, base, eps};
+    qknorm_ctx ck = {k, wk, k_out, seq_offsets, pos0, n_seqs, n_head_kv, head_dim, rope_dim,
+                     base, eps};
     return run_pool(qknorm_unit, &ck, T * n_head_kv, 2 * (size_t)head_dim, n_threads);
+}
+
+/* As oracle_qknorm_rope_from with every sequence starting at position 0. */
+int oracle_qknorm_rope(const float* q, const float* k, const float* wq, const float* wk,
+                       const int32_t* seq_offsets, int n_seqs, int64_t T, int n_head,
+                       int n_head_kv, int head_dim, int rope_dim, double base, double eps,
+                       double* q_out, double* k_out, int n_threads) {
+    return oracle_qknorm_rope_from(q, k, wq, wk, seq_offsets, n_seqs, NULL, T, n_head,
+                                   n_head_kv, head_dim, rope_dim, base, eps, q_out, k_out,
+                                   n_threads);
 }
 
 /* ------------------------------------------------------------------------ */
 /* O3 -- causal grouped-query attention, one (query row, head) per unit       */
 
 typedef struct {
-    const double *q, *k, *v; /* [T, H*d], [T, Hkv*d], [T, Hkv*d] */
+    const double *q, *k, *v; /* [T_q, H*d], [T_kv, Hkv*d], [T_kv, Hkv*d] */
     double* out;             /* [n_rows, H*d] */
-    const int64_t* rows;     /* NULL: row r of out is token r */
-    const int32_t* offsets;
+    const int64_t* rows;     /* NULL: row r of out is query row r */
+    const int32_t* offsets;    /* query rows of each sequence */
+    const int32_t* kv_offsets; /* key rows of each sequence (the same for plain prefill) */
     int n_seqs, H, Hkv, d, causal;
     double scale;
 } attn_ctx;
@@ -233,8 +259,12 @@ static void attn_unit(void* vctx, int64_t unit, double* e) {
     int h = (int)(unit % c->H);
     int64_t i = c->rows ? c->rows[r] : r;
     int s = seq_of_token(c->offsets, c->n_seqs, i);
-    int64_t lo = c->offsets[s];
-    int64_t hi = c->causal ? i : (int64_t)c->offsets[s + 1] - 1; /* inclusive */
+    /* the sequence's keys: its base rows already cached, then one per query row;
+     * the query row sits at the key of its own position, `last` */
+    int64_t lo = c->kv_offsets[s];
+    int64_t base = ((int64_t)c->kv_offsets[s + 1] - lo) - (c->offsets[s + 1] - c->offsets[s]);
+    int64_t last = lo + base + (i - c->offsets[s]);
+    int64_t hi = c->causal ? last : (int64_t)c->kv_offsets[s + 1] - 1; /* inclusive */
     int g = c->H / c->Hkv;
     int kv = h / g;
     int d = c->d;
@@ -267,29 +297,56 @@ static void attn_unit(void* vctx, int64_t unit, double* e) {
     for (int x = 0; x < d; ++x) o[x] /= Z;
 }
 
+/* Attention of query rows over a K/V cache.  Sequence s owns query rows
+ * q_offsets[s] .. q_offsets[s+1]-1 and cache rows kv_offsets[s] ..
+ * kv_offsets[s+1]-1, at least as many as queries: its first base_s cache rows
+ * were there before, the query rows are the last ones.  out[r, h, :] =
+ * softmax_j(scale * q[i,h,:] . k[j,kv,:]) v[j,kv,:] over the visible keys j of
+ * row i = rows[r] (or r when rows is NULL): the keys of i's sequence, and when
+ * causal only those up to i's own position (base_s + i - q_offsets[s]).  All
+ * arithmetic in f64.  NULL offsets (both): one sequence. */
+int oracle_chunk_attn(const double* q, const double* k, const double* v,
+                      const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                      int64_t T_q, int64_t T_kv, int n_head, int n_head_kv, int head_dim,
+                      double scale, int causal, const int64_t* rows, int64_t n_rows,
+                      double* out, int n_threads) {
+    int32_t one_q[2], one_kv[2];
+    if (T_q < 0 || T_kv < 0 || n_head <= 0 || n_head_kv <= 0 || head_dim <= 0 ||
+        n_head % n_head_kv || (!q_offsets) != (!kv_offsets))
+        return ORACLE_BAD_ARG;
+    if (!q_offsets) {
+        one_q[0] = 0;
+        one_q[1] = (int32_t)T_q;
+        one_kv[0] = 0;
+        one_kv[1] = (int32_t)T_kv;
+        q_offsets = one_q;
+        kv_offsets = one_kv;
+        n_seqs = 1;
+    }
+    if (!check_offsets(q_offsets, n_seqs, T_q) || !check_offsets(kv_offsets, n_seqs, T_kv))
+        return ORACLE_BAD_ARG;
+    for (int s = 0; s < n_seqs; ++s)
+        if (kv_offsets[s + 1] - kv_offsets[s] < q_offsets[s + 1] - q_offsets[s])
+            return ORACLE_BAD_ARG;
+    if (T_q == 0) return ORACLE_OK;
+    if (!rows) n_rows = T_q;
+    for (int64_t r = 0; rows && r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= T_q) return ORACLE_BAD_ARG;
+    attn_ctx c = {q, k, v, out, rows, q_offsets, kv_offsets, n_seqs, n_head, n_head_kv,
+                  head_dim, causal ? 1 : 0, scale};
+    return run_pool(attn_unit, &c, n_rows * n_head, (size_t)T_kv, n_threads); /* scores: <= T_kv */
+}
+
 /* out[r, h, :] = softmax_j(scale * q[i,h,:] . k[j,kv,:]) v[j,kv,:] over the
  * visible keys j of row i = rows[r] (or r when rows is NULL).  Visible: same
- * sequence as i and, when causal, j <= i.  All arithmetic in f64. */
+ * sequence as i and, when causal, j <= i.  All arithmetic in f64.  (The chunk
+ * case with nothing cached before: each sequence's keys are its query rows.) */
 int oracle_gqa_attn(const double* q, const double* k, const double* v,
                     const int32_t* seq_offsets, int n_seqs, int64_t T, int n_head,
                     int n_head_kv, int head_dim, double scale, int causal,
                     const int64_t* rows, int64_t n_rows, double* out, int n_threads) {
-    int32_t one[2];
-    if (T < 0 || n_head <= 0 || n_head_kv <= 0 || head_dim <= 0 || n_head % n_head_kv)
-        return ORACLE_BAD_ARG;
-    if (T == 0) return ORACLE_OK;
-    if (!seq_offsets) {
-        one[0] = 0;
-        one[1] = (int32_t)T;
-        seq_offsets = one;
-        n_seqs = 1;
-    }
-    if (!check_offsets(seq_offsets, n_seqs, T)) return ORACLE_BAD_ARG;
-    if (!rows) n_rows = T;
-    for (int64_t r = 0; rows && r < n_rows; ++r)
-        if (rows[r] < 0 || rows[r] >= T) return ORACLE_BAD_ARG;
-    attn_ctx c = {q, k, v, out, rows, seq_offsets, n_seqs, n_head, n_head_kv, head_dim, causal ? 1 : 0, scale};
-    return run_pool(attn_unit, &c, n_rows * n_head, (size_t)T, n_threads); /* scores: <= T */
+    return oracle_chunk_attn(q, k, v, seq_offsets, seq_offsets, n_seqs, T, T, n_head,
+                             n_head_kv, head_dim, scale, causal, rows, n_rows, out, n_threads);
 }
 
 const char* oracle_version(void) { return "pfa-oracle 1 (f64, plain loops)"; }

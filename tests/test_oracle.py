@@ -467,3 +467,102 @@ def test_workload_generator_is_seeded_and_shaped():
     assert wl.CONFIGS["mixed"].seq_offsets.tolist() == [0, 128, 384, 896, 1920, 3968, 6968,
                                                         11064, 16064]
     assert wl.CONFIGS["prefill_8192"].attn_flops() == 4 * 128 * 32 * (8192 * 8193 // 2)
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill over a cached prefix (memra-engine 0.101.0 src/spec.rs,
+# `full_attn_verify`: new rows are normalised and rotated at their positions,
+# appended to the cache, and row r attends cache rows 0 .. base_len + r).
+
+def _chunk_case(seed, lens, bases, H=4, Hkv=2, d=16, n=16):
+    """Raw inputs of len + base rows per sequence, split into the cached prefix
+    (the first base rows of each) and the new rows (the rest)."""
+    r = _rng(seed)
+    tot = [b + n_ for b, n_ in zip(bases, lens)]
+    T = sum(tot)
+    q = r.standard_normal((T, H * d)).astype(np.float32)
+    k = r.standard_normal((T, Hkv * d)).astype(np.float32)
+    v = r.standard_normal((T, Hkv * d))
+    wq = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    wk = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    kv_offs = np.concatenate([[0], np.cumsum(tot)]).astype(np.int32)
+    q_offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    new = np.concatenate([np.arange(kv_offs[s] + bases[s], kv_offs[s + 1])
+                          for s in range(len(lens))]).astype(np.int64)
+    return q, k, v, wq, wk, kv_offs, q_offs, new
+
+
+@pytest.mark.parametrize("lens,bases", [((7,), (5,)), ((1,), (9,)), ((6,), (0,)),
+                                        ((3, 4, 1), (2, 0, 6)), ((0, 5), (3, 1))])
+def test_chunk_over_prefix_equals_rows_of_full_prefill(lens, bases):
+    # The whole sequences prefilled at once and the new rows run over the cached
+    # prefix are the same computation: bit-identical outputs, and the cache rows the
+    # chunk writes are the full prefill's rotated K and the values.
+    H, Hkv, d, n = 4, 2, 16, 12
+    q, k, v, wq, wk, kv_offs, q_offs, new = _chunk_case(11, lens, bases, H, Hkv, d, n)
+    kw = dict(n_head=H, n_head_kv=Hkv, head_dim=d, rope_dim=n, rope_freq_base=1e4,
+              rms_eps=1e-6, scale=0.3)
+    full, kn = oracle.qk_prep_attn(q, k, v, wq, wk, seq_offsets=kv_offs, return_k_rot=True,
+                                   **kw)
+    k_cache = np.where(np.isin(np.arange(len(k)), new)[:, None], 0.0, kn)
+    v_cache = np.where(np.isin(np.arange(len(v)), new)[:, None], 0.0, v)
+    out, kc, vc = oracle.qk_prep_chunk_attn(q[new], k[new], v[new], wq, wk, k_cache, v_cache,
+                                            q_offsets=q_offs, kv_offsets=kv_offs, **kw)
+    np.testing.assert_array_equal(out, full[new])
+    np.testing.assert_array_equal(kc, kn)
+    np.testing.assert_array_equal(vc, v)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_matches_torch_sdpa_with_bottom_right_mask(causal):
+    # torch's f64 SDPA per (sequence, head) with an explicit mask: query row r of a
+    # sequence with base cached rows may see cache rows 0 .. base + r.
+    H, Hkv, d = 6, 2, 16
+    r = _rng(12)
+    lens, bases = (5, 3), (4, 9)
+    q_offs = np.array([0, 5, 8], dtype=np.int32)
+    kv_offs = np.array([0, 9, 21], dtype=np.int32)
+    q = r.standard_normal((8, H * d))
+    kc = r.standard_normal((21, Hkv * d))
+    vc = r.standard_normal((21, Hkv * d))
+    out = oracle.chunk_attn(q, kc, vc, n_head=H, n_head_kv=Hkv, head_dim=d, scale=0.2,
+                            causal=causal, q_offsets=q_offs, kv_offsets=kv_offs)
+    for s in range(2):
+        qs = torch.from_numpy(q[q_offs[s]:q_offs[s + 1]]).view(-1, H, d).transpose(0, 1)
+        ks = torch.from_numpy(kc[kv_offs[s]:kv_offs[s + 1]]).view(-1, Hkv, d).transpose(0, 1)
+        vs = torch.from_numpy(vc[kv_offs[s]:kv_offs[s + 1]]).view(-1, Hkv, d).transpose(0, 1)
+        ks = ks.repeat_interleave(H // Hkv, 0)
+        vs = vs.repeat_interleave(H // Hkv, 0)
+        mask = None
+        if causal:
+            rr = torch.arange(lens[s])[:, None]
+            jj = torch.arange(lens[s] + bases[s])[None, :]
+            mask = jj <= bases[s] + rr
+        ref = F.scaled_dot_product_attention(qs, ks, vs, attn_mask=mask, scale=0.2)
+        ref = ref.transpose(0, 1).reshape(lens[s], H * d).numpy()
+        np.testing.assert_allclose(out[q_offs[s]:q_offs[s + 1]], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_chunk_single_new_row_sees_the_whole_cache():
+    # one new row (a decode step) attends every cached row of its sequence and itself:
+    # causal and non-causal agree, and constant values give that constant
+    H, Hkv, d = 4, 4, 8
+    r = _rng(13)
+    q = r.standard_normal((1, H * d))
+    kc = r.standard_normal((10, Hkv * d))
+    vc = np.tile(r.standard_normal(Hkv * d), (10, 1))
+    kw = dict(n_head=H, n_head_kv=Hkv, head_dim=d, scale=0.5)
+    a = oracle.chunk_attn(q, kc, vc, causal=True, **kw)
+    b = oracle.chunk_attn(q, kc, vc, causal=False, **kw)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_allclose(a[0], vc[0], rtol=1e-14, atol=1e-14)
+
+
+def test_chunk_rejects_short_caches():
+    q = np.zeros((4, 8))
+    with pytest.raises(ValueError):
+        oracle.chunk_attn(q, np.zeros((3, 8)), np.zeros((3, 8)), n_head=1, n_head_kv=1,
+                          head_dim=8, scale=1.0)
+    with pytest.raises(ValueError):
+        oracle.chunk_attn(q, np.zeros((6, 8)), np.zeros((6, 8)), n_head=1, n_head_kv=1,
+                          head_dim=8, scale=1.0, q_offsets=[0, 3, 4], kv_offsets=[0, 2, 6])

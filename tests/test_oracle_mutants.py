@@ -13,7 +13,8 @@ import tests.test_oracle as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
-# (name, text in oracle.c, planted mistake)
+# (name, text in oracle.c, planted mistake); every mistake keeps the oracle's reads in
+# bounds, so a mutant fails pins instead of crashing the test process
 MUTANTS = [
     ("rope sign flipped", "y[j] = a * c - b * s;", "y[j] = a * c + b * s;"),
     ("rope turns clockwise", "y[j + half] = a * s + b * c;", "y[j + half] = -a * s + b * c;"),
@@ -23,10 +24,15 @@ MUTANTS = [
     ("exponent over head_dim", "-2.0 * (double)j / (double)n", "-2.0 * (double)j / (double)d"),
     ("positions never restart", "int64_t pos = t - c->offsets[s];", "int64_t pos = t;"),
     ("gqa map modulo", "int kv = h / g;", "int kv = h % c->Hkv;"),
-    ("diagonal hidden", "c->causal ? i :", "c->causal ? i - 1 + (i == lo) :"),
+    ("diagonal hidden", "c->causal ? last :", "c->causal ? last - 1 + (last == lo) :"),
     ("softmax scale dropped", "double sj = c->scale * dot;", "double sj = dot;"),
     ("k and v swapped", "const double* vj = c->v +", "const double* vj = c->k +"),
-    ("sequence boundary ignored", "int64_t lo = c->offsets[s];", "int64_t lo = 0;"),
+    ("sequence boundary ignored", "int64_t lo = c->kv_offsets[s];", "int64_t lo = 0;"),
+    ("cached prefix ignored", "int64_t last = lo + base + (i - c->offsets[s]);",
+     "int64_t last = lo + (i - c->offsets[s]);"),
+    ("prefix one short", "int64_t last = lo + base + (i - c->offsets[s]);",
+     "int64_t last = lo + base - (base > 0) + (i - c->offsets[s]);"),
+    ("start positions ignored", "if (c->pos0) pos += c->pos0[s];", "(void)c->pos0;"),
 ]
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins)
@@ -72,7 +78,8 @@ def test_planted_mistake_is_caught(name, before, after, monkeypatch):
                         "-lpthread"], check=True)
         real = oracle._load()
         mut = ctypes.CDLL(so)
-        for fn in ("oracle_qknorm_rope", "oracle_gqa_attn"):
+        for fn in ("oracle_qknorm_rope", "oracle_gqa_attn", "oracle_qknorm_rope_from",
+                   "oracle_chunk_attn"):
             getattr(mut, fn).argtypes = getattr(real, fn).argtypes
             getattr(mut, fn).restype = getattr(real, fn).restype
         monkeypatch.setattr(oracle, "_lib", mut)
