@@ -177,6 +177,76 @@ int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
                  float rope_freq_base, float rms_eps, float scale, int causal, int precision,
                  float* k_rot_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gqa_chunk_attn -- attention of a block of new query rows over a K/V cache that
+ * already holds each sequence's earlier rows (chunked prefill, or verifying a
+ * block of drafted tokens).
+ *
+ * Passages: memra-engine 0.101.0 src/spec.rs, `full_attn_verify` (the block's
+ * rows are appended to the cache after base_len rows; row r then attends cache
+ * rows 0 .. base_len + r, the per-row fallback spelling out base_len + r + 1
+ * keys); needle-core v3/model.rs, cache fill after the prefill (the cache keeps
+ * the normalised, rotated keys and the values).
+ *
+ *  q        [T_q, n_head*head_dim]   f32, device, read: the new rows, already
+ *           normalised and rotated at their positions.
+ *  k_cache, v_cache  [T_kv, n_head_kv*head_dim]  f32, device, read: sequence s
+ *           owns cache rows kv_offsets[s] .. kv_offsets[s+1]-1, of which the
+ *           last (q_offsets[s+1] - q_offsets[s]) are its new rows (already in
+ *           place) and the ones before them, base_s, its earlier rows.
+ *  out      [T_q, n_head*head_dim]   f32, device, written; must not overlap the
+ *           other tensors.
+ *  q_offsets, kv_offsets  host arrays of n_seqs+1 cumulative offsets, as
+ *           seq_offsets above, both NULL (one sequence) or both given; every
+ *           sequence needs at least as many cache rows as new rows.
+ *  Row r of sequence s (position base_s + r) sees, when causal, cache rows
+ *  0 .. base_s + r of its sequence; otherwise all of them.  base_s = 0 for every
+ *  sequence is gqa_prefill_attn.  scale, precision, workspace as for
+ *  gqa_prefill_attn, the workspace sized by pfa_chunk_workspace_bytes(..., 0).
+ */
+int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, float* out,
+                   const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                   int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                   float scale, int causal, int precision,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qk_prep_chunk_attn -- the whole verify step of a block of new rows in one
+ * call: QK-norm + NeoX RoPE of the raw new Q and K at their positions (base_s +
+ * r), the rotated K rows and the V rows written into the caller's cache, then
+ * gqa_chunk_attn over the cache.
+ *
+ * Passages: as for gqa_chunk_attn and qknorm_rope.
+ *
+ *  q [T_q, n_head*head_dim], k, v [T_q, n_head_kv*head_dim]  raw f32, device,
+ *        read: the new rows.
+ *  k_cache, v_cache  [T_kv, n_head_kv*head_dim] f32, device, read and written:
+ *        rows kv_offsets[s] .. kv_offsets[s+1]-1 - len_s hold sequence s's
+ *        earlier rows (rotated K, V) and are read; its last len_s rows receive
+ *        the new rows' rotated K and V.  They must not overlap each other or the
+ *        other tensors.
+ *  out  [T_q, n_head*head_dim] f32, device, written.
+ *  workspace  as for gqa_prefill_attn, sized by pfa_chunk_workspace_bytes(...,
+ *        1); PFA_PREC_F32 needs none unless the key split is wanted.
+ */
+int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* out,
+                       const float* q_norm_w, const float* k_norm_w,
+                       float* k_cache, float* v_cache,
+                       const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                       int T_q, int T_kv, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                       float rope_freq_base, float rms_eps, float scale, int causal,
+                       int precision, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace in bytes that gqa_chunk_attn (fused = 0) or qk_prep_chunk_attn
+ * (fused = 1) uses for these arguments: as pfa_workspace_bytes, with the bf16 tiles
+ * covering each sequence's cache rows (sum_s ceil(kv_len_s / 64) tiles) and the
+ * rotary table max_s(kv_len_s) rows; the f32 modes need room only for the key
+ * split.  Returns 0 when nothing is needed or the arguments are ones the calls
+ * would reject (pfa_last_error() then says why). */
+size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                                 int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                                 int precision, int fused);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pfa_last_error(void);
 

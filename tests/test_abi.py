@@ -245,3 +245,68 @@ def test_f32_fused_needs_a_workspace_or_k_rot_out(L):
                           p(5 << 20), None, 0, 16, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0,
                           p(0), p(8 << 20), need - 1, None) == INVALID
     assert "needed" in _msg(L)
+
+
+def _i32(a):
+    arr = (ctypes.c_int32 * len(a))(*a)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def _chunk(L, q_offs, kv_offs, T_q, T_kv, H=4, Hkv=2, D=64, prec=0, ptrs=(8, 8, 8, 8 << 20),
+           ws=0, ws_bytes=0):
+    keep_q, qp = _i32(q_offs) if q_offs is not None else (None, None)
+    keep_k, kp = _i32(kv_offs) if kv_offs is not None else (None, None)
+    n = len(q_offs) - 1 if q_offs is not None else 0
+    q, k, v, o = (ctypes.c_void_p(p) for p in ptrs)
+    return L.gqa_chunk_attn(q, k, v, o, qp, kp, n, T_q, T_kv, H, Hkv, D, 0.125, 1, prec,
+                            ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_chunk_with_no_new_rows_is_ok_without_pointers(L):
+    assert _chunk(L, None, None, 0, 0, ptrs=(0, 0, 0, 0)) == OK
+    assert _chunk(L, [0, 0], [0, 40], 0, 40, ptrs=(0, 0, 0, 0)) == OK
+
+
+def test_chunk_rejects_caches_shorter_than_their_queries(L):
+    assert _chunk(L, [0, 4], [0, 3], 4, 3) == INVALID
+    assert "cache rows" in _msg(L)
+    assert _chunk(L, [0, 2, 6], [0, 5, 8], 6, 8) == INVALID   # second sequence: 3 rows for 4
+    assert "sequence 1" in _msg(L)
+
+
+def test_chunk_offsets_come_in_pairs(L):
+    assert _chunk(L, [0, 4], None, 4, 9) == INVALID
+    assert "both or neither" in _msg(L)
+    assert _chunk(L, [0, 4], [0, 9], 4, 8) == INVALID   # kv_offsets must end at T_kv
+    assert "T = 8" in _msg(L)
+
+
+def _chunk_ws(L, q_lens, kv_lens, H, Hkv, D, prec, fused):
+    qo = np.cumsum([0] + list(q_lens)).astype(np.int32)
+    ko = np.cumsum([0] + list(kv_lens)).astype(np.int32)
+    keep_q, qp = _i32(qo.tolist())
+    keep_k, kp = _i32(ko.tolist())
+    return L.pfa_chunk_workspace_bytes(qp, kp, len(q_lens), int(qo[-1]), int(ko[-1]), H, Hkv, D,
+                                       prec, fused)
+
+
+@pytest.mark.parametrize("prec", [0, 1, 2])
+@pytest.mark.parametrize("fused", [0, 1])
+def test_chunk_workspace_without_prefix_is_the_prefill_rule(L, prec, fused):
+    # no cached rows: the chunk call plans exactly what the prefill call plans, except that
+    # the f32 fused chunk entry writes its rotated K into the cache, not the workspace
+    for lens in ((512,), (300, 1, 97), (8192,)):
+        expect = _expected_workspace(lens, 16, 8, 128, prec, fused and prec != 0)
+        assert _chunk_ws(L, lens, lens, 16, 8, 128, prec, fused) == expect
+
+
+def test_chunk_workspace_tiles_cover_the_cache(L):
+    # bf16: tiles of every sequence's cache rows; the rotary table covers the longest
+    # cache (positions base + r); no key split at this size
+    q_lens, kv_lens = (1024,), (8192,)
+    tiles = 8 * 128 * 64 * 128 * 2
+    assert _chunk_ws(L, q_lens, kv_lens, 32, 8, 128, 1, 0) == 2 * tiles
+    assert _chunk_ws(L, q_lens, kv_lens, 32, 8, 128, 1, 1) == 2 * tiles + 8192 * 64 * 8
+    assert _chunk_ws(L, q_lens, kv_lens, 32, 8, 128, 2, 0) == 3 * tiles
+    assert pfa.chunk_workspace_bytes(1024, 8192, 32, 8, 128, "bf16", fused=True) == \
+        2 * tiles + 8192 * 64 * 8

@@ -1,0 +1,181 @@
+"""GPU parity of the chunk entry points, ``gqa_chunk_attn`` and ``qk_prep_chunk_attn``
+(through the C ABI): new rows over a K/V cache that already holds each sequence's
+earlier rows, against the f64 oracle's ``chunk_attn`` / ``qk_prep_chunk_attn``.
+
+Inputs are whole sequences from the seeded workload generator; each sequence's first
+``base`` rows play the cached prefix (its K normalised and rotated by the oracle, as a
+cache keeps it, rounded to f32), the rest the new rows.  Element by element at small
+sizes (tile-aligned and ragged prefixes, one new row, no prefix, packed sequences with
+different prefixes, head_dim 64, a prefix long enough for the key split), and on
+sampled rows at the benchmark's chunk shape (8192 cache rows, 1024 new)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_prefill_attention_amd as pfa
+from transformer_prefill_attention_amd import workloads as wl
+from tests.helpers import assert_bf16_parity, assert_f32_parity, errors
+
+pytestmark = pytest.mark.gpu
+
+# name: (new rows per sequence, cached rows before them, n_head, n_head_kv, head_dim, rope_dim)
+CASES = {
+    "tile_aligned": ((100,), (128,), 8, 2, 128, 128),
+    "ragged_prefix": ((70,), (37,), 8, 2, 128, 128),
+    "one_new_row": ((1,), (300,), 4, 2, 128, 128),
+    "no_prefix": ((150,), (0,), 8, 2, 128, 128),
+    "packed": ((50, 1, 130, 0), (20, 77, 0, 5), 8, 4, 128, 64),
+    "d64": ((90,), (45,), 4, 2, 64, 64),
+    "long_prefix": ((260,), (1500,), 16, 8, 128, 128),
+}
+
+
+class Case:
+    """Whole sequences (prefix + new rows), their oracle-prepared Q/K, and the split."""
+
+    def __init__(self, name, lens, bases, H, Hkv, d, n, seed=700):
+        full = tuple(b + m for b, m in zip(bases, lens))
+        self.w = wl.Workload(f"chunk_{name}", full, H, Hkv, d, n, 1e6, 1e-6, seed=seed)
+        self.x = wl.make_inputs(self.w)
+        self.H, self.Hkv, self.d, self.n = H, Hkv, d, n
+        self.kv_offs = np.concatenate([[0], np.cumsum(full)]).astype(np.int32)
+        self.q_offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        self.new = np.concatenate(
+            [np.arange(self.kv_offs[s] + bases[s], self.kv_offs[s + 1]) for s in range(len(lens))]
+        ).astype(np.int64)
+        self.is_new = np.zeros(len(self.x.k), dtype=bool)
+        self.is_new[self.new] = True
+        self.eps = float(np.float32(1e-6))
+        self.base_f = float(np.float32(1e6))
+        qn, kn = oracle.qknorm_rope(self.x.q, self.x.k, self.x.wq, self.x.wk, n_head=H,
+                                    n_head_kv=Hkv, head_dim=d, rope_dim=n,
+                                    rope_freq_base=self.base_f, rms_eps=self.eps,
+                                    seq_offsets=self.kv_offs)
+        self.q_prep = qn[self.new].astype(np.float32)   # prepared new queries, as the GPU gets them
+        self.k_cache = kn.astype(np.float32)             # the whole cache, prepared
+        self.v_cache = self.x.v.astype(np.float32)
+        # what the fused entry starts from: the prefix rows only (new rows zeroed)
+        self.k_prefix = np.where(self.is_new[:, None], 0.0, self.k_cache).astype(np.float32)
+        self.v_prefix = np.where(self.is_new[:, None], 0.0, self.v_cache).astype(np.float32)
+
+    def label(self, entry, precision, causal=True):
+        w = self.w
+        return (f"{entry} {w.name}: T_q={len(self.new)} T_kv={w.T} H={self.H} Hkv={self.Hkv} "
+                f"d={self.d} n={self.n} seqs={w.n_seqs} causal={causal} {precision}")
+
+
+def _t(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _chunk_gpu(c, precision, causal=True):
+    print(c.label("gqa_chunk_attn", precision, causal), flush=True)
+    dev = torch.device("cuda:0")
+    out = pfa.gqa_chunk_attn(_t(c.q_prep, dev), _t(c.k_cache, dev), _t(c.v_cache, dev),
+                             head_dim=c.d, scale=c.w.softmax_scale, causal=causal,
+                             precision=precision, q_offsets=c.q_offs, kv_offsets=c.kv_offs)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _chunk_ref(c, causal=True, rows=None):
+    return oracle.chunk_attn(c.q_prep, c.k_cache, c.v_cache, n_head=c.H, n_head_kv=c.Hkv,
+                             head_dim=c.d, scale=c.w.softmax_scale, causal=causal,
+                             q_offsets=c.q_offs, kv_offsets=c.kv_offs, rows=rows)
+
+
+def _fused_gpu(c, precision, causal=True):
+    print(c.label("qk_prep_chunk_attn", precision, causal), flush=True)
+    dev = torch.device("cuda:0")
+    kc, vc = _t(c.k_prefix, dev), _t(c.v_prefix, dev)
+    out = pfa.qk_prep_chunk_attn(_t(c.x.q[c.new], dev), _t(c.x.k[c.new], dev),
+                                 _t(c.x.v[c.new], dev), _t(c.x.wq, dev), _t(c.x.wk, dev), kc, vc,
+                                 head_dim=c.d, rope_dim=c.n, rope_freq_base=1e6, rms_eps=1e-6,
+                                 scale=c.w.softmax_scale, causal=causal, precision=precision,
+                                 q_offsets=c.q_offs, kv_offsets=c.kv_offs)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy()
+
+
+def _fused_ref(c, causal=True, rows=None):
+    return oracle.qk_prep_chunk_attn(c.x.q[c.new], c.x.k[c.new], c.x.v[c.new], c.x.wq, c.x.wk,
+                                     c.k_prefix, c.v_prefix, n_head=c.H, n_head_kv=c.Hkv,
+                                     head_dim=c.d, rope_dim=c.n, rope_freq_base=c.base_f,
+                                     rms_eps=c.eps, scale=c.w.softmax_scale, causal=causal,
+                                     q_offsets=c.q_offs, kv_offsets=c.kv_offs, rows=rows)
+
+
+@pytest.fixture(scope="module", params=list(CASES))
+def case(request):
+    return Case(request.param, *CASES[request.param])
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3"])
+def test_chunk_attn_matches_oracle(case, precision):
+    got = _chunk_gpu(case, precision)
+    ref = _chunk_ref(case)
+    if precision == "f32":
+        assert_f32_parity(got, ref, case.label("gqa_chunk_attn", precision))
+    else:
+        assert_bf16_parity(got, ref, case.label("gqa_chunk_attn", precision))
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3"])
+def test_prep_chunk_attn_matches_oracle_and_fills_the_cache(case, precision):
+    got, kc, vc = _fused_gpu(case, precision)
+    ref, kref, vref = _fused_ref(case)
+    what = case.label("qk_prep_chunk_attn", precision)
+    if precision == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)
+    # the new rows' rotated K in f32 (the K the f32 QK-norm + RoPE path writes), the
+    # values copied exactly, the prefix rows untouched
+    max_abs, rel = errors(kc[case.new], kref[case.new])
+    print(f"{what} cache K: max|err| {max_abs:.3e}  rel L2 {rel:.3e}", flush=True)
+    assert max_abs <= 1e-5 and rel <= 2e-6
+    np.testing.assert_array_equal(vc[case.new], case.v_cache[case.new])
+    keep = ~case.is_new
+    np.testing.assert_array_equal(kc[keep], case.k_prefix[keep])
+    np.testing.assert_array_equal(vc[keep], case.v_prefix[keep])
+
+
+def test_chunk_without_prefix_is_prefill_bit_exact():
+    # nothing cached before: the chunk entry runs the prefill kernels on the same tables
+    c = Case("no_prefix", *CASES["no_prefix"])
+    dev = torch.device("cuda:0")
+    for precision in ("f32", "bf16"):
+        a = _chunk_gpu(c, precision)
+        print(f"gqa_prefill_attn {c.w.name}: T={c.w.T} {precision}", flush=True)
+        b = pfa.gqa_prefill_attn(_t(c.q_prep, dev), _t(c.k_cache, dev), _t(c.v_cache, dev),
+                                 head_dim=c.d, scale=c.w.softmax_scale, precision=precision)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(a, b.cpu().numpy())
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16"])
+def test_chunk_non_causal(precision):
+    c = Case("packed_nc", *CASES["packed"], seed=701)
+    got = _chunk_gpu(c, precision, causal=False)
+    ref = _chunk_ref(c, causal=False)
+    what = c.label("gqa_chunk_attn", precision, causal=False)
+    if precision == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16"])
+def test_chunk_benchmark_shape_sampled_rows(precision):
+    # 8192 cache rows per the 8B-like heads, the last 1024 new: the launch the benchmark
+    # times; 24 query rows spread over the block are checked against the oracle
+    c = Case("bench", (1024,), (7168,), 32, 8, 128, 128, seed=702)
+    rows = np.linspace(0, 1023, 24).astype(np.int64)
+    got, _, _ = _fused_gpu(c, precision)
+    ref = _fused_ref(c, rows=rows)[0]
+    what = c.label("qk_prep_chunk_attn", precision) + " (sampled rows)"
+    if precision == "f32":
+        assert_f32_parity(got[rows], ref, what)
+    else:
+        assert_bf16_parity(got[rows], ref, what)

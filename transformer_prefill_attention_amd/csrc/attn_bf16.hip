@@ -156,8 +156,8 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
     const int gt = blockIdx.x / Hkv;
     const int n_tiles = sched.n_tiles;
     const int s = find_seq(sched.tile_off, sched.n_seqs, gt);
-    const int k0 = sched.off[s] + (gt - sched.tile_off[s]) * kBN;
-    const int nval = min(kBN, sched.off[s + 1] - k0);
+    const int k0 = sched.koff[s] + (gt - sched.tile_off[s]) * kBN;  // the tile's key rows
+    const int nval = min(kBN, sched.koff[s + 1] - k0);
     const int64_t row_stride = (int64_t)Hkv * D;
     __bf16* kt = ws + ((int64_t)kv * n_tiles + gt) * (KP * kBN * D);
     __bf16* vt = ws + (int64_t)Hkv * n_tiles * (KP * kBN * D) +
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
         constexpr int DQ = D / 4;  // dims per thread
         const int r = tid >> 2, qd = tid & 3, c0 = qd * DQ;
         const bool valid = r < nval;
-        const int pos = valid ? k0 + r - sched.off[s] : 0;  // rows past the end: any valid entry
+        const int pos = valid ? k0 + r - sched.koff[s] : 0;  // rows past the end: any valid entry
         float y[DQ];
 #pragma unroll
         for (int i = 0; i < DQ; i += 4) {
@@ -332,11 +332,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 
     const WorkItem wi = decode_item(sched, geom, blockIdx.x);
     const int kv = wi.kv, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
+    // key rows of the sequence: [ks0, ks1); query row i sees keys <= i + dsh (over a
+    // cached prefix its position is base + i - s0; plain prefill: ks0 = s0, dsh = 0)
+    const int ks0 = wi.k0, ks1 = wi.k1, dsh = ks1 - s1;
     const int causal = geom.causal, H = geom.H, Hkv = geom.Hkv;
     const float qscale = geom.qscale;
     const int n_all = sched.n_tiles, tile0 = sched.tile_off[wi.sid];
-    const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
-    const int n_tiles = causal ? (min(q0 + sched.rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
+    const int nt_seq = (ks1 - ks0 + kBN - 1) / kBN;
+    const int n_tiles =
+        causal ? (min(q0 + sched.rows_per_item, s1) - 1 + dsh - ks0) / kBN + 1 : nt_seq;
     // key split: this workgroup takes tiles [t_begin, t_begin + n_local) of the item
     const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles;
     const int n_chunks = (n_tiles + kchunk - 1) / kchunk;
@@ -348,7 +352,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     const int h = kv * geom.g + wi.chunk * geom.hpw + hloc;
     const int wq0 = q0 + rblk * 32;
     const bool active = wq0 < s1;
-    const int wave_last = causal ? min((wq0 + 31 - s0) / kBN, nt_seq - 1) : nt_seq - 1;
+    const int wave_last =
+        causal ? min((min(wq0 + 31, s1 - 1) + dsh - ks0) / kBN, nt_seq - 1) : nt_seq - 1;
     const int qi = wq0 + ln;
 
     // ---- Q operand (B of K Q^T): for step s, lane (hl, ln) supplies
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     xq[s][e] = ok ? xq[s][e] * rs * prep.wq[hl * (D / 2) + 8 * s + e] : 0.0f;
-            const int pos = ok ? qi - s0 : 0;  // rows past the end: any valid table entry
+            const int pos = ok ? qi + dsh - ks0 : 0;  // rows past the end: any valid table entry
             const float2* trow = tab + pos * (D / 2);
             if (n == D) {
                 // dim c pairs with c +- D/2: the same register of the other lane half.
@@ -591,11 +596,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 for (int e = 0; e < 8; ++e) pop[i][e] = (__bf16)0.0f;
             return;
         }
-        const int k0 = s0 + t * kBN;
+        const int k0 = ks0 + t * kBN;
         // register r of block kb: key k0 + 32kb + 8(r/4) + 4hl + r%4.  A key is
-        // hidden when it lies past min(qi, s1-1) (causal) or past s1-1.
-        if ((causal && k0 + kBN - 1 > wq0) || k0 + kBN > s1) {
-            const int lim = (causal ? min(qi, s1 - 1) : s1 - 1) - (k0 + 4 * hl);
+        // hidden when it lies past min(qi + dsh, ks1-1) (causal) or past ks1-1.
+        if ((causal && k0 + kBN - 1 > wq0 + dsh) || k0 + kBN > ks1) {
+            const int lim = (causal ? min(qi + dsh, ks1 - 1) : ks1 - 1) - (k0 + 4 * hl);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -607,26 +612,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
         // the running max (the first tile, or a real jump) is the row max taken and
         // the weights recomputed, so the result is that of taking the row max
         // first: m moves to it when it passes m + kLazyMax.
+        // A row that has seen no key yet keeps m = -inf (over a cached prefix a row
+        // can see no key of a tile, or of a split key range); exponents against
+        // -1e30 then give 0 for its hidden keys, not NaN.
         const float lmax = fmaxf(max16(sacc[0]), max16(sacc[1]));
+        const float m_sub = fmaxf(m_run, -1e30f);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                pop[2 * kb + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_run);
+                pop[2 * kb + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_sub);
         // (issued ahead of the check, not sunk below it onto the max's critical path)
         asm volatile("" : "+v"(pop[0]), "+v"(pop[1]), "+v"(pop[2]), "+v"(pop[3]));
         if (__any(lmax > m_run + kLazyMax)) {
-            // every processed tile shows each query at least one key, so mt is finite
+            // (mt = -inf only in a row that sees no key here: no bump, weights 0)
             const float mt = max_halves(lmax);
             const bool bump = mt > m_run + kLazyMax;
             float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
             if (bump) m_run = mt;
+            const float m_new = fmaxf(m_run, -1e30f);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     pop[2 * kb + (r >> 3)][r & 7] =
-                        (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_run);
+                        (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
             l_run *= (double)alpha;
             // alpha is 1 in rows without a bump; hidden from the optimiser, which
             // would otherwise make the multiplication unconditional
@@ -727,8 +737,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
-                            const PrepParams* prep, const Partials& part, int n_items,
-                            hipStream_t stream) {
+                            const PrepParams* prep, bool prep_k, const Partials& part,
+                            int n_items, hipStream_t stream) {
     __bf16* w = static_cast<__bf16*>(ws);
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
     const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
@@ -740,8 +750,12 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
         if (PP)                                                                                 \
             hipLaunchKernelGGL((rope_table_kernel<DD, SS>), tgrid, tblock, 0, stream, w,      \
                                geom.Hkv, sched.n_tiles, sched.max_len, p.rope_dim, p.base);    \
-        hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, PP>), sgrid, sblock, 0, stream, k, v, \
-                           w, sched, geom.Hkv, p);                                              \
+        if (PP && prep_k)                                                                       \
+            hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, true>), sgrid, sblock, 0, stream, \
+                               k, v, w, sched, geom.Hkv, p);                                    \
+        else                                                                                    \
+            hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, false>), sgrid, sblock, 0, stream,\
+                               k, v, w, sched, geom.Hkv, p);                                    \
         hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP>), grid, block, 0, stream, q, w, out,  \
                            sched, geom, p, part);                                               \
     } while (0)

@@ -114,15 +114,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     // ---- work item (uniform across the workgroup)
     const WorkItem wi = decode_item(sched, geom, blockIdx.x);
     const int kv = wi.kv, chunk = wi.chunk, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
+    // key rows of the sequence: [ks0, ks1); query row i sees keys <= i + dsh (over a
+    // cached prefix its position is base + i - s0; plain prefill: ks0 = s0, dsh = 0)
+    const int ks0 = wi.k0, ks1 = wi.k1, dsh = ks1 - s1;
     // (the lambdas below must not capture the kernel-argument structs: taking their
     // address copies them into scratch memory and makes every value read from them
     // look divergent; they use these locals instead)
     const int rows_per_item = sched.rows_per_item;
     const int n_kv = geom.Hkv, n_q = geom.H;
     const float* const k_in = k;
-    const int nt_seq = (s1 - s0 + kBN - 1) / kBN;
+    const int nt_seq = (ks1 - ks0 + kBN - 1) / kBN;
     const int n_tiles =
-        geom.causal ? (min(q0 + rows_per_item, s1) - 1 - s0) / kBN + 1 : nt_seq;
+        geom.causal ? (min(q0 + rows_per_item, s1) - 1 + dsh - ks0) / kBN + 1 : nt_seq;
     // key split: this workgroup takes tiles [t_begin, t_end) of the item
     const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles;
     const int n_chunks = (n_tiles + kchunk - 1) / kchunk;
@@ -135,8 +138,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const int h = kv * geom.g + chunk * geom.hpw + hloc;
     const int wq0 = q0 + rblk * 32;
     const bool active = wq0 < s1;
-    const int diag_tile = (wq0 - s0) / kBN;
-    const int wave_tiles = geom.causal ? min(diag_tile + 1, nt_seq) : nt_seq;
+    // tiles holding a key some row of this wavefront may see
+    const int wave_tiles =
+        geom.causal ? min((min(wq0 + 31, s1 - 1) + dsh - ks0) / kBN + 1, nt_seq) : nt_seq;
     const int qi = wq0 + ln;
 
     // Fused entry, per lane: Q norm weights and rotary frequency (turns per position)
@@ -191,7 +195,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
                 for (int r = 0; r < 8; ++r) {
                     float cs[E], sn[E];
 #pragma unroll
-                    for (int e = 0; e < E; ++e) rope_cos_sin(wq0 + r0 + r - s0, turns[e], cs[e], sn[e]);
+                    for (int e = 0; e < E; ++e)
+                        rope_cos_sin(wq0 + r0 + r + dsh - ks0, turns[e], cs[e], sn[e]);
                     prep_row<D>(x[r], wqv, cs, sn, prep.rope_dim, prep.eps, lane);
                 }
 #pragma unroll
@@ -229,8 +234,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
         kv_off[i] = (f / F4_PER_ROW) * row_bytes + 16 * (f % F4_PER_ROW);
     }
     auto tile_rsrc = [&](const float* base, int t) {
-        const int k0 = s0 + t * kBN;
-        const uint32_t bytes = (uint32_t)(s1 - k0 - 1) * row_bytes + D * 4;
+        const int k0 = ks0 + t * kBN;
+        const uint32_t bytes = (uint32_t)(ks1 - k0 - 1) * row_bytes + D * 4;
         return buffer_rsrc(base + ((int64_t)k0 * n_kv + kv) * D, bytes);
     };
     auto load_rows = [&](const float* base, int t) {
@@ -312,12 +317,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] += sacc1[r];
             // Register r of lane (hl, ln) holds key k0 + 8(r/4) + 4hl + r%4 for query qi.
-            const int k0 = s0 + t * kBN;
-            if (t == diag_tile || t == nt_seq - 1) {
+            const int k0 = ks0 + t * kBN;
+            // tiles reaching past the first row's last visible key, or past the
+            // sequence's keys, are masked
+            if ((geom.causal && k0 + kBN - 1 > wq0 + dsh) || k0 + kBN > ks1) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if ((geom.causal && key > qi) || key >= s1) sacc[r] = -INFINITY;
+                    if ((geom.causal && key > qi + dsh) || key >= ks1) sacc[r] = -INFINITY;
                 }
             }
             float mt = sacc[0];
@@ -325,12 +332,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
             const float m_new = fmaxf(m_run, mt);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            // a row that has seen no key yet (possible in a split key range over a
+            // cached prefix) keeps m = -inf: exponents against -1e30 make its
+            // weights 0, not NaN
+            const float m_use = fmaxf(m_new, -1e30f);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
             m_run = m_new;
             float psum = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - m_new);
+                sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - m_use);
                 psum += sacc[r];
             }
             l_run = l_run * (double)alpha + (double)psum;

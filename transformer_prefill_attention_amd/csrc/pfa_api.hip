@@ -66,8 +66,8 @@ int check_rope(int head_dim, int rope_dim, float base, float eps) {
 int build_seqs(const int32_t* seq_offsets, int n_seqs, int T, pfa::SeqTable& st) {
     if (!seq_offsets) {
         st.n_seqs = 1;
-        st.off[0] = 0;
-        st.off[1] = T;
+        st.off[0] = st.koff[0] = 0;
+        st.off[1] = st.koff[1] = T;
         return PFA_OK;
     }
     if (n_seqs < 1) return fail(PFA_ERR_INVALID_ARG, "n_seqs must be >= 1 (got %d)", n_seqs);
@@ -82,7 +82,26 @@ int build_seqs(const int32_t* seq_offsets, int n_seqs, int T, pfa::SeqTable& st)
         return fail(PFA_ERR_INVALID_ARG, "seq_offsets[n_seqs] = %d but T = %d",
                     seq_offsets[n_seqs], T);
     st.n_seqs = n_seqs;
-    for (int s = 0; s <= n_seqs; ++s) st.off[s] = seq_offsets[s];
+    for (int s = 0; s <= n_seqs; ++s) st.off[s] = st.koff[s] = seq_offsets[s];
+    return PFA_OK;
+}
+
+// Query rows and cache rows of the chunk entry points: each sequence needs at
+// least as many cache rows as query rows (its queries are the last ones).
+int build_chunk_seqs(const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs, int T_q,
+                     int T_kv, pfa::SeqTable& st) {
+    if ((q_offsets == nullptr) != (kv_offsets == nullptr))
+        return fail(PFA_ERR_INVALID_ARG, "q_offsets and kv_offsets: both or neither");
+    int rc = build_seqs(q_offsets, n_seqs, T_q, st);
+    if (rc) return rc;
+    pfa::SeqTable kt;
+    if ((rc = build_seqs(kv_offsets, n_seqs, T_kv, kt))) return rc;
+    for (int s = 0; s < st.n_seqs; ++s)
+        if (kt.off[s + 1] - kt.off[s] < st.off[s + 1] - st.off[s])
+            return fail(PFA_ERR_INVALID_ARG,
+                        "sequence %d has %d cache rows for %d query rows (needs at least as many)",
+                        s, kt.off[s + 1] - kt.off[s], st.off[s + 1] - st.off[s]);
+    for (int s = 0; s <= st.n_seqs; ++s) st.koff[s] = kt.off[s];
     return PFA_OK;
 }
 
@@ -107,7 +126,10 @@ void choose_geometry(int H, int Hkv, float scale, int causal, int waves, pfa::At
 int build_sched(const pfa::SeqTable& st, int rows_per_item, pfa::AttnSched& sc) {
     sc.n_seqs = st.n_seqs;
     sc.rows_per_item = rows_per_item;
-    for (int s = 0; s <= st.n_seqs; ++s) sc.off[s] = st.off[s];
+    for (int s = 0; s <= st.n_seqs; ++s) {
+        sc.off[s] = st.off[s];
+        sc.koff[s] = st.koff[s];
+    }
     int nsb[PFA_MAX_SEQS];
     int idx[PFA_MAX_SEQS];
     for (int s = 0; s < st.n_seqs; ++s) {
@@ -130,15 +152,16 @@ int build_sched(const pfa::SeqTable& st, int rows_per_item, pfa::AttnSched& sc) 
         items += (kk + 1) * (top - next);
     }
     sc.seg_start[n_nonempty] = items;
-    // 64-key tiles of each sequence in the bf16 workspace
+    // 64-key tiles of each sequence's key rows in the bf16 workspace
     sc.tile_off[0] = 0;
     for (int s = 0; s < st.n_seqs; ++s)
         sc.tile_off[s + 1] =
-            sc.tile_off[s] + (st.off[s + 1] - st.off[s] + pfa::kBf16TileKeys - 1) /
+            sc.tile_off[s] + (st.koff[s + 1] - st.koff[s] + pfa::kBf16TileKeys - 1) /
                                  pfa::kBf16TileKeys;
     sc.n_tiles = sc.tile_off[st.n_seqs];
     sc.max_len = 0;
-    for (int s = 0; s < st.n_seqs; ++s) sc.max_len = std::max(sc.max_len, st.off[s + 1] - st.off[s]);
+    for (int s = 0; s < st.n_seqs; ++s)
+        sc.max_len = std::max(sc.max_len, st.koff[s + 1] - st.koff[s]);
     return items;
 }
 
@@ -209,11 +232,12 @@ int make_plan(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim, 
 }
 
 // Workspace bytes ahead of the partial results: the bf16 K/V tiles (+ the rotary
-// table for the fused entry), or for the f32 fused entry the rotated K unless it
-// goes to the caller's k_rot_out.
-size_t prep_part_bytes(const Plan& p, bool bf16, bool fused, bool k_rot_given) {
-    if (bf16) return p.tile_bytes + (fused ? p.table_bytes : 0);
-    return fused && !k_rot_given ? p.krot_bytes : 0;
+// table when Q is prepared in the kernel), or for the f32 fused entry the rotated
+// K unless it goes to the caller's k_rot_out (over a cached prefix it goes to the
+// cache instead).
+size_t prep_part_bytes(const Plan& p, bool bf16, bool prep_q, bool krot_in_ws) {
+    if (bf16) return p.tile_bytes + (prep_q ? p.table_bytes : 0);
+    return krot_in_ws ? p.krot_bytes : 0;
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -228,25 +252,46 @@ extern "C" {
 
 const char* pfa_last_error(void) { return g_err; }
 
-const char* pfa_version(void) { return "pfa 0.3 (gfx950; f32 and bf16 MFMA attention)"; }
+const char* pfa_version(void) {
+    return "pfa 0.4 (gfx950; f32 and bf16 MFMA attention, prefill and chunks over a cached prefix)";
+}
 
-size_t pfa_workspace_bytes(const int32_t* seq_offsets, int n_seqs, int T, int n_head,
-                           int n_head_kv, int head_dim, int precision, int fused) {
-    g_err[0] = 0;
-    if (check_geometry(T, n_head, n_head_kv, head_dim)) return 0;
+static size_t workspace_for(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
+                            int precision, bool prep_q, bool krot_in_ws) {
     if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) {
         fail(PFA_ERR_INVALID_ARG, "precision must be PFA_PREC_F32, PFA_PREC_BF16 or "
                                   "PFA_PREC_BF16X3 (got %d)", precision);
         return 0;
     }
-    if (T == 0) return 0;
-    pfa::SeqTable st;
-    if (build_seqs(seq_offsets, n_seqs, T, st)) return 0;
     Plan p;
     if (make_plan(st, n_head, n_head_kv, head_dim, 1.0f, 1, precision, p)) return 0;
     if (p.items == 0) return 0;
-    const size_t base = prep_part_bytes(p, precision != PFA_PREC_F32, fused != 0, false);
+    const size_t base = prep_part_bytes(p, precision != PFA_PREC_F32, prep_q, krot_in_ws);
     return p.part_bytes ? align256(base) + p.part_bytes : base;
+}
+
+size_t pfa_workspace_bytes(const int32_t* seq_offsets, int n_seqs, int T, int n_head,
+                           int n_head_kv, int head_dim, int precision, int fused) {
+    g_err[0] = 0;
+    if (check_geometry(T, n_head, n_head_kv, head_dim)) return 0;
+    if (T == 0) return 0;
+    pfa::SeqTable st;
+    if (build_seqs(seq_offsets, n_seqs, T, st)) return 0;
+    return workspace_for(st, n_head, n_head_kv, head_dim, precision, fused != 0,
+                         fused != 0 && precision == PFA_PREC_F32);
+}
+
+size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                                 int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                                 int precision, int fused) {
+    g_err[0] = 0;
+    if (check_geometry(T_q, n_head, n_head_kv, head_dim) ||
+        check_geometry(T_kv, n_head, n_head_kv, head_dim))
+        return 0;
+    if (T_q == 0) return 0;
+    pfa::SeqTable st;
+    if (build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st)) return 0;
+    return workspace_for(st, n_head, n_head_kv, head_dim, precision, fused != 0, false);
 }
 
 int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
@@ -270,41 +315,67 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
         return fail(PFA_ERR_INVALID_ARG, "Q and K buffers overlap");
     pfa::SeqTable st;
     if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
-    return hip_status(pfa::launch_qknorm_rope(q_in, k_in, q_out, k_out, q_norm_w, k_norm_w, st, T,
+    return hip_status(pfa::launch_qknorm_rope(q_in, k_in, q_out, k_out, nullptr, nullptr,
+                                              q_norm_w, k_norm_w, st, T,
                                               n_head, n_head_kv, head_dim, rope_dim,
                                               rope_freq_base, rms_eps, (hipStream_t)stream),
                       "qknorm_rope launch");
 }
 
-static int attn_common(const float* q, const float* k, const float* v, float* out,
-                       const int32_t* seq_offsets, int n_seqs, int T, int n_head, int n_head_kv,
-                       int head_dim, float scale, int causal, int precision,
-                       const pfa::PrepParams* prep, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+// How an attention call gets its K: as given (plain prefill, or a cache for the
+// chunk entry), prepared from raw rows into k_rot_out / the workspace (fused
+// prefill), or prepared from the new rows into the caller's cache (fused chunk).
+enum class Mode { kPlain, kFused, kChunk, kChunkFused };
+
+static int check_attn(float scale, int precision) {
     if (!std::isfinite(scale)) return fail(PFA_ERR_INVALID_ARG, "scale must be finite");
     if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3)
         return fail(PFA_ERR_INVALID_ARG,
                     "precision must be PFA_PREC_F32, PFA_PREC_BF16 or PFA_PREC_BF16X3 (got %d)",
                     precision);
-    if (T == 0) return PFA_OK;
-    if (!q || !k || !v || !out) return fail(PFA_ERR_INVALID_ARG, "null tensor pointer");
-    const size_t qb = (size_t)T * n_head * head_dim * 4, kb = (size_t)T * n_head_kv * head_dim * 4;
+    return PFA_OK;
+}
+
+static int attn_common(Mode mode, const float* q, const float* k, const float* v, float* out,
+                       float* k_cache, float* v_cache, const pfa::SeqTable& st, int n_head,
+                       int n_head_kv, int head_dim, float scale, int causal, int precision,
+                       const pfa::PrepParams* prep, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    const int T_q = st.off[st.n_seqs], T_kv = st.koff[st.n_seqs];
+    if (T_q == 0) return PFA_OK;
+    const bool chunk_fused = mode == Mode::kChunkFused;
+    if (!q || !k || !v || !out || (chunk_fused && (!k_cache || !v_cache)))
+        return fail(PFA_ERR_INVALID_ARG, "null tensor pointer");
+    // bytes of Q / out, of the K and V the call reads, and of the caches
+    const size_t qb = (size_t)T_q * n_head * head_dim * 4;
+    const size_t kb = (size_t)(mode == Mode::kChunk ? T_kv : T_q) * n_head_kv * head_dim * 4;
+    const size_t cb = (size_t)T_kv * n_head_kv * head_dim * 4;
     if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kb) || overlaps(out, qb, v, kb))
         return fail(PFA_ERR_INVALID_ARG, "out must not overlap q, k or v");
     if (prep && prep->k_rot_out &&
         (overlaps(prep->k_rot_out, kb, q, qb) || overlaps(prep->k_rot_out, kb, k, kb) ||
          overlaps(prep->k_rot_out, kb, v, kb) || overlaps(prep->k_rot_out, kb, out, qb)))
         return fail(PFA_ERR_INVALID_ARG, "k_rot_out must not overlap the inputs or out");
-    pfa::SeqTable st;
-    int rc = build_seqs(seq_offsets, n_seqs, T, st);
-    if (rc) return rc;
+    if (chunk_fused) {
+        const void* others[4] = {q, k, v, out};
+        const size_t sizes[4] = {qb, kb, kb, qb};
+        for (int i = 0; i < 4; ++i)
+            if (overlaps(k_cache, cb, others[i], sizes[i]) ||
+                overlaps(v_cache, cb, others[i], sizes[i]))
+                return fail(PFA_ERR_INVALID_ARG,
+                            "k_cache / v_cache must not overlap q, k, v or out");
+        if (overlaps(k_cache, cb, v_cache, cb))
+            return fail(PFA_ERR_INVALID_ARG, "k_cache and v_cache overlap");
+    }
     Plan p;
+    int rc;
     if ((rc = make_plan(st, n_head, n_head_kv, head_dim, scale, causal, precision, p))) return rc;
     if (p.items == 0) return PFA_OK;
     const bool bf16 = precision != PFA_PREC_F32;
-    // workspace parts: [bf16 K/V tiles + rotary table (fused), or f32 rotated K (fused,
-    // no k_rot_out)][partials, key split]
-    const size_t base = prep_part_bytes(p, bf16, prep != nullptr, prep && prep->k_rot_out);
+    // workspace parts: [bf16 K/V tiles + rotary table (Q prepared here), or f32 rotated K
+    // (fused prefill without k_rot_out)][partials, key split]
+    const bool krot_in_ws = mode == Mode::kFused && !bf16 && !prep->k_rot_out;
+    const size_t base = prep_part_bytes(p, bf16, prep != nullptr, krot_in_ws);
     const size_t part_off = p.part_bytes ? align256(base) : base;
     if (!bf16 && p.part_bytes &&
         (!workspace || workspace_bytes < part_off + p.part_bytes)) {
@@ -325,7 +396,9 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
             return fail(PFA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
         if (overlaps(workspace, need, q, qb) || overlaps(workspace, need, k, kb) ||
             overlaps(workspace, need, v, kb) || overlaps(workspace, need, out, qb) ||
-            (prep && prep->k_rot_out && overlaps(workspace, need, prep->k_rot_out, kb)))
+            (prep && prep->k_rot_out && overlaps(workspace, need, prep->k_rot_out, kb)) ||
+            (chunk_fused &&
+             (overlaps(workspace, need, k_cache, cb) || overlaps(workspace, need, v_cache, cb))))
             return fail(PFA_ERR_INVALID_ARG, "workspace must not overlap the tensors");
     }
     pfa::Partials part{nullptr, nullptr};
@@ -336,28 +409,46 @@ static int attn_common(const float* q, const float* k, const float* v, float* ou
         part.o = reinterpret_cast<float*>(w);
         part.ml = reinterpret_cast<float2*>(w + (size_t)units * p.waves * 32 * head_dim * 4);
     }
-    if (bf16)
-        return hip_status(pfa::launch_attn_bf16(q, k, v, out, workspace, p.sched, p.geom, head_dim,
-                                                precision == PFA_PREC_BF16X3, prep, part, p.items,
-                                                (hipStream_t)stream),
-                          prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
+    const char* what = prep ? (chunk_fused ? "qk_prep_chunk_attn launch" : "qk_prep_attn launch")
+                            : (mode == Mode::kChunk ? "gqa_chunk_attn launch"
+                                                    : "gqa_prefill_attn launch");
     const float* k_attn = k;
-    if (prep) {
-        // f32 fused entry: K is normalised and rotated once, by the QK-norm + RoPE
+    const float* v_attn = v;
+    if (chunk_fused) {
+        // the new rows: K normalised and rotated at their positions, K and V written
+        // to the last rows of each sequence's cache range; attention reads the caches
+        if ((rc = hip_status(pfa::launch_qknorm_rope(nullptr, k, nullptr, k_cache, v, v_cache,
+                                                     prep->wq, prep->wk, st, T_q, 0, n_head_kv,
+                                                     head_dim, prep->rope_dim, (float)prep->base,
+                                                     prep->eps, (hipStream_t)stream),
+                             what)))
+            return rc;
+        k_attn = k_cache;
+        v_attn = v_cache;
+    }
+    if (bf16)
+        return hip_status(pfa::launch_attn_bf16(q, k_attn, v_attn, out, workspace, p.sched, p.geom,
+                                                head_dim, precision == PFA_PREC_BF16X3, prep,
+                                                mode == Mode::kFused, part, p.items,
+                                                (hipStream_t)stream),
+                          what);
+    if (mode == Mode::kFused) {
+        // f32 fused prefill: K is normalised and rotated once, by the QK-norm + RoPE
         // kernel over the K rows alone, into k_rot_out or the workspace; the
         // attention kernel then prepares only its own Q rows
         float* krot = prep->k_rot_out ? prep->k_rot_out : static_cast<float*>(workspace);
-        if ((rc = hip_status(pfa::launch_qknorm_rope(nullptr, k, nullptr, krot, prep->wq, prep->wk,
-                                                     st, T, 0, n_head_kv, head_dim, prep->rope_dim,
+        if ((rc = hip_status(pfa::launch_qknorm_rope(nullptr, k, nullptr, krot, nullptr, nullptr,
+                                                     prep->wq, prep->wk, st, T_q, 0, n_head_kv,
+                                                     head_dim, prep->rope_dim,
                                                      (float)prep->base, prep->eps,
                                                      (hipStream_t)stream),
-                             "qk_prep_attn launch")))
+                             what)))
             return rc;
         k_attn = krot;
     }
-    return hip_status(pfa::launch_attn_f32(q, k_attn, v, out, p.sched, p.geom, head_dim, prep,
+    return hip_status(pfa::launch_attn_f32(q, k_attn, v_attn, out, p.sched, p.geom, head_dim, prep,
                                            part, p.items, (hipStream_t)stream),
-                      prep ? "qk_prep_attn launch" : "gqa_prefill_attn launch");
+                      what);
 }
 
 int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
@@ -366,9 +457,13 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
                      size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     int rc = check_geometry(T, n_head, n_head_kv, head_dim);
-    if (rc) return rc;
-    return attn_common(q, k, v, out, seq_offsets, n_seqs, T, n_head, n_head_kv, head_dim, scale,
-                       causal, precision, nullptr, workspace, workspace_bytes, stream);
+    if (rc || (rc = check_attn(scale, precision))) return rc;
+    if (T == 0) return PFA_OK;
+    pfa::SeqTable st;
+    if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
+    return attn_common(Mode::kPlain, q, k, v, out, nullptr, nullptr, st, n_head, n_head_kv,
+                       head_dim, scale, causal, precision, nullptr, workspace, workspace_bytes,
+                       stream);
 }
 
 int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
@@ -378,13 +473,55 @@ int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
                  float* k_rot_out, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     int rc = check_geometry(T, n_head, n_head_kv, head_dim);
-    if (rc) return rc;
+    if (rc || (rc = check_attn(scale, precision))) return rc;
     if ((rc = check_rope(head_dim, rope_dim, rope_freq_base, rms_eps))) return rc;
-    if (T > 0 && (!q_norm_w || !k_norm_w)) return fail(PFA_ERR_INVALID_ARG, "null norm weights");
+    if (T == 0) return PFA_OK;
+    if (!q_norm_w || !k_norm_w) return fail(PFA_ERR_INVALID_ARG, "null norm weights");
+    pfa::SeqTable st;
+    if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
     pfa::PrepParams prep{q_norm_w, k_norm_w, k_rot_out, rope_dim, rms_eps,
                          (double)rope_freq_base};
-    return attn_common(q, k, v, out, seq_offsets, n_seqs, T, n_head, n_head_kv, head_dim, scale,
-                       causal, precision, &prep, workspace, workspace_bytes, stream);
+    return attn_common(Mode::kFused, q, k, v, out, nullptr, nullptr, st, n_head, n_head_kv,
+                       head_dim, scale, causal, precision, &prep, workspace, workspace_bytes,
+                       stream);
+}
+
+int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, float* out,
+                   const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs, int T_q,
+                   int T_kv, int n_head, int n_head_kv, int head_dim, float scale, int causal,
+                   int precision, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T_q, n_head, n_head_kv, head_dim);
+    if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
+    if ((rc = check_attn(scale, precision))) return rc;
+    pfa::SeqTable st;
+    if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) return rc;
+    if (T_q == 0) return PFA_OK;
+    return attn_common(Mode::kChunk, q, k_cache, v_cache, out, nullptr, nullptr, st, n_head,
+                       n_head_kv, head_dim, scale, causal, precision, nullptr, workspace,
+                       workspace_bytes, stream);
+}
+
+int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* out,
+                       const float* q_norm_w, const float* k_norm_w, float* k_cache,
+                       float* v_cache, const int32_t* q_offsets, const int32_t* kv_offsets,
+                       int n_seqs, int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                       int rope_dim, float rope_freq_base, float rms_eps, float scale,
+                       int causal, int precision, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T_q, n_head, n_head_kv, head_dim);
+    if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
+    if ((rc = check_attn(scale, precision))) return rc;
+    if ((rc = check_rope(head_dim, rope_dim, rope_freq_base, rms_eps))) return rc;
+    pfa::SeqTable st;
+    if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) return rc;
+    if (T_q == 0) return PFA_OK;
+    if (!q_norm_w || !k_norm_w) return fail(PFA_ERR_INVALID_ARG, "null norm weights");
+    pfa::PrepParams prep{q_norm_w, k_norm_w, nullptr, rope_dim, rms_eps, (double)rope_freq_base};
+    return attn_common(Mode::kChunkFused, q, k, v, out, k_cache, v_cache, st, n_head, n_head_kv,
+                       head_dim, scale, causal, precision, &prep, workspace, workspace_bytes,
+                       stream);
 }
 
 }  // extern "C"

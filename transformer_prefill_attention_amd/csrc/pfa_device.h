@@ -92,7 +92,8 @@ struct WorkItem {
     int kc;              // key chunk (0 when the key range is not split)
     int item;            // index in the longest-first item order
     int sid;             // sequence index
-    int s0, s1;          // sequence token range [s0, s1)
+    int s0, s1;          // the sequence's query rows [s0, s1)
+    int k0, k1;          // its key rows [k0, k1); query row i sees keys <= i + k1 - s1
     int q0;              // first query row of the super-block
 };
 
@@ -108,6 +109,8 @@ __device__ __forceinline__ void decode_seq(const Sched& sched, WorkItem& w) {
     w.sid = sid;
     w.s0 = sched.off[sid];
     w.s1 = sched.off[sid + 1];
+    w.k0 = sched.koff[sid];
+    w.k1 = sched.koff[sid + 1];
     w.q0 = w.s0 + w.sb * sched.rows_per_item;
 }
 

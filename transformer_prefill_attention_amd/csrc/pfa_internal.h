@@ -10,10 +10,16 @@
 namespace pfa {
 
 // Packed-sequence boundaries, passed to kernels by value (kernel arguments),
-// so no device buffer and no host-to-device copy is needed.
+// so no device buffer and no host-to-device copy is needed.  Sequence s owns
+// rows off[s] .. off[s+1]-1 of the query-side tensors and rows koff[s] ..
+// koff[s+1]-1 of the key/value side, at least as many: its first
+// base_s = (koff[s+1] - koff[s]) - (off[s+1] - off[s]) key rows are a cached
+// prefix, and its query rows sit at positions base_s, base_s + 1, ... (plain
+// prefill: koff = off, base 0).
 struct SeqTable {
     int n_seqs;
-    int off[PFA_MAX_SEQS + 1];  // cumulative token offsets, off[n_seqs] = T
+    int off[PFA_MAX_SEQS + 1];   // cumulative query-row offsets, off[n_seqs] = T
+    int koff[PFA_MAX_SEQS + 1];  // cumulative key-row offsets
 };
 
 // Work schedule of the attention kernels, also passed by value.
@@ -31,14 +37,16 @@ struct AttnSched {
     int n_segs;                      // segments in use
     int rows_per_item;               // query rows per super-block (32 * row blocks)
     int off[PFA_MAX_SEQS + 1];       // as SeqTable::off
+    int koff[PFA_MAX_SEQS + 1];      // as SeqTable::koff
     int seg_start[PFA_MAX_SEQS + 1]; // first item of each segment; [n_segs] = item count
     int seg_top[PFA_MAX_SEQS];       // super-block count of the (k+1)-th longest sequence
     int32_t order[PFA_MAX_SEQS];     // sequence ids, most super-blocks first (32-bit: scalar loads)
     // 64-key tiles of the bf16 workspace (see launch_attn_bf16): sequence s owns
-    // tiles tile_off[s] .. tile_off[s+1]-1 of each K/V head; n_tiles in all.
+    // tiles tile_off[s] .. tile_off[s+1]-1 of each K/V head (its key rows); n_tiles
+    // in all.
     int n_tiles;
     int tile_off[PFA_MAX_SEQS + 1];
-    int max_len;                     // longest sequence (rows of the fused entry's rotary table)
+    int max_len;                     // most key rows of a sequence (rotary table rows)
     // Key split for short inputs: when the items alone cannot fill the GPU, each
     // item's key tiles are cut into chunks of kchunk tiles, one workgroup each
     // (grid = items x max_chunks x head chunks x K/V heads; chunk slots past an
@@ -80,10 +88,13 @@ struct PrepParams {
 };
 
 // Launchers (defined next to their kernels).  They only enqueue.
+// QK-norm + RoPE of T query-side rows (H = 0: K rows only).  K rows go to
+// k_out at the key rows the sequence table gives (the same rows for plain
+// prefill); with v_out, the V rows are copied there too.
 hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
-                              const float* wq, const float* wk, const SeqTable& seqs, int T,
-                              int H, int Hkv, int D, int rope_dim, float base, float eps,
-                              hipStream_t stream);
+                              const float* v_in, float* v_out, const float* wq, const float* wk,
+                              const SeqTable& seqs, int T, int H, int Hkv, int D, int rope_dim,
+                              float base, float eps, hipStream_t stream);
 
 // prep == nullptr: plain attention on already-normalised Q/K; otherwise the
 // fused entry (Q and K normalised and rotated inside the kernel).
@@ -109,9 +120,11 @@ inline size_t bf16_workspace_bytes(int n_tiles, int Hkv, int D, bool split_qk, i
     return (size_t)n_tiles * Hkv * (split_qk ? 3 : 2) * kBf16TileKeys * D * 2 +
            (size_t)rope_rows * (D / 2) * 8;
 }
-// prep != nullptr: the fused entry (K and Q normalised and rotated on the way in).
+// prep != nullptr: a fused entry (Q normalised and rotated inside the attention
+// kernel; K too, on its way into the tiles, when prep_k -- over a cached prefix
+// the cache already holds rotated keys).
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
-                            const PrepParams* prep, const Partials& part, int n_items,
-                            hipStream_t stream);
+                            const PrepParams* prep, bool prep_k, const Partials& part,
+                            int n_items, hipStream_t stream);
 }  // namespace pfa

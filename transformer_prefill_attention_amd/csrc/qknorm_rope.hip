@@ -17,6 +17,13 @@
 // Rotary pair (j, j + n/2): with n == head_dim == 128 both dims of a pair sit
 // in the same lane (no data movement); with n == 64 the partner is lane L ^ 32
 // (one cross-half shuffle); any other even n uses a general two-shuffle path.
+//
+// Over a cached prefix (memra-engine 0.101.0 src/spec.rs, `full_attn_verify`:
+// new rows are normalised and rotated at their own positions and appended to
+// the cache) row t of sequence s sits at position base_s + t - off[s], and its
+// K row -- with the V row, when v_out is given -- goes to key row t + koff[s+1] -
+// off[s+1] of the cache (the last rows of the sequence's key range).  Plain
+// prefill is the case koff = off.
 #include <algorithm>
 
 #include "pfa_device.h"
@@ -33,6 +40,7 @@ constexpr int kRowsInFlight = 4;  // head rows loaded before the first is reduce
 template <int D, int MODE>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const float* q_in, const float* k_in, float* q_out, float* k_out,
+    const float* __restrict__ v_in, float* __restrict__ v_out,
     const float* __restrict__ wq, const float* __restrict__ wk, SeqTable seqs, int T, int H,
     int Hkv, int n, double base, float eps, int groups) {
     constexpr int E = D / 64;  // dims per lane
@@ -64,7 +72,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     for (int u = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); u < T * groups; u += waves) {
         const int t = u / groups, r0 = (u % groups) * per, r1 = min(r0 + per, rows);
         const int s = find_seq(seqs.off, seqs.n_seqs, t);
-        const int pos = t - seqs.off[s];
+        const int q_end = seqs.off[s + 1], k_end = seqs.koff[s + 1];
+        const int pos = (k_end - seqs.koff[s]) - (q_end - t);  // base_s + t - off[s]
+        const int krow = t + k_end - q_end;                    // the K / V row it fills
         float cs[E], sn[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -134,16 +144,22 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
                     min(r1, H) - r0, wqv);
         if (r1 > H) {
             const int k0 = max(r0, H) - H;
-            do_rows(k_in + ((int64_t)t * Hkv + k0) * D, k_out + ((int64_t)t * Hkv + k0) * D,
+            do_rows(k_in + ((int64_t)t * Hkv + k0) * D, k_out + ((int64_t)krow * Hkv + k0) * D,
                     r1 - H - k0, wkv);
+            if (v_out) {
+                const float* vs = v_in + ((int64_t)t * Hkv + k0) * D;
+                float* vd = v_out + ((int64_t)krow * Hkv + k0) * D;
+                for (int c = lane; c < (r1 - H - k0) * D; c += 64) vd[c] = vs[c];
+            }
         }
     }
 }
 
 template <int D, int MODE>
 hipError_t launch_mode(const float* q_in, const float* k_in, float* q_out, float* k_out,
-                       const float* wq, const float* wk, const SeqTable& seqs, int T, int H,
-                       int Hkv, int n, float base, float eps, hipStream_t stream) {
+                       const float* v_in, float* v_out, const float* wq, const float* wk,
+                       const SeqTable& seqs, int T, int H, int Hkv, int n, float base,
+                       float eps, hipStream_t stream) {
     // Work units: tokens, or for short inputs runs of at least 4 head rows of a
     // token, so that ~8192 wavefronts (2048 workgroups of 4) have work.  Up to 4
     // units per wavefront so the per-lane rotary frequencies (f64 pow) are
@@ -155,32 +171,29 @@ hipError_t launch_mode(const float* q_in, const float* k_in, float* q_out, float
     int blocks = (int)std::min<long long>((units + 3) / 4, 2048);
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL((qknorm_rope_kernel<D, MODE>), dim3(blocks), dim3(256), 0, stream, q_in,
-                       k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv, n, (double)base, eps, groups);
+                       k_in, q_out, k_out, v_in, v_out, wq, wk, seqs, T, H, Hkv, n,
+                       (double)base, eps, groups);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
-                              const float* wq, const float* wk, const SeqTable& seqs, int T,
-                              int H, int Hkv, int D, int rope_dim, float base, float eps,
-                              hipStream_t stream) {
+                              const float* v_in, float* v_out, const float* wq, const float* wk,
+                              const SeqTable& seqs, int T, int H, int Hkv, int D, int rope_dim,
+                              float base, float eps, hipStream_t stream) {
+#define PFA_QKN(DD, MM)                                                                         \
+    launch_mode<DD, MM>(q_in, k_in, q_out, k_out, v_in, v_out, wq, wk, seqs, T, H, Hkv, rope_dim, \
+                        base, eps, stream)
     if (D == 128) {
-        if (rope_dim == 128)
-            return launch_mode<128, kPairInLane>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H,
-                                                 Hkv, rope_dim, base, eps, stream);
-        if (rope_dim == 64)
-            return launch_mode<128, kPairXor32>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H,
-                                                Hkv, rope_dim, base, eps, stream);
-        return launch_mode<128, kPairGeneral>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv,
-                                              rope_dim, base, eps, stream);
+        if (rope_dim == 128) return PFA_QKN(128, kPairInLane);
+        if (rope_dim == 64) return PFA_QKN(128, kPairXor32);
+        return PFA_QKN(128, kPairGeneral);
     }
     // D == 64: one dim per lane.
-    if (rope_dim == 64)
-        return launch_mode<64, kPairXor32>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv,
-                                           rope_dim, base, eps, stream);
-    return launch_mode<64, kPairGeneral>(q_in, k_in, q_out, k_out, wq, wk, seqs, T, H, Hkv,
-                                         rope_dim, base, eps, stream);
+    if (rope_dim == 64) return PFA_QKN(64, kPairXor32);
+    return PFA_QKN(64, kPairGeneral);
+#undef PFA_QKN
 }
 
 }  // namespace pfa

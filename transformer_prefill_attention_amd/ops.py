@@ -27,6 +27,7 @@ _PRECISIONS = {"f32": PRECISION_F32, "fp32": PRECISION_F32, "float32": PRECISION
 
 # Every symbol include/pfa.h declares.
 EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_workspace_bytes",
+           "gqa_chunk_attn", "qk_prep_chunk_attn", "pfa_chunk_workspace_bytes",
            "pfa_last_error", "pfa_version")
 
 
@@ -62,6 +63,14 @@ def lib() -> ctypes.CDLL:
     L.qk_prep_attn.restype = i32
     L.pfa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_workspace_bytes.restype = sz
+    L.gqa_chunk_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                 i32, vp, sz, vp]
+    L.gqa_chunk_attn.restype = i32
+    L.qk_prep_chunk_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                     i32, i32, i32, f32, f32, f32, i32, i32, vp, sz, vp]
+    L.qk_prep_chunk_attn.restype = i32
+    L.pfa_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
+    L.pfa_chunk_workspace_bytes.restype = sz
     L.pfa_last_error.restype = ctypes.c_char_p
     L.pfa_last_error.argtypes = []
     L.pfa_version.restype = ctypes.c_char_p
@@ -241,4 +250,104 @@ def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
                               _ptr(k_norm_w), op, n_seqs, T, H, Hkv, head_dim, rope_dim,
                               float(rope_freq_base), float(rms_eps), float(scale),
                               1 if causal else 0, prec, _ptr(k_rot_out), wp, wn, _stream(q)))
+    return out
+
+
+def _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv):
+    """Host int32 arrays of a chunk call (both or neither), their count and pointers."""
+    if (q_offsets is None) != (kv_offsets is None):
+        raise ValueError("give both q_offsets and kv_offsets, or neither")
+    qo, n_seqs, qp = _offsets(q_offsets, T_q)
+    ko, n_kv, kp = _offsets(kv_offsets, T_kv)
+    if qo is not None and n_kv != n_seqs:
+        raise ValueError("q_offsets and kv_offsets must have the same length")
+    return (qo, ko), n_seqs, qp, kp
+
+
+def chunk_workspace_bytes(T_q: int, T_kv: int, n_head: int, n_head_kv: int, head_dim: int,
+                          precision="f32", q_offsets=None, kv_offsets=None,
+                          fused: bool = False) -> int:
+    """Device workspace ``gqa_chunk_attn`` (``fused=False``) or ``qk_prep_chunk_attn``
+    (``fused=True``) uses for these arguments (``pfa_chunk_workspace_bytes``)."""
+    keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
+    return int(lib().pfa_chunk_workspace_bytes(qp, kp, n_seqs, T_q, T_kv, n_head, n_head_kv,
+                                               head_dim, _prec(precision), 1 if fused else 0))
+
+
+def _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec, fused,
+                     device):
+    import torch
+    need = int(lib().pfa_chunk_workspace_bytes(qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim,
+                                               prec, 1 if fused else 0))
+    if need == 0:
+        return None, ctypes.c_void_p(0), 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    elif not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a GPU torch.Tensor")
+    return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float] = None,
+                   causal: bool = True, precision="f32", q_offsets=None, kv_offsets=None,
+                   out=None, workspace=None):
+    """Attention of new query rows over a K/V cache (``gqa_chunk_attn`` in
+    ``include/pfa.h``); returns ``out``.  Sequence s owns query rows
+    ``q_offsets[s]..q_offsets[s+1]`` and cache rows ``kv_offsets[s]..kv_offsets[s+1]``,
+    its new rows being the last ones of its cache range."""
+    import torch
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev_f32(t, n)
+    T_q, H = _heads(q, head_dim, "q")
+    T_kv, Hkv = _heads(k_cache, head_dim, "k_cache")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = head_dim ** -0.5
+    keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
+    prec = _prec(precision)
+    ws, wp, wn = _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec,
+                                  False, q.device)
+    _check(lib().gqa_chunk_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), qp, kp,
+                                n_seqs, T_q, T_kv, H, Hkv, head_dim, float(scale),
+                                1 if causal else 0, prec, wp, wn, _stream(q)))
+    return out
+
+
+def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_dim: int,
+                       rope_dim: int, rope_freq_base: float, rms_eps: float,
+                       scale: Optional[float] = None, causal: bool = True, precision="f32",
+                       q_offsets=None, kv_offsets=None, out=None, workspace=None):
+    """Fused QK-norm + RoPE of the raw new rows at their positions, their K and V written
+    into ``k_cache`` / ``v_cache`` (the last rows of each sequence's cache range), then
+    attention over the cache (``qk_prep_chunk_attn`` in ``include/pfa.h``); returns
+    ``out``."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev_f32(t, n)
+    T_q, H = _heads(q, head_dim, "q")
+    Tk, Hkv = _heads(k, head_dim, "k")
+    if Tk != T_q or v.shape != k.shape:
+        raise ValueError("q, k, v must have the same token count and k, v the same shape")
+    T_kv, Hc = _heads(k_cache, head_dim, "k_cache")
+    if Hc != Hkv or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [T_kv, n_head_kv*head_dim] like k")
+    out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = head_dim ** -0.5
+    keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
+    prec = _prec(precision)
+    ws, wp, wn = _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec,
+                                  True, q.device)
+    _check(lib().qk_prep_chunk_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(q_norm_w),
+                                    _ptr(k_norm_w), _ptr(k_cache), _ptr(v_cache), qp, kp, n_seqs,
+                                    T_q, T_kv, H, Hkv, head_dim, rope_dim, float(rope_freq_base),
+                                    float(rms_eps), float(scale), 1 if causal else 0, prec, wp,
+                                    wn, _stream(q)))
     return out
