@@ -109,6 +109,11 @@ def main():
     ap.add_argument("--path", default="unfused", choices=["fused", "unfused"],
                     help="unfused (default, currently the faster): qknorm_rope then "
                          "gqa_prefill_attn; fused: the single qk_prep_attn call")
+    ap.add_argument("--chunk-base", type=int, default=0, metavar="B",
+                    help="time a chunk over a cached prefix instead: the workload's one sequence "
+                         "is B cached rows (K normalised and rotated, V) and T - B new rows; "
+                         "fused: qk_prep_chunk_attn on the raw new rows, unfused: gqa_chunk_attn "
+                         "on prepared ones (no CPU baseline line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -141,6 +146,9 @@ def main():
 
     w = wl.sweep_workload(args.seq_len) if args.seq_len else wl.CONFIGS[args.workload]
     x = wl.make_inputs(w)
+    if args.chunk_base:
+        run_chunk(args, w, x)
+        return
     k_in = wl.with_outlier_keys(x.k, x.outliers)
     dev = torch.device("cuda:0")
     q = torch.from_numpy(x.q).to(dev)
@@ -231,6 +239,93 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, wl.Inputs(x.q, k_in, x.v, x.wq, x.wk, x.outliers),
                                            args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def run_chunk(args, w, x):
+    """One chunk of new rows over a cached prefix per step (``--chunk-base``)."""
+    import torch
+
+    import transformer_prefill_attention_amd as pfa
+
+    if w.n_seqs != 1 or not 0 < args.chunk_base < w.T:
+        raise SystemExit("--chunk-base needs a one-sequence workload longer than the prefix")
+    B, T = args.chunk_base, w.T
+    T_q = T - B
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(getattr(x, n)).to(dev) for n in ("q", "k", "v", "wq", "wk")}
+    kw_rope = dict(head_dim=w.head_dim, rope_dim=w.rope_dim, rope_freq_base=w.rope_freq_base,
+                   rms_eps=w.rms_eps)
+    # the cache a previous call would have left: normalised, rotated K and V of all rows
+    # (the fused step rewrites its new rows in place each time)
+    qn, kn = pfa.qknorm_rope(t["q"], t["k"], t["wq"], t["wk"], **kw_rope)
+    k_cache, v_cache = kn.clone(), t["v"].clone()
+    q_new, k_new, v_new = t["q"][B:].contiguous(), t["k"][B:].contiguous(), t["v"][B:].contiguous()
+    q_prep = qn[B:].contiguous()
+    out = torch.empty_like(q_new)
+    stream = torch.cuda.current_stream(dev)
+    ev = []
+
+    def step(record):
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        if args.path == "fused":
+            pfa.qk_prep_chunk_attn(q_new, k_new, v_new, t["wq"], t["wk"], k_cache, v_cache,
+                                   scale=w.softmax_scale, precision=args.precision, out=out,
+                                   **kw_rope)
+        else:
+            pfa.gqa_chunk_attn(q_prep, k_cache, v_cache, head_dim=w.head_dim,
+                               scale=w.softmax_scale, precision=args.precision, out=out)
+        if record:
+            b.record(stream)
+            ev.append((a, b))
+
+    t_spin = time.perf_counter()
+    while (time.perf_counter() - t_spin) * 1e3 < args.spinup_ms:
+        step(False)
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # visible (query, key) pairs per head: row r sees B + r + 1 keys
+    pairs = T_q * B + T_q * (T_q + 1) // 2
+    flops = 4 * w.head_dim * w.n_head * pairs
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[args.precision]
+    d = w.head_dim
+    if args.precision == "f32":
+        kernel = (f"qknorm_rope_kernel<{d},0> + attn_f32_kernel<{d},true>" if args.path == "fused"
+                  else f"attn_f32_kernel<{d},false>")
+    else:
+        split = "true" if args.precision == "bf16x3" else "false"
+        kernel = f"stage_kv_bf16_kernel<{d},{split},false> + "
+        if args.path == "fused":
+            kernel = (f"qknorm_rope_kernel<{d},0> + rope_table_kernel<{d},{split}> + " + kernel +
+                      f"attn_bf16_kernel<{d},{split},true>")
+        else:
+            kernel += f"attn_bf16_kernel<{d},{split},false>"
+    res = {
+        "metric": METRIC, "value": round(flops / (elapsed / args.steps) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "spinup_ms": args.spinup_ms, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.precision, "data": "synthetic (seeded N(0,1) Q/K/V, norm weights 1+N(0,0.1))",
+        "config": {"workload": f"{w.name} chunk: {T_q} new rows over {B} cached rows, "
+                               f"n_head={w.n_head}, n_head_kv={w.n_head_kv}, head_dim={d}, "
+                               f"rope_dim={w.rope_dim}",
+                   "T_q": T_q, "T_kv": T, "n_head": w.n_head, "n_head_kv": w.n_head_kv,
+                   "head_dim": d, "path": args.path, "causal_flops": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": kernel, "kernel_ms": round(kern_ms, 4)},
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -140,11 +140,15 @@ def _ceil(a, b):
     return -(-a // b)
 
 
-def _expected_workspace(lens, H, Hkv, D, prec, fused):
-    """The workspace rule pfa_workspace_bytes documents, restated: bf16 tiles (plus the
-    rotary table for the fused entry) or the f32 fused entry's rotated K, then partial
-    results when the (query block, head) items cannot fill half of the GPU's workgroup
-    slots (a target of 256 f32 or 128 bf16 workgroups) and are split by key."""
+def _expected_workspace(lens, H, Hkv, D, prec, fused, kv_lens=None, chunk=False):
+    """The workspace rule pfa_workspace_bytes / pfa_chunk_workspace_bytes document,
+    restated: bf16 tiles of every sequence's key rows (plus the rotary table, as long as
+    the longest, when Q is prepared in the kernel) or the f32 fused prefill's rotated K,
+    then partial results when the (query block, head) items cannot fill the GPU's
+    workgroup slots (a target of 512 f32 or 256 bf16 workgroups) and are split by key,
+    at least 128 keys a chunk and at most 32 chunks an item.  ``lens``: query rows per
+    sequence; ``kv_lens``: key rows (default: the same)."""
+    kv_lens = lens if kv_lens is None else kv_lens
     bf16 = prec != 0
     waves, tile = (8, 64) if bf16 else (4, 32)
     g = H // Hkv
@@ -153,24 +157,27 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused):
         hpw *= 2
     chunks, rows = g // hpw, 32 * (waves // hpw)
     items = sum(_ceil(n, rows) for n in lens)
-    n_max = _ceil(max(lens), tile)
-    wgs, target = items * chunks * Hkv, (1 if bf16 else 2) * 128
+    n_max = _ceil(max(kv_lens), tile)
+    wgs, target = items * chunks * Hkv, (1 if bf16 else 2) * 256
     kchunk = 0
     if wgs < target and n_max > 1:
-        kchunk = max(1, _ceil(wgs * n_max, target))
+        # at least 128 keys a chunk, at most 32 chunks an item
+        kchunk = max(_ceil(128, tile), _ceil(n_max, 32), _ceil(wgs * n_max, target))
         if kchunk >= n_max:
             kchunk = 0
     parts = 0
-    if kchunk:
+    if kchunk and items:
         units = items * _ceil(n_max, kchunk) * chunks * Hkv
         parts = units * waves * 32 * (D * 4 + 8)
     base = 0
     if bf16:
-        base = Hkv * sum(_ceil(n, 64) for n in lens) * 64 * D * 2 * (3 if prec == 2 else 2)
+        base = Hkv * sum(_ceil(n, 64) for n in kv_lens) * 64 * D * 2 * (3 if prec == 2 else 2)
         if fused:
-            base += max(lens) * (D // 2) * 8
-    elif fused:
+            base += max(kv_lens) * (D // 2) * 8
+    elif fused and not chunk:
         base = sum(lens) * Hkv * D * 4
+    if items == 0:
+        return 0
     return (_ceil(base, 256) * 256 + parts) if parts else base
 
 
@@ -300,13 +307,22 @@ def test_chunk_workspace_without_prefix_is_the_prefill_rule(L, prec, fused):
         assert _chunk_ws(L, lens, lens, 16, 8, 128, prec, fused) == expect
 
 
+@pytest.mark.parametrize("prec", [0, 1, 2])
+@pytest.mark.parametrize("fused", [0, 1])
+@pytest.mark.parametrize("q_lens,kv_lens,H,Hkv,D", [
+    ((1024,), (8192,), 32, 8, 128), ((1,), (8192,), 32, 8, 128), ((4096,), (8192,), 32, 8, 128),
+    ((50, 1, 130, 0), (70, 78, 130, 5), 8, 4, 128), ((90,), (135,), 4, 2, 64)])
+def test_chunk_workspace_rule(L, q_lens, kv_lens, H, Hkv, D, prec, fused):
+    assert _chunk_ws(L, q_lens, kv_lens, H, Hkv, D, prec, fused) == \
+        _expected_workspace(q_lens, H, Hkv, D, prec, fused, kv_lens=kv_lens, chunk=True)
+
+
 def test_chunk_workspace_tiles_cover_the_cache(L):
-    # bf16: tiles of every sequence's cache rows; the rotary table covers the longest
-    # cache (positions base + r); no key split at this size
-    q_lens, kv_lens = (1024,), (8192,)
+    # bf16, 8192 cache rows with 4096 new: no key split, so exactly the tiles of all 8192
+    # rows (+ a rotary table as long as the cache for the fused entry)
     tiles = 8 * 128 * 64 * 128 * 2
-    assert _chunk_ws(L, q_lens, kv_lens, 32, 8, 128, 1, 0) == 2 * tiles
-    assert _chunk_ws(L, q_lens, kv_lens, 32, 8, 128, 1, 1) == 2 * tiles + 8192 * 64 * 8
-    assert _chunk_ws(L, q_lens, kv_lens, 32, 8, 128, 2, 0) == 3 * tiles
-    assert pfa.chunk_workspace_bytes(1024, 8192, 32, 8, 128, "bf16", fused=True) == \
+    assert _chunk_ws(L, (4096,), (8192,), 32, 8, 128, 1, 0) == 2 * tiles
+    assert _chunk_ws(L, (4096,), (8192,), 32, 8, 128, 1, 1) == 2 * tiles + 8192 * 64 * 8
+    assert _chunk_ws(L, (4096,), (8192,), 32, 8, 128, 2, 0) == 3 * tiles
+    assert pfa.chunk_workspace_bytes(4096, 8192, 32, 8, 128, "bf16", fused=True) == \
         2 * tiles + 8192 * 64 * 8

@@ -184,22 +184,27 @@ constexpr int kCUs = 256;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Key split: when items x head chunks x K/V heads workgroups cannot fill half of
-// the GPU's workgroup slots (target), cut every item's key tiles into chunks of
-// kchunk.  With the longest item at n_max tiles, a causal item of n tiles becomes
-// ceil(n / kchunk) units; kchunk = wgs n_max / target keeps a causal single
-// sequence near target / 2 + wgs / 2 units.  Each unit re-reads its Q rows and
-// writes a partial result, so fewer, longer chunks beat one chunk per tile: a
-// target of half the slots measured 4-12% faster than all of them at T = 512
-// (twice the slots was slower still).
+// Key split: when items x head chunks x K/V heads workgroups cannot fill the GPU's
+// workgroup slots (target: 256 CUs x 2 f32 or x 1 bf16 workgroups), cut every
+// item's key tiles into chunks of kchunk tiles.  With the longest item at n_max
+// tiles, a causal item of n tiles becomes ceil(n / kchunk) units; kchunk = wgs
+// n_max / target keeps a causal single sequence near target / 2 + wgs / 2 units.
+// Each unit re-reads its Q rows and writes a partial result, so a chunk holds at
+// least 128 keys (at T = 512 shorter chunks were 4-12% slower; a chunk of 1024
+// new rows over 7168 cached ones, whose items fill only half the slots, gets two:
+// 7-24% faster), and an item is cut into at most kMaxKeyChunks chunks (one new row
+// over 8191 cached ones ran 8-20% slower in 64 chunks than in 32).
+constexpr int kMaxKeyChunks = 32;
 void choose_split(Plan& p, int head_dim) {
     const long long wgs = (long long)p.items * p.geom.chunks * p.geom.Hkv;
-    const int target = (p.waves == 8 ? 1 : 2) * kCUs / 2;
+    const int target = (p.waves == 8 ? 1 : 2) * kCUs;
     const int n_max = (p.sched.max_len + p.tile_keys - 1) / p.tile_keys;
+    const long long k_min = std::max<long long>((128 + p.tile_keys - 1) / p.tile_keys,
+                                                (n_max + kMaxKeyChunks - 1) / kMaxKeyChunks);
     int kchunk = 0;
     if (wgs < target && n_max > 1) {
         const long long k = (wgs * n_max + target - 1) / target;
-        kchunk = (int)std::max(1LL, k);
+        kchunk = (int)std::max(k_min, k);
         if (kchunk >= n_max) kchunk = 0;
     }
     p.sched.kchunk = kchunk;
