@@ -35,6 +35,11 @@
  *    prefill).
  *  - needle-core v3/model.rs, cache fill after the prefill: what a cache keeps
  *    are the normalised, rotated keys and the values.
+ *  - memra-engine 0.101.0 src/spec.rs, sliding-window layers of the step35 MTP
+ *    path: once a sequence holds more than `window` keys, a new token attends
+ *    only the last `window` of them, itself included (needle-core v3/model.rs
+ *    passes a per-layer attention span to its attention for the same purpose):
+ *    row i sees key j when i - window < j <= i.
  *
  * Readings taken where the pages are silent (each one is listed with its
  * reason in the design notes of the repository):
@@ -250,6 +255,7 @@ typedef struct {
     const int32_t* offsets;    /* query rows of each sequence */
     const int32_t* kv_offsets; /* key rows of each sequence (the same for plain prefill) */
     int n_seqs, H, Hkv, d, causal;
+    int64_t window;            /* causal only: keys visible per row, the row's own included; 0: all */
     double scale;
 } attn_ctx;
 
@@ -265,6 +271,7 @@ static void attn_unit(void* vctx, int64_t unit, double* e) {
     int64_t base = ((int64_t)c->kv_offsets[s + 1] - lo) - (c->offsets[s + 1] - c->offsets[s]);
     int64_t last = lo + base + (i - c->offsets[s]);
     int64_t hi = c->causal ? last : (int64_t)c->kv_offsets[s + 1] - 1; /* inclusive */
+    if (c->causal && c->window > 0 && last - c->window + 1 > lo) lo = last - c->window + 1;
     int g = c->H / c->Hkv;
     int kv = h / g;
     int d = c->d;
@@ -303,16 +310,18 @@ static void attn_unit(void* vctx, int64_t unit, double* e) {
  * were there before, the query rows are the last ones.  out[r, h, :] =
  * softmax_j(scale * q[i,h,:] . k[j,kv,:]) v[j,kv,:] over the visible keys j of
  * row i = rows[r] (or r when rows is NULL): the keys of i's sequence, and when
- * causal only those up to i's own position (base_s + i - q_offsets[s]).  All
- * arithmetic in f64.  NULL offsets (both): one sequence. */
+ * causal only those up to i's own position (base_s + i - q_offsets[s]) and, with
+ * window > 0, not more than window of them (the latest).  All arithmetic in f64.
+ * NULL offsets (both): one sequence. */
 int oracle_chunk_attn(const double* q, const double* k, const double* v,
                       const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
                       int64_t T_q, int64_t T_kv, int n_head, int n_head_kv, int head_dim,
-                      double scale, int causal, const int64_t* rows, int64_t n_rows,
-                      double* out, int n_threads) {
+                      double scale, int causal, int64_t window, const int64_t* rows,
+                      int64_t n_rows, double* out, int n_threads) {
     int32_t one_q[2], one_kv[2];
     if (T_q < 0 || T_kv < 0 || n_head <= 0 || n_head_kv <= 0 || head_dim <= 0 ||
-        n_head % n_head_kv || (!q_offsets) != (!kv_offsets))
+        n_head % n_head_kv || (!q_offsets) != (!kv_offsets) || window < 0 ||
+        (window > 0 && !causal))
         return ORACLE_BAD_ARG;
     if (!q_offsets) {
         one_q[0] = 0;
@@ -333,7 +342,7 @@ int oracle_chunk_attn(const double* q, const double* k, const double* v,
     for (int64_t r = 0; rows && r < n_rows; ++r)
         if (rows[r] < 0 || rows[r] >= T_q) return ORACLE_BAD_ARG;
     attn_ctx c = {q, k, v, out, rows, q_offsets, kv_offsets, n_seqs, n_head, n_head_kv,
-                  head_dim, causal ? 1 : 0, scale};
+                  head_dim, causal ? 1 : 0, window, scale};
     return run_pool(attn_unit, &c, n_rows * n_head, (size_t)T_kv, n_threads); /* scores: <= T_kv */
 }
 
@@ -346,7 +355,8 @@ int oracle_gqa_attn(const double* q, const double* k, const double* v,
                     int n_head_kv, int head_dim, double scale, int causal,
                     const int64_t* rows, int64_t n_rows, double* out, int n_threads) {
     return oracle_chunk_attn(q, k, v, seq_offsets, seq_offsets, n_seqs, T, T, n_head,
-                             n_head_kv, head_dim, scale, causal, rows, n_rows, out, n_threads);
+                             n_head_kv, head_dim, scale, causal, 0, rows, n_rows, out,
+                             n_threads);
 }
 
 const char* oracle_version(void) { return "pfa-oracle 1 (f64, plain loops)"; }

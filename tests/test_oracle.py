@@ -566,3 +566,63 @@ def test_chunk_rejects_short_caches():
     with pytest.raises(ValueError):
         oracle.chunk_attn(q, np.zeros((6, 8)), np.zeros((6, 8)), n_head=1, n_head_kv=1,
                           head_dim=8, scale=1.0, q_offsets=[0, 3, 4], kv_offsets=[0, 2, 6])
+
+
+# ---------------------------------------------------------------------------
+# Sliding window (memra-engine 0.101.0 src/spec.rs, step35 MTP layers: past `window`
+# keys a new token attends only the last `window`, itself included).
+
+def test_window_of_one_returns_the_rows_own_value():
+    # one visible key per row, its own: softmax weight 1, the output is that value exactly
+    H, Hkv, d = 4, 2, 8
+    r = _rng(21)
+    q_offs, kv_offs = np.array([0, 6, 9], np.int32), np.array([0, 10, 14], np.int32)
+    q = r.standard_normal((9, H * d))
+    kc = r.standard_normal((14, Hkv * d))
+    vc = r.standard_normal((14, Hkv * d))
+    out = oracle.chunk_attn(q, kc, vc, n_head=H, n_head_kv=Hkv, head_dim=d, scale=0.3,
+                            q_offsets=q_offs, kv_offsets=kv_offs, window=1)
+    own = np.concatenate([np.arange(4, 10), np.arange(11, 14)])   # the keys at the rows' positions
+    for h in range(H):
+        kvh = h // (H // Hkv)
+        np.testing.assert_array_equal(out[:, h * d:(h + 1) * d], vc[own, kvh * d:(kvh + 1) * d])
+
+
+def test_window_at_least_the_cache_changes_nothing():
+    H, Hkv, d = 4, 4, 8
+    r = _rng(22)
+    q = r.standard_normal((5, H * d))
+    kc = r.standard_normal((12, Hkv * d))
+    vc = r.standard_normal((12, Hkv * d))
+    kw = dict(n_head=H, n_head_kv=Hkv, head_dim=d, scale=0.4)
+    full = oracle.chunk_attn(q, kc, vc, **kw)
+    for w in (12, 13, 1000):
+        np.testing.assert_array_equal(oracle.chunk_attn(q, kc, vc, window=w, **kw), full)
+
+
+@pytest.mark.parametrize("window", [2, 5, 9])
+def test_window_matches_torch_sdpa_with_band_mask(window):
+    # torch's f64 SDPA with the band j in (base + r - window, base + r]
+    H, Hkv, d = 6, 2, 16
+    r = _rng(23)
+    base, n = 7, 6
+    q = r.standard_normal((n, H * d))
+    kc = r.standard_normal((base + n, Hkv * d))
+    vc = r.standard_normal((base + n, Hkv * d))
+    out = oracle.chunk_attn(q, kc, vc, n_head=H, n_head_kv=Hkv, head_dim=d, scale=0.2,
+                            window=window)
+    qs = torch.from_numpy(q).view(n, H, d).transpose(0, 1)
+    ks = torch.from_numpy(kc).view(-1, Hkv, d).transpose(0, 1).repeat_interleave(H // Hkv, 0)
+    vs = torch.from_numpy(vc).view(-1, Hkv, d).transpose(0, 1).repeat_interleave(H // Hkv, 0)
+    rr = torch.arange(n)[:, None] + base
+    jj = torch.arange(base + n)[None, :]
+    mask = (jj <= rr) & (jj > rr - window)
+    ref = F.scaled_dot_product_attention(qs, ks, vs, attn_mask=mask, scale=0.2)
+    np.testing.assert_allclose(out, ref.transpose(0, 1).reshape(n, H * d).numpy(), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_window_rejected_without_causal():
+    with pytest.raises(ValueError):
+        oracle.chunk_attn(np.zeros((2, 8)), np.zeros((2, 8)), np.zeros((2, 8)), n_head=1,
+                          n_head_kv=1, head_dim=8, scale=1.0, causal=False, window=4)

@@ -33,6 +33,8 @@ MUTANTS = [
     ("prefix one short", "int64_t last = lo + base + (i - c->offsets[s]);",
      "int64_t last = lo + base - (base > 0) + (i - c->offsets[s]);"),
     ("start positions ignored", "if (c->pos0) pos += c->pos0[s];", "(void)c->pos0;"),
+    ("window one key wider", "last - c->window + 1 > lo) lo = last - c->window + 1;",
+     "last - c->window > lo) lo = last - c->window;"),
 ]
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins)
