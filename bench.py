@@ -114,6 +114,9 @@ def main():
                          "is B cached rows (K normalised and rotated, V) and T - B new rows; "
                          "fused: qk_prep_chunk_attn on the raw new rows, unfused: gqa_chunk_attn "
                          "on prepared ones (no CPU baseline line)")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="with the chunk entry points (any --chunk-base, 0 included): a sliding "
+                         "window of W keys per row, its own included")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -146,7 +149,7 @@ def main():
 
     w = wl.sweep_workload(args.seq_len) if args.seq_len else wl.CONFIGS[args.workload]
     x = wl.make_inputs(w)
-    if args.chunk_base:
+    if args.chunk_base or args.window:
         run_chunk(args, w, x)
         return
     k_in = wl.with_outlier_keys(x.k, x.outliers)
@@ -248,7 +251,7 @@ def run_chunk(args, w, x):
 
     import transformer_prefill_attention_amd as pfa
 
-    if w.n_seqs != 1 or not 0 < args.chunk_base < w.T:
+    if w.n_seqs != 1 or not 0 <= args.chunk_base < w.T:
         raise SystemExit("--chunk-base needs a one-sequence workload longer than the prefix")
     B, T = args.chunk_base, w.T
     T_q = T - B
@@ -272,11 +275,12 @@ def run_chunk(args, w, x):
             a.record(stream)
         if args.path == "fused":
             pfa.qk_prep_chunk_attn(q_new, k_new, v_new, t["wq"], t["wk"], k_cache, v_cache,
-                                   scale=w.softmax_scale, precision=args.precision, out=out,
-                                   **kw_rope)
+                                   scale=w.softmax_scale, window=args.window,
+                                   precision=args.precision, out=out, **kw_rope)
         else:
             pfa.gqa_chunk_attn(q_prep, k_cache, v_cache, head_dim=w.head_dim,
-                               scale=w.softmax_scale, precision=args.precision, out=out)
+                               scale=w.softmax_scale, window=args.window,
+                               precision=args.precision, out=out)
         if record:
             b.record(stream)
             ev.append((a, b))
@@ -293,8 +297,13 @@ def run_chunk(args, w, x):
         step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    # visible (query, key) pairs per head: row r sees B + r + 1 keys
-    pairs = T_q * B + T_q * (T_q + 1) // 2
+    # visible (query, key) pairs per head: row r sees B + r + 1 keys, or with a window
+    # min(W, B + r + 1)
+    if args.window:
+        Wn = args.window
+        pairs = sum(min(Wn, B + r + 1) for r in range(T_q))
+    else:
+        pairs = T_q * B + T_q * (T_q + 1) // 2
     flops = 4 * w.head_dim * w.n_head * pairs
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -319,7 +328,8 @@ def run_chunk(args, w, x):
         "dtype": args.precision, "data": "synthetic (seeded N(0,1) Q/K/V, norm weights 1+N(0,0.1))",
         "config": {"workload": f"{w.name} chunk: {T_q} new rows over {B} cached rows, "
                                f"n_head={w.n_head}, n_head_kv={w.n_head_kv}, head_dim={d}, "
-                               f"rope_dim={w.rope_dim}",
+                               f"rope_dim={w.rope_dim}"
+                               + (f", window={args.window}" if args.window else ""),
                    "T_q": T_q, "T_kv": T, "n_head": w.n_head, "n_head_kv": w.n_head_kv,
                    "head_dim": d, "path": args.path, "causal_flops": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,

@@ -201,13 +201,19 @@ int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
  *           sequence needs at least as many cache rows as new rows.
  *  Row r of sequence s (position base_s + r) sees, when causal, cache rows
  *  0 .. base_s + r of its sequence; otherwise all of them.  base_s = 0 for every
- *  sequence is gqa_prefill_attn.  scale, precision, workspace as for
- *  gqa_prefill_attn, the workspace sized by pfa_chunk_workspace_bytes(..., 0).
+ *  sequence is gqa_prefill_attn.
+ *  window  0, or (causal only) a sliding window: row r sees only the last `window`
+ *        of those keys, its own included -- cache rows base_s + r - window + 1 ..
+ *        base_s + r (memra-engine 0.101.0 src/spec.rs, the step35 MTP layers'
+ *        sliding-window view; needle-core v3/model.rs, per-layer attention span).
+ *        Negative, or positive without causal: PFA_ERR_INVALID_ARG.
+ *  scale, precision, workspace as for gqa_prefill_attn, the workspace sized by
+ *  pfa_chunk_workspace_bytes(..., 0).
  */
 int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, float* out,
                    const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
                    int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
-                   float scale, int causal, int precision,
+                   float scale, int causal, int window, int precision,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -226,6 +232,7 @@ int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, f
  *        the new rows' rotated K and V.  They must not overlap each other or the
  *        other tensors.
  *  out  [T_q, n_head*head_dim] f32, device, written.
+ *  window  as for gqa_chunk_attn.
  *  workspace  as for gqa_prefill_attn, sized by pfa_chunk_workspace_bytes(...,
  *        1); PFA_PREC_F32 needs none unless the key split is wanted.
  */
@@ -234,7 +241,7 @@ int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* ou
                        float* k_cache, float* v_cache,
                        const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
                        int T_q, int T_kv, int n_head, int n_head_kv, int head_dim, int rope_dim,
-                       float rope_freq_base, float rms_eps, float scale, int causal,
+                       float rope_freq_base, float rms_eps, float scale, int causal, int window,
                        int precision, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace in bytes that gqa_chunk_attn (fused = 0) or qk_prep_chunk_attn

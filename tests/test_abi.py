@@ -260,13 +260,13 @@ def _i32(a):
 
 
 def _chunk(L, q_offs, kv_offs, T_q, T_kv, H=4, Hkv=2, D=64, prec=0, ptrs=(8, 8, 8, 8 << 20),
-           ws=0, ws_bytes=0):
+           ws=0, ws_bytes=0, causal=1, window=0):
     keep_q, qp = _i32(q_offs) if q_offs is not None else (None, None)
     keep_k, kp = _i32(kv_offs) if kv_offs is not None else (None, None)
     n = len(q_offs) - 1 if q_offs is not None else 0
     q, k, v, o = (ctypes.c_void_p(p) for p in ptrs)
-    return L.gqa_chunk_attn(q, k, v, o, qp, kp, n, T_q, T_kv, H, Hkv, D, 0.125, 1, prec,
-                            ctypes.c_void_p(ws), ws_bytes, None)
+    return L.gqa_chunk_attn(q, k, v, o, qp, kp, n, T_q, T_kv, H, Hkv, D, 0.125, causal, window,
+                            prec, ctypes.c_void_p(ws), ws_bytes, None)
 
 
 def test_chunk_with_no_new_rows_is_ok_without_pointers(L):
@@ -326,3 +326,10 @@ def test_chunk_workspace_tiles_cover_the_cache(L):
     assert _chunk_ws(L, (4096,), (8192,), 32, 8, 128, 2, 0) == 3 * tiles
     assert pfa.chunk_workspace_bytes(4096, 8192, 32, 8, 128, "bf16", fused=True) == \
         2 * tiles + 8192 * 64 * 8
+
+
+def test_chunk_window_arguments(L):
+    assert _chunk(L, [0, 4], [0, 9], 4, 9, window=-1) == INVALID
+    assert "window" in _msg(L)
+    assert _chunk(L, [0, 4], [0, 9], 4, 9, window=3, causal=0) == INVALID
+    assert "causal" in _msg(L)

@@ -7,7 +7,10 @@ Inputs are whole sequences from the seeded workload generator; each sequence's f
 cache keeps it, rounded to f32), the rest the new rows.  Element by element at small
 sizes (tile-aligned and ragged prefixes, one new row, no prefix, packed sequences with
 different prefixes, head_dim 64, a prefix long enough for the key split), and on
-sampled rows at the benchmark's chunk shape (8192 cache rows, 1024 new)."""
+sampled rows at the benchmark's chunk shape (8192 cache rows, 1024 new).  The sliding
+window (each row sees only the last ``window`` keys up to its own) is checked on the
+same cases: windows on and off tile edges, of one key, across packed sequences, with
+the key split, and a windowed prefill of 8192 rows on sampled rows."""
 import numpy as np
 import pytest
 import torch
@@ -69,41 +72,44 @@ def _t(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def _chunk_gpu(c, precision, causal=True):
-    print(c.label("gqa_chunk_attn", precision, causal), flush=True)
+def _chunk_gpu(c, precision, causal=True, window=0):
+    print(c.label("gqa_chunk_attn", precision, causal) + f" window={window}", flush=True)
     dev = torch.device("cuda:0")
     out = pfa.gqa_chunk_attn(_t(c.q_prep, dev), _t(c.k_cache, dev), _t(c.v_cache, dev),
                              head_dim=c.d, scale=c.w.softmax_scale, causal=causal,
-                             precision=precision, q_offsets=c.q_offs, kv_offsets=c.kv_offs)
+                             window=window, precision=precision, q_offsets=c.q_offs,
+                             kv_offsets=c.kv_offs)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-def _chunk_ref(c, causal=True, rows=None):
+def _chunk_ref(c, causal=True, rows=None, window=0):
     return oracle.chunk_attn(c.q_prep, c.k_cache, c.v_cache, n_head=c.H, n_head_kv=c.Hkv,
                              head_dim=c.d, scale=c.w.softmax_scale, causal=causal,
-                             q_offsets=c.q_offs, kv_offsets=c.kv_offs, rows=rows)
+                             q_offsets=c.q_offs, kv_offsets=c.kv_offs, window=window,
+                             rows=rows)
 
 
-def _fused_gpu(c, precision, causal=True):
-    print(c.label("qk_prep_chunk_attn", precision, causal), flush=True)
+def _fused_gpu(c, precision, causal=True, window=0):
+    print(c.label("qk_prep_chunk_attn", precision, causal) + f" window={window}", flush=True)
     dev = torch.device("cuda:0")
     kc, vc = _t(c.k_prefix, dev), _t(c.v_prefix, dev)
     out = pfa.qk_prep_chunk_attn(_t(c.x.q[c.new], dev), _t(c.x.k[c.new], dev),
                                  _t(c.x.v[c.new], dev), _t(c.x.wq, dev), _t(c.x.wk, dev), kc, vc,
                                  head_dim=c.d, rope_dim=c.n, rope_freq_base=1e6, rms_eps=1e-6,
-                                 scale=c.w.softmax_scale, causal=causal, precision=precision,
-                                 q_offsets=c.q_offs, kv_offsets=c.kv_offs)
+                                 scale=c.w.softmax_scale, causal=causal, window=window,
+                                 precision=precision, q_offsets=c.q_offs, kv_offsets=c.kv_offs)
     torch.cuda.synchronize()
     return out.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy()
 
 
-def _fused_ref(c, causal=True, rows=None):
+def _fused_ref(c, causal=True, rows=None, window=0):
     return oracle.qk_prep_chunk_attn(c.x.q[c.new], c.x.k[c.new], c.x.v[c.new], c.x.wq, c.x.wk,
                                      c.k_prefix, c.v_prefix, n_head=c.H, n_head_kv=c.Hkv,
                                      head_dim=c.d, rope_dim=c.n, rope_freq_base=c.base_f,
                                      rms_eps=c.eps, scale=c.w.softmax_scale, causal=causal,
-                                     q_offsets=c.q_offs, kv_offsets=c.kv_offs, rows=rows)
+                                     q_offsets=c.q_offs, kv_offsets=c.kv_offs, window=window,
+                                     rows=rows)
 
 
 @pytest.fixture(scope="module", params=list(CASES))
@@ -175,6 +181,44 @@ def test_chunk_benchmark_shape_sampled_rows(precision):
     got, _, _ = _fused_gpu(c, precision)
     ref = _fused_ref(c, rows=rows)[0]
     what = c.label("qk_prep_chunk_attn", precision) + " (sampled rows)"
+    if precision == "f32":
+        assert_f32_parity(got[rows], ref, what)
+    else:
+        assert_bf16_parity(got[rows], ref, what)
+
+
+WINDOWS = [("no_prefix", 64), ("no_prefix", 100), ("ragged_prefix", 1), ("packed", 50),
+           ("long_prefix", 300), ("tile_aligned", 128), ("d64", 500)]
+
+
+@pytest.mark.parametrize("name,window", WINDOWS, ids=[f"{n}-w{w}" for n, w in WINDOWS])
+@pytest.mark.parametrize("precision", ["f32", "bf16"])
+def test_chunk_window_matches_oracle(name, window, precision):
+    c = Case(name, *CASES[name])
+    got = _chunk_gpu(c, precision, window=window)
+    ref = _chunk_ref(c, window=window)
+    what = c.label("gqa_chunk_attn", precision) + f" window={window}"
+    if precision == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)
+    got, _, _ = _fused_gpu(c, precision, window=window)
+    ref = _fused_ref(c, window=window)[0]
+    what = c.label("qk_prep_chunk_attn", precision) + f" window={window}"
+    if precision == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16"])
+def test_windowed_prefill_sampled_rows(precision):
+    # 8192 rows, no prefix, a window of 1000 keys: the chunk entry as a windowed prefill
+    c = Case("win_prefill", (8192,), (0,), 32, 8, 128, 128, seed=703)
+    rows = np.concatenate([np.arange(0, 8), np.linspace(990, 8191, 20)]).astype(np.int64)
+    got = _chunk_gpu(c, precision, window=1000)
+    ref = _chunk_ref(c, rows=rows, window=1000)
+    what = c.label("gqa_chunk_attn", precision) + " window=1000 (sampled rows)"
     if precision == "f32":
         assert_f32_parity(got[rows], ref, what)
     else:

@@ -341,11 +341,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     const int nt_seq = (ks1 - ks0 + kBN - 1) / kBN;
     const int n_tiles =
         causal ? (min(q0 + sched.rows_per_item, s1) - 1 + dsh - ks0) / kBN + 1 : nt_seq;
+    // with a sliding window the item starts at its first row's first visible key
+    const int win = causal ? geom.window : 0;
+    const int t_first = win > 0 ? max(0, q0 + dsh - win + 1 - ks0) / kBN : 0;
     // key split: this workgroup takes tiles [t_begin, t_begin + n_local) of the item
-    const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles;
-    const int n_chunks = (n_tiles + kchunk - 1) / kchunk;
+    const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles - t_first;
+    const int n_chunks = (n_tiles - t_first + kchunk - 1) / kchunk;
     if (wi.kc >= n_chunks) return;  // (uniform: the whole workgroup leaves)
-    const int t_begin = wi.kc * kchunk, n_local = min(kchunk, n_tiles - t_begin);
+    const int t_begin = t_first + wi.kc * kchunk, n_local = min(kchunk, n_tiles - t_begin);
     const bool split = n_chunks > 1;
 
     const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;
@@ -354,6 +357,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     const bool active = wq0 < s1;
     const int wave_last =
         causal ? min((min(wq0 + 31, s1 - 1) + dsh - ks0) / kBN, nt_seq - 1) : nt_seq - 1;
+    const int wave_first = win > 0 ? max(0, wq0 + dsh - win + 1 - ks0) / kBN : 0;
+    // (with a window: the lowest key the wavefront's last row sees; below it, masks)
+    const int wave_lo = wq0 + 31 + dsh - win + 1;
     const int qi = wq0 + ln;
 
     // ---- Q operand (B of K Q^T): for step s, lane (hl, ln) supplies
@@ -589,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     // X(lt): scores of local tile lt -> P (bf16, B-operand layout), running max and sum.
     auto x_phase = [&](int lt) {
         const int t = t_begin + lt;
-        if (lt < 0 || lt >= n_local || t > wave_last) {
+        if (lt < 0 || lt >= n_local || t > wave_last || t < wave_first) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -598,14 +604,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
         }
         const int k0 = ks0 + t * kBN;
         // register r of block kb: key k0 + 32kb + 8(r/4) + 4hl + r%4.  A key is
-        // hidden when it lies past min(qi + dsh, ks1-1) (causal) or past ks1-1.
-        if ((causal && k0 + kBN - 1 > wq0 + dsh) || k0 + kBN > ks1) {
+        // hidden when it lies past min(qi + dsh, ks1-1) (causal) or past ks1-1, or
+        // below the row's window.
+        if ((causal && k0 + kBN - 1 > wq0 + dsh) || k0 + kBN > ks1 ||
+            (win > 0 && k0 < wave_lo)) {
             const int lim = (causal ? min(qi + dsh, ks1 - 1) : ks1 - 1) - (k0 + 4 * hl);
+            // (window: keys below the row's first visible one, qi + dsh - win + 1)
+            const int lo = win > 0 ? qi + dsh - win + 1 - (k0 + 4 * hl) : -kBN;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int idx = 32 * kb + 8 * (r >> 2) + (r & 3);
+                    if (idx > lim || idx < lo) sacc[kb][r] = -INFINITY;
+                }
         }
         // Weights against the running max straight away; the lane's score max is
         // checked beside them.  Only when some score lies more than kLazyMax above

@@ -126,11 +126,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const int nt_seq = (ks1 - ks0 + kBN - 1) / kBN;
     const int n_tiles =
         geom.causal ? (min(q0 + rows_per_item, s1) - 1 + dsh - ks0) / kBN + 1 : nt_seq;
+    // with a sliding window the item starts at its first row's first visible key
+    const int win = geom.causal ? geom.window : 0;
+    const int t_first = win > 0 ? max(0, q0 + dsh - win + 1 - ks0) / kBN : 0;
     // key split: this workgroup takes tiles [t_begin, t_end) of the item
-    const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles;
-    const int n_chunks = (n_tiles + kchunk - 1) / kchunk;
+    const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles - t_first;
+    const int n_chunks = (n_tiles - t_first + kchunk - 1) / kchunk;
     if (wi.kc >= n_chunks) return;  // (uniform: the whole workgroup leaves)
-    const int t_begin = wi.kc * kchunk, t_end = min(t_begin + kchunk, n_tiles);
+    const int t_begin = t_first + wi.kc * kchunk, t_end = min(t_begin + kchunk, n_tiles);
     const bool split = n_chunks > 1;
 
     // ---- wavefront role
@@ -141,6 +144,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     // tiles holding a key some row of this wavefront may see
     const int wave_tiles =
         geom.causal ? min((min(wq0 + 31, s1 - 1) + dsh - ks0) / kBN + 1, nt_seq) : nt_seq;
+    const int wave_first = win > 0 ? max(0, wq0 + dsh - win + 1 - ks0) / kBN : 0;
+    // (with a window: the lowest key the wavefront's last row sees; below it, masks)
+    const int wave_lo = wq0 + 31 + dsh - win + 1;
     const int qi = wq0 + ln;
 
     // Fused entry, per lane: Q norm weights and rotary frequency (turns per position)
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
         const bool more = t + 1 < t_end;
         float* kn = smem + (cur ^ 1) * BUF;
         if (more) load_rows(k_in, t + 1);
-        if (active && t < wave_tiles) {
+        if (active && t < wave_tiles && t >= wave_first) {
             const float* ks = smem + cur * BUF;
             const float* vs = ks + kBN * KS;
             // S^T[key][query] = sum_d K[key][d] Q[query][d]; step s contracts
@@ -318,13 +324,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             for (int r = 0; r < 16; ++r) sacc[r] += sacc1[r];
             // Register r of lane (hl, ln) holds key k0 + 8(r/4) + 4hl + r%4 for query qi.
             const int k0 = ks0 + t * kBN;
-            // tiles reaching past the first row's last visible key, or past the
-            // sequence's keys, are masked
-            if ((geom.causal && k0 + kBN - 1 > wq0 + dsh) || k0 + kBN > ks1) {
+            // tiles reaching past the first row's last visible key, past the
+            // sequence's keys, or (window) below the last row's first one, are masked
+            if ((geom.causal && k0 + kBN - 1 > wq0 + dsh) || k0 + kBN > ks1 ||
+                (win > 0 && k0 < wave_lo)) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if ((geom.causal && key > qi + dsh) || key >= ks1) sacc[r] = -INFINITY;
+                    if ((geom.causal && key > qi + dsh) || key >= ks1 ||
+                        (win > 0 && key < qi + dsh - win + 1))
+                        sacc[r] = -INFINITY;
                 }
             }
             float mt = sacc[0];

@@ -120,6 +120,7 @@ void choose_geometry(int H, int Hkv, float scale, int causal, int waves, pfa::At
     geom.chunks = g / hpw;
     geom.qscale = scale * 1.4426950408889634f;
     geom.causal = causal ? 1 : 0;
+    geom.window = 0;
 }
 
 // Longest-first schedule of (sequence, super-block) items.
@@ -343,9 +344,9 @@ static int check_attn(float scale, int precision) {
 
 static int attn_common(Mode mode, const float* q, const float* k, const float* v, float* out,
                        float* k_cache, float* v_cache, const pfa::SeqTable& st, int n_head,
-                       int n_head_kv, int head_dim, float scale, int causal, int precision,
-                       const pfa::PrepParams* prep, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       int n_head_kv, int head_dim, float scale, int causal, int window,
+                       int precision, const pfa::PrepParams* prep, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     const int T_q = st.off[st.n_seqs], T_kv = st.koff[st.n_seqs];
     if (T_q == 0) return PFA_OK;
     const bool chunk_fused = mode == Mode::kChunkFused;
@@ -376,6 +377,7 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
     int rc;
     if ((rc = make_plan(st, n_head, n_head_kv, head_dim, scale, causal, precision, p))) return rc;
     if (p.items == 0) return PFA_OK;
+    p.geom.window = window;
     const bool bf16 = precision != PFA_PREC_F32;
     // workspace parts: [bf16 K/V tiles + rotary table (Q prepared here), or f32 rotated K
     // (fused prefill without k_rot_out)][partials, key split]
@@ -467,7 +469,7 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
     pfa::SeqTable st;
     if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
     return attn_common(Mode::kPlain, q, k, v, out, nullptr, nullptr, st, n_head, n_head_kv,
-                       head_dim, scale, causal, precision, nullptr, workspace, workspace_bytes,
+                       head_dim, scale, causal, 0, precision, nullptr, workspace, workspace_bytes,
                        stream);
 }
 
@@ -487,23 +489,31 @@ int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
     pfa::PrepParams prep{q_norm_w, k_norm_w, k_rot_out, rope_dim, rms_eps,
                          (double)rope_freq_base};
     return attn_common(Mode::kFused, q, k, v, out, nullptr, nullptr, st, n_head, n_head_kv,
-                       head_dim, scale, causal, precision, &prep, workspace, workspace_bytes,
+                       head_dim, scale, causal, 0, precision, &prep, workspace, workspace_bytes,
                        stream);
+}
+
+static int check_window(int window, int causal) {
+    if (window < 0) return fail(PFA_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
+    if (window > 0 && !causal)
+        return fail(PFA_ERR_INVALID_ARG, "a sliding window needs causal attention");
+    return PFA_OK;
 }
 
 int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, float* out,
                    const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs, int T_q,
                    int T_kv, int n_head, int n_head_kv, int head_dim, float scale, int causal,
-                   int precision, void* workspace, size_t workspace_bytes, void* stream) {
+                   int window, int precision, void* workspace, size_t workspace_bytes,
+                   void* stream) {
     g_err[0] = 0;
     int rc = check_geometry(T_q, n_head, n_head_kv, head_dim);
     if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
-    if ((rc = check_attn(scale, precision))) return rc;
+    if ((rc = check_attn(scale, precision)) || (rc = check_window(window, causal))) return rc;
     pfa::SeqTable st;
     if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) return rc;
     if (T_q == 0) return PFA_OK;
     return attn_common(Mode::kChunk, q, k_cache, v_cache, out, nullptr, nullptr, st, n_head,
-                       n_head_kv, head_dim, scale, causal, precision, nullptr, workspace,
+                       n_head_kv, head_dim, scale, causal, window, precision, nullptr, workspace,
                        workspace_bytes, stream);
 }
 
@@ -512,12 +522,12 @@ int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* ou
                        float* v_cache, const int32_t* q_offsets, const int32_t* kv_offsets,
                        int n_seqs, int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
                        int rope_dim, float rope_freq_base, float rms_eps, float scale,
-                       int causal, int precision, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       int causal, int window, int precision, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     int rc = check_geometry(T_q, n_head, n_head_kv, head_dim);
     if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
-    if ((rc = check_attn(scale, precision))) return rc;
+    if ((rc = check_attn(scale, precision)) || (rc = check_window(window, causal))) return rc;
     if ((rc = check_rope(head_dim, rope_dim, rope_freq_base, rms_eps))) return rc;
     pfa::SeqTable st;
     if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) return rc;
@@ -525,8 +535,8 @@ int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* ou
     if (!q_norm_w || !k_norm_w) return fail(PFA_ERR_INVALID_ARG, "null norm weights");
     pfa::PrepParams prep{q_norm_w, k_norm_w, nullptr, rope_dim, rms_eps, (double)rope_freq_base};
     return attn_common(Mode::kChunkFused, q, k, v, out, k_cache, v_cache, st, n_head, n_head_kv,
-                       head_dim, scale, causal, precision, &prep, workspace, workspace_bytes,
-                       stream);
+                       head_dim, scale, causal, window, precision, &prep, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

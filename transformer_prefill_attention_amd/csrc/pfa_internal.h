@@ -75,6 +75,7 @@ struct AttnGeom {
     int chunks;             // workgroups per K/V head per item (g / hpw)
     float qscale;           // softmax scale * log2(e), folded into Q
     int causal;
+    int window;             // causal only: keys a row sees, its own included (0: all)
 };
 
 // Rotary + norm parameters for the fused entry.

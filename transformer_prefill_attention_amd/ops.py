@@ -64,10 +64,10 @@ def lib() -> ctypes.CDLL:
     L.pfa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_workspace_bytes.restype = sz
     L.gqa_chunk_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
-                                 i32, vp, sz, vp]
+                                 i32, i32, vp, sz, vp]
     L.gqa_chunk_attn.restype = i32
     L.qk_prep_chunk_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
-                                     i32, i32, i32, f32, f32, f32, i32, i32, vp, sz, vp]
+                                     i32, i32, i32, f32, f32, f32, i32, i32, i32, vp, sz, vp]
     L.qk_prep_chunk_attn.restype = i32
     L.pfa_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_chunk_workspace_bytes.restype = sz
@@ -289,12 +289,13 @@ def _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, pre
 
 
 def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float] = None,
-                   causal: bool = True, precision="f32", q_offsets=None, kv_offsets=None,
-                   out=None, workspace=None):
+                   causal: bool = True, window: int = 0, precision="f32", q_offsets=None,
+                   kv_offsets=None, out=None, workspace=None):
     """Attention of new query rows over a K/V cache (``gqa_chunk_attn`` in
     ``include/pfa.h``); returns ``out``.  Sequence s owns query rows
     ``q_offsets[s]..q_offsets[s+1]`` and cache rows ``kv_offsets[s]..kv_offsets[s+1]``,
-    its new rows being the last ones of its cache range."""
+    its new rows being the last ones of its cache range.  ``window > 0``: each row sees
+    only the last ``window`` keys up to its own."""
     import torch
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev_f32(t, n)
@@ -313,14 +314,15 @@ def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float]
                                   False, q.device)
     _check(lib().gqa_chunk_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), qp, kp,
                                 n_seqs, T_q, T_kv, H, Hkv, head_dim, float(scale),
-                                1 if causal else 0, prec, wp, wn, _stream(q)))
+                                1 if causal else 0, int(window), prec, wp, wn, _stream(q)))
     return out
 
 
 def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_dim: int,
                        rope_dim: int, rope_freq_base: float, rms_eps: float,
-                       scale: Optional[float] = None, causal: bool = True, precision="f32",
-                       q_offsets=None, kv_offsets=None, out=None, workspace=None):
+                       scale: Optional[float] = None, causal: bool = True, window: int = 0,
+                       precision="f32", q_offsets=None, kv_offsets=None, out=None,
+                       workspace=None):
     """Fused QK-norm + RoPE of the raw new rows at their positions, their K and V written
     into ``k_cache`` / ``v_cache`` (the last rows of each sequence's cache range), then
     attention over the cache (``qk_prep_chunk_attn`` in ``include/pfa.h``); returns
@@ -348,6 +350,6 @@ def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_di
     _check(lib().qk_prep_chunk_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(q_norm_w),
                                     _ptr(k_norm_w), _ptr(k_cache), _ptr(v_cache), qp, kp, n_seqs,
                                     T_q, T_kv, H, Hkv, head_dim, rope_dim, float(rope_freq_base),
-                                    float(rms_eps), float(scale), 1 if causal else 0, prec, wp,
-                                    wn, _stream(q)))
+                                    float(rms_eps), float(scale), 1 if causal else 0,
+                                    int(window), prec, wp, wn, _stream(q)))
     return out
