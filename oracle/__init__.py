@@ -65,8 +65,8 @@ def _load():
     lib.oracle_qknorm_rope_from.restype = ctypes.c_int
     lib.oracle_chunk_attn.argtypes = [dp, dp, dp, ip, ip, ctypes.c_int, ctypes.c_int64,
                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_double, ctypes.c_int, ctypes.c_int64, lp,
-                                      ctypes.c_int64, dp, ctypes.c_int]
+                                      ctypes.c_double, ctypes.c_int, ctypes.c_int64, dp,
+                                      ctypes.c_int, lp, ctypes.c_int64, dp, ctypes.c_int]
     lib.oracle_chunk_attn.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_char_p
     _lib = lib
@@ -163,14 +163,16 @@ def qk_prep_attn(q, k, v, wq, wk, *, n_head, n_head_kv, head_dim, rope_dim, rope
 
 
 def chunk_attn(q, k_cache, v_cache, *, n_head, n_head_kv, head_dim, scale, causal=True,
-               q_offsets=None, kv_offsets=None, window=0, rows=None, n_threads=0):
+               q_offsets=None, kv_offsets=None, window=0, gate=None, rows=None, n_threads=0):
     """Attention of the query rows ``q [T_q, n_head*head_dim]`` over a K/V cache
     ``k_cache``/``v_cache [T_kv, n_head_kv*head_dim]``: sequence s owns query rows
     ``q_offsets[s]..q_offsets[s+1]`` and cache rows ``kv_offsets[s]..kv_offsets[s+1]``
     (at least as many); its queries are the last rows of its cache, so query row r sits
     at position ``base_s + r`` with ``base_s`` the rows cached before.  Causal: row r
     sees cache rows 0 .. base_s + r of its sequence, and with ``window > 0`` only the last
-    ``window`` of those.  Offsets: both or neither."""
+    ``window`` of those.  ``gate`` (``[T_q, n_head*head_dim]`` or ``[T_q, n_head]``): the
+    output is multiplied by its logistic sigmoid, per element or per head.  Offsets: both
+    or neither."""
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k_cache, dtype=np.float64)
     v = np.ascontiguousarray(v_cache, dtype=np.float64)
@@ -182,6 +184,14 @@ def chunk_attn(q, k_cache, v_cache, *, n_head, n_head_kv, head_dim, scale, causa
         raise ValueError("give both offset arrays or neither")
     qo = _offsets(q_offsets, T_q)
     ko = _offsets(kv_offsets, T_kv)
+    gp, per_head = None, 0
+    if gate is not None:
+        g = np.ascontiguousarray(gate, dtype=np.float64)
+        if g.size == T_q * n_head:
+            per_head = 1
+        elif g.size != T_q * n_head * head_dim:
+            raise ValueError("gate must be [T_q, n_head*head_dim] or [T_q, n_head]")
+        gp = _ptr(g, ctypes.c_double)
     if rows is None:
         n_rows, rp = T_q, None
     else:
@@ -192,8 +202,8 @@ def chunk_attn(q, k_cache, v_cache, *, n_head, n_head_kv, head_dim, scale, causa
                                    _ptr(v, ctypes.c_double), _ptr(qo, ctypes.c_int32),
                                    _ptr(ko, ctypes.c_int32), len(qo) - 1, T_q, T_kv, n_head,
                                    n_head_kv, head_dim, float(scale), 1 if causal else 0,
-                                   int(window), rp, n_rows, _ptr(out, ctypes.c_double),
-                                   n_threads)
+                                   int(window), gp, per_head, rp, n_rows,
+                                   _ptr(out, ctypes.c_double), n_threads)
     if rc != 0:
         raise ValueError(f"oracle_chunk_attn failed ({rc})")
     return out
@@ -201,7 +211,7 @@ def chunk_attn(q, k_cache, v_cache, *, n_head, n_head_kv, head_dim, scale, causa
 
 def qk_prep_chunk_attn(q, k, v, wq, wk, k_cache, v_cache, *, n_head, n_head_kv, head_dim,
                        rope_dim, rope_freq_base, rms_eps, scale, causal=True, q_offsets=None,
-                       kv_offsets=None, window=0, rows=None, n_threads=0):
+                       kv_offsets=None, window=0, gate=None, rows=None, n_threads=0):
     """A block of new rows over a cache: the raw f32 ``q``, ``k``, ``v [T_q, ...]`` are
     normalised and rotated (Q and K) at the positions of the new rows, K and V are
     written into the last rows of each sequence's cache range, and the queries attend
@@ -229,7 +239,7 @@ def qk_prep_chunk_attn(q, k, v, wq, wk, k_cache, v_cache, *, n_head, n_head_kv, 
         vc[dst] = v[qo[s]:qo[s + 1]]
     out = chunk_attn(qn, kc, vc, n_head=n_head, n_head_kv=n_head_kv, head_dim=head_dim,
                      scale=scale, causal=causal, q_offsets=qo, kv_offsets=ko, window=window,
-                     rows=rows, n_threads=n_threads)
+                     gate=gate, rows=rows, n_threads=n_threads)
     return out, kc, vc
 
 

@@ -40,6 +40,11 @@
  *    only the last `window` of them, itself included (needle-core v3/model.rs
  *    passes a per-layer attention span to its attention for the same purpose):
  *    row i sees key j when i - window < j <= i.
+ *  - needle-core v3/model.rs, gated attention output: every element of the
+ *    attention output is multiplied by the logistic sigmoid of the matching
+ *    element of a gate tensor before the output projection; memra-engine
+ *    0.101.0 src/spec.rs does the same with the gate split off the Q
+ *    projection, and its step35 layers with one gate value per head.
  *
  * Readings taken where the pages are silent (each one is listed with its
  * reason in the design notes of the repository):
@@ -256,6 +261,8 @@ typedef struct {
     const int32_t* kv_offsets; /* key rows of each sequence (the same for plain prefill) */
     int n_seqs, H, Hkv, d, causal;
     int64_t window;            /* causal only: keys visible per row, the row's own included; 0: all */
+    const double* gate;        /* NULL, or [T_q, H*d] (per element) / [T_q, H] (per head) */
+    int gate_per_head;
     double scale;
 } attn_ctx;
 
@@ -302,6 +309,13 @@ static void attn_unit(void* vctx, int64_t unit, double* e) {
         for (int x = 0; x < d; ++x) o[x] += wgt * vj[x];
     }
     for (int x = 0; x < d; ++x) o[x] /= Z;
+    /* gated output: o * sigmoid(gate) */
+    if (c->gate) {
+        for (int x = 0; x < d; ++x) {
+            double g = c->gate_per_head ? c->gate[i * c->H + h] : c->gate[(i * c->H + h) * (int64_t)d + x];
+            o[x] *= 1.0 / (1.0 + exp(-g));
+        }
+    }
 }
 
 /* Attention of query rows over a K/V cache.  Sequence s owns query rows
@@ -311,13 +325,16 @@ static void attn_unit(void* vctx, int64_t unit, double* e) {
  * softmax_j(scale * q[i,h,:] . k[j,kv,:]) v[j,kv,:] over the visible keys j of
  * row i = rows[r] (or r when rows is NULL): the keys of i's sequence, and when
  * causal only those up to i's own position (base_s + i - q_offsets[s]) and, with
- * window > 0, not more than window of them (the latest).  All arithmetic in f64.
- * NULL offsets (both): one sequence. */
+ * window > 0, not more than window of them (the latest); with a gate, the row's
+ * output is then multiplied by sigmoid(gate) per element (gate [T_q, H*d]) or per
+ * head (gate [T_q, H]).  All arithmetic in f64.  NULL offsets (both): one
+ * sequence. */
 int oracle_chunk_attn(const double* q, const double* k, const double* v,
                       const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
                       int64_t T_q, int64_t T_kv, int n_head, int n_head_kv, int head_dim,
-                      double scale, int causal, int64_t window, const int64_t* rows,
-                      int64_t n_rows, double* out, int n_threads) {
+                      double scale, int causal, int64_t window, const double* gate,
+                      int gate_per_head, const int64_t* rows, int64_t n_rows, double* out,
+                      int n_threads) {
     int32_t one_q[2], one_kv[2];
     if (T_q < 0 || T_kv < 0 || n_head <= 0 || n_head_kv <= 0 || head_dim <= 0 ||
         n_head % n_head_kv || (!q_offsets) != (!kv_offsets) || window < 0 ||
@@ -342,7 +359,7 @@ int oracle_chunk_attn(const double* q, const double* k, const double* v,
     for (int64_t r = 0; rows && r < n_rows; ++r)
         if (rows[r] < 0 || rows[r] >= T_q) return ORACLE_BAD_ARG;
     attn_ctx c = {q, k, v, out, rows, q_offsets, kv_offsets, n_seqs, n_head, n_head_kv,
-                  head_dim, causal ? 1 : 0, window, scale};
+                  head_dim, causal ? 1 : 0, window, gate, gate_per_head ? 1 : 0, scale};
     return run_pool(attn_unit, &c, n_rows * n_head, (size_t)T_kv, n_threads); /* scores: <= T_kv */
 }
 
@@ -355,8 +372,8 @@ int oracle_gqa_attn(const double* q, const double* k, const double* v,
                     int n_head_kv, int head_dim, double scale, int causal,
                     const int64_t* rows, int64_t n_rows, double* out, int n_threads) {
     return oracle_chunk_attn(q, k, v, seq_offsets, seq_offsets, n_seqs, T, T, n_head,
-                             n_head_kv, head_dim, scale, causal, 0, rows, n_rows, out,
-                             n_threads);
+                             n_head_kv, head_dim, scale, causal, 0, NULL, 0, rows, n_rows,
+                             out, n_threads);
 }
 
 const char* oracle_version(void) { return "pfa-oracle 1 (f64, plain loops)"; }

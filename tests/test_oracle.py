@@ -626,3 +626,49 @@ def test_window_rejected_without_causal():
     with pytest.raises(ValueError):
         oracle.chunk_attn(np.zeros((2, 8)), np.zeros((2, 8)), np.zeros((2, 8)), n_head=1,
                           n_head_kv=1, head_dim=8, scale=1.0, causal=False, window=4)
+
+
+# ---------------------------------------------------------------------------
+# Gated attention output (needle-core v3/model.rs: each output element times the sigmoid
+# of its gate element; memra-engine 0.101.0 src/spec.rs: the same with the gate split off
+# Q, and one gate value per head in its step35 layers).
+
+def _gate_case(seed):
+    H, Hkv, d = 4, 2, 8
+    r = _rng(seed)
+    q = r.standard_normal((6, H * d))
+    kc = r.standard_normal((9, Hkv * d))
+    vc = r.standard_normal((9, Hkv * d))
+    kw = dict(n_head=H, n_head_kv=Hkv, head_dim=d, scale=0.3)
+    return q, kc, vc, kw, r
+
+
+def test_gate_of_zero_halves_the_output_exactly():
+    q, kc, vc, kw, _ = _gate_case(31)
+    plain = oracle.chunk_attn(q, kc, vc, **kw)
+    np.testing.assert_array_equal(oracle.chunk_attn(q, kc, vc, gate=np.zeros((6, 32)), **kw),
+                                  plain / 2)
+    np.testing.assert_array_equal(oracle.chunk_attn(q, kc, vc, gate=np.zeros((6, 4)), **kw),
+                                  plain / 2)
+
+
+def test_gate_saturates_to_pass_and_block():
+    q, kc, vc, kw, _ = _gate_case(32)
+    plain = oracle.chunk_attn(q, kc, vc, **kw)
+    np.testing.assert_array_equal(oracle.chunk_attn(q, kc, vc, gate=np.full((6, 32), 800.0),
+                                                    **kw), plain)
+    np.testing.assert_array_equal(oracle.chunk_attn(q, kc, vc, gate=np.full((6, 4), -800.0),
+                                                    **kw), 0 * plain)
+
+
+def test_gate_matches_torch_sigmoid_and_heads_broadcast():
+    q, kc, vc, kw, r = _gate_case(33)
+    plain = oracle.chunk_attn(q, kc, vc, **kw)
+    g = 3 * r.standard_normal((6, 32))
+    got = oracle.chunk_attn(q, kc, vc, gate=g, **kw)
+    np.testing.assert_allclose(got, plain * torch.sigmoid(torch.from_numpy(g)).numpy(),
+                               rtol=1e-14, atol=1e-15)
+    gh = 3 * r.standard_normal((6, 4))   # one value per head equals that value on every dim
+    np.testing.assert_array_equal(oracle.chunk_attn(q, kc, vc, gate=gh, **kw),
+                                  oracle.chunk_attn(q, kc, vc, gate=np.repeat(gh, 8, axis=1),
+                                                    **kw))

@@ -35,6 +35,8 @@ MUTANTS = [
     ("start positions ignored", "if (c->pos0) pos += c->pos0[s];", "(void)c->pos0;"),
     ("window one key wider", "last - c->window + 1 > lo) lo = last - c->window + 1;",
      "last - c->window > lo) lo = last - c->window;"),
+    ("gate sign flipped", "o[x] *= 1.0 / (1.0 + exp(-g));", "o[x] *= 1.0 / (1.0 + exp(g));"),
+    ("gate head index off", "c->gate[i * c->H + h]", "c->gate[i * c->H + (h + 1) % c->H]"),
 ]
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins)
