@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="with the chunk entry points (any --chunk-base, 0 included): a sliding "
                          "window of W keys per row, its own included")
+    ap.add_argument("--gate", default="none", choices=["none", "elem", "head"],
+                    help="with the chunk entry points: a gated output, out = O * sigmoid(gate), "
+                         "the gate per element or per head (seeded N(0,1))")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -149,7 +152,7 @@ def main():
 
     w = wl.sweep_workload(args.seq_len) if args.seq_len else wl.CONFIGS[args.workload]
     x = wl.make_inputs(w)
-    if args.chunk_base or args.window:
+    if args.chunk_base or args.window or args.gate != "none":
         run_chunk(args, w, x)
         return
     k_in = wl.with_outlier_keys(x.k, x.outliers)
@@ -266,6 +269,11 @@ def run_chunk(args, w, x):
     q_new, k_new, v_new = t["q"][B:].contiguous(), t["k"][B:].contiguous(), t["v"][B:].contiguous()
     q_prep = qn[B:].contiguous()
     out = torch.empty_like(q_new)
+    gate = None
+    if args.gate != "none":
+        g = torch.Generator().manual_seed(w.seed + 1)
+        cols = w.n_head * (w.head_dim if args.gate == "elem" else 1)
+        gate = torch.randn(T_q, cols, generator=g).to(dev)
     stream = torch.cuda.current_stream(dev)
     ev = []
 
@@ -275,11 +283,11 @@ def run_chunk(args, w, x):
             a.record(stream)
         if args.path == "fused":
             pfa.qk_prep_chunk_attn(q_new, k_new, v_new, t["wq"], t["wk"], k_cache, v_cache,
-                                   scale=w.softmax_scale, window=args.window,
+                                   scale=w.softmax_scale, window=args.window, gate=gate,
                                    precision=args.precision, out=out, **kw_rope)
         else:
             pfa.gqa_chunk_attn(q_prep, k_cache, v_cache, head_dim=w.head_dim,
-                               scale=w.softmax_scale, window=args.window,
+                               scale=w.softmax_scale, window=args.window, gate=gate,
                                precision=args.precision, out=out)
         if record:
             b.record(stream)
@@ -329,7 +337,8 @@ def run_chunk(args, w, x):
         "config": {"workload": f"{w.name} chunk: {T_q} new rows over {B} cached rows, "
                                f"n_head={w.n_head}, n_head_kv={w.n_head_kv}, head_dim={d}, "
                                f"rope_dim={w.rope_dim}"
-                               + (f", window={args.window}" if args.window else ""),
+                               + (f", window={args.window}" if args.window else "")
+                               + (f", gate per {args.gate}" if gate is not None else ""),
                    "T_q": T_q, "T_kv": T, "n_head": w.n_head, "n_head_kv": w.n_head_kv,
                    "head_dim": d, "path": args.path, "causal_flops": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,

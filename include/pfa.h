@@ -196,6 +196,12 @@ int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
  *           place) and the ones before them, base_s, its earlier rows.
  *  out      [T_q, n_head*head_dim]   f32, device, written; must not overlap the
  *           other tensors.
+ *  gate     NULL, or f32, device, read: a gated output, out = O * sigmoid(gate)
+ *           (needle-core v3/model.rs: every output element times the sigmoid of its
+ *           gate element; memra-engine 0.101.0 src/spec.rs: the gate split off the
+ *           Q projection, or one value per head in its step35 layers), the gate
+ *           [T_q, n_head*head_dim] (gate_per_head = 0) or [T_q, n_head] (1), not
+ *           overlapping out.
  *  q_offsets, kv_offsets  host arrays of n_seqs+1 cumulative offsets, as
  *           seq_offsets above, both NULL (one sequence) or both given; every
  *           sequence needs at least as many cache rows as new rows.
@@ -211,6 +217,7 @@ int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
  *  pfa_chunk_workspace_bytes(..., 0).
  */
 int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, float* out,
+                   const float* gate, int gate_per_head,
                    const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
                    int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
                    float scale, int causal, int window, int precision,
@@ -232,11 +239,12 @@ int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, f
  *        the new rows' rotated K and V.  They must not overlap each other or the
  *        other tensors.
  *  out  [T_q, n_head*head_dim] f32, device, written.
- *  window  as for gqa_chunk_attn.
+ *  gate, gate_per_head, window  as for gqa_chunk_attn.
  *  workspace  as for gqa_prefill_attn, sized by pfa_chunk_workspace_bytes(...,
  *        1); PFA_PREC_F32 needs none unless the key split is wanted.
  */
 int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* out,
+                       const float* gate, int gate_per_head,
                        const float* q_norm_w, const float* k_norm_w,
                        float* k_cache, float* v_cache,
                        const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,

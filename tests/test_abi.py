@@ -260,13 +260,14 @@ def _i32(a):
 
 
 def _chunk(L, q_offs, kv_offs, T_q, T_kv, H=4, Hkv=2, D=64, prec=0, ptrs=(8, 8, 8, 8 << 20),
-           ws=0, ws_bytes=0, causal=1, window=0):
+           ws=0, ws_bytes=0, causal=1, window=0, gate=0, gate_per_head=0):
     keep_q, qp = _i32(q_offs) if q_offs is not None else (None, None)
     keep_k, kp = _i32(kv_offs) if kv_offs is not None else (None, None)
     n = len(q_offs) - 1 if q_offs is not None else 0
     q, k, v, o = (ctypes.c_void_p(p) for p in ptrs)
-    return L.gqa_chunk_attn(q, k, v, o, qp, kp, n, T_q, T_kv, H, Hkv, D, 0.125, causal, window,
-                            prec, ctypes.c_void_p(ws), ws_bytes, None)
+    return L.gqa_chunk_attn(q, k, v, o, ctypes.c_void_p(gate), gate_per_head, qp, kp, n, T_q,
+                            T_kv, H, Hkv, D, 0.125, causal, window, prec, ctypes.c_void_p(ws),
+                            ws_bytes, None)
 
 
 def test_chunk_with_no_new_rows_is_ok_without_pointers(L):
@@ -333,3 +334,9 @@ def test_chunk_window_arguments(L):
     assert "window" in _msg(L)
     assert _chunk(L, [0, 4], [0, 9], 4, 9, window=3, causal=0) == INVALID
     assert "causal" in _msg(L)
+
+
+def test_chunk_gate_must_not_overlap_out(L):
+    # out is [4, 4*64] f32 at 8 MiB; a gate inside it is refused before any launch
+    assert _chunk(L, [0, 4], [0, 9], 4, 9, gate=(8 << 20) + 256) == INVALID
+    assert "gate" in _msg(L)

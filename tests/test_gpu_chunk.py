@@ -10,7 +10,8 @@ different prefixes, head_dim 64, a prefix long enough for the key split), and on
 sampled rows at the benchmark's chunk shape (8192 cache rows, 1024 new).  The sliding
 window (each row sees only the last ``window`` keys up to its own) is checked on the
 same cases: windows on and off tile edges, of one key, across packed sequences, with
-the key split, and a windowed prefill of 8192 rows on sampled rows."""
+the key split, and a windowed prefill of 8192 rows on sampled rows; the gated output
+(``out = O * sigmoid(gate)``, per element or per head) with and without the key split."""
 import numpy as np
 import pytest
 import torch
@@ -72,44 +73,48 @@ def _t(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def _chunk_gpu(c, precision, causal=True, window=0):
-    print(c.label("gqa_chunk_attn", precision, causal) + f" window={window}", flush=True)
+def _chunk_gpu(c, precision, causal=True, window=0, gate=None):
+    print(c.label("gqa_chunk_attn", precision, causal) + f" window={window}"
+          + ("" if gate is None else f" gate{list(gate.shape)}"), flush=True)
     dev = torch.device("cuda:0")
     out = pfa.gqa_chunk_attn(_t(c.q_prep, dev), _t(c.k_cache, dev), _t(c.v_cache, dev),
                              head_dim=c.d, scale=c.w.softmax_scale, causal=causal,
                              window=window, precision=precision, q_offsets=c.q_offs,
-                             kv_offsets=c.kv_offs)
+                             kv_offsets=c.kv_offs,
+                             gate=None if gate is None else _t(gate, dev))
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-def _chunk_ref(c, causal=True, rows=None, window=0):
+def _chunk_ref(c, causal=True, rows=None, window=0, gate=None):
     return oracle.chunk_attn(c.q_prep, c.k_cache, c.v_cache, n_head=c.H, n_head_kv=c.Hkv,
                              head_dim=c.d, scale=c.w.softmax_scale, causal=causal,
                              q_offsets=c.q_offs, kv_offsets=c.kv_offs, window=window,
-                             rows=rows)
+                             gate=gate, rows=rows)
 
 
-def _fused_gpu(c, precision, causal=True, window=0):
-    print(c.label("qk_prep_chunk_attn", precision, causal) + f" window={window}", flush=True)
+def _fused_gpu(c, precision, causal=True, window=0, gate=None):
+    print(c.label("qk_prep_chunk_attn", precision, causal) + f" window={window}"
+          + ("" if gate is None else f" gate{list(gate.shape)}"), flush=True)
     dev = torch.device("cuda:0")
     kc, vc = _t(c.k_prefix, dev), _t(c.v_prefix, dev)
     out = pfa.qk_prep_chunk_attn(_t(c.x.q[c.new], dev), _t(c.x.k[c.new], dev),
                                  _t(c.x.v[c.new], dev), _t(c.x.wq, dev), _t(c.x.wk, dev), kc, vc,
                                  head_dim=c.d, rope_dim=c.n, rope_freq_base=1e6, rms_eps=1e-6,
                                  scale=c.w.softmax_scale, causal=causal, window=window,
-                                 precision=precision, q_offsets=c.q_offs, kv_offsets=c.kv_offs)
+                                 precision=precision, q_offsets=c.q_offs, kv_offsets=c.kv_offs,
+                                 gate=None if gate is None else _t(gate, dev))
     torch.cuda.synchronize()
     return out.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy()
 
 
-def _fused_ref(c, causal=True, rows=None, window=0):
+def _fused_ref(c, causal=True, rows=None, window=0, gate=None):
     return oracle.qk_prep_chunk_attn(c.x.q[c.new], c.x.k[c.new], c.x.v[c.new], c.x.wq, c.x.wk,
                                      c.k_prefix, c.v_prefix, n_head=c.H, n_head_kv=c.Hkv,
                                      head_dim=c.d, rope_dim=c.n, rope_freq_base=c.base_f,
                                      rms_eps=c.eps, scale=c.w.softmax_scale, causal=causal,
                                      q_offsets=c.q_offs, kv_offsets=c.kv_offs, window=window,
-                                     rows=rows)
+                                     gate=gate, rows=rows)
 
 
 @pytest.fixture(scope="module", params=list(CASES))
@@ -223,3 +228,32 @@ def test_windowed_prefill_sampled_rows(precision):
         assert_f32_parity(got[rows], ref, what)
     else:
         assert_bf16_parity(got[rows], ref, what)
+
+
+GATES = [("tile_aligned", False), ("long_prefix", True), ("packed", False), ("no_prefix", True)]
+
+
+@pytest.mark.parametrize("name,per_head", GATES,
+                         ids=[f"{n}-{'head' if h else 'elem'}" for n, h in GATES])
+@pytest.mark.parametrize("precision", ["f32", "bf16"])
+def test_chunk_gated_output(name, per_head, precision):
+    # out = O * sigmoid(gate), per element or per head; long_prefix splits its keys, so
+    # its gate is applied where the combine step stores the rows
+    c = Case(name, *CASES[name])
+    r = np.random.default_rng(900 + len(name))
+    T_q = len(c.new)
+    gate = (2.0 * r.standard_normal((T_q, c.H if per_head else c.H * c.d))).astype(np.float32)
+    got = _chunk_gpu(c, precision, gate=gate)
+    ref = _chunk_ref(c, gate=gate)
+    what = c.label("gqa_chunk_attn", precision) + (" gate/head" if per_head else " gate/elem")
+    if precision == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)
+    got, _, _ = _fused_gpu(c, precision, gate=gate, window=64 if name == "packed" else 0)
+    ref = _fused_ref(c, gate=gate, window=64 if name == "packed" else 0)[0]
+    what = c.label("qk_prep_chunk_attn", precision) + (" gate/head" if per_head else " gate/elem")
+    if precision == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)

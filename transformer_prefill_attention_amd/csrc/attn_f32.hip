@@ -425,8 +425,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             const floatx4 x = *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
             if (split)
                 *reinterpret_cast<floatx4*>(part.o + (slot * 32 + r) * D + 4 * c4) = x;
-            else if (row < s1)
-                *reinterpret_cast<floatx4*>(out + ((int64_t)row * n_q + h) * D + 4 * c4) = x;
+            else if (row < s1) {
+                floatx4 y = x;
+                if (geom.gate) y *= gate_factors(geom.gate, geom.gate_per_head, row, n_q, h,
+                                                 D, 4 * c4);
+                *reinterpret_cast<floatx4*>(out + ((int64_t)row * n_q + h) * D + 4 * c4) = y;
+            }
         }
     }
 }

@@ -108,6 +108,9 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(Partials part,
         floatx4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = acc[i][e] * inv;
+        if (geom.gate)
+            x *= gate_factors(geom.gate, geom.gate_per_head, row, geom.H, h, D,
+                              c0 + 4 * i);
         *reinterpret_cast<floatx4*>(dst + 4 * i) = x;
     }
 }

@@ -121,6 +121,8 @@ void choose_geometry(int H, int Hkv, float scale, int causal, int waves, pfa::At
     geom.qscale = scale * 1.4426950408889634f;
     geom.causal = causal ? 1 : 0;
     geom.window = 0;
+    geom.gate = nullptr;
+    geom.gate_per_head = 0;
 }
 
 // Longest-first schedule of (sequence, super-block) items.
@@ -343,10 +345,11 @@ static int check_attn(float scale, int precision) {
 }
 
 static int attn_common(Mode mode, const float* q, const float* k, const float* v, float* out,
-                       float* k_cache, float* v_cache, const pfa::SeqTable& st, int n_head,
-                       int n_head_kv, int head_dim, float scale, int causal, int window,
-                       int precision, const pfa::PrepParams* prep, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       float* k_cache, float* v_cache, const float* gate, int gate_per_head,
+                       const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
+                       float scale, int causal, int window, int precision,
+                       const pfa::PrepParams* prep, void* workspace, size_t workspace_bytes,
+                       void* stream) {
     const int T_q = st.off[st.n_seqs], T_kv = st.koff[st.n_seqs];
     if (T_q == 0) return PFA_OK;
     const bool chunk_fused = mode == Mode::kChunkFused;
@@ -358,6 +361,9 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
     const size_t cb = (size_t)T_kv * n_head_kv * head_dim * 4;
     if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kb) || overlaps(out, qb, v, kb))
         return fail(PFA_ERR_INVALID_ARG, "out must not overlap q, k or v");
+    const size_t gb = gate ? (size_t)T_q * n_head * (gate_per_head ? 1 : head_dim) * 4 : 0;
+    if (gate && overlaps(gate, gb, out, qb))
+        return fail(PFA_ERR_INVALID_ARG, "gate must not overlap out");
     if (prep && prep->k_rot_out &&
         (overlaps(prep->k_rot_out, kb, q, qb) || overlaps(prep->k_rot_out, kb, k, kb) ||
          overlaps(prep->k_rot_out, kb, v, kb) || overlaps(prep->k_rot_out, kb, out, qb)))
@@ -378,6 +384,8 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
     if ((rc = make_plan(st, n_head, n_head_kv, head_dim, scale, causal, precision, p))) return rc;
     if (p.items == 0) return PFA_OK;
     p.geom.window = window;
+    p.geom.gate = gate;
+    p.geom.gate_per_head = gate_per_head ? 1 : 0;
     const bool bf16 = precision != PFA_PREC_F32;
     // workspace parts: [bf16 K/V tiles + rotary table (Q prepared here), or f32 rotated K
     // (fused prefill without k_rot_out)][partials, key split]
@@ -468,9 +476,9 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
     if (T == 0) return PFA_OK;
     pfa::SeqTable st;
     if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
-    return attn_common(Mode::kPlain, q, k, v, out, nullptr, nullptr, st, n_head, n_head_kv,
-                       head_dim, scale, causal, 0, precision, nullptr, workspace, workspace_bytes,
-                       stream);
+    return attn_common(Mode::kPlain, q, k, v, out, nullptr, nullptr, nullptr, 0, st, n_head,
+                       n_head_kv, head_dim, scale, causal, 0, precision, nullptr, workspace,
+                       workspace_bytes, stream);
 }
 
 int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
@@ -488,9 +496,9 @@ int qk_prep_attn(const float* q, const float* k, const float* v, float* out,
     if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
     pfa::PrepParams prep{q_norm_w, k_norm_w, k_rot_out, rope_dim, rms_eps,
                          (double)rope_freq_base};
-    return attn_common(Mode::kFused, q, k, v, out, nullptr, nullptr, st, n_head, n_head_kv,
-                       head_dim, scale, causal, 0, precision, &prep, workspace, workspace_bytes,
-                       stream);
+    return attn_common(Mode::kFused, q, k, v, out, nullptr, nullptr, nullptr, 0, st, n_head,
+                       n_head_kv, head_dim, scale, causal, 0, precision, &prep, workspace,
+                       workspace_bytes, stream);
 }
 
 static int check_window(int window, int causal) {
@@ -501,10 +509,10 @@ static int check_window(int window, int causal) {
 }
 
 int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, float* out,
-                   const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs, int T_q,
-                   int T_kv, int n_head, int n_head_kv, int head_dim, float scale, int causal,
-                   int window, int precision, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+                   const float* gate, int gate_per_head, const int32_t* q_offsets,
+                   const int32_t* kv_offsets, int n_seqs, int T_q, int T_kv, int n_head,
+                   int n_head_kv, int head_dim, float scale, int causal, int window,
+                   int precision, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     int rc = check_geometry(T_q, n_head, n_head_kv, head_dim);
     if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
@@ -512,14 +520,15 @@ int gqa_chunk_attn(const float* q, const float* k_cache, const float* v_cache, f
     pfa::SeqTable st;
     if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) return rc;
     if (T_q == 0) return PFA_OK;
-    return attn_common(Mode::kChunk, q, k_cache, v_cache, out, nullptr, nullptr, st, n_head,
-                       n_head_kv, head_dim, scale, causal, window, precision, nullptr, workspace,
-                       workspace_bytes, stream);
+    return attn_common(Mode::kChunk, q, k_cache, v_cache, out, nullptr, nullptr, gate,
+                       gate_per_head, st, n_head, n_head_kv, head_dim, scale, causal, window,
+                       precision, nullptr, workspace, workspace_bytes, stream);
 }
 
 int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* out,
-                       const float* q_norm_w, const float* k_norm_w, float* k_cache,
-                       float* v_cache, const int32_t* q_offsets, const int32_t* kv_offsets,
+                       const float* gate, int gate_per_head, const float* q_norm_w,
+                       const float* k_norm_w, float* k_cache, float* v_cache,
+                       const int32_t* q_offsets, const int32_t* kv_offsets,
                        int n_seqs, int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
                        int rope_dim, float rope_freq_base, float rms_eps, float scale,
                        int causal, int window, int precision, void* workspace,
@@ -534,9 +543,9 @@ int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* ou
     if (T_q == 0) return PFA_OK;
     if (!q_norm_w || !k_norm_w) return fail(PFA_ERR_INVALID_ARG, "null norm weights");
     pfa::PrepParams prep{q_norm_w, k_norm_w, nullptr, rope_dim, rms_eps, (double)rope_freq_base};
-    return attn_common(Mode::kChunkFused, q, k, v, out, k_cache, v_cache, st, n_head, n_head_kv,
-                       head_dim, scale, causal, window, precision, &prep, workspace,
-                       workspace_bytes, stream);
+    return attn_common(Mode::kChunkFused, q, k, v, out, k_cache, v_cache, gate, gate_per_head,
+                       st, n_head, n_head_kv, head_dim, scale, causal, window, precision, &prep,
+                       workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -73,6 +73,23 @@ __device__ __forceinline__ void rope_cos_sin(int pos, double turns_per_pos, floa
     sincospif((float)(2.0 * r), &s, &c);
 }
 
+// Factors of a gated output for elements c .. c+3 of head h of output row `row`: the
+// logistic sigmoid of the gate, one value per element (gate [rows, H*D]) or per head
+// (gate [rows, H]).  1 / (1 + 2^(-g log2 e)): saturates to exactly 0 and 1.
+__device__ __forceinline__ floatx4 gate_factors(const float* gate, int per_head, int64_t row,
+                                                int H, int h, int D, int c) {
+    floatx4 g;
+    if (per_head) {
+        const float x = gate[row * H + h];
+        g = floatx4{x, x, x, x};
+    } else {
+        g = *reinterpret_cast<const floatx4*>(gate + (row * H + h) * D + c);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g[e] * kLog2e));
+    return g;
+}
+
 // Index of the packed sequence holding token t: the largest s < n_seqs with
 // off[s] <= t (empty sequences resolve to the next non-empty one).
 __device__ __forceinline__ int find_seq(const int* off, int n_seqs, int t) {

@@ -76,6 +76,10 @@ struct AttnGeom {
     float qscale;           // softmax scale * log2(e), folded into Q
     int causal;
     int window;             // causal only: keys a row sees, its own included (0: all)
+    // gated output: out = O * sigmoid(gate), gate [T_q, H*D] per element or [T_q, H] per
+    // head (gate_per_head); applied where the final output rows are stored
+    const float* gate;      // null: no gate
+    int gate_per_head;
 };
 
 // Rotary + norm parameters for the fused entry.

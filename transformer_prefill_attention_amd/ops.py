@@ -63,11 +63,12 @@ def lib() -> ctypes.CDLL:
     L.qk_prep_attn.restype = i32
     L.pfa_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_workspace_bytes.restype = sz
-    L.gqa_chunk_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
-                                 i32, i32, vp, sz, vp]
+    L.gqa_chunk_attn.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32,
+                                 f32, i32, i32, i32, vp, sz, vp]
     L.gqa_chunk_attn.restype = i32
-    L.qk_prep_chunk_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
-                                     i32, i32, i32, f32, f32, f32, i32, i32, i32, vp, sz, vp]
+    L.qk_prep_chunk_attn.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, i32,
+                                     i32, i32, i32, i32, i32, f32, f32, f32, i32, i32, i32, vp,
+                                     sz, vp]
     L.qk_prep_chunk_attn.restype = i32
     L.pfa_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_chunk_workspace_bytes.restype = sz
@@ -274,6 +275,18 @@ def chunk_workspace_bytes(T_q: int, T_kv: int, n_head: int, n_head_kv: int, head
                                                head_dim, _prec(precision), 1 if fused else 0))
 
 
+def _gate(gate, T_q, H, head_dim):
+    """(pointer, per-head flag) of an optional output gate: [T_q, H*head_dim] or [T_q, H]."""
+    if gate is None:
+        return ctypes.c_void_p(0), 0
+    _dev_f32(gate, "gate")
+    if gate.numel() == T_q * H * head_dim:
+        return _ptr(gate), 0
+    if gate.numel() == T_q * H:
+        return _ptr(gate), 1
+    raise ValueError("gate must be [T_q, n_head*head_dim] or [T_q, n_head]")
+
+
 def _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec, fused,
                      device):
     import torch
@@ -289,13 +302,14 @@ def _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, pre
 
 
 def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float] = None,
-                   causal: bool = True, window: int = 0, precision="f32", q_offsets=None,
-                   kv_offsets=None, out=None, workspace=None):
+                   causal: bool = True, window: int = 0, gate=None, precision="f32",
+                   q_offsets=None, kv_offsets=None, out=None, workspace=None):
     """Attention of new query rows over a K/V cache (``gqa_chunk_attn`` in
     ``include/pfa.h``); returns ``out``.  Sequence s owns query rows
     ``q_offsets[s]..q_offsets[s+1]`` and cache rows ``kv_offsets[s]..kv_offsets[s+1]``,
     its new rows being the last ones of its cache range.  ``window > 0``: each row sees
-    only the last ``window`` keys up to its own."""
+    only the last ``window`` keys up to its own.  ``gate`` ([T_q, n_head*head_dim] or
+    [T_q, n_head]): the output is multiplied by its sigmoid."""
     import torch
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev_f32(t, n)
@@ -312,8 +326,9 @@ def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float]
     prec = _prec(precision)
     ws, wp, wn = _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec,
                                   False, q.device)
-    _check(lib().gqa_chunk_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), qp, kp,
-                                n_seqs, T_q, T_kv, H, Hkv, head_dim, float(scale),
+    gp, gh = _gate(gate, T_q, H, head_dim)
+    _check(lib().gqa_chunk_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), gp, gh, qp,
+                                kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, float(scale),
                                 1 if causal else 0, int(window), prec, wp, wn, _stream(q)))
     return out
 
@@ -321,7 +336,7 @@ def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float]
 def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_dim: int,
                        rope_dim: int, rope_freq_base: float, rms_eps: float,
                        scale: Optional[float] = None, causal: bool = True, window: int = 0,
-                       precision="f32", q_offsets=None, kv_offsets=None, out=None,
+                       gate=None, precision="f32", q_offsets=None, kv_offsets=None, out=None,
                        workspace=None):
     """Fused QK-norm + RoPE of the raw new rows at their positions, their K and V written
     into ``k_cache`` / ``v_cache`` (the last rows of each sequence's cache range), then
@@ -347,8 +362,9 @@ def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_di
     prec = _prec(precision)
     ws, wp, wn = _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec,
                                   True, q.device)
-    _check(lib().qk_prep_chunk_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(q_norm_w),
-                                    _ptr(k_norm_w), _ptr(k_cache), _ptr(v_cache), qp, kp, n_seqs,
+    gp, gh = _gate(gate, T_q, H, head_dim)
+    _check(lib().qk_prep_chunk_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), gp, gh,
+                                    _ptr(q_norm_w), _ptr(k_norm_w), _ptr(k_cache), _ptr(v_cache), qp, kp, n_seqs,
                                     T_q, T_kv, H, Hkv, head_dim, rope_dim, float(rope_freq_base),
                                     float(rms_eps), float(scale), 1 if causal else 0,
                                     int(window), prec, wp, wn, _stream(q)))
