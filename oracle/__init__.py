@@ -15,6 +15,12 @@ rows); this module builds it with the host C compiler and wraps it for numpy.
   (``Model::forward``, SDPA block; memra-engine 0.101.0 ``src/spec.rs``,
   ``full_attn_verify`` per-row fallback for the causal rule).
 * :func:`qk_prep_attn` -- the two composed in f64 with no rounding between.
+* :func:`chunk_attn`, :func:`qk_prep_chunk_attn` -- new rows over a cached prefix
+  (memra-engine 0.101.0 ``src/spec.rs``, ``full_attn_verify``), with a sliding
+  window and a gated output.
+* :func:`quant_rows`, :func:`q8_chunk_attn`, :func:`qk_prep_q8_attn` -- 8-bit
+  per-(token, head) quantisation of Q, K and V and attention through the 8-bit
+  store (needle-core ``v3/model.rs``, ``quant_rows`` / ``quantize_rows``).
 """
 from __future__ import annotations
 
@@ -68,6 +74,9 @@ def _load():
                                       ctypes.c_double, ctypes.c_int, ctypes.c_int64, dp,
                                       ctypes.c_int, lp, ctypes.c_int64, dp, ctypes.c_int]
     lib.oracle_chunk_attn.restype = ctypes.c_int
+    lib.oracle_quant_rows.argtypes = [fp, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_int8), fp, fp]
+    lib.oracle_quant_rows.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -241,6 +250,91 @@ def qk_prep_chunk_attn(q, k, v, wq, wk, k_cache, v_cache, *, n_head, n_head_kv, 
                      scale=scale, causal=causal, q_offsets=qo, kv_offsets=ko, window=window,
                      gate=gate, rows=rows, n_threads=n_threads)
     return out, kc, vc
+
+
+def quant_rows(x, row_len):
+    """8-bit quantisation of every ``row_len`` consecutive values of ``x`` (one row per
+    (token, head) when ``row_len`` is the head size).  Returns ``(codes int8, scales f32,
+    fake-quantised f32)`` shaped like ``x``, ``x.size / row_len`` and ``x``.  The input is
+    taken as f32 (the integer decisions are made in single precision)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.size % row_len:
+        raise ValueError("x does not hold whole rows")
+    n = x.size // row_len
+    codes = np.empty(x.shape, dtype=np.int8)
+    scales = np.empty(n, dtype=np.float32)
+    deq = np.empty(x.shape, dtype=np.float32)
+    rc = _load().oracle_quant_rows(_ptr(x, ctypes.c_float), n, int(row_len),
+                                   _ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_float),
+                                   _ptr(deq, ctypes.c_float))
+    if rc != 0:
+        raise ValueError(f"oracle_quant_rows failed ({rc})")
+    return codes, scales, deq
+
+
+def _dequant(codes, scales, row_len):
+    """codes x their row's scale, in f64 (exact: an 8-bit integer times a float)."""
+    c = np.asarray(codes, dtype=np.float64).reshape(-1, row_len)
+    return (c * np.asarray(scales, dtype=np.float64).reshape(-1, 1)).reshape(np.shape(codes))
+
+
+def q8_chunk_attn(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, *, n_head,
+                  n_head_kv, head_dim, scale, causal=True, q_offsets=None, kv_offsets=None,
+                  window=0, gate=None, rows=None, n_threads=0):
+    """Attention through the 8-bit store: every row (one per (token, head)) of Q, K and
+    V is its integer codes times its scale.  The store's reader takes the scales out of
+    the dot products, which is the attention of the dequantised rows; that is what is
+    computed here (f64, :func:`chunk_attn`)."""
+    return chunk_attn(_dequant(q_codes, q_scales, head_dim),
+                      _dequant(k_codes, k_scales, head_dim),
+                      _dequant(v_codes, v_scales, head_dim), n_head=n_head,
+                      n_head_kv=n_head_kv, head_dim=head_dim, scale=scale, causal=causal,
+                      q_offsets=q_offsets, kv_offsets=kv_offsets, window=window, gate=gate,
+                      rows=rows, n_threads=n_threads)
+
+
+def qk_prep_q8_attn(q, k, v, wq, wk, k_codes, k_scales, v_codes, v_scales, *, n_head,
+                    n_head_kv, head_dim, rope_dim, rope_freq_base, rms_eps, scale,
+                    causal=True, q_offsets=None, kv_offsets=None, window=0, gate=None,
+                    rows=None, n_threads=0):
+    """A quantised session's attention over an 8-bit cache: the raw f32 rows are
+    normalised and rotated (Q and K, f64) at the positions of the new rows, rounded to
+    f32, quantised per (token, head) with V (:func:`quant_rows`), the new K and V codes
+    and scales are written into the last rows of each sequence's cache range, and the
+    queries attend the cache through the store (:func:`q8_chunk_attn`).  Returns
+    ``(out, k_codes', k_scales', v_codes', v_scales', q_codes, q_scales)``."""
+    T_q = np.asarray(q).shape[0]
+    T_kv = np.asarray(k_codes).shape[0]
+    if (q_offsets is None) != (kv_offsets is None):
+        raise ValueError("give both offset arrays or neither")
+    qo = _offsets(q_offsets, T_q)
+    ko = _offsets(kv_offsets, T_kv)
+    base = (ko[1:] - ko[:-1]) - (qo[1:] - qo[:-1])
+    if np.any(base < 0):
+        raise ValueError("a sequence has fewer cache rows than new rows")
+    qn, kn = qknorm_rope(q, k, wq, wk, n_head=n_head, n_head_kv=n_head_kv, head_dim=head_dim,
+                         rope_dim=rope_dim, rope_freq_base=rope_freq_base, rms_eps=rms_eps,
+                         seq_offsets=qo, pos0=base, n_threads=n_threads)
+    qc, qs, _ = quant_rows(qn.astype(np.float32), head_dim)
+    kq, kqs, _ = quant_rows(kn.astype(np.float32), head_dim)
+    vq, vqs, _ = quant_rows(np.asarray(v, dtype=np.float32), head_dim)
+    kc = np.array(k_codes, dtype=np.int8, copy=True).reshape(T_kv, n_head_kv * head_dim)
+    ks = np.array(k_scales, dtype=np.float32, copy=True).reshape(T_kv, n_head_kv)
+    vc = np.array(v_codes, dtype=np.int8, copy=True).reshape(T_kv, n_head_kv * head_dim)
+    vs = np.array(v_scales, dtype=np.float32, copy=True).reshape(T_kv, n_head_kv)
+    kq = kq.reshape(T_q, -1)
+    vq = vq.reshape(T_q, -1)
+    for s in range(len(qo) - 1):
+        dst = slice(int(ko[s] + base[s]), int(ko[s + 1]))
+        src = slice(int(qo[s]), int(qo[s + 1]))
+        kc[dst], vc[dst] = kq[src], vq[src]
+        ks[dst] = kqs.reshape(T_q, n_head_kv)[src]
+        vs[dst] = vqs.reshape(T_q, n_head_kv)[src]
+    out = q8_chunk_attn(qc, qs, kc, ks, vc, vs, n_head=n_head, n_head_kv=n_head_kv,
+                        head_dim=head_dim, scale=scale, causal=causal, q_offsets=qo,
+                        kv_offsets=ko, window=window, gate=gate, rows=rows,
+                        n_threads=n_threads)
+    return out, kc, ks, vc, vs, qc.reshape(T_q, -1), qs.reshape(T_q, n_head)
 
 
 def version() -> str:

@@ -45,6 +45,12 @@
  *    element of a gate tensor before the output projection; memra-engine
  *    0.101.0 src/spec.rs does the same with the gate split off the Q
  *    projection, and its step35 layers with one gate value per head.
+ *  - needle-core v3/model.rs, 8-bit activation quantisation of a session
+ *    (`quant_rows`, `quantize_rows` and the 8-bit K/V store): after RoPE the
+ *    query, key and value rows are quantised per (token, head) with 8 bits,
+ *    the store keeps integer rows with one scale per row, and its reader takes
+ *    the scale outside the dot product (which is algebraically the dot product
+ *    of the dequantised rows); quantising twice changes nothing.
  *
  * Readings taken where the pages are silent (each one is listed with its
  * reason in the design notes of the repository):
@@ -54,6 +60,11 @@
  *  - Query head h reads K/V head floor(h / (n_head / n_head_kv)).
  *  - Packed sequences never attend across their boundaries and their positions
  *    restart at 0.
+ *  - 8-bit quantisation is symmetric with the row's largest magnitude on the
+ *    top code: scale = max|x| / 127, code = x / scale rounded to the nearest
+ *    integer, ties to even, within -127..127; a row of zeros gets scale 0 and
+ *    codes 0.  These are integer decisions, so they are taken in single
+ *    precision, the precision of the values being quantised.
  */
 #include <math.h>
 #include <pthread.h>
@@ -374,6 +385,36 @@ int oracle_gqa_attn(const double* q, const double* k, const double* v,
     return oracle_chunk_attn(q, k, v, seq_offsets, seq_offsets, n_seqs, T, T, n_head,
                              n_head_kv, head_dim, scale, causal, 0, NULL, 0, rows, n_rows,
                              out, n_threads);
+}
+
+/* 8-bit quantisation of n_rows rows of len floats each (needle-core v3/model.rs,
+ * `quant_rows` per (token, head) row; `quantize_rows` returning the integer rows
+ * and one scale per row).  codes[r, i] * scales[r] (rounded to float) is the
+ * fake-quantised value, written to deq when deq is not NULL.  Single precision
+ * throughout: scale = max|x| / 127, code = nearest integer to x / scale (ties to
+ * even), clamped to -127..127. */
+int oracle_quant_rows(const float* x, int64_t n_rows, int len, int8_t* codes, float* scales,
+                      float* deq) {
+    if (n_rows < 0 || len <= 0 || (n_rows > 0 && (!x || !codes || !scales)))
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const float* xr = x + r * len;
+        float amax = 0.0f;
+        for (int i = 0; i < len; ++i) {
+            const float m = fabsf(xr[i]);
+            if (m > amax) amax = m;
+        }
+        const float scale = amax / 127.0f;
+        scales[r] = scale;
+        for (int i = 0; i < len; ++i) {
+            float c = scale > 0.0f ? rintf(xr[i] / scale) : 0.0f;
+            if (c > 127.0f) c = 127.0f;
+            if (c < -127.0f) c = -127.0f;
+            codes[r * len + i] = (int8_t)c;
+            if (deq) deq[r * len + i] = c * scale;
+        }
+    }
+    return ORACLE_OK;
 }
 
 const char* oracle_version(void) { return "pfa-oracle 1 (f64, plain loops)"; }

@@ -672,3 +672,153 @@ def test_gate_matches_torch_sigmoid_and_heads_broadcast():
     np.testing.assert_array_equal(oracle.chunk_attn(q, kc, vc, gate=gh, **kw),
                                   oracle.chunk_attn(q, kc, vc, gate=np.repeat(gh, 8, axis=1),
                                                     **kw))
+
+
+# ---------------------------------------------------------------------------
+# 8-bit quantised session (needle-core v3/model.rs: `quant_rows` quantises the query, key
+# and value rows per (token, head) with 8 bits after RoPE; `quantize_rows` gives the
+# integer rows and one scale per row; the store's reader takes the scales out of the dot
+# products; quantising twice changes neither the scale nor any integer).
+
+def test_quant_hand_example():
+    # scale 1 exactly (largest magnitude 127): codes are x rounded, ties to even
+    row = np.array([127, 2.5, -3.5, 0.5, -0.49, 126.6, -126.5, 1.5], np.float32)
+    want = np.array([127, 2, -4, 0, 0, 127, -126, 2], np.int8)
+    x = np.stack([row, row * np.float32(0.125), np.zeros(8, np.float32),
+                  np.array([-254, 1, 3, 5, -7, 0, 200, 2], np.float32)])
+    codes, scales, deq = oracle.quant_rows(x, 8)
+    np.testing.assert_array_equal(scales, np.array([1.0, 0.125, 0.0, 2.0], np.float32))
+    np.testing.assert_array_equal(codes[0], want)
+    np.testing.assert_array_equal(codes[1], want)                  # a power of two: same codes
+    np.testing.assert_array_equal(codes[2], np.zeros(8, np.int8))  # a row of zeros
+    np.testing.assert_array_equal(codes[3], np.array([-127, 0, 2, 2, -4, 0, 100, 1], np.int8))
+    np.testing.assert_array_equal(deq[3], np.array([-254, 0, 4, 4, -8, 0, 200, 2], np.float32))
+    np.testing.assert_array_equal(deq[0], want.astype(np.float32))
+
+
+@pytest.mark.parametrize("mag", [1.0, 1e-3, 37.0, 1e-30, 3e30])
+def test_quant_second_pass_changes_nothing(mag):
+    x = (_rng(41).standard_normal((3000, 64)) * mag).astype(np.float32)
+    c1, s1, d1 = oracle.quant_rows(x, 64)
+    c2, s2, d2 = oracle.quant_rows(d1, 64)
+    np.testing.assert_array_equal(c2, c1)
+    np.testing.assert_array_equal(s2, s1)
+    np.testing.assert_array_equal(d2, d1)
+
+
+def test_quant_error_bound_range_and_top_code():
+    r = _rng(42)
+    x = (r.standard_normal((2000, 128)) * np.exp(r.standard_normal((2000, 1)))).astype(np.float32)
+    c, s, d = oracle.quant_rows(x, 128)
+    ci = c.astype(np.int64)
+    assert ci.min() >= -127 and ci.max() <= 127
+    np.testing.assert_array_equal(np.abs(ci).max(axis=1), np.full(2000, 127))
+    # the largest magnitude sits on the top code, and the scale is it over 127
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    np.testing.assert_allclose(s.astype(np.float64), amax / 127, rtol=2 ** -23)
+    err = np.abs(x.astype(np.float64) - ci * s.astype(np.float64)[:, None])
+    assert np.all(err <= s.astype(np.float64)[:, None] * (0.5 + 1e-5))
+    np.testing.assert_array_equal(d, (c.astype(np.float32) * s[:, None]).astype(np.float32))
+
+
+def test_quant_rows_are_independent():
+    x = _rng(43).standard_normal((5, 3, 16)).astype(np.float32)
+    c, s, _ = oracle.quant_rows(x, 16)
+    assert c.shape == x.shape and s.shape == (15,)
+    y = x.copy()
+    y[2, 1] *= np.float32(1024.0)
+    c2, s2, _ = oracle.quant_rows(y, 16)
+    np.testing.assert_array_equal(c2, c)
+    changed = np.zeros(15, bool)
+    changed[7] = True
+    np.testing.assert_array_equal(s2[~changed], s[~changed])
+    assert s2[7] == s[7] * 1024
+
+
+def _q8_case(seed, H=4, Hkv=2, d=16, Tq=7, Tkv=11):
+    r = _rng(seed)
+    qc = r.integers(-127, 128, size=(Tq, H * d)).astype(np.int8)
+    kc = r.integers(-127, 128, size=(Tkv, Hkv * d)).astype(np.int8)
+    vc = r.integers(-127, 128, size=(Tkv, Hkv * d)).astype(np.int8)
+    qs = (0.01 * np.exp(r.standard_normal((Tq, H)))).astype(np.float32)
+    ks = (0.01 * np.exp(r.standard_normal((Tkv, Hkv)))).astype(np.float32)
+    vs = (0.01 * np.exp(r.standard_normal((Tkv, Hkv)))).astype(np.float32)
+    return qc, qs, kc, ks, vc, vs
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_q8_attention_is_the_stored_int_reader(causal):
+    # integer dot products (exact, int64) with both row scales taken outside, then softmax
+    H, Hkv, d, Tq, Tkv = 4, 2, 16, 7, 11
+    qc, qs, kc, ks, vc, vs = _q8_case(44)
+    out = oracle.q8_chunk_attn(qc, qs, kc, ks, vc, vs, n_head=H, n_head_kv=Hkv, head_dim=d,
+                               scale=0.25, causal=causal)
+    want = np.zeros((Tq, H * d))
+    base = Tkv - Tq
+    for h in range(H):
+        kv = h // (H // Hkv)
+        qi = qc[:, h * d:(h + 1) * d].astype(np.int64)
+        ki = kc[:, kv * d:(kv + 1) * d].astype(np.int64)
+        dots = qi @ ki.T
+        sc = 0.25 * qs[:, h:h + 1].astype(np.float64) * ks[None, :, kv].astype(np.float64) * dots
+        if causal:
+            sc[np.arange(Tkv)[None, :] > np.arange(Tq)[:, None] + base] = -np.inf
+        p = np.exp(sc - sc.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        vv = vc[:, kv * d:(kv + 1) * d].astype(np.float64) * vs[:, kv:kv + 1].astype(np.float64)
+        want[:, h * d:(h + 1) * d] = p @ vv
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
+
+
+def test_q8_attention_matches_torch_sdpa_over_dequantised_rows():
+    H, Hkv, d, Tq, Tkv = 4, 2, 16, 7, 7
+    qc, qs, kc, ks, vc, vs = _q8_case(45, Tkv=7)
+    out = oracle.q8_chunk_attn(qc, qs, kc, ks, vc, vs, n_head=H, n_head_kv=Hkv, head_dim=d,
+                               scale=0.25)
+
+    def deq(c, s, n):
+        return torch.from_numpy(c.astype(np.float64).reshape(-1, n, d) *
+                                s.astype(np.float64)[..., None]).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(deq(qc, qs, H), deq(kc, ks, Hkv), deq(vc, vs, Hkv),
+                                         is_causal=True, scale=0.25, enable_gqa=True)
+    np.testing.assert_allclose(out, ref.transpose(0, 1).reshape(Tq, H * d).numpy(),
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_qk_prep_q8_attn_is_prep_then_quant_then_store():
+    # a 5-row block over a 4-row prefix: the new rows are normalised and rotated at
+    # positions 4..8, rounded to f32, quantised per (token, head); the cache keeps the
+    # prefix rows and gains the new ones; attention reads the store
+    H, Hkv, d, n = 4, 2, 16, 16
+    r = _rng(46)
+    q = r.standard_normal((5, H * d)).astype(np.float32)
+    k = r.standard_normal((5, Hkv * d)).astype(np.float32)
+    v = r.standard_normal((5, Hkv * d)).astype(np.float32)
+    wq = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    wk = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    _, _, kc0, ks0, vc0, vs0 = _q8_case(47, Tq=9, Tkv=9)
+    kw = dict(n_head=H, n_head_kv=Hkv, head_dim=d, rope_dim=n, rope_freq_base=1e4,
+              rms_eps=1e-6)
+    out, kc, ks, vc, vs, qc, qs = oracle.qk_prep_q8_attn(
+        q, k, v, wq, wk, kc0, ks0, vc0, vs0, scale=0.25, q_offsets=[0, 5],
+        kv_offsets=[0, 9], **kw)
+    np.testing.assert_array_equal(kc[:4], kc0[:4])
+    np.testing.assert_array_equal(vs[:4], vs0[:4])
+    qn, kn = oracle.qknorm_rope(q, k, wq, wk, seq_offsets=[0, 5], pos0=[4], **kw)
+    for got_c, got_s, x in ((qc, qs, qn), (kc[4:], ks[4:], kn), (vc[4:], vs[4:], v)):
+        c, s, _ = oracle.quant_rows(np.asarray(x, np.float32), d)
+        np.testing.assert_array_equal(got_c, c.reshape(got_c.shape))
+        np.testing.assert_array_equal(got_s, s.reshape(got_s.shape))
+    np.testing.assert_array_equal(
+        out, oracle.q8_chunk_attn(qc, qs, kc, ks, vc, vs, n_head=H, n_head_kv=Hkv, head_dim=d,
+                                  scale=0.25, q_offsets=[0, 5], kv_offsets=[0, 9]))
+    # and 8 bits are close to no quantisation at all
+    full = oracle.chunk_attn(qn, np.concatenate([kc0[:4] * 0.0, kn]),
+                             np.concatenate([vc0[:4] * 0.0, v]), n_head=H, n_head_kv=Hkv,
+                             head_dim=d, scale=0.25, q_offsets=[0, 5], kv_offsets=[0, 9])
+    mine = oracle.q8_chunk_attn(qc, qs, np.concatenate([kc0[:4] * 0, kc[4:]]),
+                                np.concatenate([ks0[:4], ks[4:]]),
+                                np.concatenate([vc0[:4] * 0, vc[4:]]),
+                                np.concatenate([vs0[:4], vs[4:]]), n_head=H, n_head_kv=Hkv,
+                                head_dim=d, scale=0.25, q_offsets=[0, 5], kv_offsets=[0, 9])
+    assert np.abs(mine - full).max() < 0.05

@@ -37,6 +37,11 @@ MUTANTS = [
      "last - c->window > lo) lo = last - c->window;"),
     ("gate sign flipped", "o[x] *= 1.0 / (1.0 + exp(-g));", "o[x] *= 1.0 / (1.0 + exp(g));"),
     ("gate head index off", "c->gate[i * c->H + h]", "c->gate[i * c->H + (h + 1) % c->H]"),
+    ("quant divisor 128", "const float scale = amax / 127.0f;",
+     "const float scale = amax / 128.0f;"),
+    ("quant truncates", "rintf(xr[i] / scale)", "truncf(xr[i] / scale)"),
+    ("quant ties away from zero", "rintf(xr[i] / scale)", "roundf(xr[i] / scale)"),
+    ("fake-quant value unscaled", "deq[r * len + i] = c * scale;", "deq[r * len + i] = c;"),
 ]
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins)
@@ -83,7 +88,7 @@ def test_planted_mistake_is_caught(name, before, after, monkeypatch):
         real = oracle._load()
         mut = ctypes.CDLL(so)
         for fn in ("oracle_qknorm_rope", "oracle_gqa_attn", "oracle_qknorm_rope_from",
-                   "oracle_chunk_attn"):
+                   "oracle_chunk_attn", "oracle_quant_rows"):
             getattr(mut, fn).argtypes = getattr(real, fn).argtypes
             getattr(mut, fn).restype = getattr(real, fn).restype
         monkeypatch.setattr(oracle, "_lib", mut)

@@ -140,3 +140,22 @@ def sample_rows(w: Workload, n_random: int = 64, seed: int = 0) -> np.ndarray:
                 rows.add(r)
     rows.update(int(x) for x in rng.integers(0, w.T, size=n_random))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def q8_store(rows: int, heads: int, head_dim: int, seed: int, spread: float = 45.0,
+             scale: float = 0.022):
+    """Random contents of an 8-bit K/V (or Q) store, shaped like quantised normal rows:
+    ``codes [rows, heads*head_dim]`` int8 and ``scales [rows, heads]`` f32.
+
+    Draw order (numpy PCG64 seeded with ``seed``): codes as ``N(0, spread^2)`` rounded to
+    integers and clipped to -127..127; then one position per (row, head) and a sign, where
+    the code is set to +-127 (every quantised row has its largest magnitude on the top
+    code); then scales ``scale * exp(0.1 N(0,1))``.  ``spread = 45`` and ``scale = 0.022``
+    match unit-variance rows of 128 values."""
+    rng = np.random.default_rng(seed)
+    c = np.clip(np.rint(rng.normal(0.0, spread, size=(rows, heads, head_dim))), -127, 127)
+    top = rng.integers(0, head_dim, size=(rows, heads))
+    sign = np.where(rng.integers(0, 2, size=(rows, heads)) == 1, 127, -127)
+    np.put_along_axis(c, top[..., None], sign[..., None], axis=2)
+    scales = (scale * np.exp(0.1 * rng.standard_normal((rows, heads)))).astype(np.float32)
+    return c.astype(np.int8).reshape(rows, heads * head_dim), scales
