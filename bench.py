@@ -120,6 +120,11 @@ def main():
     ap.add_argument("--gate", default="none", choices=["none", "elem", "head"],
                     help="with the chunk entry points: a gated output, out = O * sigmoid(gate), "
                          "the gate per element or per head (seeded N(0,1))")
+    ap.add_argument("--q8", action="store_true",
+                    help="time the 8-bit quantised session instead (Q, K, V quantised per "
+                         "(token, head) after RoPE, attention through the int8 store): fused: "
+                         "qk_prep_attn_q8 on the raw rows, unfused: gqa_attn_q8 on a filled "
+                         "store; --chunk-base, --window and --gate apply (no CPU baseline line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -152,6 +157,9 @@ def main():
 
     w = wl.sweep_workload(args.seq_len) if args.seq_len else wl.CONFIGS[args.workload]
     x = wl.make_inputs(w)
+    if args.q8:
+        run_q8(args, w, x)
+        return
     if args.chunk_base or args.window or args.gate != "none":
         run_chunk(args, w, x)
         return
@@ -337,6 +345,101 @@ def run_chunk(args, w, x):
         "config": {"workload": f"{w.name} chunk: {T_q} new rows over {B} cached rows, "
                                f"n_head={w.n_head}, n_head_kv={w.n_head_kv}, head_dim={d}, "
                                f"rope_dim={w.rope_dim}"
+                               + (f", window={args.window}" if args.window else "")
+                               + (f", gate per {args.gate}" if gate is not None else ""),
+                   "T_q": T_q, "T_kv": T, "n_head": w.n_head, "n_head_kv": w.n_head_kv,
+                   "head_dim": d, "path": args.path, "causal_flops": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": kernel, "kernel_ms": round(kern_ms, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def run_q8(args, w, x):
+    """One step of an 8-bit quantised session (``--q8``): prefill of the workload, or with
+    ``--chunk-base B`` its last T - B rows over B stored rows."""
+    import torch
+
+    import transformer_prefill_attention_amd as pfa
+
+    if w.n_seqs != 1 or not 0 <= args.chunk_base < w.T:
+        raise SystemExit("--q8 needs a one-sequence workload longer than --chunk-base")
+    B, T, d = args.chunk_base, w.T, w.head_dim
+    T_q = T - B
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(getattr(x, n)).to(dev) for n in ("q", "k", "v", "wq", "wk")}
+    kw_rope = dict(head_dim=d, rope_dim=w.rope_dim, rope_freq_base=w.rope_freq_base,
+                   rms_eps=w.rms_eps)
+    offs = dict(q_offsets=[0, T_q], kv_offsets=[0, T]) if B else {}
+    # the store a session holds after prefilling all T rows (the fused step rewrites its new
+    # rows in place each time); the unfused step also needs the new rows' Q codes
+    kc = torch.zeros(T, w.n_head_kv * d, dtype=torch.int8, device=dev)
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros(T, w.n_head_kv, dtype=torch.float32, device=dev)
+    vs = torch.zeros_like(ks)
+    pfa.qk_prep_attn_q8(t["q"], t["k"], t["v"], t["wq"], t["wk"], kc, ks, vc, vs,
+                        scale=w.softmax_scale, **kw_rope)
+    qn, _ = pfa.qknorm_rope(t["q"], t["k"], t["wq"], t["wk"], **kw_rope)
+    qc, qs = pfa.quantize_rows(qn[B:].contiguous(), d)
+    q_new, k_new, v_new = t["q"][B:].contiguous(), t["k"][B:].contiguous(), t["v"][B:].contiguous()
+    out = torch.empty_like(q_new)
+    gate = None
+    if args.gate != "none":
+        g = torch.Generator().manual_seed(w.seed + 1)
+        gate = torch.randn(T_q, w.n_head * (d if args.gate == "elem" else 1), generator=g).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = []
+
+    def step(record):
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+        if args.path == "fused":
+            pfa.qk_prep_attn_q8(q_new, k_new, v_new, t["wq"], t["wk"], kc, ks, vc, vs,
+                                scale=w.softmax_scale, window=args.window, gate=gate, out=out,
+                                **kw_rope, **offs)
+        else:
+            pfa.gqa_attn_q8(qc, qs.view(T_q, w.n_head), kc, ks, vc, vs, head_dim=d,
+                            scale=w.softmax_scale, window=args.window, gate=gate, out=out,
+                            **offs)
+        if record:
+            b.record(stream)
+            ev.append((a, b))
+
+    t_spin = time.perf_counter()
+    while (time.perf_counter() - t_spin) * 1e3 < args.spinup_ms:
+        step(False)
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if args.window:
+        pairs = sum(min(args.window, B + r + 1) for r in range(T_q))
+    else:
+        pairs = T_q * B + T_q * (T_q + 1) // 2
+    flops = 4 * d * w.n_head * pairs
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    kernel = f"stage_kv_q8_kernel<{d}> + attn_bf16_kernel<{d},false,false,true>"
+    if args.path == "fused":
+        kernel = f"qknorm_rope_kernel<{d},0,true> + " + kernel
+    what = (f"{T_q} new rows over {B} stored rows" if B else f"prefill of {T} rows")
+    res = {
+        "metric": METRIC, "value": round(flops / (elapsed / args.steps) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "spinup_ms": args.spinup_ms, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8 codes, bf16 MFMA",
+        "data": "synthetic (seeded N(0,1) Q/K/V, norm weights 1+N(0,0.1)), quantised per row",
+        "config": {"workload": f"{w.name} 8-bit session: {what}, n_head={w.n_head}, "
+                               f"n_head_kv={w.n_head_kv}, head_dim={d}, rope_dim={w.rope_dim}"
                                + (f", window={args.window}" if args.window else "")
                                + (f", gate per {args.gate}" if gate is not None else ""),
                    "T_q": T_q, "T_kv": T, "n_head": w.n_head, "n_head_kv": w.n_head_kv,

@@ -262,6 +262,100 @@ size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_off
                                  int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
                                  int precision, int fused);
 
+/*
+ * 8-bit quantised sessions
+ * ------------------------
+ * Passages: needle-core v3/model.rs, `quant_rows` (a quantised session
+ * quantises every (token, head) row of the query, the keys and the values with
+ * 8 bits right after RoPE, before attention and before the cache write),
+ * `quantize_rows` and its int8 K/V store (integer rows plus one scale per row,
+ * the form decode reads; the store's reader takes the scales out of the dot
+ * products).  The rule, in IEEE single precision: a row's scale is its largest
+ * magnitude / 127; a value's code is the nearest integer to value / scale, ties
+ * to even, within -127..127; a row of zeros has scale 0 and codes 0.  A value
+ * of the store is code * scale.
+ *
+ * An 8-bit store of `heads` heads over `rows` rows is a pair of device arrays:
+ * codes int8 [rows, heads*head_dim] (16-byte aligned) and scales f32
+ * [rows, heads], row-major like the f32 tensors.
+ */
+
+/*
+ * pfa_quantize_rows -- quantise n_rows rows of row_len floats (one row per
+ * (token, head) when row_len is the head size).
+ *  x       [n_rows, row_len] f32, device, read.
+ *  codes   [n_rows, row_len] int8, device, written.
+ *  scales  [n_rows] f32, device, written.
+ *  x_fq    NULL, or [n_rows, row_len] f32, device, written: the fake-quantised
+ *          values code * scale; may be x itself (in place, as `quant_rows`
+ *          does), otherwise must not overlap x.  codes, scales and x_fq must not
+ *          overlap each other or x.
+ *  1 <= row_len <= 65536, n_rows * row_len <= 2^40; n_rows == 0 is a no-op.
+ */
+int pfa_quantize_rows(const float* x, int64_t n_rows, int row_len, int8_t* codes,
+                      float* scales, float* x_fq, void* stream);
+
+/*
+ * gqa_attn_q8 -- gqa_chunk_attn through 8-bit stores: the scores are the
+ * integer dot products of the Q and K codes (exact) times the two row scales
+ * and `scale`; the weights multiply the dequantised V rows.  Plain prefill is
+ * q_offsets = kv_offsets (or both NULL with T_q = T_kv).
+ *  q, q_scale  8-bit store of the query rows, [T_q, n_head*head_dim] codes and
+ *        [T_q, n_head] scales, device, read.
+ *  k_cache, k_scale, v_cache, v_scale  8-bit stores of the keys and values,
+ *        [T_kv, n_head_kv*head_dim] codes and [T_kv, n_head_kv] scales, device,
+ *        read; sequence s owns rows kv_offsets[s] .. kv_offsets[s+1]-1, its new
+ *        rows last, as for gqa_chunk_attn.
+ *  out   [T_q, n_head*head_dim] f32, device, written; must not overlap the rest.
+ *  gate, gate_per_head, q_offsets, kv_offsets, n_seqs, causal, window  as for
+ *        gqa_chunk_attn.
+ *  scale  finite and > 0 (the row scales are applied inside the exponent).
+ *  The products run on bf16 matrix cores: codes are exact in bf16 and every
+ *  partial sum of code products is an integer below 2^24, so the integer scores
+ *  are exact; V is dequantised and rounded to bf16, and the weights are rounded
+ *  to bf16, as in PFA_PREC_BF16.
+ *  workspace  device, 256-byte aligned, pfa_q8_workspace_bytes(..., 0) bytes.
+ */
+int gqa_attn_q8(const int8_t* q, const float* q_scale, const int8_t* k_cache,
+                const float* k_scale, const int8_t* v_cache, const float* v_scale, float* out,
+                const float* gate, int gate_per_head, const int32_t* q_offsets,
+                const int32_t* kv_offsets, int n_seqs, int T_q, int T_kv, int n_head,
+                int n_head_kv, int head_dim, float scale, int causal, int window,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qk_prep_attn_q8 -- a quantised session's attention step in one call: QK-norm +
+ * NeoX RoPE of the raw new Q and K at their positions (as qk_prep_chunk_attn),
+ * then Q, K and V quantised per (token, head); the K and V codes and scales go
+ * into the last rows of each sequence's range of the caller's 8-bit store, the
+ * Q codes into the workspace, and gqa_attn_q8 runs over the store.
+ *  q [T_q, n_head*head_dim], k, v [T_q, n_head_kv*head_dim]  raw f32, device, read.
+ *  k_cache, k_scale, v_cache, v_scale  the 8-bit K/V store over T_kv rows, device,
+ *        read and written as k_cache / v_cache of qk_prep_chunk_attn; none may
+ *        overlap another tensor.
+ *  out, gate, gate_per_head, offsets, window  as for gqa_chunk_attn; scale as for
+ *        gqa_attn_q8.
+ *  workspace  device, 256-byte aligned, pfa_q8_workspace_bytes(..., 1) bytes.
+ */
+int qk_prep_attn_q8(const float* q, const float* k, const float* v, float* out,
+                    const float* gate, int gate_per_head,
+                    const float* q_norm_w, const float* k_norm_w,
+                    int8_t* k_cache, float* k_scale, int8_t* v_cache, float* v_scale,
+                    const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                    int T_q, int T_kv, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                    float rope_freq_base, float rms_eps, float scale, int causal, int window,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace in bytes of gqa_attn_q8 (fused = 0) or qk_prep_attn_q8
+ * (fused = 1): bf16 K/V tiles over each sequence's store rows (sum_s
+ * ceil(kv_len_s / 64) tiles of 2 * 64 * head_dim * 2 bytes per K/V head) and 256
+ * bytes of key scales per tile and head, (fused) the Q codes and scales, and the
+ * key split's partial results.  0 when T_q == 0 or the arguments would be
+ * rejected (pfa_last_error() then says why). */
+size_t pfa_q8_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                              int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                              int fused);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pfa_last_error(void);
 

@@ -340,3 +340,99 @@ def test_chunk_gate_must_not_overlap_out(L):
     # out is [4, 4*64] f32 at 8 MiB; a gate inside it is refused before any launch
     assert _chunk(L, [0, 4], [0, 9], 4, 9, gate=(8 << 20) + 256) == INVALID
     assert "gate" in _msg(L)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit quantised sessions
+
+def _q8_ws(L, q_lens, kv_lens, H, Hkv, D, fused):
+    qo = np.cumsum([0] + list(q_lens)).astype(np.int32)
+    ko = np.cumsum([0] + list(kv_lens)).astype(np.int32)
+    keep_q, qp = _i32(qo.tolist())
+    keep_k, kp = _i32(ko.tolist())
+    return L.pfa_q8_workspace_bytes(qp, kp, len(q_lens), int(qo[-1]), int(ko[-1]), H, Hkv, D,
+                                    fused)
+
+
+@pytest.mark.parametrize("fused", [0, 1])
+@pytest.mark.parametrize("q_lens,kv_lens,H,Hkv,D", [
+    ((8192,), (8192,), 32, 8, 128), ((1024,), (8192,), 32, 8, 128), ((512,), (512,), 16, 8, 128),
+    ((50, 1, 130, 0), (70, 78, 130, 5), 8, 4, 128), ((90,), (135,), 4, 2, 64)])
+def test_q8_workspace_rule(L, q_lens, kv_lens, H, Hkv, D, fused):
+    # the bf16 plan's tiles, 256 bytes of key scales per tile and K/V head, (fused) the Q
+    # codes and scales, each part 256-byte aligned, then the bf16 plan's partial results
+    bf16_chunk = _expected_workspace(q_lens, H, Hkv, D, 1, 0, kv_lens=kv_lens, chunk=True)
+    tiles = Hkv * sum(_ceil(n, 64) for n in kv_lens) * 64 * D * 2 * 2
+    parts = bf16_chunk - _ceil(tiles, 256) * 256 if bf16_chunk > tiles else 0
+    end = tiles + Hkv * sum(_ceil(n, 64) for n in kv_lens) * 256
+    if fused:
+        T_q = sum(q_lens)
+        qs_off = _ceil(_ceil(end, 256) * 256 + T_q * H * D, 256) * 256
+        end = qs_off + T_q * H * 4
+    expect = (_ceil(end, 256) * 256 + parts) if parts else end
+    assert _q8_ws(L, q_lens, kv_lens, H, Hkv, D, fused) == expect
+
+
+def _q8(L, T_q=4, T_kv=9, H=4, Hkv=2, D=64, scale=0.125, window=0, causal=1, ptrs=None,
+        ws=1 << 30, ws_bytes=1 << 24, offs=([0, 4], [0, 9])):
+    # q codes, q scales, k codes, k scales, v codes, v scales, out, gate: disjoint by default
+    p = ptrs or (1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 6 << 20, 8 << 20, 0)
+    keep_q, qp = _i32(offs[0])
+    keep_k, kp = _i32(offs[1])
+    c = [ctypes.c_void_p(x) for x in p]
+    return L.gqa_attn_q8(*c[:7], c[7], 0, qp, kp, len(offs[0]) - 1, T_q, T_kv, H, Hkv, D,
+                         scale, causal, window, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_q8_attention_argument_checks(L):
+    assert _q8(L, scale=0.0) == INVALID and "scale > 0" in _msg(L)
+    assert _q8(L, scale=-0.5) == INVALID
+    assert _q8(L, window=-2) == INVALID and "window" in _msg(L)
+    assert _q8(L, ws=0) == INVALID and "workspace" in _msg(L)
+    assert _q8(L, ws_bytes=16) == INVALID and "needed" in _msg(L)
+    assert _q8(L, ws=(1 << 30) + 64) == INVALID and "256-byte" in _msg(L)
+    p = [1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 6 << 20, 8 << 20, 0]
+    p[2] += 8   # K codes not 16-byte aligned
+    assert _q8(L, ptrs=tuple(p)) == INVALID and "aligned" in _msg(L)
+    p = [1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20, 6 << 20, (3 << 20) + 64, 0]   # out in K
+    assert _q8(L, ptrs=tuple(p)) == INVALID and "out must not overlap k_cache" in _msg(L)
+    assert _q8(L, ws=(8 << 20)) == INVALID and "overlap" in _msg(L)   # workspace over out
+    assert _q8(L, T_q=0, T_kv=0, offs=([0, 0], [0, 0]), ptrs=(0,) * 8, ws=0, ws_bytes=0) == OK
+    assert _q8(L, offs=([0, 4], [0, 3]), T_kv=3) == INVALID and "cache rows" in _msg(L)
+
+
+def test_q8_prep_argument_checks(L):
+    keep_q, qp = _i32([0, 4])
+    keep_k, kp = _i32([0, 9])
+    v = ctypes.c_void_p
+    args = [v(1 << 20), v(2 << 20), v(3 << 20), v(8 << 20), v(0), 0, v(4 << 20), v(5 << 20),
+            v(6 << 20), v(7 << 20), v(9 << 20), v(10 << 20), qp, kp, 1, 4, 9, 4, 2, 64, 64,
+            1e4, 1e-6, 0.125, 1, 0, v(1 << 30), 1 << 24, None]
+    a = list(args)
+    a[20] = 63   # odd rope_dim
+    assert L.qk_prep_attn_q8(*a) == INVALID and "rope_dim" in _msg(L)
+    a = list(args)
+    a[6] = v(0)   # no norm weights
+    assert L.qk_prep_attn_q8(*a) == INVALID and "norm weights" in _msg(L)
+    a = list(args)
+    a[9] = v((6 << 20) + 16)   # K scales inside the K codes (written)
+    assert L.qk_prep_attn_q8(*a) == INVALID and "overlap" in _msg(L)
+    a = list(args)
+    a[23] = 0.0
+    assert L.qk_prep_attn_q8(*a) == INVALID and "scale > 0" in _msg(L)
+
+
+def test_quantize_rows_argument_checks(L):
+    v = ctypes.c_void_p
+    assert L.pfa_quantize_rows(v(0), 0, 128, v(0), v(0), v(0), None) == OK
+    assert L.pfa_quantize_rows(v(1 << 20), 4, 0, v(2 << 20), v(3 << 20), v(0), None) == INVALID
+    assert "row_len" in _msg(L)
+    assert L.pfa_quantize_rows(v(1 << 20), -1, 8, v(2 << 20), v(3 << 20), v(0), None) == INVALID
+    assert L.pfa_quantize_rows(v(1 << 20), 4, 8, v(0), v(3 << 20), v(0), None) == INVALID
+    assert "null" in _msg(L)
+    # codes inside x, and an x_fq that overlaps x without being x
+    assert L.pfa_quantize_rows(v(1 << 20), 4, 8, v((1 << 20) + 8), v(3 << 20), v(0),
+                               None) == INVALID
+    assert L.pfa_quantize_rows(v(1 << 20), 4, 8, v(2 << 20), v(3 << 20), v((1 << 20) + 4),
+                               None) == INVALID
+    assert "overlap" in _msg(L)

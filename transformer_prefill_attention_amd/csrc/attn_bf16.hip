@@ -133,6 +133,25 @@ __global__ __launch_bounds__(256) void rope_table_kernel(__bf16* ws, int Hkv, in
     }
 }
 
+// V^T staging buffer of the staging kernels: D rows of kVts bf16 (the 4-key runs stay
+// 8-byte aligned).  store_vt_rows writes its rows to a V tile: row d holds 8 groups of
+// 8 keys, group p = 2s + h being keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3} (the
+// keys lane half h feeds at P.V step s), group p stored at position swz(d, p, 8).
+constexpr int kVts = kBN + 8;
+template <int D>
+__device__ __forceinline__ void store_vt_rows(const __bf16* vts, __bf16* vt, int tid) {
+#pragma unroll
+    for (int i = 0; i < 8 * D / 256; ++i) {
+        const int f = tid + 256 * i;
+        const int d = f / 8, p = f % 8;
+        const int s4 = p >> 1, h = p & 1;
+        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(vts + d * kVts + 16 * s4 + 4 * h);
+        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vts + d * kVts + 16 * s4 + 8 + 4 * h);
+        const bf16x8 x = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        *reinterpret_cast<bf16x8*>(vt + d * kBN + 8 * swz(d, p, 8)) = x;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // K/V -> bf16 tiles.  Block = (K/V head, tile over all sequences).
 //  K tile: KP parts (high, low) x 64 rows x D; element (r, c) at r*D + 8*swz(r, c/8, D/8) + c%8.
@@ -147,9 +166,8 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
                                                             PrepParams prep) {
     constexpr int KP = SPLIT ? 2 : 1;
     constexpr int NCH = D / 8;
-    constexpr int VTS = kBN + 8;  // V^T row stride in LDS (bf16): 4-key runs stay 8-byte aligned
     constexpr int KRS = D + 4;    // raw K row stride in LDS (f32), fused entry only
-    __shared__ __attribute__((aligned(16))) __bf16 vts[D * VTS];
+    __shared__ __attribute__((aligned(16))) __bf16 vts[D * kVts];
     __shared__ __attribute__((aligned(16))) float kraw[PREP ? kBN * KRS : 4];
     const int tid = threadIdx.x;
     const int kv = blockIdx.x % Hkv;
@@ -193,7 +211,7 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
             bf16x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = (__bf16)r[e][c];
-            *reinterpret_cast<bf16x4*>(vts + (d0 + c) * VTS + key0) = x;
+            *reinterpret_cast<bf16x4*>(vts + (d0 + c) * kVts + key0) = x;
         }
     }
     if constexpr (!PREP) {
@@ -289,26 +307,84 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
         for (int cc = 0; cc < DQ / 8; ++cc) store_k_chunk(kt, r, c0 / 8 + cc, y + 8 * cc);
     }
     __syncthreads();
-    // V^T rows out: group p = 2s + h of row d is keys 16s + 4h + {0..3} then 16s + 8 + 4h + {0..3}
-#pragma unroll
-    for (int i = 0; i < 8 * D / 256; ++i) {
-        const int f = tid + 256 * i;
-        const int d = f / 8, p = f % 8;
-        const int s4 = p >> 1, h = p & 1;
-        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(vts + d * VTS + 16 * s4 + 4 * h);
-        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vts + d * VTS + 16 * s4 + 8 + 4 * h);
-        const bf16x8 x = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        *reinterpret_cast<bf16x8*>(vt + d * kBN + 8 * swz(d, p, 8)) = x;
-    }
+    store_vt_rows<D>(vts, vt, tid);
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, bool PREP>
+// An 8-bit store -> bf16 tiles (needle-core v3/model.rs: the int8 K/V store of a
+// quantised session, each row its codes and one scale).  Same tiles as above: K
+// codes converted unchanged (exact in bf16), V dequantised (code x its row's
+// scale, rounded to bf16).  The tile's 64 key scales (0 past the end of the
+// sequence) go to ks_ws[(kv head, tile)][64]: the attention kernel multiplies the
+// integer scores by them.
+template <int D>
+__global__ __launch_bounds__(256) void stage_kv_q8_kernel(Q8Store q8, __bf16* __restrict__ ws,
+                                                          float* __restrict__ ks_ws,
+                                                          AttnSched sched, int Hkv) {
+    constexpr int NCH = D / 8;
+    __shared__ __attribute__((aligned(16))) __bf16 vts[D * kVts];
+    const int tid = threadIdx.x;
+    const int kv = blockIdx.x % Hkv;
+    const int gt = blockIdx.x / Hkv;
+    const int n_tiles = sched.n_tiles;
+    const int s = find_seq(sched.tile_off, sched.n_seqs, gt);
+    const int k0 = sched.koff[s] + (gt - sched.tile_off[s]) * kBN;  // the tile's key rows
+    const int nval = min(kBN, sched.koff[s + 1] - k0);
+    const int64_t row_stride = (int64_t)Hkv * D;
+    __bf16* kt = ws + ((int64_t)kv * n_tiles + gt) * (kBN * D);
+    __bf16* vt = ws + (int64_t)Hkv * n_tiles * (kBN * D) + ((int64_t)kv * n_tiles + gt) * (kBN * D);
+    const int8_t* kin = q8.k + (int64_t)k0 * row_stride + kv * D;
+    const int8_t* vin = q8.v + (int64_t)k0 * row_stride + kv * D;
+    if (tid < kBN)
+        ks_ws[((int64_t)kv * n_tiles + gt) * kBN + tid] =
+            tid < nval ? q8.ks[(int64_t)(k0 + tid) * Hkv + kv] : 0.0f;
+    // V: 4 keys x 4 dims per block (4-byte code loads), dequantised, written to LDS as
+    // four 4-key runs of V^T.  Block b: dims 4 (b % (D/4)) .., keys 4 (b / (D/4)) ..
+    constexpr int VB = kBN * D / 16;
+#pragma unroll
+    for (int i = 0; i < VB / 256; ++i) {
+        const int b = tid + 256 * i;
+        const int d0 = 4 * (b % (D / 4)), key0 = 4 * (b / (D / 4));
+        float r[4][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = key0 + e < nval;
+            const uint32_t w = ok ? *reinterpret_cast<const uint32_t*>(vin + (key0 + e) * row_stride + d0) : 0u;
+            const float sc = ok ? q8.vs[(int64_t)(k0 + key0 + e) * Hkv + kv] : 0.0f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) r[e][c] = (float)(int8_t)(w >> (8 * c)) * sc;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bf16x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (__bf16)r[e][c];
+            *reinterpret_cast<bf16x4*>(vts + (d0 + c) * kVts + key0) = x;
+        }
+    }
+    // K: 8 codes (one 16-byte bf16 chunk) per step, to their swizzled place
+    for (int i = tid; i < kBN * NCH; i += 256) {
+        const int r = i / NCH, c = i % NCH;
+        bf16x8 x;
+        const uint2 w = r < nval ? *reinterpret_cast<const uint2*>(kin + r * row_stride + 8 * c)
+                                 : uint2{0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            x[e] = (__bf16)(float)(int8_t)((e < 4 ? w.x : w.y) >> (8 * (e & 3)));
+        *reinterpret_cast<bf16x8*>(kt + r * D + 8 * swz(r, c, NCH)) = x;
+    }
+    __syncthreads();
+    store_vt_rows<D>(vts, vt, tid);
+}
+
+// ---------------------------------------------------------------------------
+template <int D, bool SPLIT, bool PREP, bool Q8>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __restrict__ q,
                                                                 const __bf16* __restrict__ ws,
                                                                 float* __restrict__ out,
                                                                 AttnSched sched, AttnGeom geom,
-                                                                PrepParams prep, Partials part) {
+                                                                PrepParams prep, Partials part,
+                                                                Q8Store q8) {
     constexpr int KP = SPLIT ? 2 : 1;
     constexpr int NCH = D / 8;            // 16-byte chunks per K row
     constexpr int KT = KP * kBN * D * 2;  // K tile bytes
@@ -321,9 +397,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     static_assert(K_LOADS >= 1 && V_LOADS >= 1 && KT % (kThreads * 16) == 0 &&
                   VT % (kThreads * 16) == 0, "tiles are whole 8 KB workgroup loads");
     constexpr int SMEM_TILES = 2 * KT + 2 * VT;
+    // Q8: a ring of four 64-float key-scale vectors after the tiles.  Slot t & 3 is
+    // filled with K(t) and read by X(t) of both groups; it is refilled by K(t+4),
+    // issued two phases after group B's X(t).
+    constexpr int SMEM_RING = SMEM_TILES, RING_SLOT = kBN * 4;
+    constexpr int SMEM_MAIN = SMEM_TILES + (Q8 ? 4 * RING_SLOT : 0);
     constexpr int SMEM_OUT = 4 * 32 * QS * 4;
     __shared__ __attribute__((aligned(16)))
-    unsigned char smem[SMEM_TILES > SMEM_OUT ? SMEM_TILES : SMEM_OUT];
+    unsigned char smem[SMEM_MAIN > SMEM_OUT ? SMEM_MAIN : SMEM_OUT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, hl = lane >> 5, ln = lane & 31;
@@ -365,7 +446,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     // ---- Q operand (B of K Q^T): for step s, lane (hl, ln) supplies
     // Q[qi][hl*D/2 + 8s + e], e = 0..7 -- the contraction order is free to permute.
     bf16x8 qop[NQS], qlo[SPLIT ? NQS : 1];
-    {
+    // Q8: the row's scale x softmax scale x log2(e), kept out of the exact integer
+    // scores and applied in the exponent (clamped above 0: a row of zero codes has
+    // scores 0, and hidden keys stay -inf)
+    float qf = 0.0f;
+    if constexpr (Q8) {
+        // codes of Q[qi][hl*D/2 + 8s + e], exact in bf16
+        const bool ok = active && qi < s1;
+        const int8_t* src = q8.q + ((int64_t)(ok ? qi : s0) * H + h) * D + hl * (D / 2);
+#pragma unroll
+        for (int s = 0; s < NQS; s += 2) {
+            const uint4 w = ok ? *reinterpret_cast<const uint4*>(src + 8 * s) : uint4{0, 0, 0, 0};
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                qop[s + e / 8][e % 8] = (__bf16)(float)(int8_t)(ww[e / 4] >> (8 * (e % 4)));
+        }
+        qf = fmaxf((ok ? q8.qs[(int64_t)qi * H + h] : 0.0f) * qscale, 1e-30f);
+    } else {
         const bool ok = active && qi < s1;
         const float* src = q + ((int64_t)(ok ? qi : s0) * H + h) * D + hl * (D / 2);
         float xq[NQS][8];
@@ -473,6 +571,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 if constexpr (SPLIT) qlo[s][e] = (__bf16)(x - (float)qop[s][e]);
             }
     }
+    // Q8: the key scales of this workgroup's tiles (64 per tile, after the V tiles)
+    const float* ks_src =
+        reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(ws) +
+                                       (int64_t)Hkv * n_all * (KT + VT)) +
+        ((int64_t)kv * n_all + tile0 + t_begin) * kBN;
 
     // ---- tile sources in the workspace and per-lane LDS read addresses
     // (tile sources start at this workgroup's first tile; tiles are indexed locally)
@@ -499,6 +602,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
             for (int i = 0; i < K_LOADS; ++i)
                 __builtin_amdgcn_global_load_lds(src + 8192 * i, dst + 8192 * i, 16, 0, 0);
+            // Q8: its 64 key scales into ring slot (t+1) & 3, four bytes a lane of wavefront 0
+            if (Q8 && wave == 0)
+                __builtin_amdgcn_global_load_lds(
+                    reinterpret_cast<const unsigned char*>(ks_src + (int64_t)(t + 1) * kBN + lane),
+                    smem + SMEM_RING + ((t + 1) & 3) * RING_SLOT, 4, 0, 0);
         }
         if (t >= 0 && t < n_local) {
             const unsigned char* src = vt_src + (int64_t)t * VT + 16 * tid;
@@ -603,6 +711,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
             return;
         }
         const int k0 = ks0 + t * kBN;
+        if constexpr (Q8) {
+            // integer scores x the scales of their key rows (register r of block kb:
+            // key 32kb + 8(r/4) + 4hl + r%4 of the tile)
+            const float* ksr =
+                reinterpret_cast<const float*>(smem + SMEM_RING + (lt & 3) * RING_SLOT);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const floatx4 k4 =
+                        *reinterpret_cast<const floatx4*>(ksr + 32 * kb + 8 * g + 4 * hl);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sacc[kb][4 * g + i] *= k4[i];
+                }
+        }
         // register r of block kb: key k0 + 32kb + 8(r/4) + 4hl + r%4.  A key is
         // hidden when it lies past min(qi + dsh, ks1-1) (causal) or past ks1-1, or
         // below the row's window.
@@ -627,13 +750,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
         // A row that has seen no key yet keeps m = -inf (over a cached prefix a row
         // can see no key of a tile, or of a split key range); exponents against
         // -1e30 then give 0 for its hidden keys, not NaN.
-        const float lmax = fmaxf(max16(sacc[0]), max16(sacc[1]));
+        // (Q8: scores are sacc x qf, qf > 0, so their max is max(sacc) x qf)
+        const float lmax = fmaxf(max16(sacc[0]), max16(sacc[1])) * (Q8 ? qf : 1.0f);
         const float m_sub = fmaxf(m_run, -1e30f);
+        // exponent of a weight: score - m
+        auto ex = [&](float x, float m) { return Q8 ? fmaf(x, qf, -m) : x - m; };
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                pop[2 * kb + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_sub);
+                pop[2 * kb + (r >> 3)][r & 7] =
+                    (__bf16)__builtin_amdgcn_exp2f(ex(sacc[kb][r], m_sub));
         // (issued ahead of the check, not sunk below it onto the max's critical path)
         asm volatile("" : "+v"(pop[0]), "+v"(pop[1]), "+v"(pop[2]), "+v"(pop[3]));
         if (__any(lmax > m_run + kLazyMax)) {
@@ -648,7 +775,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     pop[2 * kb + (r >> 3)][r & 7] =
-                        (__bf16)__builtin_amdgcn_exp2f(sacc[kb][r] - m_new);
+                        (__bf16)__builtin_amdgcn_exp2f(ex(sacc[kb][r], m_new));
             l_run *= (double)alpha;
             // alpha is 1 in rows without a bump; hidden from the optimiser, which
             // would otherwise make the multiplication unconditional
@@ -773,8 +900,8 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
         else                                                                                    \
             hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, false>), sgrid, sblock, 0, stream,\
                                k, v, w, sched, geom.Hkv, p);                                    \
-        hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP>), grid, block, 0, stream, q, w, out,  \
-                           sched, geom, p, part);                                               \
+        hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP, false>), grid, block, 0, stream, q, w, \
+                           out, sched, geom, p, part, Q8Store{});                               \
     } while (0)
 #define PFA_LAUNCH_BF16_P(DD, SS)                   \
     do {                                            \
@@ -790,6 +917,34 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
     }
 #undef PFA_LAUNCH_BF16_P
 #undef PFA_LAUNCH_BF16
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && sched.max_chunks > 1)
+        e = launch_attn_combine(part, out, sched, geom, D, kWaves, kBN, n_items, stream);
+    return e;
+}
+
+hipError_t launch_attn_q8(const Q8Store& st8, float* out, void* ws, const AttnSched& sched,
+                          const AttnGeom& geom, int D, const Partials& part, int n_items,
+                          hipStream_t stream) {
+    __bf16* w = static_cast<__bf16*>(ws);
+    float* ks_ws = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
+                                            bf16_workspace_bytes(sched.n_tiles, geom.Hkv, D,
+                                                                 false, 0));
+    const PrepParams p{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
+    const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
+    const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv),
+        block(kThreads);
+    if (D == 128) {
+        hipLaunchKernelGGL((stage_kv_q8_kernel<128>), sgrid, sblock, 0, stream, st8, w, ks_ws,
+                           sched, geom.Hkv);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true>), grid, block, 0, stream,
+                           nullptr, w, out, sched, geom, p, part, st8);
+    } else {
+        hipLaunchKernelGGL((stage_kv_q8_kernel<64>), sgrid, sblock, 0, stream, st8, w, ks_ws,
+                           sched, geom.Hkv);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true>), grid, block, 0, stream,
+                           nullptr, w, out, sched, geom, p, part, st8);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && sched.max_chunks > 1)
         e = launch_attn_combine(part, out, sched, geom, D, kWaves, kBN, n_items, stream);

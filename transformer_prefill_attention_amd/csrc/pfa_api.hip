@@ -261,7 +261,8 @@ extern "C" {
 const char* pfa_last_error(void) { return g_err; }
 
 const char* pfa_version(void) {
-    return "pfa 0.4 (gfx950; f32 and bf16 MFMA attention, prefill and chunks over a cached prefix)";
+    return "pfa 0.5 (gfx950; f32 and bf16 MFMA attention, prefill and chunks over a cached prefix, "
+           "8-bit quantised sessions)";
 }
 
 static size_t workspace_for(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
@@ -546,6 +547,217 @@ int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* ou
     return attn_common(Mode::kChunkFused, q, k, v, out, k_cache, v_cache, gate, gate_per_head,
                        st, n_head, n_head_kv, head_dim, scale, causal, window, precision, &prep,
                        workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// 8-bit quantised session (needle-core v3/model.rs: Q, K and V quantised per
+// (token, head) after RoPE; attention through the int8 store).
+
+// A device buffer an entry point reads or writes, for the overlap checks.
+struct Span {
+    const void* p;
+    size_t n;
+    bool written;
+    const char* name;
+};
+
+// No written span may overlap another span (reads may alias each other).
+static int check_spans(const Span* sp, int n) {
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j)
+            if ((sp[i].written || sp[j].written) && sp[i].p && sp[j].p &&
+                overlaps(sp[i].p, sp[i].n, sp[j].p, sp[j].n))
+                return fail(PFA_ERR_INVALID_ARG, "%s must not overlap %s", sp[i].name, sp[j].name);
+    return PFA_OK;
+}
+
+// Workspace of the 8-bit attention: the bf16 K/V tiles and the tiles' key scales,
+// then (fused entry) the Q codes and Q scales, then the key split's partial results.
+struct Q8Layout {
+    size_t scales_off = 0, qc_off = 0, qs_off = 0, part_off = 0, need = 0;
+};
+static Q8Layout q8_layout(const Plan& p, int T_q, int n_head, int head_dim, bool fused) {
+    Q8Layout l;
+    l.scales_off = p.tile_bytes;
+    size_t end = l.scales_off + pfa::q8_scale_bytes(p.sched.n_tiles, p.geom.Hkv);
+    if (fused) {
+        l.qc_off = align256(end);
+        l.qs_off = align256(l.qc_off + (size_t)T_q * n_head * head_dim);
+        end = l.qs_off + (size_t)T_q * n_head * 4;
+    }
+    l.part_off = p.part_bytes ? align256(end) : end;
+    l.need = l.part_off + p.part_bytes;
+    return l;
+}
+
+static int check_q8_attn(float scale) {
+    if (!std::isfinite(scale) || !(scale > 0.0f))
+        return fail(PFA_ERR_INVALID_ARG,
+                    "the 8-bit entry points need a finite scale > 0 (got %g)", (double)scale);
+    return PFA_OK;
+}
+
+static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+size_t pfa_q8_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                              int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                              int fused) {
+    g_err[0] = 0;
+    if (check_geometry(T_q, n_head, n_head_kv, head_dim) ||
+        check_geometry(T_kv, n_head, n_head_kv, head_dim))
+        return 0;
+    if (T_q == 0) return 0;
+    pfa::SeqTable st;
+    if (build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st)) return 0;
+    Plan p;
+    if (make_plan(st, n_head, n_head_kv, head_dim, 1.0f, 1, PFA_PREC_BF16, p)) return 0;
+    if (p.items == 0) return 0;
+    return q8_layout(p, T_q, n_head, head_dim, fused != 0).need;
+}
+
+int pfa_quantize_rows(const float* x, int64_t n_rows, int row_len, int8_t* codes, float* scales,
+                      float* x_fq, void* stream) {
+    g_err[0] = 0;
+    if (n_rows < 0) return fail(PFA_ERR_INVALID_ARG, "n_rows must be >= 0");
+    if (row_len < 1 || row_len > (1 << 16))
+        return fail(PFA_ERR_INVALID_ARG, "row_len must be in 1..65536 (got %d)", row_len);
+    if (n_rows > (int64_t(1) << 40) / row_len)
+        return fail(PFA_ERR_UNSUPPORTED, "n_rows * row_len exceeds 2^40");
+    if (n_rows == 0) return PFA_OK;
+    if (!x || !codes || !scales) return fail(PFA_ERR_INVALID_ARG, "null tensor pointer");
+    const size_t n = (size_t)n_rows * row_len;
+    // x_fq may be x itself (in place); otherwise no buffer may overlap another
+    const Span sp[4] = {{x, n * 4, false, "x"},
+                        {codes, n, true, "codes"},
+                        {scales, (size_t)n_rows * 4, true, "scales"},
+                        {x_fq == x ? nullptr : x_fq, n * 4, true, "x_fq"}};
+    int rc = check_spans(sp, 4);
+    if (rc) return rc;
+    if (x_fq == x && (overlaps(x, n * 4, codes, n) || overlaps(x, n * 4, scales, n_rows * 4)))
+        return fail(PFA_ERR_INVALID_ARG, "codes and scales must not overlap x");
+    return hip_status(pfa::launch_quant_rows(x, n_rows, row_len, codes, scales, x_fq,
+                                             (hipStream_t)stream),
+                      "pfa_quantize_rows launch");
+}
+
+// Shared part of gqa_attn_q8 (store given) and qk_prep_attn_q8 (raw rows prepared,
+// quantised and appended to the caller's store first).
+static int attn_q8_common(bool fused, pfa::Q8Store in, const float* q, const float* k,
+                          const float* v, float* out, const float* gate, int gate_per_head,
+                          const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
+                          float scale, int causal, int window, const pfa::PrepParams* prep,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    const int T_q = st.off[st.n_seqs], T_kv = st.koff[st.n_seqs];
+    if (T_q == 0) return PFA_OK;
+    if (!out || !in.k || !in.ks || !in.v || !in.vs || (!fused && (!in.q || !in.qs)) ||
+        (fused && (!q || !k || !v)))
+        return fail(PFA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(in.k) || !aligned16(in.v) || (!fused && !aligned16(in.q)))
+        return fail(PFA_ERR_INVALID_ARG, "8-bit code arrays must be 16-byte aligned");
+    Plan p;
+    int rc;
+    if ((rc = make_plan(st, n_head, n_head_kv, head_dim, scale, causal, PFA_PREC_BF16, p)))
+        return rc;
+    if (p.items == 0) return PFA_OK;
+    p.geom.window = window;
+    p.geom.gate = gate;
+    p.geom.gate_per_head = gate_per_head ? 1 : 0;
+    const Q8Layout l = q8_layout(p, T_q, n_head, head_dim, fused);
+    if (!workspace)
+        return fail(PFA_ERR_INVALID_ARG, "the 8-bit attention needs a workspace (%zu bytes)",
+                    l.need);
+    if (workspace_bytes < l.need)
+        return fail(PFA_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    l.need);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+        return fail(PFA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t qrow = (size_t)T_q * n_head, krow = (size_t)T_kv * n_head_kv;
+    const size_t newk = (size_t)T_q * n_head_kv * head_dim;
+    const Span sp[12] = {
+        {out, qrow * head_dim * 4, true, "out"},
+        {gate, gate ? qrow * (gate_per_head ? 1 : head_dim) * 4 : 0, false, "gate"},
+        {workspace, l.need, true, "the workspace"},
+        {fused ? nullptr : in.q, qrow * head_dim, false, "q"},
+        {fused ? nullptr : in.qs, qrow * 4, false, "q_scale"},
+        {in.k, krow * head_dim, fused, "k_cache"},
+        {in.ks, krow * 4, fused, "k_scale"},
+        {in.v, krow * head_dim, fused, "v_cache"},
+        {in.vs, krow * 4, fused, "v_scale"},
+        {fused ? q : nullptr, qrow * head_dim * 4, false, "q"},
+        {fused ? k : nullptr, newk * 4, false, "k"},
+        {fused ? v : nullptr, newk * 4, false, "v"}};
+    if ((rc = check_spans(sp, 12))) return rc;
+    char* ws = static_cast<char*>(workspace);
+    pfa::Partials part{nullptr, nullptr};
+    if (p.part_bytes) {
+        const long long units =
+            (long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv;
+        part.o = reinterpret_cast<float*>(ws + l.part_off);
+        part.ml = reinterpret_cast<float2*>(ws + l.part_off +
+                                            (size_t)units * p.waves * 32 * head_dim * 4);
+    }
+    const char* what = fused ? "qk_prep_attn_q8 launch" : "gqa_attn_q8 launch";
+    if (fused) {
+        // the new rows: Q and K normalised and rotated at their positions, then Q (into
+        // the workspace), K and V (into the last rows of each sequence's store range)
+        // quantised
+        in.q = reinterpret_cast<int8_t*>(ws + l.qc_off);
+        in.qs = reinterpret_cast<float*>(ws + l.qs_off);
+        const pfa::Q8Rows rows{const_cast<int8_t*>(in.q), const_cast<float*>(in.qs),
+                               const_cast<int8_t*>(in.k), const_cast<float*>(in.ks),
+                               const_cast<int8_t*>(in.v), const_cast<float*>(in.vs)};
+        if ((rc = hip_status(pfa::launch_qknorm_rope_q8(q, k, v, prep->wq, prep->wk, st, T_q,
+                                                        n_head, n_head_kv, head_dim,
+                                                        prep->rope_dim, (float)prep->base,
+                                                        prep->eps, rows, (hipStream_t)stream),
+                             what)))
+            return rc;
+    }
+    return hip_status(pfa::launch_attn_q8(in, out, workspace, p.sched, p.geom, head_dim, part,
+                                          p.items, (hipStream_t)stream),
+                      what);
+}
+
+int gqa_attn_q8(const int8_t* q, const float* q_scale, const int8_t* k_cache,
+                const float* k_scale, const int8_t* v_cache, const float* v_scale, float* out,
+                const float* gate, int gate_per_head, const int32_t* q_offsets,
+                const int32_t* kv_offsets, int n_seqs, int T_q, int T_kv, int n_head,
+                int n_head_kv, int head_dim, float scale, int causal, int window,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T_q, n_head, n_head_kv, head_dim);
+    if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
+    if ((rc = check_q8_attn(scale)) || (rc = check_window(window, causal))) return rc;
+    pfa::SeqTable st;
+    if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) return rc;
+    if (T_q == 0) return PFA_OK;
+    const pfa::Q8Store in{q, q_scale, k_cache, k_scale, v_cache, v_scale};
+    return attn_q8_common(false, in, nullptr, nullptr, nullptr, out, gate, gate_per_head, st,
+                          n_head, n_head_kv, head_dim, scale, causal, window, nullptr, workspace,
+                          workspace_bytes, stream);
+}
+
+int qk_prep_attn_q8(const float* q, const float* k, const float* v, float* out,
+                    const float* gate, int gate_per_head, const float* q_norm_w,
+                    const float* k_norm_w, int8_t* k_cache, float* k_scale, int8_t* v_cache,
+                    float* v_scale, const int32_t* q_offsets, const int32_t* kv_offsets,
+                    int n_seqs, int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                    int rope_dim, float rope_freq_base, float rms_eps, float scale, int causal,
+                    int window, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T_q, n_head, n_head_kv, head_dim);
+    if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
+    if ((rc = check_q8_attn(scale)) || (rc = check_window(window, causal))) return rc;
+    if ((rc = check_rope(head_dim, rope_dim, rope_freq_base, rms_eps))) return rc;
+    pfa::SeqTable st;
+    if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) return rc;
+    if (T_q == 0) return PFA_OK;
+    if (!q_norm_w || !k_norm_w) return fail(PFA_ERR_INVALID_ARG, "null norm weights");
+    pfa::PrepParams prep{q_norm_w, k_norm_w, nullptr, rope_dim, rms_eps, (double)rope_freq_base};
+    const pfa::Q8Store in{nullptr, nullptr, k_cache, k_scale, v_cache, v_scale};
+    return attn_q8_common(true, in, q, k, v, out, gate, gate_per_head, st, n_head, n_head_kv,
+                          head_dim, scale, causal, window, &prep, workspace, workspace_bytes,
+                          stream);
 }
 
 }  // extern "C"

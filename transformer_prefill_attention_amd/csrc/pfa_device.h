@@ -50,6 +50,24 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
     return x;
 }
 
+// Max over the 64 lanes of a wavefront (every lane receives it).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+// 8-bit quantisation of a (token, head) row (needle-core v3/model.rs, `quant_rows` /
+// `quantize_rows`): the row's scale is its largest magnitude over 127, and a value's
+// code is the nearest integer to value / scale (ties to even) within -127..127; a row
+// of zeros has scale 0 and codes 0.  IEEE single-precision division, so the codes are
+// those of any correctly rounded implementation.
+__device__ __forceinline__ float quant8_scale(float amax) { return amax / 127.0f; }
+__device__ __forceinline__ int quant8(float x, float scale) {
+    const float c = scale > 0.0f ? __builtin_rintf(x / scale) : 0.0f;
+    return (int)fminf(fmaxf(c, -127.0f), 127.0f);
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {

@@ -92,6 +92,28 @@ struct PrepParams {
     double base;            // rotary frequency base
 };
 
+// An 8-bit store (needle-core v3/model.rs, the int8 K/V store of a quantised session):
+// int8 codes [rows, heads * D] and one f32 scale per (row, head), [rows, heads]; a value
+// is its code times its row's scale.  Q, K and V each have one.
+struct Q8Store {
+    const int8_t* q;
+    const float* qs;
+    const int8_t* k;
+    const float* ks;
+    const int8_t* v;
+    const float* vs;
+};
+// Outputs of the QK-norm + RoPE pass of a quantised session: Q codes per query row, K
+// and V codes per key row (as k_out / v_out of launch_qknorm_rope); null parts skipped.
+struct Q8Rows {
+    int8_t* q;
+    float* qs;
+    int8_t* k;
+    float* ks;
+    int8_t* v;
+    float* vs;
+};
+
 // Launchers (defined next to their kernels).  They only enqueue.
 // QK-norm + RoPE of T query-side rows (H = 0: K rows only).  K rows go to
 // k_out at the key rows the sequence table gives (the same rows for plain
@@ -100,6 +122,18 @@ hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out
                               const float* v_in, float* v_out, const float* wq, const float* wk,
                               const SeqTable& seqs, int T, int H, int Hkv, int D, int rope_dim,
                               float base, float eps, hipStream_t stream);
+
+// The same pass for a quantised session: Q and K normalised and rotated, then Q, K and V
+// quantised per (token, head) with 8 bits into `out` (nothing written in f32).
+hipError_t launch_qknorm_rope_q8(const float* q_in, const float* k_in, const float* v_in,
+                                 const float* wq, const float* wk, const SeqTable& seqs, int T,
+                                 int H, int Hkv, int D, int rope_dim, float base, float eps,
+                                 const Q8Rows& out, hipStream_t stream);
+
+// 8-bit quantisation of n_rows rows of len floats: codes, one scale per row and, when
+// deq is not null, the dequantised values (code x scale).
+hipError_t launch_quant_rows(const float* x, int64_t n_rows, int len, int8_t* codes,
+                             float* scales, float* deq, hipStream_t stream);
 
 // prep == nullptr: plain attention on already-normalised Q/K; otherwise the
 // fused entry (Q and K normalised and rotated inside the kernel).
@@ -132,4 +166,16 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
                             const PrepParams* prep, bool prep_k, const Partials& part,
                             int n_items, hipStream_t stream);
+
+// Attention through an 8-bit store, on the bf16 kernel: K codes go into the bf16 tiles
+// unchanged (|code| <= 127 is exact in bf16, and the MFMA sums of code products stay
+// exact integers in f32), each tile carries its 64 key scales after the V tiles, and V
+// is dequantised (code x scale, rounded to bf16) into its tiles.  The scores are the
+// integer dot products times the query and key row scales.
+inline size_t q8_scale_bytes(int n_tiles, int Hkv) {
+    return (size_t)n_tiles * Hkv * kBf16TileKeys * 4;
+}
+hipError_t launch_attn_q8(const Q8Store& st8, float* out, void* ws, const AttnSched& sched,
+                          const AttnGeom& geom, int D, const Partials& part, int n_items,
+                          hipStream_t stream);
 }  // namespace pfa

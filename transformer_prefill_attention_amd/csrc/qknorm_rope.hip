@@ -37,12 +37,12 @@ enum PairMode { kPairInLane = 0, kPairXor32 = 1, kPairGeneral = 2 };
 
 constexpr int kRowsInFlight = 4;  // head rows loaded before the first is reduced
 
-template <int D, int MODE>
+template <int D, int MODE, bool Q8>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const float* q_in, const float* k_in, float* q_out, float* k_out,
     const float* __restrict__ v_in, float* __restrict__ v_out,
     const float* __restrict__ wq, const float* __restrict__ wk, SeqTable seqs, int T, int H,
-    int Hkv, int n, double base, float eps, int groups) {
+    int Hkv, int n, double base, float eps, int groups, Q8Rows q8) {
     constexpr int E = D / 64;  // dims per lane
     const int lane = threadIdx.x & 63;
     const int half = n >> 1;
@@ -86,7 +86,23 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
             }
         }
 
-        auto do_rows = [&](const float* in, float* out, int nrows, const float* wv) {
+        // a finished row: f32 out, or (Q8) codes and the row's scale
+        auto store_row = [&](const float* o, float* out, int8_t* c8, float* s8) {
+            if constexpr (Q8) {
+                float m = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(o[e]));
+                const float sc = quant8_scale(wave_max(m));
+#pragma unroll
+                for (int e = 0; e < E; ++e) c8[lane + 64 * e] = (int8_t)quant8(o[e], sc);
+                if (lane == 0) *s8 = sc;
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) out[lane + 64 * e] = o[e];
+            }
+        };
+        auto do_rows = [&](const float* in, float* out, int8_t* c8, float* s8, int nrows,
+                           const float* wv) {
             for (int h0 = 0; h0 < nrows; h0 += kRowsInFlight) {
                 float x[kRowsInFlight][E];
 #pragma unroll
@@ -133,20 +149,39 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
                         for (int e = 0; e < E; ++e)
                             o[e] = rot[e] ? y[e] * cs[e] + sgn[e] * pv[e] * sn[e] : y[e];
                     }
-#pragma unroll
-                    for (int e = 0; e < E; ++e) out[(h0 + u) * D + lane + 64 * e] = o[e];
+                    store_row(o, Q8 ? nullptr : out + (h0 + u) * D,
+                              Q8 ? c8 + (h0 + u) * D : nullptr, Q8 ? s8 + h0 + u : nullptr);
                 }
             }
         };
         // rows [r0, r1) of (Q heads, then K heads)
-        if (r0 < H)
-            do_rows(q_in + ((int64_t)t * H + r0) * D, q_out + ((int64_t)t * H + r0) * D,
-                    min(r1, H) - r0, wqv);
+        if (r0 < H) {
+            const int64_t row = (int64_t)t * H + r0;
+            if constexpr (Q8)
+                do_rows(q_in + row * D, nullptr, q8.q + row * D, q8.qs + row, min(r1, H) - r0,
+                        wqv);
+            else
+                do_rows(q_in + row * D, q_out + row * D, nullptr, nullptr, min(r1, H) - r0, wqv);
+        }
         if (r1 > H) {
             const int k0 = max(r0, H) - H;
-            do_rows(k_in + ((int64_t)t * Hkv + k0) * D, k_out + ((int64_t)krow * Hkv + k0) * D,
-                    r1 - H - k0, wkv);
-            if (v_out) {
+            const int64_t row = (int64_t)krow * Hkv + k0;
+            if constexpr (Q8)
+                do_rows(k_in + ((int64_t)t * Hkv + k0) * D, nullptr, q8.k + row * D, q8.ks + row,
+                        r1 - H - k0, wkv);
+            else
+                do_rows(k_in + ((int64_t)t * Hkv + k0) * D, k_out + row * D, nullptr, nullptr,
+                        r1 - H - k0, wkv);
+            if (Q8 && q8.v) {
+                // V rows: quantised as given (no norm, no rotation)
+                for (int hh = 0; hh < r1 - H - k0; ++hh) {
+                    float x[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        x[e] = v_in[((int64_t)t * Hkv + k0 + hh) * D + lane + 64 * e];
+                    store_row(x, nullptr, q8.v + (row + hh) * D, q8.vs + row + hh);
+                }
+            } else if (v_out) {
                 const float* vs = v_in + ((int64_t)t * Hkv + k0) * D;
                 float* vd = v_out + ((int64_t)krow * Hkv + k0) * D;
                 for (int c = lane; c < (r1 - H - k0) * D; c += 64) vd[c] = vs[c];
@@ -155,11 +190,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool Q8>
 hipError_t launch_mode(const float* q_in, const float* k_in, float* q_out, float* k_out,
                        const float* v_in, float* v_out, const float* wq, const float* wk,
                        const SeqTable& seqs, int T, int H, int Hkv, int n, float base,
-                       float eps, hipStream_t stream) {
+                       float eps, const Q8Rows& q8, hipStream_t stream) {
     // Work units: tokens, or for short inputs runs of at least 4 head rows of a
     // token, so that ~8192 wavefronts (2048 workgroups of 4) have work.  Up to 4
     // units per wavefront so the per-lane rotary frequencies (f64 pow) are
@@ -170,21 +205,20 @@ hipError_t launch_mode(const float* q_in, const float* k_in, float* q_out, float
     const long long units = (long long)T * groups;
     int blocks = (int)std::min<long long>((units + 3) / 4, 2048);
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((qknorm_rope_kernel<D, MODE>), dim3(blocks), dim3(256), 0, stream, q_in,
-                       k_in, q_out, k_out, v_in, v_out, wq, wk, seqs, T, H, Hkv, n,
-                       (double)base, eps, groups);
+    hipLaunchKernelGGL((qknorm_rope_kernel<D, MODE, Q8>), dim3(blocks), dim3(256), 0, stream,
+                       q_in, k_in, q_out, k_out, v_in, v_out, wq, wk, seqs, T, H, Hkv, n,
+                       (double)base, eps, groups, q8);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
-                              const float* v_in, float* v_out, const float* wq, const float* wk,
-                              const SeqTable& seqs, int T, int H, int Hkv, int D, int rope_dim,
-                              float base, float eps, hipStream_t stream) {
+template <bool Q8>
+hipError_t launch_any(const float* q_in, const float* k_in, float* q_out, float* k_out,
+                      const float* v_in, float* v_out, const float* wq, const float* wk,
+                      const SeqTable& seqs, int T, int H, int Hkv, int D, int rope_dim,
+                      float base, float eps, const Q8Rows& q8, hipStream_t stream) {
 #define PFA_QKN(DD, MM)                                                                         \
-    launch_mode<DD, MM>(q_in, k_in, q_out, k_out, v_in, v_out, wq, wk, seqs, T, H, Hkv, rope_dim, \
-                        base, eps, stream)
+    launch_mode<DD, MM, Q8>(q_in, k_in, q_out, k_out, v_in, v_out, wq, wk, seqs, T, H, Hkv,     \
+                            rope_dim, base, eps, q8, stream)
     if (D == 128) {
         if (rope_dim == 128) return PFA_QKN(128, kPairInLane);
         if (rope_dim == 64) return PFA_QKN(128, kPairXor32);
@@ -194,6 +228,24 @@ hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out
     if (rope_dim == 64) return PFA_QKN(64, kPairXor32);
     return PFA_QKN(64, kPairGeneral);
 #undef PFA_QKN
+}
+
+}  // namespace
+
+hipError_t launch_qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
+                              const float* v_in, float* v_out, const float* wq, const float* wk,
+                              const SeqTable& seqs, int T, int H, int Hkv, int D, int rope_dim,
+                              float base, float eps, hipStream_t stream) {
+    return launch_any<false>(q_in, k_in, q_out, k_out, v_in, v_out, wq, wk, seqs, T, H, Hkv, D,
+                             rope_dim, base, eps, Q8Rows{}, stream);
+}
+
+hipError_t launch_qknorm_rope_q8(const float* q_in, const float* k_in, const float* v_in,
+                                 const float* wq, const float* wk, const SeqTable& seqs, int T,
+                                 int H, int Hkv, int D, int rope_dim, float base, float eps,
+                                 const Q8Rows& out, hipStream_t stream) {
+    return launch_any<true>(q_in, k_in, nullptr, nullptr, v_in, nullptr, wq, wk, seqs, T, H, Hkv,
+                            D, rope_dim, base, eps, out, stream);
 }
 
 }  // namespace pfa

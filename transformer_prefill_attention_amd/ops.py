@@ -28,6 +28,7 @@ _PRECISIONS = {"f32": PRECISION_F32, "fp32": PRECISION_F32, "float32": PRECISION
 # Every symbol include/pfa.h declares.
 EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_workspace_bytes",
            "gqa_chunk_attn", "qk_prep_chunk_attn", "pfa_chunk_workspace_bytes",
+           "pfa_quantize_rows", "gqa_attn_q8", "qk_prep_attn_q8", "pfa_q8_workspace_bytes",
            "pfa_last_error", "pfa_version")
 
 
@@ -73,6 +74,18 @@ def lib() -> ctypes.CDLL:
     L.pfa_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_chunk_workspace_bytes.restype = sz
     L.pfa_last_error.restype = ctypes.c_char_p
+    i64 = ctypes.c_int64
+    L.pfa_quantize_rows.argtypes = [vp, i64, i32, vp, vp, vp, vp]
+    L.pfa_quantize_rows.restype = i32
+    L.gqa_attn_q8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
+                              i32, i32, f32, i32, i32, vp, sz, vp]
+    L.gqa_attn_q8.restype = i32
+    L.qk_prep_attn_q8.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                  i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, i32, vp, sz,
+                                  vp]
+    L.qk_prep_attn_q8.restype = i32
+    L.pfa_q8_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32]
+    L.pfa_q8_workspace_bytes.restype = sz
     L.pfa_last_error.argtypes = []
     L.pfa_version.restype = ctypes.c_char_p
     L.pfa_version.argtypes = []
@@ -368,4 +381,140 @@ def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_di
                                     T_q, T_kv, H, Hkv, head_dim, rope_dim, float(rope_freq_base),
                                     float(rms_eps), float(scale), 1 if causal else 0,
                                     int(window), prec, wp, wn, _stream(q)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 8-bit quantised sessions: stores are (codes int8 [rows, heads*head_dim], scales f32
+# [rows, heads]) pairs of GPU tensors.
+
+def _dev(t, name, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _store(codes, scales, head_dim, name):
+    """(rows, heads) of an 8-bit store, checked."""
+    import torch
+    _dev(codes, f"{name} codes", torch.int8)
+    _dev(scales, f"{name} scales", torch.float32)
+    rows, heads = _heads(codes, head_dim, f"{name} codes")
+    if scales.numel() != rows * heads:
+        raise ValueError(f"{name} scales must be [rows, heads] = [{rows}, {heads}]")
+    return rows, heads
+
+
+def quantize_rows(x, row_len: int, *, codes=None, scales=None, x_fq=None):
+    """8-bit quantisation of every ``row_len`` values of ``x`` (``pfa_quantize_rows`` in
+    ``include/pfa.h``); returns ``(codes, scales)``.  ``x_fq``: optional output of the
+    fake-quantised values (may be ``x`` for in place)."""
+    import torch
+    _dev_f32(x, "x")
+    if x.numel() % row_len:
+        raise ValueError("x does not hold whole rows")
+    n = x.numel() // row_len
+    codes = torch.empty(x.shape, dtype=torch.int8, device=x.device) if codes is None else \
+        _dev(codes, "codes", torch.int8)
+    scales = torch.empty(n, dtype=torch.float32, device=x.device) if scales is None else \
+        _dev(scales, "scales", torch.float32)
+    if codes.numel() != x.numel() or scales.numel() != n:
+        raise ValueError("codes must have x's size and scales one value per row")
+    if x_fq is not None:
+        _dev_f32(x_fq, "x_fq")
+        if x_fq.numel() != x.numel():
+            raise ValueError("x_fq must have x's size")
+    _check(lib().pfa_quantize_rows(_ptr(x), n, int(row_len), _ptr(codes), _ptr(scales),
+                                   _ptr(x_fq), _stream(x)))
+    return codes, scales
+
+
+def q8_workspace_bytes(T_q: int, T_kv: int, n_head: int, n_head_kv: int, head_dim: int,
+                       q_offsets=None, kv_offsets=None, fused: bool = False) -> int:
+    """Device workspace ``gqa_attn_q8`` (``fused=False``) or ``qk_prep_attn_q8``
+    (``fused=True``) uses (``pfa_q8_workspace_bytes``)."""
+    keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
+    return int(lib().pfa_q8_workspace_bytes(qp, kp, n_seqs, T_q, T_kv, n_head, n_head_kv,
+                                            head_dim, 1 if fused else 0))
+
+
+def _q8_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, fused, device):
+    import torch
+    need = int(lib().pfa_q8_workspace_bytes(qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim,
+                                            1 if fused else 0))
+    if need == 0:
+        return None, ctypes.c_void_p(0), 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    elif not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+        raise TypeError("workspace must be a GPU torch.Tensor")
+    return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def gqa_attn_q8(q, q_scale, k_cache, k_scale, v_cache, v_scale, *, head_dim: int,
+                scale: Optional[float] = None, causal: bool = True, window: int = 0, gate=None,
+                q_offsets=None, kv_offsets=None, out=None, workspace=None):
+    """Attention through 8-bit stores (``gqa_attn_q8`` in ``include/pfa.h``); returns
+    ``out`` (f32).  Offsets, window and gate as for :func:`gqa_chunk_attn`."""
+    import torch
+    T_q, H = _store(q, q_scale, head_dim, "q")
+    T_kv, Hkv = _store(k_cache, k_scale, head_dim, "k_cache")
+    if _store(v_cache, v_scale, head_dim, "v_cache") != (T_kv, Hkv):
+        raise ValueError("k and v stores must have the same shape")
+    out = torch.empty((T_q, H * head_dim), dtype=torch.float32, device=q.device) \
+        if out is None else _dev_f32(out, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = head_dim ** -0.5
+    keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
+    ws, wp, wn = _q8_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, False,
+                               q.device)
+    gp, gh = _gate(gate, T_q, H, head_dim)
+    _check(lib().gqa_attn_q8(_ptr(q), _ptr(q_scale), _ptr(k_cache), _ptr(k_scale),
+                             _ptr(v_cache), _ptr(v_scale), _ptr(out), gp, gh, qp, kp, n_seqs,
+                             T_q, T_kv, H, Hkv, head_dim, float(scale), 1 if causal else 0,
+                             int(window), wp, wn, _stream(q)))
+    return out
+
+
+def qk_prep_attn_q8(q, k, v, q_norm_w, k_norm_w, k_cache, k_scale, v_cache, v_scale, *,
+                    head_dim: int, rope_dim: int, rope_freq_base: float, rms_eps: float,
+                    scale: Optional[float] = None, causal: bool = True, window: int = 0,
+                    gate=None, q_offsets=None, kv_offsets=None, out=None, workspace=None):
+    """A quantised session's step (``qk_prep_attn_q8`` in ``include/pfa.h``): QK-norm +
+    RoPE of the raw new rows, Q, K and V quantised per (token, head), K and V appended
+    to the 8-bit store (the last rows of each sequence's range), attention through the
+    store; returns ``out`` (f32)."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        _dev_f32(t, n)
+    T_q, H = _heads(q, head_dim, "q")
+    Tk, Hkv = _heads(k, head_dim, "k")
+    if Tk != T_q or v.shape != k.shape:
+        raise ValueError("q, k, v must have the same token count and k, v the same shape")
+    T_kv, Hc = _store(k_cache, k_scale, head_dim, "k_cache")
+    if Hc != Hkv or _store(v_cache, v_scale, head_dim, "v_cache") != (T_kv, Hkv):
+        raise ValueError("the K and V stores must be [T_kv, n_head_kv*head_dim] like k")
+    out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = head_dim ** -0.5
+    keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
+    ws, wp, wn = _q8_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, True,
+                               q.device)
+    gp, gh = _gate(gate, T_q, H, head_dim)
+    _check(lib().qk_prep_attn_q8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), gp, gh, _ptr(q_norm_w),
+                                 _ptr(k_norm_w), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+                                 _ptr(v_scale), qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim,
+                                 rope_dim, float(rope_freq_base), float(rms_eps), float(scale),
+                                 1 if causal else 0, int(window), wp, wn, _stream(q)))
     return out
