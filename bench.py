@@ -29,7 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "causal GQA prefill attention TFLOP/s (and % of MFMA peak) at T=512..16384"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "bf16x3": 2500.0}   # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "bf16x3": 2500.0,
+               "int8": 5000.0}   # MI355X dense MFMA peaks (int8: TOP/s)
 HBM_PEAK_GBS = 8000.0
 
 
@@ -224,14 +225,15 @@ def main():
         split = "true" if args.precision == "bf16x3" else "false"
         fused = "true" if args.path == "fused" else "false"
         kernel = (f"stage_kv_bf16_kernel<{w.head_dim},{split},{fused}> + "
-                  f"attn_bf16_kernel<{w.head_dim},{split},{fused}>")
+                  f"attn_bf16_kernel<{w.head_dim},{split},{fused},false>")
         if args.path == "fused":
             kernel = f"rope_table_kernel<{w.head_dim},{split}> + " + kernel
     elif args.path == "fused":
         # the f32 fused entry: K prepared once (QK-norm + RoPE over the K rows), then
         # the attention kernel preparing its own Q rows
         mode = 0 if w.rope_dim == w.head_dim == 128 else (1 if w.rope_dim == 64 else 2)
-        kernel = f"qknorm_rope_kernel<{w.head_dim},{mode}> + attn_f32_kernel<{w.head_dim},true>"
+        kernel = (f"qknorm_rope_kernel<{w.head_dim},{mode},false> + "
+                  f"attn_f32_kernel<{w.head_dim},true>")
     else:
         kernel = f"attn_f32_kernel<{w.head_dim},false>"
     traffic = load_traffic(w.name, kernel, args.precision, args.path)
@@ -326,16 +328,16 @@ def run_chunk(args, w, x):
     peak = PEAK_TFLOPS[args.precision]
     d = w.head_dim
     if args.precision == "f32":
-        kernel = (f"qknorm_rope_kernel<{d},0> + attn_f32_kernel<{d},true>" if args.path == "fused"
-                  else f"attn_f32_kernel<{d},false>")
+        kernel = (f"qknorm_rope_kernel<{d},0,false> + attn_f32_kernel<{d},true>"
+                  if args.path == "fused" else f"attn_f32_kernel<{d},false>")
     else:
         split = "true" if args.precision == "bf16x3" else "false"
         kernel = f"stage_kv_bf16_kernel<{d},{split},false> + "
         if args.path == "fused":
-            kernel = (f"qknorm_rope_kernel<{d},0> + rope_table_kernel<{d},{split}> + " + kernel +
-                      f"attn_bf16_kernel<{d},{split},true>")
+            kernel = (f"qknorm_rope_kernel<{d},0,false> + rope_table_kernel<{d},{split}> + " +
+                      kernel + f"attn_bf16_kernel<{d},{split},true,false>")
         else:
-            kernel += f"attn_bf16_kernel<{d},{split},false>"
+            kernel += f"attn_bf16_kernel<{d},{split},false,false>"
     res = {
         "metric": METRIC, "value": round(flops / (elapsed / args.steps) / 1e12, 3),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -426,11 +428,18 @@ def run_q8(args, w, x):
     flops = 4 * d * w.n_head * pairs
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     achieved = flops / (kern_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS["bf16"]
-    kernel = f"stage_kv_q8_kernel<{d}> + attn_bf16_kernel<{d},false,false,true>"
+    # head_dim 128: Q.K^T on int8 matrix cores (5.0 POP/s dense), P.V on bf16 (2.5 PF):
+    # half the FLOPs each, so the least time is F/2 (1/5000 + 1/2500) -> a 3333 TFLOP/s
+    # peak for the whole; head_dim 64 runs both products on bf16
+    peak = (2.0 / (1.0 / PEAK_TFLOPS["int8"] + 1.0 / PEAK_TFLOPS["bf16"]) if d == 128
+            else PEAK_TFLOPS["bf16"])
+    kernel = (f"stage_kv_q8_kernel<{d},{'true' if d == 128 else 'false'}> + "
+              f"attn_bf16_kernel<{d},false,false,true>")
     if args.path == "fused":
         kernel = f"qknorm_rope_kernel<{d},0,true> + " + kernel
     what = (f"{T_q} new rows over {B} stored rows" if B else f"prefill of {T} rows")
+    traffic = None if (B or args.window or gate is not None) else \
+        load_traffic(w.name, kernel, "q8", args.path)
     res = {
         "metric": METRIC, "value": round(flops / (elapsed / args.steps) / 1e12, 3),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -445,7 +454,7 @@ def run_q8(args, w, x):
                    "T_q": T_q, "T_kv": T, "n_head": w.n_head, "n_head_kv": w.n_head_kv,
                    "head_dim": d, "path": args.path, "causal_flops": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": kernel, "kernel_ms": round(kern_ms, 4)},
     }
     print(json.dumps(res), flush=True)

@@ -310,10 +310,10 @@ int pfa_quantize_rows(const float* x, int64_t n_rows, int row_len, int8_t* codes
  *  gate, gate_per_head, q_offsets, kv_offsets, n_seqs, causal, window  as for
  *        gqa_chunk_attn.
  *  scale  finite and > 0 (the row scales are applied inside the exponent).
- *  The products run on bf16 matrix cores: codes are exact in bf16 and every
- *  partial sum of code products is an integer below 2^24, so the integer scores
- *  are exact; V is dequantised and rounded to bf16, and the weights are rounded
- *  to bf16, as in PFA_PREC_BF16.
+ *  The scores are exact integer dot products (int8 matrix cores for head_dim 128;
+ *  for 64, codes in bf16 on bf16 matrix cores, where every partial sum is an
+ *  integer below 2^24); V is dequantised and rounded to bf16, and the weights are
+ *  rounded to bf16, as in PFA_PREC_BF16.
  *  workspace  device, 256-byte aligned, pfa_q8_workspace_bytes(..., 0) bytes.
  */
 int gqa_attn_q8(const int8_t* q, const float* q_scale, const int8_t* k_cache,
@@ -347,10 +347,11 @@ int qk_prep_attn_q8(const float* q, const float* k, const float* v, float* out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace in bytes of gqa_attn_q8 (fused = 0) or qk_prep_attn_q8
- * (fused = 1): bf16 K/V tiles over each sequence's store rows (sum_s
- * ceil(kv_len_s / 64) tiles of 2 * 64 * head_dim * 2 bytes per K/V head) and 256
- * bytes of key scales per tile and head, (fused) the Q codes and scales, and the
- * key split's partial results.  0 when T_q == 0 or the arguments would be
+ * (fused = 1): K/V tiles over each sequence's store rows (sum_s ceil(kv_len_s /
+ * 64) tiles per K/V head, each 64 * head_dim bytes of K codes for head_dim 128 or
+ * 64 * head_dim * 2 of bf16 K for 64, plus 64 * head_dim * 2 of bf16 V), 256 bytes
+ * of key scales per tile and head, (fused) the Q codes and scales, and the key
+ * split's partial results.  0 when T_q == 0 or the arguments would be
  * rejected (pfa_last_error() then says why). */
 size_t pfa_q8_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
                               int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,

@@ -359,11 +359,14 @@ def _q8_ws(L, q_lens, kv_lens, H, Hkv, D, fused):
     ((8192,), (8192,), 32, 8, 128), ((1024,), (8192,), 32, 8, 128), ((512,), (512,), 16, 8, 128),
     ((50, 1, 130, 0), (70, 78, 130, 5), 8, 4, 128), ((90,), (135,), 4, 2, 64)])
 def test_q8_workspace_rule(L, q_lens, kv_lens, H, Hkv, D, fused):
-    # the bf16 plan's tiles, 256 bytes of key scales per tile and K/V head, (fused) the Q
-    # codes and scales, each part 256-byte aligned, then the bf16 plan's partial results
+    # K tiles (int8 codes for head_dim 128, bf16 for 64) and bf16 V tiles, 256 bytes of
+    # key scales per tile and K/V head, (fused) the Q codes and scales, each part 256-byte
+    # aligned, then the bf16 plan's partial results
     bf16_chunk = _expected_workspace(q_lens, H, Hkv, D, 1, 0, kv_lens=kv_lens, chunk=True)
-    tiles = Hkv * sum(_ceil(n, 64) for n in kv_lens) * 64 * D * 2 * 2
-    parts = bf16_chunk - _ceil(tiles, 256) * 256 if bf16_chunk > tiles else 0
+    bf16_tiles = Hkv * sum(_ceil(n, 64) for n in kv_lens) * 64 * D * 2 * 2
+    parts = bf16_chunk - _ceil(bf16_tiles, 256) * 256 if bf16_chunk > bf16_tiles else 0
+    n_t = Hkv * sum(_ceil(n, 64) for n in kv_lens)
+    tiles = n_t * (64 * D * (1 if D == 128 else 2) + 64 * D * 2)
     end = tiles + Hkv * sum(_ceil(n, 64) for n in kv_lens) * 256
     if fused:
         T_q = sum(q_lens)

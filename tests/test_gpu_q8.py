@@ -9,8 +9,9 @@ per (token, head) with 8 bits after RoPE; attention through the int8 store).
   quantised unit-variance rows, a +-127 code in every row, scales near 0.022), element
   by element at small sizes (prefill, ragged and tile-aligned prefixes, one new row,
   packed sequences, head_dim 64, a long prefix that takes the key split), non-causal, a
-  sliding window and a gated output; the tolerance is the bf16 path's, since V is
-  dequantised to bf16 and the weights are rounded to bf16 (the integer scores are exact).
+  sliding window and a gated output; the tolerance is the bf16 path's max-abs gate plus a
+  relative-L2 bound of 4e-3, since V is dequantised to bf16 and the weights are rounded to
+  bf16 (2^-9 relative each; the integer scores are exact).
 * The fused step: raw rows normalised and rotated, quantised and appended to the store.
   V codes and scales are exact; a Q or K code may differ by one from the oracle's only
   where the oracle's value / scale lies within 1e-3 of a rounding tie (the two sides
@@ -24,7 +25,7 @@ import torch
 import oracle
 import transformer_prefill_attention_amd as pfa
 from transformer_prefill_attention_amd import workloads as wl
-from tests.helpers import assert_bf16_parity
+from tests.helpers import assert_q8_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -115,20 +116,20 @@ class Store:
 @pytest.mark.parametrize("name", list(CASES))
 def test_q8_attention_parity(name):
     st = Store(name, *CASES[name])
-    assert_bf16_parity(st.gpu(), st.ref(), f"gqa_attn_q8 {name}")
+    assert_q8_parity(st.gpu(), st.ref(), f"gqa_attn_q8 {name}")
 
 
 @pytest.mark.parametrize("name", ["ragged_prefix", "packed"])
 def test_q8_attention_non_causal(name):
     st = Store(name, *CASES[name])
-    assert_bf16_parity(st.gpu(causal=False), st.ref(causal=False), f"gqa_attn_q8 {name} nc")
+    assert_q8_parity(st.gpu(causal=False), st.ref(causal=False), f"gqa_attn_q8 {name} nc")
 
 
 @pytest.mark.parametrize("name,window", [("tile_aligned", 64), ("ragged_prefix", 1),
                                          ("packed", 33), ("long_prefix", 700)])
 def test_q8_attention_window(name, window):
     st = Store(name, *CASES[name])
-    assert_bf16_parity(st.gpu(window=window), st.ref(window=window),
+    assert_q8_parity(st.gpu(window=window), st.ref(window=window),
                        f"gqa_attn_q8 {name} window {window}")
 
 
@@ -139,7 +140,7 @@ def test_q8_attention_gate(name, per_head):
     T_q = int(st.q_offs[-1])
     g = 2.0 * np.random.default_rng(5).standard_normal(
         (T_q, st.H) if per_head else (T_q, st.H * st.d)).astype(np.float32)
-    assert_bf16_parity(st.gpu(gate=g), st.ref(gate=g), f"gqa_attn_q8 {name} gate")
+    assert_q8_parity(st.gpu(gate=g), st.ref(gate=g), f"gqa_attn_q8 {name} gate")
 
 
 def test_q8_attention_zero_query_row():
@@ -148,7 +149,7 @@ def test_q8_attention_zero_query_row():
     st.qc[5] = 0
     st.qs[5] = 0.0
     got, ref = st.gpu(), st.ref()
-    assert_bf16_parity(got, ref, "gqa_attn_q8 zero query row")
+    assert_q8_parity(got, ref, "gqa_attn_q8 zero query row")
 
 
 # ---------------------------------------------------------------------------
@@ -209,7 +210,7 @@ def test_qk_prep_attn_q8_parity(lens, bases, H, Hkv, d, n):
                                pos0=(kv_offs[1:] - kv_offs[:-1]) - (q_offs[1:] - q_offs[:-1]))
     np.testing.assert_allclose(gks[new], rks[new], rtol=4e-6, atol=0)
     _near_tie_ok(gkc[new], rkc[new], kn.astype(np.float32), rks[new], d, "K codes")
-    assert_bf16_parity(out.cpu().numpy(), ref, "qk_prep_attn_q8")
+    assert_q8_parity(out.cpu().numpy(), ref, "qk_prep_attn_q8")
 
 
 def test_qk_prep_attn_q8_bench_shape_sampled():
@@ -230,4 +231,4 @@ def test_qk_prep_attn_q8_bench_shape_sampled():
                                  n_head_kv=8, head_dim=128, rope_dim=128, rope_freq_base=1e6,
                                  rms_eps=float(np.float32(1e-6)), scale=w.softmax_scale,
                                  rows=rows)[0]
-    assert_bf16_parity(out.cpu().numpy()[rows], ref, "qk_prep_attn_q8 prefill_8192 sampled")
+    assert_q8_parity(out.cpu().numpy()[rows], ref, "qk_prep_attn_q8 prefill_8192 sampled")

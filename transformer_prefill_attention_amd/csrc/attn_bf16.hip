@@ -41,6 +41,16 @@
 // for a cache), and the attention kernel does the same to its Q rows once, in its
 // prologue.  The normalised Q and K never go to HBM except for that optional copy.
 //
+// Q8 = true reads an 8-bit store (needle-core v3/model.rs: a quantised session's int8
+// K/V store, one scale per row; launch_attn_q8): Q arrives as codes and the softmax
+// scale, log2(e) and the row's Q scale stay in one register qf.  With head_dim 128 the
+// K tiles hold int8 codes and the scores come from v_mfma_i32_32x32x32_i8 (half the
+// matrix-core time of the bf16 product, half the K tile bytes); with 64, codes sit in
+// bf16 K tiles (exact) on the bf16 MFMA.  Either way the integer scores are exact.  The
+// 64 key scales of a tile ride with its K tile into a ring of four LDS slots, and the X
+// phase computes score = s_int * k_scale, weight = 2^(score * qf - m).  V tiles are
+// dequantised by the staging kernel, so P.V is unchanged.
+//
 // SPLIT = true is the PFA_PREC_BF16X3 mode: Q and K are each split into a bf16
 // high part and a bf16 low part (x = hi + lo to ~2^-17) and the scores take the
 // three products hi.hi + hi.lo + lo.hi, so score rounding no longer grows with
@@ -56,6 +66,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBN = kBf16TileKeys;  // keys per tile (64)
 constexpr int kWaves = 8;
@@ -311,17 +323,20 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// An 8-bit store -> bf16 tiles (needle-core v3/model.rs: the int8 K/V store of a
-// quantised session, each row its codes and one scale).  Same tiles as above: K
-// codes converted unchanged (exact in bf16), V dequantised (code x its row's
-// scale, rounded to bf16).  The tile's 64 key scales (0 past the end of the
-// sequence) go to ks_ws[(kv head, tile)][64]: the attention kernel multiplies the
-// integer scores by them.
-template <int D>
-__global__ __launch_bounds__(256) void stage_kv_q8_kernel(Q8Store q8, __bf16* __restrict__ ws,
+// An 8-bit store -> tiles (needle-core v3/model.rs: the int8 K/V store of a
+// quantised session, each row its codes and one scale).  V is dequantised (code x
+// its row's scale, rounded to bf16) into the V tiles above.  K: with I8 the codes
+// stay int8, 64 rows x D bytes with the 16-byte chunks of a row swizzled as the
+// V^T rows are (the operand of v_mfma_i32_32x32x32_i8); otherwise they are
+// converted unchanged into the bf16 K tiles above (exact in bf16).  The tile's 64
+// key scales (0 past the end of the sequence) go to ks_ws[(kv head, tile)][64]:
+// the attention kernel multiplies the integer scores by them.
+template <int D, bool I8>
+__global__ __launch_bounds__(256) void stage_kv_q8_kernel(Q8Store q8, unsigned char* __restrict__ wsb,
                                                           float* __restrict__ ks_ws,
                                                           AttnSched sched, int Hkv) {
     constexpr int NCH = D / 8;
+    constexpr int KT = I8 ? kBN * D : kBN * D * 2;  // K tile bytes
     __shared__ __attribute__((aligned(16))) __bf16 vts[D * kVts];
     const int tid = threadIdx.x;
     const int kv = blockIdx.x % Hkv;
@@ -331,8 +346,9 @@ __global__ __launch_bounds__(256) void stage_kv_q8_kernel(Q8Store q8, __bf16* __
     const int k0 = sched.koff[s] + (gt - sched.tile_off[s]) * kBN;  // the tile's key rows
     const int nval = min(kBN, sched.koff[s + 1] - k0);
     const int64_t row_stride = (int64_t)Hkv * D;
-    __bf16* kt = ws + ((int64_t)kv * n_tiles + gt) * (kBN * D);
-    __bf16* vt = ws + (int64_t)Hkv * n_tiles * (kBN * D) + ((int64_t)kv * n_tiles + gt) * (kBN * D);
+    unsigned char* ktb = wsb + ((int64_t)kv * n_tiles + gt) * KT;
+    __bf16* vt = reinterpret_cast<__bf16*>(wsb + (int64_t)Hkv * n_tiles * KT) +
+                 ((int64_t)kv * n_tiles + gt) * (kBN * D);
     const int8_t* kin = q8.k + (int64_t)k0 * row_stride + kv * D;
     const int8_t* vin = q8.v + (int64_t)k0 * row_stride + kv * D;
     if (tid < kBN)
@@ -362,16 +378,28 @@ __global__ __launch_bounds__(256) void stage_kv_q8_kernel(Q8Store q8, __bf16* __
             *reinterpret_cast<bf16x4*>(vts + (d0 + c) * kVts + key0) = x;
         }
     }
-    // K: 8 codes (one 16-byte bf16 chunk) per step, to their swizzled place
-    for (int i = tid; i < kBN * NCH; i += 256) {
-        const int r = i / NCH, c = i % NCH;
-        bf16x8 x;
-        const uint2 w = r < nval ? *reinterpret_cast<const uint2*>(kin + r * row_stride + 8 * c)
-                                 : uint2{0u, 0u};
+    if constexpr (I8) {
+        // K: 16-byte chunks of codes, copied to their swizzled place
+        constexpr int NC16 = D / 16;
+        for (int i = tid; i < kBN * NC16; i += 256) {
+            const int r = i / NC16, c = i % NC16;
+            const uint4 w = r < nval ? *reinterpret_cast<const uint4*>(kin + r * row_stride + 16 * c)
+                                     : uint4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<uint4*>(ktb + r * D + 16 * swz(r, c, NC16)) = w;
+        }
+    } else {
+        // K: 8 codes (one 16-byte bf16 chunk) per step, to their swizzled place
+        __bf16* kt = reinterpret_cast<__bf16*>(ktb);
+        for (int i = tid; i < kBN * NCH; i += 256) {
+            const int r = i / NCH, c = i % NCH;
+            bf16x8 x;
+            const uint2 w = r < nval ? *reinterpret_cast<const uint2*>(kin + r * row_stride + 8 * c)
+                                     : uint2{0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            x[e] = (__bf16)(float)(int8_t)((e < 4 ? w.x : w.y) >> (8 * (e & 3)));
-        *reinterpret_cast<bf16x8*>(kt + r * D + 8 * swz(r, c, NCH)) = x;
+            for (int e = 0; e < 8; ++e)
+                x[e] = (__bf16)(float)(int8_t)((e < 4 ? w.x : w.y) >> (8 * (e & 3)));
+            *reinterpret_cast<bf16x8*>(kt + r * D + 8 * swz(r, c, NCH)) = x;
+        }
     }
     __syncthreads();
     store_vt_rows<D>(vts, vt, tid);
@@ -386,10 +414,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                                                                 PrepParams prep, Partials part,
                                                                 Q8Store q8) {
     constexpr int KP = SPLIT ? 2 : 1;
-    constexpr int NCH = D / 8;            // 16-byte chunks per K row
-    constexpr int KT = KP * kBN * D * 2;  // K tile bytes
+    // Q8 with head_dim 128: int8 K tiles and v_mfma_i32_32x32x32_i8 scores
+    constexpr bool I8 = Q8 && D == 128;
+    constexpr int NCH = D / 8;            // 16-byte chunks per bf16 K row
+    constexpr int KT = I8 ? kBN * D : KP * kBN * D * 2;  // K tile bytes
     constexpr int VT = kBN * D * 2;       // V tile bytes
-    constexpr int NQS = D / 16;           // MFMA steps of K Q^T
+    constexpr int NQS = D / 16;           // MFMA steps of K Q^T (bf16)
+    constexpr int NQ8 = D / 32;           // MFMA steps of K Q^T (int8)
     constexpr int NCB = D / 32;           // 32-row blocks of O^T
     constexpr int QS = D + 4;             // f32 row stride of the epilogue staging
     constexpr int K_LOADS = KT / (kThreads * 16);  // 16-byte direct loads per thread
@@ -450,7 +481,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     // scores and applied in the exponent (clamped above 0: a row of zero codes has
     // scores 0, and hidden keys stay -inf)
     float qf = 0.0f;
-    if constexpr (Q8) {
+    intx4 qop8[I8 ? NQ8 : 1];
+    if constexpr (I8) {
+        // codes of Q[qi][hl*D/2 + 16s + j], j = 0..15, for int8 step s
+        const bool ok = active && qi < s1;
+        const int8_t* src = q8.q + ((int64_t)(ok ? qi : s0) * H + h) * D + hl * (D / 2);
+#pragma unroll
+        for (int s = 0; s < NQ8; ++s)
+            qop8[s] = ok ? *reinterpret_cast<const intx4*>(src + 16 * s) : intx4{0, 0, 0, 0};
+        qf = fmaxf((ok ? q8.qs[(int64_t)qi * H + h] : 0.0f) * qscale, 1e-30f);
+    } else if constexpr (Q8) {
         // codes of Q[qi][hl*D/2 + 8s + e], exact in bf16
         const bool ok = active && qi < s1;
         const int8_t* src = q8.q + ((int64_t)(ok ? qi : s0) * H + h) * D + hl * (D / 2);
@@ -585,9 +625,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                                   (int64_t)Hkv * n_all * KT +
                                   ((int64_t)kv * n_all + tile0 + t_begin) * VT;
     // K operand of step s, key block 0: row ln, chunk hl*NCH/2 + s (block 1: +32 rows)
+    // (int8 tiles: row ln, 16-byte chunk hl*D/32 + s of the D-byte row, block 1: +32 rows)
     uint32_t kaddr[NQS];
 #pragma unroll
-    for (int s = 0; s < NQS; ++s) kaddr[s] = ln * (D * 2) + 16 * swz(ln, hl * (NCH / 2) + s, NCH);
+    for (int s = 0; s < NQS; ++s)
+        kaddr[s] = I8 ? (s < NQ8 ? ln * D + 16 * swz(ln, hl * (D / 32) + s, D / 16) : 0)
+                      : ln * (D * 2) + 16 * swz(ln, hl * (NCH / 2) + s, NCH);
     // V^T operand of step s, row block 0: row ln, key group 2s + hl (block cb: +32cb rows)
     uint32_t vaddr[4];
 #pragma unroll
@@ -628,6 +671,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.0f;
     floatx16 sacc[2];
+    intx16 sacc8[I8 ? 2 : 1];   // int8 scores (I8), converted in the X phase
     bf16x8 pop[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -644,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     auto m_phase = [&](auto par_) {
         constexpr int PAR = decltype(par_)::value;
         constexpr int NPV = 4 * NCB;        // P.V: step s = i / NCB, block cb = i % NCB
-        constexpr int NQK = 2 * NQS * KP;   // K.Q^T: step s, key block kb, part
+        constexpr int NQK = I8 ? 2 * NQ8 : 2 * NQS * KP;  // K.Q^T: step s, key block kb, part
         constexpr int N = NPV + NQK;
         constexpr int kAhead = 4;
         const unsigned char* vb = smem + (PAR ^ 1) * VT;  // vaddr holds the V region offset
@@ -654,6 +698,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 return *reinterpret_cast<const bf16x8*>(vb + vaddr[i / NCB] +
                                                         (i % NCB) * 32 * kBN * 2);
             const int j = i - NPV;
+            if constexpr (I8)  // 16 codes of key row ln (+32 kb), chunk of step j / 2
+                return *reinterpret_cast<const bf16x8*>(kb_ + kaddr[j / 2] + (j % 2) * 32 * D);
             const int part = j % KP, kb = (j / KP) % 2, s = j / (2 * KP);
             return *reinterpret_cast<const bf16x8*>(kb_ + kaddr[s] + kb * 32 * D * 2 +
                                                     part * kBN * D * 2);
@@ -662,7 +708,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                if constexpr (I8) sacc8[kb][r] = 0;
+                else sacc[kb][r] = 0.0f;
+            }
         bf16x8 opnd[N];
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) opnd[i] = rd(i);
@@ -676,7 +725,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
             } else {
                 const int j = i - NPV;
                 const int part = j % KP, kb = (j / KP) % 2, s = j / (2 * KP);
-                if constexpr (SPLIT) {
+                if constexpr (I8) {
+                    sacc8[j % 2] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        __builtin_bit_cast(intx4, opnd[i]), qop8[j / 2], sacc8[j % 2], 0, 0, 0);
+                } else if constexpr (SPLIT) {
                     // per key block: the two small cross terms first, then the high product
                     if (part == 1) {
                         sacc[kb] = mfma_bf16(opnd[i], qop[s], sacc[kb]);
@@ -723,7 +775,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                     const floatx4 k4 =
                         *reinterpret_cast<const floatx4*>(ksr + 32 * kb + 8 * g + 4 * hl);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sacc[kb][4 * g + i] *= k4[i];
+                    for (int i = 0; i < 4; ++i) {
+                        if constexpr (I8) sacc[kb][4 * g + i] = (float)sacc8[kb][4 * g + i] * k4[i];
+                        else sacc[kb][4 * g + i] *= k4[i];
+                    }
                 }
         }
         // register r of block kb: key k0 + 32kb + 8(r/4) + 4hl + r%4.  A key is
@@ -927,21 +982,22 @@ hipError_t launch_attn_q8(const Q8Store& st8, float* out, void* ws, const AttnSc
                           const AttnGeom& geom, int D, const Partials& part, int n_items,
                           hipStream_t stream) {
     __bf16* w = static_cast<__bf16*>(ws);
-    float* ks_ws = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
-                                            bf16_workspace_bytes(sched.n_tiles, geom.Hkv, D,
-                                                                 false, 0));
+    unsigned char* wb = static_cast<unsigned char*>(ws);
+    // head_dim 128: int8 K tiles (64 x D bytes); 64: bf16 K tiles.  Then the bf16 V
+    // tiles, then the key scales (the attention kernel finds them the same way).
+    float* ks_ws = reinterpret_cast<float*>(wb + q8_tile_bytes(sched.n_tiles, geom.Hkv, D));
     const PrepParams p{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
     const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
     const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv),
         block(kThreads);
     if (D == 128) {
-        hipLaunchKernelGGL((stage_kv_q8_kernel<128>), sgrid, sblock, 0, stream, st8, w, ks_ws,
-                           sched, geom.Hkv);
+        hipLaunchKernelGGL((stage_kv_q8_kernel<128, true>), sgrid, sblock, 0, stream, st8, wb,
+                           ks_ws, sched, geom.Hkv);
         hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true>), grid, block, 0, stream,
                            nullptr, w, out, sched, geom, p, part, st8);
     } else {
-        hipLaunchKernelGGL((stage_kv_q8_kernel<64>), sgrid, sblock, 0, stream, st8, w, ks_ws,
-                           sched, geom.Hkv);
+        hipLaunchKernelGGL((stage_kv_q8_kernel<64, false>), sgrid, sblock, 0, stream, st8, wb,
+                           ks_ws, sched, geom.Hkv);
         hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true>), grid, block, 0, stream,
                            nullptr, w, out, sched, geom, p, part, st8);
     }

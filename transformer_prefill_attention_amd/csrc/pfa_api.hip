@@ -571,14 +571,14 @@ static int check_spans(const Span* sp, int n) {
     return PFA_OK;
 }
 
-// Workspace of the 8-bit attention: the bf16 K/V tiles and the tiles' key scales,
+// Workspace of the 8-bit attention: the K/V tiles and the tiles' key scales,
 // then (fused entry) the Q codes and Q scales, then the key split's partial results.
 struct Q8Layout {
     size_t scales_off = 0, qc_off = 0, qs_off = 0, part_off = 0, need = 0;
 };
 static Q8Layout q8_layout(const Plan& p, int T_q, int n_head, int head_dim, bool fused) {
     Q8Layout l;
-    l.scales_off = p.tile_bytes;
+    l.scales_off = pfa::q8_tile_bytes(p.sched.n_tiles, p.geom.Hkv, head_dim);
     size_t end = l.scales_off + pfa::q8_scale_bytes(p.sched.n_tiles, p.geom.Hkv);
     if (fused) {
         l.qc_off = align256(end);

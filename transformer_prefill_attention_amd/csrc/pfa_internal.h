@@ -167,11 +167,16 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
                             const PrepParams* prep, bool prep_k, const Partials& part,
                             int n_items, hipStream_t stream);
 
-// Attention through an 8-bit store, on the bf16 kernel: K codes go into the bf16 tiles
-// unchanged (|code| <= 127 is exact in bf16, and the MFMA sums of code products stay
-// exact integers in f32), each tile carries its 64 key scales after the V tiles, and V
-// is dequantised (code x scale, rounded to bf16) into its tiles.  The scores are the
-// integer dot products times the query and key row scales.
+// Attention through an 8-bit store, on the bf16 kernel's schedule: the scores are the
+// integer dot products of the codes (v_mfma_i32_32x32x32_i8 on int8 K tiles for
+// head_dim 128; for 64, codes in bf16 K tiles on the bf16 MFMA -- |code| <= 127 is
+// exact in bf16 and the sums of code products stay exact integers in f32) times the
+// query and key row scales; V is dequantised (code x scale, rounded to bf16) into bf16
+// V tiles.  Workspace: K tiles, V tiles, then 64 key scales per tile and K/V head.
+inline size_t q8_tile_bytes(int n_tiles, int Hkv, int D) {
+    const size_t kt = (size_t)kBf16TileKeys * D * (D == 128 ? 1 : 2);
+    return (size_t)n_tiles * Hkv * (kt + (size_t)kBf16TileKeys * D * 2);
+}
 inline size_t q8_scale_bytes(int n_tiles, int Hkv) {
     return (size_t)n_tiles * Hkv * kBf16TileKeys * 4;
 }
