@@ -57,6 +57,18 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
+// Max over the 64 lanes with DPP inside each 16-lane row, then two cross-row exchanges
+// (as wave_sum_dpp).  Every lane receives it.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    x = fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8
+    x = fmaxf(x, dpp_f32<0x124>(x));  // row_ror:4
+    x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    x = fmaxf(x, __shfl_xor(x, 32, 64));
+    return x;
+}
+
 // 8-bit quantisation of a (token, head) row (needle-core v3/model.rs, `quant_rows` /
 // `quantize_rows`): the row's scale is its largest magnitude over 127, and a value's
 // code is the nearest integer to value / scale (ties to even) within -127..127; a row

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
                 float m = 0.0f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(o[e]));
-                const float sc = quant8_scale(wave_max(m));
+                const float sc = quant8_scale(wave_max_dpp(m));
 #pragma unroll
                 for (int e = 0; e < E; ++e) c8[lane + 64 * e] = (int8_t)quant8(o[e], sc);
                 if (lane == 0) *s8 = sc;
@@ -173,13 +173,24 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
                 do_rows(k_in + ((int64_t)t * Hkv + k0) * D, k_out + row * D, nullptr, nullptr,
                         r1 - H - k0, wkv);
             if (Q8 && q8.v) {
-                // V rows: quantised as given (no norm, no rotation)
-                for (int hh = 0; hh < r1 - H - k0; ++hh) {
-                    float x[E];
+                // V rows: quantised as given (no norm, no rotation), kRowsInFlight
+                // rows loaded before the first is reduced
+                const int nv = r1 - H - k0;
+                const float* vin = v_in + ((int64_t)t * Hkv + k0) * D;
+                for (int h0 = 0; h0 < nv; h0 += kRowsInFlight) {
+                    float x[kRowsInFlight][E];
 #pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        x[e] = v_in[((int64_t)t * Hkv + k0 + hh) * D + lane + 64 * e];
-                    store_row(x, nullptr, q8.v + (row + hh) * D, q8.vs + row + hh);
+                    for (int u = 0; u < kRowsInFlight; ++u) {
+                        if (h0 + u < nv) {
+#pragma unroll
+                            for (int e = 0; e < E; ++e) x[u][e] = vin[(h0 + u) * D + lane + 64 * e];
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < kRowsInFlight; ++u) {
+                        if (h0 + u >= nv) break;
+                        store_row(x[u], nullptr, q8.v + (row + h0 + u) * D, q8.vs + row + h0 + u);
+                    }
                 }
             } else if (v_out) {
                 const float* vs = v_in + ((int64_t)t * Hkv + k0) * D;
