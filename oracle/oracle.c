@@ -64,7 +64,10 @@
  *    top code: scale = max|x| / 127, code = x / scale rounded to the nearest
  *    integer, ties to even, within -127..127; a row of zeros gets scale 0 and
  *    codes 0.  These are integer decisions, so they are taken in single
- *    precision, the precision of the values being quantised.
+ *    precision, the precision of the values being quantised.  The pages print
+ *    neither the tie direction nor the divisor: for those two details the
+ *    8-bit rule is parity unpinned against the pages (its pins hold it to the
+ *    rule as stated here).
  */
 #include <math.h>
 #include <pthread.h>
