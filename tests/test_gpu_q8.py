@@ -232,3 +232,49 @@ def test_qk_prep_attn_q8_bench_shape_sampled():
                                  rms_eps=float(np.float32(1e-6)), scale=w.softmax_scale,
                                  rows=rows)[0]
     assert_q8_parity(out.cpu().numpy()[rows], ref, "qk_prep_attn_q8 prefill_8192 sampled")
+
+
+def test_qk_prep_attn_q8_mixed_workload_sampled():
+    # the packed mixed-batch workload (8 sequences, positions restarting, 16/4 heads,
+    # partial rotary 64 of 128, base 1e4) as one quantised prefill; output rows sampled
+    w = wl.CONFIGS["mixed"]
+    x = wl.make_inputs(w)
+    rows = wl.sample_rows(w, n_random=24, seed=4)
+    print(f"qk_prep_attn_q8 mixed T={w.T} seqs={w.n_seqs} sampled rows={len(rows)}", flush=True)
+    offs = w.seq_offsets
+    z8 = np.zeros((w.T, w.n_head_kv * w.head_dim), np.int8)
+    zs = np.zeros((w.T, w.n_head_kv), np.float32)
+    kc, ks, vc, vs = _t(z8), _t(zs), _t(z8), _t(zs)
+    out = pfa.qk_prep_attn_q8(_t(x.q), _t(x.k), _t(x.v), _t(x.wq), _t(x.wk), kc, ks, vc, vs,
+                              head_dim=w.head_dim, rope_dim=w.rope_dim,
+                              rope_freq_base=w.rope_freq_base, rms_eps=w.rms_eps,
+                              scale=w.softmax_scale, q_offsets=offs, kv_offsets=offs)
+    torch.cuda.synchronize()
+    ref, rkc, rks, rvc, rvs, _, _ = oracle.qk_prep_q8_attn(
+        x.q, x.k, x.v, x.wq, x.wk, z8, zs, z8, zs, n_head=w.n_head, n_head_kv=w.n_head_kv,
+        head_dim=w.head_dim, rope_dim=w.rope_dim, rope_freq_base=w.rope_freq_base,
+        rms_eps=float(np.float32(w.rms_eps)), scale=w.softmax_scale, q_offsets=offs,
+        kv_offsets=offs, rows=rows)
+    np.testing.assert_array_equal(vc.cpu().numpy(), rvc)
+    np.testing.assert_array_equal(vs.cpu().numpy(), rvs)
+    assert_q8_parity(out.cpu().numpy()[rows], ref, "qk_prep_attn_q8 mixed sampled")
+
+
+def test_q8_attention_chunk_bench_shape_sampled():
+    # the benchmark's chunk shape through a generated store: 1024 new rows over 7168 stored
+    # (8192 store rows, 32/8 heads of 128; the keys are split in two); output rows sampled
+    T_q, T_kv, H, Hkv, d = 1024, 8192, 32, 8, 128
+    qc, qs = wl.q8_store(T_q, H, d, 960)
+    kc, ks = wl.q8_store(T_kv, Hkv, d, 961)
+    vc, vs = wl.q8_store(T_kv, Hkv, d, 962)
+    r = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 511, 1022, 1023],
+                                     r.integers(0, T_q, 40)])).astype(np.int64)
+    print(f"gqa_attn_q8 chunk 1024 over 7168 sampled rows={len(rows)}", flush=True)
+    out = pfa.gqa_attn_q8(_t(qc), _t(qs), _t(kc), _t(ks), _t(vc), _t(vs), head_dim=d,
+                          scale=d ** -0.5, q_offsets=[0, T_q], kv_offsets=[0, T_kv])
+    torch.cuda.synchronize()
+    ref = oracle.q8_chunk_attn(qc, qs, kc, ks, vc, vs, n_head=H, n_head_kv=Hkv, head_dim=d,
+                               scale=d ** -0.5, q_offsets=[0, T_q], kv_offsets=[0, T_kv],
+                               rows=rows)
+    assert_q8_parity(out.cpu().numpy()[rows], ref, "gqa_attn_q8 chunk bench shape sampled")
