@@ -77,6 +77,8 @@ CASES = {
     "packed": ((50, 1, 130, 0), (20, 77, 0, 5), 8, 4, 128),
     "d64": ((90,), (45,), 4, 2, 64),
     "long_prefix": ((260,), (1500,), 16, 8, 128),
+    "mha": ((200,), (60,), 4, 4, 128),
+    "group8": ((130,), (70,), 16, 2, 128),
 }
 
 
