@@ -29,8 +29,9 @@
  *    non-OK return means no kernel ran; pfa_last_error() then describes the
  *    problem (thread-local, valid until the next call on the same thread).
  *    T == 0 is a successful no-op.
- *  Limits.  head_dim in {64, 128}; n_head a multiple of n_head_kv; rope_dim even,
- *    2 <= rope_dim <= head_dim; T * max(n_head, n_head_kv) * head_dim < 2^31.
+ *  Limits.  head_dim in {64, 128}; n_head a multiple of n_head_kv, at most
+ *    PFA_MAX_HEADS; rope_dim even, 2 <= rope_dim <= head_dim;
+ *    T * max(n_head, n_head_kv) * head_dim < 2^31.
  */
 #ifndef PFA_H
 #define PFA_H
@@ -43,6 +44,7 @@ extern "C" {
 #endif
 
 #define PFA_MAX_SEQS 128
+#define PFA_MAX_HEADS 1024
 
 typedef enum {
     PFA_OK = 0,

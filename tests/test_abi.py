@@ -74,6 +74,7 @@ def test_zero_tokens_is_ok_without_pointers(L):
     (dict(ptrs=(0, 8, 8, 8 << 20)), INVALID, "null"),
     (dict(ptrs=(8, 8, 8, 16)), INVALID, "overlap"),
     (dict(T=1 << 20, H=64, Hkv=8, D=128), UNSUPPORTED, "2^31"),
+    (dict(T=4, H=2048, Hkv=8, D=128), UNSUPPORTED, "query heads"),
 ])
 def test_attention_rejects(L, kw, status, needle):
     assert _attn(L, **kw) == status

@@ -365,3 +365,40 @@ def test_row_max_covers_both_lane_halves(gpu_device, precision):
         # against the oracle on the rounded inputs (what the bf16 modes promise)
         assert_bf16_parity(got, _attn_ref(w, _bf16_rounded_inputs(w, x)) if precision == "bf16"
                            else ref, f"row max over both halves {precision}")
+
+
+def test_tensors_past_4gb(gpu_device):
+    # One sequence whose K and V pass 4 GB each: 128 K/V heads of 128 dims (64 KiB a row),
+    # T = 131071 rows, T * heads * head_dim just under 2^31 (the documented limit).  The
+    # f32 kernel reads K/V tiles through 32-bit buffer resources; a resource sized to the
+    # rest of the sequence wrapped past 4 GB and read key 65535 as zeros.  V of that key is
+    # planted large so any such loss shows; rows on both sides of it are checked (f32 and
+    # bf16).  Inputs are drawn on the GPU with a seeded torch generator.
+    T, H, d = 131071, 128, 128
+    assert T * H * d < 2 ** 31
+    g = torch.Generator(device=gpu_device).manual_seed(4444)
+    q = torch.randn(T, H * d, generator=g, device=gpu_device)
+    k = torch.randn(T, H * d, generator=g, device=gpu_device)
+    v = torch.randn(T, H * d, generator=g, device=gpu_device)
+    v[65535] = 1000.0
+    scale = d ** -0.5
+    rows = [0, 65534, 65535, 65536, 100000, T - 1]
+    print(f"tensors past 4 GB: T={T} H=Hkv={H} d={d} rows={rows}", flush=True)
+    kf = k.cpu().numpy().astype(np.float64)
+    vf = v.cpu().numpy().astype(np.float64)
+    qr = q[rows].cpu().numpy().astype(np.float64)
+    ref = np.stack([
+        oracle.chunk_attn(qr[i:i + 1], kf[:r + 1], vf[:r + 1], n_head=H, n_head_kv=H,
+                          head_dim=d, scale=scale, q_offsets=[0, 1], kv_offsets=[0, r + 1])[0]
+        for i, r in enumerate(rows)])
+    del kf, vf
+    for prec in ("f32", "bf16"):
+        out = pfa.gqa_prefill_attn(q, k, v, head_dim=d, scale=scale, precision=prec)
+        torch.cuda.synchronize()
+        got = out[rows].cpu().numpy()
+        del out
+        torch.cuda.empty_cache()
+        if prec == "f32":
+            assert_f32_parity(got, ref, "f32 past 4 GB")
+        else:
+            assert_bf16_parity(got, ref, "bf16 past 4 GB")

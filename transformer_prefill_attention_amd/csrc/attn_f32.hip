@@ -227,8 +227,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
 
     // ---- K/V tile staging: global -> registers -> LDS, K and V separately so that
     // only one of them is held in registers at a time.  Each tile is read through a
-    // buffer resource that ends after the sequence's last row of this K/V head, so
-    // rows past the end of the sequence read as zeros without any branch.
+    // buffer resource that ends after the tile's last row inside the sequence (for
+    // this K/V head), so rows past the end of the sequence read as zeros without any
+    // branch.  (Its 32-bit size covers at most one tile, never the rest of the
+    // sequence, which can pass 4 GB.)
     // Thread tid moves float4 number tid + 256 i of the 32 x D tile: row f / (D/4),
     // column 4 (f % (D/4)); its byte offset inside a tile is fixed.
     const uint32_t row_bytes = (uint32_t)n_kv * D * 4;
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     }
     auto tile_rsrc = [&](const float* base, int t) {
         const int k0 = ks0 + t * kBN;
-        const uint32_t bytes = (uint32_t)(ks1 - k0 - 1) * row_bytes + D * 4;
+        const uint32_t bytes = (uint32_t)(min(ks1 - k0, kBN) - 1) * row_bytes + D * 4;
         return buffer_rsrc(base + ((int64_t)k0 * n_kv + kv) * D, bytes);
     };
     auto load_rows = [&](const float* base, int t) {

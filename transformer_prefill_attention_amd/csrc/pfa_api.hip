@@ -39,6 +39,8 @@ int check_geometry(int T, int n_head, int n_head_kv, int head_dim) {
     if (n_head <= 0 || n_head_kv <= 0)
         return fail(PFA_ERR_INVALID_ARG, "n_head (%d) and n_head_kv (%d) must be positive", n_head,
                     n_head_kv);
+    if (n_head > PFA_MAX_HEADS)
+        return fail(PFA_ERR_UNSUPPORTED, "at most %d query heads (got %d)", PFA_MAX_HEADS, n_head);
     if (n_head % n_head_kv)
         return fail(PFA_ERR_INVALID_ARG, "n_head (%d) must be a multiple of n_head_kv (%d)",
                     n_head, n_head_kv);
