@@ -145,13 +145,21 @@ def test_q8_attention_gate(name, per_head):
     assert_q8_parity(st.gpu(gate=g), st.ref(gate=g), f"gqa_attn_q8 {name} gate")
 
 
-def test_q8_attention_zero_query_row():
-    # a query row of zero codes (scale 0) weighs its visible keys equally
+def test_q8_attention_zero_rows():
+    # a query row of zero codes (scale 0) weighs its visible keys equally; zero K rows
+    # (scale 0) score 0, zero V rows add nothing -- including a row's own key and the first
+    # key of a tile
     st = Store("ragged_prefix", *CASES["ragged_prefix"])
     st.qc[5] = 0
     st.qs[5] = 0.0
+    for r in (0, 37 + 5, 64, 100):
+        st.kc[r] = 0
+        st.ks[r] = 0.0
+    for r in (1, 37 + 6, 64):
+        st.vc[r] = 0
+        st.vs[r] = 0.0
     got, ref = st.gpu(), st.ref()
-    assert_q8_parity(got, ref, "gqa_attn_q8 zero query row")
+    assert_q8_parity(got, ref, "gqa_attn_q8 zero rows")
 
 
 # ---------------------------------------------------------------------------
