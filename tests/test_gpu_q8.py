@@ -288,3 +288,31 @@ def test_q8_attention_chunk_bench_shape_sampled():
                                scale=d ** -0.5, q_offsets=[0, T_q], kv_offsets=[0, T_kv],
                                rows=rows)
     assert_q8_parity(out.cpu().numpy()[rows], ref, "gqa_attn_q8 chunk bench shape sampled")
+
+
+def test_quantize_rows_ties_and_near_ties():
+    # codes decided next to rounding ties: exact ties at scale 1 (ties to even), and values
+    # within a few ulps of a tie at a scale that is not a power of two (the reciprocal
+    # product alone could round the other way there)
+    r = np.random.default_rng(17)
+    rows = []
+    for _ in range(64):                       # scale 1: largest magnitude 127, half-integers
+        x = r.integers(-126, 126, 128).astype(np.float32) + np.float32(0.5)
+        x[r.integers(0, 128)] = np.float32(127.0 * (1 if r.integers(0, 2) else -1))
+        rows.append(x)
+    for sc in (0.37, 0.0219, 3.3e-5, 1234.5):     # near ties at other scales
+        sc32 = np.float32(sc)
+        for _ in range(64):
+            k = r.integers(-126, 126, 128).astype(np.float32)
+            x = ((k + np.float32(0.5)) * sc32).astype(np.float32)
+            ulps = r.integers(-3, 4, 128).astype(np.int32)
+            x = (x.view(np.int32) + ulps).view(np.float32)
+            x[0] = np.float32(127.0) * sc32          # the row's largest magnitude
+            rows.append(x)
+    x = np.stack(rows).astype(np.float32)
+    print(f"pfa_quantize_rows ties: rows={len(x)}", flush=True)
+    c_ref, s_ref, d_ref = oracle.quant_rows(x, 128)
+    codes, scales = pfa.quantize_rows(_t(x), 128)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
