@@ -192,7 +192,9 @@ def _ws(L, lens, H, Hkv, D, prec, pass_offsets=True, fused=0):
 @pytest.mark.parametrize("lens,H,Hkv,D", [
     ((8192,), 32, 8, 128), ((512,), 16, 8, 128), ((512,), 32, 8, 128), ((1024,), 32, 8, 128),
     ((128, 256, 512, 1024, 2048, 3000, 4096, 5000), 16, 4, 128), ((16,), 4, 2, 64),
-    ((300,), 8, 2, 128), ((1, 33, 0, 64, 65, 97), 4, 2, 128), ((90,), 6, 2, 64)])
+    ((300,), 8, 2, 128), ((1, 33, 0, 64, 65, 97), 4, 2, 128), ((90,), 6, 2, 64),
+    ((2048,), 32, 8, 128), ((3072,), 32, 8, 128), ((2048, 2048), 16, 8, 128),
+    ((6000, 100, 100), 32, 8, 128)])
 @pytest.mark.parametrize("prec", [0, 1, 2])
 @pytest.mark.parametrize("fused", [0, 1])
 def test_workspace_bytes_rule(L, lens, H, Hkv, D, prec, fused):
@@ -313,7 +315,8 @@ def test_chunk_workspace_without_prefix_is_the_prefill_rule(L, prec, fused):
 @pytest.mark.parametrize("fused", [0, 1])
 @pytest.mark.parametrize("q_lens,kv_lens,H,Hkv,D", [
     ((1024,), (8192,), 32, 8, 128), ((1,), (8192,), 32, 8, 128), ((4096,), (8192,), 32, 8, 128),
-    ((50, 1, 130, 0), (70, 78, 130, 5), 8, 4, 128), ((90,), (135,), 4, 2, 64)])
+    ((50, 1, 130, 0), (70, 78, 130, 5), 8, 4, 128), ((90,), (135,), 4, 2, 64),
+    ((2048,), (2048,), 32, 8, 128), ((2048,), (2600,), 32, 8, 128)])
 def test_chunk_workspace_rule(L, q_lens, kv_lens, H, Hkv, D, prec, fused):
     assert _chunk_ws(L, q_lens, kv_lens, H, Hkv, D, prec, fused) == \
         _expected_workspace(q_lens, H, Hkv, D, prec, fused, kv_lens=kv_lens, chunk=True)

@@ -402,3 +402,24 @@ def test_tensors_past_4gb(gpu_device):
             assert_f32_parity(got, ref, "f32 past 4 GB")
         else:
             assert_bf16_parity(got, ref, "bf16 past 4 GB")
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16"])
+def test_prefill_2048_sampled(gpu_device, precision):
+    # 2048 rows with 8B-like heads: one round of workgroups exactly fills the slots (the
+    # boundary of the key-split rule); sampled rows against the oracle
+    w = wl.sweep_workload(2048)
+    x = wl.make_inputs(w)
+    rows = wl.sample_rows(w, n_random=64, seed=9)
+    print(f"prefill T=2048 {precision} rows={len(rows)}", flush=True)
+    dev = gpu_device
+    out = pfa.gqa_prefill_attn(torch.from_numpy(x.q).to(dev), torch.from_numpy(x.k).to(dev),
+                               torch.from_numpy(x.v).to(dev), head_dim=w.head_dim,
+                               scale=w.softmax_scale, precision=precision)
+    torch.cuda.synchronize()
+    ref = _attn_ref(w, x, rows=rows)
+    got = out.cpu().numpy()[rows]
+    if precision == "f32":
+        assert_f32_parity(got, ref, "prefill 2048 f32")
+    else:
+        assert_bf16_parity(got, ref, "prefill 2048 bf16")

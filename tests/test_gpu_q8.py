@@ -316,3 +316,21 @@ def test_quantize_rows_ties_and_near_ties():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+
+
+def test_q8_attention_prefill_2048_sampled():
+    # 2048 rows, 32/8 heads: one round of workgroups exactly fills the slots; sampled rows
+    # against the oracle
+    T, H, Hkv, d = 2048, 32, 8, 128
+    qc, qs = wl.q8_store(T, H, d, 970)
+    kc, ks = wl.q8_store(T, Hkv, d, 971)
+    vc, vs = wl.q8_store(T, Hkv, d, 972)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 1023, 1024, 2046, 2047],
+                                     np.random.default_rng(3).integers(0, T, 40)]))
+    print(f"gqa_attn_q8 prefill T=2048 rows={len(rows)}", flush=True)
+    out = pfa.gqa_attn_q8(_t(qc), _t(qs), _t(kc), _t(ks), _t(vc), _t(vs), head_dim=d,
+                          scale=d ** -0.5)
+    torch.cuda.synchronize()
+    ref = oracle.q8_chunk_attn(qc, qs, kc, ks, vc, vs, n_head=H, n_head_kv=Hkv, head_dim=d,
+                               scale=d ** -0.5, rows=rows)
+    assert_q8_parity(out.cpu().numpy()[rows], ref, "gqa_attn_q8 prefill 2048")
