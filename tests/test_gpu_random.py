@@ -1,8 +1,9 @@
-"""GPU parity over seeded random configurations of the chunk and 8-bit entry points, against
-the oracle: packed sequences with and without cached prefixes (empty ones included), several
-head geometries, head_dim 64 and 128, rotary widths d, d/2 and others, causal or not, sliding
-windows, gated outputs, the f32 / bf16 / bf16x3 chunk entries, the fused chunk entry and the
-8-bit entries.  Each case is drawn from its own seed (printed first), so a failure names it.
+"""GPU parity over seeded random configurations of every entry point, against the oracle:
+packed sequences with and without cached prefixes (empty ones included), several head
+geometries, head_dim 64 and 128, rotary widths d, d/2 and others, causal or not, sliding
+windows, gated outputs -- through qknorm_rope, the prefill entries (f32 / bf16 / bf16x3, fused
+with k_rot_out), the chunk entries, the fused chunk entry and the 8-bit entries.  Each case is
+drawn from its own seed (printed first), so a failure names it.
 Tolerances: the f32 gate, the bf16 gate, and for the 8-bit path the bf16 gate with its
 relative-L2 bound."""
 import numpy as np
@@ -156,3 +157,58 @@ def test_random_q8_entries(seed, entry):
                                      scale=scale, causal=c["causal"], q_offsets=q_offs,
                                      kv_offsets=kv_offs, window=c["window"], gate=gate)[0]
     assert_q8_parity(out.cpu().numpy(), ref, f"seed {seed} q8 {entry}")
+
+
+def draw_prefill(seed):
+    r = np.random.default_rng(seed)
+    lens = [int(r.integers(0, 300)) for _ in range(int(r.integers(1, 6)))]
+    if sum(lens) == 0:
+        lens[0] = 1
+    H, Hkv = GEOMS[int(r.integers(0, len(GEOMS)))]
+    d = 128 if r.random() < 0.7 else 64
+    n = [d, d // 2, 2 * int(r.integers(1, d // 2))][int(r.integers(0, 3))]
+    return dict(lens=lens, H=H, Hkv=Hkv, d=d, n=n, causal=bool(r.random() < 0.8))
+
+
+@pytest.mark.parametrize("seed", range(300, 324))
+@pytest.mark.parametrize("entry", ["qknorm_rope", "prefill_f32", "prefill_bf16", "prefill_bf16x3",
+                                   "prep_f32", "prep_bf16"])
+def test_random_prefill_entries(seed, entry):
+    c = draw_prefill(seed)
+    H, Hkv, d, n = c["H"], c["Hkv"], c["d"], c["n"]
+    w = wl.Workload(f"random_{seed}", tuple(c["lens"]), H, Hkv, d, n, 1e6, 1e-6, seed=seed)
+    x = wl.make_inputs(w)
+    offs = w.seq_offsets
+    eps = float(np.float32(1e-6))
+    print(f"seed {seed} {entry}: {c}", flush=True)
+    kw = dict(head_dim=d, rope_dim=n, rope_freq_base=1e6, rms_eps=1e-6, seq_offsets=offs)
+    qn, kn = oracle.qknorm_rope(x.q, x.k, x.wq, x.wk, n_head=H, n_head_kv=Hkv, head_dim=d,
+                                rope_dim=n, rope_freq_base=1e6, rms_eps=eps, seq_offsets=offs)
+    if entry == "qknorm_rope":
+        gq, gk = pfa.qknorm_rope(_t(x.q), _t(x.k), _t(x.wq), _t(x.wk), **kw)
+        torch.cuda.synchronize()
+        assert_f32_parity(gq.cpu().numpy(), qn, f"seed {seed} qknorm_rope Q")
+        assert_f32_parity(gk.cpu().numpy(), kn, f"seed {seed} qknorm_rope K")
+        return
+    prec = entry.split("_")[1]
+    if entry.startswith("prefill"):
+        q32, k32 = qn.astype(np.float32), kn.astype(np.float32)
+        out = pfa.gqa_prefill_attn(_t(q32), _t(k32), _t(x.v), head_dim=d, scale=d ** -0.5,
+                                   causal=c["causal"], precision=prec, seq_offsets=offs)
+        torch.cuda.synchronize()
+        ref = oracle.gqa_attn(q32, k32, x.v, n_head=H, n_head_kv=Hkv, head_dim=d,
+                              scale=d ** -0.5, causal=c["causal"], seq_offsets=offs)
+    else:
+        k_rot = torch.empty(w.T, Hkv * d, device=DEV)
+        out = pfa.qk_prep_attn(_t(x.q), _t(x.k), _t(x.v), _t(x.wq), _t(x.wk), scale=d ** -0.5,
+                               causal=c["causal"], precision=prec, k_rot_out=k_rot, **kw)
+        torch.cuda.synchronize()
+        ref = oracle.qk_prep_attn(x.q, x.k, x.v, x.wq, x.wk, n_head=H, n_head_kv=Hkv,
+                                  head_dim=d, rope_dim=n, rope_freq_base=1e6, rms_eps=eps,
+                                  scale=d ** -0.5, causal=c["causal"], seq_offsets=offs)
+        assert_f32_parity(k_rot.cpu().numpy(), kn, f"seed {seed} {entry} k_rot_out")
+    got = out.cpu().numpy()
+    if prec == "f32":
+        assert_f32_parity(got, ref, f"seed {seed} {entry}")
+    else:
+        assert_bf16_parity(got, ref, f"seed {seed} {entry}")
