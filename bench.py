@@ -150,9 +150,9 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the path "
-              "shards by K/V head with no exchange, so N GPUs would each run the one-GPU kernel "
-              "on n_head_kv/N heads.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards by "
+              "K/V head with no exchange, so N GPUs would each run the one-GPU kernel on "
+              "n_head_kv/N heads.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
