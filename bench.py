@@ -82,19 +82,15 @@ def cpu_baseline(w, x, target_s: float):
         oracle.qk_prep_attn(x.q, x.k, x.v, x.wq, x.wk, rows=rows, **kw)
         return rows, time.perf_counter() - t0
 
-    rows0, dt0 = run(32)  # calibration
-    rate = flops_of(rows0) / dt0
-    per_row = flops_of(rows0) / len(rows0)
-    n = int(max(32, min(w.T, target_s * rate / per_row)))
+    # every run also pays the whole sequence's QK-norm + RoPE: fit time = fixed + per-row
+    # cost from two small runs (evenly spaced rows cost the same on average), then size the
+    # timed sample to the target
+    rows_a, dt_a = run(32)
+    rows_b, dt_b = run(128)
+    per = max((dt_b - dt_a) / max(len(rows_b) - len(rows_a), 1), 1e-9)
+    fixed = max(dt_a - per * len(rows_a), 0.0)
+    n = int(max(128, min(w.T, (target_s - fixed) / per)))
     rows, dt = run(n)
-    # every run also pays the whole sequence's QK-norm + RoPE, so the calibration's rate is
-    # low: when the sample fell well short of the target, fit time = fixed + per-row cost from
-    # the two runs and size the sample once more
-    if dt < 0.6 * target_s and n < w.T:
-        per = max((dt - dt0) / max(len(rows) - len(rows0), 1), 1e-9)
-        fixed = max(dt0 - per * len(rows0), 0.0)
-        n = int(min(w.T, max(n, (target_s - fixed) / per)))
-        rows, dt = run(n)
     fl = flops_of(rows)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} query rows evenly spaced over T={w.T}, all {w.n_head} heads "
