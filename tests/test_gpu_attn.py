@@ -423,3 +423,21 @@ def test_prefill_2048_sampled(gpu_device, precision):
         assert_f32_parity(got, ref, "prefill 2048 f32")
     else:
         assert_bf16_parity(got, ref, "prefill 2048 bf16")
+
+
+# Paired items (each f32 workgroup takes the j-th longest and the j-th shortest query
+# block of the sequence): with 32 K/V heads of group 4, 15 or 16 blocks of 32 rows make
+# 256 paired workgroups, one per CU.  T = 480 has an odd block count, so the middle
+# workgroup takes one block.  Compared element by element, plain and fused entry.
+PAIRED = [
+    wl.Workload("paired_480", (480,), 128, 32, 128, 128, 1e6, 1e-6, seed=31),
+    wl.Workload("paired_512", (512,), 128, 32, 128, 128, 1e6, 1e-6, seed=32),
+]
+
+
+@pytest.mark.parametrize("w", PAIRED, ids=[w.name for w in PAIRED])
+def test_paired_items_full_compare(gpu_device, w):
+    x = wl.make_inputs(w)
+    t = _dev(x, gpu_device)
+    assert_f32_parity(_attn_gpu(w, t), _attn_ref(w, x), f"attn {w.name}")
+    assert_f32_parity(_fused_gpu(w, t), _fused_ref(w, x), f"fused {w.name}")

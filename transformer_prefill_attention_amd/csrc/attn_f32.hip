@@ -29,6 +29,13 @@
 //    the K/V head is the fastest-varying block index, so consecutive
 //    workgroups (which the dispatcher spreads over the 8 XCDs) walk the same
 //    key tiles of one head together while each XCD's L2 keeps them.
+//  * Paired items (AttnSched::paired, whenever the key range is not split): the
+//    workgroup of slot j takes item j and then item n - 1 - j of the longest-first
+//    order, so every workgroup of a single causal sequence visits the same number
+//    of key tiles.  A workgroup alone on a CU runs at ~92% of the rate two
+//    co-resident ones reach together, so equal work per workgroup is what fills
+//    the last part of a run; with one item each, the hardware's placement left
+//    CUs with 228 to 292 tiles at T = 4096 (8B-like heads) and a 12% tail.
 //
 // PREP = true is the fused entry: raw Q rows are RMS-normalised and rotated once
 // as the Q tile is staged.  K arrives already normalised and rotated (the entry
@@ -93,7 +100,7 @@ __device__ __forceinline__ void prep_row(float (&x)[D / 64], const float* w, con
     }
 }
 
-template <int D, bool PREP>
+template <int D, bool PREP, bool PAIRED>
 __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, AttnSched sched, AttnGeom geom, PrepParams prep, Partials part) {
@@ -111,8 +118,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, hl = lane >> 5, ln = lane & 31;
 
-    // ---- work item (uniform across the workgroup)
-    const WorkItem wi = decode_item(sched, geom, blockIdx.x);
+    // ---- work items: one, or with paired items j and n - 1 - j (see above)
+    // (a separate instantiation: the pass loop costs the single-item kernel registers)
+    int n_pass = 1, bid2 = 0;
+    if constexpr (PAIRED) {
+        const int hk = geom.chunks * geom.Hkv, j = (int)blockIdx.x / hk;
+        const int j2 = sched.seg_start[sched.n_segs] - 1 - j;
+        n_pass = j2 > j ? 2 : 1;
+        bid2 = j2 * hk + (int)blockIdx.x % hk;
+    }
+#pragma unroll 1
+    for (int pass = 0; pass < n_pass; ++pass) {
+    const int bid = pass == 0 ? (int)blockIdx.x : bid2;
+    // the previous item's output staging is read before this one's tiles are stored
+    if (pass > 0) __syncthreads();
+    const WorkItem wi = decode_item(sched, geom, bid);
     const int kv = wi.kv, chunk = wi.chunk, s0 = wi.s0, s1 = wi.s1, q0 = wi.q0;
     // key rows of the sequence: [ks0, ks1); query row i sees keys <= i + dsh (over a
     // cached prefix its position is base + i - s0; plain prefill: ks0 = s0, dsh = 0)
@@ -400,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     // or for a split item to this unit's partial-result slot)
     const double l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = l_tot > 0.0 ? (float)(1.0 / l_tot) : 0.0f;
-    const size_t slot = (size_t)blockIdx.x * kWaves + wave;
+    const size_t slot = (size_t)bid * kWaves + wave;
     if (split && hl == 0) part.ml[slot * 32 + ln] = float2{m_run, (float)l_tot};
     float* os = smem + wave * 32 * QS;
     if (active) {
@@ -435,6 +455,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             }
         }
     }
+    }  // pass
 }
 
 }  // namespace
@@ -443,11 +464,19 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
                            const AttnSched& sched, const AttnGeom& geom, int D,
                            const PrepParams* prep, const Partials& part, int n_items,
                            hipStream_t stream) {
-    const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv), block(kThreads);
+    // paired items: workgroup j takes items j and n_items - 1 - j
+    const long long slots = sched.paired ? (n_items + 1) / 2 : (long long)n_items * sched.max_chunks;
+    const dim3 grid((unsigned)(slots * geom.chunks * geom.Hkv)), block(kThreads);
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
 #define PFA_LAUNCH_F32(DD, PP)                                                                    \
-    hipLaunchKernelGGL((attn_f32_kernel<DD, PP>), grid, block, 0, stream, q, k, v, out, sched,  \
-                       geom, p, part)
+    do {                                                                                          \
+        if (sched.paired)                                                                         \
+            hipLaunchKernelGGL((attn_f32_kernel<DD, PP, true>), grid, block, 0, stream, q, k, v, \
+                               out, sched, geom, p, part);                                        \
+        else                                                                                      \
+            hipLaunchKernelGGL((attn_f32_kernel<DD, PP, false>), grid, block, 0, stream, q, k, v,\
+                               out, sched, geom, p, part);                                        \
+    } while (0)
     if (D == 128) {
         if (prep) PFA_LAUNCH_F32(128, true);
         else PFA_LAUNCH_F32(128, false);

@@ -131,6 +131,7 @@ void choose_geometry(int H, int Hkv, float scale, int causal, int waves, pfa::At
 int build_sched(const pfa::SeqTable& st, int rows_per_item, pfa::AttnSched& sc) {
     sc.n_seqs = st.n_seqs;
     sc.rows_per_item = rows_per_item;
+    sc.paired = 0;
     for (int s = 0; s <= st.n_seqs; ++s) {
         sc.off[s] = st.off[s];
         sc.koff[s] = st.koff[s];
@@ -217,6 +218,22 @@ void choose_split(Plan& p, int head_dim) {
     const long long units =
         (long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv;
     p.part_bytes = kchunk ? pfa::partials_bytes((int)units, p.waves, head_dim) : 0;
+}
+
+// Paired items for the f32 kernel (AttnSched::paired): each workgroup takes item j and
+// item n - 1 - j of one causal sequence, so all workgroups visit the same number of key
+// tiles.  That balances the CUs only when the paired workgroups divide evenly over the
+// 256 CUs and all fit at once (at most two per CU): measured at 8B-like heads, T = 2048
+// 0.404 -> 0.313 ms and T = 4096 1.197 -> 1.080 ms, while T = 3072 (384 workgroups,
+// one or two per CU) ran 22% slower, T = 8192 and 16384 unchanged or slower (fused
+// entry 5%), packed sequences of unequal length 7% slower.  Plain prefill of one
+// sequence only, no key split, no window.
+bool pair_items(const Plan& p, const pfa::SeqTable& st, int causal, int window, bool chunk) {
+    if (!causal || window > 0 || chunk || st.n_seqs != 1 || p.sched.max_chunks != 1 ||
+        p.items < 2)
+        return false;
+    const long long wgs = (long long)(p.items + 1) / 2 * p.geom.chunks * p.geom.Hkv;
+    return wgs % kCUs == 0 && wgs <= 2 * kCUs;
 }
 
 // Geometry, schedule, key split and workspace parts of one attention call.
@@ -464,6 +481,8 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
             return rc;
         k_attn = krot;
     }
+    p.sched.paired =
+        pair_items(p, st, causal, window, mode == Mode::kChunk || chunk_fused) ? 1 : 0;
     return hip_status(pfa::launch_attn_f32(q, k_attn, v_attn, out, p.sched, p.geom, head_dim, prep,
                                            part, p.items, (hipStream_t)stream),
                       what);

@@ -54,6 +54,10 @@ struct AttnSched {
     // results that attn_combine_kernel merges.  kchunk = 0: no split (max_chunks 1).
     int kchunk;
     int max_chunks;
+    // f32 kernel without a key split: workgroup j takes item j, then item
+    // n_items - 1 - j (n_items = seg_start[n_segs]); the grid has (n_items + 1) / 2
+    // item slots.  0: one item per workgroup.
+    int paired;
 };
 
 // Partial results of a split item, per work unit (blockIdx) and wavefront:
