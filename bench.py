@@ -41,6 +41,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def f32_paired(w) -> str:
+    """'true' when libpfa runs the f32 attention kernel with paired items for this
+    single-sequence causal prefill (each workgroup takes query blocks j and n-1-j): no key
+    split, and the paired grid is 256 or 512 workgroups (whole rounds over the 256 CUs,
+    at most two per CU).  Used for the kernel's name in the output only."""
+    g = w.n_head // w.n_head_kv
+    hpw = math.gcd(g, 4)
+    rows = 32 * (4 // hpw)
+    items = -(-w.T // rows)
+    per_item = (g // hpw) * w.n_head_kv
+    split = items * per_item < 512 and -(-w.T // 32) > 1
+    paired = (w.n_seqs == 1 and not split and items > 1 and
+              ((items + 1) // 2 * per_item) in (256, 512))
+    return "true" if paired else "false"
+
+
 def load_traffic(workload: str, kernel: str, precision: str, path: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel sources; otherwise None."""
@@ -237,9 +253,9 @@ def main():
         # the attention kernel preparing its own Q rows
         mode = 0 if w.rope_dim == w.head_dim == 128 else (1 if w.rope_dim == 64 else 2)
         kernel = (f"qknorm_rope_kernel<{w.head_dim},{mode},false> + "
-                  f"attn_f32_kernel<{w.head_dim},true>")
+                  f"attn_f32_kernel<{w.head_dim},true,{f32_paired(w)}>")
     else:
-        kernel = f"attn_f32_kernel<{w.head_dim},false>"
+        kernel = f"attn_f32_kernel<{w.head_dim},false,{f32_paired(w)}>"
     traffic = load_traffic(w.name, kernel, args.precision, args.path)
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -332,8 +348,8 @@ def run_chunk(args, w, x):
     peak = PEAK_TFLOPS[args.precision]
     d = w.head_dim
     if args.precision == "f32":
-        kernel = (f"qknorm_rope_kernel<{d},0,false> + attn_f32_kernel<{d},true>"
-                  if args.path == "fused" else f"attn_f32_kernel<{d},false>")
+        kernel = (f"qknorm_rope_kernel<{d},0,false> + attn_f32_kernel<{d},true,false>"
+                  if args.path == "fused" else f"attn_f32_kernel<{d},false,false>")
     else:
         split = "true" if args.precision == "bf16x3" else "false"
         kernel = f"stage_kv_bf16_kernel<{d},{split},false> + "
