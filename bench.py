@@ -114,6 +114,52 @@ def cpu_baseline(w, x, target_s: float):
                       f"in {dt:.2f} s"}
 
 
+def qknorm_hbm(args):
+    """qknorm_rope alone, out of place, each run after a 1 GiB read has evicted L2 and the
+    MALL, so every input byte comes from HBM.  (Evicting by writing would leave the MALL full
+    of dirty lines, whose write-back the timed kernel would then pay for.)  HIP events on the launch stream around each
+    launch; median of --steps runs (at least 20).  The same measurement of a torch device copy
+    of Q and K gives the rate a plain read + write stream reaches here."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import transformer_prefill_attention_amd as pfa
+    from transformer_prefill_attention_amd import workloads as wl
+    w = wl.CONFIGS[args.workload] if not args.seq_len else wl.sweep_workload(args.seq_len)
+    x = wl.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k = torch.from_numpy(x.q).to(dev), torch.from_numpy(x.k).to(dev)
+    wq, wk = torch.from_numpy(x.wq).to(dev), torch.from_numpy(x.wk).to(dev)
+    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    evict = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    kw = dict(head_dim=w.head_dim, rope_dim=w.rope_dim, rope_freq_base=w.rope_freq_base,
+              rms_eps=w.rms_eps, seq_offsets=w.seq_offsets if w.n_seqs > 1 else None)
+    nbytes = 2 * (q.numel() + k.numel()) * 4   # read + write of Q and K
+
+    def timed(fn, n):
+        ts = []
+        for i in range(n + 3):
+            evict.max()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    n = max(args.steps, 20)
+    t_k = timed(lambda: pfa.qknorm_rope(q, k, wq, wk, q_out=qn, k_out=kn, **kw), n)
+    t_c = timed(lambda: (qn.copy_(q), kn.copy_(k)), n)
+    print(json.dumps({
+        "kernel": "qknorm_rope", "workload": w.name, "bytes": nbytes, "runs": n,
+        "evict_bytes": evict.numel() * 4,
+        "median_ms": round(t_k, 4), "gbs": round(nbytes / t_k / 1e6, 1),
+        "frac_of_8tbs": round(nbytes / t_k / 1e6 / HBM_PEAK_GBS, 4),
+        "copy_median_ms": round(t_c, 4), "copy_gbs": round(nbytes / t_c / 1e6, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +194,10 @@ def main():
                          "store; --chunk-base, --window and --gate apply (no CPU baseline line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qknorm-hbm", action="store_true",
+                    help="only time qknorm_rope on the workload's Q and K with L2 and MALL evicted "
+                         "between runs (a 1 GiB buffer is read), beside a plain device copy of "
+                         "the same bytes; median GB/s against 8 TB/s")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch copies of a MIB-sized f32 buffer (reference kernel of "
                          "known traffic for the rocprofv3 FETCH_SIZE / WRITE_SIZE scale factor)")
@@ -162,6 +212,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 4 * n, "dispatches": 3}))
+        return
+
+    if args.qknorm_hbm:
+        qknorm_hbm(args)
         return
 
     if args.gpus != 1:
