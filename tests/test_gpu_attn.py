@@ -426,12 +426,19 @@ def test_prefill_2048_sampled(gpu_device, precision):
 
 
 # Paired items (each f32 workgroup takes the j-th longest and the j-th shortest query
-# block of the sequence): with 32 K/V heads of group 4, 15 or 16 blocks of 32 rows make
-# 256 paired workgroups, one per CU.  T = 480 has an odd block count, so the middle
+# block of the sequence): these shapes make 256 or 512 paired workgroups (e.g. 32 K/V heads
+# of group 4 and 16 or 31 blocks of 32 rows).  T = 990 has an odd block count, so the middle
 # workgroup takes one block.  Compared element by element, plain and fused entry.
 PAIRED = [
-    wl.Workload("paired_480", (480,), 128, 32, 128, 128, 1e6, 1e-6, seed=31),
+    wl.Workload("paired_990", (990,), 128, 32, 128, 128, 1e6, 1e-6, seed=31),
     wl.Workload("paired_512", (512,), 128, 32, 128, 128, 1e6, 1e-6, seed=32),
+    # group 2: two heads x two 32-row blocks per workgroup (64-row items), 16 items with a
+    # ragged last one
+    wl.Workload("paired_g2_1000", (1000,), 64, 32, 128, 128, 1e6, 1e-6, seed=33),
+    # head_dim 64, partial rotary
+    wl.Workload("paired_d64_500", (500,), 128, 32, 64, 32, 1e4, 1e-6, seed=34),
+    # group 8: two head chunks per K/V head
+    wl.Workload("paired_g8_500", (500,), 128, 16, 128, 64, 1e6, 1e-6, seed=35),
 ]
 
 
