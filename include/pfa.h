@@ -76,7 +76,9 @@ typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_pr
  *  - PFA_PREC_F32, qk_prep_attn: the normalised, rotated K, T * n_head_kv *
  *    head_dim * 4 bytes (not used when the call is given k_rot_out);
  *  - any precision, short inputs only, at the next multiple of 256 bytes: when
- *    the (query block, head) work items cannot fill the GPU, each item's key
+ *    the (query block, head) work items cannot fill the GPU (the current device's
+ *    compute units, 256 on MI355X and when no device is visible; query with the
+ *    same device current as the call), each item's key
  *    range is split over several workgroups whose partial results (32 x head_dim
  *    f32 plus two f32 per row, per wavefront) are merged by one more kernel;
  *    0 bytes otherwise.

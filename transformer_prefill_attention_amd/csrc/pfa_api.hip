@@ -185,8 +185,28 @@ struct Plan {
 };
 
 constexpr int kF32TileKeys = 32;
-// Workgroups that fill the GPU once: 256 CUs x (2 f32 or 1 bf16 workgroups per CU).
-constexpr int kCUs = 256;
+// Compute units of the current device: the workgroups that fill the GPU once are its CUs x
+// (2 f32 or 1 bf16 workgroups per CU).  256 (a whole MI355X) when no device is visible, as
+// for the size queries on a host without a GPU; a partitioned GPU reports its share.  Read
+// once per device.
+int device_cus() {
+    constexpr int kWholeGpu = 256, kMaxDevices = 64;
+    static int cache[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kWholeGpu;
+    }
+    int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        (void)hipGetLastError();
+        n = kWholeGpu;
+    }
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+    return n;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -203,7 +223,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kMaxKeyChunks = 32;
 void choose_split(Plan& p, int head_dim) {
     const long long wgs = (long long)p.items * p.geom.chunks * p.geom.Hkv;
-    const int target = (p.waves == 8 ? 1 : 2) * kCUs;
+    const int target = (p.waves == 8 ? 1 : 2) * device_cus();
     const int n_max = (p.sched.max_len + p.tile_keys - 1) / p.tile_keys;
     const long long k_min = std::max<long long>((128 + p.tile_keys - 1) / p.tile_keys,
                                                 (n_max + kMaxKeyChunks - 1) / kMaxKeyChunks);
@@ -223,7 +243,7 @@ void choose_split(Plan& p, int head_dim) {
 // Paired items for the f32 kernel (AttnSched::paired): each workgroup takes item j and
 // item n - 1 - j of one causal sequence, so all workgroups visit the same number of key
 // tiles.  That balances the CUs only when the paired workgroups divide evenly over the
-// 256 CUs and all fit at once (at most two per CU): measured at 8B-like heads, T = 2048
+// CUs (256 on MI355X) and all fit at once (at most two per CU): measured at 8B-like heads, T = 2048
 // 0.404 -> 0.313 ms and T = 4096 1.197 -> 1.080 ms, while T = 3072 (384 workgroups,
 // one or two per CU) ran 22% slower, T = 8192 and 16384 unchanged or slower (fused
 // entry 5%), packed sequences of unequal length 7% slower.  Plain prefill of one
@@ -233,7 +253,8 @@ bool pair_items(const Plan& p, const pfa::SeqTable& st, int causal, int window, 
         p.items < 2)
         return false;
     const long long wgs = (long long)(p.items + 1) / 2 * p.geom.chunks * p.geom.Hkv;
-    return wgs % kCUs == 0 && wgs <= 2 * kCUs;
+    const int cus = device_cus();
+    return wgs % cus == 0 && wgs <= 2 * cus;
 }
 
 // Geometry, schedule, key split and workspace parts of one attention call.
