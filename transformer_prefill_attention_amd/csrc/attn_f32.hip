@@ -29,10 +29,10 @@
 //    the K/V head is the fastest-varying block index, so consecutive
 //    workgroups (which the dispatcher spreads over the 8 XCDs) walk the same
 //    key tiles of one head together while each XCD's L2 keeps them.
-//  * Paired items (AttnSched::paired, whenever the key range is not split): the
-//    workgroup of slot j takes item j and then item n - 1 - j of the longest-first
-//    order, so every workgroup of a single causal sequence visits the same number
-//    of key tiles.  A workgroup alone on a CU runs at ~92% of the rate two
+//  * Paired items (AttnSched::paired; the host pairs one causal sequence without a
+//    key split when the paired grid is a whole round over the CUs): the workgroup of
+//    slot j takes item j and then item n - 1 - j of the longest-first order, so
+//    every workgroup visits the same number of key tiles.  A workgroup alone on a CU runs at ~92% of the rate two
 //    co-resident ones reach together, so equal work per workgroup is what fills
 //    the last part of a run; with one item each, the hardware's placement left
 //    CUs with 228 to 292 tiles at T = 4096 (8B-like heads) and a 12% tail.
@@ -127,6 +127,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
         n_pass = j2 > j ? 2 : 1;
         bid2 = j2 * hk + (int)blockIdx.x % hk;
     }
+    // (the loop body, the whole item, keeps the indentation of the single-item kernel)
 #pragma unroll 1
     for (int pass = 0; pass < n_pass; ++pass) {
     const int bid = pass == 0 ? (int)blockIdx.x : bid2;
