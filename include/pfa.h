@@ -12,7 +12,8 @@
  *    memra-engine 0.130.0 (src/forward.rs, `Model::forward`, activation-layout
  *    note and SDPA block) keeps between its projections and its attention.
  *  Pointers.  Tensor pointers are DEVICE pointers owned by the caller, 16-byte
- *    aligned.  The library allocates no device memory and keeps no state beyond
+ *    aligned (a misaligned f32 tensor is rejected with PFA_ERR_INVALID_ARG before
+ *    anything is enqueued).  The library allocates no device memory and keeps no state beyond
  *    its loaded code objects; the attention calls take a caller-owned device
  *    workspace (see pfa_workspace_bytes).
  *  Sequences.  `seq_offsets` is a HOST array of n_seqs + 1 int32 values

@@ -443,3 +443,23 @@ def test_quantize_rows_argument_checks(L):
     assert L.pfa_quantize_rows(v(1 << 20), 4, 8, v(2 << 20), v(3 << 20), v((1 << 20) + 4),
                                None) == INVALID
     assert "overlap" in _msg(L)
+
+
+def test_tensor_pointers_must_be_16_byte_aligned(L):
+    # the header requires 16-byte aligned tensors (the kernels move 16-byte vectors); a
+    # misaligned one is rejected on the host, after the other checks, before any launch.
+    # (Every call here fails validation: the fake addresses never reach a kernel.)
+    p = ctypes.c_void_p
+    for bad in range(4):
+        ptrs = [(i + 1) << 20 for i in range(4)]
+        ptrs[bad] += 4
+        assert _attn(L, ptrs=tuple(ptrs)) == INVALID
+        assert "16-byte aligned" in _msg(L)
+    w = [p((i + 1) << 20) for i in range(6)]
+    w[4] = p((5 << 20) + 8)  # q_norm_w
+    assert L.qknorm_rope(*w, None, 0, 16, 4, 2, 64, 64, 1e6, 1e-6, None) == INVALID
+    assert "16-byte aligned" in _msg(L)
+    assert L.qk_prep_attn(p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p((5 << 20) + 4),
+                          p(6 << 20), None, 0, 16, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0,
+                          p(7 << 20), p(8 << 20), 16 << 20, None) == INVALID
+    assert "16-byte aligned" in _msg(L)

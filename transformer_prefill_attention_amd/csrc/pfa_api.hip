@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "pfa_internal.h"
 
@@ -25,6 +26,18 @@ int fail(int status, const char* fmt, ...) {
     vsnprintf(g_err, sizeof(g_err), fmt, ap);
     va_end(ap);
     return status;
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// The f32 tensors are read and written in 16-byte vectors: every (non-null) one must be
+// 16-byte aligned, as the header requires.  Checked after the other arguments, just
+// before anything is enqueued.
+int check_aligned(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (p && !aligned16(p))
+            return fail(PFA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    return 0;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -364,6 +377,7 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
         return fail(PFA_ERR_INVALID_ARG, "Q and K buffers overlap");
     pfa::SeqTable st;
     if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
+    if ((rc = check_aligned({q_in, k_in, q_out, k_out, q_norm_w, k_norm_w}))) return rc;
     return hip_status(pfa::launch_qknorm_rope(q_in, k_in, q_out, k_out, nullptr, nullptr,
                                               q_norm_w, k_norm_w, st, T,
                                               n_head, n_head_kv, head_dim, rope_dim,
@@ -465,6 +479,9 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
         part.o = reinterpret_cast<float*>(w);
         part.ml = reinterpret_cast<float2*>(w + (size_t)units * p.waves * 32 * head_dim * 4);
     }
+    if ((rc = check_aligned({q, k, v, out, k_cache, v_cache, gate, prep ? prep->wq : nullptr,
+                             prep ? prep->wk : nullptr, prep ? prep->k_rot_out : nullptr})))
+        return rc;
     const char* what = prep ? (chunk_fused ? "qk_prep_chunk_attn launch" : "qk_prep_attn launch")
                             : (mode == Mode::kChunk ? "gqa_chunk_attn launch"
                                                     : "gqa_prefill_attn launch");
@@ -639,7 +656,6 @@ static int check_q8_attn(float scale) {
     return PFA_OK;
 }
 
-static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 size_t pfa_q8_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
                               int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
@@ -738,6 +754,9 @@ static int attn_q8_common(bool fused, pfa::Q8Store in, const float* q, const flo
         part.ml = reinterpret_cast<float2*>(ws + l.part_off +
                                             (size_t)units * p.waves * 32 * head_dim * 4);
     }
+    if ((rc = check_aligned({out, gate, q, k, v, prep ? prep->wq : nullptr,
+                             prep ? prep->wk : nullptr})))
+        return rc;
     const char* what = fused ? "qk_prep_attn_q8 launch" : "gqa_attn_q8 launch";
     if (fused) {
         // the new rows: Q and K normalised and rotated at their positions, then Q (into
