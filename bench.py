@@ -41,22 +41,6 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def f32_paired(w) -> str:
-    """'true' when libpfa runs the f32 attention kernel with paired items for this
-    single-sequence causal prefill (each workgroup takes query blocks j and n-1-j): no key
-    split, and the paired grid is 256 or 512 workgroups (whole rounds over the 256 CUs,
-    at most two per CU).  Used for the kernel's name in the output only."""
-    g = w.n_head // w.n_head_kv
-    hpw = math.gcd(g, 4)
-    rows = 32 * (4 // hpw)
-    items = -(-w.T // rows)
-    per_item = (g // hpw) * w.n_head_kv
-    split = items * per_item < 512 and -(-w.T // 32) > 1
-    paired = (w.n_seqs == 1 and not split and items > 1 and
-              ((items + 1) // 2 * per_item) in (256, 512))
-    return "true" if paired else "false"
-
-
 def load_traffic(workload: str, kernel: str, precision: str, path: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel sources; otherwise None."""
@@ -108,10 +92,15 @@ def cpu_baseline(w, x, target_s: float):
     n = int(max(128, min(w.T, (target_s - fixed) / per)))
     rows, dt = run(n)
     fl = flops_of(rows)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} query rows evenly spaced over T={w.T}, all {w.n_head} heads "
-                      f"(QK-norm + RoPE of the whole sequence included); {fl:.3e} causal FLOPs "
-                      f"in {dt:.2f} s"}
+    rate = fl / dt
+    # a row-sampled measurement: the oracle's rate on the sample; the whole workload's
+    # oracle time is that rate's extrapolation to all rows (not run here: minutes)
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"row-sampled: {len(rows)} of {w.T} query rows, evenly spaced, all "
+                      f"{w.n_head} heads (QK-norm + RoPE of the whole sequence included); "
+                      f"{fl:.3e} causal FLOPs in {dt:.2f} s",
+            "sampled_rows": int(len(rows)),
+            "full_oracle_s_extrapolated": round(w.attn_flops() / rate, 1)}
 
 
 def qknorm_hbm(args):
@@ -193,6 +182,10 @@ def main():
                          "qk_prep_attn_q8 on the raw rows, unfused: gqa_attn_q8 on a filled "
                          "store; --chunk-base, --window and --gate apply (no CPU baseline line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-bars", action="store_true",
+                    help="skip the other bars (bf16 at T=8192, T=512 f32/bf16, T=16384 f32)")
+    ap.add_argument("--no-profiler", action="store_true",
+                    help="do not use the torch profiler for the per-kernel times of the bars")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--qknorm-hbm", action="store_true",
                     help="only time qknorm_rope on the workload's Q and K with L2 and MALL evicted "
@@ -290,26 +283,12 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     flops = w.attn_flops()
     value = flops / (elapsed / args.steps) / 1e12
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    kern_ms, kern_med = event_stats(ev)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.precision]
-    if args.precision != "f32":
-        # the bf16 modes are several launches per call (the events bracket all of them):
-        # [rotary table (fused entry)], the K/V staging kernel, the attention kernel
-        split = "true" if args.precision == "bf16x3" else "false"
-        fused = "true" if args.path == "fused" else "false"
-        kernel = (f"stage_kv_bf16_kernel<{w.head_dim},{split},{fused}> + "
-                  f"attn_bf16_kernel<{w.head_dim},{split},{fused},false>")
-        if args.path == "fused":
-            kernel = f"rope_table_kernel<{w.head_dim},{split}> + " + kernel
-    elif args.path == "fused":
-        # the f32 fused entry: K prepared once (QK-norm + RoPE over the K rows), then
-        # the attention kernel preparing its own Q rows
-        mode = 0 if w.rope_dim == w.head_dim == 128 else (1 if w.rope_dim == 64 else 2)
-        kernel = (f"qknorm_rope_kernel<{w.head_dim},{mode},false> + "
-                  f"attn_f32_kernel<{w.head_dim},true,{f32_paired(w)}>")
-    else:
-        kernel = f"attn_f32_kernel<{w.head_dim},false,{f32_paired(w)}>"
+    # the kernels the call enqueues, as the library plans them (the bf16 modes and the f32
+    # fused entry are several launches per call; the events bracket all of them)
+    kernel = prefill_kernels(pfa, w, args.precision, args.path)
     traffic = load_traffic(w.name, kernel, args.precision, args.path)
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -324,12 +303,133 @@ def main():
                    "head_dim": w.head_dim, "path": args.path, "causal_flops": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": kernel, "kernel_ms": round(kern_ms, 4)},
+                     "kernel": kernel, "kernel_ms": round(kern_ms, 4),
+                     "kernel_ms_median": round(kern_med, 4), "launches": len(ev)},
     }
+    if not args.no_bars:
+        res["bars"] = measure_bars(pfa, wl, w, x, args)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, wl.Inputs(x.q, k_in, x.v, x.wq, x.wk, x.outliers),
                                            args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def event_stats(ev):
+    """(mean, median) in ms of HIP event pairs.  The mean is the figure the roofline
+    uses (rocprofv3 summaries report averages, and the two must agree); the median is
+    reported beside it."""
+    import numpy as np
+    ts = np.array([a.elapsed_time(b) for a, b in ev], dtype=np.float64)
+    return float(ts.mean()), float(np.median(ts))
+
+
+def prefill_kernels(pfa, w, precision, path):
+    entry = pfa.ENTRY_PREP if path == "fused" else pfa.ENTRY_PREFILL
+    return pfa.attn_plan(entry, T_q=w.T, n_head=w.n_head, n_head_kv=w.n_head_kv,
+                         head_dim=w.head_dim, rope_dim=w.rope_dim, precision=precision,
+                         q_offsets=w.seq_offsets if w.n_seqs > 1 else None)["kernels"]
+
+
+def time_prefill_call(pfa, w, t, precision, path, runs, warmup, profile=False):
+    """The attention call alone (unfused: gqa_prefill_attn on prepared Q/K; fused:
+    qk_prep_attn on raw rows), HIP events on the launch stream around every launch.
+    With ``profile``, also the average device time of each kernel of the call from the
+    torch profiler over the same runs (None where that is unavailable)."""
+    import torch
+    dev = t["q"].device
+    stream = torch.cuda.current_stream(dev)
+    offs = w.seq_offsets if w.n_seqs > 1 else None
+    rope = dict(head_dim=w.head_dim, rope_dim=w.rope_dim, rope_freq_base=w.rope_freq_base,
+                rms_eps=w.rms_eps, seq_offsets=offs)
+    out = torch.empty_like(t["q"])
+    if path == "fused":
+        def call():
+            pfa.qk_prep_attn(t["q"], t["k"], t["v"], t["wq"], t["wk"], scale=w.softmax_scale,
+                             precision=precision, out=out, **rope)
+    else:
+        qn, kn = pfa.qknorm_rope(t["q"], t["k"], t["wq"], t["wk"], **rope)
+
+        def call():
+            pfa.gqa_prefill_attn(qn, kn, t["v"], head_dim=w.head_dim, scale=w.softmax_scale,
+                                 precision=precision, seq_offsets=offs, out=out)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(runs):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    mean, med = event_stats(ev)
+    per_kernel = None
+    if profile:
+        try:
+            from torch.profiler import ProfilerActivity
+            from torch.profiler import profile as tprofile
+            with tprofile(activities=[ProfilerActivity.CUDA]) as prof:
+                for _ in range(runs):
+                    call()
+                torch.cuda.synchronize()
+            per_kernel = {}
+            for e in prof.key_averages():
+                us = getattr(e, "device_time", None)
+                if us is None:
+                    us = getattr(e, "cuda_time", None)
+                if us and any(n in e.key for n in ("attn_", "stage_kv", "rope_table",
+                                                    "qknorm_rope")):
+                    per_kernel[e.key] = {"avg_ms": round(us / 1e3, 4), "count": e.count}
+        except Exception as exc:  # the profiler is a diagnostic; the events stand alone
+            per_kernel = {"unavailable": f"{type(exc).__name__}: {exc}"[:200]}
+    return mean, med, per_kernel
+
+
+def measure_bars(pfa, wl, w_main, x_main, args):
+    """The other bars of the metric in the same run: bf16 at T = 8192 (the call, and its
+    attention kernel alone), the 0.6B-like shape (T = 512, 16/8 heads) in f32 and bf16,
+    and the long shape (T = 16384) in f32.  Each is the attention call alone, timed with
+    HIP events on its launch stream (20 runs after 5 warmup runs); f32 and bf16 fractions
+    against their own MFMA peaks."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    bars = []
+    specs = [("prefill_8192", "bf16", "unfused", True), ("prefill_8192", "bf16", "fused", True),
+             ("qwen3_0p6b", "f32", "unfused", False), ("qwen3_0p6b", "bf16", "unfused", False),
+             ("long", "f32", "unfused", False)]
+    cache = {}
+    for name, prec, path, prof in specs:
+        w = wl.CONFIGS[name]
+        if name not in cache:
+            x = x_main if w.name == w_main.name else wl.make_inputs(w)
+            cache.clear()
+            cache[name] = {n: torch.from_numpy(np.ascontiguousarray(
+                wl.with_outlier_keys(x.k, x.outliers) if n == "k" else getattr(x, n))).to(dev)
+                for n in ("q", "k", "v", "wq", "wk")}
+        t = cache[name]
+        print(f"bar: {name} {prec} {path}", file=sys.stderr, flush=True)
+        mean, med, per_kernel = time_prefill_call(pfa, w, t, prec, path, runs=20, warmup=5,
+                                                  profile=prof and not args.no_profiler)
+        flops = w.attn_flops()
+        peak = PEAK_TFLOPS[prec]
+        bar = {"workload": name, "T": w.T, "n_head": w.n_head, "n_head_kv": w.n_head_kv,
+               "precision": prec, "path": path,
+               "kernel": prefill_kernels(pfa, w, prec, path),
+               "call_ms": round(mean, 4), "call_ms_median": round(med, 4),
+               "tflops": round(flops / (mean * 1e-3) / 1e12, 3),
+               "frac": round(flops / (mean * 1e-3) / 1e12 / peak, 4), "peak": peak}
+        if per_kernel is not None:
+            bar["per_kernel"] = per_kernel
+            attn = [v for k, v in per_kernel.items() if isinstance(v, dict) and
+                    k.split("<")[0].split("::")[-1].startswith("attn_bf16_kernel")]
+            if attn:
+                ms = attn[0]["avg_ms"]
+                bar["attention_kernel_ms"] = ms
+                bar["attention_kernel_frac"] = round(flops / (ms * 1e-3) / 1e12 / peak, 4)
+        bars.append(bar)
+    return bars
 
 
 def run_chunk(args, w, x):
@@ -397,21 +497,14 @@ def run_chunk(args, w, x):
     else:
         pairs = T_q * B + T_q * (T_q + 1) // 2
     flops = 4 * w.head_dim * w.n_head * pairs
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    kern_ms, kern_med = event_stats(ev)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.precision]
     d = w.head_dim
-    if args.precision == "f32":
-        kernel = (f"qknorm_rope_kernel<{d},0,false> + attn_f32_kernel<{d},true,false>"
-                  if args.path == "fused" else f"attn_f32_kernel<{d},false,false>")
-    else:
-        split = "true" if args.precision == "bf16x3" else "false"
-        kernel = f"stage_kv_bf16_kernel<{d},{split},false> + "
-        if args.path == "fused":
-            kernel = (f"qknorm_rope_kernel<{d},0,false> + rope_table_kernel<{d},{split}> + " +
-                      kernel + f"attn_bf16_kernel<{d},{split},true,false>")
-        else:
-            kernel += f"attn_bf16_kernel<{d},{split},false,false>"
+    kernel = pfa.attn_plan(pfa.ENTRY_CHUNK_PREP if args.path == "fused" else pfa.ENTRY_CHUNK,
+                           T_q=T_q, T_kv=T, n_head=w.n_head, n_head_kv=w.n_head_kv, head_dim=d,
+                           rope_dim=w.rope_dim, window=args.window, precision=args.precision,
+                           q_offsets=[0, T_q], kv_offsets=[0, T])["kernels"]
     res = {
         "metric": METRIC, "value": round(flops / (elapsed / args.steps) / 1e12, 3),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -427,7 +520,8 @@ def run_chunk(args, w, x):
                    "head_dim": d, "path": args.path, "causal_flops": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": kernel, "kernel_ms": round(kern_ms, 4)},
+                     "kernel": kernel, "kernel_ms": round(kern_ms, 4),
+                     "kernel_ms_median": round(kern_med, 4)},
     }
     print(json.dumps(res), flush=True)
 
@@ -500,17 +594,17 @@ def run_q8(args, w, x):
     else:
         pairs = T_q * B + T_q * (T_q + 1) // 2
     flops = 4 * d * w.n_head * pairs
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    kern_ms, kern_med = event_stats(ev)
     achieved = flops / (kern_ms * 1e-3) / 1e12
     # head_dim 128: Q.K^T on int8 matrix cores (5.0 POP/s dense), P.V on bf16 (2.5 PF):
     # half the FLOPs each, so the least time is F/2 (1/5000 + 1/2500) -> a 3333 TFLOP/s
     # peak for the whole; head_dim 64 runs both products on bf16
     peak = (2.0 / (1.0 / PEAK_TFLOPS["int8"] + 1.0 / PEAK_TFLOPS["bf16"]) if d == 128
             else PEAK_TFLOPS["bf16"])
-    kernel = (f"stage_kv_q8_kernel<{d},{'true' if d == 128 else 'false'}> + "
-              f"attn_bf16_kernel<{d},false,false,true>")
-    if args.path == "fused":
-        kernel = f"qknorm_rope_kernel<{d},0,true> + " + kernel
+    kernel = pfa.attn_plan(pfa.ENTRY_Q8_PREP if args.path == "fused" else pfa.ENTRY_Q8,
+                           T_q=T_q, T_kv=T, n_head=w.n_head, n_head_kv=w.n_head_kv, head_dim=d,
+                           rope_dim=w.rope_dim, window=args.window,
+                           q_offsets=[0, T_q], kv_offsets=[0, T])["kernels"]
     what = (f"{T_q} new rows over {B} stored rows" if B else f"prefill of {T} rows")
     traffic = None if (B or args.window or gate is not None) else \
         load_traffic(w.name, kernel, "q8", args.path)
@@ -529,7 +623,8 @@ def run_q8(args, w, x):
                    "head_dim": d, "path": args.path, "causal_flops": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": kernel, "kernel_ms": round(kern_ms, 4)},
+                     "kernel": kernel, "kernel_ms": round(kern_ms, 4),
+                     "kernel_ms_median": round(kern_med, 4)},
     }
     print(json.dumps(res), flush=True)
 

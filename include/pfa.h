@@ -362,6 +362,66 @@ size_t pfa_q8_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_offset
                               int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
                               int fused);
 
+/*
+ * Plan report
+ * -----------
+ * What an attention call would enqueue for given arguments, decided by the same host
+ * code the entry point runs; nothing is enqueued and no device is needed (the key split
+ * is planned for the current device's compute units, 256 when none is visible).  For
+ * tools and tests: profilers name the kernels, and the work schedule can be checked.
+ *
+ * `entry` picks the entry point.  The arguments are the call's: for the prefill entries
+ * q_offsets is seq_offsets and kv_offsets / T_kv are ignored; rope_dim matters for the
+ * entries that prepare Q and K; window for the chunk and 8-bit entries; precision is
+ * ignored by the 8-bit ones.  has_k_rot_out: qk_prep_attn is given a k_rot_out.
+ * workspace_bytes: the workspace the call will be given (0: none; SIZE_MAX: enough).
+ * It matters only for PFA_PREC_F32, which drops the key split when the workspace has no
+ * room for the partial results.
+ */
+typedef enum {
+    PFA_ENTRY_PREFILL = 0,    /* gqa_prefill_attn */
+    PFA_ENTRY_PREP = 1,       /* qk_prep_attn */
+    PFA_ENTRY_CHUNK = 2,      /* gqa_chunk_attn */
+    PFA_ENTRY_CHUNK_PREP = 3, /* qk_prep_chunk_attn */
+    PFA_ENTRY_Q8 = 4,         /* gqa_attn_q8 */
+    PFA_ENTRY_Q8_PREP = 5     /* qk_prep_attn_q8 */
+} pfa_entry;
+
+typedef struct {
+    int items;               /* (sequence, query super-block) work items, longest first */
+    int rows_per_item;       /* query rows of a super-block */
+    int waves_per_workgroup; /* wavefronts of an attention workgroup */
+    int tile_keys;           /* keys per K/V tile */
+    int key_chunk_tiles;     /* key split: tiles per key chunk (0: not split) */
+    int max_key_chunks;      /* key chunks of the longest item (1: not split) */
+    int paired;              /* f32: attention workgroup j takes items j and items-1-j */
+    int reserved;
+    int64_t workgroups;      /* grid of the attention kernel */
+    size_t workspace_bytes;  /* device workspace the call uses */
+    char kernels[320];       /* kernels enqueued, in launch order, joined by " + " */
+} pfa_plan;
+
+/* Fills *plan.  Returns PFA_OK, or the status the entry point would return for these
+ * arguments (pfa_last_error() says why).  T_q == 0: a zeroed plan. */
+int pfa_attn_plan(int entry, const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                  int T_q, int T_kv, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                  int causal, int window, int precision, int has_k_rot_out,
+                  size_t workspace_bytes, pfa_plan* plan);
+
+/* The work unit of every attention workgroup, decoded on the host by the kernels' own
+ * code.  One record of PFA_UNIT_FIELDS int32 per (workgroup, item it takes): workgroup
+ * index, pass (1 for the second item of a paired workgroup, else 0), item (its index in
+ * the longest-first order), sequence, super-block of the sequence, key chunk, K/V head,
+ * head chunk of the group, first key tile, end key tile (tiles of tile_keys keys counted
+ * from the sequence's first key row; first >= end: the workgroup exits at once).
+ * Writes at most max_records records (host array `records`) and returns how many there
+ * are, or a negative pfa_status. */
+#define PFA_UNIT_FIELDS 10
+int64_t pfa_attn_units(int entry, const int32_t* q_offsets, const int32_t* kv_offsets,
+                       int n_seqs, int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                       int rope_dim, int causal, int window, int precision, int has_k_rot_out,
+                       size_t workspace_bytes, int32_t* records, int64_t max_records);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* pfa_last_error(void);
 

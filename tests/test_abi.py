@@ -131,10 +131,44 @@ def test_python_binding_raises_without_gpu_tensors():
     import torch
     with pytest.raises(ValueError):
         pfa.gqa_prefill_attn(torch.zeros(4, 128), torch.zeros(4, 64), torch.zeros(4, 64),
-                             head_dim=64)
+                             head_dim=64, scale=0.125)
     with pytest.raises(TypeError):
         pfa.gqa_prefill_attn(torch.zeros(4, 128, dtype=torch.float64), torch.zeros(4, 64),
-                             torch.zeros(4, 64), head_dim=64)
+                             torch.zeros(4, 64), head_dim=64, scale=0.125)
+
+
+@pytest.mark.parametrize("fn", ["gqa_prefill_attn", "qk_prep_attn", "gqa_chunk_attn",
+                                "qk_prep_chunk_attn", "gqa_attn_q8", "qk_prep_attn_q8"])
+def test_python_binding_takes_the_scale_from_the_caller(fn):
+    """The softmax scale is an argument of every attention call; the binding computes
+    no default (that would be the method's arithmetic outside the library)."""
+    import inspect
+    p = inspect.signature(getattr(pfa, fn)).parameters["scale"]
+    assert p.default is inspect.Parameter.empty and p.kind is inspect.Parameter.KEYWORD_ONLY
+
+
+@pytest.mark.parametrize("fn", ["qknorm_rope", "qk_prep_attn", "qk_prep_chunk_attn",
+                                "qk_prep_attn_q8"])
+def test_python_binding_checks_norm_weight_sizes(fn):
+    """The kernels read head_dim norm weights: a shorter tensor is a Python error, not an
+    out-of-bounds device read.  Checked before anything else (these are CPU tensors)."""
+    import torch
+    d = 64
+    q, k = torch.zeros(4, 2 * d), torch.zeros(4, d)
+    ok, short = torch.ones(d), torch.ones(d - 1)
+    rope = dict(head_dim=d, rope_dim=d, rope_freq_base=1e4, rms_eps=1e-6)
+    for wq, wk, bad in ((short, ok, "q_norm_w"), (ok, short, "k_norm_w")):
+        with pytest.raises(ValueError, match=bad):
+            if fn == "qknorm_rope":
+                pfa.qknorm_rope(q, k, wq, wk, **rope)
+            elif fn == "qk_prep_attn":
+                pfa.qk_prep_attn(q, k, k, wq, wk, scale=0.125, **rope)
+            elif fn == "qk_prep_chunk_attn":
+                pfa.qk_prep_chunk_attn(q, k, k, wq, wk, k, k, scale=0.125, **rope)
+            else:
+                c8 = torch.zeros(4, d, dtype=torch.int8)
+                s8 = torch.zeros(4, 1)
+                pfa.qk_prep_attn_q8(q, k, k, wq, wk, c8, s8, c8, s8, scale=0.125, **rope)
 
 
 def _ceil(a, b):

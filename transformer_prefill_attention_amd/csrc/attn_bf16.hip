@@ -450,18 +450,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     const int causal = geom.causal, H = geom.H, Hkv = geom.Hkv;
     const float qscale = geom.qscale;
     const int n_all = sched.n_tiles, tile0 = sched.tile_off[wi.sid];
-    const int nt_seq = (ks1 - ks0 + kBN - 1) / kBN;
-    const int n_tiles =
-        causal ? (min(q0 + sched.rows_per_item, s1) - 1 + dsh - ks0) / kBN + 1 : nt_seq;
-    // with a sliding window the item starts at its first row's first visible key
+    // key tiles of the item (with a sliding window it starts at its first row's first
+    // visible key); with a key split this workgroup takes tiles [t_begin, t_begin + n_local)
+    const KeyRange kr = item_key_range(sched, geom, wi, kBN);
+    const int nt_seq = kr.nt_seq, t_begin = kr.t_begin, n_local = kr.t_end - kr.t_begin;
     const int win = causal ? geom.window : 0;
-    const int t_first = win > 0 ? max(0, q0 + dsh - win + 1 - ks0) / kBN : 0;
-    // key split: this workgroup takes tiles [t_begin, t_begin + n_local) of the item
-    const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles - t_first;
-    const int n_chunks = (n_tiles - t_first + kchunk - 1) / kchunk;
-    if (wi.kc >= n_chunks) return;  // (uniform: the whole workgroup leaves)
-    const int t_begin = t_first + wi.kc * kchunk, n_local = min(kchunk, n_tiles - t_begin);
-    const bool split = n_chunks > 1;
+    if (n_local <= 0) return;  // (uniform: the whole workgroup leaves)
+    const bool split = kr.n_chunks > 1;
 
     const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;
     const int h = kv * geom.g + wi.chunk * geom.hpw + hloc;

@@ -141,21 +141,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     // (the lambdas below must not capture the kernel-argument structs: taking their
     // address copies them into scratch memory and makes every value read from them
     // look divergent; they use these locals instead)
-    const int rows_per_item = sched.rows_per_item;
     const int n_kv = geom.Hkv, n_q = geom.H;
     const float* const k_in = k;
-    const int nt_seq = (ks1 - ks0 + kBN - 1) / kBN;
-    const int n_tiles =
-        geom.causal ? (min(q0 + rows_per_item, s1) - 1 + dsh - ks0) / kBN + 1 : nt_seq;
-    // with a sliding window the item starts at its first row's first visible key
+    // key tiles of the item (with a sliding window it starts at its first row's first
+    // visible key); with a key split this workgroup takes tiles [t_begin, t_end)
+    const KeyRange kr = item_key_range(sched, geom, wi, kBN);
+    const int nt_seq = kr.nt_seq, t_begin = kr.t_begin, t_end = kr.t_end;
     const int win = geom.causal ? geom.window : 0;
-    const int t_first = win > 0 ? max(0, q0 + dsh - win + 1 - ks0) / kBN : 0;
-    // key split: this workgroup takes tiles [t_begin, t_end) of the item
-    const int kchunk = sched.kchunk > 0 ? sched.kchunk : n_tiles - t_first;
-    const int n_chunks = (n_tiles - t_first + kchunk - 1) / kchunk;
-    if (wi.kc >= n_chunks) return;  // (uniform: the whole workgroup leaves)
-    const int t_begin = t_first + wi.kc * kchunk, t_end = min(t_begin + kchunk, n_tiles);
-    const bool split = n_chunks > 1;
+    if (t_begin >= t_end) return;  // (uniform: the whole workgroup leaves)
+    const bool split = kr.n_chunks > 1;
 
     // ---- wavefront role
     const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;

@@ -36,15 +36,9 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(Partials part,
     w.item = bid / geom.chunks;
     w.kc = 0;
     decode_seq(sched, w);
-    const int s1 = w.s1, q0 = w.q0, ks0 = w.k0, dsh = w.k1 - w.s1;
-    // the item's key tiles and chunks, counted as the attention kernel counts them
-    const int nt_seq = (w.k1 - ks0 + tile_keys - 1) / tile_keys;
-    const int n_tiles =
-        geom.causal ? (min(q0 + sched.rows_per_item, s1) - 1 + dsh - ks0) / tile_keys + 1
-                    : nt_seq;
-    const int win = geom.causal ? geom.window : 0;
-    const int t_first = win > 0 ? max(0, q0 + dsh - win + 1 - ks0) / tile_keys : 0;
-    const int n_chunks = (n_tiles - t_first + sched.kchunk - 1) / sched.kchunk;
+    const int s1 = w.s1, q0 = w.q0;
+    // the item's key chunks, counted as the attention kernel counts them
+    const int n_chunks = item_key_range(sched, geom, w, tile_keys).n_chunks;
     if (n_chunks < 2) return;  // written directly by its only workgroup
     const int hloc = wave % geom.hpw, rblk = wave / geom.hpw;
     const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * (D / 8);

@@ -14,6 +14,7 @@
 #include <cstring>
 #include <initializer_list>
 
+#include "pfa_device.h"
 #include "pfa_internal.h"
 
 namespace {
@@ -399,6 +400,45 @@ static int check_attn(float scale, int precision) {
     return PFA_OK;
 }
 
+// Everything an attention call of the prefill / chunk entries decides on the host: the
+// geometry, schedule and key split (make_plan), whether the f32 key split is dropped for
+// want of workspace, paired items, and the workspace parts.  The entry points and the
+// plan report (pfa_attn_plan, pfa_attn_units) both come here, so they cannot disagree.
+struct CallPlan {
+    Plan p;
+    bool krot_in_ws = false;  // f32 fused prefill without k_rot_out: rotated K in the workspace
+    size_t base = 0;          // workspace bytes before the partial results
+    size_t part_off = 0;      // offset of the partial results
+    size_t need = 0;          // workspace bytes the call uses
+};
+
+// ws_bytes: the workspace the call is given (0 when none).
+static int plan_call(Mode mode, const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
+                     float scale, int causal, int window, int precision, bool has_k_rot_out,
+                     size_t ws_bytes, CallPlan& cp) {
+    Plan& p = cp.p;
+    int rc = make_plan(st, n_head, n_head_kv, head_dim, scale, causal, precision, p);
+    if (rc) return rc;
+    p.geom.window = window;
+    const bool bf16 = precision != PFA_PREC_F32;
+    const bool prep = mode == Mode::kFused || mode == Mode::kChunkFused;
+    const bool chunk = mode == Mode::kChunk || mode == Mode::kChunkFused;
+    // workspace parts: [bf16 K/V tiles + rotary table (Q prepared in the kernel), or f32
+    // rotated K (fused prefill without k_rot_out)][partials, key split]
+    cp.krot_in_ws = mode == Mode::kFused && !bf16 && !has_k_rot_out;
+    cp.base = prep_part_bytes(p, bf16, prep, cp.krot_in_ws);
+    cp.part_off = p.part_bytes ? align256(cp.base) : cp.base;
+    if (!bf16 && p.part_bytes && ws_bytes < cp.part_off + p.part_bytes) {
+        // f32 runs without the key split when the caller gives no (or too small a) workspace
+        p.sched.kchunk = 0;
+        p.sched.max_chunks = 1;
+        p.part_bytes = 0;
+    }
+    cp.need = p.part_bytes ? cp.part_off + p.part_bytes : cp.base;
+    p.sched.paired = !bf16 && pair_items(p, st, causal, window, chunk) ? 1 : 0;
+    return PFA_OK;
+}
+
 static int attn_common(Mode mode, const float* q, const float* k, const float* v, float* out,
                        float* k_cache, float* v_cache, const float* gate, int gate_per_head,
                        const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
@@ -434,27 +474,17 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
         if (overlaps(k_cache, cb, v_cache, cb))
             return fail(PFA_ERR_INVALID_ARG, "k_cache and v_cache overlap");
     }
-    Plan p;
+    CallPlan cp;
     int rc;
-    if ((rc = make_plan(st, n_head, n_head_kv, head_dim, scale, causal, precision, p))) return rc;
+    if ((rc = plan_call(mode, st, n_head, n_head_kv, head_dim, scale, causal, window, precision,
+                        prep && prep->k_rot_out, workspace ? workspace_bytes : 0, cp)))
+        return rc;
+    Plan& p = cp.p;
     if (p.items == 0) return PFA_OK;
-    p.geom.window = window;
     p.geom.gate = gate;
     p.geom.gate_per_head = gate_per_head ? 1 : 0;
     const bool bf16 = precision != PFA_PREC_F32;
-    // workspace parts: [bf16 K/V tiles + rotary table (Q prepared here), or f32 rotated K
-    // (fused prefill without k_rot_out)][partials, key split]
-    const bool krot_in_ws = mode == Mode::kFused && !bf16 && !prep->k_rot_out;
-    const size_t base = prep_part_bytes(p, bf16, prep != nullptr, krot_in_ws);
-    const size_t part_off = p.part_bytes ? align256(base) : base;
-    if (!bf16 && p.part_bytes &&
-        (!workspace || workspace_bytes < part_off + p.part_bytes)) {
-        // f32 runs without the key split when the caller gives no (or too small a) workspace
-        p.sched.kchunk = 0;
-        p.sched.max_chunks = 1;
-        p.part_bytes = 0;
-    }
-    const size_t need = p.part_bytes ? part_off + p.part_bytes : base;
+    const size_t part_off = cp.part_off, need = cp.need;
     if (need > 0) {
         if (!workspace)
             return fail(PFA_ERR_INVALID_ARG, "precision %d needs a workspace (%zu bytes)",
@@ -519,8 +549,6 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
             return rc;
         k_attn = krot;
     }
-    p.sched.paired =
-        pair_items(p, st, causal, window, mode == Mode::kChunk || chunk_fused) ? 1 : 0;
     return hip_status(pfa::launch_attn_f32(q, k_attn, v_attn, out, p.sched, p.geom, head_dim, prep,
                                            part, p.items, (hipStream_t)stream),
                       what);
@@ -819,6 +847,183 @@ int qk_prep_attn_q8(const float* q, const float* k, const float* v, float* out,
     return attn_q8_common(true, in, q, k, v, out, gate, gate_per_head, st, n_head, n_head_kv,
                           head_dim, scale, causal, window, &prep, workspace, workspace_bytes,
                           stream);
+}
+
+// ---------------------------------------------------------------------------
+// Plan report: what an attention call would enqueue, decided by the same host code the
+// entry points run (plan_call / make_plan), and the work unit every attention
+// workgroup decodes (the kernels' own decode, compiled for the host too).
+
+namespace {
+
+// Rotary pairing of the QK-norm + RoPE kernel (its template argument): both halves of a
+// pair in one lane (rope_dim = head_dim = 128), partner lane ^ 32 (rope_dim 64), general.
+int qknorm_mode(int head_dim, int rope_dim) {
+    if (head_dim == 128 && rope_dim == 128) return 0;
+    return rope_dim == 64 ? 1 : 2;
+}
+
+void append(char* buf, size_t n, const char* fmt, ...) {
+    const size_t used = strlen(buf);
+    if (used + 1 >= n) return;
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf + used, n - used, fmt, ap);
+    va_end(ap);
+}
+
+// Names of the kernels one call enqueues, in order (as the launchers instantiate them).
+void kernel_names(int entry, int precision, int D, int rope_dim, const Plan& p, char* buf,
+                  size_t n) {
+    buf[0] = 0;
+    const bool fused = entry == PFA_ENTRY_PREP || entry == PFA_ENTRY_CHUNK_PREP ||
+                       entry == PFA_ENTRY_Q8_PREP;
+    const bool split_keys = p.sched.max_chunks > 1;
+    const char* sep = "";
+    if (entry == PFA_ENTRY_Q8 || entry == PFA_ENTRY_Q8_PREP) {
+        if (fused) {
+            append(buf, n, "qknorm_rope_kernel<%d,%d,true>", D, qknorm_mode(D, rope_dim));
+            sep = " + ";
+        }
+        append(buf, n, "%sstage_kv_q8_kernel<%d,%s> + attn_bf16_kernel<%d,false,false,true>", sep,
+               D, D == 128 ? "true" : "false", D);
+    } else if (precision == PFA_PREC_F32) {
+        if (fused) {
+            append(buf, n, "qknorm_rope_kernel<%d,%d,false> + ", D, qknorm_mode(D, rope_dim));
+        }
+        append(buf, n, "attn_f32_kernel<%d,%s,%s>", D, fused ? "true" : "false",
+               p.sched.paired ? "true" : "false");
+    } else {
+        const char* sp = precision == PFA_PREC_BF16X3 ? "true" : "false";
+        if (entry == PFA_ENTRY_CHUNK_PREP) {
+            append(buf, n, "qknorm_rope_kernel<%d,%d,false> + ", D, qknorm_mode(D, rope_dim));
+        }
+        if (fused) append(buf, n, "rope_table_kernel<%d,%s> + ", D, sp);
+        append(buf, n, "stage_kv_bf16_kernel<%d,%s,%s> + attn_bf16_kernel<%d,%s,%s,false>", D, sp,
+               entry == PFA_ENTRY_PREP ? "true" : "false", D, sp, fused ? "true" : "false");
+    }
+    if (split_keys) append(buf, n, " + attn_combine_kernel<%d>", D);
+}
+
+// Arguments of a plan query -> sequence table and plan (what the entry point would do).
+int plan_query(int entry, const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+               int T_q, int T_kv, int n_head, int n_head_kv, int head_dim, int rope_dim,
+               int causal, int window, int precision, int has_k_rot_out, size_t ws_bytes,
+               CallPlan& cp, pfa::SeqTable& st, size_t& need) {
+    int rc;
+    if (entry < PFA_ENTRY_PREFILL || entry > PFA_ENTRY_Q8_PREP)
+        return fail(PFA_ERR_INVALID_ARG, "unknown entry %d", entry);
+    const bool prefill = entry == PFA_ENTRY_PREFILL || entry == PFA_ENTRY_PREP;
+    const bool q8 = entry == PFA_ENTRY_Q8 || entry == PFA_ENTRY_Q8_PREP;
+    const bool fused = entry == PFA_ENTRY_PREP || entry == PFA_ENTRY_CHUNK_PREP ||
+                       entry == PFA_ENTRY_Q8_PREP;
+    if (prefill) T_kv = T_q;
+    if ((rc = check_geometry(T_q, n_head, n_head_kv, head_dim)) ||
+        (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim)))
+        return rc;
+    if (q8) precision = PFA_PREC_BF16;  // the 8-bit kernels run on the bf16 schedule
+    if ((rc = check_attn(1.0f, precision))) return rc;
+    if (!prefill && (rc = check_window(window, causal))) return rc;
+    if (fused && (rc = check_rope(head_dim, rope_dim, 1e4f, 0.0f))) return rc;
+    if (prefill) {
+        if ((rc = build_seqs(q_offsets, n_seqs, T_q, st))) return rc;
+        window = 0;
+    } else if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) {
+        return rc;
+    }
+    static const Mode modes[4] = {Mode::kPlain, Mode::kFused, Mode::kChunk, Mode::kChunkFused};
+    const Mode mode = q8 ? Mode::kChunk : modes[entry];
+    if ((rc = plan_call(mode, st, n_head, n_head_kv, head_dim, 1.0f, causal, window, precision,
+                        has_k_rot_out != 0, ws_bytes, cp)))
+        return rc;
+    need = q8 ? (cp.p.items ? q8_layout(cp.p, T_q, n_head, head_dim, fused).need : 0)
+              : (cp.p.items ? cp.need : 0);
+    return PFA_OK;
+}
+
+}  // namespace
+
+int pfa_attn_plan(int entry, const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                  int T_q, int T_kv, int n_head, int n_head_kv, int head_dim, int rope_dim,
+                  int causal, int window, int precision, int has_k_rot_out,
+                  size_t workspace_bytes, pfa_plan* plan) {
+    g_err[0] = 0;
+    if (!plan) return fail(PFA_ERR_INVALID_ARG, "null plan pointer");
+    memset(plan, 0, sizeof(*plan));
+    CallPlan cp;
+    pfa::SeqTable st;
+    size_t need = 0;
+    int rc = plan_query(entry, q_offsets, kv_offsets, n_seqs, T_q, T_kv, n_head, n_head_kv,
+                        head_dim, rope_dim, causal, window, precision, has_k_rot_out,
+                        workspace_bytes, cp, st, need);
+    if (rc) return rc;
+    const Plan& p = cp.p;
+    plan->items = p.items;
+    plan->rows_per_item = p.sched.rows_per_item;
+    plan->waves_per_workgroup = p.waves;
+    plan->tile_keys = p.tile_keys;
+    plan->key_chunk_tiles = p.sched.kchunk;
+    plan->max_key_chunks = p.sched.max_chunks;
+    plan->paired = p.sched.paired;
+    const long long slots =
+        p.sched.paired ? (p.items + 1) / 2 : (long long)p.items * p.sched.max_chunks;
+    plan->workgroups = p.items ? slots * p.geom.chunks * p.geom.Hkv : 0;
+    plan->workspace_bytes = need;
+    const bool q8 = entry == PFA_ENTRY_Q8 || entry == PFA_ENTRY_Q8_PREP;
+    if (p.items)
+        kernel_names(entry, q8 ? PFA_PREC_BF16 : precision, head_dim, rope_dim, p, plan->kernels,
+                     sizeof(plan->kernels));
+    return PFA_OK;
+}
+
+int64_t pfa_attn_units(int entry, const int32_t* q_offsets, const int32_t* kv_offsets,
+                       int n_seqs, int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                       int rope_dim, int causal, int window, int precision, int has_k_rot_out,
+                       size_t workspace_bytes, int32_t* records, int64_t max_records) {
+    g_err[0] = 0;
+    if (max_records < 0 || (max_records > 0 && !records))
+        return fail(PFA_ERR_INVALID_ARG, "records: null with max_records > 0");
+    CallPlan cp;
+    pfa::SeqTable st;
+    size_t need = 0;
+    int rc = plan_query(entry, q_offsets, kv_offsets, n_seqs, T_q, T_kv, n_head, n_head_kv,
+                        head_dim, rope_dim, causal, window, precision, has_k_rot_out,
+                        workspace_bytes, cp, st, need);
+    if (rc) return rc;
+    const Plan& p = cp.p;
+    if (p.items == 0) return 0;
+    const int hk = p.geom.chunks * p.geom.Hkv;
+    const long long slots =
+        p.sched.paired ? (p.items + 1) / 2 : (long long)p.items * p.sched.max_chunks;
+    const long long n_wg = slots * hk;
+    int64_t n_rec = 0;
+    for (long long wg = 0; wg < n_wg; ++wg) {
+        // the paired f32 kernel: slot j takes item j, then item n - 1 - j (see attn_f32.hip)
+        int bids[2] = {(int)wg, -1};
+        if (p.sched.paired) {
+            const int j = (int)(wg / hk), j2 = p.items - 1 - j;
+            if (j2 > j) bids[1] = j2 * hk + (int)(wg % hk);
+        }
+        for (int pass = 0; pass < 2 && bids[pass] >= 0; ++pass) {
+            const pfa::WorkItem wi = pfa::decode_item(p.sched, p.geom, bids[pass]);
+            const pfa::KeyRange kr = pfa::item_key_range(p.sched, p.geom, wi, p.tile_keys);
+            if (n_rec < max_records) {
+                int32_t* r = records + n_rec * PFA_UNIT_FIELDS;
+                r[0] = (int32_t)wg;
+                r[1] = pass;
+                r[2] = wi.item;
+                r[3] = wi.sid;
+                r[4] = wi.sb;
+                r[5] = wi.kc;
+                r[6] = wi.kv;
+                r[7] = wi.chunk;
+                r[8] = kr.t_begin;
+                r[9] = kr.t_end;
+            }
+            ++n_rec;
+        }
+    }
+    return n_rec;
 }
 
 }  // extern "C"

@@ -145,8 +145,10 @@ struct WorkItem {
 };
 
 // item -> sequence and super-block (segment decode of the longest-first order).
+// Host and device: the library's plan report (pfa_attn_units) decodes the grid with
+// the same code the kernels run.
 template <class Sched>
-__device__ __forceinline__ void decode_seq(const Sched& sched, WorkItem& w) {
+__host__ __device__ __forceinline__ void decode_seq(const Sched& sched, WorkItem& w) {
     int seg = 0;
     while (w.item >= sched.seg_start[seg + 1]) ++seg;
     const int local = w.item - sched.seg_start[seg];
@@ -165,7 +167,7 @@ __device__ __forceinline__ void decode_seq(const Sched& sched, WorkItem& w) {
 // workgroups that the dispatcher deals to the 8 XCDs in turn share heads), then
 // the head chunk, then the key chunk, and the longest-first item order slowest.
 template <class Sched, class Geom>
-__device__ __forceinline__ WorkItem decode_item(const Sched& sched, const Geom& geom, int bid) {
+__host__ __device__ __forceinline__ WorkItem decode_item(const Sched& sched, const Geom& geom, int bid) {
     WorkItem w;
     w.kv = bid % geom.Hkv;
     bid /= geom.Hkv;
@@ -175,6 +177,37 @@ __device__ __forceinline__ WorkItem decode_item(const Sched& sched, const Geom& 
     w.item = bid / sched.max_chunks;
     decode_seq(sched, w);
     return w;
+}
+
+// The key tiles (of tile_keys keys) a work unit visits.  Causal: an item's tiles run to
+// its last query row's last visible key; with a sliding window they start at its first
+// row's first visible key.  With a key split (sched.kchunk > 0) the item's tiles are cut
+// into chunks of kchunk tiles and the unit takes chunk wi.kc: tiles [t_begin, t_end).
+// A unit whose chunk lies past the item's tiles has t_begin >= t_end (it does nothing).
+struct KeyRange {
+    int nt_seq;    // tiles over the sequence's key rows
+    int n_tiles;   // one past the item's last tile
+    int t_first;   // the item's first tile
+    int n_chunks;  // key chunks of the item (1: not split)
+    int t_begin, t_end;
+};
+template <class Sched, class Geom>
+__host__ __device__ __forceinline__ KeyRange item_key_range(const Sched& sched, const Geom& geom,
+                                                            const WorkItem& wi, int tile_keys) {
+    KeyRange r;
+    const int dsh = wi.k1 - wi.s1;  // query row i sees keys <= i + dsh
+    r.nt_seq = (wi.k1 - wi.k0 + tile_keys - 1) / tile_keys;
+    const int last_row = (wi.q0 + sched.rows_per_item < wi.s1 ? wi.q0 + sched.rows_per_item
+                                                               : wi.s1) - 1;
+    r.n_tiles = geom.causal ? (last_row + dsh - wi.k0) / tile_keys + 1 : r.nt_seq;
+    const int win = geom.causal ? geom.window : 0;
+    const int lo = wi.q0 + dsh - win + 1 - wi.k0;
+    r.t_first = win > 0 ? (lo > 0 ? lo : 0) / tile_keys : 0;
+    const int kchunk = sched.kchunk > 0 ? sched.kchunk : r.n_tiles - r.t_first;
+    r.n_chunks = (r.n_tiles - r.t_first + kchunk - 1) / kchunk;
+    r.t_begin = r.t_first + wi.kc * kchunk;
+    r.t_end = r.t_begin + kchunk < r.n_tiles ? r.t_begin + kchunk : r.n_tiles;
+    return r;
 }
 
 }  // namespace pfa

@@ -3,7 +3,8 @@
 Argument marshalling only: shapes, dtypes and devices are checked, output
 tensors are allocated with torch when the caller passes none, and the C entry
 point of the same name is called with raw device pointers and the current torch
-stream.  Every step of the computation runs in the library's HIP kernels; there
+stream.  Every attention call takes its softmax ``scale`` from the caller (the
+pages' models pass 1/sqrt(head_dim)); the binding computes nothing of the method.  Every step of the computation runs in the library's HIP kernels; there
 is no fallback of any kind -- if the library is missing, every op raises.
 """
 from __future__ import annotations
@@ -29,7 +30,22 @@ _PRECISIONS = {"f32": PRECISION_F32, "fp32": PRECISION_F32, "float32": PRECISION
 EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_workspace_bytes",
            "gqa_chunk_attn", "qk_prep_chunk_attn", "pfa_chunk_workspace_bytes",
            "pfa_quantize_rows", "gqa_attn_q8", "qk_prep_attn_q8", "pfa_q8_workspace_bytes",
-           "pfa_last_error", "pfa_version")
+           "pfa_attn_plan", "pfa_attn_units", "pfa_last_error", "pfa_version")
+
+# pfa_entry values of the plan report
+ENTRY_PREFILL, ENTRY_PREP, ENTRY_CHUNK, ENTRY_CHUNK_PREP, ENTRY_Q8, ENTRY_Q8_PREP = range(6)
+UNIT_FIELDS = ("workgroup", "pass", "item", "sequence", "super_block", "key_chunk", "kv_head",
+               "head_chunk", "tile_begin", "tile_end")
+
+
+class _Plan(ctypes.Structure):
+    """pfa_plan of include/pfa.h."""
+    _fields_ = [("items", ctypes.c_int), ("rows_per_item", ctypes.c_int),
+                ("waves_per_workgroup", ctypes.c_int), ("tile_keys", ctypes.c_int),
+                ("key_chunk_tiles", ctypes.c_int), ("max_key_chunks", ctypes.c_int),
+                ("paired", ctypes.c_int), ("reserved", ctypes.c_int),
+                ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+                ("kernels", ctypes.c_char * 320)]
 
 
 class PfaError(RuntimeError):
@@ -86,6 +102,11 @@ def lib() -> ctypes.CDLL:
     L.qk_prep_attn_q8.restype = i32
     L.pfa_q8_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_q8_workspace_bytes.restype = sz
+    plan_args = [i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, sz]
+    L.pfa_attn_plan.argtypes = plan_args + [ctypes.POINTER(_Plan)]
+    L.pfa_attn_plan.restype = i32
+    L.pfa_attn_units.argtypes = plan_args + [vp, i64]
+    L.pfa_attn_units.restype = i64
     L.pfa_last_error.argtypes = []
     L.pfa_version.restype = ctypes.c_char_p
     L.pfa_version.argtypes = []
@@ -127,6 +148,20 @@ def _dev_f32(t, name):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _norm_weights(q_norm_w, k_norm_w, head_dim):
+    """The QK-norm weights must hold head_dim floats each (the kernels read all of them):
+    checked first, before the device and dtype checks of every tensor."""
+    import torch
+    ws = ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"))
+    for t, n in ws:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor")
+        if t.numel() != head_dim:
+            raise ValueError(f"{n} must have head_dim = {head_dim} elements, got {t.numel()}")
+    for t, n in ws:
+        _dev_f32(t, n)
 
 
 def _heads(t, head_dim, name):
@@ -186,6 +221,7 @@ def qknorm_rope(q, k, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
 
     Returns ``(q_out, k_out)``; pass ``q_out=q, k_out=k`` to work in place."""
     import torch
+    _norm_weights(q_norm_w, k_norm_w, head_dim)
     for t, n in ((q, "q"), (k, "k"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
         _dev_f32(t, n)
     T, H = _heads(q, head_dim, "q")
@@ -203,7 +239,7 @@ def qknorm_rope(q, k, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
     return q_out, k_out
 
 
-def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
+def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: float,
                      causal: bool = True, precision="f32",
                      seq_offsets: Optional[Sequence[int]] = None, out=None, workspace=None):
     """Causal GQA attention (``gqa_prefill_attn`` in ``include/pfa.h``); returns ``out``.
@@ -220,8 +256,6 @@ def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
     out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
     if out.numel() != q.numel():
         raise ValueError("out must have q's shape")
-    if scale is None:
-        scale = head_dim ** -0.5
     offs, n_seqs, op = _offsets(seq_offsets, T)
     prec = _prec(precision)
     ws, wp, wn = _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, False, q.device)
@@ -232,7 +266,7 @@ def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: Optional[float] = None,
 
 
 def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
-                 rope_freq_base: float, rms_eps: float, scale: Optional[float] = None,
+                 rope_freq_base: float, rms_eps: float, scale: float,
                  causal: bool = True, precision="f32",
                  seq_offsets: Optional[Sequence[int]] = None, out=None, k_rot_out=None,
                  workspace=None):
@@ -242,6 +276,7 @@ def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
     workspace (``workspace_bytes(..., fused=True)`` bytes) is ``workspace`` or one
     taken from torch's allocator."""
     import torch
+    _norm_weights(q_norm_w, k_norm_w, head_dim)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
         _dev_f32(t, n)
     T, H = _heads(q, head_dim, "q")
@@ -255,8 +290,6 @@ def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
         _dev_f32(k_rot_out, "k_rot_out")
         if k_rot_out.numel() != k.numel():
             raise ValueError("k_rot_out must have k's shape")
-    if scale is None:
-        scale = head_dim ** -0.5
     offs, n_seqs, op = _offsets(seq_offsets, T)
     prec = _prec(precision)
     ws, wp, wn = _workspace(workspace, op, n_seqs, T, H, Hkv, head_dim, prec, True, q.device)
@@ -314,7 +347,7 @@ def _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, pre
     return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
 
 
-def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float] = None,
+def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: float,
                    causal: bool = True, window: int = 0, gate=None, precision="f32",
                    q_offsets=None, kv_offsets=None, out=None, workspace=None):
     """Attention of new query rows over a K/V cache (``gqa_chunk_attn`` in
@@ -333,8 +366,6 @@ def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float]
     out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
     if out.numel() != q.numel():
         raise ValueError("out must have q's shape")
-    if scale is None:
-        scale = head_dim ** -0.5
     keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
     prec = _prec(precision)
     ws, wp, wn = _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec,
@@ -348,7 +379,7 @@ def gqa_chunk_attn(q, k_cache, v_cache, *, head_dim: int, scale: Optional[float]
 
 def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_dim: int,
                        rope_dim: int, rope_freq_base: float, rms_eps: float,
-                       scale: Optional[float] = None, causal: bool = True, window: int = 0,
+                       scale: float, causal: bool = True, window: int = 0,
                        gate=None, precision="f32", q_offsets=None, kv_offsets=None, out=None,
                        workspace=None):
     """Fused QK-norm + RoPE of the raw new rows at their positions, their K and V written
@@ -356,6 +387,7 @@ def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_di
     attention over the cache (``qk_prep_chunk_attn`` in ``include/pfa.h``); returns
     ``out``."""
     import torch
+    _norm_weights(q_norm_w, k_norm_w, head_dim)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev_f32(t, n)
@@ -369,8 +401,6 @@ def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_di
     out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
     if out.numel() != q.numel():
         raise ValueError("out must have q's shape")
-    if scale is None:
-        scale = head_dim ** -0.5
     keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
     prec = _prec(precision)
     ws, wp, wn = _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec,
@@ -459,7 +489,7 @@ def _q8_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, fused,
 
 
 def gqa_attn_q8(q, q_scale, k_cache, k_scale, v_cache, v_scale, *, head_dim: int,
-                scale: Optional[float] = None, causal: bool = True, window: int = 0, gate=None,
+                scale: float, causal: bool = True, window: int = 0, gate=None,
                 q_offsets=None, kv_offsets=None, out=None, workspace=None):
     """Attention through 8-bit stores (``gqa_attn_q8`` in ``include/pfa.h``); returns
     ``out`` (f32).  Offsets, window and gate as for :func:`gqa_chunk_attn`."""
@@ -472,8 +502,6 @@ def gqa_attn_q8(q, q_scale, k_cache, k_scale, v_cache, v_scale, *, head_dim: int
         if out is None else _dev_f32(out, "out")
     if out.numel() != q.numel():
         raise ValueError("out must have q's shape")
-    if scale is None:
-        scale = head_dim ** -0.5
     keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
     ws, wp, wn = _q8_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, False,
                                q.device)
@@ -487,13 +515,14 @@ def gqa_attn_q8(q, q_scale, k_cache, k_scale, v_cache, v_scale, *, head_dim: int
 
 def qk_prep_attn_q8(q, k, v, q_norm_w, k_norm_w, k_cache, k_scale, v_cache, v_scale, *,
                     head_dim: int, rope_dim: int, rope_freq_base: float, rms_eps: float,
-                    scale: Optional[float] = None, causal: bool = True, window: int = 0,
+                    scale: float, causal: bool = True, window: int = 0,
                     gate=None, q_offsets=None, kv_offsets=None, out=None, workspace=None):
     """A quantised session's step (``qk_prep_attn_q8`` in ``include/pfa.h``): QK-norm +
     RoPE of the raw new rows, Q, K and V quantised per (token, head), K and V appended
     to the 8-bit store (the last rows of each sequence's range), attention through the
     store; returns ``out`` (f32)."""
     import torch
+    _norm_weights(q_norm_w, k_norm_w, head_dim)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
         _dev_f32(t, n)
     T_q, H = _heads(q, head_dim, "q")
@@ -506,8 +535,6 @@ def qk_prep_attn_q8(q, k, v, q_norm_w, k_norm_w, k_cache, k_scale, v_cache, v_sc
     out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
     if out.numel() != q.numel():
         raise ValueError("out must have q's shape")
-    if scale is None:
-        scale = head_dim ** -0.5
     keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
     ws, wp, wn = _q8_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, True,
                                q.device)
@@ -518,3 +545,59 @@ def qk_prep_attn_q8(q, k, v, q_norm_w, k_norm_w, k_cache, k_scale, v_cache, v_sc
                                  rope_dim, float(rope_freq_base), float(rms_eps), float(scale),
                                  1 if causal else 0, int(window), wp, wn, _stream(q)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Plan report (pfa_attn_plan / pfa_attn_units): what an attention call would enqueue.
+
+def _plan_args(entry, T_q, n_head, n_head_kv, head_dim, rope_dim, T_kv, causal, window,
+               precision, q_offsets, kv_offsets, has_k_rot_out, workspace_bytes):
+    if entry not in (ENTRY_CHUNK, ENTRY_CHUNK_PREP, ENTRY_Q8, ENTRY_Q8_PREP):
+        # the prefill entries (an unknown entry is left to the library to reject)
+        keep, n_seqs, qp = _offsets(q_offsets, T_q)
+        kp, T_kv = None, T_q
+    else:
+        if T_kv is None:
+            raise ValueError("the chunk and 8-bit entries need T_kv")
+        keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
+    prec = _prec(precision) if entry not in (ENTRY_Q8, ENTRY_Q8_PREP) else PRECISION_BF16
+    ws = (1 << 64) - 1 if workspace_bytes is None else int(workspace_bytes)
+    return keep, (int(entry), qp, kp, n_seqs, int(T_q), int(T_kv), int(n_head), int(n_head_kv),
+                  int(head_dim), int(rope_dim if rope_dim is not None else head_dim),
+                  1 if causal else 0, int(window), prec, 1 if has_k_rot_out else 0, ws)
+
+
+def attn_plan(entry: int, *, T_q: int, n_head: int, n_head_kv: int, head_dim: int,
+              rope_dim: Optional[int] = None, T_kv: Optional[int] = None, causal: bool = True,
+              window: int = 0, precision="f32", q_offsets=None, kv_offsets=None,
+              has_k_rot_out: bool = False, workspace_bytes: Optional[int] = None) -> dict:
+    """What one call of entry point ``entry`` (``ENTRY_*``) would enqueue for these
+    arguments (``pfa_attn_plan``): work items, key split, pairing, grid, workspace bytes and
+    the kernels in launch order.  ``workspace_bytes`` None: the call gets enough."""
+    keep, args = _plan_args(entry, T_q, n_head, n_head_kv, head_dim, rope_dim, T_kv, causal,
+                            window, precision, q_offsets, kv_offsets, has_k_rot_out,
+                            workspace_bytes)
+    plan = _Plan()
+    _check(lib().pfa_attn_plan(*args, ctypes.byref(plan)))
+    res = {name: getattr(plan, name) for name, _ in _Plan._fields_ if name != "reserved"}
+    res["kernels"] = plan.kernels.decode()
+    return res
+
+
+def attn_units(entry: int, *, T_q: int, n_head: int, n_head_kv: int, head_dim: int,
+               rope_dim: Optional[int] = None, T_kv: Optional[int] = None, causal: bool = True,
+               window: int = 0, precision="f32", q_offsets=None, kv_offsets=None,
+               has_k_rot_out: bool = False, workspace_bytes: Optional[int] = None) -> np.ndarray:
+    """The work unit of every attention workgroup (``pfa_attn_units``): an int32 array of
+    one row per (workgroup, item it takes), columns :data:`UNIT_FIELDS`."""
+    keep, args = _plan_args(entry, T_q, n_head, n_head_kv, head_dim, rope_dim, T_kv, causal,
+                            window, precision, q_offsets, kv_offsets, has_k_rot_out,
+                            workspace_bytes)
+    n = int(lib().pfa_attn_units(*args, None, 0))
+    if n < 0:
+        _check(n)
+    rec = np.zeros((max(n, 1), len(UNIT_FIELDS)), dtype=np.int32)
+    m = int(lib().pfa_attn_units(*args, rec.ctypes.data_as(ctypes.c_void_p), n))
+    if m != n:
+        raise PfaError(-100, f"pfa_attn_units returned {m} records, then {n}")
+    return rec[:n]
