@@ -1,0 +1,223 @@
+"""Out-of-bounds write guards for every entry point (through the C ABI).
+
+Every tensor and workspace a call touches is carved out of a larger device buffer with
+4 KiB of sentinel bytes on each side.  After the call the sentinels must be intact -- no
+kernel wrote outside the buffers it was given -- the read-only inputs must be unchanged,
+and every element of every output must have been written (outputs start as NaN).
+Shapes with and without the key split (short inputs cut an item's keys over several
+workgroups whose partial results live in the workspace), packed sequences with empty
+ones and ragged tails, both head sizes.  The values themselves are checked elsewhere
+against the oracle; here only where the bytes went.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_prefill_attention_amd as pfa
+from transformer_prefill_attention_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096
+SENTINEL = 0xC3
+
+
+class Guarded:
+    """Device tensors with sentinel bands before and after them."""
+
+    def __init__(self):
+        self.bufs = []
+        self.inputs = []
+
+    def alloc(self, name, shape, dtype, init=None):
+        esz = torch.empty((), dtype=dtype).element_size()
+        n = int(math.prod(shape)) * esz
+        buf = torch.full((GUARD + n + GUARD,), SENTINEL, dtype=torch.uint8, device="cuda:0")
+        inner = buf[GUARD:GUARD + n].view(dtype).view(shape)
+        if init is None:
+            if dtype.is_floating_point:
+                inner.fill_(float("nan"))
+        else:
+            inner.copy_(torch.as_tensor(init).reshape(shape))
+        self.bufs.append((name, buf, n))
+        return inner
+
+    def input(self, name, array):
+        a = np.ascontiguousarray(array)
+        t = self.alloc(name, a.shape, torch.from_numpy(a[:0]).dtype, torch.from_numpy(a))
+        self.inputs.append((name, t, torch.from_numpy(a).clone()))
+        return t
+
+    def workspace(self, nbytes):
+        return None if nbytes == 0 else self.alloc("workspace", (nbytes,), torch.uint8,
+                                                   torch.zeros(nbytes, dtype=torch.uint8))
+
+    def check(self, what, outputs=()):
+        torch.cuda.synchronize()
+        for name, buf, n in self.bufs:
+            head, tail = buf[:GUARD], buf[GUARD + n:]
+            bad = int((head != SENTINEL).sum()) + int((tail != SENTINEL).sum())
+            assert bad == 0, f"{what}: {bad} bytes written outside {name}"
+        for name, t, orig in self.inputs:
+            assert torch.equal(t.cpu(), orig), f"{what}: input {name} was modified"
+        for name, t in outputs:
+            assert bool(torch.isfinite(t).all()), f"{what}: {name} has unwritten elements"
+        print(f"{what}: guards intact on {len(self.bufs)} buffers", flush=True)
+
+
+PREFILL = [
+    # (name, seq_lens, H, Hkv, d, n): split at 0.6B-like T = 512, unsplit at 1500 / packed
+    ("split_512", (512,), 16, 8, 128, 128),
+    ("packed_ragged", (300, 0, 1, 777, 65), 8, 2, 128, 64),
+    ("d64_split", (100, 37), 8, 2, 64, 64),
+    ("unsplit_2048", (2048,), 32, 8, 128, 128),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=[c[0] for c in PREFILL])
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3"])
+def test_prefill_entry_points_write_only_their_outputs(case, precision):
+    name, lens, H, Hkv, d, n = case
+    w = wl.Workload(name, lens, H, Hkv, d, n, 1e6, 1e-6, seed=1600)
+    x = wl.make_inputs(w)
+    T, offs = w.T, w.seq_offsets
+    rope = dict(head_dim=d, rope_dim=n, rope_freq_base=w.rope_freq_base, rms_eps=w.rms_eps,
+                seq_offsets=offs)
+    plan = pfa.attn_plan(pfa.ENTRY_PREFILL, T_q=T, n_head=H, n_head_kv=Hkv, head_dim=d,
+                         precision=precision, q_offsets=offs)
+    print(f"{name} {precision}: key chunks {plan['max_key_chunks']}, kernels "
+          f"{plan['kernels']}", flush=True)
+    # qknorm_rope (out of place)
+    g = Guarded()
+    q, k = g.input("q", x.q), g.input("k", x.k)
+    wq, wk = g.input("wq", x.wq), g.input("wk", x.wk)
+    qo, ko = g.alloc("q_out", x.q.shape, torch.float32), g.alloc("k_out", x.k.shape, torch.float32)
+    pfa.qknorm_rope(q, k, wq, wk, q_out=qo, k_out=ko, **rope)
+    g.check(f"qknorm_rope {name}", [("q_out", qo), ("k_out", ko)])
+    # gqa_prefill_attn
+    g = Guarded()
+    q, k, v = g.input("q", x.q), g.input("k", x.k), g.input("v", x.v)
+    out = g.alloc("out", x.q.shape, torch.float32)
+    ws = g.workspace(pfa.workspace_bytes(T, H, Hkv, d, precision, seq_offsets=offs))
+    pfa.gqa_prefill_attn(q, k, v, head_dim=d, scale=w.softmax_scale, precision=precision,
+                         seq_offsets=offs, out=out, workspace=ws)
+    g.check(f"gqa_prefill_attn {name} {precision}", [("out", out)])
+    # qk_prep_attn with k_rot_out, and (f32) without it: the rotated K then goes to the
+    # workspace
+    for with_krot in (True, False):
+        g = Guarded()
+        q, k, v = g.input("q", x.q), g.input("k", x.k), g.input("v", x.v)
+        wq, wk = g.input("wq", x.wq), g.input("wk", x.wk)
+        out = g.alloc("out", x.q.shape, torch.float32)
+        krot = g.alloc("k_rot_out", x.k.shape, torch.float32) if with_krot else None
+        ws = g.workspace(pfa.workspace_bytes(T, H, Hkv, d, precision, seq_offsets=offs,
+                                             fused=True))
+        pfa.qk_prep_attn(q, k, v, wq, wk, scale=w.softmax_scale, precision=precision,
+                         out=out, k_rot_out=krot, workspace=ws, **rope)
+        outs = [("out", out)] + ([("k_rot_out", krot)] if with_krot else [])
+        g.check(f"qk_prep_attn {name} {precision} k_rot_out={with_krot}", outs)
+
+
+CHUNK = [
+    # (name, new rows per sequence, cached rows before them, H, Hkv, d, n, window)
+    ("one_row_split", (1,), (3000,), 8, 2, 128, 128, 0),
+    ("packed", (50, 0, 130, 7), (20, 77, 0, 5), 8, 4, 128, 64, 0),
+    ("window", (300,), (900,), 8, 2, 128, 128, 100),
+    ("d64", (90, 1), (45, 500), 4, 2, 64, 64, 0),
+]
+
+
+def _chunk_inputs(case, seed=1700):
+    name, lens, bases, H, Hkv, d, n, window = case
+    full = tuple(b + m for b, m in zip(bases, lens))
+    w = wl.Workload(name, full, H, Hkv, d, n, 1e6, 1e-6, seed=seed)
+    x = wl.make_inputs(w)
+    kv_offs = w.seq_offsets
+    q_offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    new = np.concatenate([np.arange(kv_offs[s] + bases[s], kv_offs[s + 1])
+                          for s in range(len(lens))]).astype(np.int64)
+    return w, x, q_offs, kv_offs, new
+
+
+@pytest.mark.parametrize("case", CHUNK, ids=[c[0] for c in CHUNK])
+@pytest.mark.parametrize("precision", ["f32", "bf16"])
+def test_chunk_entry_points_write_only_their_outputs(case, precision):
+    name, lens, bases, H, Hkv, d, n, window = case
+    w, x, q_offs, kv_offs, new = _chunk_inputs(case)
+    T_q, T_kv = int(q_offs[-1]), int(kv_offs[-1])
+    offs = dict(q_offsets=q_offs, kv_offsets=kv_offs)
+    rng = np.random.default_rng(1701)
+    gate = rng.standard_normal((T_q, H)).astype(np.float32)
+    # gqa_chunk_attn over a cache (the raw rows stand in for prepared ones: only the
+    # bytes' destinations matter here), gated per head
+    g = Guarded()
+    q = g.input("q", x.q[new])
+    kc, vc = g.input("k_cache", x.k), g.input("v_cache", x.v)
+    gt = g.input("gate", gate)
+    out = g.alloc("out", (T_q, H * d), torch.float32)
+    ws = g.workspace(pfa.chunk_workspace_bytes(T_q, T_kv, H, Hkv, d, precision, **offs))
+    pfa.gqa_chunk_attn(q, kc, vc, head_dim=d, scale=w.softmax_scale, window=window, gate=gt,
+                       precision=precision, out=out, workspace=ws, **offs)
+    g.check(f"gqa_chunk_attn {name} {precision}", [("out", out)])
+    # qk_prep_chunk_attn: the caches are written (new rows) and read (prefix rows)
+    g = Guarded()
+    q, k, v = g.input("q", x.q[new]), g.input("k", x.k[new]), g.input("v", x.v[new])
+    wq, wk = g.input("wq", x.wq), g.input("wk", x.wk)
+    kc = g.alloc("k_cache", x.k.shape, torch.float32, torch.from_numpy(x.k))
+    vc = g.alloc("v_cache", x.v.shape, torch.float32, torch.from_numpy(x.v))
+    out = g.alloc("out", (T_q, H * d), torch.float32)
+    ws = g.workspace(pfa.chunk_workspace_bytes(T_q, T_kv, H, Hkv, d, precision, fused=True,
+                                               **offs))
+    pfa.qk_prep_chunk_attn(q, k, v, wq, wk, kc, vc, head_dim=d, rope_dim=n,
+                           rope_freq_base=w.rope_freq_base, rms_eps=w.rms_eps,
+                           scale=w.softmax_scale, window=window, precision=precision,
+                           out=out, workspace=ws, **offs)
+    g.check(f"qk_prep_chunk_attn {name} {precision}",
+            [("out", out), ("k_cache", kc), ("v_cache", vc)])
+    keep = np.ones(T_kv, dtype=bool)
+    keep[new] = False
+    assert torch.equal(kc.cpu()[torch.from_numpy(keep)], torch.from_numpy(x.k[keep]))
+
+
+@pytest.mark.parametrize("case", CHUNK, ids=[c[0] for c in CHUNK])
+def test_8bit_entry_points_write_only_their_outputs(case):
+    name, lens, bases, H, Hkv, d, n, window = case
+    w, x, q_offs, kv_offs, new = _chunk_inputs(case, seed=1800)
+    T_q, T_kv = int(q_offs[-1]), int(kv_offs[-1])
+    offs = dict(q_offsets=q_offs, kv_offsets=kv_offs)
+    # pfa_quantize_rows
+    g = Guarded()
+    xin = g.input("x", x.q)
+    codes = g.alloc("codes", x.q.shape, torch.int8, torch.zeros(x.q.shape, dtype=torch.int8))
+    scales = g.alloc("scales", (x.q.size // d,), torch.float32)
+    fq = g.alloc("x_fq", x.q.shape, torch.float32)
+    pfa.quantize_rows(xin, d, codes=codes, scales=scales, x_fq=fq)
+    g.check(f"pfa_quantize_rows {name}", [("scales", scales), ("x_fq", fq)])
+    # gqa_attn_q8 over generated stores
+    qc, qs = wl.q8_store(T_q, H, d, 1801)
+    kc, ks = wl.q8_store(T_kv, Hkv, d, 1802)
+    vc, vs = wl.q8_store(T_kv, Hkv, d, 1803)
+    g = Guarded()
+    args = [g.input(nm, a) for nm, a in (("q", qc), ("q_scale", qs), ("k_cache", kc),
+                                         ("k_scale", ks), ("v_cache", vc), ("v_scale", vs))]
+    out = g.alloc("out", (T_q, H * d), torch.float32)
+    ws = g.workspace(pfa.q8_workspace_bytes(T_q, T_kv, H, Hkv, d, **offs))
+    pfa.gqa_attn_q8(*args, head_dim=d, scale=d ** -0.5, window=window, out=out, workspace=ws,
+                    **offs)
+    g.check(f"gqa_attn_q8 {name}", [("out", out)])
+    # qk_prep_attn_q8: the store is written (new rows) and read
+    g = Guarded()
+    q, k, v = g.input("q", x.q[new]), g.input("k", x.k[new]), g.input("v", x.v[new])
+    wq, wk = g.input("wq", x.wq), g.input("wk", x.wk)
+    skc = g.alloc("k_codes", kc.shape, torch.int8, torch.from_numpy(kc))
+    sks = g.alloc("k_scales", ks.shape, torch.float32, torch.from_numpy(ks))
+    svc = g.alloc("v_codes", vc.shape, torch.int8, torch.from_numpy(vc))
+    svs = g.alloc("v_scales", vs.shape, torch.float32, torch.from_numpy(vs))
+    out = g.alloc("out", (T_q, H * d), torch.float32)
+    ws = g.workspace(pfa.q8_workspace_bytes(T_q, T_kv, H, Hkv, d, fused=True, **offs))
+    pfa.qk_prep_attn_q8(q, k, v, wq, wk, skc, sks, svc, svs, head_dim=d, rope_dim=n,
+                        rope_freq_base=w.rope_freq_base, rms_eps=w.rms_eps, scale=d ** -0.5,
+                        window=window, out=out, workspace=ws, **offs)
+    g.check(f"qk_prep_attn_q8 {name}", [("out", out), ("k_scales", sks), ("v_scales", svs)])

@@ -1,0 +1,201 @@
+"""Full-size GPU parity of the prefill entry points (through the C ABI) against the f64
+oracle, at the workloads' real sizes and in the launch configuration the benchmark times.
+
+The output the pages define is the whole ``[T, n_head * head_dim]`` attention result
+(memra-engine 0.130.0 src/forward.rs, ``Model::forward``, SDPA block), so the 8B-like
+workload (T = 4096), the packed mixed batch (8 sequences, T = 16064) and the T = 8192
+target shape are compared on EVERY output element, for every precision mode and both
+entry points (``gqa_prefill_attn`` on prepared Q/K, ``qk_prep_attn`` on raw rows).  The
+oracle result of each workload is computed once per session (a few seconds to half a
+minute each on the host's cores).
+
+The long workload (T = 16384, 164 outlier tokens with K x8) is compared on 1500 rows
+that touch every key tile and every query block: both sides of every 32-row edge (the
+64-row bf16 tile edges among them), the last row, and one random row inside each
+32-row block.
+
+Gates (stated as such, not derived from the pages, which fix no tolerance): f32 max-abs
+2e-5 and relative L2 1e-5 over the compared elements; bf16 modes max-abs 2e-2.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_prefill_attention_amd as pfa
+from transformer_prefill_attention_amd import workloads as wl
+from tests.helpers import assert_bf16_parity, assert_f32_parity, eps32, errors
+
+pytestmark = pytest.mark.gpu
+
+THREADS = len(os.sched_getaffinity(0))
+FULL = ["tiny", "qwen3_0p6b", "qwen3_8b", "mixed", "prefill_8192"]
+MODES = [("f32", "unfused"), ("f32", "fused"), ("bf16", "unfused"), ("bf16", "fused"),
+         ("bf16x3", "unfused"), ("bf16x3", "fused")]
+LONG_ROWS_SEED = 5
+
+_inputs = {}
+_refs = {}
+
+
+def _attn_inputs(name):
+    """The workload's inputs as the attention entry points get them: the generator's Q, K,
+    V with the outlier tokens' K rows x8 (only the long workload has any; the fused entry
+    gets the same raw K and its norm erases the factor)."""
+    if name not in _inputs:
+        w = wl.CONFIGS[name]
+        x = wl.make_inputs(w)
+        _inputs.clear()  # one workload's arrays at a time
+        _inputs[name] = wl.Inputs(x.q, wl.with_outlier_keys(x.k, x.outliers), x.v, x.wq, x.wk,
+                                  x.outliers)
+    return _inputs[name]
+
+
+def _rows(name):
+    return None if name != "long" else wl.tile_edge_rows(wl.CONFIGS[name], LONG_ROWS_SEED)
+
+
+def _ref(name, path):
+    """Oracle output (f64): attention of the prepared Q/K for the unfused entry, the whole
+    chain from raw rows for the fused one (both unrounded)."""
+    key = (name, path)
+    if key not in _refs:
+        w, x, rows = wl.CONFIGS[name], _attn_inputs(name), _rows(name)
+        if len(_refs) >= 2:
+            _refs.pop(next(iter(_refs)))
+        print(f"oracle {path} {name}: T={w.T} rows={'all' if rows is None else len(rows)} "
+              f"threads={THREADS}", flush=True)
+        if path == "unfused":
+            # the unfused entry gets Q/K prepared by qknorm_rope; the oracle's attention
+            # input is the same f32 arrays, so both compare the attention step alone
+            qn, kn = _prepared(name)
+            _refs[key] = oracle.gqa_attn(qn, kn, x.v, n_head=w.n_head, n_head_kv=w.n_head_kv,
+                                         head_dim=w.head_dim, scale=w.softmax_scale,
+                                         seq_offsets=w.seq_offsets, rows=rows,
+                                         n_threads=THREADS)
+        else:
+            _refs[key] = oracle.qk_prep_attn(
+                x.q, x.k, x.v, x.wq, x.wk, n_head=w.n_head, n_head_kv=w.n_head_kv,
+                head_dim=w.head_dim, rope_dim=w.rope_dim,
+                rope_freq_base=float(np.float32(w.rope_freq_base)), rms_eps=eps32(w),
+                scale=w.softmax_scale, seq_offsets=w.seq_offsets, rows=rows, n_threads=THREADS)
+    return _refs[key]
+
+
+_prep = {}
+
+
+def _prepared(name):
+    """Q and K as the unfused attention call receives them: the generator's rows
+    normalised and rotated by the oracle, rounded once to f32, with the long workload's
+    outlier tokens' K rows x8 after the norm (QK-norm would erase a x8 before it)."""
+    if name not in _prep:
+        w, x = wl.CONFIGS[name], _attn_inputs(name)
+        raw = wl.make_inputs(w)
+        qn, kn = oracle.qknorm_rope(raw.q, raw.k, raw.wq, raw.wk, n_head=w.n_head,
+                                    n_head_kv=w.n_head_kv, head_dim=w.head_dim,
+                                    rope_dim=w.rope_dim,
+                                    rope_freq_base=float(np.float32(w.rope_freq_base)),
+                                    rms_eps=eps32(w), seq_offsets=w.seq_offsets,
+                                    n_threads=THREADS)
+        _prep.clear()
+        _prep[name] = (qn.astype(np.float32),
+                       wl.with_outlier_keys(kn.astype(np.float32), x.outliers))
+    return _prep[name]
+
+
+def _gpu(name, precision, path):
+    w, x = wl.CONFIGS[name], _attn_inputs(name)
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    print(f"{'qk_prep_attn' if path == 'fused' else 'gqa_prefill_attn'} {name}: T={w.T} "
+          f"H={w.n_head} Hkv={w.n_head_kv} d={w.head_dim} n={w.rope_dim} seqs={w.n_seqs} "
+          f"{precision}", flush=True)
+    if path == "fused":
+        out = pfa.qk_prep_attn(t(x.q), t(x.k), t(x.v), t(x.wq), t(x.wk), head_dim=w.head_dim,
+                               rope_dim=w.rope_dim, rope_freq_base=w.rope_freq_base,
+                               rms_eps=w.rms_eps, scale=w.softmax_scale, precision=precision,
+                               seq_offsets=w.seq_offsets)
+    else:
+        qn, kn = _prepared(name)
+        out = pfa.gqa_prefill_attn(t(qn), t(kn), t(x.v), head_dim=w.head_dim,
+                                   scale=w.softmax_scale, precision=precision,
+                                   seq_offsets=w.seq_offsets)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del out
+    rows = _rows(name)
+    return got if rows is None else got[rows]
+
+
+@pytest.mark.parametrize("precision,path", MODES, ids=[f"{p}-{q}" for p, q in MODES])
+@pytest.mark.parametrize("name", FULL)
+def test_every_output_element(name, precision, path, gpu_device):
+    got = _gpu(name, precision, path)
+    ref = _ref(name, path)
+    what = f"{path} {precision} {name}, all {got.shape[0]} rows"
+    if precision == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)
+
+
+LONG_MODES = [("f32", "unfused"), ("f32", "fused"), ("bf16", "fused"), ("bf16x3", "unfused"),
+              ("bf16x3", "fused")]
+
+
+@pytest.mark.parametrize("precision,path", LONG_MODES, ids=[f"{p}-{q}" for p, q in LONG_MODES])
+def test_long_every_tile(precision, path, gpu_device):
+    """T = 16384 with x8 outlier keys, 1500 rows touching every tile and query block."""
+    got = _gpu("long", precision, path)
+    ref = _ref("long", path)
+    what = f"{path} {precision} long, {got.shape[0]} tile-edge rows"
+    if precision == "f32":
+        assert_f32_parity(got, ref, what)
+    else:
+        assert_bf16_parity(got, ref, what)
+
+
+def _bf16_rounded(name):
+    """The prepared Q/K/V as plain bf16 multiplies them: Q * (scale log2 e) rounded to
+    bf16 (then divided back), K and V rounded to bf16."""
+    w, x = wl.CONFIGS[name], _attn_inputs(name)
+    qn, kn = _prepared(name)
+    c = np.float32(np.float32(w.softmax_scale) * np.float32(1.4426950408889634))
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(
+        torch.float64).numpy()
+    return bf((qn * c).astype(np.float32)) / np.float64(c), bf(kn), bf(x.v)
+
+
+def test_long_plain_bf16_on_its_rounded_inputs(gpu_device):
+    """Plain bf16 on the long workload, against the oracle on the bf16-rounded inputs R
+    (what the mode computes: its only roundings are those of its inputs and weights), at
+    the bf16 gate.  Against the unrounded oracle U it can only be as far off as the input
+    rounding moves the exact result, |gpu - U| <= |gpu - R| + |R - U|, and the x8 keys
+    make that rounding effect larger than the gate (next test); the bound asserted is that
+    triangle inequality, with |R - U| measured by the oracle itself."""
+    w = wl.CONFIGS["long"]
+    got = _gpu("long", "bf16", "unfused")
+    q, k, v = _bf16_rounded("long")
+    ref_r = oracle.gqa_attn(q, k, v, n_head=w.n_head, n_head_kv=w.n_head_kv,
+                            head_dim=w.head_dim, scale=w.softmax_scale,
+                            seq_offsets=w.seq_offsets, rows=_rows("long"), n_threads=THREADS)
+    assert_bf16_parity(got, ref_r, "unfused bf16 long vs oracle on rounded inputs")
+    ref_u = _ref("long", "unfused")
+    effect = float(np.max(np.abs(ref_r - ref_u)))
+    max_abs, rel = errors(got, ref_u)
+    print(f"unfused bf16 long vs unrounded oracle: max|err| {max_abs:.3e} rel L2 {rel:.3e}; "
+          f"input rounding alone moves the exact result by up to {effect:.3e}", flush=True)
+    assert max_abs <= effect + 2e-2
+
+
+@pytest.mark.xfail(strict=True, reason="plain bf16 inputs cannot resolve the scores of x8 "
+                   "outlier keys to the 2e-2 gate: rounding K and Q to bf16 moves a score by "
+                   "~2^-9 of |q||k|, and x8 keys make those scores ~8x larger (measured 0.116 "
+                   "over these 1500 rows, 5.9e-2 over 60).  PFA_PREC_BF16X3 and the fused bf16 "
+                   "entry meet the gate here.")
+def test_long_plain_bf16_gate(gpu_device):
+    got = _gpu("long", "bf16", "unfused")
+    assert_bf16_parity(got, _ref("long", "unfused"), "unfused bf16 long vs unrounded oracle")

@@ -142,6 +142,25 @@ def sample_rows(w: Workload, n_random: int = 64, seed: int = 0) -> np.ndarray:
     return np.array(sorted(rows), dtype=np.int64)
 
 
+def tile_edge_rows(w: Workload, seed: int = 0) -> np.ndarray:
+    """Query rows that touch every tile of every sequence: the rows on both sides of each
+    32-row edge (32j - 1 and 32j, counted from the sequence's start; the 64-row edges
+    among them), its last row, and one uniformly drawn row inside each 32-row block.
+    Sorted, unique."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    offs = w.seq_offsets
+    for s in range(w.n_seqs):
+        a, b = int(offs[s]), int(offs[s + 1])
+        if b <= a:
+            continue
+        for j in range(a, b, 32):
+            rows.update(r for r in (j - 1, j) if a <= r < b)
+            rows.add(int(j + rng.integers(0, min(32, b - j))))
+        rows.add(b - 1)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
 def q8_store(rows: int, heads: int, head_dim: int, seed: int, spread: float = 45.0,
              scale: float = 0.022):
     """Random contents of an 8-bit K/V (or Q) store, shaped like quantised normal rows:
