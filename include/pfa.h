@@ -145,8 +145,11 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
  *        aligned, at least pfa_workspace_bytes(seq_offsets, n_seqs, T, n_head,
  *        n_head_kv, head_dim, precision, 0) bytes, not overlapping the tensors; its
  *        contents are overwritten (calls in flight at the same time need separate
- *        workspaces).  Required for the bf16 modes; optional for PFA_PREC_F32
- *        (may be NULL: short inputs then run without the key split).
+ *        workspaces).  Required for the bf16 modes; optional for PFA_PREC_F32: with
+ *        NULL (or too small a workspace) short inputs run without the key split, which
+ *        is correct but slower -- about twice as slow at T = 512 with 16 query heads
+ *        over 8 K/V heads (the items then cannot fill the GPU).  pfa_attn_plan reports
+ *        which plan a given workspace size gets.
  */
 int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
                      const int32_t* seq_offsets, int n_seqs,
@@ -275,10 +278,12 @@ size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_off
  * 8 bits right after RoPE, before attention and before the cache write),
  * `quantize_rows` and its int8 K/V store (integer rows plus one scale per row,
  * the form decode reads; the store's reader takes the scales out of the dot
- * products).  The rule, in IEEE single precision: a row's scale is its largest
- * magnitude / 127; a value's code is the nearest integer to value / scale, ties
- * to even, within -127..127; a row of zeros has scale 0 and codes 0.  A value
- * of the store is code * scale.
+ * products).  The page prints neither quantiser's body.  This library's reading of
+ * the rule (symmetric, 8 bits, one scale per row), in IEEE single precision: a row's
+ * scale is its largest magnitude / 127; a value's code is the nearest integer to
+ * value / scale, ties to even, within -127..127; a row of zeros has scale 0 and codes
+ * 0.  The divisor 127 and the tie direction are choices of that reading, not
+ * statements of the page.  A value of the store is code * scale.
  *
  * An 8-bit store of `heads` heads over `rows` rows is a pair of device arrays:
  * codes int8 [rows, heads*head_dim] (16-byte aligned) and scales f32

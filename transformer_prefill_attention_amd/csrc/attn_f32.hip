@@ -146,9 +146,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     // key tiles of the item (with a sliding window it starts at its first row's first
     // visible key); with a key split this workgroup takes tiles [t_begin, t_end)
     const KeyRange kr = item_key_range(sched, geom, wi, kBN);
+    if (wi.kc >= kr.n_chunks) return;  // (uniform: the whole workgroup leaves)
     const int nt_seq = kr.nt_seq, t_begin = kr.t_begin, t_end = kr.t_end;
     const int win = geom.causal ? geom.window : 0;
-    if (t_begin >= t_end) return;  // (uniform: the whole workgroup leaves)
     const bool split = kr.n_chunks > 1;
 
     // ---- wavefront role

@@ -70,10 +70,12 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
 }
 
 // 8-bit quantisation of a (token, head) row (needle-core v3/model.rs, `quant_rows` /
-// `quantize_rows`): the row's scale is its largest magnitude over 127, and a value's
-// code is the nearest integer to value / scale (ties to even) within -127..127; a row
-// of zeros has scale 0 and codes 0.  IEEE single-precision division, so the codes are
-// those of any correctly rounded implementation.
+// `quantize_rows`, whose bodies the page does not print).  This library's reading of
+// the rule: the row's scale is its largest magnitude over 127, and a value's code is the
+// nearest integer to value / scale (ties to even) within -127..127; a row of zeros has
+// scale 0 and codes 0.  The divisor 127 and the tie direction are that reading's
+// choices, not the page's.  IEEE single-precision division, so the codes are those of
+// any correctly rounded implementation.
 __device__ __forceinline__ float quant8_scale(float amax) { return amax / 127.0f; }
 __device__ __forceinline__ int quant8(float x, float scale) {
     const float c = scale > 0.0f ? __builtin_rintf(x / scale) : 0.0f;
