@@ -158,6 +158,27 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_prefill_attn_noalloc -- gqa_prefill_attn for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The arguments are gqa_prefill_attn's without the workspace; the call uses a
+ * device array of pfa_noalloc_scratch_bytes() (64 MiB) that the library itself holds on
+ * each GPU it runs on, until the process ends, and calls no allocator.  The results are
+ * gqa_prefill_attn's, bit for bit (the same kernels and plan).
+ *  A call whose workspace would exceed the array (pfa_workspace_bytes(..., 0) larger than
+ *  pfa_noalloc_scratch_bytes(): e.g. the bf16 modes beyond 16384 key rows at 8 K/V heads of
+ *  128) fails with PFA_ERR_UNSUPPORTED before anything is enqueued.
+ *  Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ *  (on different streams, or from different threads) race and must not be issued.
+ */
+int gqa_prefill_attn_noalloc(const float* q, const float* k, const float* v, float* out,
+                             const int32_t* seq_offsets, int n_seqs, int T, int n_head,
+                             int n_head_kv, int head_dim, float scale, int causal, int precision,
+                             void* stream);
+
+/* Size in bytes of the per-GPU device array gqa_prefill_attn_noalloc uses. */
+size_t pfa_noalloc_scratch_bytes(void);
+
+/*
  * qk_prep_attn -- the whole attention core in one call: qknorm_rope applied to
  * the raw Q and K, then gqa_prefill_attn.  The normalised, rotated Q never goes
  * to memory (each attention workgroup builds its Q rows on chip); K is prepared

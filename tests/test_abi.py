@@ -497,3 +497,20 @@ def test_tensor_pointers_must_be_16_byte_aligned(L):
                           p(6 << 20), None, 0, 16, 4, 2, 64, 64, 1e6, 1e-6, 0.125, 1, 0,
                           p(7 << 20), p(8 << 20), 16 << 20, None) == INVALID
     assert "16-byte aligned" in _msg(L)
+
+
+def test_noalloc_rejects_calls_beyond_its_device_array(L):
+    """gqa_prefill_attn_noalloc refuses, before anything is enqueued, a call whose workspace
+    would not fit in the library's device array (bf16 tiles of 20000 key rows at 8 K/V
+    heads of 128 need 82 MB)."""
+    p = ctypes.c_void_p
+    T = 20000
+    assert L.pfa_noalloc_scratch_bytes() == 64 << 20
+    assert pfa.workspace_bytes(T, 32, 8, 128, "bf16") > L.pfa_noalloc_scratch_bytes()
+    assert L.gqa_prefill_attn_noalloc(p(1 << 30), p(2 << 30), p(3 << 30), p(4 << 30), None, 0,
+                                      T, 32, 8, 128, 0.088, 1, 1, None) == UNSUPPORTED
+    assert "device array" in _msg(L)
+    # argument errors come first, as for gqa_prefill_attn
+    assert L.gqa_prefill_attn_noalloc(p(1 << 30), p(2 << 30), p(3 << 30), p(4 << 30), None, 0,
+                                      16, 4, 2, 96, 0.125, 1, 0, None) == UNSUPPORTED
+    assert "head_dim" in _msg(L)

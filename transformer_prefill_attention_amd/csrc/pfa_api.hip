@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "pfa_device.h"
 #include "pfa_internal.h"
@@ -567,6 +568,82 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
     return attn_common(Mode::kPlain, q, k, v, out, nullptr, nullptr, nullptr, 0, st, n_head,
                        n_head_kv, head_dim, scale, causal, 0, precision, nullptr, workspace,
                        workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// gqa_prefill_attn_noalloc: gqa_prefill_attn for callers that cannot allocate device
+// memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+// allocation).  Its workspace is this library-owned device array (each GPU the library
+// runs on holds one copy until the process ends); it is resolved to a device address
+// once per device with hipGetSymbolAddress, and only that address reaches the kernels.
+// Nothing in it needs clearing: the staging kernels write every tile they later read and
+// the key split writes every partial result before the combine step reads it.  Calls
+// that overlap on one GPU share the array and race.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device (nullptr and a message on failure).
+void* scratch_address() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        fail(PFA_ERR_HIP, "gqa_prefill_attn_noalloc: no usable current device (%s)",
+             hipGetErrorString(e));
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(PFA_ERR_HIP, "gqa_prefill_attn_noalloc: hipGetSymbolAddress: HIP error %d (%s)",
+                 (int)e, hipGetErrorString(e));
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pfa_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int gqa_prefill_attn_noalloc(const float* q, const float* k, const float* v, float* out,
+                             const int32_t* seq_offsets, int n_seqs, int T, int n_head,
+                             int n_head_kv, int head_dim, float scale, int causal, int precision,
+                             void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T, n_head, n_head_kv, head_dim);
+    if (rc || (rc = check_attn(scale, precision))) return rc;
+    if (T == 0) return PFA_OK;
+    pfa::SeqTable st;
+    if ((rc = build_seqs(seq_offsets, n_seqs, T, st))) return rc;
+    // the workspace gqa_prefill_attn would use with room for everything (the same plan)
+    CallPlan cp;
+    if ((rc = plan_call(Mode::kPlain, st, n_head, n_head_kv, head_dim, scale, causal, 0,
+                        precision, false, SIZE_MAX, cp)))
+        return rc;
+    if (cp.p.items == 0) return PFA_OK;
+    if (cp.need > kScratchBytes)
+        return fail(PFA_ERR_UNSUPPORTED,
+                    "gqa_prefill_attn_noalloc: this call needs %zu bytes of workspace, more than "
+                    "the library's %zu-byte device array (use gqa_prefill_attn with a workspace)",
+                    cp.need, kScratchBytes);
+    void* ws = cp.need ? scratch_address() : nullptr;
+    if (cp.need && !ws) return PFA_ERR_HIP;
+    return attn_common(Mode::kPlain, q, k, v, out, nullptr, nullptr, nullptr, 0, st, n_head,
+                       n_head_kv, head_dim, scale, causal, 0, precision, nullptr, ws,
+                       cp.need ? kScratchBytes : 0, stream);
 }
 
 int qk_prep_attn(const float* q, const float* k, const float* v, float* out,

@@ -30,7 +30,8 @@ _PRECISIONS = {"f32": PRECISION_F32, "fp32": PRECISION_F32, "float32": PRECISION
 EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_workspace_bytes",
            "gqa_chunk_attn", "qk_prep_chunk_attn", "pfa_chunk_workspace_bytes",
            "pfa_quantize_rows", "gqa_attn_q8", "qk_prep_attn_q8", "pfa_q8_workspace_bytes",
-           "pfa_attn_plan", "pfa_attn_units", "pfa_last_error", "pfa_version")
+           "pfa_attn_plan", "pfa_attn_units", "gqa_prefill_attn_noalloc",
+           "pfa_noalloc_scratch_bytes", "pfa_last_error", "pfa_version")
 
 # pfa_entry values of the plan report
 ENTRY_PREFILL, ENTRY_PREP, ENTRY_CHUNK, ENTRY_CHUNK_PREP, ENTRY_Q8, ENTRY_Q8_PREP = range(6)
@@ -75,6 +76,11 @@ def lib() -> ctypes.CDLL:
     L.gqa_prefill_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
                                    vp, sz, vp]
     L.gqa_prefill_attn.restype = i32
+    L.gqa_prefill_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                           i32, i32, vp]
+    L.gqa_prefill_attn_noalloc.restype = i32
+    L.pfa_noalloc_scratch_bytes.argtypes = []
+    L.pfa_noalloc_scratch_bytes.restype = sz
     L.qk_prep_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
                                f32, i32, i32, fp_, vp, sz, vp]
     L.qk_prep_attn.restype = i32
@@ -263,6 +269,34 @@ def gqa_prefill_attn(q, k, v, *, head_dim: int, scale: float,
                                   head_dim, float(scale), 1 if causal else 0, prec, wp, wn,
                                   _stream(q)))
     return out
+
+
+def gqa_prefill_attn_noalloc(q, k, v, *, head_dim: int, scale: float, causal: bool = True,
+                             precision="f32", seq_offsets: Optional[Sequence[int]] = None,
+                             out=None):
+    """``gqa_prefill_attn`` with its workspace in the library's own device array
+    (``gqa_prefill_attn_noalloc`` in ``include/pfa.h``): the C call allocates nothing.
+    Pass ``out`` too when nothing may be allocated; calls overlapping on one GPU race."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev_f32(t, n)
+    T, H = _heads(q, head_dim, "q")
+    Tk, Hkv = _heads(k, head_dim, "k")
+    if Tk != T or v.shape != k.shape:
+        raise ValueError("q, k, v must have the same token count and k, v the same shape")
+    out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    offs, n_seqs, op = _offsets(seq_offsets, T)
+    _check(lib().gqa_prefill_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), op, n_seqs, T,
+                                          H, Hkv, head_dim, float(scale), 1 if causal else 0,
+                                          _prec(precision), _stream(q)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the device array ``gqa_prefill_attn_noalloc`` uses on each GPU."""
+    return int(lib().pfa_noalloc_scratch_bytes())
 
 
 def qk_prep_attn(q, k, v, q_norm_w, k_norm_w, *, head_dim: int, rope_dim: int,
