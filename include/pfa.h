@@ -79,7 +79,8 @@ typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_pr
  *  - any precision, short inputs only, at the next multiple of 256 bytes: when
  *    the (query block, head) work items cannot fill the GPU (the current device's
  *    compute units, 256 on MI355X and when no device is visible; query with the
- *    same device current as the call), each item's key
+ *    same device current as the call) and, for the bf16 modes, some sequence spans
+ *    at least 2048 key rows, each item's key
  *    range is split over several workgroups whose partial results (32 x head_dim
  *    f32 plus two f32 per row, per wavefront) are merged by one more kernel;
  *    0 bytes otherwise.

@@ -32,6 +32,8 @@ CASES = {
     "packed": ((50, 1, 130, 0), (20, 77, 0, 5), 8, 4, 128, 64),
     "d64": ((90,), (45,), 4, 2, 64, 64),
     "long_prefix": ((260,), (1500,), 16, 8, 128, 128),
+    # a cache long enough that the bf16 kernel splits its keys too (>= 2048 keys)
+    "split_prefix": ((64, 1), (4000, 2500), 8, 2, 128, 128),
 }
 
 

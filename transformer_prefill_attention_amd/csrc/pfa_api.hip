@@ -234,16 +234,22 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // least 128 keys (at T = 512 shorter chunks were 4-12% slower; a chunk of 1024
 // new rows over 7168 cached ones, whose items fill only half the slots, gets two:
 // 7-24% faster), and an item is cut into at most kMaxKeyChunks chunks (one new row
-// over 8191 cached ones ran 8-20% slower in 64 chunks than in 32).
+// over 8191 cached ones ran 8-20% slower in 64 chunks than in 32).  The bf16 kernel
+// splits only when a sequence spans at least kBf16SplitTiles tiles (2048 keys): a
+// bf16 tile step is short, so below that the merge launch costs more than the
+// shorter units save (unsplit at T = 512 with 16/8 heads 32.2 against 34.9 us, 32/8
+// heads 32.8 against 42.3 us, T = 1024 47.1 against 49.7 us; equal at T = 2048).
 constexpr int kMaxKeyChunks = 32;
+constexpr int kBf16SplitTiles = 32;
 void choose_split(Plan& p, int head_dim) {
     const long long wgs = (long long)p.items * p.geom.chunks * p.geom.Hkv;
     const int target = (p.waves == 8 ? 1 : 2) * device_cus();
     const int n_max = (p.sched.max_len + p.tile_keys - 1) / p.tile_keys;
     const long long k_min = std::max<long long>((128 + p.tile_keys - 1) / p.tile_keys,
                                                 (n_max + kMaxKeyChunks - 1) / kMaxKeyChunks);
+    const int n_split = p.waves == 8 ? kBf16SplitTiles : 2;  // fewest tiles worth splitting
     int kchunk = 0;
-    if (wgs < target && n_max > 1) {
+    if (wgs < target && n_max >= n_split) {
         const long long k = (wgs * n_max + target - 1) / target;
         kchunk = (int)std::max(k_min, k);
         if (kchunk >= n_max) kchunk = 0;
