@@ -51,48 +51,48 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(Partials part,
         (((size_t)w.item * sched.max_chunks * geom.chunks + w.chunk) * geom.Hkv + w.kv) * waves +
         wave;
     const size_t kstride = (size_t)geom.chunks * geom.Hkv * waves;  // slots between key chunks
-    // Chunks are taken kBatch at a time with all their loads issued together (the
-    // loads are independent; a plain loop would wait for each in turn).
+    // One pass over the chunks, kBatch at a time: each batch's (m, l) and partial rows are
+    // loaded together (up to kBatch chunks cost one memory round trip), and the running
+    // merge is rescaled when a batch raises the running max -- the online softmax's own
+    // rescaling, applied to whole chunks.
     constexpr int kBatch = 8;
-    float m_max = -INFINITY;
-    for (int k0 = 0; k0 < n_chunks; k0 += kBatch) {
-        float2 ml[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            // chunks past the count re-read the last one (always a written slot)
-            const int k = min(k0 + j, n_chunks - 1);
-            ml[j] = part.ml[(slot0 + k * kstride) * 32 + r];
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j)
-            if (ml[j].y > 0.0f) m_max = fmaxf(m_max, ml[j].x);
-    }
-    float den = 0.0f;
+    float m_run = -INFINITY, den = 0.0f;
     floatx4 acc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < n_chunks; k0 += kBatch) {
-        float wk[kBatch];
+        float2 ml[kBatch];
         floatx4 o[kBatch][D / 32];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const bool in = k0 + j < n_chunks;
             // chunks past the count re-read the last one (always a written slot), weight 0
             const size_t slot = slot0 + (size_t)min(k0 + j, n_chunks - 1) * kstride;
-            const float2 ml = part.ml[slot * 32 + r];
-            // a chunk that saw no key of the row has l = 0 and weight 0
-            wk[j] = in && ml.y > 0.0f ? ml.y * exp2f(ml.x - m_max) : 0.0f;
+            ml[j] = part.ml[slot * 32 + r];
             const float* src = part.o + (slot * 32 + r) * D + c0;
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) o[j][i] = *reinterpret_cast<const floatx4*>(src + 4 * i);
         }
+        // a chunk that saw no key of the row has l = 0 and weight 0
+        float mb = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (k0 + j < n_chunks && ml[j].y > 0.0f) mb = fmaxf(mb, ml[j].x);
+        if (mb > m_run) {
+            const float a = m_run == -INFINITY ? 0.0f : exp2f(m_run - mb);
+            den *= a;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) acc[i] *= a;
+            m_run = mb;
+        }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            den += wk[j];
+            const float wk = k0 + j < n_chunks && ml[j].y > 0.0f ? ml[j].y * exp2f(ml[j].x - m_run)
+                                                                  : 0.0f;
+            den += wk;
 #pragma unroll
             for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][e] += wk[j] * o[j][i][e];
+                for (int e = 0; e < 4; ++e) acc[i][e] += wk * o[j][i][e];
         }
     }
     const float inv = 1.0f / den;
