@@ -355,5 +355,9 @@ PAIRED = [
 def test_paired_items_full_compare(gpu_device, w):
     x = wl.make_inputs(w)
     t = _dev(x, gpu_device)
-    assert_f32_parity(_attn_gpu(w, t), _attn_ref(w, x), f"attn {w.name}")
+    ref = _attn_ref(w, x)
+    assert_f32_parity(_attn_gpu(w, t), ref, f"attn {w.name}")
     assert_f32_parity(_fused_gpu(w, t), _fused_ref(w, x), f"fused {w.name}")
+    # the same shapes through the bf16 kernel
+    for prec in ("bf16", "bf16x3"):
+        assert_bf16_parity(_attn_gpu(w, t, precision=prec), ref, f"attn {prec} {w.name}")
