@@ -79,11 +79,14 @@ typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_pr
  *  - any precision, short inputs only, at the next multiple of 256 bytes: when
  *    the (query block, head) work items cannot fill the GPU (the current device's
  *    compute units, 256 on MI355X and when no device is visible; query with the
- *    same device current as the call) and, for the bf16 modes, some sequence spans
- *    at least 2048 key rows, each item's key
- *    range is split over several workgroups whose partial results (32 x head_dim
- *    f32 plus two f32 per row, per wavefront) are merged by one more kernel;
- *    0 bytes otherwise.
+ *    same device current as the call) and, for PFA_PREC_BF16 (and the 8-bit
+ *    calls), some sequence spans at least 2048 key rows, each item's key range is
+ *    split over several workgroups whose partial results (32 x head_dim f32 plus
+ *    two f32 per row, per wavefront) are merged: when no item has more than 4 key
+ *    chunks, by the last of its workgroups to finish (then, at the next multiple
+ *    of 256 bytes, one 8-byte arrival counter per item, head group and K/V head;
+ *    tagged per call, so they need no clearing, and left 0), else by one more
+ *    kernel; 0 bytes otherwise.  Calls that share a workspace must not overlap.
  * For PFA_PREC_F32 the partial results are optional: without room for them the
  * call runs without the key split.  Returns 0 when nothing is needed or the
  * arguments are ones the attention calls would reject (pfa_last_error() then
@@ -422,7 +425,8 @@ typedef struct {
     int key_chunk_tiles;     /* key split: tiles per key chunk (0: not split) */
     int max_key_chunks;      /* key chunks of the longest item (1: not split) */
     int paired;              /* f32: attention workgroup j takes items j and items-1-j */
-    int reserved;
+    int merge_in_place;      /* key split merged by each item's last workgroup (no extra
+                                kernel); 0: by attn_combine_kernel, or not split */
     int64_t workgroups;      /* grid of the attention kernel */
     size_t workspace_bytes;  /* device workspace the call uses */
     char kernels[320];       /* kernels enqueued, in launch order, joined by " + " */

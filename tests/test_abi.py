@@ -181,9 +181,11 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused, kv_lens=None, chunk=False)
     the longest, when Q is prepared in the kernel) or the f32 fused prefill's rotated K,
     then partial results when the (query block, head) items cannot fill the GPU's
     workgroup slots (a target of 512 f32 or 256 bf16 workgroups) and are split by key,
-    at least 128 keys a chunk and at most 32 chunks an item (bf16: only when a sequence
-    spans at least 2048 keys).  ``lens``: query rows per
-    sequence; ``kv_lens``: key rows (default: the same)."""
+    at least 128 keys a chunk and at most 32 chunks an item (PFA_PREC_BF16: only when a
+    sequence spans at least 2048 keys); with at most 4 chunks an item, one 8-byte arrival
+    counter per (item, head group, K/V head) after the partial results, at the next
+    multiple of 256 bytes.  ``lens``: query rows per sequence; ``kv_lens``: key rows
+    (default: the same)."""
     kv_lens = lens if kv_lens is None else kv_lens
     bf16 = prec != 0
     waves, tile = (8, 64) if bf16 else (4, 32)
@@ -196,8 +198,8 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused, kv_lens=None, chunk=False)
     n_max = _ceil(max(kv_lens), tile)
     wgs, target = items * chunks * Hkv, (1 if bf16 else 2) * 256
     kchunk = 0
-    # the bf16 kernel splits only sequences of at least 32 tiles (2048 keys)
-    if wgs < target and n_max >= (32 if bf16 else 2):
+    # plain bf16 splits only sequences of at least 32 tiles (2048 keys)
+    if wgs < target and n_max >= (32 if prec == 1 else 2):
         # at least 128 keys a chunk, at most 32 chunks an item
         kchunk = max(_ceil(128, tile), _ceil(n_max, 32), _ceil(wgs * n_max, target))
         if kchunk >= n_max:
@@ -206,6 +208,8 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused, kv_lens=None, chunk=False)
     if kchunk and items:
         units = items * _ceil(n_max, kchunk) * chunks * Hkv
         parts = units * waves * 32 * (D * 4 + 8)
+        if _ceil(n_max, kchunk) <= 4:
+            parts = _ceil(parts, 256) * 256 + items * chunks * Hkv * 8
     base = 0
     if bf16:
         base = Hkv * sum(_ceil(n, 64) for n in kv_lens) * 64 * D * 2 * (3 if prec == 2 else 2)

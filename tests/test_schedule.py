@@ -144,7 +144,7 @@ def test_paired_items_cover_every_item_once():
     for T in (2048, 4096):
         plan = _check_schedule(pfa.ENTRY_PREFILL, [T], [T], 32, 8, 128, "f32")
         assert plan["paired"] == 1
-        assert "attn_f32_kernel<128,false,true>" in plan["kernels"]
+        assert "attn_f32_kernel<128,false,true,false>" in plan["kernels"]
     # odd item count: the middle workgroup takes one item
     plan = _check_schedule(pfa.ENTRY_PREFILL, [990], [990], 128, 32, 128, "f32")
     assert plan["paired"] == 1 and plan["items"] % 2 == 1
@@ -152,17 +152,30 @@ def test_paired_items_cover_every_item_once():
 
 def test_key_split_at_short_inputs():
     # T = 512 with 0.6B-like heads: the items cannot fill the GPU, so the key range is
-    # split (f32 only when the workspace has room for the partial results)
-    plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, "f32")
-    assert plan["max_key_chunks"] > 1 and plan["workspace_bytes"] > 0
-    assert plan["kernels"].endswith("attn_combine_kernel<128>")
+    # split (f32 only when the workspace has room for the partial results); with at most
+    # 4 chunks an item, each item's last workgroup merges them (no combine launch)
+    for prec, kernel in (("f32", "attn_f32_kernel<128,false,false,true>"),
+                         ("bf16x3", "attn_bf16_kernel<128,true,false,false,true>")):
+        plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, prec)
+        assert 1 < plan["max_key_chunks"] <= 4 and plan["workspace_bytes"] > 0
+        assert plan["merge_in_place"] == 1
+        assert plan["kernels"].endswith(kernel) and "combine" not in plan["kernels"]
+    # plain bf16 splits only sequences of at least 2048 keys
+    plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, "bf16")
+    assert plan["max_key_chunks"] == 1 and plan["merge_in_place"] == 0
+    plan = _check_schedule(pfa.ENTRY_PREFILL, [2048], [2048], 16, 8, 128, "bf16")
+    assert 1 < plan["max_key_chunks"] <= 4 and plan["merge_in_place"] == 1
     plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, "f32",
                            workspace_bytes=0)
     assert plan["max_key_chunks"] == 1 and plan["workspace_bytes"] == 0
-    assert "combine" not in plan["kernels"]
-    # one new row over a long cache: the key range of the single item is cut up
-    plan = _check_schedule(pfa.ENTRY_CHUNK, [1], [8192], 32, 8, 128, "bf16")
-    assert plan["max_key_chunks"] == 32
+    assert plan["merge_in_place"] == 0 and "combine" not in plan["kernels"]
+    # new rows over a long cache: the key range of each item is cut into more chunks than
+    # the in-place merge takes, merged by the combine launch
+    for q_len, chunks in ((1, 32), (256, 8)):
+        for prec in ("f32", "bf16"):
+            plan = _check_schedule(pfa.ENTRY_CHUNK, [q_len], [8192], 32, 8, 128, prec)
+            assert plan["max_key_chunks"] == chunks and plan["merge_in_place"] == 0
+            assert plan["kernels"].endswith("attn_combine_kernel<128>")
 
 
 def test_plan_workspace_matches_the_size_queries():
@@ -190,19 +203,19 @@ def test_plan_names_the_kernels_in_launch_order():
     p = pfa.attn_plan(pfa.ENTRY_PREP, T_q=8192, n_head=32, n_head_kv=8, head_dim=128,
                       rope_dim=128)
     assert p["kernels"] == ("qknorm_rope_kernel<128,0,false> + "
-                            "attn_f32_kernel<128,true,false>")
+                            "attn_f32_kernel<128,true,false,false>")
     p = pfa.attn_plan(pfa.ENTRY_PREP, T_q=8192, n_head=32, n_head_kv=8, head_dim=128,
                       rope_dim=128, precision="bf16")
     assert p["kernels"] == ("rope_table_kernel<128,false> + "
                             "stage_kv_bf16_kernel<128,false,true> + "
-                            "attn_bf16_kernel<128,false,true,false>")
+                            "attn_bf16_kernel<128,false,true,false,false>")
     p = pfa.attn_plan(pfa.ENTRY_PREFILL, T_q=8192, n_head=32, n_head_kv=8, head_dim=128,
                       precision="bf16x3")
     assert p["kernels"] == ("stage_kv_bf16_kernel<128,true,false> + "
-                            "attn_bf16_kernel<128,true,false,false>")
+                            "attn_bf16_kernel<128,true,false,false,false>")
     p = pfa.attn_plan(pfa.ENTRY_Q8, T_q=8192, T_kv=8192, n_head=32, n_head_kv=8, head_dim=64)
     assert p["kernels"] == ("stage_kv_q8_kernel<64,false> + "
-                            "attn_bf16_kernel<64,false,false,true>")
+                            "attn_bf16_kernel<64,false,false,true,false>")
 
 
 def test_plan_rejects_what_the_entry_points_reject():

@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256) void stage_kv_q8_kernel(Q8Store q8, unsigned c
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, bool PREP, bool Q8>
+template <int D, bool SPLIT, bool PREP, bool Q8, bool MERGE>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __restrict__ q,
                                                                 const __bf16* __restrict__ ws,
                                                                 float* __restrict__ out,
@@ -887,7 +887,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     const double l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = l_tot > 0.0 ? (float)(1.0 / l_tot) : 0.0f;
     const size_t slot = (size_t)blockIdx.x * kWaves + wave;
-    if (split && hl == 0) part.ml[slot * 32 + ln] = float2{m_run, (float)l_tot};
+    if (split && hl == 0) {
+        part.ml[slot * 32 + ln] = float2{m_run, (float)l_tot};
+    }
 #pragma unroll
     for (int round = 0; round < 2; ++round) {
         const bool mine = (wave >> 2) == round;
@@ -912,9 +914,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 const int r = f / F4, c4 = f % F4;
                 const int row = wq0 + r;
                 const floatx4 x = *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
-                if (split)
+                if (split) {
                     *reinterpret_cast<floatx4*>(part.o + (slot * 32 + r) * D + 4 * c4) = x;
-                else if (row < s1) {
+                } else if (row < s1) {
                     floatx4 y = x;
                     if (geom.gate)
                         y *= gate_factors(geom.gate, geom.gate_per_head, row, H, h, D,
@@ -924,6 +926,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
             }
         }
         if (round == 0) __syncthreads();
+    }
+    if constexpr (MERGE) {
+        // the item's last unit to arrive merges every key chunk's partial result
+        __shared__ int last_flag;
+        const size_t item_slot = ((size_t)wi.item * geom.chunks + wi.chunk) * Hkv + kv;
+        if (split && arrive_last(part, item_slot, kr.n_chunks, &last_flag)) {
+            const size_t kstride = (size_t)geom.chunks * Hkv * kWaves;
+            const size_t slot0 =
+                (((size_t)wi.item * sched.max_chunks * geom.chunks + wi.chunk) * Hkv + kv) *
+                    kWaves + wave;
+            if (active)
+                merge_slot<D>(part, slot0, kstride, kr.n_chunks, out, wq0, s1, H, h, geom.gate,
+                              geom.gate_per_head, lane);
+            if (tid == 0) reset_counter(part, item_slot);
+        }
     }
 }
 
@@ -935,6 +952,7 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
                             int n_items, hipStream_t stream) {
     __bf16* w = static_cast<__bf16*>(ws);
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
+    const bool merge = part.cnt != nullptr;  // in-place merge of split items
     const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
     const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv),
         block(kThreads);
@@ -950,8 +968,12 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
         else                                                                                    \
             hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, false>), sgrid, sblock, 0, stream,\
                                k, v, w, sched, geom.Hkv, p);                                    \
-        hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP, false>), grid, block, 0, stream, q, w, \
-                           out, sched, geom, p, part, Q8Store{});                               \
+        if (merge)                                                                              \
+            hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP, false, true>), grid, block, 0,     \
+                               stream, q, w, out, sched, geom, p, part, Q8Store{});             \
+        else                                                                                    \
+            hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP, false, false>), grid, block, 0,    \
+                               stream, q, w, out, sched, geom, p, part, Q8Store{});             \
     } while (0)
 #define PFA_LAUNCH_BF16_P(DD, SS)                   \
     do {                                            \
@@ -968,7 +990,7 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
 #undef PFA_LAUNCH_BF16_P
 #undef PFA_LAUNCH_BF16
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && sched.max_chunks > 1)
+    if (e == hipSuccess && sched.max_chunks > 1 && !merge)
         e = launch_attn_combine(part, out, sched, geom, D, kWaves, kBN, n_items, stream);
     return e;
 }
@@ -981,6 +1003,7 @@ hipError_t launch_attn_q8(const Q8Store& st8, float* out, void* ws, const AttnSc
     // head_dim 128: int8 K tiles (64 x D bytes); 64: bf16 K tiles.  Then the bf16 V
     // tiles, then the key scales (the attention kernel finds them the same way).
     float* ks_ws = reinterpret_cast<float*>(wb + q8_tile_bytes(sched.n_tiles, geom.Hkv, D));
+    const bool merge = part.cnt != nullptr;  // in-place merge of split items
     const PrepParams p{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
     const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
     const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv),
@@ -988,16 +1011,24 @@ hipError_t launch_attn_q8(const Q8Store& st8, float* out, void* ws, const AttnSc
     if (D == 128) {
         hipLaunchKernelGGL((stage_kv_q8_kernel<128, true>), sgrid, sblock, 0, stream, st8, wb,
                            ks_ws, sched, geom.Hkv);
-        hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true>), grid, block, 0, stream,
-                           nullptr, w, out, sched, geom, p, part, st8);
+        if (merge)
+            hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true, true>), grid, block, 0,
+                               stream, nullptr, w, out, sched, geom, p, part, st8);
+        else
+            hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true, false>), grid, block, 0,
+                               stream, nullptr, w, out, sched, geom, p, part, st8);
     } else {
         hipLaunchKernelGGL((stage_kv_q8_kernel<64, false>), sgrid, sblock, 0, stream, st8, wb,
                            ks_ws, sched, geom.Hkv);
-        hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true>), grid, block, 0, stream,
-                           nullptr, w, out, sched, geom, p, part, st8);
+        if (merge)
+            hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true, true>), grid, block, 0,
+                               stream, nullptr, w, out, sched, geom, p, part, st8);
+        else
+            hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true, false>), grid, block, 0,
+                               stream, nullptr, w, out, sched, geom, p, part, st8);
     }
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && sched.max_chunks > 1)
+    if (e == hipSuccess && sched.max_chunks > 1 && !merge)
         e = launch_attn_combine(part, out, sched, geom, D, kWaves, kBN, n_items, stream);
     return e;
 }

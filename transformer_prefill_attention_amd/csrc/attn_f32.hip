@@ -100,7 +100,7 @@ __device__ __forceinline__ void prep_row(float (&x)[D / 64], const float* w, con
     }
 }
 
-template <int D, bool PREP, bool PAIRED>
+template <int D, bool PREP, bool PAIRED, bool MERGE>
 __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, AttnSched sched, AttnGeom geom, PrepParams prep, Partials part) {
@@ -415,8 +415,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     // or for a split item to this unit's partial-result slot)
     const double l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = l_tot > 0.0 ? (float)(1.0 / l_tot) : 0.0f;
-    const size_t slot = (size_t)bid * kWaves + wave;
-    if (split && hl == 0) part.ml[slot * 32 + ln] = float2{m_run, (float)l_tot};
+    // (the slot is wavefront-uniform: its buffer resource lives in scalar registers)
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const size_t slot = (size_t)bid * kWaves + wave_u;
+    if (split && hl == 0) {
+        part.ml[slot * 32 + ln] = float2{m_run, (float)l_tot};
+    }
     float* os = smem + wave * 32 * QS;
     if (active) {
         // lane (hl, ln), register r of block cb holds O[qi][cb*32 + 8(r/4) + 4hl + r%4]
@@ -440,14 +444,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             const int r = f / F4_PER_ROW, c4 = f % F4_PER_ROW;
             const int row = wq0 + r;
             const floatx4 x = *reinterpret_cast<const floatx4*>(os + r * QS + 4 * c4);
-            if (split)
+            if (split) {
                 *reinterpret_cast<floatx4*>(part.o + (slot * 32 + r) * D + 4 * c4) = x;
-            else if (row < s1) {
+            } else if (row < s1) {
                 floatx4 y = x;
                 if (geom.gate) y *= gate_factors(geom.gate, geom.gate_per_head, row, n_q, h,
                                                  D, 4 * c4);
                 *reinterpret_cast<floatx4*>(out + ((int64_t)row * n_q + h) * D + 4 * c4) = y;
             }
+        }
+    }
+    if constexpr (MERGE) {
+        // the item's last unit to arrive merges every key chunk's partial result
+        __shared__ int last_flag;
+        const size_t item_slot = ((size_t)wi.item * geom.chunks + chunk) * n_kv + kv;
+        if (split && arrive_last(part, item_slot, kr.n_chunks, &last_flag)) {
+            const size_t kstride = (size_t)geom.chunks * n_kv * kWaves;
+            const size_t slot0 =
+                (((size_t)wi.item * sched.max_chunks * geom.chunks + chunk) * n_kv + kv) *
+                    kWaves + wave_u;
+            if (active)
+                merge_slot<D>(part, slot0, kstride, kr.n_chunks, out, wq0, s1, n_q, h,
+                              geom.gate, geom.gate_per_head, lane);
+            if (tid == 0) reset_counter(part, item_slot);
         }
     }
     }  // pass
@@ -463,14 +482,19 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
     const long long slots = sched.paired ? (n_items + 1) / 2 : (long long)n_items * sched.max_chunks;
     const dim3 grid((unsigned)(slots * geom.chunks * geom.Hkv)), block(kThreads);
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
+    // paired items are never split (the host pairs only without a key split)
+    const bool merge = part.cnt != nullptr;
 #define PFA_LAUNCH_F32(DD, PP)                                                                    \
     do {                                                                                          \
         if (sched.paired)                                                                         \
-            hipLaunchKernelGGL((attn_f32_kernel<DD, PP, true>), grid, block, 0, stream, q, k, v, \
-                               out, sched, geom, p, part);                                        \
+            hipLaunchKernelGGL((attn_f32_kernel<DD, PP, true, false>), grid, block, 0, stream,   \
+                               q, k, v, out, sched, geom, p, part);                               \
+        else if (merge)                                                                           \
+            hipLaunchKernelGGL((attn_f32_kernel<DD, PP, false, true>), grid, block, 0, stream,   \
+                               q, k, v, out, sched, geom, p, part);                               \
         else                                                                                      \
-            hipLaunchKernelGGL((attn_f32_kernel<DD, PP, false>), grid, block, 0, stream, q, k, v,\
-                               out, sched, geom, p, part);                                        \
+            hipLaunchKernelGGL((attn_f32_kernel<DD, PP, false, false>), grid, block, 0, stream,  \
+                               q, k, v, out, sched, geom, p, part);                               \
     } while (0)
     if (D == 128) {
         if (prep) PFA_LAUNCH_F32(128, true);
@@ -481,7 +505,7 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
     }
 #undef PFA_LAUNCH_F32
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && sched.max_chunks > 1)
+    if (e == hipSuccess && sched.max_chunks > 1 && !merge)
         e = launch_attn_combine(part, out, sched, geom, D, kWaves, kBN, n_items, stream);
     return e;
 }

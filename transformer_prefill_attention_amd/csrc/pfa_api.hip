@@ -8,6 +8,7 @@
 // as errors rather than aborts): every problem is reported as a status code
 // with a thread-local message, and T == 0 succeeds without a launch.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -192,12 +193,33 @@ struct Plan {
     pfa::AttnGeom geom;
     pfa::AttnSched sched;
     int items = 0;
-    int waves = 0, tile_keys = 0;
+    int waves = 0, tile_keys = 0, head_dim = 0;
     size_t tile_bytes = 0;   // bf16: K/V tiles
     size_t table_bytes = 0;  // bf16 fused entry: rotary table (max_len x d/2 pairs)
     size_t krot_bytes = 0;   // f32 fused entry: the normalised, rotated K (T x Hkv x d)
-    size_t part_bytes = 0;   // key split: partial results
+    size_t part_bytes = 0;   // key split: partial results (and merge counters)
+    long long counters = 0;  // key split merged in place: arrival counters (else 0)
+    // the partial-result parts inside the workspace region at `base`, this call's tag
+    pfa::Partials partials(void* base) const;
 };
+
+// Tag of one call's merge counters (see pfa::Partials): 1 .. 2^48 - 1, never repeating
+// within 2^48 - 1 calls of the process.
+unsigned long long next_call_tag() {
+    static std::atomic<unsigned long long> tag{0};
+    unsigned long long t;
+    do {
+        t = (tag.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << 48) - 1);
+    } while (t == 0);
+    return t;
+}
+
+pfa::Partials Plan::partials(void* base) const {
+    if (!part_bytes) return pfa::Partials{nullptr, nullptr, nullptr, 0};
+    const long long units = (long long)items * sched.max_chunks * geom.chunks * geom.Hkv;
+    return pfa::partials_at(base, (int)units, waves, head_dim, counters,
+                            counters ? next_call_tag() : 0);
+}
 
 constexpr int kF32TileKeys = 32;
 // Compute units of the current device: the workgroups that fill the GPU once are its CUs x
@@ -234,20 +256,27 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // least 128 keys (at T = 512 shorter chunks were 4-12% slower; a chunk of 1024
 // new rows over 7168 cached ones, whose items fill only half the slots, gets two:
 // 7-24% faster), and an item is cut into at most kMaxKeyChunks chunks (one new row
-// over 8191 cached ones ran 8-20% slower in 64 chunks than in 32).  The bf16 kernel
-// splits only when a sequence spans at least kBf16SplitTiles tiles (2048 keys): a
-// bf16 tile step is short, so below that the merge launch costs more than the
-// shorter units save (unsplit at T = 512 with 16/8 heads 32.2 against 34.9 us, 32/8
-// heads 32.8 against 42.3 us, T = 1024 47.1 against 49.7 us; equal at T = 2048).
+// over 8191 cached ones ran 8-20% slower in 64 chunks than in 32).
+// Items of at most kMergeChunks chunks are merged in place by their last unit, more
+// by the combine launch, which spreads the partial results of many chunks over more
+// workgroups (256 new rows over 8192 cached keys in 8 chunks: f32 307 us with the
+// launch against 325 in place, bf16 71 against 95; in place with up to 4 chunks, f32
+// T = 512 / 1024 with 32/8 heads 61 -> 54 / 161 -> 151 us, bf16x3 T = 1024 with 16/8
+// heads 63 -> 51 us).
+// The bf16 kernel with plain bf16 or 8-bit inputs (short_steps) splits only when a
+// sequence spans at least kBf16SplitTiles tiles (2048 keys): its tile step is short,
+// and below that neither merge gains on the unsplit kernel (T = 512 with 32/8 heads:
+// unsplit 32.7 us, split 40.1 in place, 42.3 with the combine launch).
 constexpr int kMaxKeyChunks = 32;
 constexpr int kBf16SplitTiles = 32;
-void choose_split(Plan& p, int head_dim) {
+void choose_split(Plan& p, int head_dim, bool short_steps) {
+    p.head_dim = head_dim;
     const long long wgs = (long long)p.items * p.geom.chunks * p.geom.Hkv;
     const int target = (p.waves == 8 ? 1 : 2) * device_cus();
     const int n_max = (p.sched.max_len + p.tile_keys - 1) / p.tile_keys;
     const long long k_min = std::max<long long>((128 + p.tile_keys - 1) / p.tile_keys,
                                                 (n_max + kMaxKeyChunks - 1) / kMaxKeyChunks);
-    const int n_split = p.waves == 8 ? kBf16SplitTiles : 2;  // fewest tiles worth splitting
+    const int n_split = short_steps ? kBf16SplitTiles : 2;  // fewest tiles worth splitting
     int kchunk = 0;
     if (wgs < target && n_max >= n_split) {
         const long long k = (wgs * n_max + target - 1) / target;
@@ -258,7 +287,10 @@ void choose_split(Plan& p, int head_dim) {
     p.sched.max_chunks = kchunk ? (n_max + kchunk - 1) / kchunk : 1;
     const long long units =
         (long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv;
-    p.part_bytes = kchunk ? pfa::partials_bytes((int)units, p.waves, head_dim) : 0;
+    p.counters = kchunk && p.sched.max_chunks <= pfa::kMergeChunks
+                     ? (long long)p.items * p.geom.chunks * p.geom.Hkv
+                     : 0;
+    p.part_bytes = kchunk ? pfa::partials_bytes((int)units, p.waves, head_dim, p.counters) : 0;
 }
 
 // Paired items for the f32 kernel (AttnSched::paired): each workgroup takes item j and
@@ -287,7 +319,8 @@ int make_plan(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim, 
     p.tile_keys = bf16 ? pfa::kBf16TileKeys : kF32TileKeys;
     choose_geometry(n_head, n_head_kv, scale, causal, p.waves, p.geom);
     p.items = build_sched(st, 32 * p.geom.rb, p.sched);
-    choose_split(p, head_dim);
+    // plain bf16 (and the 8-bit kernels, which plan as bf16): short tile steps
+    choose_split(p, head_dim, precision == PFA_PREC_BF16);
     if ((long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv >= (1LL << 31))
         return fail(PFA_ERR_UNSUPPORTED, "grid too large");
     if (bf16) {
@@ -440,6 +473,7 @@ static int plan_call(Mode mode, const pfa::SeqTable& st, int n_head, int n_head_
         p.sched.kchunk = 0;
         p.sched.max_chunks = 1;
         p.part_bytes = 0;
+        p.counters = 0;
     }
     cp.need = p.part_bytes ? cp.part_off + p.part_bytes : cp.base;
     p.sched.paired = !bf16 && pair_items(p, st, causal, window, chunk) ? 1 : 0;
@@ -508,14 +542,7 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
              (overlaps(workspace, need, k_cache, cb) || overlaps(workspace, need, v_cache, cb))))
             return fail(PFA_ERR_INVALID_ARG, "workspace must not overlap the tensors");
     }
-    pfa::Partials part{nullptr, nullptr};
-    if (p.part_bytes) {
-        const long long units =
-            (long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv;
-        char* w = static_cast<char*>(workspace) + part_off;
-        part.o = reinterpret_cast<float*>(w);
-        part.ml = reinterpret_cast<float2*>(w + (size_t)units * p.waves * 32 * head_dim * 4);
-    }
+    const pfa::Partials part = p.partials(static_cast<char*>(workspace) + part_off);
     if ((rc = check_aligned({q, k, v, out, k_cache, v_cache, gate, prep ? prep->wq : nullptr,
                              prep ? prep->wk : nullptr, prep ? prep->k_rot_out : nullptr})))
         return rc;
@@ -857,14 +884,7 @@ static int attn_q8_common(bool fused, pfa::Q8Store in, const float* q, const flo
         {fused ? v : nullptr, newk * 4, false, "v"}};
     if ((rc = check_spans(sp, 12))) return rc;
     char* ws = static_cast<char*>(workspace);
-    pfa::Partials part{nullptr, nullptr};
-    if (p.part_bytes) {
-        const long long units =
-            (long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv;
-        part.o = reinterpret_cast<float*>(ws + l.part_off);
-        part.ml = reinterpret_cast<float2*>(ws + l.part_off +
-                                            (size_t)units * p.waves * 32 * head_dim * 4);
-    }
+    const pfa::Partials part = p.partials(ws + l.part_off);
     if ((rc = check_aligned({out, gate, q, k, v, prep ? prep->wq : nullptr,
                              prep ? prep->wk : nullptr})))
         return rc;
@@ -962,30 +982,32 @@ void kernel_names(int entry, int precision, int D, int rope_dim, const Plan& p, 
     const bool fused = entry == PFA_ENTRY_PREP || entry == PFA_ENTRY_CHUNK_PREP ||
                        entry == PFA_ENTRY_Q8_PREP;
     const bool split_keys = p.sched.max_chunks > 1;
+    const char* merge = p.counters ? "true" : "false";  // split items merged in place
     const char* sep = "";
     if (entry == PFA_ENTRY_Q8 || entry == PFA_ENTRY_Q8_PREP) {
         if (fused) {
             append(buf, n, "qknorm_rope_kernel<%d,%d,true>", D, qknorm_mode(D, rope_dim));
             sep = " + ";
         }
-        append(buf, n, "%sstage_kv_q8_kernel<%d,%s> + attn_bf16_kernel<%d,false,false,true>", sep,
-               D, D == 128 ? "true" : "false", D);
+        append(buf, n, "%sstage_kv_q8_kernel<%d,%s> + attn_bf16_kernel<%d,false,false,true,%s>",
+               sep, D, D == 128 ? "true" : "false", D, merge);
     } else if (precision == PFA_PREC_F32) {
         if (fused) {
             append(buf, n, "qknorm_rope_kernel<%d,%d,false> + ", D, qknorm_mode(D, rope_dim));
         }
-        append(buf, n, "attn_f32_kernel<%d,%s,%s>", D, fused ? "true" : "false",
-               p.sched.paired ? "true" : "false");
+        append(buf, n, "attn_f32_kernel<%d,%s,%s,%s>", D, fused ? "true" : "false",
+               p.sched.paired ? "true" : "false", merge);
     } else {
         const char* sp = precision == PFA_PREC_BF16X3 ? "true" : "false";
         if (entry == PFA_ENTRY_CHUNK_PREP) {
             append(buf, n, "qknorm_rope_kernel<%d,%d,false> + ", D, qknorm_mode(D, rope_dim));
         }
         if (fused) append(buf, n, "rope_table_kernel<%d,%s> + ", D, sp);
-        append(buf, n, "stage_kv_bf16_kernel<%d,%s,%s> + attn_bf16_kernel<%d,%s,%s,false>", D, sp,
-               entry == PFA_ENTRY_PREP ? "true" : "false", D, sp, fused ? "true" : "false");
+        append(buf, n, "stage_kv_bf16_kernel<%d,%s,%s> + attn_bf16_kernel<%d,%s,%s,false,%s>", D,
+               sp, entry == PFA_ENTRY_PREP ? "true" : "false", D, sp, fused ? "true" : "false",
+               merge);
     }
-    if (split_keys) append(buf, n, " + attn_combine_kernel<%d>", D);
+    if (split_keys && !p.counters) append(buf, n, " + attn_combine_kernel<%d>", D);
 }
 
 // Arguments of a plan query -> sequence table and plan (what the entry point would do).
@@ -1048,6 +1070,7 @@ int pfa_attn_plan(int entry, const int32_t* q_offsets, const int32_t* kv_offsets
     plan->key_chunk_tiles = p.sched.kchunk;
     plan->max_key_chunks = p.sched.max_chunks;
     plan->paired = p.sched.paired;
+    plan->merge_in_place = p.counters ? 1 : 0;
     const long long slots =
         p.sched.paired ? (p.items + 1) / 2 : (long long)p.items * p.sched.max_chunks;
     plan->workgroups = p.items ? slots * p.geom.chunks * p.geom.Hkv : 0;

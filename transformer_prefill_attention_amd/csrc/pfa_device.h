@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pfa_internal.h"
+
 namespace pfa {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -210,6 +212,130 @@ __host__ __device__ __forceinline__ KeyRange item_key_range(const Sched& sched, 
     r.t_begin = r.t_first + wi.kc * kchunk;
     r.t_end = r.t_begin + kchunk < r.n_tiles ? r.t_begin + kchunk : r.n_tiles;
     return r;
+}
+
+// ---------------------------------------------------------------------------
+// In-place merge of a split item's partial results (see Partials).
+//
+// Units of one item may run on different XCDs, each with its own L2, so the hand-over
+// follows the agent-scope memory model: every wavefront's partial-result stores complete
+// (s_waitcnt vmcnt(0), then a workgroup barrier), one thread releases them at agent scope
+// (an L2 write-back) before counting the unit's arrival, and the last unit to arrive
+// acquires at agent scope (an L1 / L2 invalidate) before it reads the other units'
+// results with ordinary loads.
+
+// Called by every thread of a workgroup once each of its wavefronts has issued the
+// stores of its partial result: counts the unit's arrival on counter `c` and returns,
+// in every thread, whether this unit is the item's last (n_chunks arrivals).  `flag` is
+// one int of LDS.  The compare-and-swap retries only while other units change the
+// counter (at most n_chunks - 1 times); it never waits for anything.
+__device__ __forceinline__ bool arrive_last(const Partials& part, size_t c, int n_chunks,
+                                            int* flag) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's partial-result stores have completed
+    __syncthreads();                // ... and every other wavefront's
+    if (threadIdx.x == 0) {
+        // release: the unit's partial results are visible at agent scope before its arrival
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        unsigned long long* p = part.cnt + c;
+        unsigned long long old = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long nw;
+        do {
+            nw = (old >> 16) == part.tag ? old + 1 : (part.tag << 16) | 1ull;
+        } while (!__hip_atomic_compare_exchange_strong(p, &old, nw, __ATOMIC_RELAXED,
+                                                       __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+        const bool last = (int)(nw & 0xFFFF) == n_chunks;
+        // acquire: the last unit sees every other unit's released results
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    return *flag != 0;
+}
+
+// The last unit leaves the counter 0 (after its merge has read everything).
+__device__ __forceinline__ void reset_counter(const Partials& part, size_t c) {
+    __hip_atomic_store(part.cnt + c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge of one wavefront slot's key chunks (32 query rows of head h, rows row0 .. row0 +
+// 31, those below s1 real; 2 <= n_chunks <= kMergeChunks) into `out`.  The softmax over
+// the union of the chunks' keys, with M = max_k m_k and w_k = l_k 2^(m_k - M) (m in log2
+// units, as the attention kernels keep it), is O = sum_k w_k (O_k / l_k) / sum_k w_k --
+// the rescaling the online softmax applies between tiles; a chunk that saw none of a
+// row's keys has l_k = 0 and weight 0.  Chunk k sits in slot slot0 + k * kstride.
+// Lane L (< 32) forms the weights of row L; the rows themselves are read coalesced,
+// load instruction i of a chunk taking float4 number 64 i + L of the slot (row
+// (64 i + L) / (D / 4)), whose weight comes from the row's lane by a shuffle.  Every
+// chunk's (m, l) and the first two chunks' rows are loaded together, then two chunks'
+// rows per round trip.  An optional gate multiplies the merged rows (out = O *
+// sigmoid(gate)).
+template <int D>
+__device__ __forceinline__ void merge_slot(const Partials& part, size_t slot0, size_t kstride,
+                                           int n_chunks, float* out, int row0, int s1, int H,
+                                           int h, const float* gate, int gate_per_head,
+                                           int lane) {
+    constexpr int F4 = D / 4;          // float4 per row
+    constexpr int NV = 32 * F4 / 64;   // float4 per lane and chunk
+    constexpr int RPI = 64 / F4;       // rows per load instruction
+    const int r = lane & 31;
+    auto load_rows = [&](int k, floatx4* x) {
+        const floatx4* src =
+            reinterpret_cast<const floatx4*>(part.o + (slot0 + (size_t)k * kstride) * 32 * D);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) x[i] = src[64 * i + lane];
+    };
+    float m[kMergeChunks], l[kMergeChunks];
+#pragma unroll
+    for (int k = 0; k < kMergeChunks; ++k) {
+        m[k] = -INFINITY;
+        l[k] = 0.0f;
+        if (k < n_chunks) {
+            const float2 ml = part.ml[(slot0 + (size_t)k * kstride) * 32 + r];
+            m[k] = ml.x;
+            l[k] = ml.y;
+        }
+    }
+    floatx4 xa[NV], xb[NV];
+    load_rows(0, xa);
+    load_rows(1, xb);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeChunks; ++k)
+        if (l[k] > 0.0f) mx = fmaxf(mx, m[k]);
+    float w[kMergeChunks], den = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMergeChunks; ++k) {
+        w[k] = l[k] > 0.0f ? l[k] * __builtin_amdgcn_exp2f(m[k] - mx) : 0.0f;
+        den += w[k];
+    }
+    // weight of chunk k for the row of this lane's i-th float4
+    auto wrow = [&](float wk, int i) { return __shfl(wk, RPI * i + lane / F4, 64); };
+    floatx4 acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = wrow(w[0], i) * xa[i] + wrow(w[1], i) * xb[i];
+#pragma unroll
+    for (int k = 2; k < kMergeChunks; k += 2) {
+        if (k < n_chunks) {  // (uniform)
+            load_rows(k, xa);
+            load_rows(k + 1 < n_chunks ? k + 1 : k, xb);
+            const float wb = k + 1 < n_chunks ? w[k + 1] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) acc[i] += wrow(w[k], i) * xa[i] + wrow(wb, i) * xb[i];
+        }
+    }
+    const float inv_r = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int rr = RPI * i + lane / F4, c4 = lane % F4;
+        const int row = row0 + rr;
+        const float inv = __shfl(inv_r, rr, 64);
+        if (row < s1) {
+            floatx4 y = acc[i] * inv;
+            if (gate) y *= gate_factors(gate, gate_per_head, row, H, h, D, 4 * c4);
+            *reinterpret_cast<floatx4*>(out + ((int64_t)row * H + h) * D + 4 * c4) = y;
+        }
+    }
 }
 
 }  // namespace pfa

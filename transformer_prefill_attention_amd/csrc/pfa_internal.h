@@ -51,7 +51,8 @@ struct AttnSched {
     // item's key tiles are cut into chunks of kchunk tiles, one workgroup each
     // (grid = items x max_chunks x head chunks x K/V heads; chunk slots past an
     // item's count exit at once).  Items with more than one chunk write partial
-    // results that attn_combine_kernel merges.  kchunk = 0: no split (max_chunks 1).
+    // results, merged in place by the item's last unit (max_chunks <= kMergeChunks)
+    // or by attn_combine_kernel (see Partials).  kchunk = 0: no split (max_chunks 1).
     int kchunk;
     int max_chunks;
     // f32 kernel without a key split: workgroup j takes item j, then item
@@ -63,12 +64,39 @@ struct AttnSched {
 // Partial results of a split item, per work unit (blockIdx) and wavefront:
 // 32 rows x D of O / l (f32), and per row (m, l): running max (log2 units) and
 // softmax denominator.  An empty wavefront writes m = -inf, l = 0.
+//
+// Two ways to merge them.  When every item has at most kMergeChunks chunks, in place:
+// each unit counts its arrival on its item's counter once its partial result is
+// stored, and the unit that arrives last merges all of them into the output (no
+// second launch; the counters are `cnt`).  A counter is [tag : 48 bits | arrivals :
+// 16 bits]; a value whose tag is not this call's counts as no arrivals, so the
+// workspace needs no clearing, and the merging unit leaves it 0 (a replayed graph,
+// whose tag is fixed, finds it so).  Otherwise (cnt null) attn_combine_kernel merges
+// them in a second launch, which spreads the many chunks of a long cache over more
+// workgroups.
+constexpr int kMergeChunks = 4;
 struct Partials {
-    float* o;       // [units][waves][32][D]
-    float2* ml;     // [units][waves][32]
+    float* o;                  // [units][waves][32][D]
+    float2* ml;                // [units][waves][32]
+    unsigned long long* cnt;   // [items][head chunks][Hkv] arrival counters, or null
+    unsigned long long tag;    // this call's tag, 1 .. 2^48 - 1 (in-place merge only)
 };
-inline size_t partials_bytes(int units, int waves, int D) {
-    return (size_t)units * waves * 32 * (D * 4 + 8);
+// Bytes of the partial results and, for the in-place merge, `counters` counters
+// (after the results, 256-byte aligned).
+inline size_t partials_bytes(int units, int waves, int D, long long counters) {
+    const size_t b = (size_t)units * waves * 32 * (D * 4 + 8);
+    return counters ? ((b + 255) & ~(size_t)255) + (size_t)counters * 8 : b;
+}
+// The parts of a partial-result region at `base` (cnt null without counters).
+inline Partials partials_at(void* base, int units, int waves, int D, long long counters,
+                            unsigned long long tag) {
+    char* w = static_cast<char*>(base);
+    const size_t ob = (size_t)units * waves * 32 * D * 4, mb = (size_t)units * waves * 32 * 8;
+    return Partials{reinterpret_cast<float*>(w), reinterpret_cast<float2*>(w + ob),
+                    counters ? reinterpret_cast<unsigned long long*>(
+                                   w + ((ob + mb + 255) & ~(size_t)255))
+                             : nullptr,
+                    tag};
 }
 
 // Geometry common to the attention launches.

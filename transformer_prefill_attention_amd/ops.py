@@ -44,7 +44,7 @@ class _Plan(ctypes.Structure):
     _fields_ = [("items", ctypes.c_int), ("rows_per_item", ctypes.c_int),
                 ("waves_per_workgroup", ctypes.c_int), ("tile_keys", ctypes.c_int),
                 ("key_chunk_tiles", ctypes.c_int), ("max_key_chunks", ctypes.c_int),
-                ("paired", ctypes.c_int), ("reserved", ctypes.c_int),
+                ("paired", ctypes.c_int), ("merge_in_place", ctypes.c_int),
                 ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("kernels", ctypes.c_char * 320)]
 
@@ -613,7 +613,7 @@ def attn_plan(entry: int, *, T_q: int, n_head: int, n_head_kv: int, head_dim: in
                             workspace_bytes)
     plan = _Plan()
     _check(lib().pfa_attn_plan(*args, ctypes.byref(plan)))
-    res = {name: getattr(plan, name) for name, _ in _Plan._fields_ if name != "reserved"}
+    res = {name: getattr(plan, name) for name, _ in _Plan._fields_}
     res["kernels"] = plan.kernels.decode()
     return res
 
