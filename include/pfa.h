@@ -171,8 +171,11 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
  *  A call whose workspace would exceed the array (pfa_workspace_bytes(..., 0) larger than
  *  pfa_noalloc_scratch_bytes(): e.g. the bf16 modes beyond 16384 key rows at 8 K/V heads of
  *  128) fails with PFA_ERR_UNSUPPORTED before anything is enqueued.
- *  Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
- *  (on different streams, or from different threads) race and must not be issued.
+ *  Every call on one GPU shares that GPU's array, which keeps what the last call left
+ *  (staged tiles, partial results, the key split's arrival counters); nothing needs
+ *  clearing between calls (the counters are tagged per call and left 0).  Calls that
+ *  overlap in time on one GPU (on different streams, or from different threads) race and
+ *  must not be issued.
  */
 int gqa_prefill_attn_noalloc(const float* q, const float* k, const float* v, float* out,
                              const int32_t* seq_offsets, int n_seqs, int T, int n_head,

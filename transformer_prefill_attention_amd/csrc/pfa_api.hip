@@ -611,9 +611,10 @@ int gqa_prefill_attn(const float* q, const float* k, const float* v, float* out,
 // allocation).  Its workspace is this library-owned device array (each GPU the library
 // runs on holds one copy until the process ends); it is resolved to a device address
 // once per device with hipGetSymbolAddress, and only that address reaches the kernels.
-// Nothing in it needs clearing: the staging kernels write every tile they later read and
-// the key split writes every partial result before the combine step reads it.  Calls
-// that overlap on one GPU share the array and race.
+// Nothing in it needs clearing: the staging kernels write every tile they later read, the
+// key split writes every partial result before it is merged, and the in-place merge's
+// arrival counters are tagged per call (a value left by another call counts as none) and
+// left 0.  Calls that overlap on one GPU share the array and race.
 namespace {
 
 constexpr size_t kScratchBytes = (size_t)64 << 20;
