@@ -162,9 +162,11 @@ def main():
     ap.add_argument("--seq-len", type=int, default=0, help="override: one sequence of this length "
                                                            "with the 8B-like heads")
     ap.add_argument("--precision", default="f32", choices=["f32", "bf16", "bf16x3"])
-    ap.add_argument("--path", default="unfused", choices=["fused", "unfused"],
+    ap.add_argument("--path", default="unfused", choices=["fused", "unfused", "tiled"],
                     help="unfused (default, currently the faster): qknorm_rope then "
-                         "gqa_prefill_attn; fused: the single qk_prep_attn call")
+                         "gqa_prefill_attn; fused: the single qk_prep_attn call; tiled (with "
+                         "--chunk-base, bf16 modes): qk_prep_chunk_attn_tiled, the cache's bf16 "
+                         "tiles kept across calls")
     ap.add_argument("--chunk-base", type=int, default=0, metavar="B",
                     help="time a chunk over a cached prefix instead: the workload's one sequence "
                          "is B cached rows (K normalised and rotated, V) and T - B new rows; "
@@ -226,9 +228,11 @@ def main():
     w = wl.sweep_workload(args.seq_len) if args.seq_len else wl.CONFIGS[args.workload]
     x = wl.make_inputs(w)
     if args.q8:
+        if args.path == "tiled":
+            raise SystemExit("--path tiled is a chunk entry (not --q8)")
         run_q8(args, w, x)
         return
-    if args.chunk_base or args.window or args.gate != "none":
+    if args.chunk_base or args.window or args.gate != "none" or args.path == "tiled":
         run_chunk(args, w, x)
         return
     k_in = wl.with_outlier_keys(x.k, x.outliers)
@@ -453,6 +457,21 @@ def run_chunk(args, w, x):
     q_new, k_new, v_new = t["q"][B:].contiguous(), t["k"][B:].contiguous(), t["v"][B:].contiguous()
     q_prep = qn[B:].contiguous()
     out = torch.empty_like(q_new)
+    kv_tiles = None
+    if args.path == "tiled":
+        if args.precision == "f32":
+            raise SystemExit("--path tiled is for the bf16 modes")
+        # the tiles a previous call would have left: the prefix rows appended once
+        # (untimed); each step then re-stages the tiles of its new rows
+        kv_tiles = torch.empty(pfa.kv_tiles_bytes(1, T, w.n_head_kv, w.head_dim, args.precision),
+                               dtype=torch.uint8, device=dev)
+        if B:
+            kp, vp = k_cache[:B].clone(), v_cache[:B].clone()
+            pfa.qk_prep_chunk_attn_tiled(t["q"][:B].contiguous(), t["k"][:B].contiguous(),
+                                         t["v"][:B].contiguous(), t["wq"], t["wk"], kp, vp,
+                                         kv_tiles, max_rows=T, scale=w.softmax_scale,
+                                         precision=args.precision, **kw_rope)
+            torch.cuda.synchronize()
     gate = None
     if args.gate != "none":
         g = torch.Generator().manual_seed(w.seed + 1)
@@ -469,6 +488,11 @@ def run_chunk(args, w, x):
             pfa.qk_prep_chunk_attn(q_new, k_new, v_new, t["wq"], t["wk"], k_cache, v_cache,
                                    scale=w.softmax_scale, window=args.window, gate=gate,
                                    precision=args.precision, out=out, **kw_rope)
+        elif args.path == "tiled":
+            pfa.qk_prep_chunk_attn_tiled(q_new, k_new, v_new, t["wq"], t["wk"], k_cache, v_cache,
+                                         kv_tiles, max_rows=T, scale=w.softmax_scale,
+                                         window=args.window, gate=gate,
+                                         precision=args.precision, out=out, **kw_rope)
         else:
             pfa.gqa_chunk_attn(q_prep, k_cache, v_cache, head_dim=w.head_dim,
                                scale=w.softmax_scale, window=args.window, gate=gate,
@@ -501,7 +525,9 @@ def run_chunk(args, w, x):
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.precision]
     d = w.head_dim
-    kernel = pfa.attn_plan(pfa.ENTRY_CHUNK_PREP if args.path == "fused" else pfa.ENTRY_CHUNK,
+    entry = {"fused": pfa.ENTRY_CHUNK_PREP, "tiled": pfa.ENTRY_CHUNK_TILED}.get(args.path,
+                                                                          pfa.ENTRY_CHUNK)
+    kernel = pfa.attn_plan(entry,
                            T_q=T_q, T_kv=T, n_head=w.n_head, n_head_kv=w.n_head_kv, head_dim=d,
                            rope_dim=w.rope_dim, window=args.window, precision=args.precision,
                            q_offsets=[0, T_q], kv_offsets=[0, T])["kernels"]

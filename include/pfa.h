@@ -288,15 +288,65 @@ int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* ou
                        float rope_freq_base, float rms_eps, float scale, int causal, int window,
                        int precision, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device workspace in bytes that gqa_chunk_attn (fused = 0) or qk_prep_chunk_attn
- * (fused = 1) uses for these arguments: as pfa_workspace_bytes, with the bf16 tiles
- * covering each sequence's cache rows (sum_s ceil(kv_len_s / 64) tiles) and the
- * rotary table max_s(kv_len_s) rows; the f32 modes need room only for the key
- * split.  Returns 0 when nothing is needed or the arguments are ones the calls
+/* Device workspace in bytes that gqa_chunk_attn (fused = 0), qk_prep_chunk_attn
+ * (fused = 1) or qk_prep_chunk_attn_tiled (fused = 2) uses for these arguments: as
+ * pfa_workspace_bytes, with the bf16 tiles covering each sequence's cache rows (sum_s
+ * ceil(kv_len_s / 64) tiles) and the rotary table max_s(kv_len_s) rows; the f32 modes,
+ * and the tiled entry (its tiles and table are in kv_tiles), need room only for the
+ * key split.  Returns 0 when nothing is needed or the arguments are ones the calls
  * would reject (pfa_last_error() then says why). */
 size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
                                  int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
                                  int precision, int fused);
+
+/*
+ * qk_prep_chunk_attn_tiled -- qk_prep_chunk_attn in the bf16 modes, keeping the cache's
+ * bf16 K/V tiles across calls.  qk_prep_chunk_attn converts every cache row to the bf16
+ * tiles the attention kernel reads, on every call; a caller that appends blocks of rows
+ * to the same cache call after call (memra-engine 0.101.0 src/spec.rs,
+ * `full_attn_verify`: a block of rows verified against, and appended to, a persistent
+ * cache) keeps them in kv_tiles instead, and each call converts only the tiles its new
+ * rows fall in.  The result, and what the call writes to k_cache / v_cache, are
+ * qk_prep_chunk_attn's, bit for bit, given tiles that hold the cache's earlier rows.
+ *
+ * Passages: as for qk_prep_chunk_attn.
+ *
+ *  Arguments as for qk_prep_chunk_attn, precision PFA_PREC_BF16 or PFA_PREC_BF16X3
+ *  (PFA_PREC_F32: PFA_ERR_INVALID_ARG), workspace sized by pfa_chunk_workspace_bytes(...,
+ *  2) (the key split's partial results only; often 0), and:
+ *  kv_tiles  device, read and written, 256-byte aligned, pfa_kv_tiles_bytes(n_slots,
+ *        max_rows, n_head_kv, head_dim, precision) bytes, n_slots being this call's
+ *        sequence count (1 when the offsets are NULL); owned by the caller, not
+ *        overlapping the other tensors or the workspace.  Slot s holds the bf16 tiles of
+ *        sequence s's cache rows 0 .. max_rows-1 (64 rows a tile), then a rotary table of
+ *        (cos, sin) pairs by position.  The call stages from k_cache / v_cache -- after
+ *        writing its new rows there -- the tiles holding cache rows floor(base_s / 64) *
+ *        64 .. kv_len_s - 1 of each sequence with new rows, and their table rows; it
+ *        reads the tiles of rows below that from kv_tiles as earlier calls left them.
+ *        So every call on one kv_tiles must pass the same sequence count, max_rows,
+ *        n_head_kv, head_dim, precision, rope_dim and rope_freq_base, and sequence s's
+ *        rows below base_s must have been written by earlier calls on it (a first call
+ *        with base_s = 0 writes all of them).  Rows of a sequence beyond its current
+ *        kv_len_s in a tile are zeros.
+ *  max_rows  >= 1: the most cache rows any sequence may reach (kv_len_s > max_rows:
+ *        PFA_ERR_INVALID_ARG).
+ */
+int qk_prep_chunk_attn_tiled(const float* q, const float* k, const float* v, float* out,
+                             const float* gate, int gate_per_head,
+                             const float* q_norm_w, const float* k_norm_w,
+                             float* k_cache, float* v_cache, void* kv_tiles, int max_rows,
+                             const int32_t* q_offsets, const int32_t* kv_offsets, int n_seqs,
+                             int T_q, int T_kv, int n_head, int n_head_kv, int head_dim,
+                             int rope_dim, float rope_freq_base, float rms_eps, float scale,
+                             int causal, int window, int precision, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Bytes of the kv_tiles of qk_prep_chunk_attn_tiled: n_slots slots (1 .. PFA_MAX_SEQS) of
+ * ceil(max_rows / 64) tiles per K/V head (K: 64 x head_dim bf16, twice for
+ * PFA_PREC_BF16X3; V: 64 x head_dim bf16) and a rotary table of ceil(max_rows / 64) * 64
+ * rows of head_dim / 2 (cos, sin) f32 pairs.  0 (and pfa_last_error()) for arguments the
+ * call would reject. */
+size_t pfa_kv_tiles_bytes(int n_slots, int max_rows, int n_head_kv, int head_dim, int precision);
 
 /*
  * 8-bit quantised sessions
@@ -417,7 +467,8 @@ typedef enum {
     PFA_ENTRY_CHUNK = 2,      /* gqa_chunk_attn */
     PFA_ENTRY_CHUNK_PREP = 3, /* qk_prep_chunk_attn */
     PFA_ENTRY_Q8 = 4,         /* gqa_attn_q8 */
-    PFA_ENTRY_Q8_PREP = 5     /* qk_prep_attn_q8 */
+    PFA_ENTRY_Q8_PREP = 5,    /* qk_prep_attn_q8 */
+    PFA_ENTRY_CHUNK_TILED = 6 /* qk_prep_chunk_attn_tiled */
 } pfa_entry;
 
 typedef struct {

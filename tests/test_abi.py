@@ -373,6 +373,69 @@ def test_chunk_workspace_tiles_cover_the_cache(L):
         2 * tiles + 8192 * 64 * 8
 
 
+@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("q_lens,kv_lens,H,Hkv,D", [
+    ((1024,), (8192,), 32, 8, 128), ((1,), (8192,), 32, 8, 128), ((4096,), (8192,), 32, 8, 128),
+    ((50, 1, 130, 0), (70, 78, 130, 5), 8, 4, 128), ((512,), (512,), 16, 8, 128)])
+def test_tiled_chunk_workspace_holds_only_the_partials(L, q_lens, kv_lens, H, Hkv, D, prec):
+    # qk_prep_chunk_attn_tiled keeps its tiles and rotary table in kv_tiles: its workspace is
+    # the key split's part of qk_prep_chunk_attn's (the same plan)
+    full = _expected_workspace(q_lens, H, Hkv, D, prec, 1, kv_lens=kv_lens, chunk=True)
+    tiles = Hkv * sum(_ceil(n, 64) for n in kv_lens) * 64 * D * 2 * (3 if prec == 2 else 2)
+    base = tiles + max(kv_lens) * (D // 2) * 8
+    parts = full - _ceil(base, 256) * 256 if full > base else 0
+    assert _chunk_ws(L, q_lens, kv_lens, H, Hkv, D, prec, 2) == parts
+    assert _chunk_ws(L, q_lens, kv_lens, H, Hkv, D, 0, 2) == 0  # f32: rejected
+    assert "PFA_PREC_BF16" in _msg(L)
+
+
+@pytest.mark.parametrize("n_slots,max_rows,Hkv,D,prec", [
+    (1, 1, 1, 64, 1), (1, 8192, 8, 128, 1), (3, 1300, 8, 128, 2), (128, 65, 2, 64, 1)])
+def test_kv_tiles_bytes_rule(L, n_slots, max_rows, Hkv, D, prec):
+    # slots of ceil(max_rows / 64) tiles per K/V head (K twice for bf16x3, V once, 64 x D
+    # bf16 each), then a rotary table of that many rows x D/2 (cos, sin) f32 pairs
+    cap = _ceil(max_rows, 64)
+    expect = n_slots * cap * Hkv * (3 if prec == 2 else 2) * 64 * D * 2 + cap * 64 * (D // 2) * 8
+    assert L.pfa_kv_tiles_bytes(n_slots, max_rows, Hkv, D, prec) == expect
+    assert pfa.kv_tiles_bytes(n_slots, max_rows, Hkv, D, "bf16x3" if prec == 2 else "bf16") == expect
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((1, 64, 8, 128, 0), "PFA_PREC_BF16"), ((0, 64, 8, 128, 1), "n_slots"),
+    ((129, 64, 8, 128, 1), "n_slots"), ((1, 0, 8, 128, 1), "max_rows"),
+    ((1, 64, 8, 96, 1), "head_dim")])
+def test_kv_tiles_bytes_rejects(L, args, needle):
+    assert L.pfa_kv_tiles_bytes(*args) == 0
+    assert needle in _msg(L)
+
+
+def _tiled(L, q_offs, kv_offs, T_q, T_kv, max_rows=256, prec=1, tiles=1 << 30, Hkv=2, D=64):
+    keep_q, qp = _i32(q_offs)
+    keep_k, kp = _i32(kv_offs)
+    p = ctypes.c_void_p
+    # q, k, v, out, weights and caches at distinct fake addresses: only the checks run
+    return L.qk_prep_chunk_attn_tiled(p(1 << 20), p(2 << 20), p(3 << 20), p(4 << 20), p(0), 0,
+                                      p(5 << 20), p(5 << 20), p(6 << 20), p(7 << 20), p(tiles),
+                                      max_rows, qp, kp, len(q_offs) - 1, T_q, T_kv, 4, Hkv, D, D,
+                                      1e6, 1e-6, 0.125, 1, 0, prec, p(0), 0, None)
+
+
+def test_tiled_chunk_argument_checks(L):
+    assert _tiled(L, [0, 4], [0, 9], 4, 9, prec=0) == INVALID
+    assert "PFA_PREC_BF16" in _msg(L)
+    assert _tiled(L, [0, 4], [0, 9], 4, 9, tiles=0) == INVALID
+    assert "kv_tiles" in _msg(L)
+    assert _tiled(L, [0, 4], [0, 9], 4, 9, tiles=(1 << 30) + 64) == INVALID
+    assert "aligned" in _msg(L)
+    assert _tiled(L, [0, 4, 8], [0, 9, 300], 8, 300, max_rows=256) == INVALID
+    assert "max_rows" in _msg(L)
+    assert _tiled(L, [0, 4], [0, 9], 4, 9, max_rows=0) == INVALID
+    assert "max_rows" in _msg(L)
+    # kv_tiles over out (4 MiB + 8 KiB of f32 rows at 4 << 20)
+    assert _tiled(L, [0, 4], [0, 9], 4, 9, tiles=4 << 20) == INVALID
+    assert "overlap" in _msg(L)
+
+
 def test_chunk_window_arguments(L):
     assert _chunk(L, [0, 4], [0, 9], 4, 9, window=-1) == INVALID
     assert "window" in _msg(L)

@@ -213,6 +213,15 @@ def test_plan_names_the_kernels_in_launch_order():
                       precision="bf16x3")
     assert p["kernels"] == ("stage_kv_bf16_kernel<128,true,false> + "
                             "attn_bf16_kernel<128,true,false,false,false>")
+    # the tiled chunk entry: the new rows' K/V into the caches, their tiles re-staged into
+    # kv_tiles, attention (1024 rows over 8192: two key chunks, merged in place)
+    p = pfa.attn_plan(pfa.ENTRY_CHUNK_TILED, T_q=1024, T_kv=8192, n_head=32, n_head_kv=8,
+                      head_dim=128, rope_dim=128, precision="bf16", q_offsets=[0, 1024],
+                      kv_offsets=[0, 8192])
+    assert p["kernels"] == ("qknorm_rope_kernel<128,0,false> + append_tiles_kernel<128,false> + "
+                            "attn_bf16_kernel<128,false,true,false,true>")
+    assert p["workspace_bytes"] == pfa.chunk_workspace_bytes(
+        1024, 8192, 32, 8, 128, "bf16", q_offsets=[0, 1024], kv_offsets=[0, 8192], fused=2)
     p = pfa.attn_plan(pfa.ENTRY_Q8, T_q=8192, T_kv=8192, n_head=32, n_head_kv=8, head_dim=64)
     assert p["kernels"] == ("stage_kv_q8_kernel<64,false> + "
                             "attn_bf16_kernel<64,false,false,true,false>")

@@ -164,6 +164,69 @@ __device__ __forceinline__ void store_vt_rows(const __bf16* vts, __bf16* vt, int
     }
 }
 
+// One tile's rows of a 256-thread block, shared by the staging kernels.
+// 8 dims (logical chunk c of row r) -> bf16 high (and low) parts at the swizzled place.
+template <int D, bool SPLIT>
+__device__ __forceinline__ void store_k_chunk(__bf16* tile, int r, int c, const float* x) {
+    constexpr int NCH = D / 8;
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = (__bf16)x[e];
+        if constexpr (SPLIT) lo[e] = (__bf16)(x[e] - (float)hi[e]);
+    }
+    const int pos = swz(r, c, NCH);
+    *reinterpret_cast<bf16x8*>(tile + r * D + 8 * pos) = hi;
+    if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(tile + kBN * D + r * D + 8 * pos) = lo;
+}
+// V rows 0 .. nval-1 (stride row_stride floats; zeros past nval) -> V^T in vts.  4 keys x
+// 4 dims per block, loaded as 4 float4 rows, written as four 4-key runs of V^T.  Block b:
+// dims 4 (b % (D/4)) .., keys 4 (b / (D/4)) ..
+template <int D>
+__device__ __forceinline__ void stage_v_rows(const float* vin, int64_t row_stride, int nval,
+                                             __bf16* vts, int tid) {
+    constexpr int VB = kBN * D / 16;
+#pragma unroll
+    for (int i = 0; i < VB / 256; ++i) {
+        const int b = tid + 256 * i;
+        const int d0 = 4 * (b % (D / 4)), key0 = 4 * (b / (D / 4));
+        floatx4 r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r[e] = key0 + e < nval ? *reinterpret_cast<const floatx4*>(vin + (key0 + e) * row_stride + d0)
+                                   : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            bf16x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (__bf16)r[e][c];
+            *reinterpret_cast<bf16x4*>(vts + (d0 + c) * kVts + key0) = x;
+        }
+    }
+}
+// K rows 0 .. nval-1 (zeros past nval) -> the K tile: 16-byte chunks (8 dims) of each
+// row, converted and written to their swizzled place.
+template <int D, bool SPLIT>
+__device__ __forceinline__ void stage_k_rows(const float* kin, int64_t row_stride, int nval,
+                                             __bf16* kt, int tid) {
+    constexpr int NCH = D / 8;
+#pragma unroll
+    for (int i = 0; i < kBN * NCH / 256; ++i) {
+        const int f = tid + 256 * i;
+        const int r = f / NCH, c = f % NCH;
+        floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+        if (r < nval) {
+            const float* src = kin + r * row_stride + 8 * c;
+            a = *reinterpret_cast<const floatx4*>(src);
+            b = *reinterpret_cast<const floatx4*>(src + 4);
+        }
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = e < 4 ? a[e] : b[e - 4];
+        store_k_chunk<D, SPLIT>(kt, r, c, x);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // K/V -> bf16 tiles.  Block = (K/V head, tile over all sequences).
 //  K tile: KP parts (high, low) x 64 rows x D; element (r, c) at r*D + 8*swz(r, c/8, D/8) + c%8.
@@ -194,55 +257,9 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
                  ((int64_t)kv * n_tiles + gt) * (kBN * D);
     const float* kin = k + (int64_t)k0 * row_stride + kv * D;
     const float* vin = v + (int64_t)k0 * row_stride + kv * D;
-    // 8 dims (logical chunk c of row r) -> bf16 high (and low) parts at the swizzled place
-    auto store_k_chunk = [](__bf16* tile, int r, int c, const float* x) {
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            hi[e] = (__bf16)x[e];
-            if constexpr (SPLIT) lo[e] = (__bf16)(x[e] - (float)hi[e]);
-        }
-        const int pos = swz(r, c, NCH);
-        *reinterpret_cast<bf16x8*>(tile + r * D + 8 * pos) = hi;
-        if constexpr (SPLIT) *reinterpret_cast<bf16x8*>(tile + kBN * D + r * D + 8 * pos) = lo;
-    };
-    // V: 4 keys x 4 dims per block, loaded as 4 float4 rows, written to LDS as four
-    // 4-key runs of V^T.  Block b: dims 4 (b % (D/4)) .., keys 4 (b / (D/4)) ..
-    constexpr int VB = kBN * D / 16;
-#pragma unroll
-    for (int i = 0; i < VB / 256; ++i) {
-        const int b = tid + 256 * i;
-        const int d0 = 4 * (b % (D / 4)), key0 = 4 * (b / (D / 4));
-        floatx4 r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            r[e] = key0 + e < nval ? *reinterpret_cast<const floatx4*>(vin + (key0 + e) * row_stride + d0)
-                                   : floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            bf16x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (__bf16)r[e][c];
-            *reinterpret_cast<bf16x4*>(vts + (d0 + c) * kVts + key0) = x;
-        }
-    }
+    stage_v_rows<D>(vin, row_stride, nval, vts, tid);
     if constexpr (!PREP) {
-        // K: 16-byte chunks (8 dims) of each row, converted and written to their swizzled place
-#pragma unroll
-        for (int i = 0; i < kBN * NCH / 256; ++i) {
-            const int f = tid + 256 * i;
-            const int r = f / NCH, c = f % NCH;
-            floatx4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-            if (r < nval) {
-                const float* src = kin + r * row_stride + 8 * c;
-                a = *reinterpret_cast<const floatx4*>(src);
-                b = *reinterpret_cast<const floatx4*>(src + 4);
-            }
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = e < 4 ? a[e] : b[e - 4];
-            store_k_chunk(kt, r, c, x);
-        }
+        stage_k_rows<D, SPLIT>(kin, row_stride, nval, kt, tid);
     } else {
         // Fused entry: RMS-normalise and rotate each K row on its way in.  Four threads
         // per row take D/4 consecutive dims each.  A rotation partner (dim c +- n/2) sits
@@ -316,10 +333,55 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
                 *reinterpret_cast<floatx4*>(dst + i) = floatx4{y[i], y[i + 1], y[i + 2], y[i + 3]};
         }
 #pragma unroll
-        for (int cc = 0; cc < DQ / 8; ++cc) store_k_chunk(kt, r, c0 / 8 + cc, y + 8 * cc);
+        for (int cc = 0; cc < DQ / 8; ++cc) store_k_chunk<D, SPLIT>(kt, r, c0 / 8 + cc, y + 8 * cc);
     }
     __syncthreads();
     store_vt_rows<D>(vts, vt, tid);
+}
+
+// ---------------------------------------------------------------------------
+// Kept tiles (TileAppend): block = (K/V head, touched tile).  The tile's rows are
+// staged from the f32 cache as stage_kv_bf16_kernel stages them (rows past the
+// sequence's end are zeros), into the tile's place in its sequence slot; the blocks of
+// K/V head 0 also write the rotary-table rows of the tile's positions as
+// rope_table_kernel computes them.
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(256) void append_tiles_kernel(const float* __restrict__ k,
+                                                           const float* __restrict__ v,
+                                                           __bf16* __restrict__ tiles,
+                                                           TileAppend app, int Hkv) {
+    constexpr int KP = SPLIT ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) __bf16 vts[D * kVts];
+    const int tid = threadIdx.x;
+    const int kv = blockIdx.x % Hkv;
+    const int g = blockIdx.x / Hkv;
+    const int s = find_seq(app.cum, app.n_seqs, g);
+    const int lt = app.first[s] + (g - app.cum[s]);           // tile of the sequence
+    const int k0 = app.koff[s] + lt * kBN;                     // its first cache row
+    const int nval = min(kBN, app.koff[s + 1] - k0);
+    const int n_tiles = app.n_seqs * app.cap_tiles;
+    const int gt = s * app.cap_tiles + lt;
+    const int64_t row_stride = (int64_t)Hkv * D;
+    __bf16* kt = tiles + ((int64_t)kv * n_tiles + gt) * (KP * kBN * D);
+    __bf16* vt = tiles + (int64_t)Hkv * n_tiles * (KP * kBN * D) +
+                 ((int64_t)kv * n_tiles + gt) * (kBN * D);
+    stage_v_rows<D>(v + (int64_t)k0 * row_stride + kv * D, row_stride, nval, vts, tid);
+    stage_k_rows<D, SPLIT>(k + (int64_t)k0 * row_stride + kv * D, row_stride, nval, kt, tid);
+    __syncthreads();
+    store_vt_rows<D>(vts, vt, tid);
+    if (app.rope_dim > 0 && kv == 0) {
+        float2* tab = const_cast<float2*>(rope_table<D, SPLIT>(tiles, Hkv, n_tiles));
+        constexpr int RPP = 256 / (D / 2);  // positions per pass
+        const int j = tid % (D / 2);
+        const bool rot = 2 * j < app.rope_dim;
+        const double turns = rot ? rope_turns_per_pos(j, app.rope_dim, app.base) : 0.0;
+        for (int r = tid / (D / 2); r < nval; r += RPP) {
+            const int pos = lt * kBN + r;
+            float c = 1.0f, sn = 0.0f;
+            if (rot) rope_cos_sin(pos, turns, c, sn);
+            tab[(int64_t)pos * (D / 2) + j] = float2{c, sn};
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -949,7 +1011,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
                             const PrepParams* prep, bool prep_k, const Partials& part,
-                            int n_items, hipStream_t stream) {
+                            int n_items, hipStream_t stream, const TileAppend* app) {
     __bf16* w = static_cast<__bf16*>(ws);
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
     const bool merge = part.cnt != nullptr;  // in-place merge of split items
@@ -957,12 +1019,18 @@ hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, floa
     const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv),
         block(kThreads);
     const dim3 tgrid((unsigned)((sched.max_len + kTabRows - 1) / kTabRows)), tblock(256);
+    const dim3 agrid((unsigned)(app ? app->cum[app->n_seqs] * geom.Hkv : 0));
 #define PFA_LAUNCH_BF16(DD, SS, PP)                                                             \
     do {                                                                                        \
-        if (PP)                                                                                 \
+        if (app) {                                                                              \
+            if (app->cum[app->n_seqs] > 0)                                                      \
+                hipLaunchKernelGGL((append_tiles_kernel<DD, SS>), agrid, sblock, 0, stream, k,  \
+                                   v, w, *app, geom.Hkv);                                       \
+        } else if (PP)                                                                          \
             hipLaunchKernelGGL((rope_table_kernel<DD, SS>), tgrid, tblock, 0, stream, w,      \
                                geom.Hkv, sched.n_tiles, sched.max_len, p.rope_dim, p.base);    \
-        if (PP && prep_k)                                                                       \
+        if (app) {                                                                              \
+        } else if (PP && prep_k)                                                                \
             hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, true>), sgrid, sblock, 0, stream, \
                                k, v, w, sched, geom.Hkv, p);                                    \
         else                                                                                    \

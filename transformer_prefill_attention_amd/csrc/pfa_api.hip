@@ -360,7 +360,7 @@ const char* pfa_version(void) {
 }
 
 static size_t workspace_for(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
-                            int precision, bool prep_q, bool krot_in_ws) {
+                            int precision, bool prep_q, bool krot_in_ws, bool tiled = false) {
     if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) {
         fail(PFA_ERR_INVALID_ARG, "precision must be PFA_PREC_F32, PFA_PREC_BF16 or "
                                   "PFA_PREC_BF16X3 (got %d)", precision);
@@ -369,7 +369,7 @@ static size_t workspace_for(const pfa::SeqTable& st, int n_head, int n_head_kv, 
     Plan p;
     if (make_plan(st, n_head, n_head_kv, head_dim, 1.0f, 1, precision, p)) return 0;
     if (p.items == 0) return 0;
-    const size_t base = prep_part_bytes(p, precision != PFA_PREC_F32, prep_q, krot_in_ws);
+    const size_t base = tiled ? 0 : prep_part_bytes(p, precision != PFA_PREC_F32, prep_q, krot_in_ws);
     return p.part_bytes ? align256(base) + p.part_bytes : base;
 }
 
@@ -394,7 +394,34 @@ size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_off
     if (T_q == 0) return 0;
     pfa::SeqTable st;
     if (build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st)) return 0;
-    return workspace_for(st, n_head, n_head_kv, head_dim, precision, fused != 0, false);
+    if (fused == 2 && precision == PFA_PREC_F32) {
+        fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16 or "
+                                  "PFA_PREC_BF16X3");
+        return 0;
+    }
+    return workspace_for(st, n_head, n_head_kv, head_dim, precision, fused != 0, false,
+                         fused == 2);
+}
+
+size_t pfa_kv_tiles_bytes(int n_slots, int max_rows, int n_head_kv, int head_dim, int precision) {
+    g_err[0] = 0;
+    if (n_slots < 1 || n_slots > PFA_MAX_SEQS) {
+        fail(PFA_ERR_INVALID_ARG, "n_slots must be 1..%d (got %d)", PFA_MAX_SEQS, n_slots);
+        return 0;
+    }
+    if (max_rows < 1) {
+        fail(PFA_ERR_INVALID_ARG, "max_rows must be >= 1 (got %d)", max_rows);
+        return 0;
+    }
+    if (check_geometry(max_rows, n_head_kv, n_head_kv, head_dim)) return 0;
+    if (precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) {
+        fail(PFA_ERR_INVALID_ARG, "kv_tiles are for PFA_PREC_BF16 or PFA_PREC_BF16X3 (got %d)",
+             precision);
+        return 0;
+    }
+    const int cap = (max_rows + pfa::kBf16TileKeys - 1) / pfa::kBf16TileKeys;
+    return pfa::bf16_workspace_bytes(n_slots * cap, n_head_kv, head_dim,
+                                     precision == PFA_PREC_BF16X3, cap * pfa::kBf16TileKeys);
 }
 
 int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out,
@@ -428,8 +455,9 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
 
 // How an attention call gets its K: as given (plain prefill, or a cache for the
 // chunk entry), prepared from raw rows into k_rot_out / the workspace (fused
-// prefill), or prepared from the new rows into the caller's cache (fused chunk).
-enum class Mode { kPlain, kFused, kChunk, kChunkFused };
+// prefill), or prepared from the new rows into the caller's cache (fused chunk; the
+// tiled one also keeps the cache's bf16 tiles in the caller's kv_tiles across calls).
+enum class Mode { kPlain, kFused, kChunk, kChunkFused, kChunkTiled };
 
 static int check_attn(float scale, int precision) {
     if (!std::isfinite(scale)) return fail(PFA_ERR_INVALID_ARG, "scale must be finite");
@@ -461,12 +489,14 @@ static int plan_call(Mode mode, const pfa::SeqTable& st, int n_head, int n_head_
     if (rc) return rc;
     p.geom.window = window;
     const bool bf16 = precision != PFA_PREC_F32;
-    const bool prep = mode == Mode::kFused || mode == Mode::kChunkFused;
-    const bool chunk = mode == Mode::kChunk || mode == Mode::kChunkFused;
+    const bool tiled = mode == Mode::kChunkTiled;
+    const bool prep = mode == Mode::kFused || mode == Mode::kChunkFused || tiled;
+    const bool chunk = mode == Mode::kChunk || mode == Mode::kChunkFused || tiled;
     // workspace parts: [bf16 K/V tiles + rotary table (Q prepared in the kernel), or f32
-    // rotated K (fused prefill without k_rot_out)][partials, key split]
+    // rotated K (fused prefill without k_rot_out)][partials, key split]; the tiled chunk
+    // entry keeps its tiles and table in kv_tiles, so only the partials remain
     cp.krot_in_ws = mode == Mode::kFused && !bf16 && !has_k_rot_out;
-    cp.base = prep_part_bytes(p, bf16, prep, cp.krot_in_ws);
+    cp.base = tiled ? 0 : prep_part_bytes(p, bf16, prep, cp.krot_in_ws);
     cp.part_off = p.part_bytes ? align256(cp.base) : cp.base;
     if (!bf16 && p.part_bytes && ws_bytes < cp.part_off + p.part_bytes) {
         // f32 runs without the key split when the caller gives no (or too small a) workspace
@@ -485,10 +515,11 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
                        const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
                        float scale, int causal, int window, int precision,
                        const pfa::PrepParams* prep, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       void* stream, void* kv_tiles = nullptr, int cap_tiles = 0) {
     const int T_q = st.off[st.n_seqs], T_kv = st.koff[st.n_seqs];
     if (T_q == 0) return PFA_OK;
-    const bool chunk_fused = mode == Mode::kChunkFused;
+    const bool tiled = mode == Mode::kChunkTiled;
+    const bool chunk_fused = mode == Mode::kChunkFused || tiled;
     if (!q || !k || !v || !out || (chunk_fused && (!k_cache || !v_cache)))
         return fail(PFA_ERR_INVALID_ARG, "null tensor pointer");
     // bytes of Q / out, of the K and V the call reads, and of the caches
@@ -515,6 +546,27 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
         if (overlaps(k_cache, cb, v_cache, cb))
             return fail(PFA_ERR_INVALID_ARG, "k_cache and v_cache overlap");
     }
+    // the kept tiles (tiled chunk entry): slots of cap_tiles tiles, then the rotary table
+    const size_t tb = tiled ? pfa::bf16_workspace_bytes(st.n_seqs * cap_tiles, n_head_kv, head_dim,
+                                                        precision == PFA_PREC_BF16X3,
+                                                        cap_tiles * pfa::kBf16TileKeys)
+                            : 0;
+    if (tiled) {
+        if (!kv_tiles) return fail(PFA_ERR_INVALID_ARG, "null kv_tiles");
+        if (reinterpret_cast<uintptr_t>(kv_tiles) % 256)
+            return fail(PFA_ERR_INVALID_ARG, "kv_tiles must be 256-byte aligned");
+        for (int s = 0; s < st.n_seqs; ++s)
+            if (st.koff[s + 1] - st.koff[s] > cap_tiles * pfa::kBf16TileKeys)
+                return fail(PFA_ERR_INVALID_ARG,
+                            "sequence %d has %d cache rows, more than max_rows (%d, in tiles of "
+                            "%d)", s, st.koff[s + 1] - st.koff[s],
+                            cap_tiles * pfa::kBf16TileKeys, pfa::kBf16TileKeys);
+        const void* others[7] = {q, k, v, out, k_cache, v_cache, gate};
+        const size_t sizes[7] = {qb, kb, kb, qb, cb, cb, gate ? gb : 0};
+        for (int i = 0; i < 7; ++i)
+            if (others[i] && overlaps(kv_tiles, tb, others[i], sizes[i]))
+                return fail(PFA_ERR_INVALID_ARG, "kv_tiles must not overlap the other tensors");
+    }
     CallPlan cp;
     int rc;
     if ((rc = plan_call(mode, st, n_head, n_head_kv, head_dim, scale, causal, window, precision,
@@ -539,14 +591,17 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
             overlaps(workspace, need, v, kb) || overlaps(workspace, need, out, qb) ||
             (prep && prep->k_rot_out && overlaps(workspace, need, prep->k_rot_out, kb)) ||
             (chunk_fused &&
-             (overlaps(workspace, need, k_cache, cb) || overlaps(workspace, need, v_cache, cb))))
+             (overlaps(workspace, need, k_cache, cb) || overlaps(workspace, need, v_cache, cb))) ||
+            (tiled && overlaps(workspace, need, kv_tiles, tb)))
             return fail(PFA_ERR_INVALID_ARG, "workspace must not overlap the tensors");
     }
     const pfa::Partials part = p.partials(static_cast<char*>(workspace) + part_off);
     if ((rc = check_aligned({q, k, v, out, k_cache, v_cache, gate, prep ? prep->wq : nullptr,
                              prep ? prep->wk : nullptr, prep ? prep->k_rot_out : nullptr})))
         return rc;
-    const char* what = prep ? (chunk_fused ? "qk_prep_chunk_attn launch" : "qk_prep_attn launch")
+    const char* what = prep ? (tiled         ? "qk_prep_chunk_attn_tiled launch"
+                               : chunk_fused ? "qk_prep_chunk_attn launch"
+                                             : "qk_prep_attn launch")
                             : (mode == Mode::kChunk ? "gqa_chunk_attn launch"
                                                     : "gqa_prefill_attn launch");
     const float* k_attn = k;
@@ -562,6 +617,32 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
             return rc;
         k_attn = k_cache;
         v_attn = v_cache;
+    }
+    if (tiled) {
+        // the attention kernel reads sequence s's tiles from slot s of kv_tiles; the
+        // staging launch re-stages the tiles holding this call's new rows (the first
+        // of them may hold earlier rows too: they come from the cache like the rest)
+        pfa::TileAppend app{};
+        app.n_seqs = st.n_seqs;
+        app.cap_tiles = cap_tiles;
+        app.rope_dim = prep->rope_dim;
+        app.base = prep->base;
+        constexpr int TK = pfa::kBf16TileKeys;
+        for (int s = 0; s <= st.n_seqs; ++s) {
+            p.sched.tile_off[s] = s * cap_tiles;
+            app.koff[s] = st.koff[s];
+        }
+        p.sched.n_tiles = st.n_seqs * cap_tiles;
+        app.cum[0] = 0;
+        for (int s = 0; s < st.n_seqs; ++s) {
+            const int kv_len = st.koff[s + 1] - st.koff[s], n_new = st.off[s + 1] - st.off[s];
+            app.first[s] = (kv_len - n_new) / TK;
+            app.cum[s + 1] = app.cum[s] + (n_new > 0 ? (kv_len + TK - 1) / TK - app.first[s] : 0);
+        }
+        return hip_status(pfa::launch_attn_bf16(q, k_attn, v_attn, out, kv_tiles, p.sched, p.geom,
+                                                head_dim, precision == PFA_PREC_BF16X3, prep,
+                                                false, part, p.items, (hipStream_t)stream, &app),
+                          what);
     }
     if (bf16)
         return hip_status(pfa::launch_attn_bf16(q, k_attn, v_attn, out, workspace, p.sched, p.geom,
@@ -745,6 +826,36 @@ int qk_prep_chunk_attn(const float* q, const float* k, const float* v, float* ou
     return attn_common(Mode::kChunkFused, q, k, v, out, k_cache, v_cache, gate, gate_per_head,
                        st, n_head, n_head_kv, head_dim, scale, causal, window, precision, &prep,
                        workspace, workspace_bytes, stream);
+}
+
+int qk_prep_chunk_attn_tiled(const float* q, const float* k, const float* v, float* out,
+                             const float* gate, int gate_per_head, const float* q_norm_w,
+                             const float* k_norm_w, float* k_cache, float* v_cache,
+                             void* kv_tiles, int max_rows, const int32_t* q_offsets,
+                             const int32_t* kv_offsets, int n_seqs, int T_q, int T_kv,
+                             int n_head, int n_head_kv, int head_dim, int rope_dim,
+                             float rope_freq_base, float rms_eps, float scale, int causal,
+                             int window, int precision, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    g_err[0] = 0;
+    int rc = check_geometry(T_q, n_head, n_head_kv, head_dim);
+    if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
+    if ((rc = check_attn(scale, precision)) || (rc = check_window(window, causal))) return rc;
+    if (precision == PFA_PREC_F32)
+        return fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16 or "
+                                         "PFA_PREC_BF16X3 (the f32 mode reads the f32 cache: "
+                                         "qk_prep_chunk_attn)");
+    if ((rc = check_rope(head_dim, rope_dim, rope_freq_base, rms_eps))) return rc;
+    if (max_rows < 1) return fail(PFA_ERR_INVALID_ARG, "max_rows must be >= 1 (got %d)", max_rows);
+    pfa::SeqTable st;
+    if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) return rc;
+    if (T_q == 0) return PFA_OK;
+    if (!q_norm_w || !k_norm_w) return fail(PFA_ERR_INVALID_ARG, "null norm weights");
+    pfa::PrepParams prep{q_norm_w, k_norm_w, nullptr, rope_dim, rms_eps, (double)rope_freq_base};
+    const int cap_tiles = (max_rows + pfa::kBf16TileKeys - 1) / pfa::kBf16TileKeys;
+    return attn_common(Mode::kChunkTiled, q, k, v, out, k_cache, v_cache, gate, gate_per_head,
+                       st, n_head, n_head_kv, head_dim, scale, causal, window, precision, &prep,
+                       workspace, workspace_bytes, stream, kv_tiles, cap_tiles);
 }
 
 // ---------------------------------------------------------------------------
@@ -980,8 +1091,9 @@ void append(char* buf, size_t n, const char* fmt, ...) {
 void kernel_names(int entry, int precision, int D, int rope_dim, const Plan& p, char* buf,
                   size_t n) {
     buf[0] = 0;
+    const bool tiled = entry == PFA_ENTRY_CHUNK_TILED;
     const bool fused = entry == PFA_ENTRY_PREP || entry == PFA_ENTRY_CHUNK_PREP ||
-                       entry == PFA_ENTRY_Q8_PREP;
+                       entry == PFA_ENTRY_Q8_PREP || tiled;
     const bool split_keys = p.sched.max_chunks > 1;
     const char* merge = p.counters ? "true" : "false";  // split items merged in place
     const char* sep = "";
@@ -1000,8 +1112,14 @@ void kernel_names(int entry, int precision, int D, int rope_dim, const Plan& p, 
                p.sched.paired ? "true" : "false", merge);
     } else {
         const char* sp = precision == PFA_PREC_BF16X3 ? "true" : "false";
-        if (entry == PFA_ENTRY_CHUNK_PREP) {
+        if (entry == PFA_ENTRY_CHUNK_PREP || tiled) {
             append(buf, n, "qknorm_rope_kernel<%d,%d,false> + ", D, qknorm_mode(D, rope_dim));
+        }
+        if (tiled) {
+            append(buf, n, "append_tiles_kernel<%d,%s> + attn_bf16_kernel<%d,%s,true,false,%s>", D,
+                   sp, D, sp, merge);
+            if (split_keys && !p.counters) append(buf, n, " + attn_combine_kernel<%d>", D);
+            return;
         }
         if (fused) append(buf, n, "rope_table_kernel<%d,%s> + ", D, sp);
         append(buf, n, "stage_kv_bf16_kernel<%d,%s,%s> + attn_bf16_kernel<%d,%s,%s,false,%s>", D,
@@ -1017,12 +1135,16 @@ int plan_query(int entry, const int32_t* q_offsets, const int32_t* kv_offsets, i
                int causal, int window, int precision, int has_k_rot_out, size_t ws_bytes,
                CallPlan& cp, pfa::SeqTable& st, size_t& need) {
     int rc;
-    if (entry < PFA_ENTRY_PREFILL || entry > PFA_ENTRY_Q8_PREP)
+    if (entry < PFA_ENTRY_PREFILL || entry > PFA_ENTRY_CHUNK_TILED)
         return fail(PFA_ERR_INVALID_ARG, "unknown entry %d", entry);
+    const bool tiled = entry == PFA_ENTRY_CHUNK_TILED;
+    if (tiled && precision == PFA_PREC_F32)
+        return fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16 or "
+                                         "PFA_PREC_BF16X3");
     const bool prefill = entry == PFA_ENTRY_PREFILL || entry == PFA_ENTRY_PREP;
     const bool q8 = entry == PFA_ENTRY_Q8 || entry == PFA_ENTRY_Q8_PREP;
     const bool fused = entry == PFA_ENTRY_PREP || entry == PFA_ENTRY_CHUNK_PREP ||
-                       entry == PFA_ENTRY_Q8_PREP;
+                       entry == PFA_ENTRY_Q8_PREP || tiled;
     if (prefill) T_kv = T_q;
     if ((rc = check_geometry(T_q, n_head, n_head_kv, head_dim)) ||
         (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim)))
@@ -1037,8 +1159,12 @@ int plan_query(int entry, const int32_t* q_offsets, const int32_t* kv_offsets, i
     } else if ((rc = build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st))) {
         return rc;
     }
-    static const Mode modes[4] = {Mode::kPlain, Mode::kFused, Mode::kChunk, Mode::kChunkFused};
-    const Mode mode = q8 ? Mode::kChunk : modes[entry];
+    const Mode mode = q8                                  ? Mode::kChunk
+                      : tiled                             ? Mode::kChunkTiled
+                      : entry == PFA_ENTRY_PREFILL        ? Mode::kPlain
+                      : entry == PFA_ENTRY_PREP           ? Mode::kFused
+                      : entry == PFA_ENTRY_CHUNK          ? Mode::kChunk
+                                                          : Mode::kChunkFused;
     if ((rc = plan_call(mode, st, n_head, n_head_kv, head_dim, 1.0f, causal, window, precision,
                         has_k_rot_out != 0, ws_bytes, cp)))
         return rc;

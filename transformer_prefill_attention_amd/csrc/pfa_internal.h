@@ -191,13 +191,29 @@ inline size_t bf16_workspace_bytes(int n_tiles, int Hkv, int D, bool split_qk, i
     return (size_t)n_tiles * Hkv * (split_qk ? 3 : 2) * kBf16TileKeys * D * 2 +
            (size_t)rope_rows * (D / 2) * 8;
 }
+// Tiles kept across chunk calls (qk_prep_chunk_attn_tiled): sequence s owns the
+// cap_tiles tiles of slot s (tile s * cap_tiles + j holds its cache rows 64 j ..), and a
+// call re-stages only the tiles its new rows touch, from the f32 cache, together with
+// the rotary-table rows of their positions (the table, indexed by position, follows the
+// tiles: cap_tiles * 64 rows).  Passed by value to the staging launch.
+struct TileAppend {
+    int n_seqs;
+    int cap_tiles;                 // tiles per sequence slot
+    int cum[PFA_MAX_SEQS + 1];     // touched tiles of the sequences before s
+    int first[PFA_MAX_SEQS];       // first touched tile of sequence s (slot-local)
+    int koff[PFA_MAX_SEQS + 1];    // f32 cache rows of sequence s: koff[s] .. koff[s+1]-1
+    int rope_dim;                  // rotated dims of the table rows (0: no table)
+    double base;                   // rotary frequency base
+};
 // prep != nullptr: a fused entry (Q normalised and rotated inside the attention
 // kernel; K too, on its way into the tiles, when prep_k -- over a cached prefix
-// the cache already holds rotated keys).
+// the cache already holds rotated keys).  app != nullptr: ws is the caller's kept
+// tiles (sched.tile_off / n_tiles describe its slots); only the touched tiles are
+// staged and no rotary-table launch is needed.
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
                             const PrepParams* prep, bool prep_k, const Partials& part,
-                            int n_items, hipStream_t stream);
+                            int n_items, hipStream_t stream, const TileAppend* app = nullptr);
 
 // Attention through an 8-bit store, on the bf16 kernel's schedule: the scores are the
 // integer dot products of the codes (v_mfma_i32_32x32x32_i8 on int8 K tiles for

@@ -31,10 +31,12 @@ EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_workspace_byt
            "gqa_chunk_attn", "qk_prep_chunk_attn", "pfa_chunk_workspace_bytes",
            "pfa_quantize_rows", "gqa_attn_q8", "qk_prep_attn_q8", "pfa_q8_workspace_bytes",
            "pfa_attn_plan", "pfa_attn_units", "gqa_prefill_attn_noalloc",
-           "pfa_noalloc_scratch_bytes", "pfa_last_error", "pfa_version")
+           "pfa_noalloc_scratch_bytes", "qk_prep_chunk_attn_tiled", "pfa_kv_tiles_bytes",
+           "pfa_last_error", "pfa_version")
 
 # pfa_entry values of the plan report
-ENTRY_PREFILL, ENTRY_PREP, ENTRY_CHUNK, ENTRY_CHUNK_PREP, ENTRY_Q8, ENTRY_Q8_PREP = range(6)
+(ENTRY_PREFILL, ENTRY_PREP, ENTRY_CHUNK, ENTRY_CHUNK_PREP, ENTRY_Q8, ENTRY_Q8_PREP,
+ ENTRY_CHUNK_TILED) = range(7)
 UNIT_FIELDS = ("workgroup", "pass", "item", "sequence", "super_block", "key_chunk", "kv_head",
                "head_chunk", "tile_begin", "tile_end")
 
@@ -95,6 +97,12 @@ def lib() -> ctypes.CDLL:
     L.qk_prep_chunk_attn.restype = i32
     L.pfa_chunk_workspace_bytes.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
     L.pfa_chunk_workspace_bytes.restype = sz
+    L.qk_prep_chunk_attn_tiled.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp,
+                                           vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32,
+                                           i32, i32, i32, vp, sz, vp]
+    L.qk_prep_chunk_attn_tiled.restype = i32
+    L.pfa_kv_tiles_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.pfa_kv_tiles_bytes.restype = sz
     L.pfa_last_error.restype = ctypes.c_char_p
     i64 = ctypes.c_int64
     L.pfa_quantize_rows.argtypes = [vp, i64, i32, vp, vp, vp, vp]
@@ -347,12 +355,22 @@ def _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv):
 
 def chunk_workspace_bytes(T_q: int, T_kv: int, n_head: int, n_head_kv: int, head_dim: int,
                           precision="f32", q_offsets=None, kv_offsets=None,
-                          fused: bool = False) -> int:
-    """Device workspace ``gqa_chunk_attn`` (``fused=False``) or ``qk_prep_chunk_attn``
-    (``fused=True``) uses for these arguments (``pfa_chunk_workspace_bytes``)."""
+                          fused=False) -> int:
+    """Device workspace ``gqa_chunk_attn`` (``fused=False``), ``qk_prep_chunk_attn``
+    (``fused=True``) or ``qk_prep_chunk_attn_tiled`` (``fused=2``) uses for these
+    arguments (``pfa_chunk_workspace_bytes``)."""
     keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
     return int(lib().pfa_chunk_workspace_bytes(qp, kp, n_seqs, T_q, T_kv, n_head, n_head_kv,
-                                               head_dim, _prec(precision), 1 if fused else 0))
+                                               head_dim, _prec(precision), _fused_code(fused)))
+
+
+def _fused_code(fused):
+    """The size queries' ``fused`` argument: 0, 1, or 2 (the tiled chunk entry)."""
+    if fused is True or fused is False:
+        return int(fused)
+    if fused in (0, 1, 2):
+        return int(fused)
+    raise ValueError(f"fused must be False, True or 2 (got {fused!r})")
 
 
 def _gate(gate, T_q, H, head_dim):
@@ -371,7 +389,7 @@ def _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, pre
                      device):
     import torch
     need = int(lib().pfa_chunk_workspace_bytes(qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim,
-                                               prec, 1 if fused else 0))
+                                               prec, _fused_code(fused)))
     if need == 0:
         return None, ctypes.c_void_p(0), 0
     if workspace is None:
@@ -445,6 +463,60 @@ def qk_prep_chunk_attn(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, *, head_di
                                     T_q, T_kv, H, Hkv, head_dim, rope_dim, float(rope_freq_base),
                                     float(rms_eps), float(scale), 1 if causal else 0,
                                     int(window), prec, wp, wn, _stream(q)))
+    return out
+
+
+def kv_tiles_bytes(n_slots: int, max_rows: int, n_head_kv: int, head_dim: int,
+                   precision="bf16") -> int:
+    """Bytes of the kept tiles of ``qk_prep_chunk_attn_tiled`` (``pfa_kv_tiles_bytes``)."""
+    n = int(lib().pfa_kv_tiles_bytes(int(n_slots), int(max_rows), n_head_kv, head_dim,
+                                     _prec(precision)))
+    if n == 0:
+        raise PfaError(-1, lib().pfa_last_error().decode())
+    return n
+
+
+def qk_prep_chunk_attn_tiled(q, k, v, q_norm_w, k_norm_w, k_cache, v_cache, kv_tiles, *,
+                             max_rows: int, head_dim: int, rope_dim: int,
+                             rope_freq_base: float, rms_eps: float, scale: float,
+                             causal: bool = True, window: int = 0, gate=None,
+                             precision="bf16", q_offsets=None, kv_offsets=None, out=None,
+                             workspace=None):
+    """``qk_prep_chunk_attn`` in the bf16 modes with the cache's bf16 tiles kept in
+    ``kv_tiles`` across calls (``qk_prep_chunk_attn_tiled`` in ``include/pfa.h``): a GPU
+    tensor of at least :func:`kv_tiles_bytes` bytes, passed to every call on the same
+    cache with the same sequence count, ``max_rows`` and head geometry; returns ``out``."""
+    import torch
+    _norm_weights(q_norm_w, k_norm_w, head_dim)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev_f32(t, n)
+    if not isinstance(kv_tiles, torch.Tensor) or kv_tiles.device.type != "cuda":
+        raise TypeError("kv_tiles must be a GPU torch.Tensor")
+    T_q, H = _heads(q, head_dim, "q")
+    Tk, Hkv = _heads(k, head_dim, "k")
+    if Tk != T_q or v.shape != k.shape:
+        raise ValueError("q, k, v must have the same token count and k, v the same shape")
+    T_kv, Hc = _heads(k_cache, head_dim, "k_cache")
+    if Hc != Hkv or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [T_kv, n_head_kv*head_dim] like k")
+    out = torch.empty_like(q) if out is None else _dev_f32(out, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must have q's shape")
+    keep, n_seqs, qp, kp = _chunk_offsets(q_offsets, kv_offsets, T_q, T_kv)
+    prec = _prec(precision)
+    need = kv_tiles_bytes(max(n_seqs, 1), max_rows, Hkv, head_dim, precision)
+    if kv_tiles.numel() * kv_tiles.element_size() < need:
+        raise ValueError(f"kv_tiles holds {kv_tiles.numel() * kv_tiles.element_size()} bytes, "
+                         f"{need} needed")
+    ws, wp, wn = _chunk_workspace(workspace, qp, kp, n_seqs, T_q, T_kv, H, Hkv, head_dim, prec,
+                                  2, q.device)
+    gp, gh = _gate(gate, T_q, H, head_dim)
+    _check(lib().qk_prep_chunk_attn_tiled(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), gp, gh, _ptr(q_norm_w), _ptr(k_norm_w),
+        _ptr(k_cache), _ptr(v_cache), ctypes.c_void_p(kv_tiles.data_ptr()), int(max_rows), qp, kp,
+        n_seqs, T_q, T_kv, H, Hkv, head_dim, rope_dim, float(rope_freq_base), float(rms_eps),
+        float(scale), 1 if causal else 0, int(window), prec, wp, wn, _stream(q)))
     return out
 
 
@@ -586,7 +658,7 @@ def qk_prep_attn_q8(q, k, v, q_norm_w, k_norm_w, k_cache, k_scale, v_cache, v_sc
 
 def _plan_args(entry, T_q, n_head, n_head_kv, head_dim, rope_dim, T_kv, causal, window,
                precision, q_offsets, kv_offsets, has_k_rot_out, workspace_bytes):
-    if entry not in (ENTRY_CHUNK, ENTRY_CHUNK_PREP, ENTRY_Q8, ENTRY_Q8_PREP):
+    if entry not in (ENTRY_CHUNK, ENTRY_CHUNK_PREP, ENTRY_Q8, ENTRY_Q8_PREP, ENTRY_CHUNK_TILED):
         # the prefill entries (an unknown entry is left to the library to reject)
         keep, n_seqs, qp = _offsets(q_offsets, T_q)
         kp, T_kv = None, T_q
