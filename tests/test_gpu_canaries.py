@@ -182,6 +182,37 @@ def test_chunk_entry_points_write_only_their_outputs(case, precision):
 
 
 @pytest.mark.parametrize("case", CHUNK, ids=[c[0] for c in CHUNK])
+@pytest.mark.parametrize("precision", ["bf16", "bf16x3"])
+def test_tiled_chunk_entry_writes_only_its_outputs(case, precision):
+    """qk_prep_chunk_attn_tiled: writes out, the new rows of the caches and the tiles of
+    kv_tiles; nothing outside them (kv_tiles, sized for more rows than the call needs,
+    sits between sentinel bands like the rest)."""
+    name, lens, bases, H, Hkv, d, n, window = case
+    w, x, q_offs, kv_offs, new = _chunk_inputs(case)
+    T_q, T_kv = int(q_offs[-1]), int(kv_offs[-1])
+    offs = dict(q_offsets=q_offs, kv_offsets=kv_offs)
+    max_rows = max(b + m for b, m in zip(bases, lens)) + 100
+    n_tiles = pfa.kv_tiles_bytes(len(lens), max_rows, Hkv, d, precision)
+    g = Guarded()
+    q, k, v = g.input("q", x.q[new]), g.input("k", x.k[new]), g.input("v", x.v[new])
+    wq, wk = g.input("wq", x.wq), g.input("wk", x.wk)
+    kc = g.alloc("k_cache", x.k.shape, torch.float32, torch.from_numpy(x.k))
+    vc = g.alloc("v_cache", x.v.shape, torch.float32, torch.from_numpy(x.v))
+    tiles = g.alloc("kv_tiles", (n_tiles,), torch.uint8, torch.zeros(n_tiles, dtype=torch.uint8))
+    out = g.alloc("out", (T_q, H * d), torch.float32)
+    ws = g.workspace(pfa.chunk_workspace_bytes(T_q, T_kv, H, Hkv, d, precision, fused=2, **offs))
+    pfa.qk_prep_chunk_attn_tiled(q, k, v, wq, wk, kc, vc, tiles, max_rows=max_rows, head_dim=d,
+                                 rope_dim=n, rope_freq_base=w.rope_freq_base, rms_eps=w.rms_eps,
+                                 scale=w.softmax_scale, window=window, precision=precision,
+                                 out=out, workspace=ws, **offs)
+    g.check(f"qk_prep_chunk_attn_tiled {name} {precision}",
+            [("out", out), ("k_cache", kc), ("v_cache", vc)])
+    keep = np.ones(T_kv, dtype=bool)
+    keep[new] = False
+    assert torch.equal(kc.cpu()[torch.from_numpy(keep)], torch.from_numpy(x.k[keep]))
+
+
+@pytest.mark.parametrize("case", CHUNK, ids=[c[0] for c in CHUNK])
 def test_8bit_entry_points_write_only_their_outputs(case):
     name, lens, bases, H, Hkv, d, n, window = case
     w, x, q_offs, kv_offs, new = _chunk_inputs(case, seed=1800)

@@ -100,8 +100,11 @@ __device__ __forceinline__ double rope_turns_per_pos(int j, int n, double base) 
 // cos and sin of the rotary angle pos * base^(-2j/n).  The angle is formed in
 // f64 as a number of turns and reduced to [-1/2, 1/2] turn there, so only the
 // final sincos runs in f32 on an argument of at most pi: the result keeps f32
-// accuracy at any position (an f32 angle would lose ~1e-3 rad near 16k).
+// accuracy at any position (an f32 angle would lose ~1e-3 rad near 16k).  No
+// multiply-add contraction (here and in norm_rope_row): every kernel that inlines
+// them rounds the same operations, so they agree bit for bit.
 __device__ __forceinline__ void rope_cos_sin(int pos, double turns_per_pos, float& c, float& s) {
+#pragma clang fp contract(off)
     double r = (double)pos * turns_per_pos;
     r -= rint(r);
     sincospif((float)(2.0 * r), &s, &c);
@@ -212,6 +215,98 @@ __host__ __device__ __forceinline__ KeyRange item_key_range(const Sched& sched, 
     r.t_begin = r.t_first + wi.kc * kchunk;
     r.t_end = r.t_begin + kchunk < r.n_tiles ? r.t_begin + kchunk : r.n_tiles;
     return r;
+}
+
+// ---------------------------------------------------------------------------
+// QK-norm + NeoX RoPE of one head row held by one wavefront, lane L holding dims L + 64 e
+// (e < D / 64): the arithmetic of qknorm_rope_kernel, shared with the kernels that prepare
+// K rows on their way into the bf16 tiles, so that both give the same bits.
+//
+// Rotary pair (j, j + n/2): with n == D == 128 both dims of a pair sit in the same lane;
+// with n == 64 the partner is lane L ^ 32; any other even n takes a general shuffle.
+enum PairMode { kPairInLane = 0, kPairXor32 = 1, kPairGeneral = 2 };
+
+// Per-lane rotary constants: which pair each of the lane's dims belongs to.
+template <int D>
+struct RopeLane {
+    double turns[D / 64];  // turns per position of the pair (0: not rotated)
+    float sgn[D / 64];     // -1 for the first dim of a pair, +1 for the second
+    int src[D / 64], slot[D / 64];  // the partner dim's lane and register
+    bool rot[D / 64];
+};
+template <int D>
+__device__ __forceinline__ RopeLane<D> rope_lane(int lane, int n, double base) {
+    RopeLane<D> L;
+    const int half = n >> 1;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) {
+        const int c = lane + 64 * e;
+        L.rot[e] = c < n;
+        const bool first = c < half;
+        const int j = first ? c : c - half;
+        const int p = first ? c + half : c - half;
+        L.sgn[e] = first ? -1.0f : 1.0f;
+        L.src[e] = p & 63;
+        L.slot[e] = p >> 6;
+        L.turns[e] = L.rot[e] ? rope_turns_per_pos(j, n, base) : 0.0;
+    }
+    return L;
+}
+// cos / sin of the lane's dims at position pos.
+template <int D>
+__device__ __forceinline__ void rope_lane_angles(const RopeLane<D>& L, int pos, float* cs,
+                                                 float* sn) {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) {
+        if (L.rot[e]) {
+            rope_cos_sin(pos, L.turns[e], cs[e], sn[e]);
+        } else {
+            cs[e] = 1.0f;
+            sn[e] = 0.0f;
+        }
+    }
+}
+// o = RoPE(x * w / rms(x)) of one row (x, o: the lane's dims; wv: the lane's weights).
+template <int D, int MODE>
+__device__ __forceinline__ void norm_rope_row(const float* x, const float* wv, const float* cs,
+                                              const float* sn, const RopeLane<D>& L, float eps,
+                                              float* o) {
+#pragma clang fp contract(off)
+    constexpr int E = D / 64;
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss += x[e] * x[e];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = x[e] * r * wv[e];
+    if (MODE == kPairInLane) {
+        // n == D == 128: dims L and L + 64 are the two halves of pair L.
+        o[0] = y[0] * cs[0] - y[E - 1] * sn[0];
+        o[E - 1] = y[E - 1] * cs[0] + y[0] * sn[0];
+    } else if (MODE == kPairXor32) {
+        // n == 64: the partner of dim L (< 64) is dim L ^ 32, in lane L ^ 32.
+        const float pv = __shfl_xor(y[0], 32, 64);
+        o[0] = y[0] * cs[0] + L.sgn[0] * pv * sn[0];
+#pragma unroll
+        for (int e = 1; e < E; ++e) o[e] = y[e];
+    } else {
+        float pv[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float best = 0.0f;
+#pragma unroll
+            for (int sl = 0; sl < E; ++sl) {
+                const float cand = __shfl(y[sl], L.src[e], 64);
+                if (L.slot[e] == sl) best = cand;
+            }
+            pv[e] = best;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            o[e] = L.rot[e] ? y[e] * cs[e] + L.sgn[e] * pv[e] * sn[e] : y[e];
+    }
 }
 
 // ---------------------------------------------------------------------------

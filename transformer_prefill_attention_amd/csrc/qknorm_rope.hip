@@ -33,8 +33,6 @@ namespace pfa {
 
 namespace {
 
-enum PairMode { kPairInLane = 0, kPairXor32 = 1, kPairGeneral = 2 };
-
 constexpr int kRowsInFlight = 4;  // head rows loaded before the first is reduced
 
 template <int D, int MODE, bool Q8>
@@ -45,26 +43,14 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     int Hkv, int n, double base, float eps, int groups, Q8Rows q8) {
     constexpr int E = D / 64;  // dims per lane
     const int lane = threadIdx.x & 63;
-    const int half = n >> 1;
 
-    // Per-lane constants: which rotary pair each of this lane's dims belongs to.
-    double turns[E];
-    float sgn[E], wqv[E], wkv[E];
-    int src[E], slot[E];
-    bool rot[E];
+    // Per-lane constants: which rotary pair each of this lane's dims belongs to, weights.
+    const RopeLane<D> rl = rope_lane<D>(lane, n, base);
+    float wqv[E], wkv[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const int c = lane + 64 * e;
-        rot[e] = c < n;
-        const bool first = c < half;
-        const int j = first ? c : c - half;
-        const int p = first ? c + half : c - half;
-        sgn[e] = first ? -1.0f : 1.0f;
-        src[e] = p & 63;
-        slot[e] = p >> 6;
-        turns[e] = rot[e] ? rope_turns_per_pos(j, n, base) : 0.0;
-        wqv[e] = wq[c];
-        wkv[e] = wk[c];
+        wqv[e] = wq[lane + 64 * e];
+        wkv[e] = wk[lane + 64 * e];
     }
 
     const int waves = gridDim.x * (blockDim.x >> 6);
@@ -76,15 +62,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
         const int pos = (k_end - seqs.koff[s]) - (q_end - t);  // base_s + t - off[s]
         const int krow = t + k_end - q_end;                    // the K / V row it fills
         float cs[E], sn[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if (rot[e]) {
-                rope_cos_sin(pos, turns[e], cs[e], sn[e]);
-            } else {
-                cs[e] = 1.0f;
-                sn[e] = 0.0f;
-            }
-        }
+        rope_lane_angles<D>(rl, pos, cs, sn);
 
         // a finished row: f32 out, or (Q8) codes and the row's scale
         auto store_row = [&](const float* o, float* out, int8_t* c8, float* s8) {
@@ -115,40 +93,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
 #pragma unroll
                 for (int u = 0; u < kRowsInFlight; ++u) {
                     if (h0 + u >= nrows) break;
-                    float ss = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) ss += x[u][e] * x[u][e];
-                    ss = wave_sum(ss);
-                    const float r = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-                    float y[E], o[E];
-#pragma unroll
-                    for (int e = 0; e < E; ++e) y[e] = x[u][e] * r * wv[e];
-                    if (MODE == kPairInLane) {
-                        // n == D == 128: dims L and L + 64 are the two halves of pair L.
-                        o[0] = y[0] * cs[0] - y[E - 1] * sn[0];
-                        o[E - 1] = y[E - 1] * cs[0] + y[0] * sn[0];
-                    } else if (MODE == kPairXor32) {
-                        // n == 64: the partner of dim L (< 64) is dim L ^ 32, in lane L ^ 32.
-                        const float pv = __shfl_xor(y[0], 32, 64);
-                        o[0] = y[0] * cs[0] + sgn[0] * pv * sn[0];
-#pragma unroll
-                        for (int e = 1; e < E; ++e) o[e] = y[e];
-                    } else {
-                        float pv[E];
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            float best = 0.0f;
-#pragma unroll
-                            for (int sl = 0; sl < E; ++sl) {
-                                const float cand = __shfl(y[sl], src[e], 64);
-                                if (slot[e] == sl) best = cand;
-                            }
-                            pv[e] = best;
-                        }
-#pragma unroll
-                        for (int e = 0; e < E; ++e)
-                            o[e] = rot[e] ? y[e] * cs[e] + sgn[e] * pv[e] * sn[e] : y[e];
-                    }
+                    float o[E];
+                    norm_rope_row<D, MODE>(x[u], wv, cs, sn, rl, eps, o);
                     store_row(o, Q8 ? nullptr : out + (h0 + u) * D,
                               Q8 ? c8 + (h0 + u) * D : nullptr, Q8 ? s8 + h0 + u : nullptr);
                 }
