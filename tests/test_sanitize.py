@@ -4,12 +4,12 @@
   schedule, workspace layouts and the plan report -- built with host-only ASan + UBSan
   (``build.py --sanitize``) and driven by ``tests/sanitize/abi_driver.cpp``: rejected
   calls of every entry point and size / plan / unit queries over 300 random tables of up
-  to 128 sequences, with every host array allocated at its exact size.  The driver only
+  to 128 sequences, with every host array allocated at its exact size.  That program only
   makes calls that return before anything is enqueued, so it never launches a kernel.
 * The oracle (``oracle/oracle.c``) built with ASan + UBSan and driven by
   ``tests/sanitize/oracle_driver.c`` over small packed inputs of every entry point.
 
-Any sanitizer report aborts its driver, which fails the test.
+Any sanitizer report aborts the program, which fails the test.
 """
 import os
 import shutil
