@@ -394,8 +394,9 @@ def measure_bars(pfa, wl, w_main, x_main, args):
     """The other bars of the metric in the same run: bf16 at T = 8192 (the call, and its
     attention kernel alone), the 0.6B-like shape (T = 512, 16/8 heads) in f32 and bf16,
     and the long shape (T = 16384) in f32.  Each is the attention call alone, timed with
-    HIP events on its launch stream (20 runs after 5 warmup runs); f32 and bf16 fractions
-    against their own MFMA peaks."""
+    HIP events on its launch stream (20 runs after 5 warmup runs); TFLOP/s and the fraction
+    of its own MFMA peak at the median run (a mean of 20 can carry one host stall of the
+    process; the mean is reported beside it)."""
     import numpy as np
     import torch
     dev = torch.device("cuda:0")
@@ -422,8 +423,8 @@ def measure_bars(pfa, wl, w_main, x_main, args):
                "precision": prec, "path": path,
                "kernel": prefill_kernels(pfa, w, prec, path),
                "call_ms": round(mean, 4), "call_ms_median": round(med, 4),
-               "tflops": round(flops / (mean * 1e-3) / 1e12, 3),
-               "frac": round(flops / (mean * 1e-3) / 1e12 / peak, 4), "peak": peak}
+               "tflops": round(flops / (med * 1e-3) / 1e12, 3),
+               "frac": round(flops / (med * 1e-3) / 1e12 / peak, 4), "peak": peak}
         if per_kernel is not None:
             bar["per_kernel"] = per_kernel
             attn = [v for k, v in per_kernel.items() if isinstance(v, dict) and
