@@ -240,7 +240,6 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
                                                             AttnSched sched, int Hkv,
                                                             PrepParams prep) {
     constexpr int KP = SPLIT ? 2 : 1;
-    constexpr int NCH = D / 8;
     constexpr int KRS = D + 4;    // raw K row stride in LDS (f32), fused entry only
     __shared__ __attribute__((aligned(16))) __bf16 vts[D * kVts];
     __shared__ __attribute__((aligned(16))) float kraw[PREP ? kBN * KRS : 4];
