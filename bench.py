@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "causal GQA prefill attention TFLOP/s (and % of MFMA peak) at T=512..16384"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "bf16x3": 2500.0,
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "bf16x3": 2500.0, "f16": 2500.0,
                "int8": 5000.0}   # MI355X dense MFMA peaks (int8: TOP/s)
 HBM_PEAK_GBS = 8000.0
 
@@ -161,7 +161,7 @@ def main():
     ap.add_argument("--workload", default="prefill_8192")
     ap.add_argument("--seq-len", type=int, default=0, help="override: one sequence of this length "
                                                            "with the 8B-like heads")
-    ap.add_argument("--precision", default="f32", choices=["f32", "bf16", "bf16x3"])
+    ap.add_argument("--precision", default="f32", choices=["f32", "bf16", "bf16x3", "f16"])
     ap.add_argument("--path", default="unfused", choices=["fused", "unfused", "tiled"],
                     help="unfused (default, currently the faster): qknorm_rope then "
                          "gqa_prefill_attn; fused: the single qk_prep_attn call; tiled (with "
@@ -391,9 +391,10 @@ def time_prefill_call(pfa, w, t, precision, path, runs, warmup, profile=False):
 
 
 def measure_bars(pfa, wl, w_main, x_main, args):
-    """The other bars of the metric in the same run: bf16 at T = 8192 (the call, and its
-    attention kernel alone), the 0.6B-like shape (T = 512, 16/8 heads) in f32 and bf16,
-    and the long shape (T = 16384) in f32.  Each is the attention call alone, timed with
+    """The other bars of the metric in the same run: bf16 and f16 at T = 8192 (the call,
+    and its attention kernel alone), the 0.6B-like shape (T = 512, 16/8 heads) in f32 and
+    bf16, and the long shape (T = 16384, keys with large norms) in f32 and f16.  Each is
+    the attention call alone, timed with
     HIP events on its launch stream (20 runs after 5 warmup runs); TFLOP/s and the fraction
     of its own MFMA peak at the median run (a mean of 20 can carry one host stall of the
     process; the mean is reported beside it)."""
@@ -402,8 +403,9 @@ def measure_bars(pfa, wl, w_main, x_main, args):
     dev = torch.device("cuda:0")
     bars = []
     specs = [("prefill_8192", "bf16", "unfused", True), ("prefill_8192", "bf16", "fused", True),
+             ("prefill_8192", "f16", "unfused", True),
              ("qwen3_0p6b", "f32", "unfused", False), ("qwen3_0p6b", "bf16", "unfused", False),
-             ("long", "f32", "unfused", False)]
+             ("long", "f32", "unfused", False), ("long", "f16", "unfused", False)]
     cache = {}
     for name, prec, path, prof in specs:
         w = wl.CONFIGS[name]

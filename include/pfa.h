@@ -56,21 +56,33 @@ typedef enum {
 
 /* Input type of the two matrix products inside attention.  Accumulation,
  * softmax and the output are f32 in every case (the inputs and output stay f32
- * tensors; the bf16 modes convert K and V once into the workspace).
+ * tensors; the 16-bit modes convert K and V once into the workspace).
  *  PFA_PREC_F32    f32 products.
  *  PFA_PREC_BF16   the (scaled) Q, K, V and the softmax weights are rounded to
  *                  bf16 (round to nearest even) before each product.
  *  PFA_PREC_BF16X3 as PFA_PREC_BF16 for P.V; the scores use Q and K each split
  *                  into a bf16 high part plus a bf16 low part (three products),
  *                  which keeps the score error from growing with large key norms.
- * Both attention entry points take every mode. */
-typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_precision;
+ *  PFA_PREC_F16    as PFA_PREC_BF16 with IEEE binary16 in place of bf16 (round to
+ *                  nearest even; 11 significant bits against 8, so about 8 times
+ *                  less rounding, at the same matrix-core rate).  Its range is
+ *                  narrower: a scaled Q, K or V value beyond 65504 in magnitude
+ *                  becomes infinite and the rows it reaches come out NaN (the
+ *                  softmax weights stay <= 256 and cannot overflow).
+ * Every attention entry point takes every mode (qk_prep_chunk_attn_tiled all but
+ * PFA_PREC_F32). */
+typedef enum {
+    PFA_PREC_F32 = 0,
+    PFA_PREC_BF16 = 1,
+    PFA_PREC_BF16X3 = 2,
+    PFA_PREC_F16 = 3
+} pfa_precision;
 
 /* Device workspace in bytes that gqa_prefill_attn (fused = 0) or qk_prep_attn
  * (fused = 1) uses for these arguments (the same seq_offsets, n_seqs, T, heads,
  * head_dim and precision as the call).  It holds, in this order:
- *  - bf16 modes: K and V converted once to bf16 in 64-key tiles per sequence (K
- *    twice, high and low parts, for PFA_PREC_BF16X3),
+ *  - 16-bit modes: K and V converted once to bf16 (f16 for PFA_PREC_F16) in 64-key
+ *    tiles per sequence (K twice, high and low parts, for PFA_PREC_BF16X3),
  *      n_head_kv * sum_s ceil(len_s / 64) * 64 * head_dim * 2 * (2 or 3) bytes,
  *    then, for qk_prep_attn, a rotary table of max_s(len_s) * (head_dim / 2) * 8
  *    bytes;
@@ -79,8 +91,8 @@ typedef enum { PFA_PREC_F32 = 0, PFA_PREC_BF16 = 1, PFA_PREC_BF16X3 = 2 } pfa_pr
  *  - any precision, short inputs only, at the next multiple of 256 bytes: when
  *    the (query block, head) work items cannot fill the GPU (the current device's
  *    compute units, 256 on MI355X and when no device is visible; query with the
- *    same device current as the call) and, for PFA_PREC_BF16 (and the 8-bit
- *    calls), some sequence spans at least 2048 key rows, each item's key range is
+ *    same device current as the call) and, for PFA_PREC_BF16 and PFA_PREC_F16 (and
+ *    the 8-bit calls), some sequence spans at least 2048 key rows, each item's key range is
  *    split over several workgroups whose partial results (32 x head_dim f32 plus
  *    two f32 per row, per wavefront) are merged: when no item has more than 4 key
  *    chunks, by the last of its workgroups to finish (then, at the next multiple
@@ -149,7 +161,7 @@ int qknorm_rope(const float* q_in, const float* k_in, float* q_out, float* k_out
  *        aligned, at least pfa_workspace_bytes(seq_offsets, n_seqs, T, n_head,
  *        n_head_kv, head_dim, precision, 0) bytes, not overlapping the tensors; its
  *        contents are overwritten (calls in flight at the same time need separate
- *        workspaces).  Required for the bf16 modes; optional for PFA_PREC_F32: with
+ *        workspaces).  Required for the 16-bit modes; optional for PFA_PREC_F32: with
  *        NULL (or too small a workspace) short inputs run without the key split, which
  *        is correct but slower -- about twice as slow at T = 512 with 16 query heads
  *        over 8 K/V heads (the items then cannot fill the GPU).  pfa_attn_plan reports
@@ -300,8 +312,8 @@ size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_off
                                  int precision, int fused);
 
 /*
- * qk_prep_chunk_attn_tiled -- qk_prep_chunk_attn in the bf16 modes, keeping the cache's
- * bf16 K/V tiles across calls.  qk_prep_chunk_attn converts every cache row to the bf16
+ * qk_prep_chunk_attn_tiled -- qk_prep_chunk_attn in the 16-bit modes, keeping the cache's
+ * 16-bit K/V tiles across calls.  qk_prep_chunk_attn converts every cache row to the bf16
  * tiles the attention kernel reads, on every call; a caller that appends blocks of rows
  * to the same cache call after call (memra-engine 0.101.0 src/spec.rs,
  * `full_attn_verify`: a block of rows verified against, and appended to, a persistent
@@ -311,13 +323,13 @@ size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_off
  *
  * Passages: as for qk_prep_chunk_attn.
  *
- *  Arguments as for qk_prep_chunk_attn, precision PFA_PREC_BF16 or PFA_PREC_BF16X3
- *  (PFA_PREC_F32: PFA_ERR_INVALID_ARG), workspace sized by pfa_chunk_workspace_bytes(...,
+ *  Arguments as for qk_prep_chunk_attn, precision PFA_PREC_BF16, PFA_PREC_BF16X3 or
+ *  PFA_PREC_F16 (PFA_PREC_F32: PFA_ERR_INVALID_ARG), workspace sized by pfa_chunk_workspace_bytes(...,
  *  2) (the key split's partial results only; often 0), and:
  *  kv_tiles  device, read and written, 256-byte aligned, pfa_kv_tiles_bytes(n_slots,
  *        max_rows, n_head_kv, head_dim, precision) bytes, n_slots being this call's
  *        sequence count (1 when the offsets are NULL); owned by the caller, not
- *        overlapping the other tensors or the workspace.  Slot s holds the bf16 tiles of
+ *        overlapping the other tensors or the workspace.  Slot s holds the 16-bit tiles of
  *        sequence s's cache rows 0 .. max_rows-1 (64 rows a tile), then a rotary table of
  *        (cos, sin) pairs by position.  The call stages from k_cache / v_cache -- after
  *        writing its new rows there -- the tiles holding cache rows floor(base_s / 64) *
@@ -342,8 +354,8 @@ int qk_prep_chunk_attn_tiled(const float* q, const float* k, const float* v, flo
                              size_t workspace_bytes, void* stream);
 
 /* Bytes of the kv_tiles of qk_prep_chunk_attn_tiled: n_slots slots (1 .. PFA_MAX_SEQS) of
- * ceil(max_rows / 64) tiles per K/V head (K: 64 x head_dim bf16, twice for
- * PFA_PREC_BF16X3; V: 64 x head_dim bf16) and a rotary table of ceil(max_rows / 64) * 64
+ * ceil(max_rows / 64) tiles per K/V head (K: 64 x head_dim 16-bit values, twice for
+ * PFA_PREC_BF16X3; V: 64 x head_dim) and a rotary table of ceil(max_rows / 64) * 64
  * rows of head_dim / 2 (cos, sin) f32 pairs.  0 (and pfa_last_error()) for arguments the
  * call would reject. */
 size_t pfa_kv_tiles_bytes(int n_slots, int max_rows, int n_head_kv, int head_dim, int precision);

@@ -70,6 +70,8 @@ def test_zero_tokens_is_ok_without_pointers(L):
     (dict(D=96), UNSUPPORTED, "head_dim"),
     (dict(D=256), UNSUPPORTED, "head_dim"),
     (dict(prec=7), INVALID, "precision"),
+    (dict(prec=4), INVALID, "precision"),
+    (dict(prec=-1), INVALID, "precision"),
     (dict(scale=float("inf")), INVALID, "scale"),
     (dict(ptrs=(0, 8, 8, 8 << 20)), INVALID, "null"),
     (dict(ptrs=(8, 8, 8, 16)), INVALID, "overlap"),
@@ -253,6 +255,12 @@ def test_workspace_bytes_cases():
         8 * 128 * 64 * 128 * 2 * 2 + 8192 * 64 * 8
     assert pfa.workspace_bytes(8192, 32, 8, 128, "bf16x3", fused=True) == \
         8 * 128 * 64 * 128 * 2 * 3 + 8192 * 64 * 8
+    # f16 keeps the bf16 mode's tiles (same sizes, binary16 values), and its split rule
+    for fused in (False, True):
+        for T in (512, 2048, 8192):
+            assert pfa.workspace_bytes(T, 32, 8, 128, "f16", fused=fused) == \
+                pfa.workspace_bytes(T, 32, 8, 128, "bf16", fused=fused)
+    assert pfa.kv_tiles_bytes(2, 3000, 8, 128, "f16") == pfa.kv_tiles_bytes(2, 3000, 8, 128, "bf16")
 
 
 def test_workspace_bytes_rejects_what_attention_rejects(L):
@@ -264,12 +272,12 @@ def test_workspace_bytes_rejects_what_attention_rejects(L):
     assert _ws(L, (16,), 3, 2, 64, 1) == 0
 
 
-@pytest.mark.parametrize("prec", [1, 2])
+@pytest.mark.parametrize("prec", [1, 2, 3])
 def test_bf16_modes_check_the_workspace(L, prec):
     # every call below must fail its checks before any launch (the pointers are not real)
     ptrs = (1 << 20, 2 << 20, 3 << 20, 4 << 20)   # q 16x4x64 f32 = 16 KiB, k/v 8 KiB each
     need = _ws(L, (16,), 4, 2, 64, prec)
-    exact = (2 if prec == 1 else 3) * 2 * 1 * 64 * 64 * 2   # one 64-key tile per K/V head
+    exact = (3 if prec == 2 else 2) * 2 * 1 * 64 * 64 * 2   # one 64-key tile per K/V head
     assert exact <= need
     assert _attn(L, prec=prec, ptrs=ptrs) == INVALID
     assert "workspace" in _msg(L)

@@ -172,14 +172,57 @@ def test_attn_bf16_small(gpu_device, w, causal):
                        _attn_ref(w, x, causal=causal), f"attn bf16 {w.name} causal={causal}")
 
 
-def _bf16_rounded_inputs(w, x):
-    """Q, K, V as the bf16 kernel multiplies them: Q * (scale log2 e) rounded to bf16 (then
-    divided back), K and V rounded to bf16 -- for the oracle's diagnostic comparison."""
+def _bf16_rounded_inputs(w, x, dtype=torch.bfloat16):
+    """Q, K, V as the 16-bit kernel multiplies them: Q * (scale log2 e) rounded to bf16 (or
+    ``dtype``, float16 for the f16 mode; then divided back), K and V rounded the same way
+    -- for the oracle's comparison of what the mode computes."""
     c = np.float32(np.float32(w.softmax_scale) * np.float32(1.4426950408889634))
-    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dtype).to(
         torch.float64).numpy()
     q = bf((x.q * c).astype(np.float32)) / np.float64(c)
     return wl.Inputs(q, bf(x.k), bf(x.v), x.wq, x.wk, x.outliers)
+
+
+# f16 mode: its roundings are those of Q, K, V and of the weights P, each to binary16
+# (unit roundoff 2^-11).  Against the oracle on the f16-rounded inputs only the weights'
+# rounding remains: the output is an exact weighted mean of V rows with weights off by a
+# factor within 1 +- 2^-11 each, which moves it by at most 2^-11 (max V - min V) / (1 -
+# 2^-11) (weights below binary16's normal range are off by at most 2^-25 absolute, against
+# a sum of weights >= 1; that and the f32 accumulation get the 1e-4 allowance).
+F16_U = 2.0 ** -11
+
+
+def _f16_weight_bound(v):
+    return F16_U * float(v.max() - v.min()) / (1.0 - F16_U) + 1e-4
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_attn_f16_small(gpu_device, w):
+    x = wl.make_inputs(w)
+    t = _dev(x, gpu_device)
+    xr = _bf16_rounded_inputs(w, x, torch.float16)
+    for causal in (True, False):
+        got = _attn_gpu(w, t, precision="f16", causal=causal)
+        assert_bf16_parity(got, _attn_ref(w, x, causal=causal), f"attn f16 {w.name} causal={causal}")
+        max_abs, rel = errors(got, _attn_ref(w, xr, causal=causal))
+        bound = _f16_weight_bound(x.v)
+        print(f"attn f16 {w.name} causal={causal} vs oracle on f16-rounded inputs: "
+              f"max|err| {max_abs:.3e} (bound {bound:.3e}) rel L2 {rel:.3e}", flush=True)
+        assert max_abs <= bound
+
+
+def test_attn_f16_first_row_is_rounded_v(gpu_device):
+    """A first causal row has weight exactly 1 on one key: in the f16 mode the output is
+    that key's V rounded to binary16 (and nothing else)."""
+    w = wl.Workload("rows0_f16", (5, 64, 1, 200), 8, 2, 128, 128, 1e6, 1e-6, seed=32)
+    x = wl.make_inputs(w)
+    got = _attn_gpu(w, _dev(x, gpu_device), precision="f16")
+    vh = x.v.astype(np.float16).astype(np.float32)
+    for s in w.seq_offsets[:-1]:
+        for h in range(w.n_head):
+            kv = h // 4
+            np.testing.assert_array_equal(got[s, h * 128:(h + 1) * 128],
+                                          vh[s, kv * 128:(kv + 1) * 128])
 
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
@@ -208,7 +251,7 @@ def test_attn_bf16_first_row_is_rounded_v(gpu_device):
 # the attention kernel's prologue; compared with the fused f64 oracle on the raw inputs.
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
-@pytest.mark.parametrize("precision", ["bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["bf16", "bf16x3", "f16"])
 def test_fused_bf16_small(gpu_device, w, precision):
     x = wl.make_inputs(w)
     for causal in (True, False):
@@ -217,7 +260,7 @@ def test_fused_bf16_small(gpu_device, w, precision):
                            f"fused {precision} {w.name} causal={causal}")
 
 
-@pytest.mark.parametrize("precision", ["bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["bf16", "bf16x3", "f16"])
 def test_fused_bf16_k_rot_out_is_f32_exact_path(gpu_device, precision):
     """The rotated K copied out by the bf16 staging kernel is f32 and meets the f32 gates."""
     w = wl.CONFIGS["mixed"].with_(seq_lens=(128, 1, 300, 0, 77), name="mixed_small")
@@ -245,7 +288,7 @@ def test_fused_bf16_matches_unfused_chain(gpu_device):
     assert_bf16_parity(fused, unf.cpu().numpy().astype(np.float64), "fused bf16 vs unfused bf16")
 
 
-@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3", "f16"])
 def test_row_max_covers_both_lane_halves(gpu_device, precision):
     """Keys whose index is 4..7 mod 8 score ~300 (log2 units) above the others.  The two
     lanes of a query hold those two key sets in the score registers; a row max taken
@@ -270,10 +313,13 @@ def test_row_max_covers_both_lane_halves(gpu_device, precision):
         print(f"row max over both halves f32: max|err| {max_abs:.3e} rel L2 {rel:.3e}", flush=True)
         assert max_abs <= 1e-4 and rel <= 1e-4
     else:
-        # the scores are ~200 (natural units): bf16 inputs move them by ~1, so compare
-        # against the oracle on the rounded inputs (what the bf16 modes promise)
-        assert_bf16_parity(got, _attn_ref(w, _bf16_rounded_inputs(w, x)) if precision == "bf16"
-                           else ref, f"row max over both halves {precision}")
+        # the scores are ~200 (natural units): bf16 inputs move them by ~1 (f16 ones by
+        # ~0.1), so compare against the oracle on the rounded inputs (what those modes
+        # promise)
+        rounded = {"bf16": torch.bfloat16, "f16": torch.float16}
+        assert_bf16_parity(got, _attn_ref(w, _bf16_rounded_inputs(w, x, rounded[precision]))
+                           if precision in rounded else ref,
+                           f"row max over both halves {precision}")
 
 
 def test_tensors_past_4gb(gpu_device):
@@ -359,5 +405,5 @@ def test_paired_items_full_compare(gpu_device, w):
     assert_f32_parity(_attn_gpu(w, t), ref, f"attn {w.name}")
     assert_f32_parity(_fused_gpu(w, t), _fused_ref(w, x), f"fused {w.name}")
     # the same shapes through the bf16 kernel
-    for prec in ("bf16", "bf16x3"):
+    for prec in ("bf16", "bf16x3", "f16"):
         assert_bf16_parity(_attn_gpu(w, t, precision=prec), ref, f"attn {prec} {w.name}")

@@ -77,7 +77,7 @@ PREFILL = [
 
 
 @pytest.mark.parametrize("case", PREFILL, ids=[c[0] for c in PREFILL])
-@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3", "f16"])
 def test_prefill_entry_points_write_only_their_outputs(case, precision):
     name, lens, H, Hkv, d, n = case
     w = wl.Workload(name, lens, H, Hkv, d, n, 1e6, 1e-6, seed=1600)
@@ -182,7 +182,7 @@ def test_chunk_entry_points_write_only_their_outputs(case, precision):
 
 
 @pytest.mark.parametrize("case", CHUNK, ids=[c[0] for c in CHUNK])
-@pytest.mark.parametrize("precision", ["bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["bf16", "bf16x3", "f16"])
 def test_tiled_chunk_entry_writes_only_its_outputs(case, precision):
     """qk_prep_chunk_attn_tiled: writes out, the new rows of the caches and the tiles of
     kv_tiles; nothing outside them (kv_tiles, sized for more rows than the call needs,

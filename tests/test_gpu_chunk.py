@@ -124,7 +124,7 @@ def case(request):
     return Case(request.param, *CASES[request.param])
 
 
-@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3", "f16"])
 def test_chunk_attn_matches_oracle(case, precision):
     got = _chunk_gpu(case, precision)
     ref = _chunk_ref(case)
@@ -134,7 +134,7 @@ def test_chunk_attn_matches_oracle(case, precision):
         assert_bf16_parity(got, ref, case.label("gqa_chunk_attn", precision))
 
 
-@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3", "f16"])
 def test_prep_chunk_attn_matches_oracle_and_fills_the_cache(case, precision):
     got, kc, vc = _fused_gpu(case, precision)
     ref, kref, vref = _fused_ref(case)

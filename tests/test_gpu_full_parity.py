@@ -15,7 +15,8 @@ that touch every key tile and every query block: both sides of every 32-row edge
 32-row block.
 
 Gates (stated as such, not derived from the pages, which fix no tolerance): f32 max-abs
-2e-5 and relative L2 1e-5 over the compared elements; bf16 modes max-abs 2e-2.
+2e-5 and relative L2 1e-5 over the compared elements; 16-bit modes (bf16, bf16x3, f16)
+max-abs 2e-2.
 """
 import os
 
@@ -33,7 +34,7 @@ pytestmark = pytest.mark.gpu
 THREADS = len(os.sched_getaffinity(0))
 FULL = ["tiny", "qwen3_0p6b", "qwen3_8b", "mixed", "prefill_8192"]
 MODES = [("f32", "unfused"), ("f32", "fused"), ("bf16", "unfused"), ("bf16", "fused"),
-         ("bf16x3", "unfused"), ("bf16x3", "fused")]
+         ("bf16x3", "unfused"), ("bf16x3", "fused"), ("f16", "unfused"), ("f16", "fused")]
 LONG_ROWS_SEED = 5
 
 _inputs = {}
@@ -143,7 +144,7 @@ def test_every_output_element(name, precision, path, gpu_device):
 
 
 LONG_MODES = [("f32", "unfused"), ("f32", "fused"), ("bf16", "fused"), ("bf16x3", "unfused"),
-              ("bf16x3", "fused")]
+              ("bf16x3", "fused"), ("f16", "unfused"), ("f16", "fused")]
 
 
 @pytest.mark.parametrize("precision,path", LONG_MODES, ids=[f"{p}-{q}" for p, q in LONG_MODES])
@@ -194,8 +195,8 @@ def test_long_plain_bf16_on_its_rounded_inputs(gpu_device):
 @pytest.mark.xfail(strict=True, reason="plain bf16 inputs cannot resolve the scores of x8 "
                    "outlier keys to the 2e-2 gate: rounding K and Q to bf16 moves a score by "
                    "~2^-9 of |q||k|, and x8 keys make those scores ~8x larger (measured 0.116 "
-                   "over these 1500 rows, 5.9e-2 over 60).  PFA_PREC_BF16X3 and the fused bf16 "
-                   "entry meet the gate here.")
+                   "over these 1500 rows, 5.9e-2 over 60).  PFA_PREC_BF16X3, PFA_PREC_F16 and the "
+                   "fused bf16 entry meet the gate here.")
 def test_long_plain_bf16_gate(gpu_device):
     got = _gpu("long", "bf16", "unfused")
     assert_bf16_parity(got, _ref("long", "unfused"), "unfused bf16 long vs unrounded oracle")

@@ -7,7 +7,7 @@ offset tables, the longest-first segment decode over up to 128 segments, the bf1
 workspace's per-sequence tile offsets, and positions restarting at every sequence
 (multi-sequence rows as in memra-engine 0.101.0 src/spec.rs, `qwen35_tparallel_fa_layer`:
 per-row positions and per-sequence K/V).  Every entry point that takes a sequence table
-is run: prefill (f32, bf16, bf16x3), fused prefill, chunks over cached prefixes of
+is run: prefill (f32, bf16, bf16x3, f16), fused prefill, chunks over cached prefixes of
 random length (plain and fused), and the 8-bit store.
 """
 import numpy as np
@@ -64,7 +64,7 @@ def test_prefill_128_sequences(i):
                                     rope_freq_base=float(np.float32(w.rope_freq_base)),
                                     rms_eps=eps32(w), scale=w.softmax_scale,
                                     seq_offsets=w.seq_offsets)
-    for prec in ("f32", "bf16", "bf16x3"):
+    for prec in ("f32", "bf16", "bf16x3", "f16"):
         print(f"gqa_prefill_attn {w.name}: T={w.T} seqs={w.n_seqs} H={w.n_head} "
               f"Hkv={w.n_head_kv} d={w.head_dim} {prec}", flush=True)
         out = pfa.gqa_prefill_attn(_dev(qn), _dev(kn), _dev(x.v), head_dim=w.head_dim,

@@ -50,7 +50,7 @@ def _path(entry, q_lens, kv_lens, H, Hkv, d, prec):
 PREFILL = [  # name, sequence lengths, H, Hkv, d, precisions
     ("t512", (512,), 16, 8, 128, ("f32", "bf16x3")),
     ("t2048", (2048,), 16, 8, 128, ("bf16",)),
-    ("t2048_d64", (2048,), 8, 2, 64, ("f32", "bf16", "bf16x3")),
+    ("t2048_d64", (2048,), 8, 2, 64, ("f32", "bf16", "bf16x3", "f16")),
     ("packed", (300, 1500, 40), 8, 4, 128, ("f32", "bf16x3")),
 ]
 _prefill_refs = {}

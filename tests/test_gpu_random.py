@@ -1,8 +1,8 @@
 """GPU parity over seeded random configurations of every entry point, against the oracle:
 packed sequences with and without cached prefixes (empty ones included), several head
 geometries, head_dim 64 and 128, rotary widths d, d/2 and others, causal or not, sliding
-windows, gated outputs -- through qknorm_rope, the prefill entries (f32 / bf16 / bf16x3, fused
-with k_rot_out), the chunk entries, the fused chunk entry and the 8-bit entries.  Each case is
+windows, gated outputs -- through qknorm_rope, the prefill entries (f32 / bf16 / bf16x3 / f16,
+fused with k_rot_out), the chunk entries, the fused chunk entry and the 8-bit entries.  Each case is
 drawn from its own seed (printed first), so a failure names it.
 Tolerances: the f32 gate, the bf16 gate, and for the 8-bit path the bf16 gate with its
 relative-L2 bound."""
@@ -60,8 +60,8 @@ def _gate(c, T_q, r):
 
 
 @pytest.mark.parametrize("seed", range(100, 124))
-@pytest.mark.parametrize("entry", ["chunk_f32", "chunk_bf16", "chunk_bf16x3", "fused_f32",
-                                   "fused_bf16"])
+@pytest.mark.parametrize("entry", ["chunk_f32", "chunk_bf16", "chunk_bf16x3", "chunk_f16",
+                                   "fused_f32", "fused_bf16", "fused_f16"])
 def test_random_chunk_entries(seed, entry):
     c = draw(seed)
     q_offs, kv_offs, new = _offsets(c)
@@ -172,7 +172,7 @@ def draw_prefill(seed):
 
 @pytest.mark.parametrize("seed", range(300, 324))
 @pytest.mark.parametrize("entry", ["qknorm_rope", "prefill_f32", "prefill_bf16", "prefill_bf16x3",
-                                   "prep_f32", "prep_bf16"])
+                                   "prefill_f16", "prep_f32", "prep_bf16", "prep_f16"])
 def test_random_prefill_entries(seed, entry):
     c = draw_prefill(seed)
     H, Hkv, d, n = c["H"], c["Hkv"], c["d"], c["n"]

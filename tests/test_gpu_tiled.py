@@ -97,11 +97,11 @@ def _session(H, Hkv, d, n, precision, gate_call=2, window_call=3):
     assert np.all(bands == SENTINEL), "a write landed outside kv_tiles"
 
 
-@pytest.mark.parametrize("precision", ["bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["bf16", "bf16x3", "f16"])
 def test_tiled_appends_8b_heads(precision):
     _session(32, 8, 128, 128, precision)
 
 
-@pytest.mark.parametrize("precision", ["bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["bf16", "bf16x3", "f16"])
 def test_tiled_appends_d64_half_rotary(precision):
     _session(8, 2, 64, 32, precision, gate_call=0, window_call=1)

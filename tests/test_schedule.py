@@ -155,16 +155,19 @@ def test_key_split_at_short_inputs():
     # split (f32 only when the workspace has room for the partial results); with at most
     # 4 chunks an item, each item's last workgroup merges them (no combine launch)
     for prec, kernel in (("f32", "attn_f32_kernel<128,false,false,true>"),
-                         ("bf16x3", "attn_bf16_kernel<128,true,false,false,true>")):
+                         ("bf16x3", "attn_bf16_kernel<128,true,false,false,true,false>")):
         plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, prec)
         assert 1 < plan["max_key_chunks"] <= 4 and plan["workspace_bytes"] > 0
         assert plan["merge_in_place"] == 1
         assert plan["kernels"].endswith(kernel) and "combine" not in plan["kernels"]
-    # plain bf16 splits only sequences of at least 2048 keys
-    plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, "bf16")
-    assert plan["max_key_chunks"] == 1 and plan["merge_in_place"] == 0
-    plan = _check_schedule(pfa.ENTRY_PREFILL, [2048], [2048], 16, 8, 128, "bf16")
-    assert 1 < plan["max_key_chunks"] <= 4 and plan["merge_in_place"] == 1
+    # plain bf16 and f16 (the same kernel) split only sequences of at least 2048 keys
+    for prec in ("bf16", "f16"):
+        plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, prec)
+        assert plan["max_key_chunks"] == 1 and plan["merge_in_place"] == 0
+        plan = _check_schedule(pfa.ENTRY_PREFILL, [2048], [2048], 16, 8, 128, prec)
+        assert 1 < plan["max_key_chunks"] <= 4 and plan["merge_in_place"] == 1
+        assert plan["kernels"].endswith(
+            f"attn_bf16_kernel<128,false,false,false,true,{'true' if prec == 'f16' else 'false'}>")
     plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, "f32",
                            workspace_bytes=0)
     assert plan["max_key_chunks"] == 1 and plan["workspace_bytes"] == 0
@@ -207,24 +210,30 @@ def test_plan_names_the_kernels_in_launch_order():
     p = pfa.attn_plan(pfa.ENTRY_PREP, T_q=8192, n_head=32, n_head_kv=8, head_dim=128,
                       rope_dim=128, precision="bf16")
     assert p["kernels"] == ("rope_table_kernel<128,false> + "
-                            "stage_kv_bf16_kernel<128,false,true> + "
-                            "attn_bf16_kernel<128,false,true,false,false>")
+                            "stage_kv_bf16_kernel<128,false,true,false> + "
+                            "attn_bf16_kernel<128,false,true,false,false,false>")
+    p = pfa.attn_plan(pfa.ENTRY_PREP, T_q=8192, n_head=32, n_head_kv=8, head_dim=128,
+                      rope_dim=128, precision="f16")
+    assert p["kernels"] == ("rope_table_kernel<128,false> + "
+                            "stage_kv_bf16_kernel<128,false,true,true> + "
+                            "attn_bf16_kernel<128,false,true,false,false,true>")
     p = pfa.attn_plan(pfa.ENTRY_PREFILL, T_q=8192, n_head=32, n_head_kv=8, head_dim=128,
                       precision="bf16x3")
-    assert p["kernels"] == ("stage_kv_bf16_kernel<128,true,false> + "
-                            "attn_bf16_kernel<128,true,false,false,false>")
+    assert p["kernels"] == ("stage_kv_bf16_kernel<128,true,false,false> + "
+                            "attn_bf16_kernel<128,true,false,false,false,false>")
     # the tiled chunk entry: the new rows' K/V into the caches, their tiles re-staged into
     # kv_tiles, attention (1024 rows over 8192: two key chunks, merged in place)
     p = pfa.attn_plan(pfa.ENTRY_CHUNK_TILED, T_q=1024, T_kv=8192, n_head=32, n_head_kv=8,
                       head_dim=128, rope_dim=128, precision="bf16", q_offsets=[0, 1024],
                       kv_offsets=[0, 8192])
-    assert p["kernels"] == ("qknorm_rope_kernel<128,0,false> + append_tiles_kernel<128,false> + "
-                            "attn_bf16_kernel<128,false,true,false,true>")
+    assert p["kernels"] == ("qknorm_rope_kernel<128,0,false> + "
+                            "append_tiles_kernel<128,false,false> + "
+                            "attn_bf16_kernel<128,false,true,false,true,false>")
     assert p["workspace_bytes"] == pfa.chunk_workspace_bytes(
         1024, 8192, 32, 8, 128, "bf16", q_offsets=[0, 1024], kv_offsets=[0, 8192], fused=2)
     p = pfa.attn_plan(pfa.ENTRY_Q8, T_q=8192, T_kv=8192, n_head=32, n_head_kv=8, head_dim=64)
     assert p["kernels"] == ("stage_kv_q8_kernel<64,false> + "
-                            "attn_bf16_kernel<64,false,false,true,false>")
+                            "attn_bf16_kernel<64,false,false,true,false,false>")
 
 
 def test_plan_rejects_what_the_entry_points_reject():

@@ -23,7 +23,7 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
 
 
-@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3"])
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3", "f16"])
 def test_noalloc_matches_the_workspace_entry(precision):
     for w in CALLS:
         x = wl.make_inputs(w)

@@ -6,7 +6,8 @@ argument marshalling for torch tensors, nothing else.  The library is loaded on
 first use; if it has not been built every op raises.
 """
 from .ops import (ENTRY_CHUNK, ENTRY_CHUNK_PREP, ENTRY_CHUNK_TILED, ENTRY_PREFILL, ENTRY_PREP,
-                  ENTRY_Q8, ENTRY_Q8_PREP, PRECISION_BF16, PRECISION_BF16X3, PRECISION_F32,
+                  ENTRY_Q8, ENTRY_Q8_PREP, PRECISION_BF16, PRECISION_BF16X3, PRECISION_F16,
+                  PRECISION_F32,
                   PfaError, UNIT_FIELDS, attn_plan, attn_units, chunk_workspace_bytes,
                   gqa_attn_q8, gqa_chunk_attn, gqa_prefill_attn, gqa_prefill_attn_noalloc,
                   kv_tiles_bytes, lib, noalloc_scratch_bytes, q8_workspace_bytes, qk_prep_attn,
@@ -22,4 +23,4 @@ __all__ = ["qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "workspace_bytes",
            "ENTRY_CHUNK", "ENTRY_CHUNK_PREP", "ENTRY_Q8", "ENTRY_Q8_PREP", "ENTRY_CHUNK_TILED",
            "lib", "version",
            "PfaError",
-           "PRECISION_F32", "PRECISION_BF16", "PRECISION_BF16X3"]
+           "PRECISION_F32", "PRECISION_BF16", "PRECISION_BF16X3", "PRECISION_F16"]

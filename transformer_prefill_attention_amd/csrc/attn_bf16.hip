@@ -75,8 +75,46 @@ constexpr int kThreads = 64 * kWaves;
 // the running max moves only when exceeded by more than this (log2 units)
 constexpr float kLazyMax = 8.0f;
 
-__device__ __forceinline__ floatx16 mfma_bf16(bf16x8 a, bf16x8 b, floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit operands of the products: bf16, or with F16 IEEE binary16 (PFA_PREC_F16),
+// whose bits sit in the same 2-byte slots (no tile layout depends on the format).  Both
+// round to nearest even.
+template <bool F16>
+__device__ __forceinline__ __bf16 to16(float x) {
+    if constexpr (F16) return __builtin_bit_cast(__bf16, (_Float16)x);
+    else return (__bf16)x;
+}
+// Two at a time, as one packed conversion (binary16: v_cvt_pk_f16_f32, which rounds to
+// nearest even; converting the two elements separately costs two conversions and a permute)
+template <bool F16>
+__device__ __forceinline__ bf16x2 to16x2(float a, float b) {
+    if constexpr (F16) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(bf16x2, __builtin_convertvector(f32x2{a, b}, halfx2));
+    } else {
+        return bf16x2{(__bf16)a, (__bf16)b};
+    }
+}
+template <bool F16>
+__device__ __forceinline__ floatx16 mfma16(bf16x8 a, bf16x8 b, floatx16 c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                      __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// acc + x[0] + x[1], the two weights as rounded for the P.V product
+template <bool F16>
+__device__ __forceinline__ float add_pair(bf16x2 x, float acc) {
+    if constexpr (F16) {
+        const halfx2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(halfx2, x), ones, acc, false);
+    } else {
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(x, ones, acc, false);
+    }
 }
 
 // Position of 16-byte chunk `c` in row `row` of an LDS tile with `nch` chunks per
@@ -166,13 +204,14 @@ __device__ __forceinline__ void store_vt_rows(const __bf16* vts, __bf16* vt, int
 
 // One tile's rows of a 256-thread block, shared by the staging kernels.
 // 8 dims (logical chunk c of row r) -> bf16 high (and low) parts at the swizzled place.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool F16>
 __device__ __forceinline__ void store_k_chunk(__bf16* tile, int r, int c, const float* x) {
+    static_assert(!(SPLIT && F16), "the split scores are a bf16 mode");
     constexpr int NCH = D / 8;
     bf16x8 hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        hi[e] = (__bf16)x[e];
+        hi[e] = to16<F16>(x[e]);
         if constexpr (SPLIT) lo[e] = (__bf16)(x[e] - (float)hi[e]);
     }
     const int pos = swz(r, c, NCH);
@@ -182,7 +221,7 @@ __device__ __forceinline__ void store_k_chunk(__bf16* tile, int r, int c, const 
 // V rows 0 .. nval-1 (stride row_stride floats; zeros past nval) -> V^T in vts.  4 keys x
 // 4 dims per block, loaded as 4 float4 rows, written as four 4-key runs of V^T.  Block b:
 // dims 4 (b % (D/4)) .., keys 4 (b / (D/4)) ..
-template <int D>
+template <int D, bool F16>
 __device__ __forceinline__ void stage_v_rows(const float* vin, int64_t row_stride, int nval,
                                              __bf16* vts, int tid) {
     constexpr int VB = kBN * D / 16;
@@ -199,14 +238,14 @@ __device__ __forceinline__ void stage_v_rows(const float* vin, int64_t row_strid
         for (int c = 0; c < 4; ++c) {
             bf16x4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (__bf16)r[e][c];
+            for (int e = 0; e < 4; ++e) x[e] = to16<F16>(r[e][c]);
             *reinterpret_cast<bf16x4*>(vts + (d0 + c) * kVts + key0) = x;
         }
     }
 }
 // K rows 0 .. nval-1 (zeros past nval) -> the K tile: 16-byte chunks (8 dims) of each
 // row, converted and written to their swizzled place.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool F16>
 __device__ __forceinline__ void stage_k_rows(const float* kin, int64_t row_stride, int nval,
                                              __bf16* kt, int tid) {
     constexpr int NCH = D / 8;
@@ -223,7 +262,7 @@ __device__ __forceinline__ void stage_k_rows(const float* kin, int64_t row_strid
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = e < 4 ? a[e] : b[e - 4];
-        store_k_chunk<D, SPLIT>(kt, r, c, x);
+        store_k_chunk<D, SPLIT, F16>(kt, r, c, x);
     }
 }
 
@@ -233,7 +272,7 @@ __device__ __forceinline__ void stage_k_rows(const float* kin, int64_t row_strid
 //  V tile: D rows x 64 keys; row d holds 8 groups of 8 keys, group p = 2s + h being
 //  keys 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3} (the keys lane half h feeds
 //  at P.V step s), group p stored at position swz(d, p, 8).
-template <int D, bool SPLIT, bool PREP>
+template <int D, bool SPLIT, bool PREP, bool F16>
 __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restrict__ k,
                                                             const float* __restrict__ v,
                                                             __bf16* __restrict__ ws,
@@ -256,9 +295,9 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
                  ((int64_t)kv * n_tiles + gt) * (kBN * D);
     const float* kin = k + (int64_t)k0 * row_stride + kv * D;
     const float* vin = v + (int64_t)k0 * row_stride + kv * D;
-    stage_v_rows<D>(vin, row_stride, nval, vts, tid);
+    stage_v_rows<D, F16>(vin, row_stride, nval, vts, tid);
     if constexpr (!PREP) {
-        stage_k_rows<D, SPLIT>(kin, row_stride, nval, kt, tid);
+        stage_k_rows<D, SPLIT, F16>(kin, row_stride, nval, kt, tid);
     } else {
         // Fused entry: RMS-normalise and rotate each K row on its way in.  Four threads
         // per row take D/4 consecutive dims each.  A rotation partner (dim c +- n/2) sits
@@ -332,7 +371,8 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
                 *reinterpret_cast<floatx4*>(dst + i) = floatx4{y[i], y[i + 1], y[i + 2], y[i + 3]};
         }
 #pragma unroll
-        for (int cc = 0; cc < DQ / 8; ++cc) store_k_chunk<D, SPLIT>(kt, r, c0 / 8 + cc, y + 8 * cc);
+        for (int cc = 0; cc < DQ / 8; ++cc)
+            store_k_chunk<D, SPLIT, F16>(kt, r, c0 / 8 + cc, y + 8 * cc);
     }
     __syncthreads();
     store_vt_rows<D>(vts, vt, tid);
@@ -344,7 +384,7 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
 // sequence's end are zeros), into the tile's place in its sequence slot; the blocks of
 // K/V head 0 also write the rotary-table rows of the tile's positions as
 // rope_table_kernel computes them.
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool F16>
 __global__ __launch_bounds__(256) void append_tiles_kernel(const float* __restrict__ k,
                                                            const float* __restrict__ v,
                                                            __bf16* __restrict__ tiles,
@@ -364,8 +404,8 @@ __global__ __launch_bounds__(256) void append_tiles_kernel(const float* __restri
     __bf16* kt = tiles + ((int64_t)kv * n_tiles + gt) * (KP * kBN * D);
     __bf16* vt = tiles + (int64_t)Hkv * n_tiles * (KP * kBN * D) +
                  ((int64_t)kv * n_tiles + gt) * (kBN * D);
-    stage_v_rows<D>(v + (int64_t)k0 * row_stride + kv * D, row_stride, nval, vts, tid);
-    stage_k_rows<D, SPLIT>(k + (int64_t)k0 * row_stride + kv * D, row_stride, nval, kt, tid);
+    stage_v_rows<D, F16>(v + (int64_t)k0 * row_stride + kv * D, row_stride, nval, vts, tid);
+    stage_k_rows<D, SPLIT, F16>(k + (int64_t)k0 * row_stride + kv * D, row_stride, nval, kt, tid);
     __syncthreads();
     store_vt_rows<D>(vts, vt, tid);
     if (app.rope_dim > 0 && kv == 0) {
@@ -467,7 +507,7 @@ __global__ __launch_bounds__(256) void stage_kv_q8_kernel(Q8Store q8, unsigned c
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT, bool PREP, bool Q8, bool MERGE>
+template <int D, bool SPLIT, bool PREP, bool Q8, bool MERGE, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __restrict__ q,
                                                                 const __bf16* __restrict__ ws,
                                                                 float* __restrict__ out,
@@ -663,7 +703,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float x = xq[s][e] * qscale;
-                qop[s][e] = (__bf16)x;
+                qop[s][e] = to16<F16>(x);
                 if constexpr (SPLIT) qlo[s][e] = (__bf16)(x - (float)qop[s][e]);
             }
     }
@@ -777,7 +817,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
             if (i < NPV) {
                 // step s contracts keys 16s + 8(e/4) + 4hl + e%4: P registers 8(s%2)+e
                 // of score block s/2, V^T key group 2s + hl
-                oacc[i % NCB] = mfma_bf16(opnd[i], pop[i / NCB], oacc[i % NCB]);
+                oacc[i % NCB] = mfma16<F16>(opnd[i], pop[i / NCB], oacc[i % NCB]);
             } else {
                 const int j = i - NPV;
                 const int part = j % KP, kb = (j / KP) % 2, s = j / (2 * KP);
@@ -787,12 +827,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 } else if constexpr (SPLIT) {
                     // per key block: the two small cross terms first, then the high product
                     if (part == 1) {
-                        sacc[kb] = mfma_bf16(opnd[i], qop[s], sacc[kb]);
-                        sacc[kb] = mfma_bf16(opnd[i - 1], qlo[s], sacc[kb]);
-                        sacc[kb] = mfma_bf16(opnd[i - 1], qop[s], sacc[kb]);
+                        sacc[kb] = mfma16<F16>(opnd[i], qop[s], sacc[kb]);
+                        sacc[kb] = mfma16<F16>(opnd[i - 1], qlo[s], sacc[kb]);
+                        sacc[kb] = mfma16<F16>(opnd[i - 1], qop[s], sacc[kb]);
                     }
                 } else {
-                    sacc[kb] = mfma_bf16(opnd[i], qop[s], sacc[kb]);
+                    sacc[kb] = mfma16<F16>(opnd[i], qop[s], sacc[kb]);
                 }
             }
         }
@@ -869,9 +909,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                pop[2 * kb + (r >> 3)][r & 7] =
-                    (__bf16)__builtin_amdgcn_exp2f(ex(sacc[kb][r], m_sub));
+            for (int r = 0; r < 16; r += 2) {
+                const bf16x2 pr = to16x2<F16>(__builtin_amdgcn_exp2f(ex(sacc[kb][r], m_sub)),
+                                              __builtin_amdgcn_exp2f(ex(sacc[kb][r + 1], m_sub)));
+                pop[2 * kb + (r >> 3)][r & 7] = pr[0];
+                pop[2 * kb + (r >> 3)][(r & 7) + 1] = pr[1];
+            }
         // (issued ahead of the check, not sunk below it onto the max's critical path)
         asm volatile("" : "+v"(pop[0]), "+v"(pop[1]), "+v"(pop[2]), "+v"(pop[3]));
         if (__any(lmax > m_run + kLazyMax)) {
@@ -884,9 +927,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    pop[2 * kb + (r >> 3)][r & 7] =
-                        (__bf16)__builtin_amdgcn_exp2f(ex(sacc[kb][r], m_new));
+                for (int r = 0; r < 16; r += 2) {
+                    const bf16x2 pr =
+                        to16x2<F16>(__builtin_amdgcn_exp2f(ex(sacc[kb][r], m_new)),
+                                    __builtin_amdgcn_exp2f(ex(sacc[kb][r + 1], m_new)));
+                    pop[2 * kb + (r >> 3)][r & 7] = pr[0];
+                    pop[2 * kb + (r >> 3)][(r & 7) + 1] = pr[1];
+                }
             l_run *= (double)alpha;
             // alpha is 1 in rows without a bump; hidden from the optimiser, which
             // would otherwise make the multiplication unconditional
@@ -898,14 +945,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
         }
         // the denominator sums the weights as rounded for the P.V product, so the
         // output is a weighted mean of V with exactly the weights that were applied
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         float ps[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bf16x2 pr = {pop[i][2 * e], pop[i][2 * e + 1]};
-                ps[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps[e & 1], false);
+                ps[e & 1] = add_pair<F16>(pr, ps[e & 1]);
             }
         l_run += (double)(ps[0] + ps[1]);
     };
@@ -1005,59 +1051,79 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
     }
 }
 
+// The launches of one call for fixed template arguments: tiles appended (kept tiles)
+// or the rotary table and the staging kernel, then the attention kernel.
+template <int D, bool SPLIT, bool PREP, bool F16>
+void launch_bf16_kernels(const float* q, const float* k, const float* v, float* out, __bf16* w,
+                         const AttnSched& sched, const AttnGeom& geom, const PrepParams& p,
+                         bool prep_k, const Partials& part, int n_items, hipStream_t stream,
+                         const TileAppend* app) {
+    const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
+    const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv),
+        block(kThreads);
+    if (app) {
+        const dim3 agrid((unsigned)(app->cum[app->n_seqs] * geom.Hkv));
+        if (app->cum[app->n_seqs] > 0)
+            hipLaunchKernelGGL((append_tiles_kernel<D, SPLIT, F16>), agrid, sblock, 0, stream, k,
+                               v, w, *app, geom.Hkv);
+    } else {
+        if (PREP) {
+            const dim3 tgrid((unsigned)((sched.max_len + kTabRows - 1) / kTabRows));
+            hipLaunchKernelGGL((rope_table_kernel<D, SPLIT>), tgrid, sblock, 0, stream, w,
+                               geom.Hkv, sched.n_tiles, sched.max_len, p.rope_dim, p.base);
+        }
+        if (PREP && prep_k)
+            hipLaunchKernelGGL((stage_kv_bf16_kernel<D, SPLIT, true, F16>), sgrid, sblock, 0,
+                               stream, k, v, w, sched, geom.Hkv, p);
+        else
+            hipLaunchKernelGGL((stage_kv_bf16_kernel<D, SPLIT, false, F16>), sgrid, sblock, 0,
+                               stream, k, v, w, sched, geom.Hkv, p);
+    }
+    if (part.cnt)  // in-place merge of split items
+        hipLaunchKernelGGL((attn_bf16_kernel<D, SPLIT, PREP, false, true, F16>), grid, block, 0,
+                           stream, q, w, out, sched, geom, p, part, Q8Store{});
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, SPLIT, PREP, false, false, F16>), grid, block, 0,
+                           stream, q, w, out, sched, geom, p, part, Q8Store{});
+}
+
+template <int D, bool PREP>
+void launch_bf16_mode(bool split_qk, bool f16, const float* q, const float* k, const float* v,
+                      float* out, __bf16* w, const AttnSched& sched, const AttnGeom& geom,
+                      const PrepParams& p, bool prep_k, const Partials& part, int n_items,
+                      hipStream_t stream, const TileAppend* app) {
+    if (f16)
+        launch_bf16_kernels<D, false, PREP, true>(q, k, v, out, w, sched, geom, p, prep_k, part,
+                                                  n_items, stream, app);
+    else if (split_qk)
+        launch_bf16_kernels<D, true, PREP, false>(q, k, v, out, w, sched, geom, p, prep_k, part,
+                                                  n_items, stream, app);
+    else
+        launch_bf16_kernels<D, false, PREP, false>(q, k, v, out, w, sched, geom, p, prep_k, part,
+                                                   n_items, stream, app);
+}
+
 }  // namespace
 
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
-                            const PrepParams* prep, bool prep_k, const Partials& part,
+                            bool f16, const PrepParams* prep, bool prep_k, const Partials& part,
                             int n_items, hipStream_t stream, const TileAppend* app) {
     __bf16* w = static_cast<__bf16*>(ws);
     const PrepParams p = prep ? *prep : PrepParams{nullptr, nullptr, nullptr, 0, 0.0f, 0.0};
-    const bool merge = part.cnt != nullptr;  // in-place merge of split items
-    const dim3 sgrid((unsigned)sched.n_tiles * geom.Hkv), sblock(256);
-    const dim3 grid((unsigned)n_items * sched.max_chunks * geom.chunks * geom.Hkv),
-        block(kThreads);
-    const dim3 tgrid((unsigned)((sched.max_len + kTabRows - 1) / kTabRows)), tblock(256);
-    const dim3 agrid((unsigned)(app ? app->cum[app->n_seqs] * geom.Hkv : 0));
-#define PFA_LAUNCH_BF16(DD, SS, PP)                                                             \
-    do {                                                                                        \
-        if (app) {                                                                              \
-            if (app->cum[app->n_seqs] > 0)                                                      \
-                hipLaunchKernelGGL((append_tiles_kernel<DD, SS>), agrid, sblock, 0, stream, k,  \
-                                   v, w, *app, geom.Hkv);                                       \
-        } else if (PP)                                                                          \
-            hipLaunchKernelGGL((rope_table_kernel<DD, SS>), tgrid, tblock, 0, stream, w,      \
-                               geom.Hkv, sched.n_tiles, sched.max_len, p.rope_dim, p.base);    \
-        if (app) {                                                                              \
-        } else if (PP && prep_k)                                                                \
-            hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, true>), sgrid, sblock, 0, stream, \
-                               k, v, w, sched, geom.Hkv, p);                                    \
-        else                                                                                    \
-            hipLaunchKernelGGL((stage_kv_bf16_kernel<DD, SS, false>), sgrid, sblock, 0, stream,\
-                               k, v, w, sched, geom.Hkv, p);                                    \
-        if (merge)                                                                              \
-            hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP, false, true>), grid, block, 0,     \
-                               stream, q, w, out, sched, geom, p, part, Q8Store{});             \
-        else                                                                                    \
-            hipLaunchKernelGGL((attn_bf16_kernel<DD, SS, PP, false, false>), grid, block, 0,    \
-                               stream, q, w, out, sched, geom, p, part, Q8Store{});             \
-    } while (0)
-#define PFA_LAUNCH_BF16_P(DD, SS)                   \
-    do {                                            \
-        if (prep) PFA_LAUNCH_BF16(DD, SS, true);    \
-        else PFA_LAUNCH_BF16(DD, SS, false);        \
-    } while (0)
     if (D == 128) {
-        if (split_qk) PFA_LAUNCH_BF16_P(128, true);
-        else PFA_LAUNCH_BF16_P(128, false);
+        if (prep) launch_bf16_mode<128, true>(split_qk, f16, q, k, v, out, w, sched, geom, p,
+                                              prep_k, part, n_items, stream, app);
+        else launch_bf16_mode<128, false>(split_qk, f16, q, k, v, out, w, sched, geom, p,
+                                          prep_k, part, n_items, stream, app);
     } else {
-        if (split_qk) PFA_LAUNCH_BF16_P(64, true);
-        else PFA_LAUNCH_BF16_P(64, false);
+        if (prep) launch_bf16_mode<64, true>(split_qk, f16, q, k, v, out, w, sched, geom, p,
+                                             prep_k, part, n_items, stream, app);
+        else launch_bf16_mode<64, false>(split_qk, f16, q, k, v, out, w, sched, geom, p,
+                                         prep_k, part, n_items, stream, app);
     }
-#undef PFA_LAUNCH_BF16_P
-#undef PFA_LAUNCH_BF16
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && sched.max_chunks > 1 && !merge)
+    if (e == hipSuccess && sched.max_chunks > 1 && !part.cnt)
         e = launch_attn_combine(part, out, sched, geom, D, kWaves, kBN, n_items, stream);
     return e;
 }
@@ -1079,19 +1145,19 @@ hipError_t launch_attn_q8(const Q8Store& st8, float* out, void* ws, const AttnSc
         hipLaunchKernelGGL((stage_kv_q8_kernel<128, true>), sgrid, sblock, 0, stream, st8, wb,
                            ks_ws, sched, geom.Hkv);
         if (merge)
-            hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true, true>), grid, block, 0,
+            hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true, true, false>), grid, block, 0,
                                stream, nullptr, w, out, sched, geom, p, part, st8);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true, false>), grid, block, 0,
+            hipLaunchKernelGGL((attn_bf16_kernel<128, false, false, true, false, false>), grid, block, 0,
                                stream, nullptr, w, out, sched, geom, p, part, st8);
     } else {
         hipLaunchKernelGGL((stage_kv_q8_kernel<64, false>), sgrid, sblock, 0, stream, st8, wb,
                            ks_ws, sched, geom.Hkv);
         if (merge)
-            hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true, true>), grid, block, 0,
+            hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true, true, false>), grid, block, 0,
                                stream, nullptr, w, out, sched, geom, p, part, st8);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true, false>), grid, block, 0,
+            hipLaunchKernelGGL((attn_bf16_kernel<64, false, false, true, false, false>), grid, block, 0,
                                stream, nullptr, w, out, sched, geom, p, part, st8);
     }
     hipError_t e = hipGetLastError();

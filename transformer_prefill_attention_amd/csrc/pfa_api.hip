@@ -319,8 +319,8 @@ int make_plan(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim, 
     p.tile_keys = bf16 ? pfa::kBf16TileKeys : kF32TileKeys;
     choose_geometry(n_head, n_head_kv, scale, causal, p.waves, p.geom);
     p.items = build_sched(st, 32 * p.geom.rb, p.sched);
-    // plain bf16 (and the 8-bit kernels, which plan as bf16): short tile steps
-    choose_split(p, head_dim, precision == PFA_PREC_BF16);
+    // plain bf16 and f16 (and the 8-bit kernels, which plan as bf16): short tile steps
+    choose_split(p, head_dim, precision == PFA_PREC_BF16 || precision == PFA_PREC_F16);
     if ((long long)p.items * p.sched.max_chunks * p.geom.chunks * p.geom.Hkv >= (1LL << 31))
         return fail(PFA_ERR_UNSUPPORTED, "grid too large");
     if (bf16) {
@@ -359,11 +359,19 @@ const char* pfa_version(void) {
            "8-bit quantised sessions)";
 }
 
+static bool known_precision(int precision) {
+    return precision == PFA_PREC_F32 || precision == PFA_PREC_BF16 ||
+           precision == PFA_PREC_BF16X3 || precision == PFA_PREC_F16;
+}
+static int bad_precision(int precision) {
+    return fail(PFA_ERR_INVALID_ARG, "precision must be PFA_PREC_F32, PFA_PREC_BF16, "
+                                     "PFA_PREC_BF16X3 or PFA_PREC_F16 (got %d)", precision);
+}
+
 static size_t workspace_for(const pfa::SeqTable& st, int n_head, int n_head_kv, int head_dim,
                             int precision, bool prep_q, bool krot_in_ws, bool tiled = false) {
-    if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) {
-        fail(PFA_ERR_INVALID_ARG, "precision must be PFA_PREC_F32, PFA_PREC_BF16 or "
-                                  "PFA_PREC_BF16X3 (got %d)", precision);
+    if (!known_precision(precision)) {
+        bad_precision(precision);
         return 0;
     }
     Plan p;
@@ -395,8 +403,8 @@ size_t pfa_chunk_workspace_bytes(const int32_t* q_offsets, const int32_t* kv_off
     pfa::SeqTable st;
     if (build_chunk_seqs(q_offsets, kv_offsets, n_seqs, T_q, T_kv, st)) return 0;
     if (fused == 2 && precision == PFA_PREC_F32) {
-        fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16 or "
-                                  "PFA_PREC_BF16X3");
+        fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16, "
+                                  "PFA_PREC_BF16X3 or PFA_PREC_F16");
         return 0;
     }
     return workspace_for(st, n_head, n_head_kv, head_dim, precision, fused != 0, false,
@@ -414,8 +422,9 @@ size_t pfa_kv_tiles_bytes(int n_slots, int max_rows, int n_head_kv, int head_dim
         return 0;
     }
     if (check_geometry(max_rows, n_head_kv, n_head_kv, head_dim)) return 0;
-    if (precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3) {
-        fail(PFA_ERR_INVALID_ARG, "kv_tiles are for PFA_PREC_BF16 or PFA_PREC_BF16X3 (got %d)",
+    if (precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3 && precision != PFA_PREC_F16) {
+        fail(PFA_ERR_INVALID_ARG,
+             "kv_tiles are for PFA_PREC_BF16, PFA_PREC_BF16X3 or PFA_PREC_F16 (got %d)",
              precision);
         return 0;
     }
@@ -461,10 +470,7 @@ enum class Mode { kPlain, kFused, kChunk, kChunkFused, kChunkTiled };
 
 static int check_attn(float scale, int precision) {
     if (!std::isfinite(scale)) return fail(PFA_ERR_INVALID_ARG, "scale must be finite");
-    if (precision != PFA_PREC_F32 && precision != PFA_PREC_BF16 && precision != PFA_PREC_BF16X3)
-        return fail(PFA_ERR_INVALID_ARG,
-                    "precision must be PFA_PREC_F32, PFA_PREC_BF16 or PFA_PREC_BF16X3 (got %d)",
-                    precision);
+    if (!known_precision(precision)) return bad_precision(precision);
     return PFA_OK;
 }
 
@@ -640,13 +646,15 @@ static int attn_common(Mode mode, const float* q, const float* k, const float* v
             app.cum[s + 1] = app.cum[s] + (n_new > 0 ? (kv_len + TK - 1) / TK - app.first[s] : 0);
         }
         return hip_status(pfa::launch_attn_bf16(q, k_attn, v_attn, out, kv_tiles, p.sched, p.geom,
-                                                head_dim, precision == PFA_PREC_BF16X3, prep,
-                                                false, part, p.items, (hipStream_t)stream, &app),
+                                                head_dim, precision == PFA_PREC_BF16X3,
+                                                precision == PFA_PREC_F16, prep, false, part,
+                                                p.items, (hipStream_t)stream, &app),
                           what);
     }
     if (bf16)
         return hip_status(pfa::launch_attn_bf16(q, k_attn, v_attn, out, workspace, p.sched, p.geom,
-                                                head_dim, precision == PFA_PREC_BF16X3, prep,
+                                                head_dim, precision == PFA_PREC_BF16X3,
+                                                precision == PFA_PREC_F16, prep,
                                                 mode == Mode::kFused, part, p.items,
                                                 (hipStream_t)stream),
                           what);
@@ -842,9 +850,9 @@ int qk_prep_chunk_attn_tiled(const float* q, const float* k, const float* v, flo
     if (rc || (rc = check_geometry(T_kv, n_head, n_head_kv, head_dim))) return rc;
     if ((rc = check_attn(scale, precision)) || (rc = check_window(window, causal))) return rc;
     if (precision == PFA_PREC_F32)
-        return fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16 or "
-                                         "PFA_PREC_BF16X3 (the f32 mode reads the f32 cache: "
-                                         "qk_prep_chunk_attn)");
+        return fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16, "
+                                         "PFA_PREC_BF16X3 or PFA_PREC_F16 (the f32 mode reads "
+                                         "the f32 cache: qk_prep_chunk_attn)");
     if ((rc = check_rope(head_dim, rope_dim, rope_freq_base, rms_eps))) return rc;
     if (max_rows < 1) return fail(PFA_ERR_INVALID_ARG, "max_rows must be >= 1 (got %d)", max_rows);
     pfa::SeqTable st;
@@ -1102,7 +1110,8 @@ void kernel_names(int entry, int precision, int D, int rope_dim, const Plan& p, 
             append(buf, n, "qknorm_rope_kernel<%d,%d,true>", D, qknorm_mode(D, rope_dim));
             sep = " + ";
         }
-        append(buf, n, "%sstage_kv_q8_kernel<%d,%s> + attn_bf16_kernel<%d,false,false,true,%s>",
+        append(buf, n,
+               "%sstage_kv_q8_kernel<%d,%s> + attn_bf16_kernel<%d,false,false,true,%s,false>",
                sep, D, D == 128 ? "true" : "false", D, merge);
     } else if (precision == PFA_PREC_F32) {
         if (fused) {
@@ -1112,19 +1121,22 @@ void kernel_names(int entry, int precision, int D, int rope_dim, const Plan& p, 
                p.sched.paired ? "true" : "false", merge);
     } else {
         const char* sp = precision == PFA_PREC_BF16X3 ? "true" : "false";
+        const char* hf = precision == PFA_PREC_F16 ? "true" : "false";
         if (entry == PFA_ENTRY_CHUNK_PREP || tiled) {
             append(buf, n, "qknorm_rope_kernel<%d,%d,false> + ", D, qknorm_mode(D, rope_dim));
         }
         if (tiled) {
-            append(buf, n, "append_tiles_kernel<%d,%s> + attn_bf16_kernel<%d,%s,true,false,%s>", D,
-                   sp, D, sp, merge);
+            append(buf, n,
+                   "append_tiles_kernel<%d,%s,%s> + attn_bf16_kernel<%d,%s,true,false,%s,%s>", D,
+                   sp, hf, D, sp, merge, hf);
             if (split_keys && !p.counters) append(buf, n, " + attn_combine_kernel<%d>", D);
             return;
         }
         if (fused) append(buf, n, "rope_table_kernel<%d,%s> + ", D, sp);
-        append(buf, n, "stage_kv_bf16_kernel<%d,%s,%s> + attn_bf16_kernel<%d,%s,%s,false,%s>", D,
-               sp, entry == PFA_ENTRY_PREP ? "true" : "false", D, sp, fused ? "true" : "false",
-               merge);
+        append(buf, n,
+               "stage_kv_bf16_kernel<%d,%s,%s,%s> + attn_bf16_kernel<%d,%s,%s,false,%s,%s>", D,
+               sp, entry == PFA_ENTRY_PREP ? "true" : "false", hf, D, sp,
+               fused ? "true" : "false", merge, hf);
     }
     if (split_keys && !p.counters) append(buf, n, " + attn_combine_kernel<%d>", D);
 }
@@ -1139,8 +1151,8 @@ int plan_query(int entry, const int32_t* q_offsets, const int32_t* kv_offsets, i
         return fail(PFA_ERR_INVALID_ARG, "unknown entry %d", entry);
     const bool tiled = entry == PFA_ENTRY_CHUNK_TILED;
     if (tiled && precision == PFA_PREC_F32)
-        return fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16 or "
-                                         "PFA_PREC_BF16X3");
+        return fail(PFA_ERR_INVALID_ARG, "qk_prep_chunk_attn_tiled takes PFA_PREC_BF16, "
+                                         "PFA_PREC_BF16X3 or PFA_PREC_F16");
     const bool prefill = entry == PFA_ENTRY_PREFILL || entry == PFA_ENTRY_PREP;
     const bool q8 = entry == PFA_ENTRY_Q8 || entry == PFA_ENTRY_Q8_PREP;
     const bool fused = entry == PFA_ENTRY_PREP || entry == PFA_ENTRY_CHUNK_PREP ||

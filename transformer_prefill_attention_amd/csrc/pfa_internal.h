@@ -209,10 +209,11 @@ struct TileAppend {
 // kernel; K too, on its way into the tiles, when prep_k -- over a cached prefix
 // the cache already holds rotated keys).  app != nullptr: ws is the caller's kept
 // tiles (sched.tile_off / n_tiles describe its slots); only the touched tiles are
-// staged and no rotary-table launch is needed.
+// staged and no rotary-table launch is needed.  split_qk: the split-score bf16 mode;
+// f16: IEEE binary16 operands in the same tile layouts (not with split_qk).
 hipError_t launch_attn_bf16(const float* q, const float* k, const float* v, float* out, void* ws,
                             const AttnSched& sched, const AttnGeom& geom, int D, bool split_qk,
-                            const PrepParams* prep, bool prep_k, const Partials& part,
+                            bool f16, const PrepParams* prep, bool prep_k, const Partials& part,
                             int n_items, hipStream_t stream, const TileAppend* app = nullptr);
 
 // Attention through an 8-bit store, on the bf16 kernel's schedule: the scores are the

@@ -21,10 +21,12 @@ LIB_PATH = os.path.join(_HERE, "libpfa.so")
 PRECISION_F32 = 0
 PRECISION_BF16 = 1
 PRECISION_BF16X3 = 2
+PRECISION_F16 = 3
 _PRECISIONS = {"f32": PRECISION_F32, "fp32": PRECISION_F32, "float32": PRECISION_F32,
                "bf16": PRECISION_BF16, "bfloat16": PRECISION_BF16, "bf16x3": PRECISION_BF16X3,
+               "f16": PRECISION_F16, "fp16": PRECISION_F16, "float16": PRECISION_F16,
                PRECISION_F32: PRECISION_F32, PRECISION_BF16: PRECISION_BF16,
-               PRECISION_BF16X3: PRECISION_BF16X3}
+               PRECISION_BF16X3: PRECISION_BF16X3, PRECISION_F16: PRECISION_F16}
 
 # Every symbol include/pfa.h declares.
 EXPORTS = ("qknorm_rope", "gqa_prefill_attn", "qk_prep_attn", "pfa_workspace_bytes",
@@ -202,7 +204,7 @@ def _prec(precision):
     try:
         return _PRECISIONS[precision]
     except KeyError:
-        raise ValueError(f"precision must be 'f32', 'bf16' or 'bf16x3', got {precision!r}") from None
+        raise ValueError(f"precision must be 'f32', 'bf16', 'bf16x3' or 'f16', got {precision!r}") from None
 
 
 def workspace_bytes(T: int, n_head: int, n_head_kv: int, head_dim: int, precision="f32",
