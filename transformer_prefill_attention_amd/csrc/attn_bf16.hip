@@ -623,13 +623,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                 for (int e = 0; e < 8; ++e) ss += xq[s][e] * xq[s][e];
             ss += other_half(ss);
             const float rs = 1.0f / sqrtf(ss * (1.0f / D) + prep.eps);
+            // the norm weights of this lane half's dims, 16 bytes at a time (the pointer is
+            // 16-byte aligned, as the entry points check)
+            const floatx4* w4 = reinterpret_cast<const floatx4*>(prep.wq + hl * (D / 2));
 #pragma unroll
-            for (int s = 0; s < NQS; ++s)
+            for (int s = 0; s < NQS; ++s) {
+                const floatx4 wa = w4[2 * s], wb = w4[2 * s + 1];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    xq[s][e] = ok ? xq[s][e] * rs * prep.wq[hl * (D / 2) + 8 * s + e] : 0.0f;
+                    xq[s][e] = ok ? xq[s][e] * rs * (e < 4 ? wa[e] : wb[e - 4]) : 0.0f;
+            }
             const int pos = ok ? qi + dsh - ks0 : 0;  // rows past the end: any valid table entry
+            // table row of the position; two (cos, sin) pairs per 16-byte load (rows and
+            // the table start on 16-byte boundaries)
             const float2* trow = tab + pos * (D / 2);
+            auto pairs = [&](int j) {  // pairs j and j + 1 (j even)
+                return *reinterpret_cast<const floatx4*>(trow + j);
+            };
             if (n == D) {
                 // dim c pairs with c +- D/2: the same register of the other lane half.
                 // Registers are exchanged two at a time: swap(a, b) hands lanes 0-31
@@ -646,9 +656,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
                         const float pa = __builtin_bit_cast(float, hl ? ba[0] : ab[1]);
                         const float pb = __builtin_bit_cast(float, hl ? ab[0] : ba[1]);
                         const float sg = hl ? 1.0f : -1.0f;
-                        const float2 ta = trow[8 * s + e], tb = trow[8 * s + e + 1];
-                        xq[s][e] = xq[s][e] * ta.x + sg * pa * ta.y;
-                        xq[s][e + 1] = xq[s][e + 1] * tb.x + sg * pb * tb.y;
+                        const floatx4 t = pairs(8 * s + e);
+                        xq[s][e] = xq[s][e] * t[0] + sg * pa * t[1];
+                        xq[s][e + 1] = xq[s][e + 1] * t[2] + sg * pb * t[3];
                     }
             } else if (n == D / 2) {
                 // dims c < D/2 (lane half 0) pair with c + D/4: register step s + NQS/2
@@ -658,9 +668,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const float* __r
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const float a = xq[s][e], b = xq[s + NQS / 2][e];
-                            const float2 t = trow[8 * s + e];
-                            xq[s][e] = a * t.x - b * t.y;
-                            xq[s + NQS / 2][e] = a * t.y + b * t.x;
+                            const floatx4 t2 = pairs(8 * s + (e & ~1));
+                            const float c = t2[2 * (e & 1)], sn = t2[2 * (e & 1) + 1];
+                            xq[s][e] = a * c - b * sn;
+                            xq[s + NQS / 2][e] = a * sn + b * c;
                         }
                 }
             } else {
