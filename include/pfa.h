@@ -94,7 +94,9 @@ typedef enum {
  *    same device current as the call) and, for PFA_PREC_BF16 and PFA_PREC_F16 (and
  *    the 8-bit calls), some sequence spans at least 2048 key rows, each item's key range is
  *    split over several workgroups whose partial results (32 x head_dim f32 plus
- *    two f32 per row, per wavefront) are merged: when no item has more than 4 key
+ *    two f32 per row, per wavefront) are merged (the chunk length is chosen from each
+ *    item's causally visible key tiles; a call with causal = 0 needs no more than this
+ *    size, which assumes a causal call): when no item has more than 4 key
  *    chunks, by the last of its workgroups to finish (then, at the next multiple
  *    of 256 bytes, one 8-byte arrival counter per item, head group and K/V head;
  *    tagged per call, so they need no clearing, and left 0), else by one more

@@ -184,10 +184,14 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused, kv_lens=None, chunk=False)
     then partial results when the (query block, head) items cannot fill the GPU's
     workgroup slots (a target of 512 f32 or 256 bf16 workgroups) and are split by key,
     at least 128 keys a chunk and at most 32 chunks an item (PFA_PREC_BF16: only when a
-    sequence spans at least 2048 keys); with at most 4 chunks an item, one 8-byte arrival
-    counter per (item, head group, K/V head) after the partial results, at the next
-    multiple of 256 bytes.  ``lens``: query rows per sequence; ``kv_lens``: key rows
-    (default: the same)."""
+    sequence spans at least 2048 keys).  The chunk length: in the 16-bit modes, the one
+    that fills the target with items of n_max tiles each; in f32 the shortest, from that
+    floor and 320 keys on, whose non-empty units -- every item's causally visible tiles cut
+    into chunks -- fit the target, but no longer than the 16-bit modes' length and, when
+    that gives at most 4 chunks an item, no shorter than n_max / 4.
+    With at most 4 chunks an item, one 8-byte arrival counter per (item, head group, K/V
+    head) follows the partial results, at the next multiple of 256 bytes.  ``lens``:
+    query rows per sequence; ``kv_lens``: key rows (default: the same)."""
     kv_lens = lens if kv_lens is None else kv_lens
     bf16 = prec != 0
     waves, tile = (8, 64) if bf16 else (4, 32)
@@ -200,10 +204,22 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused, kv_lens=None, chunk=False)
     n_max = _ceil(max(kv_lens), tile)
     wgs, target = items * chunks * Hkv, (1 if bf16 else 2) * 256
     kchunk = 0
-    # plain bf16 splits only sequences of at least 32 tiles (2048 keys)
-    if wgs < target and n_max >= (32 if prec == 1 else 2):
+    # plain bf16 and f16 split only sequences of at least 32 tiles (2048 keys)
+    if wgs < target and n_max >= (32 if prec in (1, 3) else 2):
         # at least 128 keys a chunk, at most 32 chunks an item
-        kchunk = max(_ceil(128, tile), _ceil(n_max, 32), _ceil(wgs * n_max, target))
+        floor = max(_ceil(128, tile), _ceil(n_max, 32))
+        k_full = max(floor, _ceil(wgs * n_max, target))
+        # each item's visible tiles: its last query row's keys (causal; a chunk's rows are
+        # the last of its sequence's key rows)
+        tiles = [(min(q0 + rows, n) - 1 + (kn - n)) // tile + 1
+                 for n, kn in zip(lens, kv_lens) for q0 in range(0, n, rows)]
+        lo = max(floor, _ceil(320, tile))
+        if _ceil(n_max, k_full) <= 4:
+            lo = max(lo, _ceil(n_max, 4))
+        if bf16:
+            lo = k_full
+        kchunk = next((c for c in range(lo, k_full)
+                       if sum(_ceil(t, c) for t in tiles) * chunks * Hkv <= target), k_full)
         if kchunk >= n_max:
             kchunk = 0
     parts = 0
@@ -237,7 +253,7 @@ def _ws(L, lens, H, Hkv, D, prec, pass_offsets=True, fused=0):
     ((300,), 8, 2, 128), ((1, 33, 0, 64, 65, 97), 4, 2, 128), ((90,), 6, 2, 64),
     ((2048,), 32, 8, 128), ((3072,), 32, 8, 128), ((2048, 2048), 16, 8, 128),
     ((6000, 100, 100), 32, 8, 128)])
-@pytest.mark.parametrize("prec", [0, 1, 2])
+@pytest.mark.parametrize("prec", [0, 1, 2, 3])
 @pytest.mark.parametrize("fused", [0, 1])
 def test_workspace_bytes_rule(L, lens, H, Hkv, D, prec, fused):
     assert _ws(L, lens, H, Hkv, D, prec, fused=fused) == \

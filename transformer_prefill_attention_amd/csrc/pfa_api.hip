@@ -15,6 +15,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <mutex>
+#include <vector>
 
 #include "pfa_device.h"
 #include "pfa_internal.h"
@@ -251,7 +252,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // workgroup slots (target: 256 CUs x 2 f32 or x 1 bf16 workgroups), cut every
 // item's key tiles into chunks of kchunk tiles.  With the longest item at n_max
 // tiles, a causal item of n tiles becomes ceil(n / kchunk) units; kchunk = wgs
-// n_max / target keeps a causal single sequence near target / 2 + wgs / 2 units.
+// n_max / target keeps a causal single sequence near target / 2 + wgs / 2 units, so the
+// f32 kernel takes the shortest chunk (from kSplitMinKeys on) whose units still fit the
+// target, counted from each item's own tiles.
 // Each unit re-reads its Q rows and writes a partial result, so a chunk holds at
 // least 128 keys (at T = 512 shorter chunks were 4-12% slower; a chunk of 1024
 // new rows over 7168 cached ones, whose items fill only half the slots, gets two:
@@ -269,6 +272,15 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // unsplit 32.7 us, split 40.1 in place, 42.3 with the combine launch).
 constexpr int kMaxKeyChunks = 32;
 constexpr int kBf16SplitTiles = 32;
+// Shortest key chunk the causally balanced split of the f32 kernel (below) may choose.
+// Measured, f32, 32/8 heads of 128: T = 896 / 1024 / 1152 / 1280 split into 10 / 11 / 15 /
+// 19-tile chunks instead of 13 / 16 / 21 / 25 ran 0.123 -> 0.101, 0.144 -> 0.111, 0.180 ->
+// 0.140 and 0.213 -> 0.171 ms, but T = 768 in 6-tile chunks (192 keys) instead of 9 ran
+// 0.092 -> 0.110 ms.  The 16-bit kernel lost at every length tried (bf16x3: T = 1024 in
+// 6 tiles of 64 keys instead of 8, +2.6%; T = 1280 in 10 instead of 13, +6%): its units'
+// fixed work (eight wavefronts' prologue, partial results, merge) weighs more.
+constexpr int kSplitMinKeys = 320;
+
 void choose_split(Plan& p, int head_dim, bool short_steps) {
     p.head_dim = head_dim;
     const long long wgs = (long long)p.items * p.geom.chunks * p.geom.Hkv;
@@ -279,8 +291,38 @@ void choose_split(Plan& p, int head_dim, bool short_steps) {
     const int n_split = short_steps ? kBf16SplitTiles : 2;  // fewest tiles worth splitting
     int kchunk = 0;
     if (wgs < target && n_max >= n_split) {
-        const long long k = (wgs * n_max + target - 1) / target;
-        kchunk = (int)std::max(k_min, k);
+        // As if every item spanned n_max tiles: the chunk length that fills the target
+        const long long k_full = std::max(k_min, (wgs * n_max + target - 1) / target);
+        // The items' own tile counts (under the causal mask a sequence's early query blocks
+        // see few keys, so k_full leaves most units short and half the slots idle): the
+        // shortest chunk length from k_min on whose non-empty units still fit the target,
+        // and, where k_full's chunks can be merged in place, no more chunks than that takes.
+        // Chunks stay at least kSplitMinKeys long; the 16-bit kernels keep k_full (see
+        // kSplitMinKeys).  Computed without the window, as the workspace query is.
+        const long long min_tiles = (kSplitMinKeys + p.tile_keys - 1) / p.tile_keys;
+        long long c_lo = std::max(k_min, min_tiles);
+        if ((n_max + k_full - 1) / k_full <= pfa::kMergeChunks)
+            c_lo = std::max(c_lo, (long long)(n_max + pfa::kMergeChunks - 1) / pfa::kMergeChunks);
+        if (p.waves == 8) c_lo = k_full;
+        p.sched.kchunk = 0;
+        p.sched.max_chunks = 1;
+        std::vector<int> tiles((size_t)p.items);
+        for (int i = 0; i < p.items; ++i) {
+            const pfa::WorkItem w =
+                pfa::decode_item(p.sched, p.geom, i * p.geom.chunks * p.geom.Hkv);
+            const pfa::KeyRange r = pfa::item_key_range(p.sched, p.geom, w, p.tile_keys);
+            tiles[(size_t)i] = r.n_tiles - r.t_first;
+        }
+        long long k = k_full;
+        for (long long c = c_lo; c < k_full; ++c) {
+            long long units = 0;
+            for (const int t : tiles) units += (t + c - 1) / c;
+            if (units * p.geom.chunks * p.geom.Hkv <= target) {
+                k = c;
+                break;
+            }
+        }
+        kchunk = (int)k;
         if (kchunk >= n_max) kchunk = 0;
     }
     p.sched.kchunk = kchunk;
