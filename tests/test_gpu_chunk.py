@@ -167,6 +167,40 @@ def test_chunk_without_prefix_is_prefill_bit_exact():
         np.testing.assert_array_equal(a, b.cpu().numpy())
 
 
+def test_chunk_without_prefix_pairs_like_prefill():
+    """1536 rows, nothing cached, 32/8 heads of 128: the f32 prefill plan pairs query blocks
+    (one workgroup per CU) in place of a split into long key chunks, and the chunk entry --
+    whose call is prefill -- takes the same plan, so the two agree bit for bit; the gated
+    chunk output and the fused chunk entry on that plan match the oracle on sampled rows."""
+    c = Case("no_prefix_1536", (1536,), (0,), 32, 8, 128, 128, seed=702)
+    kw = dict(T_q=1536, n_head=32, n_head_kv=8, head_dim=128)
+    offs = dict(q_offsets=[0, 1536], kv_offsets=[0, 1536])
+    pp = pfa.attn_plan(pfa.ENTRY_PREFILL, **kw)
+    pc = pfa.attn_plan(pfa.ENTRY_CHUNK, T_kv=1536, **kw, **offs)
+    pf = pfa.attn_plan(pfa.ENTRY_CHUNK_PREP, T_kv=1536, **kw, **offs)
+    assert pp["paired"] == pc["paired"] == pf["paired"] == 1
+    assert pp["kernels"] == pc["kernels"] == "attn_f32_kernel<128,false,true,false>"
+    dev = torch.device("cuda:0")
+    a = _chunk_gpu(c, "f32")
+    print(f"gqa_prefill_attn {c.w.name}: T={c.w.T} f32 (paired)", flush=True)
+    b = pfa.gqa_prefill_attn(_t(c.q_prep, dev), _t(c.k_cache, dev), _t(c.v_cache, dev),
+                             head_dim=c.d, scale=c.w.softmax_scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(a, b.cpu().numpy())
+    rng = np.random.default_rng(703)
+    rows = np.unique(np.concatenate([[0, 31, 32, 767, 768, 1535],
+                                     rng.integers(0, 1536, 40)])).astype(np.int64)
+    assert_f32_parity(a[rows], _chunk_ref(c, rows=rows), c.label("gqa_chunk_attn", "f32") +
+                      " (paired), sampled rows")
+    gate = (2.0 * rng.standard_normal((1536, 32))).astype(np.float32)
+    g = _chunk_gpu(c, "f32", gate=gate)
+    assert_f32_parity(g[rows], _chunk_ref(c, rows=rows, gate=gate),
+                      c.label("gqa_chunk_attn", "f32") + " (paired, gate per head), sampled rows")
+    f, kc, vc = _fused_gpu(c, "f32")
+    assert_f32_parity(f[rows], _fused_ref(c, rows=rows)[0],
+                      c.label("qk_prep_chunk_attn", "f32") + " (paired), sampled rows")
+
+
 @pytest.mark.parametrize("precision", ["f32", "bf16"])
 def test_chunk_non_causal(precision):
     c = Case("packed_nc", *CASES["packed"], seed=701)

@@ -342,14 +342,35 @@ void choose_split(Plan& p, int head_dim, bool short_steps) {
 // 0.404 -> 0.313 ms and T = 4096 1.197 -> 1.080 ms, while T = 3072 (384 workgroups,
 // one or two per CU) ran 22% slower, T = 8192 and 16384 unchanged or slower (fused
 // entry 5%), packed sequences of unequal length 7% slower.  Plain prefill of one
-// sequence only, no key split, no window.
-bool pair_items(const Plan& p, const pfa::SeqTable& st, int causal, int window, bool chunk) {
+// sequence only, no key split, no window.  one_round: also when the paired grid is at most
+// one workgroup per CU (in place of a key split, below).
+bool pair_items(const Plan& p, const pfa::SeqTable& st, int causal, int window, bool chunk,
+                bool one_round) {
     if (!causal || window > 0 || chunk || st.n_seqs != 1 || p.sched.max_chunks != 1 ||
         p.items < 2)
         return false;
     const long long wgs = (long long)(p.items + 1) / 2 * p.geom.chunks * p.geom.Hkv;
     const int cus = device_cus();
-    return wgs % cus == 0 && wgs <= 2 * cus;
+    return (wgs % cus == 0 && wgs <= 2 * cus) || (one_round && wgs <= cus);
+}
+
+// Key tiles of the longest pair (items j and n - 1 - j; the middle item of an odd count
+// alone), from the items' own tile counts.
+static long long longest_pair_tiles(const Plan& p) {
+    pfa::AttnSched sc = p.sched;
+    sc.kchunk = 0;
+    sc.max_chunks = 1;
+    auto tiles = [&](int i) {
+        const pfa::WorkItem w = pfa::decode_item(sc, p.geom, i * p.geom.chunks * p.geom.Hkv);
+        const pfa::KeyRange r = pfa::item_key_range(sc, p.geom, w, p.tile_keys);
+        return (long long)(r.n_tiles - r.t_first);
+    };
+    long long best = 0;
+    for (int j = 0; j < (p.items + 1) / 2; ++j) {
+        const int k = p.items - 1 - j;
+        best = std::max(best, tiles(j) + (k != j ? tiles(k) : 0));
+    }
+    return best;
 }
 
 // Geometry, schedule, key split and workspace parts of one attention call.
@@ -543,6 +564,27 @@ static int plan_call(Mode mode, const pfa::SeqTable& st, int n_head, int n_head_
     // workspace parts: [bf16 K/V tiles + rotary table (Q prepared in the kernel), or f32
     // rotated K (fused prefill without k_rot_out)][partials, key split]; the tiled chunk
     // entry keeps its tiles and table in kv_tiles, so only the partials remain
+    // f32, one causal sequence, no window: paired items (one workgroup per CU) in place of
+    // a key split whose chunks are long, i.e. when a pair spans fewer tiles than two chunks
+    // (measured, 32/8 heads of 128: T = 1536 / 1792, chunks of 32 / 48 tiles against pairs of
+    // 49 / 57, 0.337 -> 0.241 and 0.485 -> 0.279 ms; T = 896 / 1024 / 1280, chunks of 10 /
+    // 11 / 19 against pairs of 29 / 33 / 41, the split stays faster: 0.101 / 0.111 / 0.171
+    // against 0.148 / 0.167 / 0.203 ms).  The size queries still count the split's partial
+    // results.  Only chunks of at least kSplitMinKeys (the lengths measured).  A chunk call
+    // over no cached rows is prefill and is planned as such, so that its results stay
+    // gqa_prefill_attn's bit for bit.
+    const bool as_prefill = !chunk || (st.n_seqs == 1 && st.koff[1] == st.off[1]);
+    bool pairs_for_split = false;
+    if (!bf16 && p.sched.max_chunks > 1 && causal && window == 0 && as_prefill &&
+        st.n_seqs == 1 && p.items >= 2 && (long long)p.sched.kchunk * p.tile_keys >= kSplitMinKeys &&
+        (long long)(p.items + 1) / 2 * p.geom.chunks * p.geom.Hkv <= device_cus() &&
+        longest_pair_tiles(p) < 2LL * p.sched.kchunk) {
+        p.sched.kchunk = 0;
+        p.sched.max_chunks = 1;
+        p.part_bytes = 0;
+        p.counters = 0;
+        pairs_for_split = true;
+    }
     cp.krot_in_ws = mode == Mode::kFused && !bf16 && !has_k_rot_out;
     cp.base = tiled ? 0 : prep_part_bytes(p, bf16, prep, cp.krot_in_ws);
     cp.part_off = p.part_bytes ? align256(cp.base) : cp.base;
@@ -554,7 +596,8 @@ static int plan_call(Mode mode, const pfa::SeqTable& st, int n_head, int n_head_
         p.counters = 0;
     }
     cp.need = p.part_bytes ? cp.part_off + p.part_bytes : cp.base;
-    p.sched.paired = !bf16 && pair_items(p, st, causal, window, chunk) ? 1 : 0;
+    p.sched.paired =
+        !bf16 && pair_items(p, st, causal, window, !as_prefill, pairs_for_split) ? 1 : 0;
     return PFA_OK;
 }
 
