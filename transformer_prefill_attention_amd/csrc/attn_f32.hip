@@ -16,9 +16,12 @@
 //    the B-operand layout the second product O^T += V^T P^T needs, so the
 //    probabilities never leave registers; the contraction index of each step is
 //    free to permute, and the V reads follow the score registers' key order.
-//  * Online softmax in base 2: Q is pre-multiplied by scale * log2(e); the row
-//    max is a 16-register max plus one cross-half exchange; the row sum stays a
-//    per-lane partial until the end.
+//  * Online softmax in base 2: Q is pre-multiplied by scale * log2(e).  The
+//    running max is lazy: the weights are taken against it at once and only a
+//    tile whose scores pass it by more than 8 takes the row max (one cross-half
+//    exchange), moves it and rescales O and the sum, so most tiles do no
+//    reduction and no rescaling.  The row sum stays a per-lane partial until the
+//    end.
 //  * Causal tile skipping: a workgroup visits only key tiles up to its last
 //    query row; a wavefront skips the tiles past its own diagonal, and only the
 //    diagonal/last tile is masked.
@@ -275,6 +278,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             *reinterpret_cast<floatx4*>(dst + row * stride + 4 * c4) = kvreg[i];
         }
     };
+
     // ---- accumulators
     floatx16 oacc[NCB];
 #pragma unroll
@@ -354,33 +358,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
                         sacc[r] = -INFINITY;
                 }
             }
-            float mt = sacc[0];
+            // Weights against the running max straight away; only when some score
+            // passes it by more than kLazyMax is the row max taken, O and l rescaled
+            // and the weights recomputed (m moves to the row max).  A row that has
+            // seen no key yet keeps m = -inf; exponents against -1e30 then give 0.
+            const float lmax = max16(sacc);
+            float pw[16];
+            {
+                const float m_sub = fmaxf(m_run, -1e30f);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float m_new = fmaxf(m_run, mt);
-            // a row that has seen no key yet (possible in a split key range over a
-            // cached prefix) keeps m = -inf: exponents against -1e30 make its
-            // weights 0, not NaN
-            const float m_use = fmaxf(m_new, -1e30f);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
+                for (int r = 0; r < 16; ++r) pw[r] = __builtin_amdgcn_exp2f(sacc[r] - m_sub);
+            }
+            if (__any(lmax > m_run + kLazyMax)) {
+                const float mt = max_halves(lmax);
+                const bool bump = mt > m_run + kLazyMax;
+                float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+                if (bump) m_run = mt;
+                const float m_new = fmaxf(m_run, -1e30f);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pw[r] = __builtin_amdgcn_exp2f(sacc[r] - m_new);
+                l_run *= (double)alpha;
+                // alpha is 1 in rows without a bump; hidden from the optimiser, which
+                // would otherwise make the multiplication unconditional
+                asm volatile("" : "+v"(alpha));
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+            }
             float psum = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[r] = __builtin_amdgcn_exp2f(sacc[r] - m_use);
-                psum += sacc[r];
-            }
-            l_run = l_run * (double)alpha + (double)psum;
+            for (int r = 0; r < 16; ++r) psum += pw[r];
+            l_run += (double)psum;
             if (more) {
                 store_rows(kn, KS);
                 load_rows(v, t + 1);
             }
-            // O^T[d][query] = alpha * O^T + sum_key V[key][d] P[query][key].  Each
-            // tile's products go into a fresh accumulator that is folded into O
-            // with one FMA per element: O is rounded once per tile instead of once
-            // per key, which keeps long rows dominated by one key accurate.  Step s
-            // contracts key 8(s/4) + 4hl + s%4, i.e. score register s of the lane.
+            // O^T[d][query] += sum_key V[key][d] P[query][key].  Each tile's products go
+            // into a fresh accumulator that is added to O once per element: O is rounded
+            // once per tile instead of once per key, which keeps long rows dominated by
+            // one key accurate.  Step s contracts key 8(s/4) + 4hl + s%4, i.e. score
+            // register s of the lane.
             float vop[16], vnext[16];
             auto read_v = [&](int cb, float* dst) {
 #pragma unroll
@@ -395,9 +413,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) pv[r] = 0.0f;
 #pragma unroll
-                for (int s = 0; s < 16; ++s) pv = mfma32x32x2(vop[s], sacc[s], pv);
+                for (int s = 0; s < 16; ++s) pv = mfma32x32x2(vop[s], pw[s], pv);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[cb][r] = fmaf(oacc[cb][r], alpha, pv[r]);
+                for (int r = 0; r < 16; ++r) oacc[cb][r] += pv[r];
 #pragma unroll
                 for (int s = 0; s < 16; ++s) vop[s] = vnext[s];
                 // keep the column-block chains apart (bounded live registers)

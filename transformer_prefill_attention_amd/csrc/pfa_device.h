@@ -34,6 +34,42 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Online softmax with a lazy running max: the max used as the exponent offset moves
+// only when a tile's score max passes it by more than this (log2 units), so weights
+// stay below 2^8 and the output and denominator are rescaled only when it moves.
+constexpr float kLazyMax = 8.0f;
+
+// v_max3_f32 without the NaN-quieting operand canonicalisation fmaxf gets (the
+// scores are MFMA results or -inf, never signalling NaNs)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// max of the 16 registers of a score block
+__device__ __forceinline__ float max16(const floatx16& x) {
+    float m = max3(x[0], x[1], x[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) m = max3(m, x[r], x[r + 1]);
+    return max3(m, x[15], x[15]);
+}
+
+// The value lane l ^ 32 holds.  v_permlane32_swap(a, b) leaves lanes 0-31 of a in
+// both halves of its first result and lanes 32-63 of b in both halves of its
+// second.  The second operand goes through an empty asm so that the compiler
+// cannot treat the two operands, and hence the two results, as one value (it
+// folds the second result into the first when both operands are the same value).
+__device__ __forceinline__ float other_half(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// max over the two lanes of one query (lanes l and l ^ 32)
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, other_half(x)); }
+
 // Sum over the 64 lanes of a wavefront: DPP rotations and quad permutations
 // inside each 16-lane row (plain VALU operand modifiers), then two cross-row
 // exchanges.  Every lane receives the total.
