@@ -109,15 +109,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, AttnSched sched, AttnGeom geom, PrepParams prep, Partials part) {
     constexpr int KS = D + 4;          // K tile row stride in LDS (floats): b128 reads conflict-free
-    constexpr int VS = D + 8;          // V tile row stride
+    // V tile: key 8j + 4h + i (h = bit 2 of the key) at row 4j + i of half h, rows of D
+    // floats; half 1 starts 16 D + 32 floats in.  A lane of half h reads its 16 operands of
+    // a column block from one base at offsets s * D (ds_read2st64_b32 pairs, no address
+    // arithmetic), and the two lane halves fall in different banks.
+    constexpr int VH = 16 * D + 32;
+    constexpr int VT = 32 * D + 32;
     constexpr int NQ = D / 2;          // Q operand registers per lane = MFMA steps of K Q^T
     constexpr int NCB = D / 32;        // 32-wide column blocks of O^T
-    constexpr int BUF = kBN * KS + kBN * VS;
+    constexpr int BUF = kBN * KS + VT;
     constexpr int F4_PER_ROW = D / 4;
     constexpr int LD_PER_THREAD = kBN * F4_PER_ROW / kThreads;  // float4 of K (and of V) per thread
     constexpr int QS = D + 4;          // staging stride of Q / O rows
-    static_assert(kWaves * 32 * QS <= 2 * BUF, "Q/O staging must fit in the K/V buffers");
-    __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+    // two K/V buffers, or the Q / O staging of the four wavefronts where that is larger
+    constexpr int SMEM = 2 * BUF > kWaves * 32 * QS ? 2 * BUF : kWaves * 32 * QS;
+    __shared__ __attribute__((aligned(16))) float smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, hl = lane >> 5, ln = lane & 31;
@@ -278,6 +284,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             *reinterpret_cast<floatx4*>(dst + row * stride + 4 * c4) = kvreg[i];
         }
     };
+    auto store_v = [&](float* dst) {
+#pragma unroll
+        for (int i = 0; i < LD_PER_THREAD; ++i) {
+            const int f = tid + kThreads * i;
+            const int key = f / F4_PER_ROW, c4 = f % F4_PER_ROW;
+            const int at = ((key >> 2) & 1) * VH + (4 * (key >> 3) + (key & 3)) * D + 4 * c4;
+            *reinterpret_cast<floatx4*>(dst + at) = kvreg[i];
+        }
+    };
 
     // ---- accumulators
     floatx16 oacc[NCB];
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
     load_rows(k_in, t_begin);
     store_rows(smem, KS);
     load_rows(v, t_begin);
-    store_rows(smem + kBN * KS, VS);
+    store_v(smem + kBN * KS);
     __syncthreads();
 
     for (int t = t_begin; t < t_end; ++t) {
@@ -386,14 +401,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
             }
-            float psum = 0.0f;
+            float psum = pw[0];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) psum += pw[r];
+            for (int r = 1; r < 16; ++r) psum += pw[r];
             l_run += (double)psum;
-            if (more) {
-                store_rows(kn, KS);
-                load_rows(v, t + 1);
-            }
             // O^T[d][query] += sum_key V[key][d] P[query][key].  Each tile's products go
             // into a fresh accumulator that is added to O once per element: O is rounded
             // once per tile instead of once per key, which keeps long rows dominated by
@@ -401,11 +412,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             // register s of the lane.
             float vop[16], vnext[16];
             auto read_v = [&](int cb, float* dst) {
+                const float* vb = vs + hl * VH + ln + 32 * cb;
 #pragma unroll
-                for (int s = 0; s < 16; ++s)
-                    dst[s] = vs[(8 * (s >> 2) + 4 * hl + (s & 3)) * VS + ln + 32 * cb];
+                for (int s = 0; s < 16; ++s) dst[s] = vb[s * D];
             };
+            // (the first block's operands are read before the next tile's K is staged)
             read_v(0, vop);
+            if (more) {
+                store_rows(kn, KS);
+                load_rows(v, t + 1);
+            }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 if (cb + 1 < NCB) read_v(cb + 1, vnext);
@@ -426,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_f32_kernel(
             store_rows(kn, KS);
             load_rows(v, t + 1);
         }
-        if (more) store_rows(kn + kBN * KS, VS);
+        if (more) store_v(kn + kBN * KS);
         __syncthreads();
     }
 
