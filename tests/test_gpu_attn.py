@@ -381,7 +381,7 @@ def test_prefill_2048_sampled(gpu_device, precision):
 
 
 # Paired items (each f32 workgroup takes the j-th longest and the j-th shortest query
-# block of the sequence): these shapes make 256 or 512 paired workgroups (e.g. 32 K/V heads
+# block of the sequence): these shapes make 256, 512 or 1024 paired workgroups (e.g. 32 K/V heads
 # of group 4 and 16 or 31 blocks of 32 rows).  T = 990 has an odd block count, so the middle
 # workgroup takes one block.  Compared element by element, plain and fused entry.
 PAIRED = [
@@ -394,6 +394,9 @@ PAIRED = [
     wl.Workload("paired_d64_500", (500,), 128, 32, 64, 32, 1e4, 1e-6, seed=34),
     # group 8: two head chunks per K/V head
     wl.Workload("paired_g8_500", (500,), 128, 16, 128, 64, 1e6, 1e-6, seed=35),
+    # 1024 paired workgroups (64 K/V heads, 32 blocks of 32 rows, a ragged last one): two
+    # whole rounds of two per CU
+    wl.Workload("paired_2rounds_1000", (1000,), 256, 64, 128, 128, 1e6, 1e-6, seed=36),
 ]
 
 

@@ -148,6 +148,18 @@ def test_paired_items_cover_every_item_once():
     # odd item count: the middle workgroup takes one item
     plan = _check_schedule(pfa.ENTRY_PREFILL, [990], [990], 128, 32, 128, "f32")
     assert plan["paired"] == 1 and plan["items"] % 2 == 1
+    # whole rounds of two paired workgroups per CU: 1024 at T = 8192, 2048 at 16384, and
+    # 1024 for 64 K/V heads at T = 1000 (odd item count again)
+    for T, H, Hkv in ((8192, 32, 8), (16384, 32, 8), (1000, 256, 64)):
+        plan = _check_schedule(pfa.ENTRY_PREFILL, [T], [T], H, Hkv, 128, "f32")
+        assert plan["paired"] == 1 and plan["workgroups"] % 512 == 0, (T, H, plan)
+        plan = _check_schedule(pfa.ENTRY_PREP, [T], [T], H, Hkv, 128, "f32")
+        assert plan["paired"] == 1, (T, H, plan)
+    # 1536 paired workgroups at T = 6144 (three per CU) stay unpaired, as does a 16-bit call
+    plan = _check_schedule(pfa.ENTRY_PREFILL, [6144], [6144], 32, 8, 128, "f32")
+    assert plan["paired"] == 0
+    plan = _check_schedule(pfa.ENTRY_PREFILL, [8192], [8192], 32, 8, 128, "bf16")
+    assert plan["paired"] == 0
 
 
 def test_key_split_at_short_inputs():
@@ -205,8 +217,9 @@ def test_plan_workspace_matches_the_size_queries():
 def test_plan_names_the_kernels_in_launch_order():
     p = pfa.attn_plan(pfa.ENTRY_PREP, T_q=8192, n_head=32, n_head_kv=8, head_dim=128,
                       rope_dim=128)
+    # (8192 rows: 1024 paired workgroups, two whole rounds)
     assert p["kernels"] == ("qknorm_rope_kernel<128,0,false> + "
-                            "attn_f32_kernel<128,true,false,false>")
+                            "attn_f32_kernel<128,true,true,false>")
     p = pfa.attn_plan(pfa.ENTRY_PREP, T_q=8192, n_head=32, n_head_kv=8, head_dim=128,
                       rope_dim=128, precision="bf16")
     assert p["kernels"] == ("rope_table_kernel<128,false> + "

@@ -337,13 +337,14 @@ void choose_split(Plan& p, int head_dim, bool short_steps) {
 
 // Paired items for the f32 kernel (AttnSched::paired): each workgroup takes item j and
 // item n - 1 - j of one causal sequence, so all workgroups visit the same number of key
-// tiles.  That balances the CUs only when the paired workgroups divide evenly over the
-// CUs (256 on MI355X) and all fit at once (at most two per CU): measured at 8B-like heads, T = 2048
-// 0.404 -> 0.313 ms and T = 4096 1.197 -> 1.080 ms, while T = 3072 (384 workgroups,
-// one or two per CU) ran 22% slower, T = 8192 and 16384 unchanged or slower (fused
-// entry 5%), packed sequences of unequal length 7% slower.  Plain prefill of one
-// sequence only, no key split, no window.  one_round: also when the paired grid is at most
-// one workgroup per CU (in place of a key split, below).
+// tiles.  That balances the CUs when the paired workgroups divide evenly over the CUs (256
+// on MI355X) with at most two per CU, or fill whole rounds of two per CU (every later
+// round then starts as the previous one's equal-length pairs end): measured at 8B-like
+// heads, T = 2048 0.404 -> 0.313 ms, T = 4096 1.197 -> 1.080 ms, T = 8192 (two rounds)
+// 4.13 -> 4.08 ms (fused entry 4.21 -> 4.14), T = 12288 and 16384 -1%; T = 3072 (384
+// workgroups, one or two per CU) ran 22% slower and packed sequences of unequal length 7%
+// slower.  Plain prefill of one sequence only, no key split, no window.  one_round: also
+// when the paired grid is at most one workgroup per CU (in place of a key split, below).
 bool pair_items(const Plan& p, const pfa::SeqTable& st, int causal, int window, bool chunk,
                 bool one_round) {
     if (!causal || window > 0 || chunk || st.n_seqs != 1 || p.sched.max_chunks != 1 ||
@@ -351,7 +352,8 @@ bool pair_items(const Plan& p, const pfa::SeqTable& st, int causal, int window, 
         return false;
     const long long wgs = (long long)(p.items + 1) / 2 * p.geom.chunks * p.geom.Hkv;
     const int cus = device_cus();
-    return (wgs % cus == 0 && wgs <= 2 * cus) || (one_round && wgs <= cus);
+    return (wgs % cus == 0 && wgs <= 2 * cus) || wgs % (2 * cus) == 0 ||
+           (one_round && wgs <= cus);
 }
 
 // Key tiles of the longest pair (items j and n - 1 - j; the middle item of an odd count
