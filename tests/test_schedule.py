@@ -155,7 +155,7 @@ def test_paired_items_cover_every_item_once():
         assert plan["paired"] == 1 and plan["workgroups"] % 512 == 0, (T, H, plan)
         plan = _check_schedule(pfa.ENTRY_PREP, [T], [T], H, Hkv, 128, "f32")
         assert plan["paired"] == 1, (T, H, plan)
-    # 1536 paired workgroups at T = 6144 (three per CU) stay unpaired, as does a 16-bit call
+    # T = 6144 would make 768 paired workgroups (a round and a half): unpaired; 16-bit calls too
     plan = _check_schedule(pfa.ENTRY_PREFILL, [6144], [6144], 32, 8, 128, "f32")
     assert plan["paired"] == 0
     plan = _check_schedule(pfa.ENTRY_PREFILL, [8192], [8192], 32, 8, 128, "bf16")
