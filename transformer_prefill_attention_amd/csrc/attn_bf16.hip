@@ -303,13 +303,19 @@ __global__ __launch_bounds__(256) void stage_kv_bf16_kernel(const float* __restr
             const bool full = n == D;
             const bool first = full ? qd < 2 : qd == 0;  // holds the pair's first dims
             const bool rot = full || qd < 2;
-            const float2* tj = trow + (full ? (qd & 1) * DQ : 0);
+            // (cos, sin) of two pairs per 16-byte load (table rows start on 16-byte
+            // boundaries)
+            const floatx4* tj = reinterpret_cast<const floatx4*>(trow + (full ? (qd & 1) * DQ : 0));
 #pragma unroll
-            for (int i = 0; i < DQ; ++i) {
-                const float yp = full ? dpp_f32<0x4E>(y[i]) : dpp_f32<0xB1>(y[i]);
-                const float2 t = tj[i];
-                const float yr = first ? y[i] * t.x - yp * t.y : y[i] * t.x + yp * t.y;
-                y[i] = rot ? yr : y[i];
+            for (int i = 0; i < DQ; i += 2) {
+                const floatx4 t2 = tj[i / 2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const float yp = full ? dpp_f32<0x4E>(y[i + u]) : dpp_f32<0xB1>(y[i + u]);
+                    const float tc = t2[2 * u], ts = t2[2 * u + 1];
+                    const float yr = first ? y[i + u] * tc - yp * ts : y[i + u] * tc + yp * ts;
+                    y[i + u] = rot ? yr : y[i + u];
+                }
             }
         } else {
             __syncthreads();  // (uniform: n is a kernel argument)

@@ -33,8 +33,9 @@
 //    workgroups (which the dispatcher spreads over the 8 XCDs) walk the same
 //    key tiles of one head together while each XCD's L2 keeps them.
 //  * Paired items (AttnSched::paired; the host pairs one causal sequence without a
-//    key split when the paired grid is a whole round over the CUs, or at most one
-//    workgroup per CU in place of a split into long chunks): the workgroup of
+//    key split when the paired grid is a whole round over the CUs or whole rounds of
+//    two per CU, or at most one workgroup per CU in place of a split into long
+//    chunks): the workgroup of
 //    slot j takes item j and then item n - 1 - j of the longest-first order, so
 //    every workgroup visits the same number of key tiles.  A workgroup alone on a CU runs at ~92% of the rate two
 //    co-resident ones reach together, so equal work per workgroup is what fills
