@@ -322,6 +322,52 @@ def test_row_max_covers_both_lane_halves(gpu_device, precision):
                            f"row max over both halves {precision}")
 
 
+@pytest.mark.parametrize("precision", ["f32", "bf16", "bf16x3", "f16"])
+def test_running_max_moves_mid_row(gpu_device, precision):
+    """The attention kernels keep a lazy running max: a tile moves it (and rescales the
+    output and the sum) only when one of its scores passes it by more than 8 (log2 units).
+    Here every query's component along a unit vector u is 3 (the rest N(0, 1/4)), keys are
+    N(0, 1/4), and two keys carry +36.6 u and +68 u, scoring ~14 and ~26 log2 units where
+    the others stay within ~2, so every row at or after key 150 moves its max in the middle
+    of its key range, and again at key 260 (on a later tile than its first in both tile
+    sizes: 32 keys in f32, 64 in the 16-bit kernels).  Scores stay within the long
+    workload's range (its x8 outlier keys reach ~29), so the workload gates apply."""
+    w = wl.Workload("late_max", (300,), 8, 2, 128, 128, 1e6, 1e-6, seed=43)
+    T, d, H, Hkv = w.T, w.head_dim, w.n_head, w.n_head_kv
+    rng = np.random.default_rng(43)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = 0.5 * rng.standard_normal((T, H, d))
+    q += (3.0 - q @ u)[..., None] * u          # every query: component 3 along u
+    k = 0.5 * rng.standard_normal((T, Hkv, d))
+    spikes = {150: 36.6, 260: 68.0}
+    for j, beta in spikes.items():
+        k[j] += beta * u
+    v = rng.standard_normal((T, Hkv, d))
+    q, k, v = (a.reshape(T, -1).astype(np.float32) for a in (q, k, v))
+    # the construction does what it says: for rows past each spike, the spike's score is
+    # more than 8 above every key of the tiles before its own (f64, log2 units)
+    sc = w.softmax_scale / np.log(2.0)
+    qh = q.reshape(T, H, d).astype(np.float64)
+    kh = k.reshape(T, Hkv, d).astype(np.float64)
+    for j in spikes:
+        for h in range(H):
+            s = (qh[j:, h] @ kh[:, h // (H // Hkv)].T) * sc   # rows j.. against all keys
+            first = (j // 64) * 64                             # the spike's 64-key tile
+            assert (s[:, j] - s[:, :first].max(axis=1) > 8.0).all()
+    x = wl.Inputs(q, k, v, np.ones(d, np.float32), np.ones(d, np.float32), np.zeros(0, np.int64))
+    got = _attn_gpu(w, _dev(x, gpu_device), precision=precision)
+    assert np.isfinite(got).all()
+    ref = _attn_ref(w, x)
+    if precision == "f32":
+        assert_f32_parity(got, ref, "running max moved mid-row f32")
+    else:
+        rounded = {"bf16": torch.bfloat16, "f16": torch.float16}
+        assert_bf16_parity(got, _attn_ref(w, _bf16_rounded_inputs(w, x, rounded[precision]))
+                           if precision in rounded else ref,
+                           f"running max moved mid-row {precision}")
+
+
 def test_tensors_past_4gb(gpu_device):
     # One sequence whose K and V pass 4 GB each: 128 K/V heads of 128 dims (64 KiB a row),
     # T = 131071 rows, T * heads * head_dim just under 2^31 (the documented limit).  The
