@@ -183,8 +183,9 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused, kv_lens=None, chunk=False)
     the longest, when Q is prepared in the kernel) or the f32 fused prefill's rotated K,
     then partial results when the (query block, head) items cannot fill the GPU's
     workgroup slots (a target of 512 f32 or 256 bf16 workgroups) and are split by key,
-    at least 128 keys a chunk and at most 32 chunks an item (PFA_PREC_BF16: only when a
-    sequence spans at least 2048 keys).  The chunk length: in the 16-bit modes, the one
+    at least 128 keys a chunk and at most 32 chunks an item (PFA_PREC_BF16 and F16: only
+    when a sequence spans at least 2048 keys; shorter ones, with items filling at most a
+    quarter of the slots, in two halves).  The chunk length: in the 16-bit modes, the one
     that fills the target with items of n_max tiles each; in f32 the shortest, from that
     floor and 320 keys on, whose non-empty units -- every item's causally visible tiles cut
     into chunks -- fit the target, but no longer than the 16-bit modes' length and, when
@@ -222,6 +223,12 @@ def _expected_workspace(lens, H, Hkv, D, prec, fused, kv_lens=None, chunk=False)
                        if sum(_ceil(t, c) for t in tiles) * chunks * Hkv <= target), k_full)
         if kchunk >= n_max:
             kchunk = 0
+    elif prec in (1, 3) and n_max >= 8 and wgs * 4 <= target:
+        # shorter inputs in plain bf16 / f16 with few items: two halves, when a half is at
+        # least 6 tiles or the items fill at most an eighth of the slots
+        half = _ceil(n_max, 2)
+        if half >= 6 or wgs * 8 <= target:
+            kchunk = half
     parts = 0
     if kchunk and items:
         units = items * _ceil(n_max, kchunk) * chunks * Hkv

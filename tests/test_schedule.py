@@ -172,10 +172,20 @@ def test_key_split_at_short_inputs():
         assert 1 < plan["max_key_chunks"] <= 4 and plan["workspace_bytes"] > 0
         assert plan["merge_in_place"] == 1
         assert plan["kernels"].endswith(kernel) and "combine" not in plan["kernels"]
-    # plain bf16 and f16 (the same kernel) split only sequences of at least 2048 keys
+    # plain bf16 and f16 (the same kernel) split sequences of at least 2048 keys to fill
+    # the slots; shorter ones whose items fill at most a quarter of them in two halves,
+    # when a half is at least 6 tiles (T = 768 and 1024 with 16/8 heads) or the items fill
+    # at most an eighth (T = 512 with 16/8 heads), not otherwise (T = 512 with 32/8 heads,
+    # T = 1024 with 32/8 heads)
     for prec in ("bf16", "f16"):
-        plan = _check_schedule(pfa.ENTRY_PREFILL, [512], [512], 16, 8, 128, prec)
-        assert plan["max_key_chunks"] == 1 and plan["merge_in_place"] == 0
+        for T, H, halves in ((512, 16, True), (768, 16, True), (1024, 16, True),
+                             (512, 32, False), (1024, 32, False), (256, 16, False)):
+            plan = _check_schedule(pfa.ENTRY_PREFILL, [T], [T], H, 8, 128, prec)
+            if halves:
+                assert plan["max_key_chunks"] == 2 and plan["merge_in_place"] == 1, (T, H, plan)
+                assert plan["key_chunk_tiles"] == (T // 64 + 1) // 2
+            else:
+                assert plan["max_key_chunks"] == 1 and plan["merge_in_place"] == 0, (T, H, plan)
         plan = _check_schedule(pfa.ENTRY_PREFILL, [2048], [2048], 16, 8, 128, prec)
         assert 1 < plan["max_key_chunks"] <= 4 and plan["merge_in_place"] == 1
         assert plan["kernels"].endswith(

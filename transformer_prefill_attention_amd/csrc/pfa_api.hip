@@ -266,10 +266,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // launch against 325 in place, bf16 71 against 95; in place with up to 4 chunks, f32
 // T = 512 / 1024 with 32/8 heads 61 -> 54 / 161 -> 151 us, bf16x3 T = 1024 with 16/8
 // heads 63 -> 51 us).
-// The bf16 kernel with plain bf16 or 8-bit inputs (short_steps) splits only when a
-// sequence spans at least kBf16SplitTiles tiles (2048 keys): its tile step is short,
-// and below that neither merge gains on the unsplit kernel (T = 512 with 32/8 heads:
-// unsplit 32.7 us, split 40.1 in place, 42.3 with the combine launch).
+// The bf16 kernel with plain bf16, f16 or 8-bit inputs (short_steps) splits by the
+// rule below only when a sequence spans at least kBf16SplitTiles tiles (2048 keys): its
+// tile step is short, and below that the fill-the-target chunks lose to the unsplit
+// kernel (T = 512 with 32/8 heads: unsplit 32.7 us, split 40.1 in place, 42.3 with the
+// combine launch).  Shorter inputs whose items fill at most a quarter of the slots are
+// cut in two halves instead (merged in place), when a half is at least 6 tiles or the
+// items fill at most an eighth of the slots: measured with 16/8 heads, T = 512 / 768 /
+// 1024, plain bf16 32.2 / 38.3 / 44.5 -> 31.2 / 35.4 / 41.2 us, fused entry 46.7 / 53.0
+// / 59.7 -> 45.2 / 50.8 / 55.9, 8-bit store 29.6 / 35.8 / 42.2 -> 28.6 / 32.4 / 36.5;
+// halves of 4 tiles at T = 512 with 32/8 heads lost (32.8 -> 33.9 us).
 constexpr int kMaxKeyChunks = 32;
 constexpr int kBf16SplitTiles = 32;
 // Shortest key chunk the causally balanced split of the f32 kernel (below) may choose.
@@ -324,6 +330,9 @@ void choose_split(Plan& p, int head_dim, bool short_steps) {
         }
         kchunk = (int)k;
         if (kchunk >= n_max) kchunk = 0;
+    } else if (short_steps && n_max >= 8 && wgs * 4 <= target) {
+        const int half = (n_max + 1) / 2;  // two chunks an item (see kBf16SplitTiles)
+        if (half >= 6 || wgs * 8 <= target) kchunk = half;
     }
     p.sched.kchunk = kchunk;
     p.sched.max_chunks = kchunk ? (n_max + kchunk - 1) / kchunk : 1;
