@@ -246,6 +246,43 @@ def test_attn_bf16_first_row_is_rounded_v(gpu_device):
                                           vb[s, kv * 128:(kv + 1) * 128])
 
 
+# Short 16-bit inputs whose items fill at most a quarter of the slots cut each item's keys in
+# two halves, merged in place by the item's second unit.  Ragged shapes on both branches of
+# that rule: a half of at least 6 tiles (T = 700: 11 tiles, halves of 6 and 5; T = 1000:
+# 16 tiles), and items filling at most an eighth of the slots (T = 600 with 8/4 heads:
+# halves of 5 tiles).  Compared element by element with the oracle, causal and not, through
+# the plain and the fused entry.
+HALVES = [
+    wl.Workload("halves_700", (700,), 16, 8, 128, 128, 1e6, 1e-6, seed=51),
+    wl.Workload("halves_1000", (1000,), 16, 8, 128, 128, 1e6, 1e-6, seed=52),
+    wl.Workload("halves_600_g2", (600,), 8, 4, 128, 128, 1e6, 1e-6, seed=53),
+]
+
+
+@pytest.mark.parametrize("w", HALVES, ids=[w.name for w in HALVES])
+@pytest.mark.parametrize("precision", ["bf16", "f16"])
+def test_attn_16bit_key_halves(gpu_device, w, precision):
+    plan = pfa.attn_plan(pfa.ENTRY_PREFILL, T_q=w.T, n_head=w.n_head, n_head_kv=w.n_head_kv,
+                         head_dim=w.head_dim, causal=True, precision=precision,
+                         q_offsets=np.asarray(w.seq_offsets, np.int32))
+    n_tiles = -(-w.T // 64)
+    assert plan["max_key_chunks"] == 2 and plan["merge_in_place"] == 1, plan
+    assert plan["key_chunk_tiles"] == -(-n_tiles // 2), plan
+    fplan = pfa.attn_plan(pfa.ENTRY_PREP, T_q=w.T, n_head=w.n_head, n_head_kv=w.n_head_kv,
+                          head_dim=w.head_dim, rope_dim=w.rope_dim, causal=True,
+                          precision=precision, q_offsets=np.asarray(w.seq_offsets, np.int32))
+    assert fplan["max_key_chunks"] == 2 and fplan["merge_in_place"] == 1, fplan
+    x = wl.make_inputs(w)
+    t = _dev(x, gpu_device)
+    for causal in (True, False):
+        assert_bf16_parity(_attn_gpu(w, t, precision=precision, causal=causal),
+                           _attn_ref(w, x, causal=causal),
+                           f"attn {precision} {w.name} causal={causal}")
+        assert_bf16_parity(_fused_gpu(w, t, precision=precision, causal=causal),
+                           _fused_ref(w, x, causal=causal),
+                           f"fused {precision} {w.name} causal={causal}")
+
+
 # ----------------------------------------------------------------------------- fused, bf16
 # qk_prep_attn with bf16 products: K is normalised and rotated in the staging kernel, Q in
 # the attention kernel's prologue; compared with the fused f64 oracle on the raw inputs.
